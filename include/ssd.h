@@ -1,0 +1,185 @@
+/*
+ * libssd — Mamba-2 selective state-space (SSD) chunked scan for AMD MI355X (gfx950).
+ *
+ * What it computes.  Per sequence and head h (group g = h / (nheads/ngroups)),
+ * with the state S = h^T of shape (headdim P, dstate N):
+ *
+ *     delta_t = softplus(dt_t + dt_bias_h)  (dt_softplus = 1)   or   dt_t + dt_bias_h
+ *     S_t     = exp(delta_t * A_h) * S_{t-1} + delta_t * x_t B_t^T
+ *     y_t     = S_t C_t + D_h * x_t,        S_{-1} = init,   final = S_last
+ *
+ * This is the selective SSM recurrence of gigipick.blogspot.com "LLM Mamba ...",
+ * section 1 (its printed equation was lost; the Mamba-2 form with one scalar decay
+ * per head is used).  It runs as a chunked scan: a per-chunk cumulative sum of
+ * delta*A, per-chunk states, cross-chunk state passing as an associative scan
+ * (scan page, section 2; aitrends.kr/articles/109906, "Helion-based B200 kernel
+ * redesign", which replaces the sequential state-passing loops forward and
+ * backward by an associative scan), and a per-chunk output stage.  The chunk
+ * carry (one chunk's final state seeds the next) follows the scan page,
+ * section 3 ("memory hierarchy").
+ *
+ * Conventions for every entry point.
+ *  - Tensors are dense, row-major (last index fastest):
+ *        x, out, dout, dx        (batch, seqlen, nheads, headdim)     io dtype
+ *        dt, ddt                 (batch, seqlen, nheads)              fp32
+ *        B, C, dB, dC            (batch, seqlen, ngroups, dstate)     io dtype
+ *        dt_bias, A, D, dA, dD, d_dt_bias   (nheads)                 fp32
+ *        init, final, d_final, d_init       (nstates, nheads, headdim, dstate)  fp32
+ *            nstates = batch, or nseq when cu_seqlens is given
+ *        cu_seqlens              (nseq + 1) int32, device memory, rising from 0 to seqlen
+ *  - With cu_seqlens the problem is one packed row (batch must be 1) holding nseq
+ *    sequences; each is chunked from its own first token, starts from its own init
+ *    state, and no state crosses a boundary.  Empty sequences are allowed (their
+ *    final state is their init).
+ *  - Every pointer except `problem` is DEVICE memory owned by the caller.  The
+ *    library allocates nothing, keeps no pointer after returning, and modifies no
+ *    input.  Outputs must not alias inputs or the workspace.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is queued on
+ *    it and the call returns before it runs; keep buffers alive until then.
+ *  - Every error the host can detect (NULL, shape, alignment, workspace size,
+ *    unsupported configuration) is returned BEFORE anything is queued.  A failed
+ *    launch returns SSD_ERR_HIP.  Nothing is printed; no exception crosses the ABI.
+ *  - Pointers must be 16-byte aligned.
+ *  - Supported: io dtype f32 or bf16; headdim and dstate in {16, 32, 64, 128}
+ *    (bf16 additionally needs headdim >= 32 and dstate >= 32);
+ *    chunk_size in {64, 128, 256}; nheads % ngroups == 0; any seqlen >= 0 and any
+ *    sequence lengths (partial chunks are masked).  Anything else returns
+ *    SSD_ERR_UNSUPPORTED.
+ *  - cu_seqlens contents are the caller's contract; with the environment variable
+ *    SSD_DEBUG=1 they are copied to the host and checked (SSD_ERR_VARLEN).  That
+ *    check synchronises the stream.
+ *  - Results are bitwise reproducible run to run (every reduction has a fixed
+ *    order); they differ from a sequential evaluation only by rounding order.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSD_ERR_SHAPE = 2,       /* negative or inconsistent sizes */
+  SSD_ERR_UNSUPPORTED = 3, /* valid, but outside the supported set above */
+  SSD_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  SSD_ERR_VARLEN = 6,      /* cu_seqlens failed the SSD_DEBUG check */
+  SSD_ERR_HIP = 7          /* a HIP call or kernel launch failed */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+  int32_t batch;       /* B (1 when cu_seqlens is given) */
+  int32_t seqlen;      /* L: tokens per batch row (total packed tokens with cu_seqlens) */
+  int32_t nheads;      /* H */
+  int32_t headdim;     /* P */
+  int32_t dstate;      /* N */
+  int32_t ngroups;     /* G; heads h*G/H share B and C of group h / (H/G) */
+  int32_t nseq;        /* number of packed sequences; read only when cu_seqlens != NULL */
+  int32_t io_dtype;    /* ssd_dtype of x, B, C, out, dout, dx, dB, dC */
+  int32_t dt_softplus; /* 1: delta = softplus(dt + dt_bias); 0: delta = dt + dt_bias */
+} ssd_problem;
+
+/* ABI version (SSD_ABI_VERSION) and a static message for a status code. */
+int32_t ssd_abi_version(void);
+const char* ssd_status_string(int32_t status);
+
+/* Number of chunk slots the per-chunk stage arrays below must hold:
+ * batch * ceil(seqlen / chunk_size), or floor((seqlen + nseq*(chunk_size-1)) / chunk_size)
+ * with cu_seqlens (an upper bound; unused trailing slots are never written).
+ * Returns -1 for an invalid problem. */
+int64_t ssd_num_chunks(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+
+/* Workspace sizes in bytes (0 for an invalid problem).  `packed` = 1 when
+ * cu_seqlens will be passed.  The forward workspace holds the chunk table,
+ * delta, the within-chunk cumsum, the chunk states, the passed states and
+ * C.B^T per chunk; the backward one adds the adjoint states. */
+size_t ssd_fwd_workspace_bytes(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+size_t ssd_bwd_workspace_bytes(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+/* Workspace for the ssd_stage_* entries (the chunk table only). */
+size_t ssd_stage_workspace_bytes(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+
+/* Forward pass: out = y, final_states = S_last (optional, may be NULL).
+ * dt_bias, D, init_states and cu_seqlens may be NULL (zero bias, no skip term,
+ * zero initial state, unpacked batch). */
+ssd_status ssd_fwd(const ssd_problem* problem,
+                   const void* x, const float* dt, const float* dt_bias, const float* A,
+                   const void* B, const void* C, const float* D,
+                   const float* init_states, const int32_t* cu_seqlens, int32_t chunk_size,
+                   void* out, float* final_states,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass for the loss L = <dout, y> + <d_final_states, final>.
+ * Inputs are those of ssd_fwd plus dout and d_final_states (NULL = 0).
+ * Outputs: dx, dB, dC (io dtype; dB and dC summed over each group's heads in
+ * fp32 before rounding), ddt (w.r.t. the raw dt input), dA (required), and the
+ * optional dD (required iff D != NULL), d_dt_bias, d_init_states.
+ * The forward intermediates are recomputed inside (nothing is saved). */
+ssd_status ssd_bwd(const ssd_problem* problem,
+                   const void* x, const float* dt, const float* dt_bias, const float* A,
+                   const void* B, const void* C, const float* D,
+                   const float* init_states, const int32_t* cu_seqlens, int32_t chunk_size,
+                   const void* dout, const float* d_final_states,
+                   void* dx, float* ddt, float* dA, void* dB, void* dC,
+                   float* dD, float* d_dt_bias, float* d_init_states,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Single-stage entry points (testing and per-stage timing).  Each queues exactly
+ * the kernels of one stage of ssd_fwd on explicit buffers.  nck = ssd_num_chunks().
+ * Per-chunk layouts (fp32 unless noted):
+ *     delta, acs     (nck, nheads, chunk_size); acs = within-chunk inclusive cumsum
+ *                    of delta*A in LOG2 units (natural-log value * log2(e));
+ *                    entries past a chunk's length are zero
+ *     chunk_decay    (nck, nheads) = acs at the chunk's last token (log2 units)
+ *     states, passed (nck, nheads, headdim, dstate): chunk-local end state T_c, and
+ *                    the state H_c entering each chunk
+ *     CB             (nck, ngroups, chunk_size, chunk_size) io dtype: C_i . B_j for
+ *                    j <= i (entries above the diagonal are not written)
+ */
+/* Stage 1 — per-chunk cumulative sum of delta*A (wavefront prefix sum). */
+ssd_status ssd_stage_chunk_cumsum(const ssd_problem* problem, const float* dt,
+                                  const float* dt_bias, const float* A,
+                                  const int32_t* cu_seqlens, int32_t chunk_size,
+                                  float* delta, float* acs, float* chunk_decay,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+/* Stage 2 — chunk states T_c = sum_j delta_j exp(acs_last - acs_j) x_j B_j^T (MFMA). */
+ssd_status ssd_stage_chunk_state(const ssd_problem* problem, const void* x, const void* B,
+                                 const float* delta, const float* acs,
+                                 const int32_t* cu_seqlens, int32_t chunk_size, float* states,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+/* Stage 3 — cross-chunk state passing E_c = exp(chunk_decay_c) H_c + T_c as an
+ * associative scan; passed = H_c, final_states = E_last (may be NULL). */
+ssd_status ssd_stage_state_passing(const ssd_problem* problem, const float* states,
+                                   const float* chunk_decay, const float* init_states,
+                                   const int32_t* cu_seqlens, int32_t chunk_size,
+                                   float* passed, float* final_states,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+/* Stage 4 — CB = C B^T per chunk and group (MFMA), lower triangle. */
+ssd_status ssd_stage_bmm_chunk(const ssd_problem* problem, const void* B, const void* C,
+                               const int32_t* cu_seqlens, int32_t chunk_size, void* CB,
+                               void* workspace, size_t workspace_bytes, void* stream);
+/* Stage 5 — y_i = sum_{j<=i} CB_ij exp(acs_i - acs_j) delta_j x_j
+ *               + exp(acs_i) H_c C_i + D x_i   (MFMA, bf16/fp32 store). */
+ssd_status ssd_stage_chunk_scan(const ssd_problem* problem, const void* x, const void* C,
+                                const void* CB, const float* delta, const float* acs,
+                                const float* passed, const float* D,
+                                const int32_t* cu_seqlens, int32_t chunk_size, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Plain device-to-device copy kernel of `bytes` bytes (16-byte multiple), used to
+ * calibrate hardware traffic counters against a kernel of known traffic. */
+ssd_status ssd_util_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBSSD_SSD_H */

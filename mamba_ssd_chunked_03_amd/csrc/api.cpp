@@ -1,0 +1,326 @@
+// C ABI of libssd: argument validation, workspace layout and launch order.
+//
+// Every check the host can make happens before the first launch, so an error
+// return never leaves partial work queued.  The library allocates nothing and
+// keeps no state between calls.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "internal.hpp"
+#include "ssd.h"
+
+using namespace ssd;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool okdim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Validate sizes and fill the kernel-side problem (device pointers unset).
+ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
+  if (!pr) return SSD_ERR_NULL;
+  if (pr->batch < 0 || pr->seqlen < 0 || pr->nheads <= 0 || pr->headdim <= 0 ||
+      pr->dstate <= 0 || pr->ngroups <= 0)
+    return SSD_ERR_SHAPE;
+  if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
+  if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
+  if (packed && (pr->batch != 1 || pr->nseq < 0)) return SSD_ERR_SHAPE;
+  if (pr->io_dtype != SSD_F32 && pr->io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+  if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
+  if (!okdim(pr->headdim) || !okdim(pr->dstate)) return SSD_ERR_UNSUPPORTED;
+  if (pr->io_dtype == SSD_BF16 && (pr->headdim < 32 || pr->dstate < 32)) return SSD_ERR_UNSUPPORTED;
+  const int64_t tokens = (int64_t)pr->batch * pr->seqlen;
+  if (tokens > INT32_MAX / 2 || (int64_t)pr->nheads > 65535 || (int64_t)pr->ngroups > 65535)
+    return SSD_ERR_UNSUPPORTED;
+  p.B = pr->batch;
+  p.L = pr->seqlen;
+  p.H = pr->nheads;
+  p.P = pr->headdim;
+  p.N = pr->dstate;
+  p.G = pr->ngroups;
+  p.io = pr->io_dtype;
+  p.softplus = pr->dt_softplus;
+  p.Q = Q;
+  p.packed = packed;
+  p.nseq = packed ? pr->nseq : pr->batch;
+  if (packed) {
+    if (p.nseq > 65535) return SSD_ERR_UNSUPPORTED;
+    p.nck = ((int64_t)p.L + (int64_t)p.nseq * (Q - 1)) / Q;
+  } else {
+    p.nck = (int64_t)p.B * ((p.L + Q - 1) / Q);
+  }
+  if (p.nck > INT32_MAX / 4) return SSD_ERR_UNSUPPORTED;
+  std::memset(&p.map, 0, sizeof(p.map));
+  p.map.Q = Q;
+  p.map.nck = (int32_t)p.nck;
+  p.map.packed = packed;
+  p.map.seqlen = p.L;
+  p.map.ncs = (p.L + Q - 1) / Q;
+  return SSD_OK;
+}
+
+inline size_t esize(const Prob& p) { return p.io == SSD_BF16 ? 2 : 4; }
+
+// Forward workspace layout (byte offsets, each 256-aligned).
+struct FwdLayout {
+  size_t tab, seq_off, delta, acs, decay, T, Hp, CB, end;
+};
+FwdLayout fwd_layout(const Prob& p) {
+  FwdLayout l;
+  size_t o = 0;
+  const size_t nck = (size_t)p.nck, H = p.H, st = (size_t)p.P * p.N;
+  l.tab = o;     o += p.packed ? up(nck * 16) : 0;
+  l.seq_off = o; o += p.packed ? up(((size_t)p.nseq + 1) * 4) : 0;
+  l.delta = o;   o += up(nck * H * p.Q * 4);
+  l.acs = o;     o += up(nck * H * p.Q * 4);
+  l.decay = o;   o += up(nck * H * 4);
+  l.T = o;       o += up(nck * H * st * 4);
+  l.Hp = o;      o += up(nck * H * st * 4);
+  l.CB = o;      o += up(nck * (size_t)p.G * p.Q * p.Q * esize(p));
+  l.end = o;
+  return l;
+}
+struct BwdLayout {
+  FwdLayout f;
+  size_t U, dE, end;
+};
+BwdLayout bwd_layout(const Prob& p) {
+  BwdLayout l;
+  l.f = fwd_layout(p);
+  size_t o = l.f.end;
+  const size_t nck = (size_t)p.nck, H = p.H, st = (size_t)p.P * p.N;
+  l.U = o;  o += up(nck * H * st * 4);
+  l.dE = o; o += up(nck * H * st * 4);
+  l.end = o;
+  return l;
+}
+size_t stage_ws(const Prob& p) { return fwd_layout(p).delta; }
+
+// Point the chunk map at the table inside a workspace and queue its build.
+ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st) {
+  if (!p.packed) return SSD_OK;
+  FwdLayout l = fwd_layout(p);
+  p.map.tab = (const int4*)(ws + l.tab);
+  p.map.seq_off = (const int32_t*)(ws + l.seq_off);
+  if (std::getenv("SSD_DEBUG") && std::getenv("SSD_DEBUG")[0] == '1') {
+    std::vector<int32_t> h((size_t)p.nseq + 1);
+    if (hipMemcpyAsync(h.data(), cu, h.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return SSD_ERR_HIP;
+    if (h[0] != 0 || h[p.nseq] != p.L) return SSD_ERR_VARLEN;
+    for (int s = 0; s < p.nseq; ++s)
+      if (h[s + 1] < h[s]) return SSD_ERR_VARLEN;
+  }
+  if (launch_build_table(p, cu, (int4*)(ws + l.tab), (int32_t*)(ws + l.seq_off), st) != hipSuccess)
+    return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+#define SSD_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return SSD_ERR_HIP; \
+  } while (0)
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if (q && !al16(q)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(int32_t s) {
+  switch (s) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL: return "a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "negative or inconsistent sizes";
+    case SSD_ERR_UNSUPPORTED: return "configuration outside the supported set";
+    case SSD_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_VARLEN: return "cu_seqlens failed the debug check";
+    case SSD_ERR_HIP: return "HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t ssd_num_chunks(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return -1;
+  return p.nck;
+}
+
+size_t ssd_fwd_workspace_bytes(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
+  return fwd_layout(p).end;
+}
+
+size_t ssd_bwd_workspace_bytes(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
+  return bwd_layout(p).end;
+}
+
+size_t ssd_stage_workspace_bytes(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
+  return stage_ws(p);
+}
+
+ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const float* dt_bias,
+                   const float* A, const void* B, const void* C, const float* D,
+                   const float* init_states, const int32_t* cu_seqlens, int32_t Q, void* out,
+                   float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  const bool has_tokens = (int64_t)p.B * p.L > 0;
+  if (has_tokens && (!x || !dt || !A || !B || !C || !out)) return SSD_ERR_NULL;
+  if (!all_aligned({x, dt, dt_bias, A, B, C, D, init_states, cu_seqlens, out, final_states, workspace}))
+    return SSD_ERR_ALIGN;
+  const FwdLayout l = fwd_layout(p);
+  if (l.end > 0 && (!workspace || workspace_bytes < l.end)) return SSD_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  s = setup_map(p, cu_seqlens, ws, st);
+  if (s != SSD_OK) return s;
+  float* delta = (float*)(ws + l.delta);
+  float* acs = (float*)(ws + l.acs);
+  float* decay = (float*)(ws + l.decay);
+  float* T = (float*)(ws + l.T);
+  float* Hp = (float*)(ws + l.Hp);
+  void* CB = ws + l.CB;
+  SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
+  SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
+  SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, final_states, 0, st));
+  SSD_TRY(launch_bmm_chunk(p, B, C, CB, st));
+  SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, D, out, st));
+  return SSD_OK;
+}
+
+ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const float* dt_bias,
+                   const float* A, const void* B, const void* C, const float* D,
+                   const float* init_states, const int32_t* cu_seqlens, int32_t Q,
+                   const void* dout, const float* d_final_states, void* dx, float* ddt, float* dA,
+                   void* dB, void* dC, float* dD, float* d_dt_bias, float* d_init_states,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  (void)x; (void)dt; (void)dt_bias; (void)A; (void)B; (void)C; (void)D; (void)init_states;
+  (void)dout; (void)d_final_states; (void)dx; (void)ddt; (void)dA; (void)dB; (void)dC; (void)dD;
+  (void)d_dt_bias; (void)d_init_states; (void)workspace; (void)workspace_bytes; (void)stream;
+  return SSD_ERR_UNSUPPORTED;
+}
+
+ssd_status ssd_stage_chunk_cumsum(const ssd_problem* pr, const float* dt, const float* dt_bias,
+                                  const float* A, const int32_t* cu_seqlens, int32_t Q,
+                                  float* delta, float* acs, float* chunk_decay, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  if (p.nck > 0 && (!dt || !A || !delta || !acs || !chunk_decay)) return SSD_ERR_NULL;
+  if (!all_aligned({dt, dt_bias, A, cu_seqlens, delta, acs, chunk_decay, workspace})) return SSD_ERR_ALIGN;
+  const size_t need = stage_ws(p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  s = setup_map(p, cu_seqlens, (char*)workspace, st);
+  if (s != SSD_OK) return s;
+  SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, chunk_decay, st));
+  return SSD_OK;
+}
+
+ssd_status ssd_stage_chunk_state(const ssd_problem* pr, const void* x, const void* B,
+                                 const float* delta, const float* acs, const int32_t* cu_seqlens,
+                                 int32_t Q, float* states, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  if (p.nck > 0 && (!x || !B || !delta || !acs || !states)) return SSD_ERR_NULL;
+  if (!all_aligned({x, B, delta, acs, cu_seqlens, states, workspace})) return SSD_ERR_ALIGN;
+  const size_t need = stage_ws(p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  s = setup_map(p, cu_seqlens, (char*)workspace, st);
+  if (s != SSD_OK) return s;
+  SSD_TRY(launch_chunk_state(p, x, B, delta, acs, states, kStateFwd, st));
+  return SSD_OK;
+}
+
+ssd_status ssd_stage_state_passing(const ssd_problem* pr, const float* states,
+                                   const float* chunk_decay, const float* init_states,
+                                   const int32_t* cu_seqlens, int32_t Q, float* passed,
+                                   float* final_states, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  if (p.nck > 0 && (!states || !chunk_decay || !passed)) return SSD_ERR_NULL;
+  if (!all_aligned({states, chunk_decay, init_states, cu_seqlens, passed, final_states, workspace}))
+    return SSD_ERR_ALIGN;
+  const size_t need = stage_ws(p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  s = setup_map(p, cu_seqlens, (char*)workspace, st);
+  if (s != SSD_OK) return s;
+  SSD_TRY(launch_state_passing(p, states, chunk_decay, init_states, passed, final_states, 0, st));
+  return SSD_OK;
+}
+
+ssd_status ssd_stage_bmm_chunk(const ssd_problem* pr, const void* B, const void* C,
+                               const int32_t* cu_seqlens, int32_t Q, void* CB, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  if (p.nck > 0 && (!B || !C || !CB)) return SSD_ERR_NULL;
+  if (!all_aligned({B, C, cu_seqlens, CB, workspace})) return SSD_ERR_ALIGN;
+  const size_t need = stage_ws(p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  s = setup_map(p, cu_seqlens, (char*)workspace, st);
+  if (s != SSD_OK) return s;
+  SSD_TRY(launch_bmm_chunk(p, B, C, CB, st));
+  return SSD_OK;
+}
+
+ssd_status ssd_stage_chunk_scan(const ssd_problem* pr, const void* x, const void* C,
+                                const void* CB, const float* delta, const float* acs,
+                                const float* passed, const float* D, const int32_t* cu_seqlens,
+                                int32_t Q, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  if (p.nck > 0 && (!x || !C || !CB || !delta || !acs || !passed || !out)) return SSD_ERR_NULL;
+  if (!all_aligned({x, C, CB, delta, acs, passed, D, cu_seqlens, out, workspace})) return SSD_ERR_ALIGN;
+  const size_t need = stage_ws(p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  s = setup_map(p, cu_seqlens, (char*)workspace, st);
+  if (s != SSD_OK) return s;
+  SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, passed, D, out, st));
+  return SSD_OK;
+}
+
+ssd_status ssd_util_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes == 0) return SSD_OK;
+  if (!dst || !src) return SSD_ERR_NULL;
+  if (!al16(dst) || !al16(src) || (bytes & 15)) return SSD_ERR_ALIGN;
+  SSD_TRY(launch_copy(dst, src, bytes, (hipStream_t)stream));
+  return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Device-side building blocks shared by the libssd kernels (gfx950 / CDNA4).
+//
+// - bf16 storage and conversion (hardware round-to-nearest-even on gfx950),
+// - MFMA wrappers with the lane layouts of v_mfma_f32_16x16x32_bf16 and
+//   v_mfma_f32_16x16x4_f32 (64-lane wavefronts),
+// - DPP-based wavefront scans (row_shr within 16-lane rows, row_bcast15/31
+//   across rows),
+// - the chunk map: which tokens a chunk slot covers, for batched rows and for
+//   packed sequences.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// log2(e): decays are stored and evaluated in base 2 so each exp is one v_exp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, b);
+}
+// two floats -> packed bf16 pair (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------------------ exp ----
+// 2^x with the hardware v_exp_f32 (results below 2^-126 flush to zero, which the
+// scan accepts: such decays are below fp32's normal range anyway).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// softplus(z) = max(z, 0) + log1p(exp(-|z|)), from its definition.
+__device__ __forceinline__ float softplus_f(float z) {
+  return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+}
+// d softplus / dz = 1 / (1 + exp(-z)), in a form that never overflows.
+__device__ __forceinline__ float sigmoid_f(float z) {
+  float e = expf(-fabsf(z));
+  float r = 1.f / (1.f + e);
+  return z >= 0.f ? r : e * r;
+}
+
+// ----------------------------------------------------------------- MFMA ----
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%16][8*(l/16) + 0..7], B[8*(l/16) + 0..7][l%16] and
+// D[4*(l/16) + r][l%16] for r = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(16x16) += A(16x4) * B(4x16), true fp32.  Lane l holds A[l%16][l/16],
+// B[l/16][l%16] and D[4*(l/16) + r][l%16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ DPP ----
+// DPP controls (GFX9 encoding).
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (Hillis-Steele with
+// DPP: shifts 1, 2, 4, 8 inside each 16-lane row, then the row carries).
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  v += dpp_f<kRowShr1>(0.f, v);
+  v += dpp_f<kRowShr2>(0.f, v);
+  v += dpp_f<kRowShr4>(0.f, v);
+  v += dpp_f<kRowShr8>(0.f, v);
+  v += dpp_f<kRowBcast15, 0xa>(0.f, v);
+  v += dpp_f<kRowBcast31, 0xc>(0.f, v);
+  return v;
+}
+
+// Broadcast lane 63's value to the whole wavefront.
+__device__ __forceinline__ float wave_last(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// ------------------------------------------------------------ chunk map ----
+// A chunk slot k covers tokens [start, start + len) of the flattened
+// (batch * seqlen) token axis, inside sequence `seq`.  Batched rows: row b is
+// sequence b, cut into ceil(seqlen / Q) chunks from its first token.  Packed
+// sequences: a table built on the device from cu_seqlens (len 0 = unused slot).
+struct ChunkMap {
+  int32_t Q;        // chunk size
+  int32_t nck;      // number of chunk slots
+  int32_t packed;   // 0: batched rows; 1: table
+  int32_t seqlen;   // batched: tokens per row
+  int32_t ncs;      // batched: chunks per row
+  const int4* tab;  // packed: {start, len, seq, flags (1 first, 2 last)}
+  const int32_t* seq_off;  // packed: first chunk slot of each sequence (nseq + 1)
+};
+
+struct ChunkInfo {
+  int32_t start, len, seq;
+  bool first, last;
+};
+
+__device__ __forceinline__ ChunkInfo chunk_info(const ChunkMap& m, int k) {
+  ChunkInfo ci;
+  if (!m.packed) {
+    int b = k / m.ncs, c = k - b * m.ncs;
+    ci.start = b * m.seqlen + c * m.Q;
+    ci.len = min(m.Q, m.seqlen - c * m.Q);
+    ci.seq = b;
+    ci.first = (c == 0);
+    ci.last = (c == m.ncs - 1);
+  } else {
+    int4 e = m.tab[k];
+    ci.start = e.x;
+    ci.len = e.y;
+    ci.seq = e.z;
+    ci.first = (e.w & 1) != 0;
+    ci.last = (e.w & 2) != 0;
+  }
+  return ci;
+}
+
+// Chunk slots [c0, c1) of sequence s.
+__device__ __forceinline__ void seq_chunks(const ChunkMap& m, int s, int& c0, int& c1) {
+  if (!m.packed) {
+    c0 = s * m.ncs;
+    c1 = c0 + m.ncs;
+  } else {
+    c0 = m.seq_off[s];
+    c1 = m.seq_off[s + 1];
+  }
+}
+
+}  // namespace ssd

@@ -1,0 +1,43 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace ssd {
+
+// Validated problem, as the kernels see it.
+struct Prob {
+  int32_t B, L, H, P, N, G;
+  int32_t nseq;      // number of state slots (batch rows, or packed sequences)
+  int32_t io;        // 0 fp32, 1 bf16
+  int32_t softplus;  // delta = softplus(dt + bias)
+  int32_t Q;         // chunk size
+  int32_t packed;
+  int64_t nck;       // chunk slots
+  ChunkMap map;      // device view of the chunk layout (table pointers set when packed)
+};
+
+// mode of the chunk-state contraction
+enum { kStateFwd = 0,      // T_c = sum_j delta_j 2^(acs_last - acs_j) x_j B_j^T
+       kStateDstates = 1   // U_c = sum_i 2^(acs_i) dy_i C_i^T
+};
+
+hipError_t launch_build_table(const Prob& p, const int32_t* cu_seqlens, int4* tab, int32_t* seq_off,
+                              hipStream_t st);
+hipError_t launch_chunk_cumsum(const Prob& p, const float* dt, const float* dt_bias, const float* A,
+                               float* delta, float* acs, float* decay, hipStream_t st);
+hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,
+                              const float* acs, float* out, int mode, hipStream_t st);
+hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
+                                const float* init, float* passed, float* final_states, int reverse,
+                                hipStream_t st);
+hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st);
+hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const void* CB,
+                             const float* delta, const float* acs, const float* passed,
+                             const float* D, void* out, hipStream_t st);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+
+}  // namespace ssd

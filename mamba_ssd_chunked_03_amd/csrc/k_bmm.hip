@@ -1,0 +1,110 @@
+// Stage 4 (ssd_bmm_chunk): CB_ij = C_i . B_j for every chunk and group, the
+// intra-chunk Gram matrix that the output stage weights by the decay mask.
+//
+// bf16 path: one workgroup per (chunk, group); the lower triangle of the QxQ
+// product is cut into 64x64 tiles (j-tile <= i-tile), handed to the four
+// wavefronts round-robin.  Both operands keep dstate (the contraction index)
+// contiguous in memory, so MFMA fragments are read straight from global memory
+// (16 bytes per lane) without LDS staging.  Tiles above the diagonal are never
+// computed; inside diagonal tiles the upper part is written but unspecified.
+//
+// fp32 path: one thread per (i, j <= i), plain dot product.
+#include "internal.hpp"
+
+namespace ssd {
+
+template <int N>
+__global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
+                                                             const uint16_t* __restrict__ Bm,
+                                                             const uint16_t* __restrict__ Cm,
+                                                             uint16_t* __restrict__ CB) {
+  const int k = blockIdx.x, g = blockIdx.y;
+  const ChunkInfo ci = chunk_info(m, k);
+  if (ci.len <= 0) return;
+  const int Q = m.Q;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4, r = lane & 15;
+  const int T = Q / 64;
+  const int ntiles = T * (T + 1) / 2;
+  const int64_t row = (int64_t)G * N;
+  const uint16_t* cb0 = Cm + (int64_t)ci.start * row + (int64_t)g * N;
+  const uint16_t* bb0 = Bm + (int64_t)ci.start * row + (int64_t)g * N;
+  uint16_t* out = CB + ((int64_t)k * G + g) * Q * Q;
+  for (int tile = w; tile < ntiles; tile += 4) {
+    int ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+    const int tj = tile - ti * (ti + 1) / 2;
+    if (ti * 64 >= ci.len) continue;  // rows past the chunk's end are never read
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < N; kk += 32) {
+      bf16x8 af[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int i = ti * 64 + a * 16 + r;
+        const int j = tj * 64 + a * 16 + r;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        af[a] = as_bf16x8(i < ci.len ? *(const u32x4*)(cb0 + (int64_t)i * row + kk + q * 8) : z);
+        bf[a] = as_bf16x8(j < ci.len ? *(const u32x4*)(bb0 + (int64_t)j * row + kk + q * 8) : z);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_bf16(af[a], bf[b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int i = ti * 64 + a * 16 + q * 4 + rr;
+          const int j = tj * 64 + b * 16 + r;
+          out[(int64_t)i * Q + j] = f2bf(acc[a][b][rr]);
+        }
+  }
+}
+
+__global__ __launch_bounds__(256) void bmm_chunk_f32_kernel(ChunkMap m, int G, int N,
+                                                            const float* __restrict__ Bm,
+                                                            const float* __restrict__ Cm,
+                                                            float* __restrict__ CB) {
+  const int k = blockIdx.x, g = blockIdx.y;
+  const ChunkInfo ci = chunk_info(m, k);
+  if (ci.len <= 0) return;
+  const int Q = m.Q;
+  const int o = blockIdx.z * 256 + threadIdx.x;
+  const int i = o / Q, j = o % Q;
+  if (i >= ci.len || j > i) return;
+  const float* ci_ = Cm + ((int64_t)(ci.start + i) * G + g) * N;
+  const float* bj_ = Bm + ((int64_t)(ci.start + j) * G + g) * N;
+  float acc = 0.f;
+  for (int n = 0; n < N; ++n) acc += ci_[n] * bj_[n];
+  CB[(((int64_t)k * G + g) * Q + i) * Q + j] = acc;
+}
+
+hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st) {
+  if (p.nck == 0) return hipSuccess;
+  if (p.io == 0) {
+    dim3 grid((unsigned)p.nck, p.G, (p.Q * p.Q + 255) / 256);
+    hipLaunchKernelGGL(bmm_chunk_f32_kernel, grid, dim3(256), 0, st, p.map, p.G, p.N,
+                       (const float*)B, (const float*)C, (float*)CB);
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)p.nck, p.G);
+#define SSD_BMM_CASE(NN)                                                                   \
+  if (p.N == NN) {                                                                         \
+    hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN>), grid, dim3(256), 0, st, p.map, p.G,    \
+                       (const uint16_t*)B, (const uint16_t*)C, (uint16_t*)CB);             \
+    return hipGetLastError();                                                              \
+  }
+  SSD_BMM_CASE(32) SSD_BMM_CASE(64) SSD_BMM_CASE(128)
+#undef SSD_BMM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssd

@@ -1,0 +1,237 @@
+"""ctypes binding over libssd.so (argument marshalling only).
+
+Every step of the scan runs in the library's HIP kernels; this module checks
+tensor placement and layout, allocates outputs and the workspace with torch
+(device memory only), passes raw device pointers and torch's current HIP
+stream, and turns a non-zero status into an exception.  There is no fallback:
+if the library is missing, or a tensor is not on a GPU, it raises.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libssd.so")
+
+F32, BF16 = 0, 1
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "nseq",
+                 "io_dtype", "dt_softplus")]
+
+
+_SIGS = {
+    "ssd_abi_version": ([], _I32),
+    "ssd_status_string": ([_I32], ctypes.c_char_p),
+    "ssd_num_chunks": ([_P, _I32, _I32], _I64),
+    "ssd_fwd_workspace_bytes": ([_P, _I32, _I32], _SZ),
+    "ssd_bwd_workspace_bytes": ([_P, _I32, _I32], _SZ),
+    "ssd_stage_workspace_bytes": ([_P, _I32, _I32], _SZ),
+    "ssd_fwd": ([_P] + [_P] * 9 + [_I32, _P, _P, _P, _SZ, _P], _I32),
+    "ssd_bwd": ([_P] + [_P] * 9 + [_I32] + [_P] * 12 + [_SZ, _P], _I32),
+    "ssd_stage_chunk_cumsum": ([_P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
+    "ssd_stage_chunk_state": ([_P, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], _I32),
+    "ssd_stage_state_passing": ([_P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
+    "ssd_stage_bmm_chunk": ([_P, _P, _P, _P, _I32, _P, _P, _SZ, _P], _I32),
+    "ssd_stage_chunk_scan": ([_P] + [_P] * 8 + [_I32, _P, _P, _SZ, _P], _I32),
+    "ssd_util_copy": ([_P, _P, _SZ, _P], _I32),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+def lib():
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libssd.so is not built; run __graft_entry__.build() "
+                               "(or python mamba_ssd_chunked_03_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__("libssd: %s (status %d)" % (lib().ssd_status_string(status).decode(), status))
+
+
+def _check(status):
+    if status != 0:
+        raise SSDError(status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libssd needs GPU tensors (got one on %s)" % t.device)
+        if not t.is_contiguous():
+            raise ValueError("libssd needs contiguous tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise ValueError("%s must be float32" % name)
+
+
+def problem(x, B, cu_seqlens=None, dt_softplus=True):
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    io = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if io is None:
+        raise ValueError("x must be float32 or bfloat16")
+    if B.dtype != x.dtype:
+        raise ValueError("B, C must have x's dtype")
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    return Problem(batch, seqlen, nheads, headdim, dstate, ngroups, nseq, io, int(bool(dt_softplus)))
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ws(nbytes, dev):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+def num_chunks(prob, chunk_size, packed):
+    return lib().ssd_num_chunks(ctypes.byref(prob), chunk_size, int(packed))
+
+
+def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
+        dt_softplus=True, workspace=None, out=None, final=None):
+    """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h."""
+    dev = _dev(x, dt, A, B, C, D, dt_bias, init, cu_seqlens, workspace, out, final)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (dt_bias, "dt_bias"), (init, "init")):
+        _f32(t, n)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    prob = problem(x, B, cu_seqlens, dt_softplus)
+    L = lib()
+    packed = int(cu_seqlens is not None)
+    need = L.ssd_fwd_workspace_bytes(ctypes.byref(prob), chunk_size, packed)
+    if workspace is None:
+        workspace = _ws(need, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    if final is None:
+        nst = prob.nseq if packed else prob.batch
+        final = torch.empty(nst, prob.nheads, prob.headdim, prob.dstate, dtype=torch.float32, device=dev)
+    _check(L.ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+                     _ptr(D), _ptr(init), _ptr(cu_seqlens), chunk_size, _ptr(out), _ptr(final),
+                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, final
+
+
+def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
+        chunk_size=256, dt_softplus=True, workspace=None):
+    """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors)."""
+    dev = _dev(x, dt, A, B, C, dout, D, dt_bias, init, d_final, cu_seqlens, workspace)
+    prob = problem(x, B, cu_seqlens, dt_softplus)
+    L = lib()
+    packed = int(cu_seqlens is not None)
+    need = L.ssd_bwd_workspace_bytes(ctypes.byref(prob), chunk_size, packed)
+    if workspace is None:
+        workspace = _ws(need, dev)
+    nst = prob.nseq if packed else prob.batch
+    g = {
+        "dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dA": torch.empty_like(A),
+        "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+        "dD": None if D is None else torch.empty_like(D),
+        "d_dt_bias": torch.empty(prob.nheads, dtype=torch.float32, device=dev),
+        "d_init": torch.empty(nst, prob.nheads, prob.headdim, prob.dstate, dtype=torch.float32, device=dev),
+    }
+    _check(L.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+                     _ptr(D), _ptr(init), _ptr(cu_seqlens), chunk_size, _ptr(dout), _ptr(d_final),
+                     _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                     _ptr(g["dD"]), _ptr(g["d_dt_bias"]), _ptr(g["d_init"]),
+                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return g
+
+
+# ------------------------------------------------------------ single stages ----
+class Stages:
+    """Run one forward stage at a time on explicit buffers (tests, timing)."""
+
+    def __init__(self, x, B, cu_seqlens=None, chunk_size=256, dt_softplus=True):
+        self.dev = _dev(x, B, cu_seqlens)
+        self.prob = problem(x, B, cu_seqlens, dt_softplus)
+        self.Q = chunk_size
+        self.cu = cu_seqlens
+        self.packed = int(cu_seqlens is not None)
+        self.nck = num_chunks(self.prob, chunk_size, self.packed)
+        self.ws = _ws(lib().ssd_stage_workspace_bytes(ctypes.byref(self.prob), chunk_size, self.packed), self.dev)
+        self.io_dtype = x.dtype
+
+    def _f(self, *shape):
+        return torch.zeros(*shape, dtype=torch.float32, device=self.dev)
+
+    def chunk_cumsum(self, dt, A, dt_bias=None):
+        p = self.prob
+        delta, acs = self._f(self.nck, p.nheads, self.Q), self._f(self.nck, p.nheads, self.Q)
+        decay = self._f(self.nck, p.nheads)
+        _check(lib().ssd_stage_chunk_cumsum(ctypes.byref(p), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                                            _ptr(self.cu), self.Q, _ptr(delta), _ptr(acs), _ptr(decay),
+                                            _ptr(self.ws), self.ws.numel(), _stream(self.dev)))
+        return delta, acs, decay
+
+    def chunk_state(self, x, B, delta, acs):
+        p = self.prob
+        T = self._f(self.nck, p.nheads, p.headdim, p.dstate)
+        _check(lib().ssd_stage_chunk_state(ctypes.byref(p), _ptr(x), _ptr(B), _ptr(delta), _ptr(acs),
+                                           _ptr(self.cu), self.Q, _ptr(T), _ptr(self.ws), self.ws.numel(),
+                                           _stream(self.dev)))
+        return T
+
+    def state_passing(self, T, decay, init=None):
+        p = self.prob
+        Hp = self._f(self.nck, p.nheads, p.headdim, p.dstate)
+        nst = p.nseq if self.packed else p.batch
+        final = self._f(nst, p.nheads, p.headdim, p.dstate)
+        _check(lib().ssd_stage_state_passing(ctypes.byref(p), _ptr(T), _ptr(decay), _ptr(init),
+                                             _ptr(self.cu), self.Q, _ptr(Hp), _ptr(final), _ptr(self.ws),
+                                             self.ws.numel(), _stream(self.dev)))
+        return Hp, final
+
+    def bmm_chunk(self, B, C):
+        p = self.prob
+        CB = torch.zeros(self.nck, p.ngroups, self.Q, self.Q, dtype=self.io_dtype, device=self.dev)
+        _check(lib().ssd_stage_bmm_chunk(ctypes.byref(p), _ptr(B), _ptr(C), _ptr(self.cu), self.Q,
+                                         _ptr(CB), _ptr(self.ws), self.ws.numel(), _stream(self.dev)))
+        return CB
+
+    def chunk_scan(self, x, C, CB, delta, acs, Hp, D=None):
+        p = self.prob
+        y = torch.empty_like(x)
+        _check(lib().ssd_stage_chunk_scan(ctypes.byref(p), _ptr(x), _ptr(C), _ptr(CB), _ptr(delta),
+                                          _ptr(acs), _ptr(Hp), _ptr(D), _ptr(self.cu), self.Q, _ptr(y),
+                                          _ptr(self.ws), self.ws.numel(), _stream(self.dev)))
+        return y
+
+
+def util_copy(dst, src):
+    dev = _dev(dst, src)
+    _check(lib().ssd_util_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(dev)))

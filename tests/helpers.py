@@ -1,0 +1,67 @@
+"""Shared test helpers: error measures and oracle/GPU plumbing."""
+import math
+
+import numpy as np
+import torch
+
+from mamba_ssd_chunked_03_amd import inputs
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def has_gpu():
+    return torch.cuda.is_available()
+
+
+def to_dev(inp, dev="cuda"):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def np64(t):
+    return None if t is None else t.detach().cpu().double().numpy()
+
+
+def normwise(got, ref):
+    """max |got - ref| / max |ref| (normwise relative error)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    if den == 0.0:
+        return float(np.max(np.abs(got))) if got.size else 0.0
+    return float(np.max(np.abs(got - ref)) / den)
+
+
+def half_ulp_bf16(ref):
+    """Half a bf16 ulp at each reference value (the output rounding alone)."""
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 1e-38)))
+    return 0.5 * np.exp2(e - 7)
+
+
+def bf16_excess(got, ref):
+    """max(|got - ref| - half_ulp_bf16(ref)): error beyond the output rounding."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref) - half_ulp_bf16(ref))) if ref.size else 0.0
+
+
+def oracle_args(inp):
+    a = inputs.to_f64(inp)
+    return dict(x=a["x"], dt=a["dt"], A=a["A"], B=a["B"], C=a["C"], D=a["D"],
+                dt_bias=a["dt_bias"], init=a["init"], dt_softplus=inp["dt_softplus"],
+                cu_seqlens=a["cu_seqlens"])
+
+
+def gpu_fwd(ssd, inp, chunk_size, **kw):
+    d = to_dev(inp)
+    return ssd.fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], dt_bias=d["dt_bias"],
+                   init=d["init"], cu_seqlens=d["cu_seqlens"], chunk_size=chunk_size,
+                   dt_softplus=inp["dt_softplus"], **kw)
+
+
+def gpu_bwd(ssd, inp, chunk_size, **kw):
+    d = to_dev(inp)
+    return ssd.bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["dout"], D=d["D"],
+                   dt_bias=d["dt_bias"], init=d["init"], d_final=d["d_final"],
+                   cu_seqlens=d["cu_seqlens"], chunk_size=chunk_size,
+                   dt_softplus=inp["dt_softplus"], **kw)
