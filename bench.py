@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD chunked scan on one MI355X.
+
+Workload: the Mamba-2 layer shape the pages measure on (batch 2, sequence
+length 8192, bf16), with seeded synthetic inputs: 64 heads of headdim 64,
+dstate 128, 8 groups, chunk 256 (dt raw N(0,1), bias U[-4,-2], softplus in the
+kernel, zero initial state, dout N(0,1)).  One step is one pass of the whole
+path: ssd_fwd and, when the library provides it, ssd_bwd.  Inputs and outputs
+are resident in HBM before timing starts; the K timed steps are bracketed by
+torch.cuda.synchronize() and HIP events recorded on the stream the library
+launches on (torch's current stream).
+
+Printed (last line, JSON): tokens/s of the step, ms per step, the per-stage
+times and algorithmic HBM rates (each stage timed on its own through its stage
+entry point, same kernels and launch shapes as inside ssd_fwd), the roofline
+of the dominant kernel, and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD layer tokens/s + ms/call (fwd, fwd+bwd) & % HBM peak, B=2 L=8192"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true", help="time ssd_fwd alone as the step")
+    return ap.parse_args()
+
+
+def stage_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, final=True):
+    """Algorithmic HBM bytes of each forward stage: inputs read once, outputs
+    written once (no cache re-reads, no skipped causal work)."""
+    tok = B * L
+    dt = tok * H * 4
+    dl_acs = 2 * nck * H * Q * 4
+    decay = nck * H * 4
+    states = nck * H * P * N * 4
+    x = tok * H * P * esz
+    bc = tok * G * N * esz
+    cb = nck * G * Q * Q * esz
+    st0 = nseq * H * P * N * 4
+    return {
+        "chunk_cumsum": dt + dl_acs + decay,
+        "chunk_state": x + bc + dl_acs + states,
+        "state_passing": 2 * states + decay + (st0 if init else 0) + (st0 if final else 0),
+        "bmm_chunk": 2 * bc + cb,
+        "chunk_scan": 2 * x + bc + cb + dl_acs + states,
+    }
+
+
+KERNEL_FILES = {
+    "chunk_cumsum": "k_cumsum.hip", "chunk_state": "k_chunk_state.hip",
+    "state_passing": "k_state_passing.hip", "bmm_chunk": "k_bmm.hip",
+    "chunk_scan": "k_chunk_scan.hip",
+}
+
+
+def source_hash(stage):
+    path = os.path.join(ROOT, "mamba_ssd_chunked_03_amd", "csrc", KERNEL_FILES[stage])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(stage):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current source of this kernel (else None)."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(stage)
+    if not e or e.get("source_sha") != source_hash(stage):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(with_bwd, budget_s=10.0):
+    """The oracle as it stands, on a bounded sample of the same workload: batch
+    row 0 with all 64 heads, in windows of 512 tokens (fresh seeded inputs per
+    window) until about ``budget_s`` seconds of CPU work; the oracle's cost is
+    linear in tokens at a fixed head count, so tokens/s carries over."""
+    from mamba_ssd_chunked_03_amd import inputs
+    from oracle import recurrence
+    T = 512
+    done, sec = 0, 0.0
+    while sec < budget_s and done < 8192:
+        inp = inputs.make_inputs(1, T, 64, 64, 128, 8, io="bf16", bwd=True, seed=100 + done)
+        a = inputs.to_f64(inp)
+        t0 = time.perf_counter()
+        recurrence.fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], D=a["D"], dt_bias=a["dt_bias"],
+                       init=a["init"], dt_softplus=True)
+        if with_bwd:
+            recurrence.bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["dout"], D=a["D"],
+                           dt_bias=a["dt_bias"], init=a["init"], dt_softplus=True)
+        sec += time.perf_counter() - t0
+        done += T
+    return {"value": round(done / sec, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "batch row 0, 64 heads, %d tokens in 512-token windows, %s, fp64 numpy "
+                      "token loop, %.1f s" % (done, "fwd+bwd" if with_bwd else "fwd", sec),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the SSD scan of one GPU's share); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mamba_ssd_chunked_03_amd import inputs, ssd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = inputs.CONFIGS[2]
+    Q = cfg["chunk"]
+    inp = inputs.config_inputs(2)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    x, dt, A, Bm, Cm, D, bias, init, dout = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                                             d["dt_bias"], d["init"], d["dout"])
+    Bsz, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    prob = ssd.problem(x, Bm)
+    import ctypes
+    lib = ssd.lib()
+    ws_f = torch.empty(lib.ssd_fwd_workspace_bytes(ctypes.byref(prob), Q, 0), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    final = torch.empty(Bsz, H, P, N, dtype=torch.float32, device=dev)
+
+    def fwd():
+        ssd.fwd(x, dt, A, Bm, Cm, D=D, dt_bias=bias, init=init, chunk_size=Q, workspace=ws_f,
+                out=y, final=final)
+
+    have_bwd = not args.fwd_only
+    if have_bwd:
+        ws_b = torch.empty(lib.ssd_bwd_workspace_bytes(ctypes.byref(prob), Q, 0), dtype=torch.uint8, device=dev)
+        try:
+            ssd.bwd(x, dt, A, Bm, Cm, dout, D=D, dt_bias=bias, init=init, chunk_size=Q, workspace=ws_b)
+        except ssd.SSDError as e:
+            if e.status != 3:
+                raise
+            have_bwd = False
+
+    def bwd():
+        ssd.bwd(x, dt, A, Bm, Cm, dout, D=D, dt_bias=bias, init=init, chunk_size=Q, workspace=ws_b)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(st)
+        for _ in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return e0.elapsed_time(e1) / steps, wall
+
+    def step():
+        fwd()
+        if have_bwd:
+            bwd()
+
+    print("bench: warmup %d, steps %d, bwd %s" % (args.warmup, args.steps, have_bwd), file=sys.stderr, flush=True)
+    ms_step, wall_step = timed(step, args.steps, args.warmup)
+    ms_fwd, _ = timed(fwd, args.steps, 2)
+    ms_bwd = None
+    if have_bwd:
+        ms_bwd, _ = timed(bwd, args.steps, 2)
+    tokens = Bsz * L
+    print("bench: step %.3f ms (wall %.3f), fwd %.3f ms" % (ms_step, wall_step, ms_fwd), file=sys.stderr, flush=True)
+
+    stages = {}
+    roof = None
+    if not args.no_stages:
+        sg = ssd.Stages(x, Bm, None, Q, True)
+        delta, acs, decay = sg.chunk_cumsum(dt, A, bias)
+        T = sg.chunk_state(x, Bm, delta, acs)
+        Hp, fin = sg.state_passing(T, decay, init)
+        CB = sg.bmm_chunk(Bm, Cm)
+        y2 = torch.empty_like(x)
+        fns = {
+            "chunk_cumsum": lambda: sg.chunk_cumsum(dt, A, bias, out=(delta, acs, decay)),
+            "chunk_state": lambda: sg.chunk_state(x, Bm, delta, acs, out=T),
+            "state_passing": lambda: sg.state_passing(T, decay, init, out=(Hp, fin)),
+            "bmm_chunk": lambda: sg.bmm_chunk(Bm, Cm, out=CB),
+            "chunk_scan": lambda: sg.chunk_scan(x, Cm, CB, delta, acs, Hp, D, out=y2),
+        }
+        # time the launches alone: output buffers allocated once, then only the
+        # C entry point is called inside the timed region
+        nbytes = stage_bytes(Bsz, L, H, P, N, G, Q, sg.nck, Bsz, 2)
+        for name, fn in fns.items():
+            ms, _ = timed(fn, args.steps, 2)
+            gbs = nbytes[name] / (ms * 1e-3) / 1e9
+            stages[name] = {"ms": round(ms, 4), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            print("bench: stage %-14s %.4f ms  %.0f GB/s" % (name, ms, gbs), file=sys.stderr, flush=True)
+        dom = max(stages, key=lambda k: stages[k]["ms"])
+        s = stages[dom]
+        roof = {"kernel": dom, "bound": "hbm", "achieved": s["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": s["frac_hbm"], "traffic": load_traffic(dom),
+                "alg_bytes_per_launch": s["alg_bytes"], "avg_launch_ms": s["ms"]}
+        fwd_bytes = sum(v["alg_bytes"] for v in stages.values())
+        fwd_stage_ms = sum(v["ms"] for v in stages.values())
+        stages["_forward_aggregate"] = {"ms": round(fwd_stage_ms, 4), "alg_bytes": fwd_bytes,
+                                        "GB/s": round(fwd_bytes / (fwd_stage_ms * 1e-3) / 1e9, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(have_bwd)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the pages' layer workload)",
+        "config": {"workload": "SSD layer %s, batch 2, seqlen 8192, 64 heads, headdim 64, "
+                               "dstate 128, 8 groups, chunk 256" % ("fwd+bwd" if have_bwd else "fwd"),
+                   "global_batch": Bsz, "seq_len": L, "parallelism": "single GPU"},
+        "fwd": {"ms": round(ms_fwd, 4), "tokens/s": round(tokens / (ms_fwd * 1e-3), 1)},
+        "fwd_bwd": None if not have_bwd else {"ms": round(ms_fwd + ms_bwd, 4), "bwd_ms": round(ms_bwd, 4),
+                                              "tokens/s": round(tokens / ((ms_fwd + ms_bwd) * 1e-3), 1)},
+        "stages": stages,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ _SIGS = {
     "ssd_bwd_workspace_bytes": ([_P, _I32, _I32], _SZ),
     "ssd_stage_workspace_bytes": ([_P, _I32, _I32], _SZ),
     "ssd_fwd": ([_P] + [_P] * 9 + [_I32, _P, _P, _P, _SZ, _P], _I32),
-    "ssd_bwd": ([_P] + [_P] * 9 + [_I32] + [_P] * 12 + [_SZ, _P], _I32),
+    "ssd_bwd": ([_P] + [_P] * 9 + [_I32] + [_P] * 11 + [_SZ, _P], _I32),
     "ssd_stage_chunk_cumsum": ([_P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
     "ssd_stage_chunk_state": ([_P, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], _I32),
     "ssd_stage_state_passing": ([_P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
@@ -187,48 +187,48 @@ class Stages:
         self.io_dtype = x.dtype
 
     def _f(self, *shape):
-        return torch.zeros(*shape, dtype=torch.float32, device=self.dev)
+        return torch.empty(*shape, dtype=torch.float32, device=self.dev)
 
-    def chunk_cumsum(self, dt, A, dt_bias=None):
+    def _call(self, name, *args):
+        _check(getattr(lib(), name)(ctypes.byref(self.prob), *args))
+
+    def chunk_cumsum(self, dt, A, dt_bias=None, out=None):
         p = self.prob
-        delta, acs = self._f(self.nck, p.nheads, self.Q), self._f(self.nck, p.nheads, self.Q)
-        decay = self._f(self.nck, p.nheads)
-        _check(lib().ssd_stage_chunk_cumsum(ctypes.byref(p), _ptr(dt), _ptr(dt_bias), _ptr(A),
-                                            _ptr(self.cu), self.Q, _ptr(delta), _ptr(acs), _ptr(decay),
-                                            _ptr(self.ws), self.ws.numel(), _stream(self.dev)))
+        delta, acs, decay = out or (self._f(self.nck, p.nheads, self.Q), self._f(self.nck, p.nheads, self.Q),
+                                    self._f(self.nck, p.nheads))
+        self._call("ssd_stage_chunk_cumsum", _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(self.cu), self.Q,
+                   _ptr(delta), _ptr(acs), _ptr(decay), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return delta, acs, decay
 
-    def chunk_state(self, x, B, delta, acs):
+    def chunk_state(self, x, B, delta, acs, out=None):
         p = self.prob
-        T = self._f(self.nck, p.nheads, p.headdim, p.dstate)
-        _check(lib().ssd_stage_chunk_state(ctypes.byref(p), _ptr(x), _ptr(B), _ptr(delta), _ptr(acs),
-                                           _ptr(self.cu), self.Q, _ptr(T), _ptr(self.ws), self.ws.numel(),
-                                           _stream(self.dev)))
+        T = out if out is not None else self._f(self.nck, p.nheads, p.headdim, p.dstate)
+        self._call("ssd_stage_chunk_state", _ptr(x), _ptr(B), _ptr(delta), _ptr(acs), _ptr(self.cu),
+                   self.Q, _ptr(T), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return T
 
-    def state_passing(self, T, decay, init=None):
+    def state_passing(self, T, decay, init=None, out=None):
         p = self.prob
-        Hp = self._f(self.nck, p.nheads, p.headdim, p.dstate)
         nst = p.nseq if self.packed else p.batch
-        final = self._f(nst, p.nheads, p.headdim, p.dstate)
-        _check(lib().ssd_stage_state_passing(ctypes.byref(p), _ptr(T), _ptr(decay), _ptr(init),
-                                             _ptr(self.cu), self.Q, _ptr(Hp), _ptr(final), _ptr(self.ws),
-                                             self.ws.numel(), _stream(self.dev)))
+        Hp, final = out or (self._f(self.nck, p.nheads, p.headdim, p.dstate),
+                            self._f(nst, p.nheads, p.headdim, p.dstate))
+        self._call("ssd_stage_state_passing", _ptr(T), _ptr(decay), _ptr(init), _ptr(self.cu), self.Q,
+                   _ptr(Hp), _ptr(final), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return Hp, final
 
-    def bmm_chunk(self, B, C):
+    def bmm_chunk(self, B, C, out=None):
         p = self.prob
-        CB = torch.zeros(self.nck, p.ngroups, self.Q, self.Q, dtype=self.io_dtype, device=self.dev)
-        _check(lib().ssd_stage_bmm_chunk(ctypes.byref(p), _ptr(B), _ptr(C), _ptr(self.cu), self.Q,
-                                         _ptr(CB), _ptr(self.ws), self.ws.numel(), _stream(self.dev)))
+        CB = out if out is not None else torch.empty(self.nck, p.ngroups, self.Q, self.Q,
+                                                     dtype=self.io_dtype, device=self.dev)
+        self._call("ssd_stage_bmm_chunk", _ptr(B), _ptr(C), _ptr(self.cu), self.Q, _ptr(CB),
+                   _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return CB
 
-    def chunk_scan(self, x, C, CB, delta, acs, Hp, D=None):
-        p = self.prob
-        y = torch.empty_like(x)
-        _check(lib().ssd_stage_chunk_scan(ctypes.byref(p), _ptr(x), _ptr(C), _ptr(CB), _ptr(delta),
-                                          _ptr(acs), _ptr(Hp), _ptr(D), _ptr(self.cu), self.Q, _ptr(y),
-                                          _ptr(self.ws), self.ws.numel(), _stream(self.dev)))
+    def chunk_scan(self, x, C, CB, delta, acs, Hp, D=None, out=None):
+        y = out if out is not None else torch.empty_like(x)
+        self._call("ssd_stage_chunk_scan", _ptr(x), _ptr(C), _ptr(CB), _ptr(delta), _ptr(acs), _ptr(Hp),
+                   _ptr(D), _ptr(self.cu), self.Q, _ptr(y), _ptr(self.ws), self.ws.numel(),
+                   _stream(self.dev))
         return y
 
 

@@ -64,6 +64,28 @@ def test_null_problem(L):
     assert fwd_status(L, None) == NULL
 
 
+def test_bwd_validation(L):
+    # ssd_bwd through the binding's argtypes (counts must match the header)
+    p = prob()
+    pp = ctypes.byref(p)
+    need = L.ssd_bwd_workspace_bytes(pp, 256, 0)
+    args = [FAKE] * 9
+    args[2] = None                      # dt_bias
+    args[6] = None                      # D
+    args[7] = None                      # init
+    args[8] = None                      # cu_seqlens
+    grads = [FAKE] * 10                 # dout, d_final, dx, ddt, dA, dB, dC, dD, d_dt_bias, d_init
+    grads[1] = None
+    grads[7] = None
+    assert L.ssd_bwd(None, *args, 256, *grads, FAKE, need, None) == NULL
+    assert L.ssd_bwd(pp, *args, 96, *grads, FAKE, need, None) == UNSUP
+    g2 = list(grads); g2[0] = None      # dout missing
+    assert L.ssd_bwd(pp, *args, 256, *g2, FAKE, need, None) == NULL
+    g3 = list(grads); g3[4] = FAKE + 4  # dA misaligned
+    assert L.ssd_bwd(pp, *args, 256, *g3, FAKE, need, None) == ALIGN
+    assert L.ssd_bwd(pp, *args, 256, *grads, FAKE, need - 1, None) == WS
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(ngroups=3), SHAPE), (dict(nheads=0), SHAPE), (dict(batch=-1), SHAPE),
     (dict(seqlen=-5), SHAPE), (dict(dt_softplus=2), SHAPE),
