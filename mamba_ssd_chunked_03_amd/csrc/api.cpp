@@ -88,15 +88,24 @@ FwdLayout fwd_layout(const Prob& p) {
 }
 struct BwdLayout {
   FwdLayout f;
-  size_t U, dE, end;
+  size_t CBt, U, dE, ddd, Ks, rR, last, dDp, dAp, dbp, end;
 };
 BwdLayout bwd_layout(const Prob& p) {
   BwdLayout l;
   l.f = fwd_layout(p);
   size_t o = l.f.end;
   const size_t nck = (size_t)p.nck, H = p.H, st = (size_t)p.P * p.N;
-  l.U = o;  o += up(nck * H * st * 4);
-  l.dE = o; o += up(nck * H * st * 4);
+  const size_t cb = p.io == SSD_BF16 ? nck * (size_t)p.G * p.Q * p.Q * 2 : 0;
+  l.CBt = o;  o += up(cb);
+  l.U = o;    o += up(nck * H * st * 4);
+  l.dE = o;   o += up(nck * H * st * 4);
+  l.ddd = o;  o += up(nck * H * p.Q * 4);
+  l.Ks = o;   o += up(nck * H * p.Q * 4);
+  l.rR = o;   o += up(nck * H * p.Q * 4);
+  l.last = o; o += up(nck * H * 4);
+  l.dDp = o;  o += up(nck * H * 4);
+  l.dAp = o;  o += up(nck * H * 4);
+  l.dbp = o;  o += up(nck * H * 4);
   l.end = o;
   return l;
 }
@@ -217,10 +226,50 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   Prob p;
   ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
   if (s != SSD_OK) return s;
-  (void)x; (void)dt; (void)dt_bias; (void)A; (void)B; (void)C; (void)D; (void)init_states;
-  (void)dout; (void)d_final_states; (void)dx; (void)ddt; (void)dA; (void)dB; (void)dC; (void)dD;
-  (void)d_dt_bias; (void)d_init_states; (void)workspace; (void)workspace_bytes; (void)stream;
-  return SSD_ERR_UNSUPPORTED;
+  const bool has_tokens = (int64_t)p.B * p.L > 0;
+  if (has_tokens && (!x || !dt || !A || !B || !C || !dout || !dx || !ddt || !dB || !dC))
+    return SSD_ERR_NULL;
+  if (!dA || (D && !dD)) return SSD_ERR_NULL;
+  if (!all_aligned({x, dt, dt_bias, A, B, C, D, init_states, cu_seqlens, dout, d_final_states, dx,
+                    ddt, dA, dB, dC, dD, d_dt_bias, d_init_states, workspace}))
+    return SSD_ERR_ALIGN;
+  const BwdLayout l = bwd_layout(p);
+  if (!workspace || workspace_bytes < l.end) return SSD_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  s = setup_map(p, cu_seqlens, ws, st);
+  if (s != SSD_OK) return s;
+  float* delta = (float*)(ws + l.f.delta);
+  float* acs = (float*)(ws + l.f.acs);
+  float* decay = (float*)(ws + l.f.decay);
+  float* T = (float*)(ws + l.f.T);
+  float* Hp = (float*)(ws + l.f.Hp);
+  void* CB = ws + l.f.CB;
+  void* CBt = ws + l.CBt;
+  float* U = (float*)(ws + l.U);
+  float* dE = (float*)(ws + l.dE);
+  // forward intermediates, recomputed
+  SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
+  SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
+  SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, nullptr, 0, st));
+  SSD_TRY(launch_bmm_chunk(p, B, C, CB, st));
+  if (p.io == SSD_BF16) SSD_TRY(launch_bmm_chunk_t(p, B, C, CBt, st));
+  // adjoint of the state carried into each chunk, then the reverse scan
+  SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
+  SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, d_init_states, 1, st));
+  BwdArgs a;
+  a.x = x; a.B = B; a.C = C; a.dout = dout;
+  a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.D = D;
+  a.delta = delta; a.acs = acs; a.decay = decay; a.Hp = Hp; a.dE = dE;
+  a.CB = CB; a.CBt = CBt;
+  a.dx = dx; a.dB = dB; a.dC = dC;
+  a.ddt = ddt; a.dA = dA; a.dD = dD; a.d_dt_bias = d_dt_bias;
+  a.ddd = (float*)(ws + l.ddd); a.Ks = (float*)(ws + l.Ks); a.rR = (float*)(ws + l.rR);
+  a.last_term = (float*)(ws + l.last); a.dDp = (float*)(ws + l.dDp);
+  a.dAp = (float*)(ws + l.dAp); a.dbp = (float*)(ws + l.dbp);
+  SSD_TRY(launch_bwd_chunk(p, a, st));
+  SSD_TRY(launch_bwd_finalize(p, a, st));
+  return SSD_OK;
 }
 
 ssd_status ssd_stage_chunk_cumsum(const ssd_problem* pr, const float* dt, const float* dt_bias,

@@ -67,6 +67,27 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// MFMA operand fragment from an LDS tile stored K-major (tile[k][col], row
+// stride `ld` bf16 elements) with the gfx950 transpose read ds_read_b64_tr_b16:
+// in each 16-lane group, output lane i, slot s comes from source lane 4s + i/4,
+// element i%4.  Pointing lane j of group q at row 8q + j/4, columns 4(j%4)..+3
+// makes two reads (rows +0 and +4) deliver tile[8q + 0..7][col0 + lane%16],
+// the 16x16x32 operand layout.  `tile` points at tile[k0][col0].
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ int tr_offset(int lane, int ld) {
+  return (8 * (lane >> 4) + ((lane & 15) >> 2)) * ld + 4 * (lane & 3);
+}
+__device__ __forceinline__ bf16x8 frag_kmajor(const uint16_t* tile, int ld, int lane) {
+  const uint16_t* p = tile + tr_offset(lane, ld);
+  v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * ld));
+  v8i16 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
 // ------------------------------------------------------------------ DPP ----
 // DPP controls (GFX9 encoding).
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
@@ -87,6 +108,24 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
   v += dpp_f<kRowShr8>(0.f, v);
   v += dpp_f<kRowBcast15, 0xa>(0.f, v);
   v += dpp_f<kRowBcast31, 0xc>(0.f, v);
+  return v;
+}
+
+// Sum over the 16 lanes of each DPP row (every lane of the row gets the sum):
+// rotations by 8, 4, 2, 1 inside the row.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0x128>(0.f, v);  // row_ror:8
+  v += dpp_f<0x124>(0.f, v);  // row_ror:4
+  v += dpp_f<0x122>(0.f, v);  // row_ror:2
+  v += dpp_f<0x121>(0.f, v);  // row_ror:1
+  return v;
+}
+
+// Sum over all 64 lanes (result valid in every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   return v;
 }
 

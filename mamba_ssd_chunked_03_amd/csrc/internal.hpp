@@ -40,4 +40,24 @@ hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const 
                              const float* D, void* out, hipStream_t st);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 
+// CBt[j][i] = B_j . C_i on the upper tile triangle (bf16 only; the backward's
+// row-j kernels read it with 16-byte loads).
+hipError_t launch_bmm_chunk_t(const Prob& p, const void* B, const void* C, void* CBt, hipStream_t st);
+
+// Everything the backward chunk kernels read and write.
+struct BwdArgs {
+  const void *x, *B, *C, *dout;
+  const float *dt, *dt_bias, *A, *D;
+  const float *delta, *acs, *decay, *Hp, *dE;
+  const void *CB, *CBt;
+  void *dx, *dB, *dC;
+  float *ddt, *dA, *dD, *d_dt_bias;
+  // per token (nck, H, Q): direct d(delta), K+s, r+R
+  float *ddd, *Ks, *rR;
+  // per (chunk, head): alpha<dE,H> + sum s, and partials of dD, dA, d_dt_bias
+  float *last_term, *dDp, *dAp, *dbp;
+};
+hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st);
+
 }  // namespace ssd

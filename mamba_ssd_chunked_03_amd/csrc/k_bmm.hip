@@ -7,16 +7,20 @@
 // contiguous in memory, so MFMA fragments are read straight from global memory
 // (16 bytes per lane) without LDS staging.  Tiles above the diagonal are never
 // computed; inside diagonal tiles the upper part is written but unspecified.
+// The backward also needs the transpose, CBt[j][i] = B_j . C_i for i >= j
+// (upper triangle): the same kernel with the operands swapped and the tile
+// walk mirrored.
 //
 // fp32 path: one thread per (i, j <= i), plain dot product.
 #include "internal.hpp"
 
 namespace ssd {
 
-template <int N>
+// out[a][b] = R_a . S_b on the lower (UPPER = false) or upper tile triangle.
+template <int N, bool UPPER>
 __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
-                                                             const uint16_t* __restrict__ Bm,
-                                                             const uint16_t* __restrict__ Cm,
+                                                             const uint16_t* __restrict__ Sm,
+                                                             const uint16_t* __restrict__ Rm,
                                                              uint16_t* __restrict__ CB) {
   const int k = blockIdx.x, g = blockIdx.y;
   const ChunkInfo ci = chunk_info(m, k);
@@ -27,14 +31,15 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
   const int T = Q / 64;
   const int ntiles = T * (T + 1) / 2;
   const int64_t row = (int64_t)G * N;
-  const uint16_t* cb0 = Cm + (int64_t)ci.start * row + (int64_t)g * N;
-  const uint16_t* bb0 = Bm + (int64_t)ci.start * row + (int64_t)g * N;
+  const uint16_t* cb0 = Rm + (int64_t)ci.start * row + (int64_t)g * N;
+  const uint16_t* bb0 = Sm + (int64_t)ci.start * row + (int64_t)g * N;
   uint16_t* out = CB + ((int64_t)k * G + g) * Q * Q;
   for (int tile = w; tile < ntiles; tile += 4) {
-    int ti = 0;
-    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
-    const int tj = tile - ti * (ti + 1) / 2;
-    if (ti * 64 >= ci.len) continue;  // rows past the chunk's end are never read
+    int lo = 0;
+    while ((lo + 1) * (lo + 2) / 2 <= tile) ++lo;
+    const int hi = tile - lo * (lo + 1) / 2;  // hi <= lo
+    const int ti = UPPER ? hi : lo, tj = UPPER ? lo : hi;
+    if (lo * 64 >= ci.len) continue;  // rows / columns past the chunk's end are never read
     f32x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -87,6 +92,21 @@ __global__ __launch_bounds__(256) void bmm_chunk_f32_kernel(ChunkMap m, int G, i
   CB[(((int64_t)k * G + g) * Q + i) * Q + j] = acc;
 }
 
+hipError_t launch_bmm_chunk_t(const Prob& p, const void* B, const void* C, void* CBt, hipStream_t st) {
+  if (p.nck == 0) return hipSuccess;
+  if (p.io == 0) return hipErrorInvalidValue;  // the fp32 backward reads CB directly
+  dim3 grid((unsigned)p.nck, p.G);
+#define SSD_BMMT_CASE(NN)                                                                      \
+  if (p.N == NN) {                                                                             \
+    hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN, true>), grid, dim3(256), 0, st, p.map, p.G,  \
+                       (const uint16_t*)C, (const uint16_t*)B, (uint16_t*)CBt);                \
+    return hipGetLastError();                                                                  \
+  }
+  SSD_BMMT_CASE(32) SSD_BMMT_CASE(64) SSD_BMMT_CASE(128)
+#undef SSD_BMMT_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
   if (p.io == 0) {
@@ -98,8 +118,8 @@ hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* C
   dim3 grid((unsigned)p.nck, p.G);
 #define SSD_BMM_CASE(NN)                                                                   \
   if (p.N == NN) {                                                                         \
-    hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN>), grid, dim3(256), 0, st, p.map, p.G,    \
-                       (const uint16_t*)B, (const uint16_t*)C, (uint16_t*)CB);             \
+    hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN, false>), grid, dim3(256), 0, st, p.map,  \
+                       p.G, (const uint16_t*)B, (const uint16_t*)C, (uint16_t*)CB);        \
     return hipGetLastError();                                                              \
   }
   SSD_BMM_CASE(32) SSD_BMM_CASE(64) SSD_BMM_CASE(128)

@@ -1,0 +1,766 @@
+// Backward of the chunked scan (the adjoint of the forward stages).
+//
+// Per chunk c, head h (group g), tokens i, j of the chunk, with
+//   L_ij = 2^(acs_i - acs_j) (i >= j), w_j = 2^(acs_last - acs_j),
+//   CB_ij = C_i . B_j, dT = dE_c (from the reverse state-passing scan), H = H_c:
+//   dx_j  = delta_j [ sum_{i>=j} CB_ij L_ij dy_i + w_j dT B_j ] + D dy_j
+//   dC_i  = sum_h [ 2^acs_i H^T dy_i + sum_{j<=i} dCB_ij B_j ]
+//   dB_j  = sum_h [ sum_{i>=j} dCB_ij C_i + w_j delta_j dT^T x_j ]
+//   with dCB_ij = (dy_i . x_j) L_ij delta_j.
+// Decay gradients: the gradient w.r.t. the within-chunk cumsum at token i is
+//   dAcs_i = r_i + R_i - K_i - s_i  (+ at the last token: sum_j s_j + alpha <dE, H>)
+// where r_i = 2^acs_i dy_i . (H C_i), R_i = sum_{j<i} M_ij, K_j = sum_{i>j} M_ij,
+// s_j = w_j delta_j x_j . (dT B_j), M_ij = (dy_i . x_j) CB_ij L_ij delta_j, and the
+// gradient w.r.t. each token's delta*A is the suffix sum ddA_t = sum_{i>=t} dAcs_i.
+// Two identities keep this cheap: sum_{i>=j} (dy_i . x_j) CB_ij L_ij = x_j . U_j
+// where U_j is dx_j's intra-chunk bracket, so the per-token "direct" delta
+// gradient and K_j come out of the dx accumulator; R_i comes out of the dC
+// kernel's dCB tile.
+//
+// Kernels (bf16 on MFMA; fp32 plain loops):
+//   bwd_dx   (chunk, head)        dx, direct d(delta), K+s per token, dD and
+//                                 alpha<dE,H> + sum s per chunk
+//   bwd_dc   (chunk, group, 64 rows)  dC summed over the group's heads, r+R per token
+//   bwd_db   (chunk, group, 64 rows)  dB summed over the group's heads
+//   finalize (chunk, head)        suffix sum of dAcs (DPP scan), d(delta)->ddt,
+//                                 per-chunk partials of dA and d_dt_bias
+//   reduce   (head)               fixed-order sums over chunks: dA, dD, d_dt_bias
+// Every reduction has a fixed order, so results are bitwise reproducible.
+#include "internal.hpp"
+
+namespace ssd {
+
+constexpr int QMAX = 256;
+
+// ------------------------------------------------------------ bwd_dx bf16 ----
+template <int P, int N>
+__global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
+    ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Bm,
+    const uint16_t* __restrict__ DY, const uint16_t* __restrict__ CBt,
+    const float* __restrict__ delta, const float* __restrict__ acs,
+    const float* __restrict__ decay, const float* __restrict__ dE, const float* __restrict__ Hs,
+    const float* __restrict__ D, uint16_t* __restrict__ DX, float* __restrict__ ddd,
+    float* __restrict__ Ks, float* __restrict__ last_term, float* __restrict__ dDp) {
+  constexpr int LDY = P + 16;  // dy tile row stride (bf16): odd multiple of 32 bytes
+  constexpr int LDT = N + 8;   // dT tile row stride
+  __shared__ __attribute__((aligned(16))) uint16_t dyt[QMAX * LDY];
+  __shared__ __attribute__((aligned(16))) uint16_t dts[P * LDT];
+  __shared__ float sa[QMAX], sd[QMAX];
+  __shared__ float red[3][4];
+
+  const int k = blockIdx.x, h = blockIdx.y;
+  const ChunkInfo ci = chunk_info(m, k);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t kh = (int64_t)k * H + h;
+  if (ci.len <= 0) {
+    if (tid == 0) {
+      last_term[kh] = 0.f;
+      dDp[kh] = 0.f;
+    }
+    return;
+  }
+  const int Q = m.Q, len = ci.len;
+  const int g = h / (H / G);
+  const int q = lane >> 4, r = lane & 15;
+  const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
+  const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
+  const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
+  const uint16_t* bb = Bm + (int64_t)ci.start * brow + (int64_t)g * N;
+  const uint16_t* cbt = CBt + ((int64_t)k * G + g) * Q * Q;
+
+  for (int t = tid; t < Q; t += 256) {
+    sa[t] = acs[kh * Q + t];
+    sd[t] = delta[kh * Q + t];
+  }
+  // dy tile, token-major (rows past the chunk's end are zero)
+  for (int e = tid; e < Q * (P / 8); e += 256) {
+    const int i = e / (P / 8), c8 = e % (P / 8);
+    const u32x4 v = (i < len) ? *(const u32x4*)(dyb + (int64_t)i * xrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(dyt + i * LDY + c8 * 8) = v;
+  }
+  // dT = dE_c as bf16 [p][n]; alpha <dE, H> in fp32 on the way
+  float dot = 0.f;
+  {
+    const float* de = dE + kh * (int64_t)(P * N);
+    const float* hh = Hs + kh * (int64_t)(P * N);
+    for (int e = tid * 4; e < P * N; e += 1024) {
+      const float4 a = *(const float4*)(de + e);
+      const float4 b = *(const float4*)(hh + e);
+      dot += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+      const int p = e / N, n = e % N;
+      uint32_t* dst = (uint32_t*)(dts + p * LDT + n);
+      dst[0] = pack_bf2(a.x, a.y);
+      dst[1] = pack_bf2(a.z, a.w);
+    }
+  }
+  dot = wave_sum(dot);
+  __syncthreads();
+
+  const float Dh = D ? D[h] : 0.f;
+  const float a_last = sa[len - 1];
+  float s_sum = 0.f, dxx_sum = 0.f;  // lane r == 0 of each row group accumulates its rows
+  const int NB = Q / 16;
+  for (int ii = 0; ii < NB / 4; ++ii) {
+    const int rb = 4 * ii + ((ii & 1) ? (3 - w) : w);
+    const int j0 = rb * 16;
+    if (j0 >= len) continue;
+    f32x4 acc[P / 16];
+#pragma unroll
+    for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int jrow = j0 + r;  // A-fragment row of this lane
+    // state part: sum_n B_j[n] dT[p][n]
+#pragma unroll
+    for (int kk = 0; kk < N; kk += 32) {
+      const bf16x8 a = as_bf16x8(jrow < len ? *(const u32x4*)(bb + (int64_t)jrow * brow + kk + q * 8)
+                                            : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int tp = 0; tp < P / 16; ++tp)
+        acc[tp] = mfma_bf16(a, as_bf16x8(*(const u32x4*)(dts + (tp * 16 + r) * LDT + kk + q * 8)), acc[tp]);
+    }
+    float xv[P / 16][4];
+    float xs[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int j = j0 + q * 4 + rr;
+      const float wj = (j < len) ? exp2_fast(a_last - sa[j]) : 0.f;
+      xs[rr] = 0.f;
+#pragma unroll
+      for (int tp = 0; tp < P / 16; ++tp) {
+        acc[tp][rr] *= wj;
+        xv[tp][rr] = (j < len) ? bf2f(xb[(int64_t)j * xrow + tp * 16 + r]) : 0.f;
+        xs[rr] += xv[tp][rr] * acc[tp][rr];
+      }
+    }
+    // intra part: sum_{i>=j} CBt[j][i] 2^(acs_i - acs_j) dy_i
+    const float aj = sa[min(jrow, Q - 1)];
+    for (int kk = (j0 / 32) * 32; kk < len; kk += 32) {
+      u32x4 cv = u32x4{0u, 0u, 0u, 0u};
+      if (jrow < len) cv = *(const u32x4*)(cbt + (int64_t)jrow * Q + kk + q * 8);
+      // hi + lo bf16 split: K_j built from these values must cancel against R_i
+      // (built from the same bf16 CB in the dC kernel) inside the decay gradient
+      u32x4 ah, al;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int i0 = kk + q * 8 + 2 * d;
+        float v0 = bf_lo(cv[d]) * exp2_fast(sa[i0] - aj);
+        float v1 = bf_hi(cv[d]) * exp2_fast(sa[i0 + 1] - aj);
+        v0 = (i0 >= jrow && i0 < len) ? v0 : 0.f;
+        v1 = (i0 + 1 >= jrow && i0 + 1 < len) ? v1 : 0.f;
+        ah[d] = pack_bf2(v0, v1);
+        al[d] = pack_bf2(v0 - bf_lo(ah[d]), v1 - bf_hi(ah[d]));
+      }
+#pragma unroll
+      for (int tp = 0; tp < P / 16; ++tp) {
+        const bf16x8 b = frag_kmajor(dyt + kk * LDY + tp * 16, LDY, lane);
+        acc[tp] = mfma_bf16(as_bf16x8(ah), b, acc[tp]);
+        acc[tp] = mfma_bf16(as_bf16x8(al), b, acc[tp]);
+      }
+    }
+    // per-row dots and the store
+    float xt[4], dxx[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int j = j0 + q * 4 + rr;
+      const float dj = (j < len) ? sd[j] : 0.f;
+      xt[rr] = 0.f;
+      dxx[rr] = 0.f;
+#pragma unroll
+      for (int tp = 0; tp < P / 16; ++tp) {
+        const int p = tp * 16 + r;
+        const float dy = bf2f(dyt[min(j, Q - 1) * LDY + p]);
+        xt[rr] += xv[tp][rr] * acc[tp][rr];
+        dxx[rr] += xv[tp][rr] * dy;
+        if (j < len) DX[(int64_t)(ci.start + j) * xrow + (int64_t)h * P + p] = f2bf(dj * acc[tp][rr] + Dh * dy);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      xs[rr] = row_sum16(xs[rr]);
+      xt[rr] = row_sum16(xt[rr]);
+      dxx[rr] = row_sum16(dxx[rr]);
+      const int j = j0 + q * 4 + rr;
+      if (r == 0 && j < len) {
+        const float dj = sd[j];
+        const float cbjj = bf2f(cbt[(int64_t)j * Q + j]);
+        ddd[kh * Q + j] = xt[rr];
+        Ks[kh * Q + j] = dj * (xt[rr] - dxx[rr] * cbjj);
+        s_sum += dj * xs[rr];
+        dxx_sum += dxx[rr];
+      }
+    }
+  }
+  // fixed-order workgroup reductions: lanes (w, q) -> wave -> waves 0..3
+  s_sum = wave_sum(s_sum);
+  dxx_sum = wave_sum(dxx_sum);
+  if (lane == 0) {
+    red[0][w] = s_sum;
+    red[1][w] = dxx_sum;
+    red[2][w] = dot;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float S = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const float DD = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    const float HD = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    last_term[kh] = S + exp2_fast(decay[kh]) * HD;
+    dDp[kh] = DD;
+  }
+}
+
+// ------------------------------------------------------------ bwd_dc bf16 ----
+template <int P, int N>
+__global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
+    ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Bm,
+    const uint16_t* __restrict__ Cm, const uint16_t* __restrict__ DY,
+    const uint16_t* __restrict__ CB, const float* __restrict__ delta,
+    const float* __restrict__ acs, const float* __restrict__ Hs, uint16_t* __restrict__ dC,
+    float* __restrict__ rR) {
+  constexpr int LDB = N + 16;  // odd multiple of 32 bytes for the transpose reads
+  constexpr int LDS_ = 40;     // dCB staging row stride
+  __shared__ __attribute__((aligned(16))) uint16_t bt[QMAX * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t ht[P * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t stg[4][16 * LDS_];
+  __shared__ float sa[QMAX], sd[QMAX];
+
+  const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const ChunkInfo ci = chunk_info(m, k);
+  if (ci.len <= 0 || tile * 64 >= ci.len) return;
+  const int Q = m.Q, len = ci.len;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4, r = lane & 15;
+  const int hpg = H / G;
+  const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
+  const uint16_t* bb = Bm + (int64_t)ci.start * brow + (int64_t)g * N;
+  const uint16_t* cb = Cm + (int64_t)ci.start * brow + (int64_t)g * N;
+  const uint16_t* cbm = CB + ((int64_t)k * G + g) * Q * Q;
+  const int i0 = tile * 64 + w * 16;
+  const bool active = i0 < len;
+  const int jend = ((min(len, tile * 64 + 64) + 31) / 32) * 32;  // B rows needed, padded
+
+  for (int e = tid; e < jend * (N / 8); e += 256) {
+    const int j = e / (N / 8), c8 = e % (N / 8);
+    const u32x4 v = (j < len) ? *(const u32x4*)(bb + (int64_t)j * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(bt + j * LDB + c8 * 8) = v;
+  }
+  f32x4 acc[N / 16];
+#pragma unroll
+  for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int irow = i0 + r;  // A-fragment row
+  float cv[N / 16][4];      // C_i[n] in the accumulator layout (for r_i)
+#pragma unroll
+  for (int nb = 0; nb < N / 16; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int i = i0 + q * 4 + rr;
+      cv[nb][rr] = (i < len) ? bf2f(cb[(int64_t)i * brow + nb * 16 + r]) : 0.f;
+    }
+
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h;
+    __syncthreads();
+    for (int t = tid; t < Q; t += 256) {
+      sa[t] = acs[kh * Q + t];
+      sd[t] = delta[kh * Q + t];
+    }
+    {
+      const float* hb = Hs + kh * (int64_t)(P * N);
+      for (int e = tid * 4; e < P * N; e += 1024) {
+        const float4 v = *(const float4*)(hb + e);
+        const int p = e / N, n = e % N;
+        uint32_t* dst = (uint32_t*)(ht + p * LDB + n);
+        dst[0] = pack_bf2(v.x, v.y);
+        dst[1] = pack_bf2(v.z, v.w);
+      }
+    }
+    __syncthreads();
+    if (!active) continue;
+    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
+    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
+    // dy fragments of rows i (unscaled, and scaled by 2^acs_i for the state part)
+    u32x4 ay[P / 32];
+    bf16x8 ays[P / 32];
+    const float ei = (irow < len) ? exp2_fast(sa[irow]) : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb) {
+      ay[kb] = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+      u32x4 s;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) s[d] = pack_bf2(bf_lo(ay[kb][d]) * ei, bf_hi(ay[kb][d]) * ei);
+      ays[kb] = as_bf16x8(s);
+    }
+    // state part of this head: tmp[i][n] = 2^acs_i sum_p dy_i[p] H[p][n]
+    f32x4 tmp[N / 16];
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) tmp[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb)
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        tmp[nb] = mfma_bf16(ays[kb], frag_kmajor(ht + kb * 32 * LDB + nb * 16, LDB, lane), tmp[nb]);
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        rsum[rr] += cv[nb][rr] * tmp[nb][rr];
+        acc[nb][rr] += tmp[nb][rr];
+      }
+    // intra part: dCB_ij = (dy_i . x_j) 2^(acs_i - acs_j) delta_j, j <= i
+    float Rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < min(i0 + 16, len); jb += 32) {
+      f32x4 dxb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        dxb[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int jcol = jb + c * 16 + r;  // B-operand column of this lane
+#pragma unroll
+        for (int kb = 0; kb < P / 32; ++kb) {
+          const u32x4 xvv = (jcol < len) ? *(const u32x4*)(xb + (int64_t)jcol * xrow + kb * 32 + q * 8)
+                                         : u32x4{0u, 0u, 0u, 0u};
+          dxb[c] = mfma_bf16(as_bf16x8(ay[kb]), as_bf16x8(xvv), dxb[c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int i = i0 + q * 4 + rr, j = jb + c * 16 + r;
+          float v = dxb[c][rr] * exp2_fast(sa[min(i, Q - 1)] - sa[j]) * sd[j];
+          v = (j <= i && i < len) ? v : 0.f;
+          if (j < i) Rsum[rr] += v * bf2f(cbm[(int64_t)min(i, Q - 1) * Q + j]);
+          stg[w][(q * 4 + rr) * LDS_ + c * 16 + r] = f2bf(v);
+        }
+      __builtin_amdgcn_wave_barrier();
+      const bf16x8 a = as_bf16x8(*(const u32x4*)(&stg[w][r * LDS_ + q * 8]));
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        acc[nb] = mfma_bf16(a, frag_kmajor(bt + jb * LDB + nb * 16, LDB, lane), acc[nb]);
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = row_sum16(rsum[rr] + Rsum[rr]);
+      const int i = i0 + q * 4 + rr;
+      if (r == 0 && i < len) rR[kh * Q + i] = v;
+    }
+  }
+  if (!active) return;
+#pragma unroll
+  for (int nb = 0; nb < N / 16; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int i = i0 + q * 4 + rr;
+      if (i < len) dC[(int64_t)(ci.start + i) * brow + (int64_t)g * N + nb * 16 + r] = f2bf(acc[nb][rr]);
+    }
+}
+
+// ------------------------------------------------------------ bwd_db bf16 ----
+template <int P, int N>
+__global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
+    ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ DY, const float* __restrict__ delta,
+    const float* __restrict__ acs, const float* __restrict__ dE, uint16_t* __restrict__ dB) {
+  constexpr int LDB = N + 16;
+  constexpr int LDS_ = 40;
+  __shared__ __attribute__((aligned(16))) uint16_t ct[QMAX * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t dtt[P * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t stg[4][16 * LDS_];
+  __shared__ float sa[QMAX], sd[QMAX];
+
+  const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const ChunkInfo ci = chunk_info(m, k);
+  if (ci.len <= 0 || tile * 64 >= ci.len) return;
+  const int Q = m.Q, len = ci.len;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4, r = lane & 15;
+  const int hpg = H / G;
+  const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
+  const uint16_t* cb = Cm + (int64_t)ci.start * brow + (int64_t)g * N;
+  const int j0 = tile * 64 + w * 16;
+  const bool active = j0 < len;
+  const int ibeg = tile * 64, iend = ((len + 31) / 32) * 32;
+
+  for (int e = tid; e < (iend - ibeg) * (N / 8); e += 256) {
+    const int i = ibeg + e / (N / 8), c8 = e % (N / 8);
+    const u32x4 v = (i < len) ? *(const u32x4*)(cb + (int64_t)i * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(ct + i * LDB + c8 * 8) = v;
+  }
+  f32x4 acc[N / 16];
+#pragma unroll
+  for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int jrow = j0 + r;
+
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h;
+    __syncthreads();
+    for (int t = tid; t < Q; t += 256) {
+      sa[t] = acs[kh * Q + t];
+      sd[t] = delta[kh * Q + t];
+    }
+    {
+      const float* de = dE + kh * (int64_t)(P * N);
+      for (int e = tid * 4; e < P * N; e += 1024) {
+        const float4 v = *(const float4*)(de + e);
+        const int p = e / N, n = e % N;
+        uint32_t* dst = (uint32_t*)(dtt + p * LDB + n);
+        dst[0] = pack_bf2(v.x, v.y);
+        dst[1] = pack_bf2(v.z, v.w);
+      }
+    }
+    __syncthreads();
+    if (!active) continue;
+    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
+    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
+    u32x4 ax[P / 32];
+    bf16x8 axs[P / 32];
+    const float sj = (jrow < len) ? exp2_fast(sa[len - 1] - sa[jrow]) * sd[jrow] : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb) {
+      ax[kb] = (jrow < len) ? *(const u32x4*)(xb + (int64_t)jrow * xrow + kb * 32 + q * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+      u32x4 s;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) s[d] = pack_bf2(bf_lo(ax[kb][d]) * sj, bf_hi(ax[kb][d]) * sj);
+      axs[kb] = as_bf16x8(s);
+    }
+    // state part: w_j delta_j sum_p x_j[p] dT[p][n]
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb)
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        acc[nb] = mfma_bf16(axs[kb], frag_kmajor(dtt + kb * 32 * LDB + nb * 16, LDB, lane), acc[nb]);
+    // intra part: dCBt[j][i] = (x_j . dy_i) 2^(acs_i - acs_j) delta_j, i >= j
+    for (int ib = (j0 / 32) * 32; ib < len; ib += 32) {
+      f32x4 dxb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        dxb[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int icol = ib + c * 16 + r;
+#pragma unroll
+        for (int kb = 0; kb < P / 32; ++kb) {
+          const u32x4 dv = (icol < len) ? *(const u32x4*)(dyb + (int64_t)icol * xrow + kb * 32 + q * 8)
+                                        : u32x4{0u, 0u, 0u, 0u};
+          dxb[c] = mfma_bf16(as_bf16x8(ax[kb]), as_bf16x8(dv), dxb[c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int j = j0 + q * 4 + rr, i = ib + c * 16 + r;
+          float v = dxb[c][rr] * exp2_fast(sa[i] - sa[min(j, Q - 1)]) * sd[min(j, Q - 1)];
+          v = (i >= j && i < len && j < len) ? v : 0.f;
+          stg[w][(q * 4 + rr) * LDS_ + c * 16 + r] = f2bf(v);
+        }
+      __builtin_amdgcn_wave_barrier();
+      const bf16x8 a = as_bf16x8(*(const u32x4*)(&stg[w][r * LDS_ + q * 8]));
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        acc[nb] = mfma_bf16(a, frag_kmajor(ct + ib * LDB + nb * 16, LDB, lane), acc[nb]);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  if (!active) return;
+#pragma unroll
+  for (int nb = 0; nb < N / 16; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int j = j0 + q * 4 + rr;
+      if (j < len) dB[(int64_t)(ci.start + j) * brow + (int64_t)g * N + nb * 16 + r] = f2bf(acc[nb][rr]);
+    }
+}
+
+// ------------------------------------------------------------ fp32 paths ----
+// One thread per row j: dx, direct d(delta), K+s; workgroup sums in fixed order.
+__global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
+    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
+    const float* __restrict__ Bm, const float* __restrict__ DY, const float* __restrict__ CB,
+    const float* __restrict__ delta, const float* __restrict__ acs,
+    const float* __restrict__ decay, const float* __restrict__ dE, const float* __restrict__ Hs,
+    const float* __restrict__ D, float* __restrict__ DX, float* __restrict__ ddd,
+    float* __restrict__ Ks, float* __restrict__ last_term, float* __restrict__ dDp) {
+  __shared__ float red[3][256];
+  const int k = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const ChunkInfo ci = chunk_info(m, k);
+  const int64_t kh = (int64_t)k * H + h;
+  if (ci.len <= 0) {
+    if (tid == 0) {
+      last_term[kh] = 0.f;
+      dDp[kh] = 0.f;
+    }
+    return;
+  }
+  const int Q = m.Q, len = ci.len, g = h / (H / G);
+  const float* ac = acs + kh * Q;
+  const float* dl = delta + kh * Q;
+  const float* dT = dE + kh * (int64_t)P * N;
+  const float* cbm = CB + ((int64_t)k * G + g) * Q * Q;
+  const float Dh = D ? D[h] : 0.f;
+  float s_part = 0.f, dxx_part = 0.f, dot = 0.f;
+  for (int e = tid; e < P * N; e += 256) dot += dT[e] * Hs[kh * (int64_t)P * N + e];
+  for (int j = tid; j < len; j += 256) {
+    const int64_t tj = ci.start + j;
+    const float wj = exp2_fast(ac[len - 1] - ac[j]);
+    float xs = 0.f, xt = 0.f, dxx = 0.f;
+    for (int p = 0; p < P; ++p) {
+      float st = 0.f;
+      for (int n = 0; n < N; ++n) st += Bm[(tj * G + g) * N + n] * dT[p * N + n];
+      st *= wj;
+      float in = 0.f;
+      for (int i = j; i < len; ++i)
+        in += cbm[(int64_t)i * Q + j] * exp2_fast(ac[i] - ac[j]) * DY[((ci.start + i) * (int64_t)H + h) * P + p];
+      const float xjp = X[(tj * H + h) * P + p], dyjp = DY[(tj * H + h) * P + p];
+      xs += xjp * st;
+      xt += xjp * (st + in);
+      dxx += xjp * dyjp;
+      DX[(tj * H + h) * P + p] = dl[j] * (st + in) + Dh * dyjp;
+    }
+    const float cbjj = cbm[(int64_t)j * Q + j];
+    ddd[kh * Q + j] = xt;
+    Ks[kh * Q + j] = dl[j] * (xt - dxx * cbjj);
+    s_part += dl[j] * xs;
+    dxx_part += dxx;
+  }
+  red[0][tid] = s_part;
+  red[1][tid] = dxx_part;
+  red[2][tid] = dot;
+  __syncthreads();
+  if (tid == 0) {
+    float S = 0.f, DD = 0.f, HD = 0.f;
+    for (int t = 0; t < 256; ++t) {
+      S += red[0][t];
+      DD += red[1][t];
+      HD += red[2][t];
+    }
+    last_term[kh] = S + exp2_fast(decay[kh]) * HD;
+    dDp[kh] = DD;
+  }
+}
+
+// One thread per (i, n) of a group: dC summed over the group's heads.
+__global__ __launch_bounds__(256) void bwd_dc_f32_kernel(
+    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
+    const float* __restrict__ Bm, const float* __restrict__ DY, const float* __restrict__ delta,
+    const float* __restrict__ acs, const float* __restrict__ Hs, float* __restrict__ dC) {
+  const int k = blockIdx.x, g = blockIdx.y;
+  const ChunkInfo ci = chunk_info(m, k);
+  if (ci.len <= 0) return;
+  const int o = blockIdx.z * 256 + threadIdx.x;
+  const int i = o / N, n = o % N;
+  if (i >= ci.len) return;
+  const int Q = m.Q, hpg = H / G;
+  const int64_t ti = ci.start + i;
+  float acc = 0.f;
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h;
+    const float* ac = acs + kh * Q;
+    const float* dl = delta + kh * Q;
+    float st = 0.f;
+    for (int p = 0; p < P; ++p) st += DY[(ti * H + h) * P + p] * Hs[kh * (int64_t)P * N + (int64_t)p * N + n];
+    acc += exp2_fast(ac[i]) * st;
+    for (int j = 0; j <= i; ++j) {
+      const int64_t tj = ci.start + j;
+      float dxij = 0.f;
+      for (int p = 0; p < P; ++p) dxij += DY[(ti * H + h) * P + p] * X[(tj * H + h) * P + p];
+      acc += dxij * exp2_fast(ac[i] - ac[j]) * dl[j] * Bm[(tj * G + g) * N + n];
+    }
+  }
+  dC[(ti * G + g) * N + n] = acc;
+}
+
+// One thread per (i) of a head: r_i + R_i.
+__global__ __launch_bounds__(256) void bwd_rr_f32_kernel(
+    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
+    const float* __restrict__ Cm, const float* __restrict__ DY, const float* __restrict__ CB,
+    const float* __restrict__ delta, const float* __restrict__ acs, const float* __restrict__ Hs,
+    float* __restrict__ rR) {
+  const int k = blockIdx.x, h = blockIdx.y;
+  const ChunkInfo ci = chunk_info(m, k);
+  if (ci.len <= 0) return;
+  const int i = blockIdx.z * 256 + threadIdx.x;
+  if (i >= ci.len) return;
+  const int Q = m.Q, g = h / (H / G);
+  const int64_t kh = (int64_t)k * H + h, ti = ci.start + i;
+  const float* ac = acs + kh * Q;
+  const float* dl = delta + kh * Q;
+  const float* cbm = CB + ((int64_t)k * G + g) * Q * Q;
+  float rv = 0.f;
+  for (int p = 0; p < P; ++p) {
+    float hc = 0.f;
+    for (int n = 0; n < N; ++n) hc += Hs[kh * (int64_t)P * N + (int64_t)p * N + n] * Cm[(ti * G + g) * N + n];
+    rv += DY[(ti * H + h) * P + p] * hc;
+  }
+  rv *= exp2_fast(ac[i]);
+  float Rv = 0.f;
+  for (int j = 0; j < i; ++j) {
+    const int64_t tj = ci.start + j;
+    float dxij = 0.f;
+    for (int p = 0; p < P; ++p) dxij += DY[(ti * H + h) * P + p] * X[(tj * H + h) * P + p];
+    Rv += dxij * cbm[(int64_t)i * Q + j] * exp2_fast(ac[i] - ac[j]) * dl[j];
+  }
+  rR[kh * Q + i] = rv + Rv;
+}
+
+// One thread per (j, n) of a group: dB summed over the group's heads.
+__global__ __launch_bounds__(256) void bwd_db_f32_kernel(
+    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
+    const float* __restrict__ Cm, const float* __restrict__ DY, const float* __restrict__ delta,
+    const float* __restrict__ acs, const float* __restrict__ dE, float* __restrict__ dB) {
+  const int k = blockIdx.x, g = blockIdx.y;
+  const ChunkInfo ci = chunk_info(m, k);
+  if (ci.len <= 0) return;
+  const int o = blockIdx.z * 256 + threadIdx.x;
+  const int j = o / N, n = o % N;
+  const int len = ci.len;
+  if (j >= len) return;
+  const int Q = m.Q, hpg = H / G;
+  const int64_t tj = ci.start + j;
+  float acc = 0.f;
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h;
+    const float* ac = acs + kh * Q;
+    const float* dl = delta + kh * Q;
+    float st = 0.f;
+    for (int p = 0; p < P; ++p) st += X[(tj * H + h) * P + p] * dE[kh * (int64_t)P * N + (int64_t)p * N + n];
+    acc += exp2_fast(ac[len - 1] - ac[j]) * dl[j] * st;
+    for (int i = j; i < len; ++i) {
+      const int64_t ti = ci.start + i;
+      float dxij = 0.f;
+      for (int p = 0; p < P; ++p) dxij += DY[(ti * H + h) * P + p] * X[(tj * H + h) * P + p];
+      acc += dxij * exp2_fast(ac[i] - ac[j]) * dl[j] * Cm[(ti * G + g) * N + n];
+    }
+  }
+  dB[(tj * G + g) * N + n] = acc;
+}
+
+// ---------------------------------------------------------------- finalize ----
+// One wavefront per (chunk, head): dAcs_i = rR_i - Ks_i (+ last_term at the last
+// token), ddA_t = sum_{i>=t} dAcs_i by a reversed DPP prefix sum in 64-token
+// blocks from the chunk's end, d(delta)_t = ddd_t + A ddA_t, ddt = d(delta)
+// sigmoid(z) when softplus is on; per-chunk partial sums of delta*ddA and ddt.
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(
+    ChunkMap m, int H, int softplus, const float* __restrict__ dt,
+    const float* __restrict__ dt_bias, const float* __restrict__ A,
+    const float* __restrict__ delta, const float* __restrict__ rR, const float* __restrict__ Ks,
+    const float* __restrict__ ddd, const float* __restrict__ last_term, float* __restrict__ ddt,
+    float* __restrict__ dAp, float* __restrict__ dbp) {
+  const int k = blockIdx.x;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + w;
+  if (h >= H) return;
+  const ChunkInfo ci = chunk_info(m, k);
+  const int64_t kh = (int64_t)k * H + h;
+  if (ci.len <= 0) {
+    if (lane == 0) {
+      dAp[kh] = 0.f;
+      dbp[kh] = 0.f;
+    }
+    return;
+  }
+  const int Q = m.Q, len = ci.len;
+  const float Ah = A[h], bias = dt_bias ? dt_bias[h] : 0.f;
+  const float lt = last_term[kh];
+  float carry = 0.f, pa = 0.f, pb = 0.f;
+  for (int t0 = Q - 64; t0 >= 0; t0 -= 64) {
+    const int t = t0 + 63 - lane;  // lane order reversed: prefix over lanes = suffix over t
+    float v = 0.f;
+    if (t < len) v = rR[kh * Q + t] - Ks[kh * Q + t] + (t == len - 1 ? lt : 0.f);
+    const float incl = wave_inclusive_sum(v) + carry;
+    carry = wave_last(incl);
+    if (t < len) {
+      const float dl = delta[kh * Q + t];
+      const float dd = ddd[kh * Q + t] + Ah * incl;
+      const int64_t tok = ci.start + t;
+      const float g = softplus ? dd * sigmoid_f(dt[tok * H + h] + bias) : dd;
+      ddt[tok * H + h] = g;
+      pa += dl * incl;
+      pb += g;
+    }
+  }
+  pa = wave_sum(pa);
+  pb = wave_sum(pb);
+  if (lane == 0) {
+    dAp[kh] = pa;
+    dbp[kh] = pb;
+  }
+}
+
+// Fixed-order sums over chunk slots, one thread per head.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(int nck, int H, const float* __restrict__ dAp,
+                                                         const float* __restrict__ dbp,
+                                                         const float* __restrict__ dDp,
+                                                         float* __restrict__ dA,
+                                                         float* __restrict__ d_dt_bias,
+                                                         float* __restrict__ dD) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= H) return;
+  float a = 0.f, b = 0.f, d = 0.f;
+  for (int k = 0; k < nck; ++k) {
+    a += dAp[(int64_t)k * H + h];
+    b += dbp[(int64_t)k * H + h];
+    d += dDp[(int64_t)k * H + h];
+  }
+  dA[h] = a;
+  if (d_dt_bias) d_dt_bias[h] = b;
+  if (dD) dD[h] = d;
+}
+
+// ---------------------------------------------------------------- launchers ----
+template <int P, int N>
+static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(256), 0, st, p.map,
+                     p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B, (const uint16_t*)a.dout,
+                     (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, a.dE, a.Hp, a.D,
+                     (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
+  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, p.Q / 64), dim3(256), 0,
+                     st, p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B,
+                     (const uint16_t*)a.C, (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta,
+                     a.acs, a.Hp, (uint16_t*)a.dC, a.rR);
+  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, p.Q / 64), dim3(256), 0,
+                     st, p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
+                     (const uint16_t*)a.dout, a.delta, a.acs, a.dE, (uint16_t*)a.dB);
+}
+
+hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, hipStream_t st) {
+  if (p.nck == 0) return hipSuccess;
+  if (p.io == 0) {
+    hipLaunchKernelGGL(bwd_dx_f32_kernel, dim3((unsigned)p.nck, p.H), dim3(256), 0, st, p.map, p.H,
+                       p.G, p.P, p.N, (const float*)a.x, (const float*)a.B, (const float*)a.dout,
+                       (const float*)a.CB, a.delta, a.acs, a.decay, a.dE, a.Hp, a.D, (float*)a.dx,
+                       a.ddd, a.Ks, a.last_term, a.dDp);
+    hipLaunchKernelGGL(bwd_dc_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
+                       dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
+                       (const float*)a.B, (const float*)a.dout, a.delta, a.acs, a.Hp, (float*)a.dC);
+    hipLaunchKernelGGL(bwd_rr_f32_kernel, dim3((unsigned)p.nck, p.H, (p.Q + 255) / 256), dim3(256), 0,
+                       st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x, (const float*)a.C,
+                       (const float*)a.dout, (const float*)a.CB, a.delta, a.acs, a.Hp, a.rR);
+    hipLaunchKernelGGL(bwd_db_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
+                       dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
+                       (const float*)a.C, (const float*)a.dout, a.delta, a.acs, a.dE, (float*)a.dB);
+    return hipGetLastError();
+  }
+#define SSD_BWD_CASE(PP, NN) \
+  if (p.P == PP && p.N == NN) { launch_bwd_bf16<PP, NN>(p, a, st); return hipGetLastError(); }
+  SSD_BWD_CASE(32, 32) SSD_BWD_CASE(32, 64) SSD_BWD_CASE(32, 128)
+  SSD_BWD_CASE(64, 32) SSD_BWD_CASE(64, 64) SSD_BWD_CASE(64, 128)
+  SSD_BWD_CASE(128, 32) SSD_BWD_CASE(128, 64) SSD_BWD_CASE(128, 128)
+#undef SSD_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st) {
+  if (p.nck > 0)
+    hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, (p.H + 3) / 4), dim3(256), 0, st,
+                       p.map, p.H, p.softplus, a.dt, a.dt_bias, a.A, a.delta, a.rR, a.Ks, a.ddd,
+                       a.last_term, a.ddt, a.dAp, a.dbp);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((p.H + 255) / 256), dim3(256), 0, st, (int)p.nck, p.H,
+                     a.dAp, a.dbp, a.dDp, a.dA, a.d_dt_bias, a.dD);
+  return hipGetLastError();
+}
+
+}  // namespace ssd
