@@ -50,9 +50,12 @@ struct BwdArgs {
   const float *dt, *dt_bias, *A, *D;
   const float *delta, *acs, *decay, *Hp, *dE;
   const void *CB, *CBt;
+  void *dCBg, *dCBgT;  // head-summed dCB per (chunk, group), both orientations
+  float *Rp, *Kp;      // per (chunk, head, 64-token tile, token): R and K partials
   void *dx, *dB, *dC;
   float *ddt, *dA, *dD, *d_dt_bias;
-  // per token (nck, H, Q): direct d(delta), K+s, r+R
+  // per token (nck, H, Q): direct d(delta); s (bf16 path) or K+s (fp32 path);
+  // r (bf16 path) or r+R (fp32 path)
   float *ddd, *Ks, *rR;
   // per (chunk, head): alpha<dE,H> + sum s, and partials of dD, dA, d_dt_bias
   float *last_term, *dDp, *dAp, *dbp;

@@ -12,16 +12,18 @@
 // where r_i = 2^acs_i dy_i . (H C_i), R_i = sum_{j<i} M_ij, K_j = sum_{i>j} M_ij,
 // s_j = w_j delta_j x_j . (dT B_j), M_ij = (dy_i . x_j) CB_ij L_ij delta_j, and the
 // gradient w.r.t. each token's delta*A is the suffix sum ddA_t = sum_{i>=t} dAcs_i.
-// Two identities keep this cheap: sum_{i>=j} (dy_i . x_j) CB_ij L_ij = x_j . U_j
-// where U_j is dx_j's intra-chunk bracket, so the per-token "direct" delta
-// gradient and K_j come out of the dx accumulator; R_i comes out of the dC
-// kernel's dCB tile.
+// The identity sum_{i>=j} (dy_i . x_j) CB_ij L_ij = x_j . U_j, with U_j dx_j's
+// intra-chunk bracket, gives the per-token "direct" delta gradient straight from
+// the dx accumulator.  R_i and K_j are built together from one set of M values
+// (they cancel exactly where the decay gradient subtracts them).
 //
 // Kernels (bf16 on MFMA; fp32 plain loops):
-//   bwd_dx   (chunk, head)        dx, direct d(delta), K+s per token, dD and
-//                                 alpha<dE,H> + sum s per chunk
-//   bwd_dc   (chunk, group, 64 rows)  dC summed over the group's heads, r+R per token
-//   bwd_db   (chunk, group, 64 rows)  dB summed over the group's heads
+//   bwd_dx   (chunk, head)            dx, direct d(delta), s_j, dD and
+//                                     alpha<dE,H> + sum s per chunk
+//   bwd_dcb  (chunk, group, 64x64 causal tile)  head-summed dCB_g in both
+//                                     orientations; per-head tile partials of R, K
+//   bwd_dc   (chunk, group, 64 rows)  dC = dCB_g B + sum_h (state term); r_i
+//   bwd_db   (chunk, group, 64 rows)  dB = dCB_g^T C + sum_h (state term)
 //   finalize (chunk, head)        suffix sum of dAcs (DPP scan), d(delta)->ddt,
 //                                 per-chunk partials of dA and d_dt_bias
 //   reduce   (head)               fixed-order sums over chunks: dA, dD, d_dt_bias
@@ -136,9 +138,7 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
     for (int kk = (j0 / 32) * 32; kk < len; kk += 32) {
       u32x4 cv = u32x4{0u, 0u, 0u, 0u};
       if (jrow < len) cv = *(const u32x4*)(cbt + (int64_t)jrow * Q + kk + q * 8);
-      // hi + lo bf16 split: K_j built from these values must cancel against R_i
-      // (built from the same bf16 CB in the dC kernel) inside the decay gradient
-      u32x4 ah, al;
+      u32x4 av;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int i0 = kk + q * 8 + 2 * d;
@@ -146,15 +146,12 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
         float v1 = bf_hi(cv[d]) * exp2_fast(sa[i0 + 1] - aj);
         v0 = (i0 >= jrow && i0 < len) ? v0 : 0.f;
         v1 = (i0 + 1 >= jrow && i0 + 1 < len) ? v1 : 0.f;
-        ah[d] = pack_bf2(v0, v1);
-        al[d] = pack_bf2(v0 - bf_lo(ah[d]), v1 - bf_hi(ah[d]));
+        av[d] = pack_bf2(v0, v1);
       }
+      const bf16x8 a = as_bf16x8(av);
 #pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) {
-        const bf16x8 b = frag_kmajor(dyt + kk * LDY + tp * 16, LDY, lane);
-        acc[tp] = mfma_bf16(as_bf16x8(ah), b, acc[tp]);
-        acc[tp] = mfma_bf16(as_bf16x8(al), b, acc[tp]);
-      }
+      for (int tp = 0; tp < P / 16; ++tp)
+        acc[tp] = mfma_bf16(a, frag_kmajor(dyt + kk * LDY + tp * 16, LDY, lane), acc[tp]);
     }
     // per-row dots and the store
     float xt[4], dxx[4];
@@ -181,9 +178,8 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
       const int j = j0 + q * 4 + rr;
       if (r == 0 && j < len) {
         const float dj = sd[j];
-        const float cbjj = bf2f(cbt[(int64_t)j * Q + j]);
         ddd[kh * Q + j] = xt[rr];
-        Ks[kh * Q + j] = dj * (xt[rr] - dxx[rr] * cbjj);
+        Ks[kh * Q + j] = dj * xs[rr];  // s_j (K_j comes from bwd_dcb)
         s_sum += dj * xs[rr];
         dxx_sum += dxx[rr];
       }
@@ -207,21 +203,150 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
   }
 }
 
+// ------------------------------------------------------------ bwd_dcb bf16 ----
+// One workgroup per (chunk, group, 64x64 causal tile (ti, tj), tj <= ti).  B and
+// C are shared by the group's heads, so the intra-chunk parts of dC and dB only
+// need the head-summed dCB_g = sum_h dCB^h: it is formed here once per tile and
+// written in both orientations, so dC and dB each become one GEMM per group.
+// For every head the tile's contributions to R_i (row sums over j < i) and K_j
+// (column sums over i > j) of M_ij = dCB_ij CB_ij come from the same values,
+// so they cancel exactly where the decay gradient subtracts them.
+template <int P, int N>
+__global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
+    ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ DY,
+    const uint16_t* __restrict__ CB, const float* __restrict__ delta,
+    const float* __restrict__ acs, uint16_t* __restrict__ dCBg, uint16_t* __restrict__ dCBgT,
+    float* __restrict__ Rp, float* __restrict__ Kp) {
+  constexpr int LT = 64 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t stg[64 * LT];
+  __shared__ float kred[4][64];
+  const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const ChunkInfo ci = chunk_info(m, k);
+  const int Q = m.Q, T = Q / 64;
+  int ti = 0;
+  while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+  const int tj = tile - ti * (ti + 1) / 2;
+  if (ci.len <= 0 || ti * 64 >= ci.len) return;
+  const int len = ci.len;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4, r = lane & 15;
+  const int hpg = H / G;
+  const int64_t xrow = (int64_t)H * P;
+  const int i0 = ti * 64 + w * 16, jt0 = tj * 64;
+  const int irow = i0 + r;
+  const int64_t kg = (int64_t)k * G + g;
+  const uint16_t* cbm = CB + kg * Q * Q;
+  float cbv[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
+      cbv[b][rr] = (i < len && j < i) ? bf2f(cbm[(int64_t)i * Q + j]) : 0.f;
+    }
+  f32x4 sum[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) sum[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h;
+    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
+    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
+    u32x4 ay[P / 32];
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb)
+      ay[kb] = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+    f32x4 dxb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      dxb[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int jcol = jt0 + b * 16 + r;
+#pragma unroll
+      for (int kb = 0; kb < P / 32; ++kb) {
+        const u32x4 xv = (jcol < len) ? *(const u32x4*)(xb + (int64_t)jcol * xrow + kb * 32 + q * 8)
+                                      : u32x4{0u, 0u, 0u, 0u};
+        dxb[b] = mfma_bf16(as_bf16x8(ay[kb]), as_bf16x8(xv), dxb[b]);
+      }
+    }
+    const float* ac = acs + kh * Q;
+    const float* dl = delta + kh * Q;
+    float ai[4], aj[4], dj[4], Rl[4], Kl[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      ai[rr] = ac[min(i0 + q * 4 + rr, Q - 1)];
+      Rl[rr] = 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      aj[b] = ac[jt0 + b * 16 + r];
+      dj[b] = dl[jt0 + b * 16 + r];
+      Kl[b] = 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
+        float v = dxb[b][rr] * exp2_fast(ai[rr] - aj[b]) * dj[b];
+        v = (j <= i && i < len) ? v : 0.f;
+        sum[b][rr] += v;
+        const float mij = v * cbv[b][rr];  // cbv is zero unless j < i < len
+        Rl[rr] += mij;
+        Kl[b] += mij;
+      }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = row_sum16(Rl[rr]);
+      const int i = i0 + q * 4 + rr;
+      if (r == 0 && i < len) Rp[(kh * T + tj) * Q + i] = v;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float c = Kl[b];
+      c += __shfl_xor(c, 16);
+      c += __shfl_xor(c, 32);
+      if (q == 0) kred[w][b * 16 + r] = c;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int j = jt0 + tid;
+      const float v = kred[0][tid] + kred[1][tid] + kred[2][tid] + kred[3][tid];
+      if (j < len) Kp[(kh * T + ti) * Q + j] = v;
+    }
+    __syncthreads();
+  }
+  // head-summed tile -> bf16, through LDS to 16-byte row stores in both orientations
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) stg[(w * 16 + q * 4 + rr) * LT + b * 16 + r] = f2bf(sum[b][rr]);
+  __syncthreads();
+  for (int e = tid; e < 64 * 8; e += 256) {
+    const int row = e >> 3, c8 = e & 7;
+    *(u32x4*)(dCBg + (kg * Q + ti * 64 + row) * Q + jt0 + c8 * 8) = *(const u32x4*)(stg + row * LT + c8 * 8);
+    u32x4 t;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      t[d] = (uint32_t)stg[(c8 * 8 + 2 * d) * LT + row] | ((uint32_t)stg[(c8 * 8 + 2 * d + 1) * LT + row] << 16);
+    *(u32x4*)(dCBgT + (kg * Q + jt0 + row) * Q + ti * 64 + c8 * 8) = t;
+  }
+}
+
 // ------------------------------------------------------------ bwd_dc bf16 ----
+// One workgroup per (chunk, group, 64 rows i).  dC_i = sum_{j<=i} dCB_g[i][j] B_j
+// (A fragments straight from the dCB_g rows, B through LDS one 64-row piece at a
+// time and read with transpose reads) + sum_h 2^acs_i H^T dy_i (one K=headdim
+// GEMM per head with H staged in LDS); r_i = C_i . (that head's state term).
 template <int P, int N>
 __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
-    ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Bm,
-    const uint16_t* __restrict__ Cm, const uint16_t* __restrict__ DY,
-    const uint16_t* __restrict__ CB, const float* __restrict__ delta,
+    ChunkMap m, int H, int G, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ DY, const uint16_t* __restrict__ dCBg,
     const float* __restrict__ acs, const float* __restrict__ Hs, uint16_t* __restrict__ dC,
-    float* __restrict__ rR) {
+    float* __restrict__ rout) {
   constexpr int LDB = N + 16;  // odd multiple of 32 bytes for the transpose reads
-  constexpr int LDS_ = 40;     // dCB staging row stride
-  __shared__ __attribute__((aligned(16))) uint16_t bt[QMAX * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t bt[64 * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t ht[P * LDB];
-  __shared__ __attribute__((aligned(16))) uint16_t stg[4][16 * LDS_];
-  __shared__ float sa[QMAX], sd[QMAX];
-
   const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0 || tile * 64 >= ci.len) return;
@@ -232,21 +357,31 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
   const uint16_t* bb = Bm + (int64_t)ci.start * brow + (int64_t)g * N;
   const uint16_t* cb = Cm + (int64_t)ci.start * brow + (int64_t)g * N;
-  const uint16_t* cbm = CB + ((int64_t)k * G + g) * Q * Q;
+  const uint16_t* dcb = dCBg + ((int64_t)k * G + g) * Q * Q;
   const int i0 = tile * 64 + w * 16;
   const bool active = i0 < len;
-  const int jend = ((min(len, tile * 64 + 64) + 31) / 32) * 32;  // B rows needed, padded
-
-  for (int e = tid; e < jend * (N / 8); e += 256) {
-    const int j = e / (N / 8), c8 = e % (N / 8);
-    const u32x4 v = (j < len) ? *(const u32x4*)(bb + (int64_t)j * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    *(u32x4*)(bt + j * LDB + c8 * 8) = v;
-  }
+  const int irow = i0 + r;
   f32x4 acc[N / 16];
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int irow = i0 + r;  // A-fragment row
-  float cv[N / 16][4];      // C_i[n] in the accumulator layout (for r_i)
+  for (int jt = 0; jt <= tile; ++jt) {
+    __syncthreads();
+    for (int e = tid; e < 64 * (N / 8); e += 256) {
+      const int jj = e / (N / 8), c8 = e % (N / 8), j = jt * 64 + jj;
+      *(u32x4*)(bt + jj * LDB + c8 * 8) =
+          (j < len) ? *(const u32x4*)(bb + (int64_t)j * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    if (!active) continue;
+    for (int jb = jt * 64; jb < min(jt * 64 + 64, i0 + 16); jb += 32) {
+      const bf16x8 a = as_bf16x8(irow < len ? *(const u32x4*)(dcb + (int64_t)irow * Q + jb + q * 8)
+                                            : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        acc[nb] = mfma_bf16(a, frag_kmajor(bt + (jb - jt * 64) * LDB + nb * 16, LDB, lane), acc[nb]);
+    }
+  }
+  float cv[N / 16][4];
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb)
 #pragma unroll
@@ -254,15 +389,10 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
       const int i = i0 + q * 4 + rr;
       cv[nb][rr] = (i < len) ? bf2f(cb[(int64_t)i * brow + nb * 16 + r]) : 0.f;
     }
-
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
     __syncthreads();
-    for (int t = tid; t < Q; t += 256) {
-      sa[t] = acs[kh * Q + t];
-      sd[t] = delta[kh * Q + t];
-    }
     {
       const float* hb = Hs + kh * (int64_t)(P * N);
       for (int e = tid * 4; e < P * N; e += 1024) {
@@ -276,74 +406,35 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     __syncthreads();
     if (!active) continue;
     const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
-    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
-    // dy fragments of rows i (unscaled, and scaled by 2^acs_i for the state part)
-    u32x4 ay[P / 32];
+    const float ei = (irow < len) ? exp2_fast(acs[kh * Q + irow]) : 0.f;
     bf16x8 ays[P / 32];
-    const float ei = (irow < len) ? exp2_fast(sa[irow]) : 0.f;
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb) {
-      ay[kb] = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
-      u32x4 s;
+      const u32x4 ay = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
+                                    : u32x4{0u, 0u, 0u, 0u};
+      u32x4 sv;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) s[d] = pack_bf2(bf_lo(ay[kb][d]) * ei, bf_hi(ay[kb][d]) * ei);
-      ays[kb] = as_bf16x8(s);
+      for (int d = 0; d < 4; ++d) sv[d] = pack_bf2(bf_lo(ay[d]) * ei, bf_hi(ay[d]) * ei);
+      ays[kb] = as_bf16x8(sv);
     }
-    // state part of this head: tmp[i][n] = 2^acs_i sum_p dy_i[p] H[p][n]
-    f32x4 tmp[N / 16];
-#pragma unroll
-    for (int nb = 0; nb < N / 16; ++nb) tmp[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < P / 32; ++kb)
-#pragma unroll
-      for (int nb = 0; nb < N / 16; ++nb)
-        tmp[nb] = mfma_bf16(ays[kb], frag_kmajor(ht + kb * 32 * LDB + nb * 16, LDB, lane), tmp[nb]);
     float rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < N / 16; ++nb)
+    for (int nb = 0; nb < N / 16; ++nb) {
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < P / 32; ++kb)
+        t = mfma_bf16(ays[kb], frag_kmajor(ht + kb * 32 * LDB + nb * 16, LDB, lane), t);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        rsum[rr] += cv[nb][rr] * tmp[nb][rr];
-        acc[nb][rr] += tmp[nb][rr];
+        rsum[rr] += cv[nb][rr] * t[rr];
+        acc[nb][rr] += t[rr];
       }
-    // intra part: dCB_ij = (dy_i . x_j) 2^(acs_i - acs_j) delta_j, j <= i
-    float Rsum[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int jb = 0; jb < min(i0 + 16, len); jb += 32) {
-      f32x4 dxb[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        dxb[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int jcol = jb + c * 16 + r;  // B-operand column of this lane
-#pragma unroll
-        for (int kb = 0; kb < P / 32; ++kb) {
-          const u32x4 xvv = (jcol < len) ? *(const u32x4*)(xb + (int64_t)jcol * xrow + kb * 32 + q * 8)
-                                         : u32x4{0u, 0u, 0u, 0u};
-          dxb[c] = mfma_bf16(as_bf16x8(ay[kb]), as_bf16x8(xvv), dxb[c]);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int i = i0 + q * 4 + rr, j = jb + c * 16 + r;
-          float v = dxb[c][rr] * exp2_fast(sa[min(i, Q - 1)] - sa[j]) * sd[j];
-          v = (j <= i && i < len) ? v : 0.f;
-          if (j < i) Rsum[rr] += v * bf2f(cbm[(int64_t)min(i, Q - 1) * Q + j]);
-          stg[w][(q * 4 + rr) * LDS_ + c * 16 + r] = f2bf(v);
-        }
-      __builtin_amdgcn_wave_barrier();
-      const bf16x8 a = as_bf16x8(*(const u32x4*)(&stg[w][r * LDS_ + q * 8]));
-#pragma unroll
-      for (int nb = 0; nb < N / 16; ++nb)
-        acc[nb] = mfma_bf16(a, frag_kmajor(bt + jb * LDB + nb * 16, LDB, lane), acc[nb]);
-      __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const float v = row_sum16(rsum[rr] + Rsum[rr]);
+      const float v = row_sum16(rsum[rr]);
       const int i = i0 + q * 4 + rr;
-      if (r == 0 && i < len) rR[kh * Q + i] = v;
+      if (r == 0 && i < len) rout[kh * Q + i] = v;
     }
   }
   if (!active) return;
@@ -357,18 +448,17 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
 }
 
 // ------------------------------------------------------------ bwd_db bf16 ----
+// One workgroup per (chunk, group, 64 rows j).  dB_j = sum_{i>=j} dCB_g[i][j] C_i
+// (A fragments from the transposed dCB_g rows, C through LDS in 64-row pieces)
+// + sum_h w_j delta_j dT^T x_j (one K=headdim GEMM per head, dT staged in LDS).
 template <int P, int N>
 __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
-    const uint16_t* __restrict__ DY, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dCBgT, const float* __restrict__ delta,
     const float* __restrict__ acs, const float* __restrict__ dE, uint16_t* __restrict__ dB) {
   constexpr int LDB = N + 16;
-  constexpr int LDS_ = 40;
-  __shared__ __attribute__((aligned(16))) uint16_t ct[QMAX * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t ct[64 * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t dtt[P * LDB];
-  __shared__ __attribute__((aligned(16))) uint16_t stg[4][16 * LDS_];
-  __shared__ float sa[QMAX], sd[QMAX];
-
   const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0 || tile * 64 >= ci.len) return;
@@ -378,28 +468,35 @@ __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
   const int hpg = H / G;
   const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
   const uint16_t* cb = Cm + (int64_t)ci.start * brow + (int64_t)g * N;
+  const uint16_t* dcbt = dCBgT + ((int64_t)k * G + g) * Q * Q;
   const int j0 = tile * 64 + w * 16;
   const bool active = j0 < len;
-  const int ibeg = tile * 64, iend = ((len + 31) / 32) * 32;
-
-  for (int e = tid; e < (iend - ibeg) * (N / 8); e += 256) {
-    const int i = ibeg + e / (N / 8), c8 = e % (N / 8);
-    const u32x4 v = (i < len) ? *(const u32x4*)(cb + (int64_t)i * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    *(u32x4*)(ct + i * LDB + c8 * 8) = v;
-  }
+  const int jrow = j0 + r;
   f32x4 acc[N / 16];
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int jrow = j0 + r;
-
+  for (int it = tile; it * 64 < len; ++it) {
+    __syncthreads();
+    for (int e = tid; e < 64 * (N / 8); e += 256) {
+      const int ii = e / (N / 8), c8 = e % (N / 8), i = it * 64 + ii;
+      *(u32x4*)(ct + ii * LDB + c8 * 8) =
+          (i < len) ? *(const u32x4*)(cb + (int64_t)i * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    if (!active) continue;
+    const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
+    for (int ib = ib0; ib < min(it * 64 + 64, len); ib += 32) {
+      const bf16x8 a = as_bf16x8(jrow < len ? *(const u32x4*)(dcbt + (int64_t)jrow * Q + ib + q * 8)
+                                            : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        acc[nb] = mfma_bf16(a, frag_kmajor(ct + (ib - it * 64) * LDB + nb * 16, LDB, lane), acc[nb]);
+    }
+  }
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
     __syncthreads();
-    for (int t = tid; t < Q; t += 256) {
-      sa[t] = acs[kh * Q + t];
-      sd[t] = delta[kh * Q + t];
-    }
     {
       const float* de = dE + kh * (int64_t)(P * N);
       for (int e = tid * 4; e < P * N; e += 1024) {
@@ -412,55 +509,20 @@ __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
     }
     __syncthreads();
     if (!active) continue;
-    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
     const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
-    u32x4 ax[P / 32];
-    bf16x8 axs[P / 32];
-    const float sj = (jrow < len) ? exp2_fast(sa[len - 1] - sa[jrow]) * sd[jrow] : 0.f;
+    const float* ac = acs + kh * Q;
+    const float sj = (jrow < len) ? exp2_fast(ac[len - 1] - ac[jrow]) * delta[kh * Q + jrow] : 0.f;
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb) {
-      ax[kb] = (jrow < len) ? *(const u32x4*)(xb + (int64_t)jrow * xrow + kb * 32 + q * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
-      u32x4 s;
+      const u32x4 ax = (jrow < len) ? *(const u32x4*)(xb + (int64_t)jrow * xrow + kb * 32 + q * 8)
+                                    : u32x4{0u, 0u, 0u, 0u};
+      u32x4 sv;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) s[d] = pack_bf2(bf_lo(ax[kb][d]) * sj, bf_hi(ax[kb][d]) * sj);
-      axs[kb] = as_bf16x8(s);
-    }
-    // state part: w_j delta_j sum_p x_j[p] dT[p][n]
-#pragma unroll
-    for (int kb = 0; kb < P / 32; ++kb)
+      for (int d = 0; d < 4; ++d) sv[d] = pack_bf2(bf_lo(ax[d]) * sj, bf_hi(ax[d]) * sj);
+      const bf16x8 a = as_bf16x8(sv);
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
-        acc[nb] = mfma_bf16(axs[kb], frag_kmajor(dtt + kb * 32 * LDB + nb * 16, LDB, lane), acc[nb]);
-    // intra part: dCBt[j][i] = (x_j . dy_i) 2^(acs_i - acs_j) delta_j, i >= j
-    for (int ib = (j0 / 32) * 32; ib < len; ib += 32) {
-      f32x4 dxb[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        dxb[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int icol = ib + c * 16 + r;
-#pragma unroll
-        for (int kb = 0; kb < P / 32; ++kb) {
-          const u32x4 dv = (icol < len) ? *(const u32x4*)(dyb + (int64_t)icol * xrow + kb * 32 + q * 8)
-                                        : u32x4{0u, 0u, 0u, 0u};
-          dxb[c] = mfma_bf16(as_bf16x8(ax[kb]), as_bf16x8(dv), dxb[c]);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int j = j0 + q * 4 + rr, i = ib + c * 16 + r;
-          float v = dxb[c][rr] * exp2_fast(sa[i] - sa[min(j, Q - 1)]) * sd[min(j, Q - 1)];
-          v = (i >= j && i < len && j < len) ? v : 0.f;
-          stg[w][(q * 4 + rr) * LDS_ + c * 16 + r] = f2bf(v);
-        }
-      __builtin_amdgcn_wave_barrier();
-      const bf16x8 a = as_bf16x8(*(const u32x4*)(&stg[w][r * LDS_ + q * 8]));
-#pragma unroll
-      for (int nb = 0; nb < N / 16; ++nb)
-        acc[nb] = mfma_bf16(a, frag_kmajor(ct + ib * LDB + nb * 16, LDB, lane), acc[nb]);
-      __builtin_amdgcn_wave_barrier();
+        acc[nb] = mfma_bf16(a, frag_kmajor(dtt + kb * 32 * LDB + nb * 16, LDB, lane), acc[nb]);
     }
   }
   if (!active) return;
@@ -639,15 +701,16 @@ __global__ __launch_bounds__(256) void bwd_db_f32_kernel(
 }
 
 // ---------------------------------------------------------------- finalize ----
-// One wavefront per (chunk, head): dAcs_i = rR_i - Ks_i (+ last_term at the last
-// token), ddA_t = sum_{i>=t} dAcs_i by a reversed DPP prefix sum in 64-token
+// One wavefront per (chunk, head): dAcs_i = rR_i - Ks_i + (R, K tile partials)
+// (+ last_term at the last token), ddA_t = sum_{i>=t} dAcs_i by a reversed DPP prefix sum in 64-token
 // blocks from the chunk's end, d(delta)_t = ddd_t + A ddA_t, ddt = d(delta)
 // sigmoid(z) when softplus is on; per-chunk partial sums of delta*ddA and ddt.
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     ChunkMap m, int H, int softplus, const float* __restrict__ dt,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ delta, const float* __restrict__ rR, const float* __restrict__ Ks,
-    const float* __restrict__ ddd, const float* __restrict__ last_term, float* __restrict__ ddt,
+    const float* __restrict__ ddd, const float* __restrict__ last_term,
+    const float* __restrict__ Rp, const float* __restrict__ Kp, int ntile, float* __restrict__ ddt,
     float* __restrict__ dAp, float* __restrict__ dbp) {
   const int k = blockIdx.x;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -669,7 +732,12 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
   for (int t0 = Q - 64; t0 >= 0; t0 -= 64) {
     const int t = t0 + 63 - lane;  // lane order reversed: prefix over lanes = suffix over t
     float v = 0.f;
-    if (t < len) v = rR[kh * Q + t] - Ks[kh * Q + t] + (t == len - 1 ? lt : 0.f);
+    if (t < len) {
+      v = rR[kh * Q + t] - Ks[kh * Q + t] + (t == len - 1 ? lt : 0.f);
+      // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
+      for (int tl = 0; tl <= t / 64 && tl < ntile; ++tl) v += Rp[(kh * ntile + tl) * Q + t];
+      for (int tl = t / 64; tl <= (len - 1) / 64 && tl < ntile; ++tl) v -= Kp[(kh * ntile + tl) * Q + t];
+    }
     const float incl = wave_inclusive_sum(v) + carry;
     carry = wave_last(incl);
     if (t < len) {
@@ -690,40 +758,52 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
   }
 }
 
-// Fixed-order sums over chunk slots, one thread per head.
+// Fixed-order sums over chunk slots: one wavefront per head, lane l takes slots
+// l, l + 64, ... in order, then a fixed DPP tree across lanes.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(int nck, int H, const float* __restrict__ dAp,
                                                          const float* __restrict__ dbp,
                                                          const float* __restrict__ dDp,
                                                          float* __restrict__ dA,
                                                          float* __restrict__ d_dt_bias,
                                                          float* __restrict__ dD) {
-  const int h = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (h >= H) return;
   float a = 0.f, b = 0.f, d = 0.f;
-  for (int k = 0; k < nck; ++k) {
+  for (int k = lane; k < nck; k += 64) {
     a += dAp[(int64_t)k * H + h];
     b += dbp[(int64_t)k * H + h];
     d += dDp[(int64_t)k * H + h];
   }
-  dA[h] = a;
-  if (d_dt_bias) d_dt_bias[h] = b;
-  if (dD) dD[h] = d;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  d = wave_sum(d);
+  if (lane == 0) {
+    dA[h] = a;
+    if (d_dt_bias) d_dt_bias[h] = b;
+    if (dD) dD[h] = d;
+  }
 }
 
 // ---------------------------------------------------------------- launchers ----
 template <int P, int N>
 static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, hipStream_t st) {
+  const int T = p.Q / 64;
   hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(256), 0, st, p.map,
                      p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B, (const uint16_t*)a.dout,
                      (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, a.dE, a.Hp, a.D,
                      (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
-  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, p.Q / 64), dim3(256), 0,
-                     st, p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B,
-                     (const uint16_t*)a.C, (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta,
-                     a.acs, a.Hp, (uint16_t*)a.dC, a.rR);
-  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, p.Q / 64), dim3(256), 0,
-                     st, p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
-                     (const uint16_t*)a.dout, a.delta, a.acs, a.dE, (uint16_t*)a.dB);
+  hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, T * (T + 1) / 2),
+                     dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
+                     (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
+                     (uint16_t*)a.dCBg, (uint16_t*)a.dCBgT, a.Rp, a.Kp);
+  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, T), dim3(256), 0, st,
+                     p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
+                     (const uint16_t*)a.dout, (const uint16_t*)a.dCBg, a.acs, a.Hp,
+                     (uint16_t*)a.dC, a.rR);
+  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, T), dim3(256), 0, st,
+                     p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
+                     (const uint16_t*)a.dCBgT, a.delta, a.acs, a.dE, (uint16_t*)a.dB);
 }
 
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, hipStream_t st) {
@@ -757,8 +837,8 @@ hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st) 
   if (p.nck > 0)
     hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, (p.H + 3) / 4), dim3(256), 0, st,
                        p.map, p.H, p.softplus, a.dt, a.dt_bias, a.A, a.delta, a.rR, a.Ks, a.ddd,
-                       a.last_term, a.ddt, a.dAp, a.dbp);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((p.H + 255) / 256), dim3(256), 0, st, (int)p.nck, p.H,
+                       a.last_term, a.Rp, a.Kp, p.io == 0 ? 0 : p.Q / 64, a.ddt, a.dAp, a.dbp);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((p.H + 3) / 4), dim3(256), 0, st, (int)p.nck, p.H,
                      a.dAp, a.dbp, a.dDp, a.dA, a.d_dt_bias, a.dD);
   return hipGetLastError();
 }
