@@ -88,6 +88,52 @@ __device__ __forceinline__ bf16x8 frag_kmajor(const uint16_t* tile, int ld, int 
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// --------------------------------------------------------- LDS staging ----
+// Copy ROWS token rows of W bf16 (16-byte pieces) from global rows `src`
+// (stride `srow` elements) into LDS rows `dst` (stride `ld`); rows >= nvalid are
+// zero.  Every load is issued before the first LDS store, so the whole tile
+// costs one memory latency (a loop with a run-time trip count would wait on
+// each load in turn).
+template <int ROWS, int W>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, int ld, const uint16_t* src, int64_t srow,
+                                           int nvalid, int tid) {
+  constexpr int PER = W / 8;
+  constexpr int NC = (ROWS * PER + 255) / 256;
+  u32x4 t[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e = tid + c * 256, j = e / PER, c8 = e % PER;
+    t[c] = (e < ROWS * PER && j < nvalid) ? *(const u32x4*)(src + (int64_t)j * srow + c8 * 8)
+                                          : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e = tid + c * 256, j = e / PER, c8 = e % PER;
+    if (e < ROWS * PER) *(u32x4*)(dst + j * ld + c8 * 8) = t[c];
+  }
+}
+
+// fp32 P x N state (row-major) -> bf16 LDS [p][n] with row stride ld; loads first.
+template <int P, int N>
+__device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const float* src, int tid) {
+  constexpr int NC = (P * N / 4 + 255) / 256;
+  float4 t[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e = (tid + c * 256) * 4;
+    t[c] = (e < P * N) ? *(const float4*)(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e = (tid + c * 256) * 4;
+    if (e < P * N) {
+      uint32_t* d = (uint32_t*)(dst + (e / N) * ld + (e % N));
+      d[0] = pack_bf2(t[c].x, t[c].y);
+      d[1] = pack_bf2(t[c].z, t[c].w);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ DPP ----
 // DPP controls (GFX9 encoding).
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;

@@ -75,24 +75,26 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
     sd[t] = delta[kh * Q + t];
   }
   // dy tile, token-major (rows past the chunk's end are zero)
-  for (int e = tid; e < Q * (P / 8); e += 256) {
-    const int i = e / (P / 8), c8 = e % (P / 8);
-    const u32x4 v = (i < len) ? *(const u32x4*)(dyb + (int64_t)i * xrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    *(u32x4*)(dyt + i * LDY + c8 * 8) = v;
-  }
-  // dT = dE_c as bf16 [p][n]; alpha <dE, H> in fp32 on the way
+  stage_rows<QMAX, P>(dyt, LDY, dyb, xrow, len, tid);
+  // dT = dE_c as bf16 [p][n]; alpha <dE, H> in fp32 on the way (loads first)
   float dot = 0.f;
   {
+    constexpr int NC = P * N / 1024;
     const float* de = dE + kh * (int64_t)(P * N);
     const float* hh = Hs + kh * (int64_t)(P * N);
-    for (int e = tid * 4; e < P * N; e += 1024) {
-      const float4 a = *(const float4*)(de + e);
-      const float4 b = *(const float4*)(hh + e);
-      dot += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-      const int p = e / N, n = e % N;
-      uint32_t* dst = (uint32_t*)(dts + p * LDT + n);
-      dst[0] = pack_bf2(a.x, a.y);
-      dst[1] = pack_bf2(a.z, a.w);
+    float4 ta[NC], tb[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      ta[c] = *(const float4*)(de + (tid + c * 256) * 4);
+      tb[c] = *(const float4*)(hh + (tid + c * 256) * 4);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e = (tid + c * 256) * 4;
+      dot += ta[c].x * tb[c].x + ta[c].y * tb[c].y + ta[c].z * tb[c].z + ta[c].w * tb[c].w;
+      uint32_t* dst = (uint32_t*)(dts + (e / N) * LDT + (e % N));
+      dst[0] = pack_bf2(ta[c].x, ta[c].y);
+      dst[1] = pack_bf2(ta[c].z, ta[c].w);
     }
   }
   dot = wave_sum(dot);
@@ -133,25 +135,35 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
         xs[rr] += xv[tp][rr] * acc[tp][rr];
       }
     }
-    // intra part: sum_{i>=j} CBt[j][i] 2^(acs_i - acs_j) dy_i
+    // intra part: sum_{i>=j} CBt[j][i] 2^(acs_i - acs_j) dy_i; the row block's
+    // CBt fragments are all loaded first (one memory latency)
     const float aj = sa[min(jrow, Q - 1)];
-    for (int kk = (j0 / 32) * 32; kk < len; kk += 32) {
-      u32x4 cv = u32x4{0u, 0u, 0u, 0u};
-      if (jrow < len) cv = *(const u32x4*)(cbt + (int64_t)jrow * Q + kk + q * 8);
-      u32x4 av;
+    const int s_lo = j0 / 32, s_hi = (len + 31) / 32;
+    u32x4 cbf[QMAX / 32];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int i0 = kk + q * 8 + 2 * d;
-        float v0 = bf_lo(cv[d]) * exp2_fast(sa[i0] - aj);
-        float v1 = bf_hi(cv[d]) * exp2_fast(sa[i0 + 1] - aj);
-        v0 = (i0 >= jrow && i0 < len) ? v0 : 0.f;
-        v1 = (i0 + 1 >= jrow && i0 + 1 < len) ? v1 : 0.f;
-        av[d] = pack_bf2(v0, v1);
+    for (int sx = 0; sx < QMAX / 32; ++sx)
+      cbf[sx] = (jrow < len && sx >= s_lo && sx < s_hi)
+                    ? *(const u32x4*)(cbt + (int64_t)jrow * Q + sx * 32 + q * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int sx = 0; sx < QMAX / 32; ++sx) {
+      if (sx >= s_lo && sx < s_hi) {
+        const int kk = sx * 32;
+        u32x4 av;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int i0 = kk + q * 8 + 2 * d;
+          float v0 = bf_lo(cbf[sx][d]) * exp2_fast(sa[i0] - aj);
+          float v1 = bf_hi(cbf[sx][d]) * exp2_fast(sa[i0 + 1] - aj);
+          v0 = (i0 >= jrow && i0 < len) ? v0 : 0.f;
+          v1 = (i0 + 1 >= jrow && i0 + 1 < len) ? v1 : 0.f;
+          av[d] = pack_bf2(v0, v1);
+        }
+        const bf16x8 a = as_bf16x8(av);
+#pragma unroll
+        for (int tp = 0; tp < P / 16; ++tp)
+          acc[tp] = mfma_bf16(a, frag_kmajor(dyt + kk * LDY + tp * 16, LDY, lane), acc[tp]);
       }
-      const bf16x8 a = as_bf16x8(av);
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(a, frag_kmajor(dyt + kk * LDY + tp * 16, LDY, lane), acc[tp]);
     }
     // per-row dots and the store
     float xt[4], dxx[4];
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
     float* __restrict__ Rp, float* __restrict__ Kp) {
   constexpr int LT = 64 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t stg[64 * LT];
-  __shared__ float kred[4][64];
+  __shared__ float kred[8][4][64];
   const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
   const ChunkInfo ci = chunk_info(m, k);
   const int Q = m.Q, T = Q / 64;
@@ -247,28 +259,35 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
   f32x4 sum[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) sum[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int hh = 0; hh < hpg; ++hh) {
-    const int h = g * hpg + hh;
-    const int64_t kh = (int64_t)k * H + h;
+  u32x4 ay[P / 32], xf[4][P / 32];
+  auto load_head = [&](int h) {
     const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
     const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
-    u32x4 ay[P / 32];
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb)
       ay[kb] = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
                             : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int jcol = jt0 + b * 16 + r;
+#pragma unroll
+      for (int kb = 0; kb < P / 32; ++kb)
+        xf[b][kb] = (jcol < len) ? *(const u32x4*)(xb + (int64_t)jcol * xrow + kb * 32 + q * 8)
+                                 : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  load_head(g * hpg);
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h;
     f32x4 dxb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       dxb[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int jcol = jt0 + b * 16 + r;
 #pragma unroll
-      for (int kb = 0; kb < P / 32; ++kb) {
-        const u32x4 xv = (jcol < len) ? *(const u32x4*)(xb + (int64_t)jcol * xrow + kb * 32 + q * 8)
-                                      : u32x4{0u, 0u, 0u, 0u};
-        dxb[b] = mfma_bf16(as_bf16x8(ay[kb]), as_bf16x8(xv), dxb[b]);
-      }
+      for (int kb = 0; kb < P / 32; ++kb) dxb[b] = mfma_bf16(as_bf16x8(ay[kb]), as_bf16x8(xf[b][kb]), dxb[b]);
     }
+    if (hh + 1 < hpg) load_head(h + 1);  // in flight during this head's element-wise work
     const float* ac = acs + kh * Q;
     const float* dl = delta + kh * Q;
     float ai[4], aj[4], dj[4], Rl[4], Kl[4];
@@ -301,20 +320,24 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
       const int i = i0 + q * 4 + rr;
       if (r == 0 && i < len) Rp[(kh * T + tj) * Q + i] = v;
     }
+    const int slot = hh & 7;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       float c = Kl[b];
       c += __shfl_xor(c, 16);
       c += __shfl_xor(c, 32);
-      if (q == 0) kred[w][b * 16 + r] = c;
+      if (q == 0) kred[slot][w][b * 16 + r] = c;
     }
-    __syncthreads();
-    if (tid < 64) {
-      const int j = jt0 + tid;
-      const float v = kred[0][tid] + kred[1][tid] + kred[2][tid] + kred[3][tid];
-      if (j < len) Kp[(kh * T + ti) * Q + j] = v;
+    if (slot == 7 || hh == hpg - 1) {  // cross-wave column sums, fixed order, every 8 heads
+      __syncthreads();
+      for (int e = tid; e < (slot + 1) * 64; e += 256) {
+        const int sl = e >> 6, jj = e & 63, j = jt0 + jj;
+        const int64_t khs = (int64_t)k * H + h - slot + sl;
+        const float v = kred[sl][0][jj] + kred[sl][1][jj] + kred[sl][2][jj] + kred[sl][3][jj];
+        if (j < len) Kp[(khs * T + ti) * Q + j] = v;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   // head-summed tile -> bf16, through LDS to 16-byte row stores in both orientations
 #pragma unroll
@@ -366,11 +389,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int jt = 0; jt <= tile; ++jt) {
     __syncthreads();
-    for (int e = tid; e < 64 * (N / 8); e += 256) {
-      const int jj = e / (N / 8), c8 = e % (N / 8), j = jt * 64 + jj;
-      *(u32x4*)(bt + jj * LDB + c8 * 8) =
-          (j < len) ? *(const u32x4*)(bb + (int64_t)j * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    stage_rows<64, N>(bt, LDB, bb + (int64_t)jt * 64 * brow, brow, len - jt * 64, tid);
     __syncthreads();
     if (!active) continue;
     for (int jb = jt * 64; jb < min(jt * 64 + 64, i0 + 16); jb += 32) {
@@ -393,16 +412,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
     __syncthreads();
-    {
-      const float* hb = Hs + kh * (int64_t)(P * N);
-      for (int e = tid * 4; e < P * N; e += 1024) {
-        const float4 v = *(const float4*)(hb + e);
-        const int p = e / N, n = e % N;
-        uint32_t* dst = (uint32_t*)(ht + p * LDB + n);
-        dst[0] = pack_bf2(v.x, v.y);
-        dst[1] = pack_bf2(v.z, v.w);
-      }
-    }
+    stage_state_bf16<P, N>(ht, LDB, Hs + kh * (int64_t)(P * N), tid);
     __syncthreads();
     if (!active) continue;
     const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
@@ -477,11 +487,7 @@ __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int it = tile; it * 64 < len; ++it) {
     __syncthreads();
-    for (int e = tid; e < 64 * (N / 8); e += 256) {
-      const int ii = e / (N / 8), c8 = e % (N / 8), i = it * 64 + ii;
-      *(u32x4*)(ct + ii * LDB + c8 * 8) =
-          (i < len) ? *(const u32x4*)(cb + (int64_t)i * brow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    stage_rows<64, N>(ct, LDB, cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
     __syncthreads();
     if (!active) continue;
     const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
@@ -497,16 +503,7 @@ __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
     __syncthreads();
-    {
-      const float* de = dE + kh * (int64_t)(P * N);
-      for (int e = tid * 4; e < P * N; e += 1024) {
-        const float4 v = *(const float4*)(de + e);
-        const int p = e / N, n = e % N;
-        uint32_t* dst = (uint32_t*)(dtt + p * LDB + n);
-        dst[0] = pack_bf2(v.x, v.y);
-        dst[1] = pack_bf2(v.z, v.w);
-      }
-    }
+    stage_state_bf16<P, N>(dtt, LDB, dE + kh * (int64_t)(P * N), tid);
     __syncthreads();
     if (!active) continue;
     const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;

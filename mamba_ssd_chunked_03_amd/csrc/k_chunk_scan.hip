@@ -7,14 +7,15 @@
 // the chunk's total decay gets.
 //
 // bf16 path: one workgroup per (chunk, head), four wavefronts.  LDS holds the
-// chunk's x transposed to [p][token] (8x8 register transposes on the way in),
-// H_c rounded to bf16 as [p][n], and the chunk's acs and delta.  Each wavefront
-// owns 16-row blocks of the output in a snake order (w, 7-w, 8+w, 15-w for four
-// waves) so the causal work is balanced.  Per row block:
-//   1. acc = C_rows . H_c^T on MFMA (K = dstate; C fragments straight from
-//      global memory, dstate is contiguous), then each row scaled by 2^(acs_i);
+// chunk's x in its natural token-major layout (16-byte copies; the MFMA
+// operand, 8 consecutive tokens per lane, comes from the gfx950 transpose read
+// ds_read_b64_tr_b16), H_c rounded to bf16 as [p][n], and the chunk's acs and
+// delta.  Each wavefront owns 16-row blocks of the output in a snake order (w,
+// 7-w, 8+w, 15-w for four waves) so the causal work is balanced.  Per row
+// block, all its C and CB fragments are loaded first (one memory latency), then:
+//   1. acc = C_rows . H_c^T on MFMA (K = dstate), each row scaled by 2^(acs_i);
 //   2. acc += M . X where M_ij = CB_ij 2^(acs_i - acs_j) delta_j (j <= i) is
-//      formed in registers from 16-byte CB loads and packed to bf16 as the A
+//      formed in registers from the CB fragments and packed to bf16 as the A
 //      fragment; K runs only up to the row block's last token;
 //   3. + D x_i and the bf16 store.
 //
@@ -29,15 +30,15 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
     const uint16_t* __restrict__ CB, const float* __restrict__ delta,
     const float* __restrict__ acs, const float* __restrict__ Hs, const float* __restrict__ D,
     uint16_t* __restrict__ Y) {
-  constexpr int QMAX = 256, XLD = QMAX + 8, HLD = N + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t xt[P * XLD];
+  constexpr int QMAX = 256, LDX = P + 8, HLD = N + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[QMAX * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t hs[P * HLD];
   __shared__ float sa[QMAX], sd[QMAX];
 
   const int k = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
-  const int Q = m.Q;
+  const int Q = m.Q, len = ci.len;
   const int g = h / (H / G);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, r = lane & 15;
@@ -51,34 +52,8 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
     sa[t] = acs[kh * Q + t];
     sd[t] = delta[kh * Q + t];
   }
-  for (int bidx = tid; bidx < (Q / 8) * (P / 8); bidx += 256) {
-    const int jb = bidx % (Q / 8), c8 = bidx / (Q / 8);
-    u32x4 rows[8], cols[8];
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int j = jb * 8 + rr;
-      rows[rr] = (j < ci.len) ? *(const u32x4*)(xb + (int64_t)j * xrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const uint32_t a = rows[2 * kq][c >> 1], b = rows[2 * kq + 1][c >> 1];
-        cols[c][kq] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-      }
-      *(u32x4*)(xt + (c8 * 8 + c) * XLD + jb * 8) = cols[c];
-    }
-  }
-  {
-    const float* hb = Hs + kh * (int64_t)(P * N);
-    for (int e = tid * 4; e < P * N; e += 1024) {
-      const float4 v = *(const float4*)(hb + e);
-      const int p = e / N, n = e % N;
-      uint32_t* dst = (uint32_t*)(hs + p * HLD + n);
-      dst[0] = pack_bf2(v.x, v.y);
-      dst[1] = pack_bf2(v.z, v.w);
-    }
-  }
+  stage_rows<QMAX, P>(xs, LDX, xb, xrow, len, tid);
+  stage_state_bf16<P, N>(hs, HLD, Hs + kh * (int64_t)(P * N), tid);
   __syncthreads();
 
   const float Dh = D ? D[h] : 0.f;
@@ -86,46 +61,55 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
   for (int ii = 0; ii < NB / 4; ++ii) {
     const int rb = 4 * ii + ((ii & 1) ? (3 - w) : w);
     const int i0 = rb * 16;
-    if (i0 >= ci.len) continue;
+    if (i0 >= len) continue;
+    const int irow = i0 + r;  // the A-fragment row of this lane
+    const bool rowok = irow < len;
+    const int nks = (i0 + 16 + 31) / 32;  // 32-token steps covering j <= i0 + 15
+    u32x4 cf[N / 32], cbf[QMAX / 32];
+#pragma unroll
+    for (int kb = 0; kb < N / 32; ++kb)
+      cf[kb] = rowok ? *(const u32x4*)(cb + (int64_t)irow * crow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < QMAX / 32; ++s)
+      cbf[s] = (rowok && s < nks) ? *(const u32x4*)(cbm + (int64_t)irow * Q + s * 32 + q * 8)
+                                  : u32x4{0u, 0u, 0u, 0u};
     f32x4 acc[P / 16];
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int irow = i0 + r;  // the A-fragment row of this lane
     // 1. state carried in: C_i . H_c^T, then scale rows by 2^acs_i
 #pragma unroll
-    for (int kk = 0; kk < N; kk += 32) {
-      const bf16x8 a = as_bf16x8(irow < ci.len ? *(const u32x4*)(cb + (int64_t)irow * crow + kk + q * 8)
-                                               : u32x4{0u, 0u, 0u, 0u});
+    for (int kb = 0; kb < N / 32; ++kb)
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(a, as_bf16x8(*(const u32x4*)(hs + (tp * 16 + r) * HLD + kk + q * 8)), acc[tp]);
-    }
+        acc[tp] = mfma_bf16(as_bf16x8(cf[kb]),
+                            as_bf16x8(*(const u32x4*)(hs + (tp * 16 + r) * HLD + kb * 32 + q * 8)), acc[tp]);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int i = i0 + q * 4 + rr;
-      const float e = (i < ci.len) ? exp2_fast(sa[i]) : 0.f;
+      const float e = (i < len) ? exp2_fast(sa[i]) : 0.f;
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= e;
     }
     // 2. intra-chunk causal part
     const float ai = sa[min(irow, Q - 1)];
-    for (int kk = 0; kk < i0 + 16; kk += 32) {
-      u32x4 cv = u32x4{0u, 0u, 0u, 0u};
-      if (irow < ci.len) cv = *(const u32x4*)(cbm + (int64_t)irow * Q + kk + q * 8);
-      u32x4 av;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int j0 = kk + q * 8 + 2 * d;
-        float v0 = bf_lo(cv[d]) * exp2_fast(ai - sa[j0]) * sd[j0];
-        float v1 = bf_hi(cv[d]) * exp2_fast(ai - sa[j0 + 1]) * sd[j0 + 1];
-        v0 = (j0 <= irow) ? v0 : 0.f;
-        v1 = (j0 + 1 <= irow) ? v1 : 0.f;
-        av[d] = pack_bf2(v0, v1);
+    for (int s = 0; s < QMAX / 32; ++s) {
+      if (s < nks) {
+        u32x4 av;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int j0 = s * 32 + q * 8 + 2 * d;
+          float v0 = bf_lo(cbf[s][d]) * exp2_fast(ai - sa[j0]) * sd[j0];
+          float v1 = bf_hi(cbf[s][d]) * exp2_fast(ai - sa[j0 + 1]) * sd[j0 + 1];
+          v0 = (j0 <= irow) ? v0 : 0.f;
+          v1 = (j0 + 1 <= irow) ? v1 : 0.f;
+          av[d] = pack_bf2(v0, v1);
+        }
+        const bf16x8 a = as_bf16x8(av);
+#pragma unroll
+        for (int tp = 0; tp < P / 16; ++tp)
+          acc[tp] = mfma_bf16(a, frag_kmajor(xs + s * 32 * LDX + tp * 16, LDX, lane), acc[tp]);
       }
-      const bf16x8 a = as_bf16x8(av);
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(a, as_bf16x8(*(const u32x4*)(xt + (tp * 16 + r) * XLD + kk + q * 8)), acc[tp]);
     }
     // 3. skip term and store
 #pragma unroll
@@ -133,8 +117,8 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int i = i0 + q * 4 + rr, p = tp * 16 + r;
-        if (i < ci.len) {
-          const float v = acc[tp][rr] + Dh * bf2f(xt[p * XLD + i]);
+        if (i < len) {
+          const float v = acc[tp][rr] + Dh * bf2f(xs[i * LDX + p]);
           Y[(int64_t)(ci.start + i) * xrow + (int64_t)h * P + p] = f2bf(v);
         }
       }

@@ -9,33 +9,21 @@
 // produces that chunk-local end state.
 //
 // bf16 path (v_mfma_f32_16x16x32_bf16).  The contraction index is the token
-// index, which is the slow index of both operands in memory, while the MFMA
-// wants 8 consecutive k values per lane.  Tiles of 64 tokens are therefore
-// transposed on their way into LDS: each thread loads an 8x8 block (8 token
-// rows x 16 bytes, coalesced across the wavefront), transposes it in registers
-// and writes 8 rows of 16 bytes.  The scaled operand is split into bf16 hi +
-// lo parts (two MFMAs) so the chunk state keeps ~16 bits of precision; the
-// states feed the fp32 final states.  Four wavefronts, each a
-// (P/2) x (N/2) tile of 16x16 blocks.
+// index, the slow index of both operands in memory, while the MFMA wants 8
+// consecutive k values per lane.  Slices of 64 tokens are copied into LDS in
+// their natural token-major layout with 16-byte moves and the fragments are
+// read with the gfx950 transpose read (ds_read_b64_tr_b16), which hands each
+// lane 8 consecutive tokens of one column.  The next slice's global loads are
+// issued before the current slice's MFMAs, so memory latency overlaps compute.
+// The scaled operand is split into bf16 hi + lo parts (two MFMAs) so the chunk
+// state keeps ~16 bits of precision; the states feed the fp32 final states.
+// Four wavefronts, each a (P/2) x (N/2) tile of 16x16 blocks.
 //
 // fp32 path: one thread per output element, plain FMA loop (correctness path
 // for fp32 inputs; no rounding of any operand).
 #include "internal.hpp"
 
 namespace ssd {
-
-// 8x8 transpose of bf16 values: in[r] holds row r (element c in dword c/2,
-// half c&1); out[c] holds column c (element r at position r).
-__device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t a = in[2 * k][c >> 1], b = in[2 * k + 1][c >> 1];
-      out[c][k] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-    }
-  }
-}
 
 __device__ __forceinline__ float token_scale(int mode, const float* dl, const float* ac, int j,
                                              float a_last) {
@@ -50,27 +38,30 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H
                                                                const float* __restrict__ acs,
                                                                float* __restrict__ out) {
   constexpr int KS = 64;       // tokens per LDS slice
-  constexpr int LD = KS + 8;   // padded row (bf16): b128 reads of 8 rows hit distinct banks
+  constexpr int LDX = P + 16;  // row strides: odd multiples of 32 bytes for the transpose reads
+  constexpr int LDY = N + 16;
   constexpr int WM = 2, WN = 2;
   constexpr int TM = P / 16 / WM, TN = N / 16 / WN;
-  static_assert(TM >= 1 && TN >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t xh[P * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t xl[P * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t ys[N * LD];
+  constexpr int XC = KS * (P / 8) / 256;  // 16-byte chunks per thread per slice
+  constexpr int YC = KS * (N / 8) / 256;
+  static_assert(TM >= 1 && TN >= 1 && XC >= 1 && YC >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t xh[KS * LDX];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[KS * LDX];
+  __shared__ __attribute__((aligned(16))) uint16_t ys[KS * LDY];
   __shared__ float sc[256];
 
   const int k = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
-  const int Q = m.Q;
+  const int Q = m.Q, len = ci.len;
   const int g = h / (H / G);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t kh = (int64_t)k * H + h;
   {
     const float* dl = delta + kh * Q;
     const float* ac = acs + kh * Q;
-    const float a_last = ac[ci.len - 1];
-    for (int t = tid; t < Q; t += 256) sc[t] = (t < ci.len) ? token_scale(mode, dl, ac, t, a_last) : 0.f;
+    const float a_last = ac[len - 1];
+    for (int t = tid; t < Q; t += 256) sc[t] = (t < len) ? token_scale(mode, dl, ac, t, a_last) : 0.f;
   }
   const int64_t xrow = (int64_t)H * P, yrow = (int64_t)G * N;
   const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
@@ -78,67 +69,60 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H
 
   const int wm = w / WN, wn = w % WN;
   const int p0 = wm * (P / WM), n0 = wn * (N / WN);
-  const int q = lane >> 4, r = lane & 15;
+  const int r = lane & 15;
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int NBX = (KS / 8) * (P / 8), NBY = (KS / 8) * (N / 8);
+  u32x4 xr[XC], yr[YC];
+  auto load_slice = [&](int s0) {
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+      const int e = tid + c * 256, j = s0 + e / (P / 8), c8 = e % (P / 8);
+      xr[c] = (j < len) ? *(const u32x4*)(xb + (int64_t)j * xrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int c = 0; c < YC; ++c) {
+      const int e = tid + c * 256, j = s0 + e / (N / 8), c8 = e % (N / 8);
+      yr[c] = (j < len) ? *(const u32x4*)(yb + (int64_t)j * yrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
   __syncthreads();
-  for (int s0 = 0; s0 < ci.len; s0 += KS) {
-    for (int bidx = tid; bidx < NBX + NBY; bidx += 256) {
-      const bool isx = bidx < NBX;
-      const int bb = isx ? bidx : bidx - NBX;
-      const int jb = bb % (KS / 8), cb = bb / (KS / 8);
-      u32x4 rows[8], cols[8];
+  load_slice(0);
+  for (int s0 = 0; s0 < len; s0 += KS) {
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int j = s0 + jb * 8 + rr;
-        if (j < ci.len)
-          rows[rr] = isx ? *(const u32x4*)(xb + (int64_t)j * xrow + cb * 8)
-                         : *(const u32x4*)(yb + (int64_t)j * yrow + cb * 8);
-        else
-          rows[rr] = u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < XC; ++c) {
+      const int e = tid + c * 256, jj = e / (P / 8), c8 = e % (P / 8);
+      const float sv = sc[s0 + jj];
+      u32x4 hi, lo;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float v0 = bf_lo(xr[c][d]) * sv, v1 = bf_hi(xr[c][d]) * sv;
+        hi[d] = pack_bf2(v0, v1);
+        lo[d] = pack_bf2(v0 - bf_lo(hi[d]), v1 - bf_hi(hi[d]));
       }
-      if (isx) {
-        u32x4 lo[8];
+      *(u32x4*)(xh + jj * LDX + c8 * 8) = hi;
+      *(u32x4*)(xl + jj * LDX + c8 * 8) = lo;
+    }
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const float s = sc[s0 + jb * 8 + rr];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const float v0 = bf_lo(rows[rr][d]) * s, v1 = bf_hi(rows[rr][d]) * s;
-            const uint32_t hi = pack_bf2(v0, v1);
-            rows[rr][d] = hi;
-            lo[rr][d] = pack_bf2(v0 - bf_lo(hi), v1 - bf_hi(hi));
-          }
-        }
-        transpose8x8(rows, cols);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *(u32x4*)(xh + (cb * 8 + c) * LD + jb * 8) = cols[c];
-        transpose8x8(lo, cols);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *(u32x4*)(xl + (cb * 8 + c) * LD + jb * 8) = cols[c];
-      } else {
-        transpose8x8(rows, cols);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *(u32x4*)(ys + (cb * 8 + c) * LD + jb * 8) = cols[c];
-      }
+    for (int c = 0; c < YC; ++c) {
+      const int e = tid + c * 256, jj = e / (N / 8), c8 = e % (N / 8);
+      *(u32x4*)(ys + jj * LDY + c8 * 8) = yr[c];
     }
     __syncthreads();
+    if (s0 + KS < len) load_slice(s0 + KS);  // in flight during the MFMAs below
 #pragma unroll
     for (int kk = 0; kk < KS; kk += 32) {
       bf16x8 ah[TM], al[TM], bv[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        ah[i] = as_bf16x8(*(const u32x4*)(xh + (p0 + i * 16 + r) * LD + kk + q * 8));
-        al[i] = as_bf16x8(*(const u32x4*)(xl + (p0 + i * 16 + r) * LD + kk + q * 8));
+        ah[i] = frag_kmajor(xh + kk * LDX + p0 + i * 16, LDX, lane);
+        al[i] = frag_kmajor(xl + kk * LDX + p0 + i * 16, LDX, lane);
       }
 #pragma unroll
-      for (int jj = 0; jj < TN; ++jj)
-        bv[jj] = as_bf16x8(*(const u32x4*)(ys + (n0 + jj * 16 + r) * LD + kk + q * 8));
+      for (int jj = 0; jj < TN; ++jj) bv[jj] = frag_kmajor(ys + kk * LDY + n0 + jj * 16, LDY, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -149,6 +133,7 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H
     }
     __syncthreads();
   }
+  const int q = lane >> 4;
   float* ob = out + kh * (int64_t)(P * N);
 #pragma unroll
   for (int i = 0; i < TM; ++i)

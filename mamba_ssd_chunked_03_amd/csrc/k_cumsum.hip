@@ -28,12 +28,19 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(ChunkMap m, int H, in
   if (ci.len <= 0) return;
   const int Q = m.Q;
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < Q * kCumsumHeads; idx += 256) {
-    int t = idx / kCumsumHeads, hh = idx % kCumsumHeads;
-    int h = h0 + hh;
-    float v = 0.f;
-    if (t < ci.len && h < H) v = dt[(int64_t)(ci.start + t) * H + h];
-    tile[t * (kCumsumHeads + 1) + hh] = v;
+  {
+    constexpr int NC = 256 * kCumsumHeads / 256;  // loads issued together, then stored
+    float v[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int idx = tid + c * 256, t = idx / kCumsumHeads, h = h0 + idx % kCumsumHeads;
+      v[c] = (t < ci.len && h < H) ? dt[(int64_t)(ci.start + t) * H + h] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int idx = tid + c * 256, t = idx / kCumsumHeads, hh = idx % kCumsumHeads;
+      if (t < Q) tile[t * (kCumsumHeads + 1) + hh] = v[c];
+    }
   }
   __syncthreads();
   const int w = tid >> 6, lane = tid & 63;
