@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time ssd_fwd alone as the step")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run the library's plain copy kernel (counter calibration)")
     return ap.parse_args()
 
 
@@ -131,6 +133,14 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            ssd.util_copy(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}))
+        return
     cfg = inputs.CONFIGS[2]
     Q = cfg["chunk"]
     inp = inputs.config_inputs(2)

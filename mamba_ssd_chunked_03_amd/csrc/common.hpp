@@ -94,38 +94,38 @@ __device__ __forceinline__ bf16x8 frag_kmajor(const uint16_t* tile, int ld, int 
 // zero.  Every load is issued before the first LDS store, so the whole tile
 // costs one memory latency (a loop with a run-time trip count would wait on
 // each load in turn).
-template <int ROWS, int W>
+template <int ROWS, int W, int NT = 256>
 __device__ __forceinline__ void stage_rows(uint16_t* dst, int ld, const uint16_t* src, int64_t srow,
                                            int nvalid, int tid) {
   constexpr int PER = W / 8;
-  constexpr int NC = (ROWS * PER + 255) / 256;
+  constexpr int NC = (ROWS * PER + NT - 1) / NT;
   u32x4 t[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int e = tid + c * 256, j = e / PER, c8 = e % PER;
+    const int e = tid + c * NT, j = e / PER, c8 = e % PER;
     t[c] = (e < ROWS * PER && j < nvalid) ? *(const u32x4*)(src + (int64_t)j * srow + c8 * 8)
                                           : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int e = tid + c * 256, j = e / PER, c8 = e % PER;
+    const int e = tid + c * NT, j = e / PER, c8 = e % PER;
     if (e < ROWS * PER) *(u32x4*)(dst + j * ld + c8 * 8) = t[c];
   }
 }
 
 // fp32 P x N state (row-major) -> bf16 LDS [p][n] with row stride ld; loads first.
-template <int P, int N>
+template <int P, int N, int NT = 256>
 __device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const float* src, int tid) {
-  constexpr int NC = (P * N / 4 + 255) / 256;
+  constexpr int NC = (P * N / 4 + NT - 1) / NT;
   float4 t[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int e = (tid + c * 256) * 4;
+    const int e = (tid + c * NT) * 4;
     t[c] = (e < P * N) ? *(const float4*)(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int e = (tid + c * 256) * 4;
+    const int e = (tid + c * NT) * 4;
     if (e < P * N) {
       uint32_t* d = (uint32_t*)(dst + (e / N) * ld + (e % N));
       d[0] = pack_bf2(t[c].x, t[c].y);
@@ -178,6 +178,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Broadcast lane 63's value to the whole wavefront.
 __device__ __forceinline__ float wave_last(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// ------------------------------------------------------- XCD-aware order ----
+// Workgroups are handed to the 8 XCDs round-robin (linear id L goes to XCD
+// L % 8) and each XCD has its own L2.  xcd_order(L, W) renumbers a 1-D grid of
+// W workgroups so that consecutive logical ids run on the same XCD, one after
+// the other: tiles that share operands (the row tiles of one chunk and group)
+// then find them in that XCD's L2 instead of fetching them again from HBM.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_order(int L, int W) {
+  const int x = L % kNumXcd, s = L / kNumXcd;
+  const int per = W / kNumXcd, rem = W % kNumXcd;
+  return x * per + min(x, rem) + s;
 }
 
 // ------------------------------------------------------------ chunk map ----

@@ -35,8 +35,10 @@ namespace ssd {
 constexpr int QMAX = 256;
 
 // ------------------------------------------------------------ bwd_dx bf16 ----
+constexpr int kDxWaves = 8;
+
 template <int P, int N>
-__global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
+__global__ __launch_bounds__(kDxWaves * 64) void bwd_dx_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ DY, const uint16_t* __restrict__ CBt,
     const float* __restrict__ delta, const float* __restrict__ acs,
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t dyt[QMAX * LDY];
   __shared__ __attribute__((aligned(16))) uint16_t dts[P * LDT];
   __shared__ float sa[QMAX], sd[QMAX];
-  __shared__ float red[3][4];
+  __shared__ float red[3][kDxWaves];
 
   const int k = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = chunk_info(m, k);
@@ -70,31 +72,34 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
   const uint16_t* bb = Bm + (int64_t)ci.start * brow + (int64_t)g * N;
   const uint16_t* cbt = CBt + ((int64_t)k * G + g) * Q * Q;
 
-  for (int t = tid; t < Q; t += 256) {
+  for (int t = tid; t < Q; t += kDxWaves * 64) {
     sa[t] = acs[kh * Q + t];
     sd[t] = delta[kh * Q + t];
   }
   // dy tile, token-major (rows past the chunk's end are zero)
-  stage_rows<QMAX, P>(dyt, LDY, dyb, xrow, len, tid);
+  stage_rows<QMAX, P, kDxWaves * 64>(dyt, LDY, dyb, xrow, len, tid);
   // dT = dE_c as bf16 [p][n]; alpha <dE, H> in fp32 on the way (loads first)
   float dot = 0.f;
   {
-    constexpr int NC = P * N / 1024;
+    constexpr int NT = kDxWaves * 64, NC = (P * N / 4 + NT - 1) / NT;
     const float* de = dE + kh * (int64_t)(P * N);
     const float* hh = Hs + kh * (int64_t)(P * N);
     float4 ta[NC], tb[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      ta[c] = *(const float4*)(de + (tid + c * 256) * 4);
-      tb[c] = *(const float4*)(hh + (tid + c * 256) * 4);
+      const int e = (tid + c * NT) * 4;
+      ta[c] = (e < P * N) ? *(const float4*)(de + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      tb[c] = (e < P * N) ? *(const float4*)(hh + e) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int e = (tid + c * 256) * 4;
-      dot += ta[c].x * tb[c].x + ta[c].y * tb[c].y + ta[c].z * tb[c].z + ta[c].w * tb[c].w;
-      uint32_t* dst = (uint32_t*)(dts + (e / N) * LDT + (e % N));
-      dst[0] = pack_bf2(ta[c].x, ta[c].y);
-      dst[1] = pack_bf2(ta[c].z, ta[c].w);
+      const int e = (tid + c * NT) * 4;
+      if (e < P * N) {
+        dot += ta[c].x * tb[c].x + ta[c].y * tb[c].y + ta[c].z * tb[c].z + ta[c].w * tb[c].w;
+        uint32_t* dst = (uint32_t*)(dts + (e / N) * LDT + (e % N));
+        dst[0] = pack_bf2(ta[c].x, ta[c].y);
+        dst[1] = pack_bf2(ta[c].z, ta[c].w);
+      }
     }
   }
   dot = wave_sum(dot);
@@ -104,8 +109,9 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
   const float a_last = sa[len - 1];
   float s_sum = 0.f, dxx_sum = 0.f;  // lane r == 0 of each row group accumulates its rows
   const int NB = Q / 16;
-  for (int ii = 0; ii < NB / 4; ++ii) {
-    const int rb = 4 * ii + ((ii & 1) ? (3 - w) : w);
+  for (int ii = 0; ii * kDxWaves < NB; ++ii) {
+    const int rb = kDxWaves * ii + ((ii & 1) ? (kDxWaves - 1 - w) : w);
+    if (rb >= NB) continue;  // chunk sizes with fewer row blocks than wavefronts
     const int j0 = rb * 16;
     if (j0 >= len) continue;
     f32x4 acc[P / 16];
@@ -207,9 +213,12 @@ __global__ __launch_bounds__(256) void bwd_dx_bf16_kernel(
   }
   __syncthreads();
   if (tid == 0) {
-    const float S = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const float DD = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    const float HD = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    float S = 0.f, DD = 0.f, HD = 0.f;
+    for (int i = 0; i < kDxWaves; ++i) {
+      S += red[0][i];
+      DD += red[1][i];
+      HD += red[2][i];
+    }
     last_term[kh] = S + exp2_fast(decay[kh]) * HD;
     dDp[kh] = DD;
   }
@@ -232,9 +241,10 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
   constexpr int LT = 64 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t stg[64 * LT];
   __shared__ float kred[8][4][64];
-  const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const int Q = m.Q, T = Q / 64, NT = T * (T + 1) / 2;
+  const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
+  const int tile = lid % NT, k = lid / NT / G, g = (lid / NT) % G;
   const ChunkInfo ci = chunk_info(m, k);
-  const int Q = m.Q, T = Q / 64;
   int ti = 0;
   while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
   const int tj = tile - ti * (ti + 1) / 2;
@@ -370,7 +380,9 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   constexpr int LDB = N + 16;  // odd multiple of 32 bytes for the transpose reads
   __shared__ __attribute__((aligned(16))) uint16_t bt[64 * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t ht[P * LDB];
-  const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const int T = m.Q / 64;
+  const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
+  const int tile = lid % T, k = lid / T / G, g = (lid / T) % G;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0 || tile * 64 >= ci.len) return;
   const int Q = m.Q, len = ci.len;
@@ -469,7 +481,9 @@ __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
   constexpr int LDB = N + 16;
   __shared__ __attribute__((aligned(16))) uint16_t ct[64 * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t dtt[P * LDB];
-  const int k = blockIdx.x, g = blockIdx.y, tile = blockIdx.z;
+  const int T = m.Q / 64;
+  const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
+  const int tile = lid % T, k = lid / T / G, g = (lid / T) % G;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0 || tile * 64 >= ci.len) return;
   const int Q = m.Q, len = ci.len;
@@ -786,19 +800,19 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(int nck, int H, const f
 template <int P, int N>
 static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, hipStream_t st) {
   const int T = p.Q / 64;
-  hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(256), 0, st, p.map,
+  hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(kDxWaves * 64), 0, st, p.map,
                      p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B, (const uint16_t*)a.dout,
                      (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, a.dE, a.Hp, a.D,
                      (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
-  hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, T * (T + 1) / 2),
+  hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
                      dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
                      (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
                      (uint16_t*)a.dCBg, (uint16_t*)a.dCBgT, a.Rp, a.Kp);
-  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, T), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
                      (const uint16_t*)a.dout, (const uint16_t*)a.dCBg, a.acs, a.Hp,
                      (uint16_t*)a.dC, a.rR);
-  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.G, T), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
                      (const uint16_t*)a.dCBgT, a.delta, a.acs, a.dE, (uint16_t*)a.dB);
 }

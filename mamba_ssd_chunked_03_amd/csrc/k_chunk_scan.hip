@@ -6,26 +6,37 @@
 // within-chunk cumsum (acs_i - acs_j <= 0), so nothing overflows however long
 // the chunk's total decay gets.
 //
-// bf16 path: one workgroup per (chunk, head), four wavefronts.  LDS holds the
+// bf16 path: one workgroup per (chunk, head), eight wavefronts.  LDS holds the
 // chunk's x in its natural token-major layout (16-byte copies; the MFMA
 // operand, 8 consecutive tokens per lane, comes from the gfx950 transpose read
 // ds_read_b64_tr_b16), H_c rounded to bf16 as [p][n], and the chunk's acs and
-// delta.  Each wavefront owns 16-row blocks of the output in a snake order (w,
-// 7-w, 8+w, 15-w for four waves) so the causal work is balanced.  Per row
-// block, all its C and CB fragments are loaded first (one memory latency), then:
-//   1. acc = C_rows . H_c^T on MFMA (K = dstate), each row scaled by 2^(acs_i);
-//   2. acc += M . X where M_ij = CB_ij 2^(acs_i - acs_j) delta_j (j <= i) is
-//      formed in registers from the CB fragments and packed to bf16 as the A
-//      fragment; K runs only up to the row block's last token;
-//   3. + D x_i and the bf16 store.
+// delta.  Each wavefront owns 16-row blocks of the output in a snake order (w and
+// 15-w for eight waves) so the causal work is balanced.  Per row
+// block, all its C and CB fragments are loaded first (one memory latency).
+// The decay 2^(acs_i - acs_j) is factored through an anchor token e with
+// j <= e < i, 2^(acs_i - acs_e) * 2^(acs_e - acs_j), both factors <= 1 (acs never
+// increases), so nothing can overflow.  For a row block starting in the 32-token
+// block [b0, b0 + 32), every column j < b0 uses e = b0 - 1: the column factors
+// 2^(acs_e - acs_j) delta_j are tabulated once per workgroup in LDS, and the row
+// factor is applied to the accumulator.  Only the diagonal 32-block needs one
+// exp per element.  Per row block:
+//   1. acc = 2^(acs_e) C_rows . H_c^T on MFMA (K = dstate);
+//   2. acc += (CB_ij * column factor) . X over the blocks before b0 (the A
+//      fragment formed in registers from the CB fragments, packed to bf16);
+//   3. acc *= 2^(acs_i - acs_e) per row, which also turns 1.'s factor into 2^acs_i;
+//   4. acc += M . X over the diagonal block, M_ij = CB_ij 2^(acs_i - acs_j) delta_j
+//      masked to j <= i;
+//   5. + D x_i and the bf16 store.
 //
 // fp32 path: one thread per (token, p), plain loops.
 #include "internal.hpp"
 
 namespace ssd {
 
+constexpr int kScanWaves = 8;
+
 template <int P, int N>
-__global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
+__global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ CB, const float* __restrict__ delta,
     const float* __restrict__ acs, const float* __restrict__ Hs, const float* __restrict__ D,
@@ -34,6 +45,7 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t xs[QMAX * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t hs[P * HLD];
   __shared__ float sa[QMAX], sd[QMAX];
+  __shared__ __attribute__((aligned(16))) float vt[QMAX / 32][QMAX];  // column factors per anchor
 
   const int k = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = chunk_info(m, k);
@@ -48,70 +60,99 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
   const uint16_t* cb = Cm + (int64_t)ci.start * crow + (int64_t)g * N;
   const uint16_t* cbm = CB + ((int64_t)k * G + g) * Q * Q;
 
-  for (int t = tid; t < Q; t += 256) {
+  for (int t = tid; t < Q; t += kScanWaves * 64) {
     sa[t] = acs[kh * Q + t];
     sd[t] = delta[kh * Q + t];
   }
-  stage_rows<QMAX, P>(xs, LDX, xb, xrow, len, tid);
-  stage_state_bf16<P, N>(hs, HLD, Hs + kh * (int64_t)(P * N), tid);
+  stage_rows<QMAX, P, kScanWaves * 64>(xs, LDX, xb, xrow, len, tid);
+  stage_state_bf16<P, N, kScanWaves * 64>(hs, HLD, Hs + kh * (int64_t)(P * N), tid);
+  __syncthreads();
+  // column factors for anchor e = 32b - 1: 2^(acs_e - acs_j) delta_j for j <= e
+  for (int idx = tid; idx < (Q / 32) * Q; idx += kScanWaves * 64) {
+    const int b = idx / Q, j = idx % Q;
+    vt[b][j] = (b > 0 && j < 32 * b) ? exp2_fast(sa[32 * b - 1] - sa[j]) * sd[j] : 0.f;
+  }
   __syncthreads();
 
   const float Dh = D ? D[h] : 0.f;
   const int NB = Q / 16;
-  for (int ii = 0; ii < NB / 4; ++ii) {
-    const int rb = 4 * ii + ((ii & 1) ? (3 - w) : w);
+  for (int ii = 0; ii * kScanWaves < NB; ++ii) {
+    const int rb = kScanWaves * ii + ((ii & 1) ? (kScanWaves - 1 - w) : w);
+    if (rb >= NB) continue;  // chunk sizes with fewer row blocks than wavefronts
     const int i0 = rb * 16;
     if (i0 >= len) continue;
     const int irow = i0 + r;  // the A-fragment row of this lane
     const bool rowok = irow < len;
-    const int nks = (i0 + 16 + 31) / 32;  // 32-token steps covering j <= i0 + 15
+    const int nb = i0 / 32;   // 32-token blocks strictly before the diagonal block
+    const float ae = nb > 0 ? sa[32 * nb - 1] : 0.f;
     u32x4 cf[N / 32], cbf[QMAX / 32];
 #pragma unroll
     for (int kb = 0; kb < N / 32; ++kb)
       cf[kb] = rowok ? *(const u32x4*)(cb + (int64_t)irow * crow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int s = 0; s < QMAX / 32; ++s)
-      cbf[s] = (rowok && s < nks) ? *(const u32x4*)(cbm + (int64_t)irow * Q + s * 32 + q * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
+    for (int sx = 0; sx < QMAX / 32; ++sx)
+      cbf[sx] = (rowok && sx <= nb) ? *(const u32x4*)(cbm + (int64_t)irow * Q + sx * 32 + q * 8)
+                                    : u32x4{0u, 0u, 0u, 0u};
     f32x4 acc[P / 16];
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // 1. state carried in: C_i . H_c^T, then scale rows by 2^acs_i
+    // 1. state carried in, pre-scaled by 2^acs_e
 #pragma unroll
     for (int kb = 0; kb < N / 32; ++kb)
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
         acc[tp] = mfma_bf16(as_bf16x8(cf[kb]),
                             as_bf16x8(*(const u32x4*)(hs + (tp * 16 + r) * HLD + kb * 32 + q * 8)), acc[tp]);
+    {
+      const float s0 = exp2_fast(ae);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = i0 + q * 4 + rr;
-      const float e = (i < len) ? exp2_fast(sa[i]) : 0.f;
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= e;
+      for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= s0;
     }
-    // 2. intra-chunk causal part
-    const float ai = sa[min(irow, Q - 1)];
+    // 2. blocks before the diagonal block, through the anchor's column factors
+    const float* vrow = &vt[nb][0];
 #pragma unroll
-    for (int s = 0; s < QMAX / 32; ++s) {
-      if (s < nks) {
+    for (int sx = 0; sx < QMAX / 32; ++sx) {
+      if (sx < nb) {
+        const float4 f0 = *(const float4*)(vrow + sx * 32 + q * 8);
+        const float4 f1 = *(const float4*)(vrow + sx * 32 + q * 8 + 4);
         u32x4 av;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int j0 = s * 32 + q * 8 + 2 * d;
-          float v0 = bf_lo(cbf[s][d]) * exp2_fast(ai - sa[j0]) * sd[j0];
-          float v1 = bf_hi(cbf[s][d]) * exp2_fast(ai - sa[j0 + 1]) * sd[j0 + 1];
-          v0 = (j0 <= irow) ? v0 : 0.f;
-          v1 = (j0 + 1 <= irow) ? v1 : 0.f;
-          av[d] = pack_bf2(v0, v1);
-        }
+        av[0] = pack_bf2(bf_lo(cbf[sx][0]) * f0.x, bf_hi(cbf[sx][0]) * f0.y);
+        av[1] = pack_bf2(bf_lo(cbf[sx][1]) * f0.z, bf_hi(cbf[sx][1]) * f0.w);
+        av[2] = pack_bf2(bf_lo(cbf[sx][2]) * f1.x, bf_hi(cbf[sx][2]) * f1.y);
+        av[3] = pack_bf2(bf_lo(cbf[sx][3]) * f1.z, bf_hi(cbf[sx][3]) * f1.w);
         const bf16x8 a = as_bf16x8(av);
 #pragma unroll
         for (int tp = 0; tp < P / 16; ++tp)
-          acc[tp] = mfma_bf16(a, frag_kmajor(xs + s * 32 * LDX + tp * 16, LDX, lane), acc[tp]);
+          acc[tp] = mfma_bf16(a, frag_kmajor(xs + sx * 32 * LDX + tp * 16, LDX, lane), acc[tp]);
       }
     }
-    // 3. skip term and store
+    // 3. row factors 2^(acs_i - acs_e)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int i = i0 + q * 4 + rr;
+      const float u = (i < len) ? exp2_fast(sa[i] - ae) : 0.f;
+#pragma unroll
+      for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= u;
+    }
+    // 4. the diagonal block, one exp per element
+    {
+      const float ai = sa[min(irow, Q - 1)];
+      u32x4 av;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int j0 = nb * 32 + q * 8 + 2 * d;
+        float v0 = bf_lo(cbf[nb][d]) * exp2_fast(ai - sa[j0]) * sd[j0];
+        float v1 = bf_hi(cbf[nb][d]) * exp2_fast(ai - sa[j0 + 1]) * sd[j0 + 1];
+        v0 = (j0 <= irow) ? v0 : 0.f;
+        v1 = (j0 + 1 <= irow) ? v1 : 0.f;
+        av[d] = pack_bf2(v0, v1);
+      }
+      const bf16x8 a = as_bf16x8(av);
+#pragma unroll
+      for (int tp = 0; tp < P / 16; ++tp)
+        acc[tp] = mfma_bf16(a, frag_kmajor(xs + nb * 32 * LDX + tp * 16, LDX, lane), acc[tp]);
+    }
+    // 5. skip term and store
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp)
 #pragma unroll
@@ -158,7 +199,7 @@ template <int P, int N>
 static void launch_scan_bf16(const Prob& p, const void* x, const void* C, const void* CB,
                              const float* delta, const float* acs, const float* passed,
                              const float* D, void* out, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_scan_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(256), 0, st,
+  hipLaunchKernelGGL((chunk_scan_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(kScanWaves * 64), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)x, (const uint16_t*)C, (const uint16_t*)CB,
                      delta, acs, passed, D, (uint16_t*)out);
 }
