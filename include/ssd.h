@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
   SSD_OK = 0,
@@ -76,6 +76,17 @@ typedef enum {
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
+/* ssd_problem.flags (bit set).
+ * SSD_FLAG_SAVE_FOR_BWD: ssd_fwd keeps its intermediates (delta, the cumsum, the
+ *   passed states and C.B^T in both orientations) in the workspace, which must then
+ *   hold ssd_bwd_workspace_bytes().
+ * SSD_FLAG_FROM_SAVED: ssd_bwd takes those intermediates from its workspace instead
+ *   of recomputing them.  The workspace must be the one a SAVE_FOR_BWD ssd_fwd call
+ *   on the same problem, inputs and chunk size last wrote, unmodified since; nothing
+ *   checks this. */
+#define SSD_FLAG_SAVE_FOR_BWD 1
+#define SSD_FLAG_FROM_SAVED 2
+
 typedef struct {
   int32_t batch;       /* B (1 when cu_seqlens is given) */
   int32_t seqlen;      /* L: tokens per batch row (total packed tokens with cu_seqlens) */
@@ -86,6 +97,7 @@ typedef struct {
   int32_t nseq;        /* number of packed sequences; read only when cu_seqlens != NULL */
   int32_t io_dtype;    /* ssd_dtype of x, B, C, out, dout, dx, dB, dC */
   int32_t dt_softplus; /* 1: delta = softplus(dt + dt_bias); 0: delta = dt + dt_bias */
+  int32_t flags;       /* SSD_FLAG_* bits, 0 for none */
 } ssd_problem;
 
 /* ABI version (SSD_ABI_VERSION) and a static message for a status code. */
@@ -121,8 +133,9 @@ ssd_status ssd_fwd(const ssd_problem* problem,
  * Inputs are those of ssd_fwd plus dout and d_final_states (NULL = 0).
  * Outputs: dx, dB, dC (io dtype; dB and dC summed over each group's heads in
  * fp32 before rounding), ddt (w.r.t. the raw dt input), dA (required), and the
- * optional dD (required iff D != NULL), d_dt_bias, d_init_states.
- * The forward intermediates are recomputed inside (nothing is saved). */
+ * optional dD (required iff D != NULL; computed whenever given), d_dt_bias,
+ * d_init_states.  The forward intermediates are recomputed inside unless
+ * problem->flags has SSD_FLAG_FROM_SAVED (see above). */
 ssd_status ssd_bwd(const ssd_problem* problem,
                    const void* x, const float* dt, const float* dt_bias, const float* A,
                    const void* B, const void* C, const float* D,

@@ -30,6 +30,7 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
     return SSD_ERR_SHAPE;
   if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
+  if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED)) return SSD_ERR_UNSUPPORTED;
   if (packed && (pr->batch != 1 || pr->nseq < 0)) return SSD_ERR_SHAPE;
   if (pr->io_dtype != SSD_F32 && pr->io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
   if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
@@ -48,6 +49,7 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   p.softplus = pr->dt_softplus;
   p.Q = Q;
   p.packed = packed;
+  p.flags = pr->flags;
   p.nseq = packed ? pr->nseq : pr->batch;
   if (packed) {
     if (p.nseq > 65535) return SSD_ERR_UNSUPPORTED;
@@ -203,7 +205,9 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   if (!all_aligned({x, dt, dt_bias, A, B, C, D, init_states, cu_seqlens, out, final_states, workspace}))
     return SSD_ERR_ALIGN;
   const FwdLayout l = fwd_layout(p);
-  if (l.end > 0 && (!workspace || workspace_bytes < l.end)) return SSD_ERR_WORKSPACE;
+  const bool save = (p.flags & SSD_FLAG_SAVE_FOR_BWD) != 0;
+  const size_t need = save ? bwd_layout(p).end : l.end;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   s = setup_map(p, cu_seqlens, ws, st);
@@ -217,7 +221,8 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
   SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
   SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, final_states, 0, st));
-  SSD_TRY(launch_bmm_chunk(p, B, C, CB, st));
+  void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
+  SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
   SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, D, out, st));
   return SSD_OK;
 }
@@ -253,12 +258,12 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   void* CBt = ws + l.CBt;
   float* U = (float*)(ws + l.U);
   float* dE = (float*)(ws + l.dE);
-  // forward intermediates, recomputed
-  SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
-  SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
-  SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, nullptr, 0, st));
-  SSD_TRY(launch_bmm_chunk(p, B, C, CB, st));
-  if (p.io == SSD_BF16) SSD_TRY(launch_bmm_chunk_t(p, B, C, CBt, st));
+  if (!(p.flags & SSD_FLAG_FROM_SAVED)) {  // forward intermediates, recomputed
+    SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
+    SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
+    SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, nullptr, 0, st));
+    SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
+  }
   // adjoint of the state carried into each chunk, then the reverse scan
   SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
   SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, d_init_states, 1, st));

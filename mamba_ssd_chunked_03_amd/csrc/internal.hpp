@@ -16,6 +16,7 @@ struct Prob {
   int32_t softplus;  // delta = softplus(dt + bias)
   int32_t Q;         // chunk size
   int32_t packed;
+  int32_t flags;     // SSD_FLAG_* bits
   int64_t nck;       // chunk slots
   ChunkMap map;      // device view of the chunk layout (table pointers set when packed)
 };
@@ -34,15 +35,13 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
 hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
                                 const float* init, float* passed, float* final_states, int reverse,
                                 hipStream_t st);
-hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st);
+// CBt (bf16 only, may be null): also store the transpose of every lower tile.
+hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st,
+                            void* CBt = nullptr);
 hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const void* CB,
                              const float* delta, const float* acs, const float* passed,
                              const float* D, void* out, hipStream_t st);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
-
-// CBt[j][i] = B_j . C_i on the upper tile triangle (bf16 only; the backward's
-// row-j kernels read it with 16-byte loads).
-hipError_t launch_bmm_chunk_t(const Prob& p, const void* B, const void* C, void* CBt, hipStream_t st);
 
 // Everything the backward chunk kernels read and write.
 struct BwdArgs {

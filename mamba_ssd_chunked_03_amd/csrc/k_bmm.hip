@@ -7,21 +7,26 @@
 // contiguous in memory, so MFMA fragments are read straight from global memory
 // (16 bytes per lane) without LDS staging.  Tiles above the diagonal are never
 // computed; inside diagonal tiles the upper part is written but unspecified.
-// The backward also needs the transpose, CBt[j][i] = B_j . C_i for i >= j
-// (upper triangle): the same kernel with the operands swapped and the tile
-// walk mirrored.
+// The backward also reads the transpose, CBt[j][i] = CB[i][j]: when asked, each
+// lower tile is stored a second time, transposed, from the same LDS copy.
 //
 // fp32 path: one thread per (i, j <= i), plain dot product.
 #include "internal.hpp"
 
 namespace ssd {
 
-// out[a][b] = R_a . S_b on the lower (UPPER = false) or upper tile triangle.
-template <int N, bool UPPER>
+// out[a][b] = R_a . S_b on the lower tile triangle.
+// Each wavefront's 64x64 tile goes through LDS so every store is a 16-byte row
+// piece; with DUAL the transposed tile is stored too (outT[b][a]), which the
+// backward reads when the forward keeps its intermediates.
+template <int N, bool DUAL>
 __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
                                                              const uint16_t* __restrict__ Sm,
                                                              const uint16_t* __restrict__ Rm,
-                                                             uint16_t* __restrict__ CB) {
+                                                             uint16_t* __restrict__ CB,
+                                                             uint16_t* __restrict__ CBt) {
+  constexpr int LT = 64 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t tls[4][64 * LT];
   const int k = blockIdx.x, g = blockIdx.y;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
@@ -34,12 +39,13 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
   const uint16_t* cb0 = Rm + (int64_t)ci.start * row + (int64_t)g * N;
   const uint16_t* bb0 = Sm + (int64_t)ci.start * row + (int64_t)g * N;
   uint16_t* out = CB + ((int64_t)k * G + g) * Q * Q;
+  uint16_t* tl = tls[w];
   for (int tile = w; tile < ntiles; tile += 4) {
     int lo = 0;
     while ((lo + 1) * (lo + 2) / 2 <= tile) ++lo;
     const int hi = tile - lo * (lo + 1) / 2;  // hi <= lo
-    const int ti = UPPER ? hi : lo, tj = UPPER ? lo : hi;
-    if (lo * 64 >= ci.len) continue;  // rows / columns past the chunk's end are never read
+    const int ti = lo, tj = hi;
+    if (ti * 64 >= ci.len) continue;  // rows past the chunk's end are never read
     f32x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -66,11 +72,21 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int i = ti * 64 + a * 16 + q * 4 + rr;
-          const int j = tj * 64 + b * 16 + r;
-          out[(int64_t)i * Q + j] = f2bf(acc[a][b][rr]);
-        }
+        for (int rr = 0; rr < 4; ++rr) tl[(a * 16 + q * 4 + rr) * LT + b * 16 + r] = f2bf(acc[a][b][rr]);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int e = lane + 64 * c, rw = e >> 3, c8 = e & 7;
+      *(u32x4*)(out + (int64_t)(ti * 64 + rw) * Q + tj * 64 + c8 * 8) = *(const u32x4*)(tl + rw * LT + c8 * 8);
+      if (DUAL) {
+        u32x4 t;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          t[d] = (uint32_t)tl[(c8 * 8 + 2 * d) * LT + rw] | ((uint32_t)tl[(c8 * 8 + 2 * d + 1) * LT + rw] << 16);
+        *(u32x4*)(CBt + ((int64_t)k * G + g) * Q * Q + (int64_t)(tj * 64 + rw) * Q + ti * 64 + c8 * 8) = t;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -92,22 +108,8 @@ __global__ __launch_bounds__(256) void bmm_chunk_f32_kernel(ChunkMap m, int G, i
   CB[(((int64_t)k * G + g) * Q + i) * Q + j] = acc;
 }
 
-hipError_t launch_bmm_chunk_t(const Prob& p, const void* B, const void* C, void* CBt, hipStream_t st) {
-  if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) return hipErrorInvalidValue;  // the fp32 backward reads CB directly
-  dim3 grid((unsigned)p.nck, p.G);
-#define SSD_BMMT_CASE(NN)                                                                      \
-  if (p.N == NN) {                                                                             \
-    hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN, true>), grid, dim3(256), 0, st, p.map, p.G,  \
-                       (const uint16_t*)C, (const uint16_t*)B, (uint16_t*)CBt);                \
-    return hipGetLastError();                                                                  \
-  }
-  SSD_BMMT_CASE(32) SSD_BMMT_CASE(64) SSD_BMMT_CASE(128)
-#undef SSD_BMMT_CASE
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st) {
+hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st,
+                            void* CBt) {
   if (p.nck == 0) return hipSuccess;
   if (p.io == 0) {
     dim3 grid((unsigned)p.nck, p.G, (p.Q * p.Q + 255) / 256);
@@ -118,8 +120,14 @@ hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* C
   dim3 grid((unsigned)p.nck, p.G);
 #define SSD_BMM_CASE(NN)                                                                   \
   if (p.N == NN) {                                                                         \
-    hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN, false>), grid, dim3(256), 0, st, p.map,  \
-                       p.G, (const uint16_t*)B, (const uint16_t*)C, (uint16_t*)CB);        \
+    if (CBt)                                                                               \
+      hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN, true>), grid, dim3(256), 0, st,  \
+                         p.map, p.G, (const uint16_t*)B, (const uint16_t*)C, (uint16_t*)CB, \
+                         (uint16_t*)CBt);                                                  \
+    else                                                                                   \
+      hipLaunchKernelGGL((bmm_chunk_bf16_kernel<NN, false>), grid, dim3(256), 0, st, \
+                         p.map, p.G, (const uint16_t*)B, (const uint16_t*)C, (uint16_t*)CB, \
+                         nullptr);                                                         \
     return hipGetLastError();                                                              \
   }
   SSD_BMM_CASE(32) SSD_BMM_CASE(64) SSD_BMM_CASE(128)

@@ -38,7 +38,7 @@ constexpr int QMAX = 256;
 constexpr int kDxWaves = 8;
 
 template <int P, int N>
-__global__ __launch_bounds__(kDxWaves * 64) void bwd_dx_bf16_kernel(
+__global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ DY, const uint16_t* __restrict__ CBt,
     const float* __restrict__ delta, const float* __restrict__ acs,
@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kDxWaves * 64) void bwd_dx_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t dts[P * LDT];
   __shared__ float sa[QMAX], sd[QMAX];
   __shared__ float red[3][kDxWaves];
+  __shared__ __attribute__((aligned(16))) float wt[QMAX / 32][QMAX];  // column factors per anchor
 
   const int k = blockIdx.x, h = blockIdx.y;
   const ChunkInfo ci = chunk_info(m, k);
@@ -104,6 +105,12 @@ __global__ __launch_bounds__(kDxWaves * 64) void bwd_dx_bf16_kernel(
   }
   dot = wave_sum(dot);
   __syncthreads();
+  // anchor e = 32b + 31: column factors 2^(acs_i - acs_e) for e < i < len
+  for (int idx = tid; idx < (Q / 32) * Q; idx += kDxWaves * 64) {
+    const int bb2 = idx / Q, i = idx % Q, e = 32 * bb2 + 31;
+    wt[bb2][i] = (i > e && i < len) ? exp2_fast(sa[i] - sa[e]) : 0.f;
+  }
+  __syncthreads();
 
   const float Dh = D ? D[h] : 0.f;
   const float a_last = sa[len - 1];
@@ -118,6 +125,11 @@ __global__ __launch_bounds__(kDxWaves * 64) void bwd_dx_bf16_kernel(
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int jrow = j0 + r;  // A-fragment row of this lane
+    const int cb0 = j0 / 32;                       // 32-token block holding this row block
+    const int e = 32 * cb0 + 31;                   // anchor: j <= e < i for later blocks
+    const int s_end = (len + 31) / 32;
+    const bool has_off = cb0 + 1 < s_end;
+    const float ae = has_off ? sa[e] : 0.f;
     // state part: sum_n B_j[n] dT[p][n]
 #pragma unroll
     for (int kk = 0; kk < N; kk += 32) {
@@ -136,40 +148,68 @@ __global__ __launch_bounds__(kDxWaves * 64) void bwd_dx_bf16_kernel(
       xs[rr] = 0.f;
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp) {
-        acc[tp][rr] *= wj;
         xv[tp][rr] = (j < len) ? bf2f(xb[(int64_t)j * xrow + tp * 16 + r]) : 0.f;
         xs[rr] += xv[tp][rr] * acc[tp][rr];
       }
+      xs[rr] *= wj;                               // x_j . (w_j dT B_j)
+      if (!has_off) {
+#pragma unroll
+        for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= wj;
+      }
     }
-    // intra part: sum_{i>=j} CBt[j][i] 2^(acs_i - acs_j) dy_i; the row block's
-    // CBt fragments are all loaded first (one memory latency)
-    const float aj = sa[min(jrow, Q - 1)];
-    const int s_lo = j0 / 32, s_hi = (len + 31) / 32;
-    u32x4 cbf[QMAX / 32];
+    if (has_off) {
+      // later blocks through the anchor: acc = 2^(acs_last - acs_e) state
+      //   + sum_i CBt[j][i] 2^(acs_i - acs_e) dy_i, then rows * 2^(acs_e - acs_j)
+      const float s0 = exp2_fast(a_last - ae);
 #pragma unroll
-    for (int sx = 0; sx < QMAX / 32; ++sx)
-      cbf[sx] = (jrow < len && sx >= s_lo && sx < s_hi)
-                    ? *(const u32x4*)(cbt + (int64_t)jrow * Q + sx * 32 + q * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int sx = 0; sx < QMAX / 32; ++sx) {
-      if (sx >= s_lo && sx < s_hi) {
-        const int kk = sx * 32;
+      for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= s0;
+      const float* wrow = &wt[cb0][0];
+      u32x4 cvn = (jrow < len) ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (cb0 + 1) * 32 + q * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+      for (int sx = cb0 + 1; sx < s_end; ++sx) {
+        const u32x4 cv = cvn;
+        if (sx + 1 < s_end)  // one step of lookahead
+          cvn = (jrow < len) ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (sx + 1) * 32 + q * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+        const float4 f0 = *(const float4*)(wrow + sx * 32 + q * 8);
+        const float4 f1 = *(const float4*)(wrow + sx * 32 + q * 8 + 4);
         u32x4 av;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int i0 = kk + q * 8 + 2 * d;
-          float v0 = bf_lo(cbf[sx][d]) * exp2_fast(sa[i0] - aj);
-          float v1 = bf_hi(cbf[sx][d]) * exp2_fast(sa[i0 + 1] - aj);
-          v0 = (i0 >= jrow && i0 < len) ? v0 : 0.f;
-          v1 = (i0 + 1 >= jrow && i0 + 1 < len) ? v1 : 0.f;
-          av[d] = pack_bf2(v0, v1);
-        }
+        av[0] = pack_bf2(bf_lo(cv[0]) * f0.x, bf_hi(cv[0]) * f0.y);
+        av[1] = pack_bf2(bf_lo(cv[1]) * f0.z, bf_hi(cv[1]) * f0.w);
+        av[2] = pack_bf2(bf_lo(cv[2]) * f1.x, bf_hi(cv[2]) * f1.y);
+        av[3] = pack_bf2(bf_lo(cv[3]) * f1.z, bf_hi(cv[3]) * f1.w);
         const bf16x8 a = as_bf16x8(av);
 #pragma unroll
         for (int tp = 0; tp < P / 16; ++tp)
-          acc[tp] = mfma_bf16(a, frag_kmajor(dyt + kk * LDY + tp * 16, LDY, lane), acc[tp]);
+          acc[tp] = mfma_bf16(a, frag_kmajor(dyt + sx * 32 * LDY + tp * 16, LDY, lane), acc[tp]);
       }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int j = j0 + q * 4 + rr;
+        const float u = (j < len) ? exp2_fast(ae - sa[j]) : 0.f;
+#pragma unroll
+        for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= u;
+      }
+    }
+    // the diagonal block, one exp per element: CBt[j][i] 2^(acs_i - acs_j), j <= i < len
+    {
+      const float aj = sa[min(jrow, Q - 1)];
+      const u32x4 cv = (jrow < len) ? *(const u32x4*)(cbt + (int64_t)jrow * Q + cb0 * 32 + q * 8)
+                                    : u32x4{0u, 0u, 0u, 0u};
+      u32x4 av;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int i0 = cb0 * 32 + q * 8 + 2 * d;
+        float v0 = bf_lo(cv[d]) * exp2_fast(sa[i0] - aj);
+        float v1 = bf_hi(cv[d]) * exp2_fast(sa[i0 + 1] - aj);
+        v0 = (i0 >= jrow && i0 < len) ? v0 : 0.f;
+        v1 = (i0 + 1 >= jrow && i0 + 1 < len) ? v1 : 0.f;
+        av[d] = pack_bf2(v0, v1);
+      }
+      const bf16x8 a = as_bf16x8(av);
+#pragma unroll
+      for (int tp = 0; tp < P / 16; ++tp)
+        acc[tp] = mfma_bf16(a, frag_kmajor(dyt + cb0 * 32 * LDY + tp * 16, LDY, lane), acc[tp]);
     }
     // per-row dots and the store
     float xt[4], dxx[4];

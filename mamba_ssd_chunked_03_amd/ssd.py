@@ -21,7 +21,9 @@ _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "nseq",
-                 "io_dtype", "dt_softplus")]
+                 "io_dtype", "dt_softplus", "flags")]
+
+FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED = 1, 2
 
 
 _SIGS = {
@@ -97,7 +99,7 @@ def _f32(t, name):
         raise ValueError("%s must be float32" % name)
 
 
-def problem(x, B, cu_seqlens=None, dt_softplus=True):
+def problem(x, B, cu_seqlens=None, dt_softplus=True, flags=0):
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = B.shape[2], B.shape[3]
     io = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
@@ -106,7 +108,8 @@ def problem(x, B, cu_seqlens=None, dt_softplus=True):
     if B.dtype != x.dtype:
         raise ValueError("B, C must have x's dtype")
     nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    return Problem(batch, seqlen, nheads, headdim, dstate, ngroups, nseq, io, int(bool(dt_softplus)))
+    return Problem(batch, seqlen, nheads, headdim, dstate, ngroups, nseq, io, int(bool(dt_softplus)),
+                   int(flags))
 
 
 def _stream(dev):
@@ -122,17 +125,24 @@ def num_chunks(prob, chunk_size, packed):
 
 
 def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
-        dt_softplus=True, workspace=None, out=None, final=None):
-    """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h."""
+        dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False):
+    """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h.
+
+    save_for_backward: keep the intermediates in ``workspace`` (which must hold
+    bwd_workspace_bytes) so that bwd(..., workspace=that, from_saved=True) skips
+    the recompute."""
     dev = _dev(x, dt, A, B, C, D, dt_bias, init, cu_seqlens, workspace, out, final)
     for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (dt_bias, "dt_bias"), (init, "init")):
         _f32(t, n)
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
-    prob = problem(x, B, cu_seqlens, dt_softplus)
+    prob = problem(x, B, cu_seqlens, dt_softplus, FLAG_SAVE_FOR_BWD if save_for_backward else 0)
     L = lib()
     packed = int(cu_seqlens is not None)
-    need = L.ssd_fwd_workspace_bytes(ctypes.byref(prob), chunk_size, packed)
+    if save_for_backward:
+        need = L.ssd_bwd_workspace_bytes(ctypes.byref(prob), chunk_size, packed)
+    else:
+        need = L.ssd_fwd_workspace_bytes(ctypes.byref(prob), chunk_size, packed)
     if workspace is None:
         workspace = _ws(need, dev)
     if out is None:
@@ -147,10 +157,15 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
 
 
 def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
-        chunk_size=256, dt_softplus=True, workspace=None):
-    """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors)."""
+        chunk_size=256, dt_softplus=True, workspace=None, from_saved=False):
+    """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors).
+
+    from_saved: ``workspace`` holds the intermediates of a save_for_backward
+    fwd call on the same inputs; the recompute is skipped."""
     dev = _dev(x, dt, A, B, C, dout, D, dt_bias, init, d_final, cu_seqlens, workspace)
-    prob = problem(x, B, cu_seqlens, dt_softplus)
+    if from_saved and workspace is None:
+        raise ValueError("from_saved needs the forward's workspace")
+    prob = problem(x, B, cu_seqlens, dt_softplus, FLAG_FROM_SAVED if from_saved else 0)
     L = lib()
     packed = int(cu_seqlens is not None)
     need = L.ssd_bwd_workspace_bytes(ctypes.byref(prob), chunk_size, packed)

@@ -39,7 +39,7 @@ def test_header_and_binding_agree(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.ssd_abi_version() == 1
+    assert L.ssd_abi_version() == 2
     for s in range(8):
         assert len(L.ssd_status_string(s)) > 0
     assert L.ssd_status_string(99) == b"unknown status"
@@ -47,7 +47,7 @@ def test_abi_version_and_strings(L):
 
 def prob(**kw):
     d = dict(batch=2, seqlen=1000, nheads=8, headdim=64, dstate=128, ngroups=2, nseq=0,
-             io_dtype=1, dt_softplus=1)
+             io_dtype=1, dt_softplus=1, flags=0)
     d.update(kw)
     return ssd.Problem(*[d[n] for n, _ in ssd.Problem._fields_])
 
@@ -130,6 +130,13 @@ def test_workspace(L):
     assert fwd_status(L, p, ws_bytes=need - 1) == WS
     assert fwd_status(L, p, ws=None) == WS
     assert L.ssd_bwd_workspace_bytes(ctypes.byref(p), 256, 0) > need
+
+
+def test_flags(L):
+    assert fwd_status(L, prob(flags=4)) == UNSUP
+    p = prob(flags=1)  # keeping the forward's intermediates needs the backward-sized workspace
+    fwd_need = L.ssd_fwd_workspace_bytes(ctypes.byref(p), 256, 0)
+    assert fwd_status(L, p, ws_bytes=fwd_need) == WS
 
 
 def test_packed_requires_batch_one(L):

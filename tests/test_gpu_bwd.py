@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import gpu_bwd, has_gpu, normwise, np64, oracle_args
+from helpers import gpu_bwd, gpu_fwd, has_gpu, normwise, np64, oracle_args, to_dev
 from mamba_ssd_chunked_03_amd import inputs
 from oracle import recurrence
 
@@ -113,6 +113,32 @@ def test_bwd_deterministic():
     g2 = gpu_bwd(ssd, inp, 256)
     for k in KEYS:
         assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_saved_context_matches_recompute(packed):
+    # a forward that keeps its intermediates + a backward that reuses them gives
+    # bit-identical outputs and gradients to the recomputing pair
+    if packed:
+        lengths = [300, 0, 257, 64]
+        inp = inputs.make_inputs(1, sum(lengths), 4, 64, 128, 2, io="bf16", init="randn", bwd=True,
+                                 d_final=True, lengths=lengths, seed=60)
+    else:
+        inp = inputs.make_inputs(2, 700, 4, 64, 128, 2, io="bf16", init="randn", bwd=True,
+                                 d_final=True, seed=60)
+    d = to_dev(inp)
+    y0, f0 = gpu_fwd(ssd, inp, 256)
+    g0 = gpu_bwd(ssd, inp, 256)
+    prob = ssd.problem(d["x"], d["B"], d["cu_seqlens"])
+    import ctypes
+    ws = torch.empty(ssd.lib().ssd_bwd_workspace_bytes(ctypes.byref(prob), 256, int(packed)),
+                     dtype=torch.uint8, device="cuda")
+    y1, f1 = gpu_fwd(ssd, inp, 256, workspace=ws, save_for_backward=True)
+    g1 = gpu_bwd(ssd, inp, 256, workspace=ws, from_saved=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    for k in KEYS:
+        assert torch.equal(g0[k], g1[k]), k
 
 
 def test_bwd_full_size_sampled_heads():
