@@ -112,8 +112,9 @@ int64_t ssd_num_chunks(const ssd_problem* problem, int32_t chunk_size, int32_t p
 
 /* Workspace sizes in bytes (0 for an invalid problem).  `packed` = 1 when
  * cu_seqlens will be passed.  The forward workspace holds the chunk table,
- * delta, the within-chunk cumsum, the chunk states, the passed states and
- * C.B^T per chunk; the backward one adds the adjoint states. */
+ * delta, the within-chunk cumsum, the chunk states (fp32), the passed states
+ * (bf16 with bf16 io, where they only feed bf16 matrix products; fp32
+ * otherwise) and C.B^T per chunk; the backward one adds the adjoint states. */
 size_t ssd_fwd_workspace_bytes(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 size_t ssd_bwd_workspace_bytes(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 /* Workspace for the ssd_stage_* entries (the chunk table only). */

@@ -68,6 +68,9 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
 }
 
 inline size_t esize(const Prob& p) { return p.io == SSD_BF16 ? 2 : 4; }
+// Passed states H_c and their adjoints dE_c: every consumer on the bf16 path
+// feeds them to bf16 matrix cores, so they are stored in bf16 there.
+inline size_t state_esize(const Prob& p) { return p.io == SSD_BF16 ? 2 : 4; }
 
 // Forward workspace layout (byte offsets, each 256-aligned).
 struct FwdLayout {
@@ -83,7 +86,7 @@ FwdLayout fwd_layout(const Prob& p) {
   l.acs = o;     o += up(nck * H * p.Q * 4);
   l.decay = o;   o += up(nck * H * 4);
   l.T = o;       o += up(nck * H * st * 4);
-  l.Hp = o;      o += up(nck * H * st * 4);
+  l.Hp = o;      o += up(nck * H * st * state_esize(p));
   l.CB = o;      o += up(nck * (size_t)p.G * p.Q * p.Q * esize(p));
   l.end = o;
   return l;
@@ -105,7 +108,7 @@ BwdLayout bwd_layout(const Prob& p) {
   l.Rp = o;   o += up(tiles);
   l.Kp = o;   o += up(tiles);
   l.U = o;    o += up(nck * H * st * 4);
-  l.dE = o;   o += up(nck * H * st * 4);
+  l.dE = o;   o += up(nck * H * st * state_esize(p));
   l.ddd = o;  o += up(nck * H * p.Q * 4);
   l.Ks = o;   o += up(nck * H * p.Q * 4);
   l.rR = o;   o += up(nck * H * p.Q * 4);
@@ -216,14 +219,15 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   float* acs = (float*)(ws + l.acs);
   float* decay = (float*)(ws + l.decay);
   float* T = (float*)(ws + l.T);
-  float* Hp = (float*)(ws + l.Hp);
+  void* Hp = ws + l.Hp;
+  const int hb = p.io == SSD_BF16;
   void* CB = ws + l.CB;
   SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
   SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
-  SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, final_states, 0, st));
+  SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
   void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
   SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
-  SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, D, out, st));
+  SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
   return SSD_OK;
 }
 
@@ -253,20 +257,21 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   float* acs = (float*)(ws + l.f.acs);
   float* decay = (float*)(ws + l.f.decay);
   float* T = (float*)(ws + l.f.T);
-  float* Hp = (float*)(ws + l.f.Hp);
+  void* Hp = ws + l.f.Hp;
+  const int hb = p.io == SSD_BF16;
   void* CB = ws + l.f.CB;
   void* CBt = ws + l.CBt;
   float* U = (float*)(ws + l.U);
-  float* dE = (float*)(ws + l.dE);
+  void* dE = ws + l.dE;
   if (!(p.flags & SSD_FLAG_FROM_SAVED)) {  // forward intermediates, recomputed
     SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
     SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
-    SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, nullptr, 0, st));
+    SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, nullptr, 0, st));
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
   }
   // adjoint of the state carried into each chunk, then the reverse scan
   SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
-  SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, d_init_states, 1, st));
+  SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
   BwdArgs a;
   a.x = x; a.B = B; a.C = C; a.dout = dout;
   a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.D = D;
@@ -336,7 +341,7 @@ ssd_status ssd_stage_state_passing(const ssd_problem* pr, const float* states,
   hipStream_t st = (hipStream_t)stream;
   s = setup_map(p, cu_seqlens, (char*)workspace, st);
   if (s != SSD_OK) return s;
-  SSD_TRY(launch_state_passing(p, states, chunk_decay, init_states, passed, final_states, 0, st));
+  SSD_TRY(launch_state_passing(p, states, chunk_decay, init_states, passed, 0, final_states, 0, st));
   return SSD_OK;
 }
 
@@ -372,7 +377,7 @@ ssd_status ssd_stage_chunk_scan(const ssd_problem* pr, const void* x, const void
   hipStream_t st = (hipStream_t)stream;
   s = setup_map(p, cu_seqlens, (char*)workspace, st);
   if (s != SSD_OK) return s;
-  SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, passed, D, out, st));
+  SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, passed, 0, D, out, st));
   return SSD_OK;
 }
 

@@ -134,6 +134,18 @@ __device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const fl
   }
 }
 
+// bf16 P x N state (row-major) -> bf16 LDS [p][n] with row stride ld.
+template <int P, int N, int NT = 256>
+__device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const uint16_t* src, int tid) {
+  stage_rows<P, N, NT>(dst, ld, src, N, P, tid);
+}
+
+// Four consecutive state elements to global memory as fp32 or bf16.
+__device__ __forceinline__ void store4(float* dst, float4 v) { *(float4*)dst = v; }
+__device__ __forceinline__ void store4(uint16_t* dst, float4 v) {
+  *(uint2*)dst = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+}
+
 // ------------------------------------------------------------------ DPP ----
 // DPP controls (GFX9 encoding).
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;

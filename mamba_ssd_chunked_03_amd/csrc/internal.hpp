@@ -32,22 +32,25 @@ hipError_t launch_chunk_cumsum(const Prob& p, const float* dt, const float* dt_b
                                float* delta, float* acs, float* decay, hipStream_t st);
 hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,
                               const float* acs, float* out, int mode, hipStream_t st);
+// passed: fp32, or bf16 when passed_bf16 (the carry and final_states stay fp32)
 hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
-                                const float* init, float* passed, float* final_states, int reverse,
-                                hipStream_t st);
+                                const float* init, void* passed, int passed_bf16,
+                                float* final_states, int reverse, hipStream_t st);
 // CBt (bf16 only, may be null): also store the transpose of every lower tile.
 hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st,
                             void* CBt = nullptr);
+// passed: fp32, or bf16 when passed_bf16 (bf16 io only)
 hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const void* CB,
-                             const float* delta, const float* acs, const float* passed,
-                             const float* D, void* out, hipStream_t st);
+                             const float* delta, const float* acs, const void* passed,
+                             int passed_bf16, const float* D, void* out, hipStream_t st);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 
 // Everything the backward chunk kernels read and write.
 struct BwdArgs {
   const void *x, *B, *C, *dout;
   const float *dt, *dt_bias, *A, *D;
-  const float *delta, *acs, *decay, *Hp, *dE;
+  const float *delta, *acs, *decay;
+  const void *Hp, *dE;  // per (chunk, head) P x N: bf16 on the bf16 path, fp32 otherwise
   const void *CB, *CBt;
   void *dCBg, *dCBgT;  // head-summed dCB per (chunk, group), both orientations
   float *Rp, *Kp;      // per (chunk, head, 64-token tile, token): R and K partials

@@ -2,7 +2,8 @@
 //
 // Per chunk c, head h (group g), tokens i, j of the chunk, with
 //   L_ij = 2^(acs_i - acs_j) (i >= j), w_j = 2^(acs_last - acs_j),
-//   CB_ij = C_i . B_j, dT = dE_c (from the reverse state-passing scan), H = H_c:
+//   CB_ij = C_i . B_j, dT = dE_c (from the reverse state-passing scan), H = H_c
+//   (both stored in bf16 on the bf16 path, fp32 on the fp32 path):
 //   dx_j  = delta_j [ sum_{i>=j} CB_ij L_ij dy_i + w_j dT B_j ] + D dy_j
 //   dC_i  = sum_h [ 2^acs_i H^T dy_i + sum_{j<=i} dCB_ij B_j ]
 //   dB_j  = sum_h [ sum_{i>=j} dCB_ij C_i + w_j delta_j dT^T x_j ]
@@ -42,9 +43,10 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ DY, const uint16_t* __restrict__ CBt,
     const float* __restrict__ delta, const float* __restrict__ acs,
-    const float* __restrict__ decay, const float* __restrict__ dE, const float* __restrict__ Hs,
-    const float* __restrict__ D, uint16_t* __restrict__ DX, float* __restrict__ ddd,
-    float* __restrict__ Ks, float* __restrict__ last_term, float* __restrict__ dDp) {
+    const float* __restrict__ decay, const uint16_t* __restrict__ dE,
+    const uint16_t* __restrict__ Hs, const float* __restrict__ D, uint16_t* __restrict__ DX,
+    float* __restrict__ ddd, float* __restrict__ Ks, float* __restrict__ last_term,
+    float* __restrict__ dDp) {
   constexpr int LDY = P + 16;  // dy tile row stride (bf16): odd multiple of 32 bytes
   constexpr int LDT = N + 8;   // dT tile row stride
   __shared__ __attribute__((aligned(16))) uint16_t dyt[QMAX * LDY];
@@ -79,27 +81,27 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   }
   // dy tile, token-major (rows past the chunk's end are zero)
   stage_rows<QMAX, P, kDxWaves * 64>(dyt, LDY, dyb, xrow, len, tid);
-  // dT = dE_c as bf16 [p][n]; alpha <dE, H> in fp32 on the way (loads first)
+  // dT = dE_c (bf16) into LDS [p][n]; alpha <dE, H> in fp32 on the way (loads first)
   float dot = 0.f;
   {
-    constexpr int NT = kDxWaves * 64, NC = (P * N / 4 + NT - 1) / NT;
-    const float* de = dE + kh * (int64_t)(P * N);
-    const float* hh = Hs + kh * (int64_t)(P * N);
-    float4 ta[NC], tb[NC];
+    constexpr int NT = kDxWaves * 64, NC = (P * N / 8 + NT - 1) / NT;
+    const uint16_t* de = dE + kh * (int64_t)(P * N);
+    const uint16_t* hh = Hs + kh * (int64_t)(P * N);
+    u32x4 ta[NC], tb[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int e = (tid + c * NT) * 4;
-      ta[c] = (e < P * N) ? *(const float4*)(de + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-      tb[c] = (e < P * N) ? *(const float4*)(hh + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int e = (tid + c * NT) * 8;
+      ta[c] = (e < P * N) ? *(const u32x4*)(de + e) : u32x4{0u, 0u, 0u, 0u};
+      tb[c] = (e < P * N) ? *(const u32x4*)(hh + e) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int e = (tid + c * NT) * 4;
+      const int e = (tid + c * NT) * 8;
       if (e < P * N) {
-        dot += ta[c].x * tb[c].x + ta[c].y * tb[c].y + ta[c].z * tb[c].z + ta[c].w * tb[c].w;
-        uint32_t* dst = (uint32_t*)(dts + (e / N) * LDT + (e % N));
-        dst[0] = pack_bf2(ta[c].x, ta[c].y);
-        dst[1] = pack_bf2(ta[c].z, ta[c].w);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          dot += bf_lo(ta[c][d]) * bf_lo(tb[c][d]) + bf_hi(ta[c][d]) * bf_hi(tb[c][d]);
+        *(u32x4*)(dts + (e / N) * LDT + (e % N)) = ta[c];
       }
     }
   }
@@ -281,6 +283,7 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
   constexpr int LT = 64 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t stg[64 * LT];
   __shared__ float kred[8][4][64];
+  __shared__ float sv[8][192];  // per head of 8: acs rows | acs cols | delta cols
   const int Q = m.Q, T = Q / 64, NT = T * (T + 1) / 2;
   const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
   const int tile = lid % NT, k = lid / NT / G, g = (lid / NT) % G;
@@ -330,6 +333,19 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
+    if ((hh & 7) == 0) {
+      // acs of the tile's rows and columns and delta of its columns for the next
+      // 8 heads, so the head loop never waits on these scalars; the previous
+      // block's readers are done (the column reduction below ends in a barrier)
+      const int nh = min(8, hpg - hh);
+      for (int e = tid; e < nh * 192; e += 256) {
+        const int sl = e / 192, c = e % 192;
+        const int64_t khs = kh + sl;
+        const int t = (c < 64) ? ti * 64 + c : tj * 64 + (c % 64);
+        sv[sl][c] = (c < 128) ? acs[khs * Q + t] : delta[khs * Q + t];
+      }
+      __syncthreads();
+    }
     f32x4 dxb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -338,18 +354,17 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
       for (int kb = 0; kb < P / 32; ++kb) dxb[b] = mfma_bf16(as_bf16x8(ay[kb]), as_bf16x8(xf[b][kb]), dxb[b]);
     }
     if (hh + 1 < hpg) load_head(h + 1);  // in flight during this head's element-wise work
-    const float* ac = acs + kh * Q;
-    const float* dl = delta + kh * Q;
+    const float* svh = sv[hh & 7];
     float ai[4], aj[4], dj[4], Rl[4], Kl[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      ai[rr] = ac[min(i0 + q * 4 + rr, Q - 1)];
+      ai[rr] = svh[w * 16 + q * 4 + rr];
       Rl[rr] = 0.f;
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      aj[b] = ac[jt0 + b * 16 + r];
-      dj[b] = dl[jt0 + b * 16 + r];
+      aj[b] = svh[64 + b * 16 + r];
+      dj[b] = svh[128 + b * 16 + r];
       Kl[b] = 0.f;
     }
 #pragma unroll
@@ -415,7 +430,7 @@ template <int P, int N>
 __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ DY, const uint16_t* __restrict__ dCBg,
-    const float* __restrict__ acs, const float* __restrict__ Hs, uint16_t* __restrict__ dC,
+    const float* __restrict__ acs, const uint16_t* __restrict__ Hs, uint16_t* __restrict__ dC,
     float* __restrict__ rout) {
   constexpr int LDB = N + 16;  // odd multiple of 32 bytes for the transpose reads
   __shared__ __attribute__((aligned(16))) uint16_t bt[64 * LDB];
@@ -517,7 +532,7 @@ template <int P, int N>
 __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dCBgT, const float* __restrict__ delta,
-    const float* __restrict__ acs, const float* __restrict__ dE, uint16_t* __restrict__ dB) {
+    const float* __restrict__ acs, const uint16_t* __restrict__ dE, uint16_t* __restrict__ dB) {
   constexpr int LDB = N + 16;
   __shared__ __attribute__((aligned(16))) uint16_t ct[64 * LDB];
   __shared__ __attribute__((aligned(16))) uint16_t dtt[P * LDB];
@@ -842,7 +857,7 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, hipStream_t st) {
   const int T = p.Q / 64;
   hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(kDxWaves * 64), 0, st, p.map,
                      p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B, (const uint16_t*)a.dout,
-                     (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, a.dE, a.Hp, a.D,
+                     (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, (const uint16_t*)a.dE, (const uint16_t*)a.Hp, a.D,
                      (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
   hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
                      dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
@@ -850,11 +865,11 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, hipStream_t st) {
                      (uint16_t*)a.dCBg, (uint16_t*)a.dCBgT, a.Rp, a.Kp);
   hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
-                     (const uint16_t*)a.dout, (const uint16_t*)a.dCBg, a.acs, a.Hp,
+                     (const uint16_t*)a.dout, (const uint16_t*)a.dCBg, a.acs, (const uint16_t*)a.Hp,
                      (uint16_t*)a.dC, a.rR);
   hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
-                     (const uint16_t*)a.dCBgT, a.delta, a.acs, a.dE, (uint16_t*)a.dB);
+                     (const uint16_t*)a.dCBgT, a.delta, a.acs, (const uint16_t*)a.dE, (uint16_t*)a.dB);
 }
 
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, hipStream_t st) {
@@ -862,17 +877,17 @@ hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, hipStream_t st) {
   if (p.io == 0) {
     hipLaunchKernelGGL(bwd_dx_f32_kernel, dim3((unsigned)p.nck, p.H), dim3(256), 0, st, p.map, p.H,
                        p.G, p.P, p.N, (const float*)a.x, (const float*)a.B, (const float*)a.dout,
-                       (const float*)a.CB, a.delta, a.acs, a.decay, a.dE, a.Hp, a.D, (float*)a.dx,
+                       (const float*)a.CB, a.delta, a.acs, a.decay, (const float*)a.dE, (const float*)a.Hp, a.D, (float*)a.dx,
                        a.ddd, a.Ks, a.last_term, a.dDp);
     hipLaunchKernelGGL(bwd_dc_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
                        dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
-                       (const float*)a.B, (const float*)a.dout, a.delta, a.acs, a.Hp, (float*)a.dC);
+                       (const float*)a.B, (const float*)a.dout, a.delta, a.acs, (const float*)a.Hp, (float*)a.dC);
     hipLaunchKernelGGL(bwd_rr_f32_kernel, dim3((unsigned)p.nck, p.H, (p.Q + 255) / 256), dim3(256), 0,
                        st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x, (const float*)a.C,
-                       (const float*)a.dout, (const float*)a.CB, a.delta, a.acs, a.Hp, a.rR);
+                       (const float*)a.dout, (const float*)a.CB, a.delta, a.acs, (const float*)a.Hp, a.rR);
     hipLaunchKernelGGL(bwd_db_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
                        dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
-                       (const float*)a.C, (const float*)a.dout, a.delta, a.acs, a.dE, (float*)a.dB);
+                       (const float*)a.C, (const float*)a.dout, a.delta, a.acs, (const float*)a.dE, (float*)a.dB);
     return hipGetLastError();
   }
 #define SSD_BWD_CASE(PP, NN) \

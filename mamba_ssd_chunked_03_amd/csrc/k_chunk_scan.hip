@@ -35,11 +35,12 @@ namespace ssd {
 
 constexpr int kScanWaves = 8;
 
-template <int P, int N>
+// HT: element type of the passed states (fp32, or bf16 from the fused forward)
+template <int P, int N, typename HT>
 __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ CB, const float* __restrict__ delta,
-    const float* __restrict__ acs, const float* __restrict__ Hs, const float* __restrict__ D,
+    const float* __restrict__ acs, const HT* __restrict__ Hs, const float* __restrict__ D,
     uint16_t* __restrict__ Y) {
   constexpr int QMAX = 256, LDX = P + 8, HLD = N + 8;
   __shared__ __attribute__((aligned(16))) uint16_t xs[QMAX * LDX];
@@ -197,26 +198,33 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(
 
 template <int P, int N>
 static void launch_scan_bf16(const Prob& p, const void* x, const void* C, const void* CB,
-                             const float* delta, const float* acs, const float* passed,
-                             const float* D, void* out, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_scan_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(kScanWaves * 64), 0, st,
-                     p.map, p.H, p.G, (const uint16_t*)x, (const uint16_t*)C, (const uint16_t*)CB,
-                     delta, acs, passed, D, (uint16_t*)out);
+                             const float* delta, const float* acs, const void* passed,
+                             int passed_bf16, const float* D, void* out, hipStream_t st) {
+  const dim3 grid((unsigned)p.nck, p.H), block(kScanWaves * 64);
+  if (passed_bf16)
+    hipLaunchKernelGGL((chunk_scan_bf16_kernel<P, N, uint16_t>), grid, block, 0, st, p.map, p.H,
+                       p.G, (const uint16_t*)x, (const uint16_t*)C, (const uint16_t*)CB, delta, acs,
+                       (const uint16_t*)passed, D, (uint16_t*)out);
+  else
+    hipLaunchKernelGGL((chunk_scan_bf16_kernel<P, N, float>), grid, block, 0, st, p.map, p.H, p.G,
+                       (const uint16_t*)x, (const uint16_t*)C, (const uint16_t*)CB, delta, acs,
+                       (const float*)passed, D, (uint16_t*)out);
 }
 
 hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const void* CB,
-                             const float* delta, const float* acs, const float* passed,
-                             const float* D, void* out, hipStream_t st) {
+                             const float* delta, const float* acs, const void* passed,
+                             int passed_bf16, const float* D, void* out, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
   if (p.io == 0) {
+    if (passed_bf16) return hipErrorInvalidValue;
     dim3 grid((unsigned)p.nck, p.H, (p.Q * p.P + 255) / 256);
     hipLaunchKernelGGL(chunk_scan_f32_kernel, grid, dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N,
-                       (const float*)x, (const float*)C, (const float*)CB, delta, acs, passed, D,
+                       (const float*)x, (const float*)C, (const float*)CB, delta, acs, (const float*)passed, D,
                        (float*)out);
     return hipGetLastError();
   }
 #define SSD_SCAN_CASE(PP, NN) \
-  if (p.P == PP && p.N == NN) { launch_scan_bf16<PP, NN>(p, x, C, CB, delta, acs, passed, D, out, st); return hipGetLastError(); }
+  if (p.P == PP && p.N == NN) { launch_scan_bf16<PP, NN>(p, x, C, CB, delta, acs, passed, passed_bf16, D, out, st); return hipGetLastError(); }
   SSD_SCAN_CASE(32, 32) SSD_SCAN_CASE(32, 64) SSD_SCAN_CASE(32, 128)
   SSD_SCAN_CASE(64, 32) SSD_SCAN_CASE(64, 64) SSD_SCAN_CASE(64, 128)
   SSD_SCAN_CASE(128, 32) SSD_SCAN_CASE(128, 64) SSD_SCAN_CASE(128, 128)

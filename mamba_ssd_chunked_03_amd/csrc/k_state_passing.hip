@@ -7,6 +7,9 @@
 //     (l1, b1) (+) (l2, b2) = (l1 + l2, 2^l2 * b1 + b2)
 // The forward output is H_c, the state entering chunk c (the exclusive prefix
 // seeded with the sequence's init state), and the final state E_last.  The
+// per-chunk outputs are stored in fp32 or, where every consumer feeds them to
+// bf16 matrix cores anyway, in bf16 (half the bytes); the carry itself and the
+// final state stay fp32.  The
 // backward runs the same scan over the chunks in reverse order (dE_c out,
 // d_final in, d_init out), replacing the sequential state-passing loop in both
 // directions (aitrends.kr/articles/109906, "Helion-based B200 kernel redesign").
@@ -29,12 +32,12 @@
 
 namespace ssd {
 
-template <int W, int S>
+template <int W, int S, typename OutT>
 __global__ __launch_bounds__(W * 64) void state_passing_kernel(ChunkMap m, int H, int PN,
                                                                const float* __restrict__ T,
                                                                const float* __restrict__ decay,
                                                                const float* __restrict__ init,
-                                                               float* __restrict__ Hout,
+                                                               OutT* __restrict__ Hout,
                                                                float* __restrict__ final_states,
                                                                int reverse) {
   __shared__ float4 sumB[W][64];  // segment summaries, b part
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(W * 64) void state_passing_kernel(ChunkMap m, int H
     for (int i = 0; i < S; ++i) {
       if (i < cnt) {
         const int c = reverse ? (c1 - 1 - (seg0 + i)) : (c0 + seg0 + i);
-        *(float4*)(Hout + (int64_t)c * cstride + (int64_t)h * hstride + pn) = E;
+        store4(Hout + (int64_t)c * cstride + (int64_t)h * hstride + pn, E);
         const float a = exp2_fast(lg[i]);
         E.x = a * E.x + tv[i].x;
         E.y = a * E.y + tv[i].y;
@@ -148,28 +151,33 @@ __global__ __launch_bounds__(W * 64) void state_passing_kernel(ChunkMap m, int H
 
 template <int W, int S>
 static void launch_sp(const Prob& p, dim3 grid, const float* states, const float* decay,
-                      const float* init, float* passed, float* final_states, int reverse,
-                      hipStream_t st) {
-  hipLaunchKernelGGL((state_passing_kernel<W, S>), grid, dim3(W * 64), 0, st, p.map, p.H,
-                     p.P * p.N, states, decay, init, passed, final_states, reverse);
+                      const float* init, void* passed, int passed_bf16, float* final_states,
+                      int reverse, hipStream_t st) {
+  if (passed_bf16)
+    hipLaunchKernelGGL((state_passing_kernel<W, S, uint16_t>), grid, dim3(W * 64), 0, st, p.map,
+                       p.H, p.P * p.N, states, decay, init, (uint16_t*)passed, final_states,
+                       reverse);
+  else
+    hipLaunchKernelGGL((state_passing_kernel<W, S, float>), grid, dim3(W * 64), 0, st, p.map, p.H,
+                       p.P * p.N, states, decay, init, (float*)passed, final_states, reverse);
 }
 
 hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
-                                const float* init, float* passed, float* final_states, int reverse,
-                                hipStream_t st) {
+                                const float* init, void* passed, int passed_bf16,
+                                float* final_states, int reverse, hipStream_t st) {
   const int PN = p.P * p.N;  // a multiple of 256 for every supported (P, N)
   dim3 grid(PN / 256, p.H, p.nseq);
   if (p.nseq == 0) return hipSuccess;
   // segment shape from the longest chunk run a sequence can have
   const int64_t ncs = p.packed ? p.nck : (p.nck / (p.B > 0 ? p.B : 1));
   if (ncs <= 8)
-    launch_sp<4, 2>(p, grid, states, decay, init, passed, final_states, reverse, st);
+    launch_sp<4, 2>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
   else if (ncs <= 32)
-    launch_sp<8, 4>(p, grid, states, decay, init, passed, final_states, reverse, st);
+    launch_sp<8, 4>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
   else if (ncs <= 64)
-    launch_sp<16, 4>(p, grid, states, decay, init, passed, final_states, reverse, st);
+    launch_sp<16, 4>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
   else
-    launch_sp<16, 8>(p, grid, states, decay, init, passed, final_states, reverse, st);
+    launch_sp<16, 8>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
   return hipGetLastError();
 }
 

@@ -153,14 +153,16 @@ def test_num_chunks(L):
 
 
 def test_workspace_bytes_layout(L):
-    # forward workspace = delta, acs (nck,H,Q) + decay (nck,H) + 2 state arrays
-    # (nck,H,P,N) fp32 + CB (nck,G,Q,Q) io dtype, each rounded up to 256 bytes
+    # forward workspace = delta, acs (nck,H,Q) + decay (nck,H) + chunk states
+    # (nck,H,P,N) fp32 + passed states (nck,H,P,N) in the io dtype + CB (nck,G,Q,Q)
+    # io dtype, each rounded up to 256 bytes
     up = lambda n: (n + 255) // 256 * 256
-    p = prob(batch=2, seqlen=8192, nheads=64, headdim=64, dstate=128, ngroups=8)
     nck = 64
-    exp = (2 * up(nck * 64 * 256 * 4) + up(nck * 64 * 4) + 2 * up(nck * 64 * 64 * 128 * 4)
-           + up(nck * 8 * 256 * 256 * 2))
-    assert L.ssd_fwd_workspace_bytes(ctypes.byref(p), 256, 0) == exp
+    for io, es in ((1, 2), (0, 4)):
+        p = prob(batch=2, seqlen=8192, nheads=64, headdim=64, dstate=128, ngroups=8, io_dtype=io)
+        exp = (2 * up(nck * 64 * 256 * 4) + up(nck * 64 * 4) + up(nck * 64 * 64 * 128 * 4)
+               + up(nck * 64 * 64 * 128 * es) + up(nck * 8 * 256 * 256 * es))
+        assert L.ssd_fwd_workspace_bytes(ctypes.byref(p), 256, 0) == exp, io
 
 
 def test_stage_validation(L):
