@@ -116,63 +116,63 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
 
   const float Dh = D ? D[h] : 0.f;
   const float a_last = sa[len - 1];
-  float s_sum = 0.f, dxx_sum = 0.f;  // lane r == 0 of each row group accumulates its rows
+  float s_sum = 0.f, dxx_sum = 0.f;  // lanes q == 0 accumulate their rows
   const int NB = Q / 16;
   for (int ii = 0; ii * kDxWaves < NB; ++ii) {
     const int rb = kDxWaves * ii + ((ii & 1) ? (kDxWaves - 1 - w) : w);
     if (rb >= NB) continue;  // chunk sizes with fewer row blocks than wavefronts
     const int j0 = rb * 16;
     if (j0 >= len) continue;
+    // Products are issued with the operands swapped, so each lane holds the
+    // transposed tile acc[tp][rr] = (dx bracket)[j0 + r][16 tp + 4 q + rr]: the
+    // lane owns row jrow, row factors are one value per lane, row dots reduce
+    // over the four lanes r, r+16, r+32, r+48, and stores are 8 bytes.
     f32x4 acc[P / 16];
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int jrow = j0 + r;  // A-fragment row of this lane
+    const int jrow = j0 + r;
+    const bool rowok = jrow < len;
     const int cb0 = j0 / 32;                       // 32-token block holding this row block
     const int e = 32 * cb0 + 31;                   // anchor: j <= e < i for later blocks
     const int s_end = (len + 31) / 32;
     const bool has_off = cb0 + 1 < s_end;
     const float ae = has_off ? sa[e] : 0.f;
+    const float aj = sa[jrow];                     // jrow < Q always
+    // this lane's x values, 4 adjacent per tp
+    uint2 xq[P / 16];
+#pragma unroll
+    for (int tp = 0; tp < P / 16; ++tp)
+      xq[tp] = rowok ? *(const uint2*)(xb + (int64_t)jrow * xrow + tp * 16 + q * 4) : make_uint2(0u, 0u);
     // state part: sum_n B_j[n] dT[p][n]
 #pragma unroll
     for (int kk = 0; kk < N; kk += 32) {
-      const bf16x8 a = as_bf16x8(jrow < len ? *(const u32x4*)(bb + (int64_t)jrow * brow + kk + q * 8)
-                                            : u32x4{0u, 0u, 0u, 0u});
+      const bf16x8 b = as_bf16x8(rowok ? *(const u32x4*)(bb + (int64_t)jrow * brow + kk + q * 8)
+                                       : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(a, as_bf16x8(*(const u32x4*)(dts + (tp * 16 + r) * LDT + kk + q * 8)), acc[tp]);
+        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(dts + (tp * 16 + r) * LDT + kk + q * 8)), b, acc[tp]);
     }
-    float xv[P / 16][4];
-    float xs[4];
+    const float wj = rowok ? exp2_fast(a_last - aj) : 0.f;
+    float xs = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int j = j0 + q * 4 + rr;
-      const float wj = (j < len) ? exp2_fast(a_last - sa[j]) : 0.f;
-      xs[rr] = 0.f;
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) {
-        xv[tp][rr] = (j < len) ? bf2f(xb[(int64_t)j * xrow + tp * 16 + r]) : 0.f;
-        xs[rr] += xv[tp][rr] * acc[tp][rr];
-      }
-      xs[rr] *= wj;                               // x_j . (w_j dT B_j)
-      if (!has_off) {
-#pragma unroll
-        for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= wj;
-      }
-    }
+    for (int tp = 0; tp < P / 16; ++tp)
+      xs += bf_lo(xq[tp].x) * acc[tp][0] + bf_hi(xq[tp].x) * acc[tp][1] +
+            bf_lo(xq[tp].y) * acc[tp][2] + bf_hi(xq[tp].y) * acc[tp][3];
+    xs *= wj;                                      // this lane's part of x_j . (w_j dT B_j)
     if (has_off) {
       // later blocks through the anchor: acc = 2^(acs_last - acs_e) state
-      //   + sum_i CBt[j][i] 2^(acs_i - acs_e) dy_i, then rows * 2^(acs_e - acs_j)
+      //   + sum_i CBt[j][i] 2^(acs_i - acs_e) dy_i, then * 2^(acs_e - acs_j)
       const float s0 = exp2_fast(a_last - ae);
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= s0;
       const float* wrow = &wt[cb0][0];
-      u32x4 cvn = (jrow < len) ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (cb0 + 1) * 32 + q * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+      u32x4 cvn = rowok ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (cb0 + 1) * 32 + q * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
       for (int sx = cb0 + 1; sx < s_end; ++sx) {
         const u32x4 cv = cvn;
         if (sx + 1 < s_end)  // one step of lookahead
-          cvn = (jrow < len) ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (sx + 1) * 32 + q * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+          cvn = rowok ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (sx + 1) * 32 + q * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
         const float4 f0 = *(const float4*)(wrow + sx * 32 + q * 8);
         const float4 f1 = *(const float4*)(wrow + sx * 32 + q * 8 + 4);
         u32x4 av;
@@ -183,21 +183,19 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
         const bf16x8 a = as_bf16x8(av);
 #pragma unroll
         for (int tp = 0; tp < P / 16; ++tp)
-          acc[tp] = mfma_bf16(a, frag_kmajor(dyt + sx * 32 * LDY + tp * 16, LDY, lane), acc[tp]);
+          acc[tp] = mfma_bf16(frag_kmajor(dyt + sx * 32 * LDY + tp * 16, LDY, lane), a, acc[tp]);
       }
+      const float u = rowok ? exp2_fast(ae - aj) : 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int j = j0 + q * 4 + rr;
-        const float u = (j < len) ? exp2_fast(ae - sa[j]) : 0.f;
+      for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= u;
+    } else {
 #pragma unroll
-        for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= u;
-      }
+      for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= wj;
     }
     // the diagonal block, one exp per element: CBt[j][i] 2^(acs_i - acs_j), j <= i < len
     {
-      const float aj = sa[min(jrow, Q - 1)];
-      const u32x4 cv = (jrow < len) ? *(const u32x4*)(cbt + (int64_t)jrow * Q + cb0 * 32 + q * 8)
-                                    : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 cv = rowok ? *(const u32x4*)(cbt + (int64_t)jrow * Q + cb0 * 32 + q * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
       u32x4 av;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -211,38 +209,35 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
       const bf16x8 a = as_bf16x8(av);
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(a, frag_kmajor(dyt + cb0 * 32 * LDY + tp * 16, LDY, lane), acc[tp]);
+        acc[tp] = mfma_bf16(frag_kmajor(dyt + cb0 * 32 * LDY + tp * 16, LDY, lane), a, acc[tp]);
     }
     // per-row dots and the store
-    float xt[4], dxx[4];
+    const float dj = rowok ? sd[jrow] : 0.f;
+    float xt = 0.f, dxx = 0.f;
+    uint16_t* dxrow = DX + (int64_t)(ci.start + jrow) * xrow + (int64_t)h * P;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int j = j0 + q * 4 + rr;
-      const float dj = (j < len) ? sd[j] : 0.f;
-      xt[rr] = 0.f;
-      dxx[rr] = 0.f;
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) {
-        const int p = tp * 16 + r;
-        const float dy = bf2f(dyt[min(j, Q - 1) * LDY + p]);
-        xt[rr] += xv[tp][rr] * acc[tp][rr];
-        dxx[rr] += xv[tp][rr] * dy;
-        if (j < len) DX[(int64_t)(ci.start + j) * xrow + (int64_t)h * P + p] = f2bf(dj * acc[tp][rr] + Dh * dy);
-      }
+    for (int tp = 0; tp < P / 16; ++tp) {
+      const int p = tp * 16 + q * 4;
+      const uint2 dq = *(const uint2*)(dyt + jrow * LDY + p);  // rows past the end are zero
+      const float x0 = bf_lo(xq[tp].x), x1 = bf_hi(xq[tp].x), x2 = bf_lo(xq[tp].y), x3 = bf_hi(xq[tp].y);
+      const float y0 = bf_lo(dq.x), y1 = bf_hi(dq.x), y2 = bf_lo(dq.y), y3 = bf_hi(dq.y);
+      xt += x0 * acc[tp][0] + x1 * acc[tp][1] + x2 * acc[tp][2] + x3 * acc[tp][3];
+      dxx += x0 * y0 + x1 * y1 + x2 * y2 + x3 * y3;
+      if (rowok)
+        *(uint2*)(dxrow + p) = make_uint2(pack_bf2(dj * acc[tp][0] + Dh * y0, dj * acc[tp][1] + Dh * y1),
+                                          pack_bf2(dj * acc[tp][2] + Dh * y2, dj * acc[tp][3] + Dh * y3));
     }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      xs[rr] = row_sum16(xs[rr]);
-      xt[rr] = row_sum16(xt[rr]);
-      dxx[rr] = row_sum16(dxx[rr]);
-      const int j = j0 + q * 4 + rr;
-      if (r == 0 && j < len) {
-        const float dj = sd[j];
-        ddd[kh * Q + j] = xt[rr];
-        Ks[kh * Q + j] = dj * xs[rr];  // s_j (K_j comes from bwd_dcb)
-        s_sum += dj * xs[rr];
-        dxx_sum += dxx[rr];
-      }
+    xs += __shfl_xor(xs, 16);
+    xs += __shfl_xor(xs, 32);
+    xt += __shfl_xor(xt, 16);
+    xt += __shfl_xor(xt, 32);
+    dxx += __shfl_xor(dxx, 16);
+    dxx += __shfl_xor(dxx, 32);
+    if (q == 0 && rowok) {
+      ddd[kh * Q + jrow] = xt;
+      Ks[kh * Q + jrow] = dj * xs;  // s_j (K_j comes from bwd_dcb)
+      s_sum += dj * xs;
+      dxx_sum += dxx;
     }
   }
   // fixed-order workgroup reductions: lanes (w, q) -> wave -> waves 0..3

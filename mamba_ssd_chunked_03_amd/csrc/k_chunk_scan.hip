@@ -13,6 +13,8 @@
 // delta.  Each wavefront owns 16-row blocks of the output in a snake order (w and
 // 15-w for eight waves) so the causal work is balanced.  Per row
 // block, all its C and CB fragments are loaded first (one memory latency).
+// Products are issued with A and B swapped, so every lane ends up owning one
+// output row (one row factor per lane, 8-byte stores).
 // The decay 2^(acs_i - acs_j) is factored through an anchor token e with
 // j <= e < i, 2^(acs_i - acs_e) * 2^(acs_e - acs_j), both factors <= 1 (acs never
 // increases), so nothing can overflow.  For a row block starting in the 32-token
@@ -86,14 +88,20 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     const bool rowok = irow < len;
     const int nb = i0 / 32;   // 32-token blocks strictly before the diagonal block
     const float ae = nb > 0 ? sa[32 * nb - 1] : 0.f;
-    u32x4 cf[N / 32], cbf[QMAX / 32];
+    // (the diagonal fragment has its own register: indexing the array with the
+    // run-time nb would become a select over every element)
+    u32x4 cf[N / 32], cbf[QMAX / 32], cbd;
 #pragma unroll
     for (int kb = 0; kb < N / 32; ++kb)
       cf[kb] = rowok ? *(const u32x4*)(cb + (int64_t)irow * crow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int sx = 0; sx < QMAX / 32; ++sx)
-      cbf[sx] = (rowok && sx <= nb) ? *(const u32x4*)(cbm + (int64_t)irow * Q + sx * 32 + q * 8)
-                                    : u32x4{0u, 0u, 0u, 0u};
+      cbf[sx] = (rowok && sx < nb) ? *(const u32x4*)(cbm + (int64_t)irow * Q + sx * 32 + q * 8)
+                                   : u32x4{0u, 0u, 0u, 0u};
+    cbd = rowok ? *(const u32x4*)(cbm + (int64_t)irow * Q + nb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    // The products are issued with the operands swapped, so each lane holds the
+    // transposed tile: acc[tp][rr] = y[i0 + r][16 tp + 4 q + rr].  A row factor
+    // is then one value per lane, and each lane's 4 outputs per tp are adjacent.
     f32x4 acc[P / 16];
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -102,8 +110,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     for (int kb = 0; kb < N / 32; ++kb)
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(as_bf16x8(cf[kb]),
-                            as_bf16x8(*(const u32x4*)(hs + (tp * 16 + r) * HLD + kb * 32 + q * 8)), acc[tp]);
+        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(hs + (tp * 16 + r) * HLD + kb * 32 + q * 8)),
+                            as_bf16x8(cf[kb]), acc[tp]);
     {
       const float s0 = exp2_fast(ae);
 #pragma unroll
@@ -124,16 +132,14 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
         const bf16x8 a = as_bf16x8(av);
 #pragma unroll
         for (int tp = 0; tp < P / 16; ++tp)
-          acc[tp] = mfma_bf16(a, frag_kmajor(xs + sx * 32 * LDX + tp * 16, LDX, lane), acc[tp]);
+          acc[tp] = mfma_bf16(frag_kmajor(xs + sx * 32 * LDX + tp * 16, LDX, lane), a, acc[tp]);
       }
     }
-    // 3. row factors 2^(acs_i - acs_e)
+    // 3. this lane's row factor 2^(acs_i - acs_e), which also turns 1.'s factor into 2^acs_i
+    {
+      const float u = rowok ? exp2_fast(sa[irow] - ae) : 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = i0 + q * 4 + rr;
-      const float u = (i < len) ? exp2_fast(sa[i] - ae) : 0.f;
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) acc[tp][rr] *= u;
+      for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= u;
     }
     // 4. the diagonal block, one exp per element
     {
@@ -142,8 +148,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int j0 = nb * 32 + q * 8 + 2 * d;
-        float v0 = bf_lo(cbf[nb][d]) * exp2_fast(ai - sa[j0]) * sd[j0];
-        float v1 = bf_hi(cbf[nb][d]) * exp2_fast(ai - sa[j0 + 1]) * sd[j0 + 1];
+        float v0 = bf_lo(cbd[d]) * exp2_fast(ai - sa[j0]) * sd[j0];
+        float v1 = bf_hi(cbd[d]) * exp2_fast(ai - sa[j0 + 1]) * sd[j0 + 1];
         v0 = (j0 <= irow) ? v0 : 0.f;
         v1 = (j0 + 1 <= irow) ? v1 : 0.f;
         av[d] = pack_bf2(v0, v1);
@@ -151,19 +157,20 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
       const bf16x8 a = as_bf16x8(av);
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(a, frag_kmajor(xs + nb * 32 * LDX + tp * 16, LDX, lane), acc[tp]);
+        acc[tp] = mfma_bf16(frag_kmajor(xs + nb * 32 * LDX + tp * 16, LDX, lane), a, acc[tp]);
     }
-    // 5. skip term and store
+    // 5. skip term and 8-byte stores of the lane's 4 adjacent outputs
+    if (rowok) {
+      uint16_t* yrow = Y + (int64_t)(ci.start + irow) * xrow + (int64_t)h * P;
 #pragma unroll
-    for (int tp = 0; tp < P / 16; ++tp)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = i0 + q * 4 + rr, p = tp * 16 + r;
-        if (i < len) {
-          const float v = acc[tp][rr] + Dh * bf2f(xs[i * LDX + p]);
-          Y[(int64_t)(ci.start + i) * xrow + (int64_t)h * P + p] = f2bf(v);
-        }
+      for (int tp = 0; tp < P / 16; ++tp) {
+        const int p = tp * 16 + q * 4;
+        const uint2 xv = *(const uint2*)(xs + irow * LDX + p);
+        const float y0 = acc[tp][0] + Dh * bf_lo(xv.x), y1 = acc[tp][1] + Dh * bf_hi(xv.x);
+        const float y2 = acc[tp][2] + Dh * bf_lo(xv.y), y3 = acc[tp][3] + Dh * bf_hi(xv.y);
+        *(uint2*)(yrow + p) = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
       }
+    }
   }
 }
 
