@@ -11,10 +11,11 @@ are resident in HBM before timing starts; the K timed steps are bracketed by
 torch.cuda.synchronize() and HIP events recorded on the stream the library
 launches on (torch's current stream).
 
-Printed (last line, JSON): tokens/s of the step, ms per step, the per-stage
-times and algorithmic HBM rates (each stage timed on its own through its stage
-entry point, same kernels and launch shapes as inside ssd_fwd), the roofline
-of the dominant kernel, and the CPU oracle timed on a bounded sample.
+Printed (last line, JSON): tokens/s of the step, ms per step, every kernel's
+time and algorithmic HBM rate (each kernel timed on its own: the step's own
+launch re-issued through the single-kernel flags of ssd_fwd / ssd_bwd, with
+HIP events on the library's stream), the roofline of the dominant kernel, and
+the CPU oracle timed on a bounded sample.
 """
 import argparse
 import hashlib
@@ -39,48 +40,64 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
     ap.add_argument("--fwd-only", action="store_true", help="time ssd_fwd alone as the step")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run the library's plain copy kernel (counter calibration)")
     return ap.parse_args()
 
 
-def stage_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, final=True):
-    """Algorithmic HBM bytes of each forward stage: inputs read once, outputs
-    written once (no cache re-reads, no skipped causal work)."""
+def kernel_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, d_final=False):
+    """Algorithmic HBM bytes of each kernel of the step: every array the kernel
+    must read is read once and every array it produces is written once (no
+    cache re-reads, no padding tiles; C.B^T and its adjoint count as their causal
+    triangle, R and K as one value per token and head).  Passed states and their
+    adjoints are bf16 on this path; chunk states and their adjoints fp32."""
     tok = B * L
+    f32_tok = nck * H * Q * 4           # one fp32 value per (chunk slot, head, token)
     dt = tok * H * 4
-    dl_acs = 2 * nck * H * Q * 4
     decay = nck * H * 4
-    states = nck * H * P * N * 4
+    st32 = nck * H * P * N * 4          # chunk states T, adjoint chunk states U
+    st16 = nck * H * P * N * esz        # passed states H, their adjoints dE
     x = tok * H * P * esz
     bc = tok * G * N * esz
-    cb = nck * G * Q * Q * esz
-    st0 = nseq * H * P * N * 4
+    tri = nck * G * (Q * (Q + 1) // 2) * esz
+    s0 = nseq * H * P * N * 4
     return {
-        "chunk_cumsum": dt + dl_acs + decay,
-        "chunk_state": x + bc + dl_acs + states,
-        "state_passing": 2 * states + decay + (st0 if init else 0) + (st0 if final else 0),
-        "bmm_chunk": 2 * bc + cb,
-        "chunk_scan": 2 * x + bc + cb + dl_acs + states,
+        "chunk_cumsum": dt + 2 * f32_tok + decay,
+        "chunk_state": x + bc + 2 * f32_tok + st32,
+        "state_passing": st32 + decay + st16 + (s0 if init else 0) + s0,
+        "bmm_chunk": 2 * bc + 2 * tri,                   # CB and its transpose (saved for bwd)
+        "chunk_scan": 2 * x + bc + tri + 2 * f32_tok + st16,
+        "dstates": x + bc + f32_tok + st32,
+        "reverse_state_passing": st32 + decay + st16 + (s0 if d_final else 0) + s0,
+        "bwd_dx": 3 * x + bc + tri + 2 * f32_tok + decay + 2 * st16 + 2 * f32_tok,
+        "bwd_dcb": 2 * x + tri + 2 * f32_tok + 2 * tri + 2 * f32_tok,
+        "bwd_dc": 2 * bc + x + tri + f32_tok + st16 + bc + f32_tok,
+        "bwd_db": x + bc + tri + 2 * f32_tok + st16 + bc,
+        "bwd_finalize": dt + 6 * f32_tok + dt,
     }
 
 
 KERNEL_FILES = {
     "chunk_cumsum": "k_cumsum.hip", "chunk_state": "k_chunk_state.hip",
     "state_passing": "k_state_passing.hip", "bmm_chunk": "k_bmm.hip",
-    "chunk_scan": "k_chunk_scan.hip",
+    "chunk_scan": "k_chunk_scan.hip", "dstates": "k_chunk_state.hip",
+    "reverse_state_passing": "k_state_passing.hip", "bwd_dx": "k_bwd.hip", "bwd_dcb": "k_bwd.hip",
+    "bwd_dc": "k_bwd.hip", "bwd_db": "k_bwd.hip", "bwd_finalize": "k_bwd.hip",
 }
 
 
-def source_hash(stage):
-    path = os.path.join(ROOT, "mamba_ssd_chunked_03_amd", "csrc", KERNEL_FILES[stage])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(kernel):
+    """Hash of the kernel's source file and the headers every kernel includes."""
+    h = hashlib.sha256()
+    for name in (KERNEL_FILES[kernel], "common.hpp", "internal.hpp"):
+        with open(os.path.join(ROOT, "mamba_ssd_chunked_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(stage):
+def load_traffic(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current source of this kernel (else None)."""
     path = os.path.join(PROFILES, "traffic.json")
@@ -88,8 +105,8 @@ def load_traffic(stage):
         return None
     with open(path) as f:
         t = json.load(f)
-    e = t.get(stage)
-    if not e or e.get("source_sha") != source_hash(stage):
+    e = t.get(kernel)
+    if not e or e.get("source_sha") != source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -157,23 +174,19 @@ def main():
     y = torch.empty_like(x)
     final = torch.empty(Bsz, H, P, N, dtype=torch.float32, device=dev)
 
-    def fwd():
-        ssd.fwd(x, dt, A, Bm, Cm, D=D, dt_bias=bias, init=init, chunk_size=Q, workspace=ws_f,
-                out=y, final=final)
+    # every call's arguments are marshalled once; the timed loops only issue them
+    common = dict(D=D, dt_bias=bias, init=init, chunk_size=Q)
+    fwd, _, _ = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_f, out=y, final=final, prepare=True, **common)
 
     have_bwd = not args.fwd_only
     ws_b = torch.empty(lib.ssd_bwd_workspace_bytes(ctypes.byref(prob), Q, 0), dtype=torch.uint8, device=dev)
-
-    def fwd_save():  # the training forward: keeps its intermediates for the backward
-        ssd.fwd(x, dt, A, Bm, Cm, D=D, dt_bias=bias, init=init, chunk_size=Q, workspace=ws_b,
-                out=y, final=final, save_for_backward=True)
-
-    def bwd_saved():
-        ssd.bwd(x, dt, A, Bm, Cm, dout, D=D, dt_bias=bias, init=init, chunk_size=Q, workspace=ws_b,
-                from_saved=True)
-
-    def bwd_recompute():
-        ssd.bwd(x, dt, A, Bm, Cm, dout, D=D, dt_bias=bias, init=init, chunk_size=Q, workspace=ws_b)
+    # the training forward keeps its intermediates for the backward
+    fwd_save, _, _ = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_b, out=y, final=final,
+                             save_for_backward=True, prepare=True, **common)
+    bwd_saved, grads = ssd.bwd(x, dt, A, Bm, Cm, dout, workspace=ws_b, from_saved=True,
+                               prepare=True, **common)
+    bwd_recompute, _ = ssd.bwd(x, dt, A, Bm, Cm, dout, workspace=ws_b, grads=grads, prepare=True,
+                               **common)
 
     def timed(fn, steps, warmup):
         for _ in range(warmup):
@@ -212,40 +225,40 @@ def main():
     tokens = Bsz * L
     print("bench: step %.3f ms (wall %.3f), fwd %.3f ms" % (ms_step, wall_step, ms_fwd), file=sys.stderr, flush=True)
 
-    stages = {}
+    # every kernel of the step on its own: the same launch (arguments, grid,
+    # buffers) as inside the step, re-issued through the single-kernel flags
+    kernels = {}
     roof = None
-    if not args.no_stages:
-        sg = ssd.Stages(x, Bm, None, Q, True)
-        delta, acs, decay = sg.chunk_cumsum(dt, A, bias)
-        T = sg.chunk_state(x, Bm, delta, acs)
-        Hp, fin = sg.state_passing(T, decay, init)
-        CB = sg.bmm_chunk(Bm, Cm)
-        y2 = torch.empty_like(x)
-        fns = {
-            "chunk_cumsum": lambda: sg.chunk_cumsum(dt, A, bias, out=(delta, acs, decay)),
-            "chunk_state": lambda: sg.chunk_state(x, Bm, delta, acs, out=T),
-            "state_passing": lambda: sg.state_passing(T, decay, init, out=(Hp, fin)),
-            "bmm_chunk": lambda: sg.bmm_chunk(Bm, Cm, out=CB),
-            "chunk_scan": lambda: sg.chunk_scan(x, Cm, CB, delta, acs, Hp, D, out=y2),
-        }
-        # time the launches alone: output buffers allocated once, then only the
-        # C entry point is called inside the timed region
-        nbytes = stage_bytes(Bsz, L, H, P, N, G, Q, sg.nck, Bsz, 2)
+    if not args.no_kernels:
+        fwd_save()
+        bwd_saved()
+        torch.cuda.synchronize()
+        nck = ssd.num_chunks(prob, Q, 0)
+        nbytes = kernel_bytes(Bsz, L, H, P, N, G, Q, nck, Bsz, 2, init=init is not None,
+                              d_final=False)
+        fns = {}
+        for k, name in enumerate(ssd.FWD_KERNELS, 1):
+            fns[name] = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_b, out=y, final=final,
+                                save_for_backward=True, only_kernel=k, prepare=True, **common)[0]
+        for k, name in enumerate(ssd.BWD_KERNELS, 1):
+            fns[name] = ssd.bwd(x, dt, A, Bm, Cm, dout, workspace=ws_b, from_saved=True, grads=grads,
+                                only_kernel=k, prepare=True, **common)[0]
         for name, fn in fns.items():
             ms, _ = timed(fn, args.steps, 2)
             gbs = nbytes[name] / (ms * 1e-3) / 1e9
-            stages[name] = {"ms": round(ms, 4), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
-                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-            print("bench: stage %-14s %.4f ms  %.0f GB/s" % (name, ms, gbs), file=sys.stderr, flush=True)
-        dom = max(stages, key=lambda k: stages[k]["ms"])
-        s = stages[dom]
+            kernels[name] = {"ms": round(ms, 4), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
+                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            print("bench: kernel %-22s %.4f ms  %.0f GB/s" % (name, ms, gbs), file=sys.stderr,
+                  flush=True)
+        dom = max(kernels, key=lambda k: kernels[k]["ms"])
+        s = kernels[dom]
         roof = {"kernel": dom, "bound": "hbm", "achieved": s["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": s["frac_hbm"], "traffic": load_traffic(dom),
                 "alg_bytes_per_launch": s["alg_bytes"], "avg_launch_ms": s["ms"]}
-        fwd_bytes = sum(v["alg_bytes"] for v in stages.values())
-        fwd_stage_ms = sum(v["ms"] for v in stages.values())
-        stages["_forward_aggregate"] = {"ms": round(fwd_stage_ms, 4), "alg_bytes": fwd_bytes,
-                                        "GB/s": round(fwd_bytes / (fwd_stage_ms * 1e-3) / 1e9, 1)}
+        tot_b = sum(v["alg_bytes"] for v in kernels.values())
+        tot_ms = sum(v["ms"] for v in kernels.values())
+        kernels["_sum"] = {"ms": round(tot_ms, 4), "alg_bytes": tot_b,
+                           "GB/s": round(tot_b / (tot_ms * 1e-3) / 1e9, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -274,7 +287,7 @@ def main():
             "tokens/s": round(tokens / (ms_step * 1e-3), 1),
             "note": "forward keeps its intermediates for the backward (SSD_FLAG_SAVE_FOR_BWD)",
             "recompute_variant_ms": round(ms_step_rc, 4)},
-        "stages": stages,
+        "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -86,6 +86,18 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   checks this. */
 #define SSD_FLAG_SAVE_FOR_BWD 1
 #define SSD_FLAG_FROM_SAVED 2
+/* SSD_FLAG_BWD_KERNEL(k), k = 1..7: a profiling aid, valid only together with
+ *   SSD_FLAG_FROM_SAVED.  ssd_bwd launches only its k-th kernel: 1 adjoint chunk
+ *   states, 2 reverse state passing, 3 dx (with the direct delta gradient),
+ *   4 head-summed dCB with the decay-gradient partials, 5 dC, 6 dB, 7 finalize
+ *   (ddt and the per-head sums).  The workspace and the gradient buffers must hold
+ *   the results of a complete ssd_bwd call on the same arguments, so that the kernel
+ *   finds its inputs; it rewrites its own outputs with the same values. */
+#define SSD_FLAG_BWD_KERNEL(k) ((k) << 8)
+/* SSD_FLAG_FWD_KERNEL(k), k = 1..5: the same for ssd_fwd, whose workspace and
+ *   outputs must hold a complete call's results on the same arguments: 1 chunk
+ *   cumsum, 2 chunk states, 3 state passing, 4 C.B^T, 5 chunk scan. */
+#define SSD_FLAG_FWD_KERNEL(k) ((k) << 12)
 
 typedef struct {
   int32_t batch;       /* B (1 when cu_seqlens is given) */

@@ -30,7 +30,12 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
     return SSD_ERR_SHAPE;
   if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
-  if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED)) return SSD_ERR_UNSUPPORTED;
+  if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_BWD_KERNEL(7) |
+                    SSD_FLAG_FWD_KERNEL(7)))
+    return SSD_ERR_UNSUPPORTED;
+  if ((pr->flags & SSD_FLAG_BWD_KERNEL(7)) && !(pr->flags & SSD_FLAG_FROM_SAVED))
+    return SSD_ERR_UNSUPPORTED;
+  if (((pr->flags >> 12) & 7) > 5) return SSD_ERR_UNSUPPORTED;
   if (packed && (pr->batch != 1 || pr->nseq < 0)) return SSD_ERR_SHAPE;
   if (pr->io_dtype != SSD_F32 && pr->io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
   if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
@@ -122,11 +127,13 @@ BwdLayout bwd_layout(const Prob& p) {
 size_t stage_ws(const Prob& p) { return fwd_layout(p).delta; }
 
 // Point the chunk map at the table inside a workspace and queue its build.
-ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st) {
+// build = false: the workspace already holds the table (single-kernel relaunch).
+ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool build = true) {
   if (!p.packed) return SSD_OK;
   FwdLayout l = fwd_layout(p);
   p.map.tab = (const int4*)(ws + l.tab);
   p.map.seq_off = (const int32_t*)(ws + l.seq_off);
+  if (!build) return SSD_OK;
   if (std::getenv("SSD_DEBUG") && std::getenv("SSD_DEBUG")[0] == '1') {
     std::vector<int32_t> h((size_t)p.nseq + 1);
     if (hipMemcpyAsync(h.data(), cu, h.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
@@ -213,7 +220,8 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  s = setup_map(p, cu_seqlens, ws, st);
+  const int only = (p.flags >> 12) & 7;  // 0: every kernel
+  s = setup_map(p, cu_seqlens, ws, st, only == 0);
   if (s != SSD_OK) return s;
   float* delta = (float*)(ws + l.delta);
   float* acs = (float*)(ws + l.acs);
@@ -222,12 +230,13 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   void* Hp = ws + l.Hp;
   const int hb = p.io == SSD_BF16;
   void* CB = ws + l.CB;
-  SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
-  SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
-  SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
+  if (!only || only == 1) SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
+  if (!only || only == 2) SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
+  if (!only || only == 3)
+    SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
   void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
-  SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
-  SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
+  if (!only || only == 4) SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
+  if (!only || only == 5) SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
   return SSD_OK;
 }
 
@@ -251,7 +260,8 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   if (!workspace || workspace_bytes < l.end) return SSD_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  s = setup_map(p, cu_seqlens, ws, st);
+  const int only = (p.flags >> 8) & 7;  // 0: every kernel
+  s = setup_map(p, cu_seqlens, ws, st, only == 0);
   if (s != SSD_OK) return s;
   float* delta = (float*)(ws + l.f.delta);
   float* acs = (float*)(ws + l.f.acs);
@@ -270,8 +280,10 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
   }
   // adjoint of the state carried into each chunk, then the reverse scan
-  SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
-  SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
+  if (!only || only == 1)
+    SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
+  if (!only || only == 2)
+    SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
   BwdArgs a;
   a.x = x; a.B = B; a.C = C; a.dout = dout;
   a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.D = D;
@@ -284,8 +296,8 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   a.ddd = (float*)(ws + l.ddd); a.Ks = (float*)(ws + l.Ks); a.rR = (float*)(ws + l.rR);
   a.last_term = (float*)(ws + l.last); a.dDp = (float*)(ws + l.dDp);
   a.dAp = (float*)(ws + l.dAp); a.dbp = (float*)(ws + l.dbp);
-  SSD_TRY(launch_bwd_chunk(p, a, st));
-  SSD_TRY(launch_bwd_finalize(p, a, st));
+  if (!only || (only >= 3 && only <= 6)) SSD_TRY(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
+  if (!only || only == 7) SSD_TRY(launch_bwd_finalize(p, a, st));
   return SSD_OK;
 }
 

@@ -62,7 +62,8 @@ struct BwdArgs {
   // per (chunk, head): alpha<dE,H> + sum s, and partials of dD, dA, d_dt_bias
   float *last_term, *dDp, *dAp, *dbp;
 };
-hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, hipStream_t st);
+// which: 0 every chunk kernel; 1 dx, 2 dCB (or the fp32 r+R kernel), 3 dC, 4 dB
+hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st);
 hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st);
 
 }  // namespace ssd

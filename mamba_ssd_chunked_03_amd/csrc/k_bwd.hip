@@ -848,45 +848,53 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(int nck, int H, const f
 
 // ---------------------------------------------------------------- launchers ----
 template <int P, int N>
-static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, hipStream_t st) {
+static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
   const int T = p.Q / 64;
+  if (!which || which == 1)
   hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(kDxWaves * 64), 0, st, p.map,
                      p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B, (const uint16_t*)a.dout,
                      (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, (const uint16_t*)a.dE, (const uint16_t*)a.Hp, a.D,
                      (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
+  if (!which || which == 2)
   hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
                      dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
                      (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
                      (uint16_t*)a.dCBg, (uint16_t*)a.dCBgT, a.Rp, a.Kp);
+  if (!which || which == 3)
   hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
                      (const uint16_t*)a.dout, (const uint16_t*)a.dCBg, a.acs, (const uint16_t*)a.Hp,
                      (uint16_t*)a.dC, a.rR);
+  if (!which || which == 4)
   hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
                      (const uint16_t*)a.dCBgT, a.delta, a.acs, (const uint16_t*)a.dE, (uint16_t*)a.dB);
 }
 
-hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
   if (p.io == 0) {
+    if (!which || which == 1)
     hipLaunchKernelGGL(bwd_dx_f32_kernel, dim3((unsigned)p.nck, p.H), dim3(256), 0, st, p.map, p.H,
                        p.G, p.P, p.N, (const float*)a.x, (const float*)a.B, (const float*)a.dout,
                        (const float*)a.CB, a.delta, a.acs, a.decay, (const float*)a.dE, (const float*)a.Hp, a.D, (float*)a.dx,
                        a.ddd, a.Ks, a.last_term, a.dDp);
+    if (!which || which == 3)
     hipLaunchKernelGGL(bwd_dc_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
                        dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
                        (const float*)a.B, (const float*)a.dout, a.delta, a.acs, (const float*)a.Hp, (float*)a.dC);
+    if (!which || which == 2)
     hipLaunchKernelGGL(bwd_rr_f32_kernel, dim3((unsigned)p.nck, p.H, (p.Q + 255) / 256), dim3(256), 0,
                        st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x, (const float*)a.C,
                        (const float*)a.dout, (const float*)a.CB, a.delta, a.acs, (const float*)a.Hp, a.rR);
+    if (!which || which == 4)
     hipLaunchKernelGGL(bwd_db_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
                        dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
                        (const float*)a.C, (const float*)a.dout, a.delta, a.acs, (const float*)a.dE, (float*)a.dB);
     return hipGetLastError();
   }
 #define SSD_BWD_CASE(PP, NN) \
-  if (p.P == PP && p.N == NN) { launch_bwd_bf16<PP, NN>(p, a, st); return hipGetLastError(); }
+  if (p.P == PP && p.N == NN) { launch_bwd_bf16<PP, NN>(p, a, which, st); return hipGetLastError(); }
   SSD_BWD_CASE(32, 32) SSD_BWD_CASE(32, 64) SSD_BWD_CASE(32, 128)
   SSD_BWD_CASE(64, 32) SSD_BWD_CASE(64, 64) SSD_BWD_CASE(64, 128)
   SSD_BWD_CASE(128, 32) SSD_BWD_CASE(128, 64) SSD_BWD_CASE(128, 128)

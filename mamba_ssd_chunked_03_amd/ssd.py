@@ -24,6 +24,21 @@ class Problem(ctypes.Structure):
                  "io_dtype", "dt_softplus", "flags")]
 
 FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED = 1, 2
+BWD_KERNELS = ("dstates", "reverse_state_passing", "bwd_dx", "bwd_dcb", "bwd_dc", "bwd_db",
+               "bwd_finalize")
+
+
+FWD_KERNELS = ("chunk_cumsum", "chunk_state", "state_passing", "bmm_chunk", "chunk_scan")
+
+
+def FLAG_BWD_KERNEL(k):
+    """ssd_bwd launches only its k-th kernel (1-based, order of BWD_KERNELS)."""
+    return int(k) << 8
+
+
+def FLAG_FWD_KERNEL(k):
+    """ssd_fwd launches only its k-th kernel (1-based, order of FWD_KERNELS)."""
+    return int(k) << 12
 
 
 _SIGS = {
@@ -69,7 +84,8 @@ class SSDError(RuntimeError):
         super().__init__("libssd: %s (status %d)" % (lib().ssd_status_string(status).decode(), status))
 
 
-def _check(status):
+def _check(status, keep=None):
+    # keep: objects the marshalled arguments point into (held by the caller's closure)
     if status != 0:
         raise SSDError(status)
 
@@ -125,18 +141,26 @@ def num_chunks(prob, chunk_size, packed):
 
 
 def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
-        dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False):
+        dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False,
+        only_kernel=0, prepare=False):
     """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h.
 
     save_for_backward: keep the intermediates in ``workspace`` (which must hold
     bwd_workspace_bytes) so that bwd(..., workspace=that, from_saved=True) skips
-    the recompute."""
+    the recompute.
+    only_kernel: k >= 1 launches only the k-th forward kernel (profiling; needs the
+    workspace, out and final of a complete call on the same inputs).
+    prepare: launch nothing; return (launch, out, final) where launch() issues the
+    call with the arguments marshalled here (timing loops)."""
+    if only_kernel and (workspace is None or out is None):
+        raise ValueError("only_kernel needs the workspace and outputs of a complete call")
     dev = _dev(x, dt, A, B, C, D, dt_bias, init, cu_seqlens, workspace, out, final)
     for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (dt_bias, "dt_bias"), (init, "init")):
         _f32(t, n)
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
-    prob = problem(x, B, cu_seqlens, dt_softplus, FLAG_SAVE_FOR_BWD if save_for_backward else 0)
+    prob = problem(x, B, cu_seqlens, dt_softplus,
+                   (FLAG_SAVE_FOR_BWD if save_for_backward else 0) | FLAG_FWD_KERNEL(only_kernel))
     L = lib()
     packed = int(cu_seqlens is not None)
     if save_for_backward:
@@ -150,40 +174,64 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     if final is None:
         nst = prob.nseq if packed else prob.batch
         final = torch.empty(nst, prob.nheads, prob.headdim, prob.dstate, dtype=torch.float32, device=dev)
-    _check(L.ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
-                     _ptr(D), _ptr(init), _ptr(cu_seqlens), chunk_size, _ptr(out), _ptr(final),
-                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    args = (ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(init), _ptr(cu_seqlens), chunk_size, _ptr(out), _ptr(final),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    keep = (prob, workspace)
+
+    def launch():
+        _check(L.ssd_fwd(*args), keep)
+
+    if prepare:
+        return launch, out, final
+    launch()
     return out, final
 
 
 def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
-        chunk_size=256, dt_softplus=True, workspace=None, from_saved=False):
+        chunk_size=256, dt_softplus=True, workspace=None, from_saved=False, grads=None,
+        only_kernel=0, prepare=False):
     """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors).
 
     from_saved: ``workspace`` holds the intermediates of a save_for_backward
-    fwd call on the same inputs; the recompute is skipped."""
+    fwd call on the same inputs; the recompute is skipped.
+    grads: a dict returned by an earlier call, written again instead of new tensors.
+    only_kernel: k >= 1 launches only the k-th backward kernel (profiling; needs
+    from_saved and the workspace and grads of a complete call on the same inputs).
+    prepare: launch nothing; return (launch, grads) (see fwd)."""
     dev = _dev(x, dt, A, B, C, dout, D, dt_bias, init, d_final, cu_seqlens, workspace)
     if from_saved and workspace is None:
         raise ValueError("from_saved needs the forward's workspace")
-    prob = problem(x, B, cu_seqlens, dt_softplus, FLAG_FROM_SAVED if from_saved else 0)
+    if only_kernel and (not from_saved or grads is None):
+        raise ValueError("only_kernel needs from_saved and the grads of a complete call")
+    flags = (FLAG_FROM_SAVED if from_saved else 0) | FLAG_BWD_KERNEL(only_kernel)
+    prob = problem(x, B, cu_seqlens, dt_softplus, flags)
     L = lib()
     packed = int(cu_seqlens is not None)
     need = L.ssd_bwd_workspace_bytes(ctypes.byref(prob), chunk_size, packed)
     if workspace is None:
         workspace = _ws(need, dev)
     nst = prob.nseq if packed else prob.batch
-    g = {
+    g = grads if grads is not None else {
         "dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dA": torch.empty_like(A),
         "dB": torch.empty_like(B), "dC": torch.empty_like(C),
         "dD": None if D is None else torch.empty_like(D),
         "d_dt_bias": torch.empty(prob.nheads, dtype=torch.float32, device=dev),
         "d_init": torch.empty(nst, prob.nheads, prob.headdim, prob.dstate, dtype=torch.float32, device=dev),
     }
-    _check(L.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
-                     _ptr(D), _ptr(init), _ptr(cu_seqlens), chunk_size, _ptr(dout), _ptr(d_final),
-                     _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
-                     _ptr(g["dD"]), _ptr(g["d_dt_bias"]), _ptr(g["d_init"]),
-                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    args = (ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(init), _ptr(cu_seqlens), chunk_size, _ptr(dout), _ptr(d_final),
+            _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+            _ptr(g["dD"]), _ptr(g["d_dt_bias"]), _ptr(g["d_init"]),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    keep = (prob, workspace)
+
+    def launch():
+        _check(L.ssd_bwd(*args), keep)
+
+    if prepare:
+        return launch, g
+    launch()
     return g
 
 

@@ -154,3 +154,35 @@ def test_bwd_full_size_sampled_heads():
     ref = oracle_bwd(inp, heads=heads)
     check(g, ref, "bf16", "config 2 sampled", keys=["dx", "ddt", "dA", "dD", "d_dt_bias", "d_init"],
           heads=heads)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_single_kernel_relaunch_is_idempotent(io):
+    # the profiling flags re-launch one forward or backward kernel on the buffers
+    # of a complete call: every output and gradient must come out bit-identical
+    kw = dict(nheads=4, headdim=64, dstate=128, ngroups=2) if io == "bf16" else \
+        dict(nheads=2, headdim=16, dstate=32, ngroups=1)
+    inp = inputs.make_inputs(2, 300, io=io, init="randn", bwd=True, d_final=True, seed=61, **kw)
+    d = to_dev(inp)
+    prob = ssd.problem(d["x"], d["B"])
+    import ctypes
+    ws = torch.empty(ssd.lib().ssd_bwd_workspace_bytes(ctypes.byref(prob), 128, 0),
+                     dtype=torch.uint8, device="cuda")
+    y, fin = gpu_fwd(ssd, inp, 128, workspace=ws, save_for_backward=True)
+    torch.cuda.synchronize()
+    y0, f0 = y.clone(), fin.clone()
+    for k in range(1, len(ssd.FWD_KERNELS) + 1):
+        gpu_fwd(ssd, inp, 128, workspace=ws, save_for_backward=True, out=y, final=fin, only_kernel=k)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0) and torch.equal(fin, f0), ssd.FWD_KERNELS[k - 1]
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["dout"])
+    kw2 = dict(D=d["D"], dt_bias=d["dt_bias"], init=d["init"], d_final=d["d_final"], chunk_size=128,
+               dt_softplus=inp["dt_softplus"], workspace=ws, from_saved=True)
+    g = ssd.bwd(*args, **kw2)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in g.items() if v is not None}
+    for k in range(1, len(ssd.BWD_KERNELS) + 1):
+        ssd.bwd(*args, grads=g, only_kernel=k, **kw2)
+        torch.cuda.synchronize()
+        for name, v in ref.items():
+            assert torch.equal(g[name], v), (ssd.BWD_KERNELS[k - 1], name)
