@@ -269,14 +269,26 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
 // For every head the tile's contributions to R_i (row sums over j < i) and K_j
 // (column sums over i > j) of M_ij = dCB_ij CB_ij come from the same values,
 // so they cancel exactly where the decay gradient subtracts them.
-template <int P, int N>
-__global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
+//
+// Wave w owns rows ti*64 + 16w .. +15.  Per head: the tile's 64 x rows are
+// staged in LDS by all four waves together (double-buffered, one barrier per
+// head), each wave's 16 dy rows stay in registers, and both are loaded one head
+// ahead.  D = dy_rows . x_tile^T on MFMA (K = headdim), then times L_ij delta_j:
+// an off-diagonal tile factors the decay through its last column e
+// (2^(acs_i - acs_e) per row times 2^(acs_e - acs_j) delta_j per column, both
+// <= 1), the diagonal tile takes one exp per element and the causal mask.
+template <int P>
+__global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ DY,
     const uint16_t* __restrict__ CB, const float* __restrict__ delta,
     const float* __restrict__ acs, uint16_t* __restrict__ dCBg, uint16_t* __restrict__ dCBgT,
     float* __restrict__ Rp, float* __restrict__ Kp) {
-  constexpr int LT = 64 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t stg[64 * LT];
+  constexpr int LX = P + 8;          // x tile row stride (bf16)
+  constexpr int LT = 64 + 8;         // output staging row stride
+  constexpr int PER = P / 8;         // 16-byte pieces per row
+  constexpr int NPX = 64 * PER / 256;  // x pieces per thread per head
+  static_assert(NPX >= 1, "headdim");
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][64 * LX];
   __shared__ float kred[8][4][64];
   __shared__ float sv[8][192];  // per head of 8: acs rows | acs cols | delta cols
   const int Q = m.Q, T = Q / 64, NT = T * (T + 1) / 2;
@@ -294,6 +306,7 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
   const int64_t xrow = (int64_t)H * P;
   const int i0 = ti * 64 + w * 16, jt0 = tj * 64;
   const int irow = i0 + r;
+  const bool diag = ti == tj;
   const int64_t kg = (int64_t)k * G + g;
   const uint16_t* cbm = CB + kg * Q * Q;
   float cbv[4][4];
@@ -307,73 +320,95 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
   f32x4 sum[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) sum[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 ay[P / 32], xf[4][P / 32];
+  // the next head's rows: this wave's dy fragments and this thread's x pieces
+  u32x4 ay[P / 32], px[NPX];
   auto load_head = [&](int h) {
     const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
-    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
+    const uint16_t* xb = X + (int64_t)(ci.start + jt0) * xrow + (int64_t)h * P;
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb)
       ay[kb] = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
                             : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int jcol = jt0 + b * 16 + r;
-#pragma unroll
-      for (int kb = 0; kb < P / 32; ++kb)
-        xf[b][kb] = (jcol < len) ? *(const u32x4*)(xb + (int64_t)jcol * xrow + kb * 32 + q * 8)
-                                 : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < NPX; ++c) {
+      const int e = tid + c * 256, row = e / PER, c8 = e % PER;
+      px[c] = (jt0 + row < len) ? *(const u32x4*)(xb + (int64_t)row * xrow + c8 * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
     }
   };
   load_head(g * hpg);
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
+    uint16_t* xbuf = xt[hh & 1];
+#pragma unroll
+    for (int c = 0; c < NPX; ++c) {
+      const int e = tid + c * 256, row = e / PER, c8 = e % PER;
+      *(u32x4*)(xbuf + row * LX + c8 * 8) = px[c];
+    }
     if ((hh & 7) == 0) {
       // acs of the tile's rows and columns and delta of its columns for the next
-      // 8 heads, so the head loop never waits on these scalars; the previous
-      // block's readers are done (the column reduction below ends in a barrier)
+      // 8 heads; the previous block's readers are done (the column reduction
+      // below ends in a barrier)
       const int nh = min(8, hpg - hh);
       for (int e = tid; e < nh * 192; e += 256) {
         const int sl = e / 192, c = e % 192;
         const int64_t khs = kh + sl;
-        const int t = (c < 64) ? ti * 64 + c : tj * 64 + (c % 64);
+        const int t = (c < 64) ? ti * 64 + c : jt0 + (c % 64);
         sv[sl][c] = (c < 128) ? acs[khs * Q + t] : delta[khs * Q + t];
       }
-      __syncthreads();
     }
+    __syncthreads();
+    bf16x8 af[P / 32];
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb) af[kb] = as_bf16x8(ay[kb]);
+    if (hh + 1 < hpg) load_head(h + 1);  // in flight during this head's work
     f32x4 dxb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       dxb[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < P / 32; ++kb) dxb[b] = mfma_bf16(as_bf16x8(ay[kb]), as_bf16x8(xf[b][kb]), dxb[b]);
+      for (int kb = 0; kb < P / 32; ++kb)
+        dxb[b] = mfma_bf16(af[kb], as_bf16x8(*(const u32x4*)(xbuf + (b * 16 + r) * LX + kb * 32 + q * 8)),
+                           dxb[b]);
     }
-    if (hh + 1 < hpg) load_head(h + 1);  // in flight during this head's element-wise work
     const float* svh = sv[hh & 7];
-    float ai[4], aj[4], dj[4], Rl[4], Kl[4];
+    float Rl[4] = {0.f, 0.f, 0.f, 0.f}, Kl[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!diag) {
+      // anchor e = the tile's last column (e < i for every row of the tile)
+      const float ae = svh[64 + 63];
+      float rho[4], gam[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      ai[rr] = svh[w * 16 + q * 4 + rr];
-      Rl[rr] = 0.f;
-    }
+      for (int rr = 0; rr < 4; ++rr)
+        rho[rr] = (i0 + q * 4 + rr < len) ? exp2_fast(svh[w * 16 + q * 4 + rr] - ae) : 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      aj[b] = svh[64 + b * 16 + r];
-      dj[b] = svh[128 + b * 16 + r];
-      Kl[b] = 0.f;
-    }
+      for (int b = 0; b < 4; ++b) gam[b] = exp2_fast(ae - svh[64 + b * 16 + r]) * svh[128 + b * 16 + r];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
-        float v = dxb[b][rr] * exp2_fast(ai[rr] - aj[b]) * dj[b];
-        v = (j <= i && i < len) ? v : 0.f;
-        sum[b][rr] += v;
-        const float mij = v * cbv[b][rr];  // cbv is zero unless j < i < len
-        Rl[rr] += mij;
-        Kl[b] += mij;
+        for (int rr = 0; rr < 4; ++rr) {
+          const float v = dxb[b][rr] * rho[rr] * gam[b];
+          sum[b][rr] += v;
+          const float mij = v * cbv[b][rr];
+          Rl[rr] += mij;
+          Kl[b] += mij;
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float aj = svh[64 + b * 16 + r], dj = svh[128 + b * 16 + r];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
+          float v = dxb[b][rr] * exp2_fast(svh[w * 16 + q * 4 + rr] - aj) * dj;
+          v = (j <= i && i < len) ? v : 0.f;
+          sum[b][rr] += v;
+          const float mij = v * cbv[b][rr];  // cbv is zero unless j < i < len
+          Rl[rr] += mij;
+          Kl[b] += mij;
+        }
       }
+    }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const float v = row_sum16(Rl[rr]);
@@ -400,6 +435,7 @@ __global__ __launch_bounds__(256) void bwd_dcb_bf16_kernel(
     }
   }
   // head-summed tile -> bf16, through LDS to 16-byte row stores in both orientations
+  uint16_t* stg = xt[0];  // every wave is past its last read of the x tiles (barrier above)
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -856,7 +892,7 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStrea
                      (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, (const uint16_t*)a.dE, (const uint16_t*)a.Hp, a.D,
                      (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
   if (!which || which == 2)
-  hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
+  hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
                      dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
                      (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
                      (uint16_t*)a.dCBg, (uint16_t*)a.dCBgT, a.Rp, a.Kp);
