@@ -454,9 +454,13 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
 
 // ------------------------------------------------------------ bwd_dc bf16 ----
 // One workgroup per (chunk, group, 64 rows i).  dC_i = sum_{j<=i} dCB_g[i][j] B_j
-// (A fragments straight from the dCB_g rows, B through LDS one 64-row piece at a
+// (dCB_g fragments straight from its rows, B through LDS one 64-row piece at a
 // time and read with transpose reads) + sum_h 2^acs_i H^T dy_i (one K=headdim
-// GEMM per head with H staged in LDS); r_i = C_i . (that head's state term).
+// GEMM per head); r_i = C_i . (that head's state term).  Per head, H (bf16) is
+// staged in a double-buffered LDS tile (one barrier per head) and the next
+// head's H, dy fragments and acs are loaded into registers while this head is
+// worked on.  Products are issued with the operands swapped, so each lane owns
+// one row i: its r_i reduces over four lanes and dC is stored 8 bytes at a time.
 template <int P, int N>
 __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
@@ -464,8 +468,9 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     const float* __restrict__ acs, const uint16_t* __restrict__ Hs, uint16_t* __restrict__ dC,
     float* __restrict__ rout) {
   constexpr int LDB = N + 16;  // odd multiple of 32 bytes for the transpose reads
-  __shared__ __attribute__((aligned(16))) uint16_t bt[64 * LDB];
-  __shared__ __attribute__((aligned(16))) uint16_t ht[P * LDB];
+  constexpr int ROWS = P > 64 ? P : 64;
+  constexpr int NPH = (P * N / 8 + 255) / 256;  // 16-byte pieces of H per thread
+  __shared__ __attribute__((aligned(16))) uint16_t ub[2][ROWS * LDB];
   const int T = m.Q / 64;
   const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
   const int tile = lid % T, k = lid / T / G, g = (lid / T) % G;
@@ -482,91 +487,110 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   const int i0 = tile * 64 + w * 16;
   const bool active = i0 < len;
   const int irow = i0 + r;
+  const bool rowok = irow < len;
+  // acc[nb][rr] = dC[irow][16 nb + 4 q + rr]
   f32x4 acc[N / 16];
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* bt = ub[0];
   for (int jt = 0; jt <= tile; ++jt) {
     __syncthreads();
     stage_rows<64, N>(bt, LDB, bb + (int64_t)jt * 64 * brow, brow, len - jt * 64, tid);
     __syncthreads();
     if (!active) continue;
     for (int jb = jt * 64; jb < min(jt * 64 + 64, i0 + 16); jb += 32) {
-      const bf16x8 a = as_bf16x8(irow < len ? *(const u32x4*)(dcb + (int64_t)irow * Q + jb + q * 8)
-                                            : u32x4{0u, 0u, 0u, 0u});
+      const bf16x8 a = as_bf16x8(rowok ? *(const u32x4*)(dcb + (int64_t)irow * Q + jb + q * 8)
+                                       : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
-        acc[nb] = mfma_bf16(a, frag_kmajor(bt + (jb - jt * 64) * LDB + nb * 16, LDB, lane), acc[nb]);
+        acc[nb] = mfma_bf16(frag_kmajor(bt + (jb - jt * 64) * LDB + nb * 16, LDB, lane), a, acc[nb]);
     }
   }
-  float cv[N / 16][4];
+  // C_i values of this lane's outputs, 4 adjacent per nb
+  uint2 cq[N / 16];
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb)
+    cq[nb] = rowok ? *(const uint2*)(cb + (int64_t)irow * brow + nb * 16 + q * 4) : make_uint2(0u, 0u);
+  // the next head's H pieces, dy fragments and acs_i
+  u32x4 ph[NPH], py[P / 32];
+  float pa = 0.f;
+  auto load_head = [&](int h) {
+    const int64_t kh = (int64_t)k * H + h;
+    const uint16_t* src = Hs + kh * (int64_t)(P * N);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = i0 + q * 4 + rr;
-      cv[nb][rr] = (i < len) ? bf2f(cb[(int64_t)i * brow + nb * 16 + r]) : 0.f;
+    for (int c = 0; c < NPH; ++c) {
+      const int e = (tid + c * 256) * 8;
+      ph[c] = e < P * N ? *(const u32x4*)(src + e) : u32x4{0u, 0u, 0u, 0u};
     }
+    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb)
+      py[kb] = rowok ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    pa = rowok ? acs[kh * Q + irow] : 0.f;
+  };
+  __syncthreads();  // every wave is done with the B pieces in ub[0]
+  load_head(g * hpg);
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
+    uint16_t* ht = ub[hh & 1];
+#pragma unroll
+    for (int c = 0; c < NPH; ++c) {
+      const int e = (tid + c * 256) * 8;
+      if (e < P * N) *(u32x4*)(ht + (e / N) * LDB + (e % N)) = ph[c];
+    }
     __syncthreads();
-    stage_state_bf16<P, N>(ht, LDB, Hs + kh * (int64_t)(P * N), tid);
-    __syncthreads();
-    if (!active) continue;
-    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
-    const float ei = (irow < len) ? exp2_fast(acs[kh * Q + irow]) : 0.f;
+    // this head's dy fragment scaled by 2^acs_i (one row per lane)
+    const float ei = rowok ? exp2_fast(pa) : 0.f;
     bf16x8 ays[P / 32];
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb) {
-      const u32x4 ay = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
-                                    : u32x4{0u, 0u, 0u, 0u};
       u32x4 sv;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) sv[d] = pack_bf2(bf_lo(ay[d]) * ei, bf_hi(ay[d]) * ei);
+      for (int d = 0; d < 4; ++d) sv[d] = pack_bf2(bf_lo(py[kb][d]) * ei, bf_hi(py[kb][d]) * ei);
       ays[kb] = as_bf16x8(sv);
     }
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    if (hh + 1 < hpg) load_head(h + 1);  // in flight during this head's work
+    if (!active) continue;
+    float rsum = 0.f;
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb) {
       f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < P / 32; ++kb)
-        t = mfma_bf16(ays[kb], frag_kmajor(ht + kb * 32 * LDB + nb * 16, LDB, lane), t);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        rsum[rr] += cv[nb][rr] * t[rr];
-        acc[nb][rr] += t[rr];
-      }
+        t = mfma_bf16(frag_kmajor(ht + kb * 32 * LDB + nb * 16, LDB, lane), ays[kb], t);
+      rsum += bf_lo(cq[nb].x) * t[0] + bf_hi(cq[nb].x) * t[1] + bf_lo(cq[nb].y) * t[2] +
+              bf_hi(cq[nb].y) * t[3];
+      acc[nb] += t;
     }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float v = row_sum16(rsum[rr]);
-      const int i = i0 + q * 4 + rr;
-      if (r == 0 && i < len) rout[kh * Q + i] = v;
-    }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    if (q == 0 && rowok) rout[kh * Q + irow] = rsum;
   }
-  if (!active) return;
+  if (!rowok) return;
+  uint16_t* dcrow = dC + (int64_t)(ci.start + irow) * brow + (int64_t)g * N;
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = i0 + q * 4 + rr;
-      if (i < len) dC[(int64_t)(ci.start + i) * brow + (int64_t)g * N + nb * 16 + r] = f2bf(acc[nb][rr]);
-    }
+    *(uint2*)(dcrow + nb * 16 + q * 4) =
+        make_uint2(pack_bf2(acc[nb][0], acc[nb][1]), pack_bf2(acc[nb][2], acc[nb][3]));
 }
 
 // ------------------------------------------------------------ bwd_db bf16 ----
 // One workgroup per (chunk, group, 64 rows j).  dB_j = sum_{i>=j} dCB_g[i][j] C_i
-// (A fragments from the transposed dCB_g rows, C through LDS in 64-row pieces)
-// + sum_h w_j delta_j dT^T x_j (one K=headdim GEMM per head, dT staged in LDS).
+// (fragments from the transposed dCB_g rows, C through LDS in 64-row pieces)
+// + sum_h w_j delta_j dT^T x_j (one K=headdim GEMM per head).  Per head, dT = dE_c
+// (bf16) is staged in a double-buffered LDS tile and the next head's dT, x
+// fragments and decay scalars are loaded into registers while this head is
+// worked on.  Operands swapped as in bwd_dc: each lane owns one row j.
 template <int P, int N>
 __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dCBgT, const float* __restrict__ delta,
     const float* __restrict__ acs, const uint16_t* __restrict__ dE, uint16_t* __restrict__ dB) {
   constexpr int LDB = N + 16;
-  __shared__ __attribute__((aligned(16))) uint16_t ct[64 * LDB];
-  __shared__ __attribute__((aligned(16))) uint16_t dtt[P * LDB];
+  constexpr int ROWS = P > 64 ? P : 64;
+  constexpr int NPH = (P * N / 8 + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t ub[2][ROWS * LDB];
   const int T = m.Q / 64;
   const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
   const int tile = lid % T, k = lid / T / G, g = (lid / T) % G;
@@ -582,9 +606,11 @@ __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
   const int j0 = tile * 64 + w * 16;
   const bool active = j0 < len;
   const int jrow = j0 + r;
-  f32x4 acc[N / 16];
+  const bool rowok = jrow < len;
+  f32x4 acc[N / 16];  // acc[nb][rr] = dB[jrow][16 nb + 4 q + rr]
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* ct = ub[0];
   for (int it = tile; it * 64 < len; ++it) {
     __syncthreads();
     stage_rows<64, N>(ct, LDB, cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
@@ -592,44 +618,66 @@ __global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
     if (!active) continue;
     const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
     for (int ib = ib0; ib < min(it * 64 + 64, len); ib += 32) {
-      const bf16x8 a = as_bf16x8(jrow < len ? *(const u32x4*)(dcbt + (int64_t)jrow * Q + ib + q * 8)
-                                            : u32x4{0u, 0u, 0u, 0u});
+      const bf16x8 a = as_bf16x8(rowok ? *(const u32x4*)(dcbt + (int64_t)jrow * Q + ib + q * 8)
+                                       : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
-        acc[nb] = mfma_bf16(a, frag_kmajor(ct + (ib - it * 64) * LDB + nb * 16, LDB, lane), acc[nb]);
+        acc[nb] = mfma_bf16(frag_kmajor(ct + (ib - it * 64) * LDB + nb * 16, LDB, lane), a, acc[nb]);
     }
   }
+  u32x4 ph[NPH], px[P / 32];
+  float pl = 0.f, pj = 0.f, pd = 0.f;
+  auto load_head = [&](int h) {
+    const int64_t kh = (int64_t)k * H + h;
+    const uint16_t* src = dE + kh * (int64_t)(P * N);
+#pragma unroll
+    for (int c = 0; c < NPH; ++c) {
+      const int e = (tid + c * 256) * 8;
+      ph[c] = e < P * N ? *(const u32x4*)(src + e) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb)
+      px[kb] = rowok ? *(const u32x4*)(xb + (int64_t)jrow * xrow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    pl = acs[kh * Q + len - 1];
+    pj = rowok ? acs[kh * Q + jrow] : 0.f;
+    pd = rowok ? delta[kh * Q + jrow] : 0.f;
+  };
+  __syncthreads();  // every wave is done with the C pieces in ub[0]
+  load_head(g * hpg);
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
-    const int64_t kh = (int64_t)k * H + h;
+    uint16_t* dtt = ub[hh & 1];
+#pragma unroll
+    for (int c = 0; c < NPH; ++c) {
+      const int e = (tid + c * 256) * 8;
+      if (e < P * N) *(u32x4*)(dtt + (e / N) * LDB + (e % N)) = ph[c];
+    }
     __syncthreads();
-    stage_state_bf16<P, N>(dtt, LDB, dE + kh * (int64_t)(P * N), tid);
-    __syncthreads();
-    if (!active) continue;
-    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
-    const float* ac = acs + kh * Q;
-    const float sj = (jrow < len) ? exp2_fast(ac[len - 1] - ac[jrow]) * delta[kh * Q + jrow] : 0.f;
+    // this head's x fragment scaled by w_j delta_j (one row per lane)
+    const float sj = rowok ? exp2_fast(pl - pj) * pd : 0.f;
+    bf16x8 axs[P / 32];
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb) {
-      const u32x4 ax = (jrow < len) ? *(const u32x4*)(xb + (int64_t)jrow * xrow + kb * 32 + q * 8)
-                                    : u32x4{0u, 0u, 0u, 0u};
       u32x4 sv;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) sv[d] = pack_bf2(bf_lo(ax[d]) * sj, bf_hi(ax[d]) * sj);
-      const bf16x8 a = as_bf16x8(sv);
+      for (int d = 0; d < 4; ++d) sv[d] = pack_bf2(bf_lo(px[kb][d]) * sj, bf_hi(px[kb][d]) * sj);
+      axs[kb] = as_bf16x8(sv);
+    }
+    if (hh + 1 < hpg) load_head(h + 1);  // in flight during this head's work
+    if (!active) continue;
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb)
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
-        acc[nb] = mfma_bf16(a, frag_kmajor(dtt + kb * 32 * LDB + nb * 16, LDB, lane), acc[nb]);
-    }
+        acc[nb] = mfma_bf16(frag_kmajor(dtt + kb * 32 * LDB + nb * 16, LDB, lane), axs[kb], acc[nb]);
   }
-  if (!active) return;
+  if (!rowok) return;
+  uint16_t* dbrow = dB + (int64_t)(ci.start + jrow) * brow + (int64_t)g * N;
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int j = j0 + q * 4 + rr;
-      if (j < len) dB[(int64_t)(ci.start + j) * brow + (int64_t)g * N + nb * 16 + r] = f2bf(acc[nb][rr]);
-    }
+    *(uint2*)(dbrow + nb * 16 + q * 4) =
+        make_uint2(pack_bf2(acc[nb][0], acc[nb][1]), pack_bf2(acc[nb][2], acc[nb][3]));
 }
 
 // ------------------------------------------------------------ fp32 paths ----
