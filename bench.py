@@ -18,7 +18,6 @@ HIP events on the library's stream), the roofline of the dominant kernel, and
 the CPU oracle timed on a bounded sample.
 """
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -79,24 +78,6 @@ def kernel_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, d_final=False):
     }
 
 
-KERNEL_FILES = {
-    "chunk_cumsum": "k_cumsum.hip", "chunk_state": "k_chunk_state.hip",
-    "state_passing": "k_state_passing.hip", "bmm_chunk": "k_bmm.hip",
-    "chunk_scan": "k_chunk_scan.hip", "dstates": "k_chunk_state.hip",
-    "reverse_state_passing": "k_state_passing.hip", "bwd_dx": "k_bwd.hip", "bwd_dcb": "k_bwd.hip",
-    "bwd_dc": "k_bwd.hip", "bwd_db": "k_bwd.hip", "bwd_finalize": "k_bwd.hip",
-}
-
-
-def source_hash(kernel):
-    """Hash of the kernel's source file and the headers every kernel includes."""
-    h = hashlib.sha256()
-    for name in (KERNEL_FILES[kernel], "common.hpp", "internal.hpp"):
-        with open(os.path.join(ROOT, "mamba_ssd_chunked_03_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current source of this kernel (else None)."""
@@ -106,6 +87,7 @@ def load_traffic(kernel):
     with open(path) as f:
         t = json.load(f)
     e = t.get(kernel)
+    from mamba_ssd_chunked_03_amd.profiling import source_hash
     if not e or e.get("source_sha") != source_hash(kernel):
         return None
     return e.get("bytes_per_launch")

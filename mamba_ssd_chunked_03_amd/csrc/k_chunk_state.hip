@@ -30,8 +30,10 @@ __device__ __forceinline__ float token_scale(int mode, const float* dl, const fl
   return mode == kStateFwd ? dl[j] * exp2_fast(a_last - ac[j]) : exp2_fast(ac[j]);
 }
 
-template <int P, int N>
-__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H, int G, int mode,
+// MODE (kStateFwd / kStateDstates) is a template argument so that profiles
+// tell the forward chunk states and the backward adjoint states apart.
+template <int P, int N, int MODE>
+__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H, int G,
                                                                const uint16_t* __restrict__ X,
                                                                const uint16_t* __restrict__ Y,
                                                                const float* __restrict__ delta,
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H
     const float* dl = delta + kh * Q;
     const float* ac = acs + kh * Q;
     const float a_last = ac[len - 1];
-    for (int t = tid; t < Q; t += 256) sc[t] = (t < len) ? token_scale(mode, dl, ac, t, a_last) : 0.f;
+    for (int t = tid; t < Q; t += 256) sc[t] = (t < len) ? token_scale(MODE, dl, ac, t, a_last) : 0.f;
   }
   const int64_t xrow = (int64_t)H * P, yrow = (int64_t)G * N;
   const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
@@ -175,8 +177,13 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H,
 template <int P, int N>
 static void launch_cs_bf16(const Prob& p, const void* X, const void* Y, const float* delta,
                            const float* acs, float* out, int mode, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(256), 0, st,
-                     p.map, p.H, p.G, mode, (const uint16_t*)X, (const uint16_t*)Y, delta, acs, out);
+  if (mode == kStateFwd)
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwd>), dim3((unsigned)p.nck, p.H), dim3(256),
+                       0, st, p.map, p.H, p.G, (const uint16_t*)X, (const uint16_t*)Y, delta, acs, out);
+  else
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateDstates>), dim3((unsigned)p.nck, p.H),
+                       dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)X, (const uint16_t*)Y, delta,
+                       acs, out);
 }
 
 hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,

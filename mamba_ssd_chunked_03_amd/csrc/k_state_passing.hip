@@ -32,14 +32,16 @@
 
 namespace ssd {
 
-template <int W, int S, typename OutT>
+// REV (0 forward, 1 reverse) is a template argument so that profiles tell the
+// two directions apart.
+template <int W, int S, typename OutT, int REV>
 __global__ __launch_bounds__(W * 64) void state_passing_kernel(ChunkMap m, int H, int PN,
                                                                const float* __restrict__ T,
                                                                const float* __restrict__ decay,
                                                                const float* __restrict__ init,
                                                                OutT* __restrict__ Hout,
-                                                               float* __restrict__ final_states,
-                                                               int reverse) {
+                                                               float* __restrict__ final_states) {
+  constexpr bool reverse = REV != 0;
   __shared__ float4 sumB[W][64];  // segment summaries, b part
   __shared__ float sumL[W];       // segment summaries, log2 decay part
   __shared__ float cin[W][256];   // carry into each segment (scalar per element)
@@ -153,13 +155,19 @@ template <int W, int S>
 static void launch_sp(const Prob& p, dim3 grid, const float* states, const float* decay,
                       const float* init, void* passed, int passed_bf16, float* final_states,
                       int reverse, hipStream_t st) {
-  if (passed_bf16)
-    hipLaunchKernelGGL((state_passing_kernel<W, S, uint16_t>), grid, dim3(W * 64), 0, st, p.map,
-                       p.H, p.P * p.N, states, decay, init, (uint16_t*)passed, final_states,
-                       reverse);
+  const int PN = p.P * p.N;
+  if (passed_bf16 && reverse)
+    hipLaunchKernelGGL((state_passing_kernel<W, S, uint16_t, 1>), grid, dim3(W * 64), 0, st, p.map,
+                       p.H, PN, states, decay, init, (uint16_t*)passed, final_states);
+  else if (passed_bf16)
+    hipLaunchKernelGGL((state_passing_kernel<W, S, uint16_t, 0>), grid, dim3(W * 64), 0, st, p.map,
+                       p.H, PN, states, decay, init, (uint16_t*)passed, final_states);
+  else if (reverse)
+    hipLaunchKernelGGL((state_passing_kernel<W, S, float, 1>), grid, dim3(W * 64), 0, st, p.map,
+                       p.H, PN, states, decay, init, (float*)passed, final_states);
   else
-    hipLaunchKernelGGL((state_passing_kernel<W, S, float>), grid, dim3(W * 64), 0, st, p.map, p.H,
-                       p.P * p.N, states, decay, init, (float*)passed, final_states, reverse);
+    hipLaunchKernelGGL((state_passing_kernel<W, S, float, 0>), grid, dim3(W * 64), 0, st, p.map,
+                       p.H, PN, states, decay, init, (float*)passed, final_states);
 }
 
 hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,

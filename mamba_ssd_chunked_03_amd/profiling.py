@@ -1,0 +1,230 @@
+"""Summaries of rocprofv3 output for the kernels of the SSD path.
+
+Two inputs, both written by rocprofv3 with ``-f csv``:
+
+* a kernel trace (``--kernel-trace``): per-kernel launch counts and average
+  durations -> a markdown table;
+* counter runs (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``) of the same
+  program and of a plain copy of known size: HBM bytes per launch of every
+  kernel, each counter scaled by what it reads for the copy (so the result is
+  in bytes whatever unit and instance sum the counter uses) -> a JSON table
+  keyed by kernel, with a hash of the kernel's source so that a reader can tell
+  whether the numbers still describe the code.
+
+Kernels are named as bench.py names them; one "launch" of bwd_finalize is its
+two kernels (the per-chunk pass and the per-head reduction).
+
+    python -m mamba_ssd_chunked_03_amd.profiling stats TRACE.csv OUT.md --command "..."
+    python -m mamba_ssd_chunked_03_amd.profiling traffic --fetch F.csv --write W.csv \\
+        --copy-fetch CF.csv --copy-write CW.csv --copy-bytes 268435456 --out profiles/traffic.json
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import shlex
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+# kernel (as bench.py names it) -> source file holding it
+KERNEL_FILES = {
+    "chunk_cumsum": "k_cumsum.hip", "chunk_state": "k_chunk_state.hip",
+    "state_passing": "k_state_passing.hip", "bmm_chunk": "k_bmm.hip",
+    "chunk_scan": "k_chunk_scan.hip", "dstates": "k_chunk_state.hip",
+    "reverse_state_passing": "k_state_passing.hip", "bwd_dx": "k_bwd.hip", "bwd_dcb": "k_bwd.hip",
+    "bwd_dc": "k_bwd.hip", "bwd_db": "k_bwd.hip", "bwd_finalize": "k_bwd.hip",
+    "bmm_chunk_cb_only": "k_bmm.hip",  # C.B^T without its transpose (a forward that keeps nothing)
+}
+
+
+def source_hash(kernel):
+    """Hash of the kernel's source file and the headers every kernel includes."""
+    h = hashlib.sha256()
+    for name in (KERNEL_FILES[kernel], "common.hpp", "internal.hpp"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_key(name):
+    """bench.py's name for a launched kernel (None for kernels outside the path)."""
+    base = re.search(r"ssd::(\w+)", name)
+    if not base:
+        return None
+    base = base.group(1)
+    targs = re.search(r"<([^>]*)>", name)
+    last = targs.group(1).split(",")[-1].strip() if targs else ""
+    if base.startswith("chunk_state"):
+        return "dstates" if last == "1" else "chunk_state"
+    if base == "state_passing_kernel":
+        return "reverse_state_passing" if last == "1" else "state_passing"
+    if base.startswith("bmm_chunk_bf16"):
+        return "bmm_chunk_cb_only" if last == "false" else "bmm_chunk"
+    for prefix, key in (("chunk_cumsum", "chunk_cumsum"), ("bmm_chunk", "bmm_chunk"),
+                        ("chunk_scan", "chunk_scan"), ("bwd_dx_", "bwd_dx"), ("bwd_dcb_", "bwd_dcb"),
+                        ("bwd_dc_", "bwd_dc"), ("bwd_db_", "bwd_db"), ("bwd_finalize", "bwd_finalize"),
+                        ("bwd_reduce", "bwd_finalize"), ("copy_kernel", "copy")):
+        if base.startswith(prefix):
+            return key
+    return None
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError("none of %s in %s" % (names, list(row)))
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def kernel_times(trace_csv):
+    """{key: {"kernels": {name: [durations ns]}}} from a kernel-trace CSV."""
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for row in _rows(trace_csv):
+        name = _col(row, "Kernel_Name", "Name")
+        key = kernel_key(name)
+        if key is None:
+            continue
+        t = int(_col(row, "End_Timestamp")) - int(_col(row, "Start_Timestamp"))
+        short = re.search(r"ssd::(\w+(?:<[^>]*>)?)", name).group(1)
+        out[key][short].append(t)
+    return out
+
+
+def stats_table(trace_csv, command, summary_cmd=""):
+    times = kernel_times(trace_csv)
+    lines = ["Profiled with (from the repository root, one MI355X):", "", "    " + command, ""]
+    if summary_cmd:
+        lines += ["Summarised with:", "", "    " + summary_cmd, ""]
+    lines += ["Per kernel of the path (bench.py's names): launches and average duration from the "
+              "kernel trace; a bwd_finalize launch is its two kernels.", "",
+             "| Kernel | Launched kernels | Launches | Average (us) | Min (us) | Max (us) |",
+             "|---|---|---|---|---|---|"]
+    total = {}
+    for key in KERNEL_FILES:
+        if key not in times:
+            continue
+        ks = times[key]
+        n = min(len(v) for v in ks.values())
+        avg = sum(sum(v) / len(v) for v in ks.values()) / 1e3
+        mn = sum(min(v) for v in ks.values()) / 1e3
+        mx = sum(max(v) for v in ks.values()) / 1e3
+        total[key] = avg
+        lines.append("| %s | %s | %d | %.1f | %.1f | %.1f |" % (
+            key, ", ".join("`%s`" % s for s in sorted(ks)), n, avg, mn, mx))
+    lines += ["", "Sum of the averages (one of each kernel): %.1f us" % sum(total.values())]
+    return "\n".join(lines) + "\n", total
+
+
+def counter_means(counter_csv, counter):
+    """{key: (mean value per launch, launches)} for one counter; a launch of a
+    multi-kernel key sums its kernels' means."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for row in _rows(counter_csv):
+        if _col(row, "Counter_Name") != counter:
+            continue
+        name = _col(row, "Kernel_Name")
+        key = kernel_key(name)
+        if key is None:
+            continue
+        per[key][name].append(float(_col(row, "Counter_Value")))
+    return {k: (sum(sum(v) / len(v) for v in d.values()), min(len(v) for v in d.values()))
+            for k, d in per.items()}
+
+
+def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    cf = counter_means(copy_fetch_csv, "FETCH_SIZE")["copy"][0]
+    cw = counter_means(copy_write_csv, "WRITE_SIZE")["copy"][0]
+    fs, ws = copy_bytes / cf, copy_bytes / cw
+    fetch = counter_means(fetch_csv, "FETCH_SIZE")
+    write = counter_means(write_csv, "WRITE_SIZE")
+    out = {"_calibration": {"copy_bytes": copy_bytes, "fetch_bytes_per_unit": fs,
+                            "write_bytes_per_unit": ws}}
+    for key in KERNEL_FILES:
+        if key not in fetch or key not in write:
+            continue
+        fb, wb = fetch[key][0] * fs, write[key][0] * ws
+        out[key] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                    "bytes_per_launch": round(fb + wb), "launches": fetch[key][1],
+                    "source_sha": source_hash(key)}
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("trace", help="kernel trace CSV, or a directory searched for one")
+    s.add_argument("out")
+    s.add_argument("--title", default="")
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    for n in ("fetch", "write", "copy-fetch", "copy-write"):
+        t.add_argument("--" + n, required=True, help="counter CSV, or a directory searched for one")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--md", help="also write a markdown summary here")
+    t.add_argument("--title", default="")
+    t.add_argument("--command", action="append", default=[],
+                   help="a profiling command to record in the markdown (repeatable)")
+    a = ap.parse_args(argv)
+    here = "python -m mamba_ssd_chunked_03_amd.profiling " + shlex.join(argv if argv else sys.argv[1:])
+
+    def csv_in(p, kind):
+        return p if os.path.isfile(p) else _one(os.path.join(p, "**", "*%s.csv" % kind))
+
+    if a.cmd == "stats":
+        text, _ = stats_table(csv_in(a.trace, "kernel_trace"), a.command, here)
+        with open(a.out, "w") as f:
+            f.write(("# " + a.title + "\n\n" if a.title else "") + text)
+    else:
+        res = traffic(csv_in(a.fetch, "counter_collection"), csv_in(a.write, "counter_collection"),
+                      csv_in(a.copy_fetch, "counter_collection"),
+                      csv_in(a.copy_write, "counter_collection"), a.copy_bytes)
+        with open(a.out, "w") as f:
+            json.dump(res, f, indent=1, sort_keys=True)
+            f.write("\n")
+        if a.md:
+            with open(a.md, "w") as f:
+                f.write(traffic_md(res, a.title, a.command, here))
+
+
+def traffic_md(res, title, commands, summary_cmd):
+    cal = res["_calibration"]
+    lines = (["# " + title, ""] if title else []) + [
+        "Counter runs (from the repository root, one MI355X, one rocprofv3 pass each):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "Summarised with:", "", "    " + summary_cmd, "",
+              "Calibration: a copy of %d bytes reads as %.1f bytes per FETCH_SIZE unit and %.1f "
+              "bytes per WRITE_SIZE unit; every kernel's counters are scaled by those factors."
+              % (cal["copy_bytes"], cal["fetch_bytes_per_unit"], cal["write_bytes_per_unit"]), "",
+              "| Kernel | HBM read (MB) | HBM written (MB) | Total per launch (MB) | Source hash |",
+              "|---|---|---|---|---|"]
+    for key in KERNEL_FILES:
+        if key in res:
+            e = res[key]
+            lines.append("| %s | %.1f | %.1f | %.1f | %s |" % (
+                key, e["fetch_bytes"] / 1e6, e["write_bytes"] / 1e6, e["bytes_per_launch"] / 1e6,
+                e["source_sha"]))
+    return "\n".join(lines) + "\n"
+
+
+if __name__ == "__main__":
+    main()

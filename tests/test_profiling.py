@@ -1,0 +1,60 @@
+"""CPU tests of the rocprofv3 summary helpers (synthetic CSV input)."""
+import csv
+import json
+
+from mamba_ssd_chunked_03_amd import profiling
+
+TRACE_COLS = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+PMC_COLS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def write(path, cols, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        w.writerows(rows)
+    return str(path)
+
+
+def test_kernel_keys():
+    k = profiling.kernel_key
+    assert k("void ssd::chunk_state_bf16_kernel<64, 128, 0>(ssd::ChunkMap)") == "chunk_state"
+    assert k("void ssd::chunk_state_bf16_kernel<64, 128, 1>(ssd::ChunkMap)") == "dstates"
+    assert k("void ssd::state_passing_kernel<16, 4, unsigned short, 1>(x)") == "reverse_state_passing"
+    assert k("void ssd::state_passing_kernel<16, 4, unsigned short, 0>(x)") == "state_passing"
+    assert k("void ssd::bwd_dc_bf16_kernel<64, 128>(x)") == "bwd_dc"
+    assert k("void ssd::bwd_dcb_bf16_kernel<64>(x)") == "bwd_dcb"
+    assert k("void ssd::bwd_reduce_kernel(int)") == "bwd_finalize"
+    assert k("void ssd::bmm_chunk_bf16_kernel<128, true>(x)") == "bmm_chunk"
+    assert k("void ssd::bmm_chunk_bf16_kernel<128, false>(x)") == "bmm_chunk_cb_only"
+    assert k("void at::native::elementwise_kernel<4>(x)") is None
+
+
+def test_stats_table(tmp_path):
+    rows = [["void ssd::bwd_dx_bf16_kernel<64, 128>(a)", 100, 1100],
+            ["void ssd::bwd_dx_bf16_kernel<64, 128>(a)", 2000, 5000],
+            ["void ssd::bwd_finalize_kernel(a)", 0, 500],
+            ["void ssd::bwd_reduce_kernel(a)", 600, 700],
+            ["void at::native::other(a)", 0, 99999]]
+    p = write(tmp_path / "t.csv", TRACE_COLS, rows)
+    text, total = profiling.stats_table(p, "cmd")
+    assert abs(total["bwd_dx"] - 2.0) < 1e-9            # (1000 + 3000) / 2 ns
+    assert abs(total["bwd_finalize"] - 0.6) < 1e-9      # 500 + 100 ns per launch
+    assert "| bwd_dx |" in text and "other" not in text
+
+
+def test_traffic_calibration(tmp_path):
+    copy = "void ssd::copy_kernel(a)"
+    dx = "void ssd::bwd_dx_bf16_kernel<64, 128>(a)"
+    cf = write(tmp_path / "cf.csv", PMC_COLS, [[1, copy, "FETCH_SIZE", 131072.0]])   # 256 MiB read
+    cw = write(tmp_path / "cw.csv", PMC_COLS, [[1, copy, "WRITE_SIZE", 262144.0]])
+    f = write(tmp_path / "f.csv", PMC_COLS, [[5, dx, "FETCH_SIZE", 1000.0], [6, dx, "FETCH_SIZE", 3000.0]])
+    w = write(tmp_path / "w.csv", PMC_COLS, [[5, dx, "WRITE_SIZE", 512.0]])
+    res = profiling.traffic(f, w, cf, cw, 268435456)
+    assert res["bwd_dx"]["fetch_bytes"] == 2000 * 2048  # each counter unit is 2 KiB here
+    assert res["bwd_dx"]["write_bytes"] == 512 * 1024
+    assert res["bwd_dx"]["source_sha"] == profiling.source_hash("bwd_dx")
+    out = tmp_path / "t.json"
+    profiling.main(["traffic", "--fetch", f, "--write", w, "--copy-fetch", cf, "--copy-write", cw,
+                    "--copy-bytes", "268435456", "--out", str(out)])
+    assert json.load(open(out))["bwd_dx"]["bytes_per_launch"] == 2000 * 2048 + 512 * 1024
