@@ -141,6 +141,21 @@ def test_saved_context_matches_recompute(packed):
         assert torch.equal(g0[k], g1[k]), k
 
 
+def test_bwd_full_size_packed_sampled_heads():
+    # the packed workload (65536 tokens in sequences of 512..16384, per-sequence
+    # init states): per-head gradients of two sampled heads against the oracle
+    inp = inputs.config_inputs(4)
+    inp["d_final"] = None
+    g = gpu_bwd(ssd, inp, 256)
+    torch.cuda.synchronize()
+    for k in KEYS:
+        assert torch.isfinite(g[k].float()).all(), k
+    heads = [7, 50]
+    ref = oracle_bwd(inp, heads=heads)
+    check(g, ref, "bf16", "config 4 sampled", keys=["dx", "ddt", "dA", "dD", "d_dt_bias", "d_init"],
+          heads=heads)
+
+
 def test_bwd_full_size_sampled_heads():
     # the layer workload (batch 2, seqlen 8192, 64 heads): per-head gradients of two
     # sampled heads against the oracle run on those heads alone

@@ -196,7 +196,7 @@ def test_stages(kw, lengths, Q):
 
 
 # ------------------------------------------------- full sizes, sampled heads ----
-@pytest.mark.parametrize("cfg,heads", [(1, [0, 21, 63]), (3, [5, 30])])
+@pytest.mark.parametrize("cfg,heads", [(1, [0, 21, 63]), (3, [5, 30]), (4, [7, 50])])
 def test_full_size_sampled(cfg, heads):
     inp = inputs.config_inputs(cfg)
     y, final = gpu_fwd(ssd, inp, inputs.CONFIGS[cfg]["chunk"])
