@@ -29,9 +29,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   __bf16 b = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint16_t, b);
 }
-// two floats -> packed bf16 pair (lo in bits 0..15)
+// two floats -> packed bf16 pair (lo in bits 0..15): one v_cvt_pk_bf16_f32 with
+// both sources (converting the two halves separately costs two converts, a
+// shift and an or)
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const f32x2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -133,6 +138,30 @@ __device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const fl
     }
   }
 }
+
+// stage_rows split in two, so that several tiles' loads (and other loads) can
+// all be in flight before the first LDS store waits for its data.
+template <int ROWS, int W, int NT = 256>
+struct RowTile {
+  static constexpr int PER = W / 8;
+  static constexpr int NC = (ROWS * PER + NT - 1) / NT;
+  u32x4 t[NC];
+  __device__ __forceinline__ void load(const uint16_t* src, int64_t srow, int nvalid, int tid) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e = tid + c * NT, j = e / PER, c8 = e % PER;
+      t[c] = (e < ROWS * PER && j < nvalid) ? *(const u32x4*)(src + (int64_t)j * srow + c8 * 8)
+                                            : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int ld, int tid) const {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e = tid + c * NT, j = e / PER, c8 = e % PER;
+      if (e < ROWS * PER) *(u32x4*)(dst + j * ld + c8 * 8) = t[c];
+    }
+  }
+};
 
 // bf16 P x N state (row-major) -> bf16 LDS [p][n] with row stride ld.
 template <int P, int N, int NT = 256>

@@ -75,13 +75,36 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   const uint16_t* bb = Bm + (int64_t)ci.start * brow + (int64_t)g * N;
   const uint16_t* cbt = CBt + ((int64_t)k * G + g) * Q * Q;
 
-  for (int t = tid; t < Q; t += kDxWaves * 64) {
-    sa[t] = acs[kh * Q + t];
-    sd[t] = delta[kh * Q + t];
-  }
-  // dy tile, token-major (rows past the chunk's end are zero)
-  stage_rows<QMAX, P, kDxWaves * 64>(dyt, LDY, dyb, xrow, len, tid);
-  // dT = dE_c (bf16) into LDS [p][n]; alpha <dE, H> in fp32 on the way (loads first)
+  // Row blocks of this wave (snake order), and their x values, B rows and first
+  // and diagonal CBt fragments: the next row block's are loaded before the
+  // current one's stores, so the wait for them does not also wait for those
+  // stores (one in-order memory counter); the first row block's are in flight
+  // during the prologue.
+  const int NB = Q / 16, nii = (NB + kDxWaves - 1) / kDxWaves;
+  auto rb_of = [&](int ii) { return kDxWaves * ii + ((ii & 1) ? (kDxWaves - 1 - w) : w); };
+  auto live = [&](int ii) { return ii < nii && rb_of(ii) < NB && rb_of(ii) * 16 < len; };
+  uint2 px[P / 16];
+  u32x4 bq[N / 32], pc1, pcd;
+  auto load_rb = [&](int rb) {
+    const int jr = rb * 16 + r, c0 = rb / 2;
+    const bool ok = jr < len, off = ok && c0 + 1 < (len + 31) / 32;
+#pragma unroll
+    for (int tp = 0; tp < P / 16; ++tp)
+      px[tp] = ok ? *(const uint2*)(xb + (int64_t)jr * xrow + tp * 16 + q * 4) : make_uint2(0u, 0u);
+#pragma unroll
+    for (int kk = 0; kk < N / 32; ++kk)
+      bq[kk] = ok ? *(const u32x4*)(bb + (int64_t)jr * brow + kk * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    pc1 = off ? *(const u32x4*)(cbt + (int64_t)jr * Q + (c0 + 1) * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    pcd = ok ? *(const u32x4*)(cbt + (int64_t)jr * Q + c0 * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+  };
+  if (live(0)) load_rb(rb_of(0));
+  // every prologue load in flight before the first LDS store waits on one:
+  // acs/delta, the dy tile (token-major, rows past the chunk's end zero), and
+  // dT = dE_c (bf16, into LDS [p][n]) with H_c for alpha <dE, H> in fp32
+  static_assert(QMAX <= kDxWaves * 64, "one acs/delta value per thread");
+  const float av = tid < Q ? acs[kh * Q + tid] : 0.f, dv = tid < Q ? delta[kh * Q + tid] : 0.f;
+  RowTile<QMAX, P, kDxWaves * 64> ytile;
+  ytile.load(dyb, xrow, len, tid);
   float dot = 0.f;
   {
     constexpr int NT = kDxWaves * 64, NC = (P * N / 8 + NT - 1) / NT;
@@ -93,6 +116,11 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
       const int e = (tid + c * NT) * 8;
       ta[c] = (e < P * N) ? *(const u32x4*)(de + e) : u32x4{0u, 0u, 0u, 0u};
       tb[c] = (e < P * N) ? *(const u32x4*)(hh + e) : u32x4{0u, 0u, 0u, 0u};
+    }
+    ytile.store(dyt, LDY, tid);
+    if (tid < Q) {
+      sa[tid] = av;
+      sd[tid] = dv;
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -117,12 +145,10 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   const float Dh = D ? D[h] : 0.f;
   const float a_last = sa[len - 1];
   float s_sum = 0.f, dxx_sum = 0.f;  // lanes q == 0 accumulate their rows
-  const int NB = Q / 16;
-  for (int ii = 0; ii * kDxWaves < NB; ++ii) {
-    const int rb = kDxWaves * ii + ((ii & 1) ? (kDxWaves - 1 - w) : w);
-    if (rb >= NB) continue;  // chunk sizes with fewer row blocks than wavefronts
+  for (int ii = 0; ii < nii; ++ii) {
+    if (!live(ii)) continue;  // chunk sizes with fewer row blocks than wavefronts, short chunks
+    const int rb = rb_of(ii);
     const int j0 = rb * 16;
-    if (j0 >= len) continue;
     // Products are issued with the operands swapped, so each lane holds the
     // transposed tile acc[tp][rr] = (dx bracket)[j0 + r][16 tp + 4 q + rr]: the
     // lane owns row jrow, row factors are one value per lane, row dots reduce
@@ -138,19 +164,16 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     const bool has_off = cb0 + 1 < s_end;
     const float ae = has_off ? sa[e] : 0.f;
     const float aj = sa[jrow];                     // jrow < Q always
-    // this lane's x values, 4 adjacent per tp
-    uint2 xq[P / 16];
+    uint2 xq[P / 16];                              // this lane's x values, 4 adjacent per tp
 #pragma unroll
-    for (int tp = 0; tp < P / 16; ++tp)
-      xq[tp] = rowok ? *(const uint2*)(xb + (int64_t)jrow * xrow + tp * 16 + q * 4) : make_uint2(0u, 0u);
+    for (int tp = 0; tp < P / 16; ++tp) xq[tp] = px[tp];
     // state part: sum_n B_j[n] dT[p][n]
 #pragma unroll
-    for (int kk = 0; kk < N; kk += 32) {
-      const bf16x8 b = as_bf16x8(rowok ? *(const u32x4*)(bb + (int64_t)jrow * brow + kk + q * 8)
-                                       : u32x4{0u, 0u, 0u, 0u});
+    for (int kk = 0; kk < N / 32; ++kk) {
+      const bf16x8 b = as_bf16x8(bq[kk]);
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(dts + (tp * 16 + r) * LDT + kk + q * 8)), b, acc[tp]);
+        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(dts + (tp * 16 + r) * LDT + kk * 32 + q * 8)), b, acc[tp]);
     }
     const float wj = rowok ? exp2_fast(a_last - aj) : 0.f;
     float xs = 0.f;
@@ -166,8 +189,7 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= s0;
       const float* wrow = &wt[cb0][0];
-      u32x4 cvn = rowok ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (cb0 + 1) * 32 + q * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
+      u32x4 cvn = pc1;
       for (int sx = cb0 + 1; sx < s_end; ++sx) {
         const u32x4 cv = cvn;
         if (sx + 1 < s_end)  // one step of lookahead
@@ -194,8 +216,7 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     }
     // the diagonal block, one exp per element: CBt[j][i] 2^(acs_i - acs_j), j <= i < len
     {
-      const u32x4 cv = rowok ? *(const u32x4*)(cbt + (int64_t)jrow * Q + cb0 * 32 + q * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 cv = pcd;
       u32x4 av;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -211,6 +232,7 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
       for (int tp = 0; tp < P / 16; ++tp)
         acc[tp] = mfma_bf16(frag_kmajor(dyt + cb0 * 32 * LDY + tp * 16, LDY, lane), a, acc[tp]);
     }
+    if (live(ii + 1)) load_rb(rb_of(ii + 1));  // the fragments above are dead now
     // per-row dots and the store
     const float dj = rowok ? sd[jrow] : 0.f;
     float xt = 0.f, dxx = 0.f;
@@ -583,7 +605,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
 // fragments and decay scalars are loaded into registers while this head is
 // worked on.  Operands swapped as in bwd_dc: each lane owns one row j.
 template <int P, int N>
-__global__ __launch_bounds__(256) void bwd_db_bf16_kernel(
+__global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dCBgT, const float* __restrict__ delta,
     const float* __restrict__ acs, const uint16_t* __restrict__ dE, uint16_t* __restrict__ dB) {

@@ -63,12 +63,49 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
   const uint16_t* cb = Cm + (int64_t)ci.start * crow + (int64_t)g * N;
   const uint16_t* cbm = CB + ((int64_t)k * G + g) * Q * Q;
 
-  for (int t = tid; t < Q; t += kScanWaves * 64) {
-    sa[t] = acs[kh * Q + t];
-    sd[t] = delta[kh * Q + t];
+  // Row blocks of this wave (snake order), and their C / CB fragments: the next
+  // row block's are loaded before the current one's stores, so the wait for
+  // them does not also wait for those stores (one in-order memory counter);
+  // the first row block's are in flight during the prologue.
+  const int NB = Q / 16, nii = (NB + kScanWaves - 1) / kScanWaves;
+  auto rb_of = [&](int ii) { return kScanWaves * ii + ((ii & 1) ? (kScanWaves - 1 - w) : w); };
+  auto live = [&](int ii) { return ii < nii && rb_of(ii) < NB && rb_of(ii) * 16 < len; };
+  // (the diagonal fragment has its own register: indexing the array with the
+  // run-time block index would become a select over every element)
+  u32x4 cf[N / 32], cbf[QMAX / 32], cbd;
+  auto load_rb = [&](int rb) {
+    const int irow = rb * 16 + r, nb = rb / 2;
+    const bool ok = irow < len;
+#pragma unroll
+    for (int kb = 0; kb < N / 32; ++kb)
+      cf[kb] = ok ? *(const u32x4*)(cb + (int64_t)irow * crow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int sx = 0; sx < QMAX / 32; ++sx)
+      cbf[sx] = (ok && sx < nb) ? *(const u32x4*)(cbm + (int64_t)irow * Q + sx * 32 + q * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
+    cbd = ok ? *(const u32x4*)(cbm + (int64_t)irow * Q + nb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+  };
+  if (live(0)) load_rb(rb_of(0));
+  {
+    // every prologue load in flight before the first LDS store waits on one
+    static_assert(QMAX <= kScanWaves * 64, "one acs/delta value per thread");
+    const float av = tid < Q ? acs[kh * Q + tid] : 0.f, dv = tid < Q ? delta[kh * Q + tid] : 0.f;
+    RowTile<QMAX, P, kScanWaves * 64> xt;
+    xt.load(xb, xrow, len, tid);
+    if constexpr (sizeof(HT) == 2) {
+      RowTile<P, N, kScanWaves * 64> ht;
+      ht.load((const uint16_t*)(Hs + kh * (int64_t)(P * N)), N, P, tid);
+      xt.store(xs, LDX, tid);
+      ht.store(hs, HLD, tid);
+    } else {
+      xt.store(xs, LDX, tid);
+      stage_state_bf16<P, N, kScanWaves * 64>(hs, HLD, Hs + kh * (int64_t)(P * N), tid);
+    }
+    if (tid < Q) {
+      sa[tid] = av;
+      sd[tid] = dv;
+    }
   }
-  stage_rows<QMAX, P, kScanWaves * 64>(xs, LDX, xb, xrow, len, tid);
-  stage_state_bf16<P, N, kScanWaves * 64>(hs, HLD, Hs + kh * (int64_t)(P * N), tid);
   __syncthreads();
   // column factors for anchor e = 32b - 1: 2^(acs_e - acs_j) delta_j for j <= e
   for (int idx = tid; idx < (Q / 32) * Q; idx += kScanWaves * 64) {
@@ -78,27 +115,14 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
   __syncthreads();
 
   const float Dh = D ? D[h] : 0.f;
-  const int NB = Q / 16;
-  for (int ii = 0; ii * kScanWaves < NB; ++ii) {
-    const int rb = kScanWaves * ii + ((ii & 1) ? (kScanWaves - 1 - w) : w);
-    if (rb >= NB) continue;  // chunk sizes with fewer row blocks than wavefronts
+  for (int ii = 0; ii < nii; ++ii) {
+    if (!live(ii)) continue;  // chunk sizes with fewer row blocks than wavefronts, short chunks
+    const int rb = rb_of(ii);
     const int i0 = rb * 16;
-    if (i0 >= len) continue;
-    const int irow = i0 + r;  // the A-fragment row of this lane
+    const int irow = i0 + r;  // the output row of this lane
     const bool rowok = irow < len;
     const int nb = i0 / 32;   // 32-token blocks strictly before the diagonal block
     const float ae = nb > 0 ? sa[32 * nb - 1] : 0.f;
-    // (the diagonal fragment has its own register: indexing the array with the
-    // run-time nb would become a select over every element)
-    u32x4 cf[N / 32], cbf[QMAX / 32], cbd;
-#pragma unroll
-    for (int kb = 0; kb < N / 32; ++kb)
-      cf[kb] = rowok ? *(const u32x4*)(cb + (int64_t)irow * crow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int sx = 0; sx < QMAX / 32; ++sx)
-      cbf[sx] = (rowok && sx < nb) ? *(const u32x4*)(cbm + (int64_t)irow * Q + sx * 32 + q * 8)
-                                   : u32x4{0u, 0u, 0u, 0u};
-    cbd = rowok ? *(const u32x4*)(cbm + (int64_t)irow * Q + nb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
     // The products are issued with the operands swapped, so each lane holds the
     // transposed tile: acc[tp][rr] = y[i0 + r][16 tp + 4 q + rr].  A row factor
     // is then one value per lane, and each lane's 4 outputs per tp are adjacent.
@@ -159,6 +183,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
       for (int tp = 0; tp < P / 16; ++tp)
         acc[tp] = mfma_bf16(frag_kmajor(xs + nb * 32 * LDX + tp * 16, LDX, lane), a, acc[tp]);
     }
+    if (live(ii + 1)) load_rb(rb_of(ii + 1));  // the fragments above are dead now
     // 5. skip term and 8-byte stores of the lane's 4 adjacent outputs
     if (rowok) {
       uint16_t* yrow = Y + (int64_t)(ci.start + irow) * xrow + (int64_t)h * P;

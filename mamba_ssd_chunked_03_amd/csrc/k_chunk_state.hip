@@ -33,7 +33,7 @@ __device__ __forceinline__ float token_scale(int mode, const float* dl, const fl
 // MODE (kStateFwd / kStateDstates) is a template argument so that profiles
 // tell the forward chunk states and the backward adjoint states apart.
 template <int P, int N, int MODE>
-__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H, int G,
+__global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, int H, int G,
                                                                const uint16_t* __restrict__ X,
                                                                const uint16_t* __restrict__ Y,
                                                                const float* __restrict__ delta,
@@ -59,12 +59,6 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H
   const int g = h / (H / G);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t kh = (int64_t)k * H + h;
-  {
-    const float* dl = delta + kh * Q;
-    const float* ac = acs + kh * Q;
-    const float a_last = ac[len - 1];
-    for (int t = tid; t < Q; t += 256) sc[t] = (t < len) ? token_scale(MODE, dl, ac, t, a_last) : 0.f;
-  }
   const int64_t xrow = (int64_t)H * P, yrow = (int64_t)G * N;
   const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
   const uint16_t* yb = Y + (int64_t)ci.start * yrow + (int64_t)g * N;
@@ -91,8 +85,14 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H
       yr[c] = (j < len) ? *(const u32x4*)(yb + (int64_t)j * yrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  load_slice(0);  // independent of the token scales: in flight while they are formed
+  {
+    const float* dl = delta + kh * Q;
+    const float* ac = acs + kh * Q;
+    const float a_last = ac[len - 1];
+    for (int t = tid; t < Q; t += 256) sc[t] = (t < len) ? token_scale(MODE, dl, ac, t, a_last) : 0.f;
+  }
   __syncthreads();
-  load_slice(0);
   for (int s0 = 0; s0 < len; s0 += KS) {
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
@@ -129,21 +129,22 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(ChunkMap m, int H
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) {
-          acc[i][jj] = mfma_bf16(ah[i], bv[jj], acc[i][jj]);
-          acc[i][jj] = mfma_bf16(al[i], bv[jj], acc[i][jj]);
+          acc[i][jj] = mfma_bf16(bv[jj], ah[i], acc[i][jj]);
+          acc[i][jj] = mfma_bf16(bv[jj], al[i], acc[i][jj]);
         }
     }
     __syncthreads();
   }
+  // operands were swapped: acc[i][jj][rr] = T[p0 + 16 i + r][n0 + 16 jj + 4 q + rr], so each
+  // lane stores 16 contiguous bytes
   const int q = lane >> 4;
   float* ob = out + kh * (int64_t)(P * N);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        ob[(p0 + i * 16 + q * 4 + rr) * N + n0 + jj * 16 + r] = acc[i][jj][rr];
+      *(float4*)(ob + (p0 + i * 16 + r) * N + n0 + jj * 16 + q * 4) =
+          make_float4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
 }
 
 // fp32: grid (chunk, head, output blocks of 256 elements)
