@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 
 METRIC = "SSD layer tokens/s + ms/call (fwd, fwd+bwd) & % HBM peak, B=2 L=8192"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
+FLUSH_BYTES = 512 << 20         # > the 256 MB last-level cache, read before each cold call
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -78,6 +80,25 @@ def kernel_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, d_final=False):
     }
 
 
+def kernel_flops(B, L, H, P, N, G, Q, nck):
+    """Algorithmic matrix-product flops of each kernel (causal triangles only;
+    the bf16 hi/lo split of chunk_state is not counted).  Kernels without
+    products are absent."""
+    tok = B * L
+    state = 2 * tok * H * P * N                 # a per-token P x N contraction
+    tri = Q * (Q + 1)                           # 2 x causal entries of one chunk
+    return {
+        "chunk_state": state,
+        "bmm_chunk": nck * G * N * tri,
+        "chunk_scan": nck * H * P * tri + state,
+        "dstates": state,
+        "bwd_dx": nck * H * P * tri + state,
+        "bwd_dcb": nck * H * P * tri,
+        "bwd_dc": nck * G * N * tri + state,
+        "bwd_db": nck * G * N * tri + state,
+    }
+
+
 def load_traffic(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current source of this kernel (else None)."""
@@ -98,8 +119,10 @@ def cpu_baseline(with_bwd, budget_s=10.0):
     row 0 with all 64 heads, in windows of 512 tokens (fresh seeded inputs per
     window) until about ``budget_s`` seconds of CPU work; the oracle's cost is
     linear in tokens at a fixed head count, so tokens/s carries over."""
+    import threadpoolctl
     from mamba_ssd_chunked_03_amd import inputs
     from oracle import recurrence
+    threadpoolctl.threadpool_limits(1)  # the reported core count is the one used
     T = 512
     done, sec = 0, 0.0
     while sec < budget_s and done < 8192:
@@ -117,6 +140,52 @@ def cpu_baseline(with_bwd, budget_s=10.0):
             "sample": "batch row 0, 64 heads, %d tokens in 512-token windows, %s, fp64 numpy "
                       "token loop, %.1f s" % (done, "fwd+bwd" if with_bwd else "fwd", sec),
             "cpu": platform.processor() or platform.machine()}
+
+
+def _worker_init():
+    sys.path.insert(0, ROOT)
+    import threadpoolctl
+    threadpoolctl.threadpool_limits(1)  # one thread per worker: cores = workers
+    from mamba_ssd_chunked_03_amd import inputs  # noqa: F401  (imports before timing)
+    from oracle import recurrence  # noqa: F401
+
+
+def _oracle_window(args):
+    """One 512-token window of the oracle on a subset of heads (a worker task)."""
+    seed, heads, with_bwd = args
+    if seed < 0:
+        return 0.0  # start-up task
+    from mamba_ssd_chunked_03_amd import inputs
+    from oracle import recurrence
+    inp = inputs.make_inputs(1, 512, 64, 64, 128, 8, io="bf16", bwd=True, seed=seed)
+    a = inputs.to_f64(inp)
+    t0 = time.perf_counter()
+    recurrence.fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], D=a["D"], dt_bias=a["dt_bias"],
+                   init=a["init"], dt_softplus=True, heads=heads)
+    if with_bwd:
+        recurrence.bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["dout"], D=a["D"],
+                       dt_bias=a["dt_bias"], init=a["init"], dt_softplus=True, heads=heads)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_parallel(with_bwd):
+    """The same oracle with independent 512-token windows (all 64 heads each)
+    spread over a process pool, one window per worker (spawned workers: they
+    import only numpy and the oracle)."""
+    import multiprocessing as mp
+    nproc = max(1, min(16, os.cpu_count() or 1))
+    windows = nproc
+    tasks = [(100 + 512 * wi, None, with_bwd) for wi in range(windows)]
+    with mp.get_context("spawn").Pool(nproc, initializer=_worker_init) as pool:
+        pool.map(_oracle_window, [(-1, None, False)] * nproc, chunksize=1)  # workers started
+        t0 = time.perf_counter()
+        pool.map(_oracle_window, tasks, chunksize=1)
+        sec = time.perf_counter() - t0
+    done = 512 * windows
+    return {"value": round(done / sec, 2), "unit": "tokens/s", "cores": nproc, "kind": "oracle",
+            "sample": "batch row 0, 64 heads, %d tokens in 512-token windows, one per "
+                      "single-threaded process of %d (input generation included), %s, %.1f s"
+                      % (done, nproc, "fwd+bwd" if with_bwd else "fwd", sec)}
 
 
 def main():
@@ -185,6 +254,42 @@ def main():
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return e0.elapsed_time(e1) / steps, wall
 
+    def trials(fn, per, n=7, warmup=2):
+        """median / min / max ms per call over n back-to-back windows of `per` calls"""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        res = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(per):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / per)
+        res.sort()
+        return res[n // 2], res[0], res[-1]
+
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def cold(fn, n=7):
+        """median ms of single calls, each after a 512 MiB read (outside the event pair)
+        that replaces the last-level cache's contents with clean lines"""
+        st = torch.cuda.current_stream()
+        res = []
+        for _ in range(n):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1))
+        res.sort()
+        return res[n // 2]
+
     def step():
         if have_bwd:
             fwd_save()
@@ -206,6 +311,10 @@ def main():
         ms_step_rc, _ = timed(step_recompute, args.steps, 2)
     tokens = Bsz * L
     print("bench: step %.3f ms (wall %.3f), fwd %.3f ms" % (ms_step, wall_step, ms_fwd), file=sys.stderr, flush=True)
+    step_med, step_min, step_max = trials(step, max(1, args.steps // 2))
+    step_cold = cold(step)
+    print("bench: step over 7 trials: median %.3f ms (min %.3f, max %.3f); cold %.3f ms"
+          % (step_med, step_min, step_max, step_cold), file=sys.stderr, flush=True)
 
     # every kernel of the step on its own: the same launch (arguments, grid,
     # buffers) as inside the step, re-issued through the single-kernel flags
@@ -218,6 +327,7 @@ def main():
         nck = ssd.num_chunks(prob, Q, 0)
         nbytes = kernel_bytes(Bsz, L, H, P, N, G, Q, nck, Bsz, 2, init=init is not None,
                               d_final=False)
+        nflops = kernel_flops(Bsz, L, H, P, N, G, Q, nck)
         fns = {}
         for k, name in enumerate(ssd.FWD_KERNELS, 1):
             fns[name] = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_b, out=y, final=final,
@@ -226,26 +336,45 @@ def main():
             fns[name] = ssd.bwd(x, dt, A, Bm, Cm, dout, workspace=ws_b, from_saved=True, grads=grads,
                                 only_kernel=k, prepare=True, **common)[0]
         for name, fn in fns.items():
-            ms, _ = timed(fn, args.steps, 2)
+            ms, ms_min, ms_max = trials(fn, max(1, args.steps // 2))
+            ms_cold = cold(fn)
             gbs = nbytes[name] / (ms * 1e-3) / 1e9
-            kernels[name] = {"ms": round(ms, 4), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
-                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-            print("bench: kernel %-22s %.4f ms  %.0f GB/s" % (name, ms, gbs), file=sys.stderr,
-                  flush=True)
+            e = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_max": round(ms_max, 4),
+                 "ms_cold": round(ms_cold, 4), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
+                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                 "frac_hbm_cold": round(nbytes[name] / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if name in nflops:
+                tf = nflops[name] / (ms * 1e-3) / 1e12
+                e["alg_tflops"] = round(tf, 1)
+                e["frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+            kernels[name] = e
+            print("bench: kernel %-22s %.4f ms (cold %.4f)  %.0f GB/s" % (name, ms, ms_cold, gbs),
+                  file=sys.stderr, flush=True)
         dom = max(kernels, key=lambda k: kernels[k]["ms"])
         s = kernels[dom]
         roof = {"kernel": dom, "bound": "hbm", "achieved": s["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": s["frac_hbm"], "traffic": load_traffic(dom),
                 "alg_bytes_per_launch": s["alg_bytes"], "avg_launch_ms": s["ms"]}
-        tot_b = sum(v["alg_bytes"] for v in kernels.values())
-        tot_ms = sum(v["ms"] for v in kernels.values())
-        kernels["_sum"] = {"ms": round(tot_ms, 4), "alg_bytes": tot_b,
-                           "GB/s": round(tot_b / (tot_ms * 1e-3) / 1e9, 1)}
+        def aggregate(names):
+            b = sum(kernels[n]["alg_bytes"] for n in names)
+            t = sum(kernels[n]["ms"] for n in names)
+            tc = sum(kernels[n]["ms_cold"] for n in names)
+            return {"ms": round(t, 4), "alg_bytes": b, "GB/s": round(b / (t * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "frac_hbm_cold": round(b / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        names = [n for n in kernels]
+        kernels["_forward_aggregate"] = aggregate(list(ssd.FWD_KERNELS))
+        kernels["_backward_aggregate"] = aggregate(list(ssd.BWD_KERNELS))
+        kernels["_all"] = aggregate(names)
 
-    cpu = None
+    cpu = cpu_par = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(have_bwd)
+        try:
+            cpu_par = cpu_baseline_parallel(have_bwd)
+        except Exception as e:  # a host that cannot start worker processes
+            cpu_par = {"error": repr(e)}
 
     out = {
         "metric": METRIC,
@@ -269,9 +398,14 @@ def main():
             "tokens/s": round(tokens / (ms_step * 1e-3), 1),
             "note": "forward keeps its intermediates for the backward (SSD_FLAG_SAVE_FOR_BWD)",
             "recompute_variant_ms": round(ms_step_rc, 4)},
+        "step_trials": {"median_ms": round(step_med, 4), "min_ms": round(step_min, 4),
+                        "max_ms": round(step_max, 4), "cold_ms": round(step_cold, 4),
+                        "note": "7 windows of steps/2 back-to-back steps; cold = single steps "
+                                "after a 512 MiB read that evicts the last-level cache"},
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": cpu_par,
     }
     print(json.dumps(out))
 
