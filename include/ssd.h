@@ -36,6 +36,12 @@
  *    input.  Outputs must not alias inputs or the workspace.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is queued on
  *    it and the call returns before it runs; keep buffers alive until then.
+ *    ssd_fwd and ssd_bwd run kernels that do not depend on each other on a second
+ *    stream of the library's own (one per device, created on first use, default
+ *    priority), forked from and joined back to `stream` with events: the call as a
+ *    whole stays ordered on `stream`, and it can be captured into a HIP graph.
+ *    Calls issued on different streams at the same time share that second stream
+ *    (they stay correct; their side kernels queue behind each other).
  *  - Every error the host can detect (NULL, shape, alignment, workspace size,
  *    unsupported configuration) is returned BEFORE anything is queued.  A failed
  *    launch returns SSD_ERR_HIP.  Nothing is printed; no exception crosses the ABI.

@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "internal.hpp"
@@ -148,6 +149,21 @@ ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool 
   return SSD_OK;
 }
 
+// A second stream per device, created on first use (default priority), for
+// kernels of one call that do not depend on the ones queued before them; the
+// caller's stream forks to it and joins it again through events, so the call
+// stays ordered on the caller's stream as a whole.
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
+    streams[dev] = nullptr;
+  return streams[dev];
+}
+
 #define SSD_TRY(expr)                          \
   do {                                         \
     if ((expr) != hipSuccess) return SSD_ERR_HIP; \
@@ -230,12 +246,32 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   void* Hp = ws + l.Hp;
   const int hb = p.io == SSD_BF16;
   void* CB = ws + l.CB;
+  void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
+  // C.B^T needs only B and C: it runs on a side stream beside the cumsum, the
+  // chunk states and the state passing; the chunk scan waits for it.
+  hipStream_t side = (!only && p.nck > 0) ? side_stream() : nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};  // fork, C.B^T done
+  for (int i = 0; side && i < 2; ++i)
+    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) side = nullptr;
+  if (!side)
+    for (int i = 0; i < 2; ++i)
+      if (ev[i]) hipEventDestroy(ev[i]);
+  if (side) {
+    SSD_TRY(hipEventRecord(ev[0], st));
+    SSD_TRY(hipStreamWaitEvent(side, ev[0], 0));
+    SSD_TRY(launch_bmm_chunk(p, B, C, CB, side, CBt));
+    SSD_TRY(hipEventRecord(ev[1], side));
+  }
   if (!only || only == 1) SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
   if (!only || only == 2) SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
   if (!only || only == 3)
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
-  void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
-  if (!only || only == 4) SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
+  if (side) {
+    SSD_TRY(hipStreamWaitEvent(st, ev[1], 0));
+    for (int i = 0; i < 2; ++i) hipEventDestroy(ev[i]);
+  } else if (!only || only == 4) {
+    SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
+  }
   if (!only || only == 5) SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
   return SSD_OK;
 }
@@ -279,11 +315,6 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, nullptr, 0, st));
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
   }
-  // adjoint of the state carried into each chunk, then the reverse scan
-  if (!only || only == 1)
-    SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
-  if (!only || only == 2)
-    SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
   BwdArgs a;
   a.x = x; a.B = B; a.C = C; a.dout = dout;
   a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.D = D;
@@ -296,7 +327,38 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   a.ddd = (float*)(ws + l.ddd); a.Ks = (float*)(ws + l.Ks); a.rR = (float*)(ws + l.rR);
   a.last_term = (float*)(ws + l.last); a.dDp = (float*)(ws + l.dDp);
   a.dAp = (float*)(ws + l.dAp); a.dbp = (float*)(ws + l.dbp);
-  if (!only || (only >= 3 && only <= 6)) SSD_TRY(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
+  // The head-summed dCB (with the R, K partials) and then dC need only forward
+  // quantities: on the bf16 path they run on a side stream beside the adjoint
+  // states, the reverse scan and dx; dB waits for dCB, the finalize for dC.
+  hipStream_t side = (!only && p.io == SSD_BF16 && p.nck > 0) ? side_stream() : nullptr;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};  // fork, dCB done, dC done
+  for (int i = 0; side && i < 3; ++i)
+    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) side = nullptr;
+  if (!side)
+    for (int i = 0; i < 3; ++i)
+      if (ev[i]) hipEventDestroy(ev[i]);
+  if (side) {
+    SSD_TRY(hipEventRecord(ev[0], st));
+    SSD_TRY(hipStreamWaitEvent(side, ev[0], 0));
+    SSD_TRY(launch_bwd_chunk(p, a, 2, side));
+    SSD_TRY(hipEventRecord(ev[1], side));
+    SSD_TRY(launch_bwd_chunk(p, a, 3, side));
+    SSD_TRY(hipEventRecord(ev[2], side));
+  }
+  // adjoint of the state carried into each chunk, then the reverse scan
+  if (!only || only == 1)
+    SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
+  if (!only || only == 2)
+    SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
+  if (side) {
+    SSD_TRY(launch_bwd_chunk(p, a, 1, st));
+    SSD_TRY(hipStreamWaitEvent(st, ev[1], 0));
+    SSD_TRY(launch_bwd_chunk(p, a, 4, st));
+    SSD_TRY(hipStreamWaitEvent(st, ev[2], 0));
+    for (int i = 0; i < 3; ++i) hipEventDestroy(ev[i]);
+  } else if (!only || (only >= 3 && only <= 6)) {
+    SSD_TRY(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
+  }
   if (!only || only == 7) SSD_TRY(launch_bwd_finalize(p, a, st));
   return SSD_OK;
 }

@@ -201,3 +201,46 @@ def test_single_kernel_relaunch_is_idempotent(io):
         torch.cuda.synchronize()
         for name, v in ref.items():
             assert torch.equal(g[name], v), (ssd.BWD_KERNELS[k - 1], name)
+
+
+def test_graph_capture_of_training_step():
+    # ssd_fwd + ssd_bwd (which fork to an internal side stream and join it with
+    # events) captured into a HIP graph: every replay, with eager work of the
+    # library in between, must reproduce the eager results bit for bit
+    inp = inputs.make_inputs(2, 700, 4, 64, 128, 2, io="bf16", init="randn", bwd=True,
+                             d_final=True, seed=62)
+    d = to_dev(inp)
+    prob = ssd.problem(d["x"], d["B"])
+    import ctypes
+    ws = torch.empty(ssd.lib().ssd_bwd_workspace_bytes(ctypes.byref(prob), 256, 0),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(d["x"])
+    fin = torch.empty(2, 4, 64, 128, dtype=torch.float32, device="cuda")
+    common = dict(D=d["D"], dt_bias=d["dt_bias"], init=d["init"], chunk_size=256)
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fs, _, _ = ssd.fwd(*args, workspace=ws, out=y, final=fin, save_for_backward=True,
+                           prepare=True, **common)
+        bs, g = ssd.bwd(*args, d["dout"], d_final=d["d_final"], workspace=ws, from_saved=True,
+                        prepare=True, **common)
+        fs()
+        bs()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in g.items() if v is not None}
+    yref, fref = y.clone(), fin.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        fs()
+        bs()
+    for i in range(3):
+        for v in list(g.values()) + [y, fin]:
+            if v is not None:
+                v.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, yref) and torch.equal(fin, fref), i
+        for k in ref:
+            assert torch.equal(g[k], ref[k]), (i, k)
+        ssd.fwd(*args, **common)  # eager work of the library between replays
+        torch.cuda.synchronize()
