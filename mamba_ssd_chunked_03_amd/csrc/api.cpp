@@ -149,19 +149,35 @@ ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool 
   return SSD_OK;
 }
 
-// A second stream per device, created on first use (default priority), for
-// kernels of one call that do not depend on the ones queued before them; the
-// caller's stream forks to it and joins it again through events, so the call
-// stays ordered on the caller's stream as a whole.
-hipStream_t side_stream() {
+// A second stream per device, with three events, created on first use (default
+// priority) and kept for the life of the process: kernels of one call that do
+// not depend on the ones queued before them run there; the caller's stream forks
+// to it and joins it again through the events, so each call stays ordered on the
+// caller's stream as a whole.  The lock is held while a call queues its work, so
+// calls from several host threads do not interleave their event records.
+struct SideLane {
+  bool tried = false, ok = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+};
+SideLane* side_lane(std::unique_lock<std::mutex>& lock) {
   static std::mutex mu;
-  static hipStream_t streams[64] = {};
+  static SideLane lanes[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
-    streams[dev] = nullptr;
-  return streams[dev];
+  lock = std::unique_lock<std::mutex>(mu);
+  SideLane& l = lanes[dev];
+  if (!l.tried) {
+    l.tried = true;
+    l.ok = hipStreamCreateWithFlags(&l.stream, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; l.ok && i < 3; ++i)
+      l.ok = hipEventCreateWithFlags(&l.ev[i], hipEventDisableTiming) == hipSuccess;
+  }
+  if (!l.ok) {
+    lock.unlock();
+    return nullptr;
+  }
+  return &l;
 }
 
 #define SSD_TRY(expr)                          \
@@ -247,28 +263,22 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   const int hb = p.io == SSD_BF16;
   void* CB = ws + l.CB;
   void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
-  // C.B^T needs only B and C: it runs on a side stream beside the cumsum, the
+  // C.B^T needs only B and C: it runs on the side stream beside the cumsum, the
   // chunk states and the state passing; the chunk scan waits for it.
-  hipStream_t side = (!only && p.nck > 0) ? side_stream() : nullptr;
-  hipEvent_t ev[2] = {nullptr, nullptr};  // fork, C.B^T done
-  for (int i = 0; side && i < 2; ++i)
-    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) side = nullptr;
-  if (!side)
-    for (int i = 0; i < 2; ++i)
-      if (ev[i]) hipEventDestroy(ev[i]);
-  if (side) {
-    SSD_TRY(hipEventRecord(ev[0], st));
-    SSD_TRY(hipStreamWaitEvent(side, ev[0], 0));
-    SSD_TRY(launch_bmm_chunk(p, B, C, CB, side, CBt));
-    SSD_TRY(hipEventRecord(ev[1], side));
+  std::unique_lock<std::mutex> lane_lock;
+  SideLane* side = (!only && p.nck > 0) ? side_lane(lane_lock) : nullptr;
+  if (side) {  // events: 0 fork, 1 C.B^T done
+    SSD_TRY(hipEventRecord(side->ev[0], st));
+    SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
+    SSD_TRY(launch_bmm_chunk(p, B, C, CB, side->stream, CBt));
+    SSD_TRY(hipEventRecord(side->ev[1], side->stream));
   }
   if (!only || only == 1) SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
   if (!only || only == 2) SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
   if (!only || only == 3)
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
   if (side) {
-    SSD_TRY(hipStreamWaitEvent(st, ev[1], 0));
-    for (int i = 0; i < 2; ++i) hipEventDestroy(ev[i]);
+    SSD_TRY(hipStreamWaitEvent(st, side->ev[1], 0));
   } else if (!only || only == 4) {
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
   }
@@ -330,20 +340,15 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   // The head-summed dCB (with the R, K partials) and then dC need only forward
   // quantities: on the bf16 path they run on a side stream beside the adjoint
   // states, the reverse scan and dx; dB waits for dCB, the finalize for dC.
-  hipStream_t side = (!only && p.io == SSD_BF16 && p.nck > 0) ? side_stream() : nullptr;
-  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};  // fork, dCB done, dC done
-  for (int i = 0; side && i < 3; ++i)
-    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) side = nullptr;
-  if (!side)
-    for (int i = 0; i < 3; ++i)
-      if (ev[i]) hipEventDestroy(ev[i]);
-  if (side) {
-    SSD_TRY(hipEventRecord(ev[0], st));
-    SSD_TRY(hipStreamWaitEvent(side, ev[0], 0));
-    SSD_TRY(launch_bwd_chunk(p, a, 2, side));
-    SSD_TRY(hipEventRecord(ev[1], side));
-    SSD_TRY(launch_bwd_chunk(p, a, 3, side));
-    SSD_TRY(hipEventRecord(ev[2], side));
+  std::unique_lock<std::mutex> lane_lock;
+  SideLane* side = (!only && p.io == SSD_BF16 && p.nck > 0) ? side_lane(lane_lock) : nullptr;
+  if (side) {  // events: 0 fork, 1 dCB done, 2 dC done
+    SSD_TRY(hipEventRecord(side->ev[0], st));
+    SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
+    SSD_TRY(launch_bwd_chunk(p, a, 2, side->stream));
+    SSD_TRY(hipEventRecord(side->ev[1], side->stream));
+    SSD_TRY(launch_bwd_chunk(p, a, 3, side->stream));
+    SSD_TRY(hipEventRecord(side->ev[2], side->stream));
   }
   // adjoint of the state carried into each chunk, then the reverse scan
   if (!only || only == 1)
@@ -352,10 +357,9 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
     SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
   if (side) {
     SSD_TRY(launch_bwd_chunk(p, a, 1, st));
-    SSD_TRY(hipStreamWaitEvent(st, ev[1], 0));
+    SSD_TRY(hipStreamWaitEvent(st, side->ev[1], 0));
     SSD_TRY(launch_bwd_chunk(p, a, 4, st));
-    SSD_TRY(hipStreamWaitEvent(st, ev[2], 0));
-    for (int i = 0; i < 3; ++i) hipEventDestroy(ev[i]);
+    SSD_TRY(hipStreamWaitEvent(st, side->ev[2], 0));
   } else if (!only || (only >= 3 && only <= 6)) {
     SSD_TRY(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
   }
