@@ -95,17 +95,34 @@ def _one(pattern):
 
 
 def kernel_times(trace_csv):
-    """{key: {"kernels": {name: [durations ns]}}} from a kernel-trace CSV."""
-    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    """{key: {name: [(duration ns, overlapped)]}} from a kernel-trace CSV.
+
+    A launch is "overlapped" when its [start, end) interval meets that of any
+    other kernel in the trace (the path runs some kernels on a second stream),
+    so that its duration is not the kernel's alone."""
+    spans = []
     for row in _rows(trace_csv):
         name = _col(row, "Kernel_Name", "Name")
+        spans.append((int(_col(row, "Start_Timestamp")), int(_col(row, "End_Timestamp")), name))
+    spans.sort()
+    over = [False] * len(spans)
+    for i, (s0, e0, _) in enumerate(spans):
+        j = i + 1
+        while j < len(spans) and spans[j][0] < e0:
+            over[i] = over[j] = True
+            j += 1
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (s0, e0, name), ov in zip(spans, over):
         key = kernel_key(name)
         if key is None:
             continue
-        t = int(_col(row, "End_Timestamp")) - int(_col(row, "Start_Timestamp"))
         short = re.search(r"ssd::(\w+(?:<[^>]*>)?)", name).group(1)
-        out[key][short].append(t)
+        out[key][short].append((e0 - s0, ov))
     return out
+
+
+def _mean(v):
+    return sum(v) / len(v) if v else float("nan")
 
 
 def stats_table(trace_csv, command, summary_cmd=""):
@@ -113,23 +130,34 @@ def stats_table(trace_csv, command, summary_cmd=""):
     lines = ["Profiled with (from the repository root, one MI355X):", "", "    " + command, ""]
     if summary_cmd:
         lines += ["Summarised with:", "", "    " + summary_cmd, ""]
-    lines += ["Per kernel of the path (bench.py's names): launches and average duration from the "
-              "kernel trace; a bwd_finalize launch is its two kernels.", "",
-             "| Kernel | Launched kernels | Launches | Average (us) | Min (us) | Max (us) |",
-             "|---|---|---|---|---|---|"]
+    lines += ["Per kernel of the path (bench.py's names): launches and durations from the kernel "
+              "trace; a bwd_finalize launch is its two kernels.  Inside ssd_fwd / ssd_bwd some "
+              "kernels run side by side on two streams, and the program also times each kernel "
+              "on its own; a launch counts as overlapped when its interval meets another "
+              "kernel's, and the two kinds are averaged apart.", "",
+              "| Kernel | Launched kernels | Launches | Alone | Alone avg (us) | Overlapped "
+              "| Overlapped avg (us) | Min (us) | Max (us) |",
+              "|---|---|---|---|---|---|---|---|---|"]
     total = {}
     for key in KERNEL_FILES:
         if key not in times:
             continue
         ks = times[key]
         n = min(len(v) for v in ks.values())
-        avg = sum(sum(v) / len(v) for v in ks.values()) / 1e3
-        mn = sum(min(v) for v in ks.values()) / 1e3
-        mx = sum(max(v) for v in ks.values()) / 1e3
-        total[key] = avg
-        lines.append("| %s | %s | %d | %.1f | %.1f | %.1f |" % (
-            key, ", ".join("`%s`" % s for s in sorted(ks)), n, avg, mn, mx))
-    lines += ["", "Sum of the averages (one of each kernel): %.1f us" % sum(total.values())]
+        # a multi-kernel launch (bwd_finalize) counts as alone only when all its kernels are
+        alone = sum(_mean([t for t, ov in v if not ov]) for v in ks.values()) / 1e3
+        lapped = sum(_mean([t for t, ov in v if ov]) for v in ks.values()) / 1e3
+        n_alone = min(sum(1 for _, ov in v if not ov) for v in ks.values())
+        n_over = max(sum(1 for _, ov in v if ov) for v in ks.values())
+        mn = sum(min(t for t, _ in v) for v in ks.values()) / 1e3
+        mx = sum(max(t for t, _ in v) for v in ks.values()) / 1e3
+        total[key] = alone
+        fmt = lambda x: "-" if x != x else "%.1f" % x
+        lines.append("| %s | %s | %d | %d | %s | %d | %s | %.1f | %.1f |" % (
+            key, ", ".join("`%s`" % s for s in sorted(ks)), n, n_alone, fmt(alone), n_over,
+            fmt(lapped), mn, mx))
+    lines += ["", "Sum of the averages alone (one of each kernel): %.1f us"
+              % sum(v for v in total.values() if v == v)]
     return "\n".join(lines) + "\n", total
 
 

@@ -31,16 +31,20 @@ def test_kernel_keys():
 
 
 def test_stats_table(tmp_path):
-    rows = [["void ssd::bwd_dx_bf16_kernel<64, 128>(a)", 100, 1100],
-            ["void ssd::bwd_dx_bf16_kernel<64, 128>(a)", 2000, 5000],
-            ["void ssd::bwd_finalize_kernel(a)", 0, 500],
-            ["void ssd::bwd_reduce_kernel(a)", 600, 700],
-            ["void at::native::other(a)", 0, 99999]]
+    rows = [["void ssd::bwd_dx_bf16_kernel<64, 128>(a)", 100, 1100],      # alone
+            ["void ssd::bwd_dx_bf16_kernel<64, 128>(a)", 2000, 5000],     # meets the bwd_dc below
+            ["void ssd::bwd_dc_bf16_kernel<64, 128>(a)", 4000, 4500],
+            ["void ssd::bwd_finalize_kernel(a)", 6000, 6500],
+            ["void ssd::bwd_reduce_kernel(a)", 6600, 6700],
+            ["void at::native::other(a)", 9000, 9999]]
     p = write(tmp_path / "t.csv", TRACE_COLS, rows)
     text, total = profiling.stats_table(p, "cmd")
-    assert abs(total["bwd_dx"] - 2.0) < 1e-9            # (1000 + 3000) / 2 ns
+    assert abs(total["bwd_dx"] - 1.0) < 1e-9            # the launch alone: 1000 ns
     assert abs(total["bwd_finalize"] - 0.6) < 1e-9      # 500 + 100 ns per launch
-    assert "| bwd_dx |" in text and "other" not in text
+    assert total["bwd_dc"] != total["bwd_dc"]           # never alone: no figure (nan)
+    line = [l for l in text.splitlines() if l.startswith("| bwd_dx |")][0]
+    assert "| 2 | 1 | 1.0 | 1 | 3.0 | 1.0 | 3.0 |" in line
+    assert "at::native" not in text
 
 
 def test_traffic_calibration(tmp_path):
