@@ -93,17 +93,62 @@ __device__ __forceinline__ bf16x8 frag_kmajor(const uint16_t* tile, int ld, int 
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// ---------------------------------------------- column order of MFMA rows ----
+// A row of W outputs (W a multiple of 32) computed as W/16 transposed 16x16
+// tiles, the column index coming from a K-major LDS operand read with
+// frag_kmajor, leaves lane group q (lanes 16q..16q+15) of tile t holding the
+// LDS columns 16t + 4q + 0..3.  The operand is staged with its 4-column groups
+// permuted inside every 32-column block (logical group 2g + u stored as group
+// 4u + g), so those LDS columns hold the logical columns
+// 32(t/2) + 8q + 4(t%2) + 0..3 (pcol below): a lane then owns 8 consecutive
+// logical columns in the tile pair 2s, 2s + 1, and its part of a row is read
+// and written 16 bytes at a time (64 contiguous bytes per row per instruction,
+// where the natural order gives 32).  The transpose reads are untouched, so
+// their LDS bank pattern stays that of the natural layout.
+__device__ __forceinline__ int pcol(int t, int c) {  // logical column of tile t's column c
+  return 32 * (t >> 1) + 8 * (c >> 2) + 4 * (t & 1) + (c & 3);
+}
+// LDS columns of the low and high 8 bytes of logical 16-byte piece c8 (columns 8 c8 .. +7)
+__device__ __forceinline__ int perm_lo(int c8) { return 32 * (c8 >> 2) + 4 * (c8 & 3); }
+__device__ __forceinline__ int perm_hi(int c8) { return 32 * (c8 >> 2) + 16 + 4 * (c8 & 3); }
+// one 16-byte piece of an LDS row, in the natural or the permuted column order
+template <bool PERM>
+__device__ __forceinline__ void lds_piece(uint16_t* row, int c8, u32x4 v) {
+  if constexpr (PERM) {
+    *(uint2*)(row + perm_lo(c8)) = make_uint2(v[0], v[1]);
+    *(uint2*)(row + perm_hi(c8)) = make_uint2(v[2], v[3]);
+  } else {
+    *(u32x4*)(row + c8 * 8) = v;
+  }
+}
+// a lane's 8 logical columns 32s + 8q .. +7 of a permuted LDS row
+__device__ __forceinline__ u32x4 lds_cols8_perm(const uint16_t* row, int s, int q) {
+  const uint2 lo = *(const uint2*)(row + 32 * s + 4 * q);
+  const uint2 hi = *(const uint2*)(row + 32 * s + 16 + 4 * q);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+// sum of a lane's 8 bf16 values (columns 32s + 8q .. +7) times its outputs of tiles 2s, 2s + 1
+__device__ __forceinline__ float dot_bf8(u32x4 v, f32x4 a, f32x4 b) {
+  return bf_lo(v[0]) * a[0] + bf_hi(v[0]) * a[1] + bf_lo(v[1]) * a[2] + bf_hi(v[1]) * a[3] +
+         bf_lo(v[2]) * b[0] + bf_hi(v[2]) * b[1] + bf_lo(v[3]) * b[2] + bf_hi(v[3]) * b[3];
+}
+// two adjacent tiles' 4 outputs of one lane (columns 32s + 8q .. +7) as 8 bf16
+__device__ __forceinline__ u32x4 pack_bf8(f32x4 a, f32x4 b) {
+  return u32x4{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3])};
+}
+
 // --------------------------------------------------------- LDS staging ----
 // Copy ROWS token rows of W bf16 (16-byte pieces) from global rows `src`
-// (stride `srow` elements) into LDS rows `dst` (stride `ld`); rows >= nvalid are
-// zero.  Every load is issued before the first LDS store, so the whole tile
-// costs one memory latency (a loop with a run-time trip count would wait on
-// each load in turn).
-template <int ROWS, int W, int NT = 256>
+// (stride `srow` elements) into LDS rows `dst` (stride `ld`), in the natural or
+// the permuted column order; rows >= nvalid are zero.  Every load is issued
+// before the first LDS store, so the whole tile costs one memory latency (a
+// loop with a run-time trip count would wait on each load in turn).
+template <int ROWS, int W, int NT = 256, bool PERM = false>
 __device__ __forceinline__ void stage_rows(uint16_t* dst, int ld, const uint16_t* src, int64_t srow,
                                            int nvalid, int tid) {
   constexpr int PER = W / 8;
   constexpr int NC = (ROWS * PER + NT - 1) / NT;
+  static_assert(!PERM || W % 32 == 0, "permuted rows are whole 32-column blocks");
   u32x4 t[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -114,7 +159,7 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, int ld, const uint16_t
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int e = tid + c * NT, j = e / PER, c8 = e % PER;
-    if (e < ROWS * PER) *(u32x4*)(dst + j * ld + c8 * 8) = t[c];
+    if (e < ROWS * PER) lds_piece<PERM>(dst + j * ld, c8, t[c]);
   }
 }
 
@@ -140,34 +185,35 @@ __device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const fl
 }
 
 // stage_rows split in two, so that several tiles' loads (and other loads) can
-// all be in flight before the first LDS store waits for its data.
-template <int ROWS, int W, int NT = 256>
+// all be in flight before the first LDS store waits for its data.  STREAM
+// marks the loads nontemporal: for a tile that this kernel reads exactly once,
+// it keeps the tile from displacing the operands that other workgroups re-read
+// from the cache.
+template <int ROWS, int W, int NT = 256, bool PERM = false, bool STREAM = false>
 struct RowTile {
   static constexpr int PER = W / 8;
   static constexpr int NC = (ROWS * PER + NT - 1) / NT;
+  static_assert(!PERM || W % 32 == 0, "permuted rows are whole 32-column blocks");
   u32x4 t[NC];
   __device__ __forceinline__ void load(const uint16_t* src, int64_t srow, int nvalid, int tid) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = tid + c * NT, j = e / PER, c8 = e % PER;
-      t[c] = (e < ROWS * PER && j < nvalid) ? *(const u32x4*)(src + (int64_t)j * srow + c8 * 8)
-                                            : u32x4{0u, 0u, 0u, 0u};
+      const u32x4* p = (const u32x4*)(src + (int64_t)j * srow + c8 * 8);
+      if constexpr (STREAM)
+        t[c] = (e < ROWS * PER && j < nvalid) ? __builtin_nontemporal_load(p) : u32x4{0u, 0u, 0u, 0u};
+      else
+        t[c] = (e < ROWS * PER && j < nvalid) ? *p : u32x4{0u, 0u, 0u, 0u};
     }
   }
   __device__ __forceinline__ void store(uint16_t* dst, int ld, int tid) const {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = tid + c * NT, j = e / PER, c8 = e % PER;
-      if (e < ROWS * PER) *(u32x4*)(dst + j * ld + c8 * 8) = t[c];
+      if (e < ROWS * PER) lds_piece<PERM>(dst + j * ld, c8, t[c]);
     }
   }
 };
-
-// bf16 P x N state (row-major) -> bf16 LDS [p][n] with row stride ld.
-template <int P, int N, int NT = 256>
-__device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const uint16_t* src, int tid) {
-  stage_rows<P, N, NT>(dst, ld, src, N, P, tid);
-}
 
 // Four consecutive state elements to global memory as fp32 or bf16.
 __device__ __forceinline__ void store4(float* dst, float4 v) { *(float4*)dst = v; }

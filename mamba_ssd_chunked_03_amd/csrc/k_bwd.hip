@@ -83,14 +83,14 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   const int NB = Q / 16, nii = (NB + kDxWaves - 1) / kDxWaves;
   auto rb_of = [&](int ii) { return kDxWaves * ii + ((ii & 1) ? (kDxWaves - 1 - w) : w); };
   auto live = [&](int ii) { return ii < nii && rb_of(ii) < NB && rb_of(ii) * 16 < len; };
-  uint2 px[P / 16];
+  u32x4 px[P / 32];  // x_j, the lane's 8 adjacent columns per tile pair (pcol)
   u32x4 bq[N / 32], pc1, pcd;
   auto load_rb = [&](int rb) {
     const int jr = rb * 16 + r, c0 = rb / 2;
     const bool ok = jr < len, off = ok && c0 + 1 < (len + 31) / 32;
 #pragma unroll
-    for (int tp = 0; tp < P / 16; ++tp)
-      px[tp] = ok ? *(const uint2*)(xb + (int64_t)jr * xrow + tp * 16 + q * 4) : make_uint2(0u, 0u);
+    for (int s = 0; s < P / 32; ++s)
+      px[s] = ok ? *(const u32x4*)(xb + (int64_t)jr * xrow + 32 * s + 8 * q) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk)
       bq[kk] = ok ? *(const u32x4*)(bb + (int64_t)jr * brow + kk * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
@@ -99,11 +99,13 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   };
   if (live(0)) load_rb(rb_of(0));
   // every prologue load in flight before the first LDS store waits on one:
-  // acs/delta, the dy tile (token-major, rows past the chunk's end zero), and
+  // acs/delta, the dy tile (token-major, rows past the chunk's end zero, column
+  // groups permuted so that a lane's outputs are adjacent columns; read once,
+  // so loaded nontemporally), and
   // dT = dE_c (bf16, into LDS [p][n]) with H_c for alpha <dE, H> in fp32
   static_assert(QMAX <= kDxWaves * 64, "one acs/delta value per thread");
   const float av = tid < Q ? acs[kh * Q + tid] : 0.f, dv = tid < Q ? delta[kh * Q + tid] : 0.f;
-  RowTile<QMAX, P, kDxWaves * 64> ytile;
+  RowTile<QMAX, P, kDxWaves * 64, true, true> ytile;
   ytile.load(dyb, xrow, len, tid);
   float dot = 0.f;
   {
@@ -150,9 +152,10 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     const int rb = rb_of(ii);
     const int j0 = rb * 16;
     // Products are issued with the operands swapped, so each lane holds the
-    // transposed tile acc[tp][rr] = (dx bracket)[j0 + r][16 tp + 4 q + rr]: the
-    // lane owns row jrow, row factors are one value per lane, row dots reduce
-    // over the four lanes r, r+16, r+32, r+48, and stores are 8 bytes.
+    // transposed tile acc[tp][rr] = (dx bracket)[j0 + r][pcol(tp, 4 q + rr)]:
+    // the lane owns row jrow, row factors are one value per lane, row dots
+    // reduce over the four lanes r, r+16, r+32, r+48, and acc[2s], acc[2s + 1]
+    // are 8 adjacent columns (16-byte loads of x and stores of dx).
     f32x4 acc[P / 16];
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -164,23 +167,21 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     const bool has_off = cb0 + 1 < s_end;
     const float ae = has_off ? sa[e] : 0.f;
     const float aj = sa[jrow];                     // jrow < Q always
-    uint2 xq[P / 16];                              // this lane's x values, 4 adjacent per tp
+    u32x4 xq[P / 32];                              // this lane's x values
 #pragma unroll
-    for (int tp = 0; tp < P / 16; ++tp) xq[tp] = px[tp];
+    for (int s = 0; s < P / 32; ++s) xq[s] = px[s];
     // state part: sum_n B_j[n] dT[p][n]
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk) {
       const bf16x8 b = as_bf16x8(bq[kk]);
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(dts + (tp * 16 + r) * LDT + kk * 32 + q * 8)), b, acc[tp]);
+        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(dts + pcol(tp, r) * LDT + kk * 32 + q * 8)), b, acc[tp]);
     }
     const float wj = rowok ? exp2_fast(a_last - aj) : 0.f;
     float xs = 0.f;
 #pragma unroll
-    for (int tp = 0; tp < P / 16; ++tp)
-      xs += bf_lo(xq[tp].x) * acc[tp][0] + bf_hi(xq[tp].x) * acc[tp][1] +
-            bf_lo(xq[tp].y) * acc[tp][2] + bf_hi(xq[tp].y) * acc[tp][3];
+    for (int s = 0; s < P / 32; ++s) xs += dot_bf8(xq[s], acc[2 * s], acc[2 * s + 1]);
     xs *= wj;                                      // this lane's part of x_j . (w_j dT B_j)
     if (has_off) {
       // later blocks through the anchor: acc = 2^(acs_last - acs_e) state
@@ -238,16 +239,21 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     float xt = 0.f, dxx = 0.f;
     uint16_t* dxrow = DX + (int64_t)(ci.start + jrow) * xrow + (int64_t)h * P;
 #pragma unroll
-    for (int tp = 0; tp < P / 16; ++tp) {
-      const int p = tp * 16 + q * 4;
-      const uint2 dq = *(const uint2*)(dyt + jrow * LDY + p);  // rows past the end are zero
-      const float x0 = bf_lo(xq[tp].x), x1 = bf_hi(xq[tp].x), x2 = bf_lo(xq[tp].y), x3 = bf_hi(xq[tp].y);
-      const float y0 = bf_lo(dq.x), y1 = bf_hi(dq.x), y2 = bf_lo(dq.y), y3 = bf_hi(dq.y);
-      xt += x0 * acc[tp][0] + x1 * acc[tp][1] + x2 * acc[tp][2] + x3 * acc[tp][3];
-      dxx += x0 * y0 + x1 * y1 + x2 * y2 + x3 * y3;
-      if (rowok)
-        *(uint2*)(dxrow + p) = make_uint2(pack_bf2(dj * acc[tp][0] + Dh * y0, dj * acc[tp][1] + Dh * y1),
-                                          pack_bf2(dj * acc[tp][2] + Dh * y2, dj * acc[tp][3] + Dh * y3));
+    for (int s = 0; s < P / 32; ++s) {
+      const u32x4 dq = lds_cols8_perm(dyt + jrow * LDY, s, q);  // rows past the end are zero
+      xt += dot_bf8(xq[s], acc[2 * s], acc[2 * s + 1]);
+      u32x4 o;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {  // tile 2s + u: the lane's columns 32s + 8q + 4u .. +3
+        const f32x4 a = acc[2 * s + u];
+        const float y0 = bf_lo(dq[2 * u]), y1 = bf_hi(dq[2 * u]);
+        const float y2 = bf_lo(dq[2 * u + 1]), y3 = bf_hi(dq[2 * u + 1]);
+        dxx += bf_lo(xq[s][2 * u]) * y0 + bf_hi(xq[s][2 * u]) * y1 + bf_lo(xq[s][2 * u + 1]) * y2 +
+               bf_hi(xq[s][2 * u + 1]) * y3;
+        o[2 * u] = pack_bf2(dj * a[0] + Dh * y0, dj * a[1] + Dh * y1);
+        o[2 * u + 1] = pack_bf2(dj * a[2] + Dh * y2, dj * a[3] + Dh * y3);
+      }
+      if (rowok) *(u32x4*)(dxrow + 32 * s + 8 * q) = o;
     }
     xs += __shfl_xor(xs, 16);
     xs += __shfl_xor(xs, 32);
@@ -482,7 +488,9 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
 // staged in a double-buffered LDS tile (one barrier per head) and the next
 // head's H, dy fragments and acs are loaded into registers while this head is
 // worked on.  Products are issued with the operands swapped, so each lane owns
-// one row i: its r_i reduces over four lanes and dC is stored 8 bytes at a time.
+// one row i: its r_i reduces over four lanes.  B and H are staged with their
+// column groups permuted (common.hpp, pcol), so a lane's outputs are 8 adjacent
+// columns per tile pair and C is loaded and dC stored 16 bytes at a time.
 template <int P, int N>
 __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
@@ -510,14 +518,14 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   const bool active = i0 < len;
   const int irow = i0 + r;
   const bool rowok = irow < len;
-  // acc[nb][rr] = dC[irow][16 nb + 4 q + rr]
+  // acc[nb][rr] = dC[irow][pcol(nb, 4 q + rr)]
   f32x4 acc[N / 16];
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* bt = ub[0];
   for (int jt = 0; jt <= tile; ++jt) {
     __syncthreads();
-    stage_rows<64, N>(bt, LDB, bb + (int64_t)jt * 64 * brow, brow, len - jt * 64, tid);
+    stage_rows<64, N, 256, true>(bt, LDB, bb + (int64_t)jt * 64 * brow, brow, len - jt * 64, tid);
     __syncthreads();
     if (!active) continue;
     for (int jb = jt * 64; jb < min(jt * 64 + 64, i0 + 16); jb += 32) {
@@ -528,11 +536,11 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
         acc[nb] = mfma_bf16(frag_kmajor(bt + (jb - jt * 64) * LDB + nb * 16, LDB, lane), a, acc[nb]);
     }
   }
-  // C_i values of this lane's outputs, 4 adjacent per nb
-  uint2 cq[N / 16];
+  // C_i values of this lane's outputs, 8 adjacent per tile pair
+  u32x4 cq[N / 32];
 #pragma unroll
-  for (int nb = 0; nb < N / 16; ++nb)
-    cq[nb] = rowok ? *(const uint2*)(cb + (int64_t)irow * brow + nb * 16 + q * 4) : make_uint2(0u, 0u);
+  for (int s = 0; s < N / 32; ++s)
+    cq[s] = rowok ? *(const u32x4*)(cb + (int64_t)irow * brow + 32 * s + 8 * q) : u32x4{0u, 0u, 0u, 0u};
   // the next head's H pieces, dy fragments and acs_i
   u32x4 ph[NPH], py[P / 32];
   float pa = 0.f;
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
       const int e = (tid + c * 256) * 8;
-      if (e < P * N) *(u32x4*)(ht + (e / N) * LDB + (e % N)) = ph[c];
+      if (e < P * N) lds_piece<true>(ht + (e / N) * LDB, (e % N) / 8, ph[c]);
     }
     __syncthreads();
     // this head's dy fragment scaled by 2^acs_i (one row per lane)
@@ -581,8 +589,8 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < P / 32; ++kb)
         t = mfma_bf16(frag_kmajor(ht + kb * 32 * LDB + nb * 16, LDB, lane), ays[kb], t);
-      rsum += bf_lo(cq[nb].x) * t[0] + bf_hi(cq[nb].x) * t[1] + bf_lo(cq[nb].y) * t[2] +
-              bf_hi(cq[nb].y) * t[3];
+      const uint32_t c0 = cq[nb >> 1][2 * (nb & 1)], c1 = cq[nb >> 1][2 * (nb & 1) + 1];
+      rsum += bf_lo(c0) * t[0] + bf_hi(c0) * t[1] + bf_lo(c1) * t[2] + bf_hi(c1) * t[3];
       acc[nb] += t;
     }
     rsum += __shfl_xor(rsum, 16);
@@ -592,9 +600,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   if (!rowok) return;
   uint16_t* dcrow = dC + (int64_t)(ci.start + irow) * brow + (int64_t)g * N;
 #pragma unroll
-  for (int nb = 0; nb < N / 16; ++nb)
-    *(uint2*)(dcrow + nb * 16 + q * 4) =
-        make_uint2(pack_bf2(acc[nb][0], acc[nb][1]), pack_bf2(acc[nb][2], acc[nb][3]));
+  for (int s = 0; s < N / 32; ++s) *(u32x4*)(dcrow + 32 * s + 8 * q) = pack_bf8(acc[2 * s], acc[2 * s + 1]);
 }
 
 // ------------------------------------------------------------ bwd_db bf16 ----
@@ -603,7 +609,8 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
 // + sum_h w_j delta_j dT^T x_j (one K=headdim GEMM per head).  Per head, dT = dE_c
 // (bf16) is staged in a double-buffered LDS tile and the next head's dT, x
 // fragments and decay scalars are loaded into registers while this head is
-// worked on.  Operands swapped as in bwd_dc: each lane owns one row j.
+// worked on.  Operands swapped and C, dT staged in the permuted column order as
+// in bwd_dc: each lane owns one row j and stores dB 16 bytes at a time.
 template <int P, int N>
 __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
@@ -629,13 +636,13 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   const bool active = j0 < len;
   const int jrow = j0 + r;
   const bool rowok = jrow < len;
-  f32x4 acc[N / 16];  // acc[nb][rr] = dB[jrow][16 nb + 4 q + rr]
+  f32x4 acc[N / 16];  // acc[nb][rr] = dB[jrow][pcol(nb, 4 q + rr)]
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* ct = ub[0];
   for (int it = tile; it * 64 < len; ++it) {
     __syncthreads();
-    stage_rows<64, N>(ct, LDB, cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
+    stage_rows<64, N, 256, true>(ct, LDB, cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
     __syncthreads();
     if (!active) continue;
     const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
@@ -673,7 +680,7 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
       const int e = (tid + c * 256) * 8;
-      if (e < P * N) *(u32x4*)(dtt + (e / N) * LDB + (e % N)) = ph[c];
+      if (e < P * N) lds_piece<true>(dtt + (e / N) * LDB, (e % N) / 8, ph[c]);
     }
     __syncthreads();
     // this head's x fragment scaled by w_j delta_j (one row per lane)
@@ -697,9 +704,7 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   if (!rowok) return;
   uint16_t* dbrow = dB + (int64_t)(ci.start + jrow) * brow + (int64_t)g * N;
 #pragma unroll
-  for (int nb = 0; nb < N / 16; ++nb)
-    *(uint2*)(dbrow + nb * 16 + q * 4) =
-        make_uint2(pack_bf2(acc[nb][0], acc[nb][1]), pack_bf2(acc[nb][2], acc[nb][3]));
+  for (int s = 0; s < N / 32; ++s) *(u32x4*)(dbrow + 32 * s + 8 * q) = pack_bf8(acc[2 * s], acc[2 * s + 1]);
 }
 
 // ------------------------------------------------------------ fp32 paths ----

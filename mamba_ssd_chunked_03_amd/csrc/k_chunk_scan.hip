@@ -14,7 +14,9 @@
 // 15-w for eight waves) so the causal work is balanced.  Per row
 // block, all its C and CB fragments are loaded first (one memory latency).
 // Products are issued with A and B swapped, so every lane ends up owning one
-// output row (one row factor per lane, 8-byte stores).
+// output row (one row factor per lane).  The x tile is staged with its column
+// groups permuted (common.hpp, pcol), so each lane's outputs are 8 adjacent
+// columns per tile pair: the skip term's x and the output go 16 bytes a lane.
 // The decay 2^(acs_i - acs_j) is factored through an anchor token e with
 // j <= e < i, 2^(acs_i - acs_e) * 2^(acs_e - acs_j), both factors <= 1 (acs never
 // increases), so nothing can overflow.  For a row block starting in the 32-token
@@ -29,6 +31,7 @@
 //   4. acc += M . X over the diagonal block, M_ij = CB_ij 2^(acs_i - acs_j) delta_j
 //      masked to j <= i;
 //   5. + D x_i and the bf16 store.
+// The x and H tiles are read once per workgroup and loaded nontemporally.
 //
 // fp32 path: one thread per (token, p), plain loops.
 #include "internal.hpp"
@@ -90,10 +93,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     // every prologue load in flight before the first LDS store waits on one
     static_assert(QMAX <= kScanWaves * 64, "one acs/delta value per thread");
     const float av = tid < Q ? acs[kh * Q + tid] : 0.f, dv = tid < Q ? delta[kh * Q + tid] : 0.f;
-    RowTile<QMAX, P, kScanWaves * 64> xt;
+    RowTile<QMAX, P, kScanWaves * 64, true, true> xt;
     xt.load(xb, xrow, len, tid);
     if constexpr (sizeof(HT) == 2) {
-      RowTile<P, N, kScanWaves * 64> ht;
+      RowTile<P, N, kScanWaves * 64, false, true> ht;
       ht.load((const uint16_t*)(Hs + kh * (int64_t)(P * N)), N, P, tid);
       xt.store(xs, LDX, tid);
       ht.store(hs, HLD, tid);
@@ -124,8 +127,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     const int nb = i0 / 32;   // 32-token blocks strictly before the diagonal block
     const float ae = nb > 0 ? sa[32 * nb - 1] : 0.f;
     // The products are issued with the operands swapped, so each lane holds the
-    // transposed tile: acc[tp][rr] = y[i0 + r][16 tp + 4 q + rr].  A row factor
-    // is then one value per lane, and each lane's 4 outputs per tp are adjacent.
+    // transposed tile: acc[tp][rr] = y[i0 + r][pcol(tp, 4 q + rr)].  A row
+    // factor is then one value per lane, and acc[2s], acc[2s + 1] are the
+    // lane's 8 adjacent outputs 32 s + 8 q .. +7.
     f32x4 acc[P / 16];
 #pragma unroll
     for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     for (int kb = 0; kb < N / 32; ++kb)
 #pragma unroll
       for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(hs + (tp * 16 + r) * HLD + kb * 32 + q * 8)),
+        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(hs + pcol(tp, r) * HLD + kb * 32 + q * 8)),
                             as_bf16x8(cf[kb]), acc[tp]);
     {
       const float s0 = exp2_fast(ae);
@@ -184,16 +188,22 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
         acc[tp] = mfma_bf16(frag_kmajor(xs + nb * 32 * LDX + tp * 16, LDX, lane), a, acc[tp]);
     }
     if (live(ii + 1)) load_rb(rb_of(ii + 1));  // the fragments above are dead now
-    // 5. skip term and 8-byte stores of the lane's 4 adjacent outputs
+    // 5. skip term and 16-byte stores of the lane's 8 adjacent outputs
     if (rowok) {
       uint16_t* yrow = Y + (int64_t)(ci.start + irow) * xrow + (int64_t)h * P;
 #pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) {
-        const int p = tp * 16 + q * 4;
-        const uint2 xv = *(const uint2*)(xs + irow * LDX + p);
-        const float y0 = acc[tp][0] + Dh * bf_lo(xv.x), y1 = acc[tp][1] + Dh * bf_hi(xv.x);
-        const float y2 = acc[tp][2] + Dh * bf_lo(xv.y), y3 = acc[tp][3] + Dh * bf_hi(xv.y);
-        *(uint2*)(yrow + p) = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
+      for (int s = 0; s < P / 32; ++s) {
+        const u32x4 xv = lds_cols8_perm(xs + irow * LDX, s, q);
+        f32x4 y0 = acc[2 * s], y1 = acc[2 * s + 1];
+        y0[0] += Dh * bf_lo(xv[0]);
+        y0[1] += Dh * bf_hi(xv[0]);
+        y0[2] += Dh * bf_lo(xv[1]);
+        y0[3] += Dh * bf_hi(xv[1]);
+        y1[0] += Dh * bf_lo(xv[2]);
+        y1[1] += Dh * bf_hi(xv[2]);
+        y1[2] += Dh * bf_lo(xv[3]);
+        y1[3] += Dh * bf_hi(xv[3]);
+        *(u32x4*)(yrow + 32 * s + 8 * q) = pack_bf8(y0, y1);
       }
     }
   }
