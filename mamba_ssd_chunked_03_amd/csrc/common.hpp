@@ -224,6 +224,7 @@ __device__ __forceinline__ void store4(uint16_t* dst, float4 v) {
 // ------------------------------------------------------------------ DPP ----
 // DPP controls (GFX9 encoding).
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowRor8 = 0x128, kRowHalfMirror = 0x141, kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
 template <int CTRL, int ROW_MASK = 0xf>
@@ -252,6 +253,35 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f<0x122>(0.f, v);  // row_ror:2
   v += dpp_f<0x121>(0.f, v);  // row_ror:1
   return v;
+}
+
+// Reduce-scatter of four per-lane values over the 16 lanes of each DPP row:
+// on return, lane r of a row holds that row's sum of v[r / 4].  Three exchange
+// steps (lanes r ^ 8, the mirror inside each half-row, then the quad) move half
+// of the remaining values each, 11 instructions instead of 4 x 8.
+__device__ __forceinline__ float row_reduce_scatter4(float v0, float v1, float v2, float v3, int r) {
+  const bool h8 = r >= 8;  // lanes below 8 keep values 0, 1; the others 2, 3
+  const float t0 = (h8 ? v2 : v0) + dpp_f<kRowRor8>(0.f, h8 ? v0 : v2);
+  const float t1 = (h8 ? v3 : v1) + dpp_f<kRowRor8>(0.f, h8 ? v1 : v3);
+  const bool h4 = (r & 7) >= 4;  // then lanes 0-3 of each half keep t0, lanes 4-7 t1
+  float u = (h4 ? t1 : t0) + dpp_f<kRowHalfMirror>(0.f, h4 ? t0 : t1);
+  u += dpp_f<kQuadXor1>(0.f, u);
+  u += dpp_f<kQuadXor2>(0.f, u);
+  return u;
+}
+
+// Reduce-scatter of four per-lane values over the four rows of a wavefront
+// (lanes r, r + 16, r + 32, r + 48): on return lane r of row q holds the sum of
+// v[q] over those lanes.  gfx950's row swaps: permlane16_swap exchanges the odd
+// rows of its first operand with the even rows of its second, permlane32_swap
+// the upper half of the first with the lower half of the second.
+__device__ __forceinline__ float col_reduce_scatter4(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+  const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows 0, 2: v0; rows 1, 3: v1
+  const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // Sum over all 64 lanes (result valid in every lane).

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
   static_assert(NPX >= 1, "headdim");
   __shared__ __attribute__((aligned(16))) uint16_t xt[2][64 * LX];
   __shared__ float kred[8][4][64];
-  __shared__ float sv[8][192];  // per head of 8: acs rows | acs cols | delta cols
+  __shared__ __attribute__((aligned(16))) float sv[8][320];  // per head of a block of 8 (below)
   const int Q = m.Q, T = Q / 64, NT = T * (T + 1) / 2;
   const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
   const int tile = lid % NT, k = lid / NT / G, g = (lid / NT) % G;
@@ -337,13 +337,16 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
   const bool diag = ti == tj;
   const int64_t kg = (int64_t)k * G + g;
   const uint16_t* cbm = CB + kg * Q * Q;
+  // CB at this lane's 16 outputs: every load unconditional (the chunk's CB
+  // tile is whole in memory), then the causal mask j < i < len
   float cbv[4][4];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
-      cbv[b][rr] = (i < len && j < i) ? bf2f(cbm[(int64_t)i * Q + j]) : 0.f;
+      const float c = bf2f(cbm[(int64_t)i * Q + j]);
+      cbv[b][rr] = (i < len && j < i) ? c : 0.f;
     }
   f32x4 sum[4];
 #pragma unroll
@@ -364,6 +367,31 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
                                 : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // Per head of a block of 8, sv holds acs of the tile's rows [0, 64), acs of
+  // its columns [64, 128) and delta of its columns [128, 192); an off-diagonal
+  // tile (anchor e = its last column, e < i for every row i) also holds
+  //   [192, 256) rho_i = 2^(acs_i - acs_e) (0 past the chunk's end),
+  //   [256, 320) gam_j = 2^(acs_e - acs_j) delta_j,
+  // so that its per-element factor is rho_i gam_j (a diagonal tile takes one
+  // exp per element).  Called at the start of each block of 8 heads: the
+  // previous block's readers are done (the column reduction ends in a barrier).
+  auto fill_sv = [&](int h0, int nh) {
+    for (int e = tid; e < nh * 192; e += 256) {
+      const int sl = e / 192, c = e % 192;
+      const int64_t khs = (int64_t)k * H + h0 + sl;
+      const int t = (c < 64) ? ti * 64 + c : jt0 + (c % 64);  // < Q: inside the workspace
+      sv[sl][c] = (c < 128) ? acs[khs * Q + t] : delta[khs * Q + t];
+    }
+    if (!diag) {
+      __syncthreads();
+      for (int e = tid; e < nh * 128; e += 256) {
+        const int sl = e >> 7, c = e & 127;
+        const float ae = sv[sl][127];
+        sv[sl][192 + c] = (c < 64) ? ((ti * 64 + c < len) ? exp2_fast(sv[sl][c] - ae) : 0.f)
+                                   : exp2_fast(ae - sv[sl][c]) * sv[sl][c + 64];
+      }
+    }
+  };
   load_head(g * hpg);
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
@@ -374,18 +402,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
       const int e = tid + c * 256, row = e / PER, c8 = e % PER;
       *(u32x4*)(xbuf + row * LX + c8 * 8) = px[c];
     }
-    if ((hh & 7) == 0) {
-      // acs of the tile's rows and columns and delta of its columns for the next
-      // 8 heads; the previous block's readers are done (the column reduction
-      // below ends in a barrier)
-      const int nh = min(8, hpg - hh);
-      for (int e = tid; e < nh * 192; e += 256) {
-        const int sl = e / 192, c = e % 192;
-        const int64_t khs = kh + sl;
-        const int t = (c < 64) ? ti * 64 + c : jt0 + (c % 64);
-        sv[sl][c] = (c < 128) ? acs[khs * Q + t] : delta[khs * Q + t];
-      }
-    }
+    if ((hh & 7) == 0) fill_sv(h, min(8, hpg - hh));
     __syncthreads();
     bf16x8 af[P / 32];
 #pragma unroll
@@ -400,27 +417,23 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
         dxb[b] = mfma_bf16(af[kb], as_bf16x8(*(const u32x4*)(xbuf + (b * 16 + r) * LX + kb * 32 + q * 8)),
                            dxb[b]);
     }
+    // v = dCB^h_ij, M_ij = v CB_ij; R_i and K_j both add the exact products
     const float* svh = sv[hh & 7];
     float Rl[4] = {0.f, 0.f, 0.f, 0.f}, Kl[4] = {0.f, 0.f, 0.f, 0.f};
     if (!diag) {
-      // anchor e = the tile's last column (e < i for every row of the tile)
-      const float ae = svh[64 + 63];
-      float rho[4], gam[4];
+      const float4 rho = *(const float4*)(svh + 192 + w * 16 + q * 4);
+      const float rr4[4] = {rho.x, rho.y, rho.z, rho.w};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        rho[rr] = (i0 + q * 4 + rr < len) ? exp2_fast(svh[w * 16 + q * 4 + rr] - ae) : 0.f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) gam[b] = exp2_fast(ae - svh[64 + b * 16 + r]) * svh[128 + b * 16 + r];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b) {
+        const float gam = svh[256 + b * 16 + r];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float v = dxb[b][rr] * rho[rr] * gam[b];
+          const float v = dxb[b][rr] * rr4[rr] * gam;
           sum[b][rr] += v;
-          const float mij = v * cbv[b][rr];
-          Rl[rr] += mij;
-          Kl[b] += mij;
+          Rl[rr] = fmaf(v, cbv[b][rr], Rl[rr]);
+          Kl[b] = fmaf(v, cbv[b][rr], Kl[b]);
         }
+      }
     } else {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -431,26 +444,20 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
           float v = dxb[b][rr] * exp2_fast(svh[w * 16 + q * 4 + rr] - aj) * dj;
           v = (j <= i && i < len) ? v : 0.f;
           sum[b][rr] += v;
-          const float mij = v * cbv[b][rr];  // cbv is zero unless j < i < len
-          Rl[rr] += mij;
-          Kl[b] += mij;
+          Rl[rr] = fmaf(v, cbv[b][rr], Rl[rr]);  // cbv is zero unless j < i < len
+          Kl[b] = fmaf(v, cbv[b][rr], Kl[b]);
         }
       }
     }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float v = row_sum16(Rl[rr]);
-      const int i = i0 + q * 4 + rr;
-      if (r == 0 && i < len) Rp[(kh * T + tj) * Q + i] = v;
+    {
+      // row sums: lane r ends with row i0 + 4q + r/4; lanes r % 4 == 0 store
+      const float v = row_reduce_scatter4(Rl[0], Rl[1], Rl[2], Rl[3], r);
+      const int i = i0 + q * 4 + (r >> 2);
+      if ((r & 3) == 0 && i < len) Rp[(kh * T + tj) * Q + i] = v;
     }
     const int slot = hh & 7;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float c = Kl[b];
-      c += __shfl_xor(c, 16);
-      c += __shfl_xor(c, 32);
-      if (q == 0) kred[slot][w][b * 16 + r] = c;
-    }
+    // column sums over the wave's rows: lane (r, q) ends with column 16 q + r
+    kred[slot][w][q * 16 + r] = col_reduce_scatter4(Kl[0], Kl[1], Kl[2], Kl[3]);
     if (slot == 7 || hh == hpg - 1) {  // cross-wave column sums, fixed order, every 8 heads
       __syncthreads();
       for (int e = tid; e < (slot + 1) * 64; e += 256) {
