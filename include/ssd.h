@@ -48,8 +48,10 @@
  *  - Pointers must be 16-byte aligned.
  *  - Supported: io dtype f32 or bf16; headdim and dstate in {16, 32, 64, 128}
  *    (bf16 additionally needs headdim >= 32 and dstate >= 32);
- *    chunk_size in {64, 128, 256}; nheads % ngroups == 0; any seqlen >= 0 and any
- *    sequence lengths (partial chunks are masked).  Anything else returns
+ *    chunk_size in {64, 128, 256}; nheads % ngroups == 0; chunk_size * nheads *
+ *    headdim * 4 and chunk_size * ngroups * dstate * 4 at most 2^31 - 1 (one
+ *    chunk's token rows are addressed with 32-bit byte offsets); any seqlen >= 0
+ *    and any sequence lengths (partial chunks are masked).  Anything else returns
  *    SSD_ERR_UNSUPPORTED.
  *  - cu_seqlens contents are the caller's contract; with the environment variable
  *    SSD_DEBUG=1 they are copied to the host and checked (SSD_ERR_VARLEN).  That

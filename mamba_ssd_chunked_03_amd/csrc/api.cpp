@@ -45,6 +45,10 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   const int64_t tokens = (int64_t)pr->batch * pr->seqlen;
   if (tokens > INT32_MAX / 2 || (int64_t)pr->nheads > 65535 || (int64_t)pr->ngroups > 65535)
     return SSD_ERR_UNSUPPORTED;
+  // kernels address a chunk's token rows with 32-bit byte offsets
+  if ((int64_t)Q * pr->nheads * pr->headdim * 4 > INT32_MAX ||
+      (int64_t)Q * pr->ngroups * pr->dstate * 4 > INT32_MAX)
+    return SSD_ERR_UNSUPPORTED;
   p.B = pr->batch;
   p.L = pr->seqlen;
   p.H = pr->nheads;

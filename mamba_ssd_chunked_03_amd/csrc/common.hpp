@@ -93,6 +93,27 @@ __device__ __forceinline__ bf16x8 frag_kmajor(const uint16_t* tile, int ld, int 
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// --------------------------------------------------------- buffer access ----
+// A buffer resource over the `bytes` bytes that start at p.  Accesses at byte
+// offsets >= bytes (vector, instruction and scalar offset together) are range
+// checked by the hardware: loads return zero and stores are dropped, without
+// touching memory.  With `bytes` ending at a chunk's last valid row, a tile's
+// rows past the chunk's end read as zero and are never written, with no branch,
+// and every offset is a 32-bit value (callers keep a chunk's span below 2^31
+// bytes).  Dword 3 of the descriptor selects the 32-bit data format with no
+// swizzling, the untyped layout of this GPU family.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(brsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(brsrc r, uint32_t off, u32x4 v) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 0);
+}
+
 // ---------------------------------------------- column order of MFMA rows ----
 // A row of W outputs (W a multiple of 32) computed as W/16 transposed 16x16
 // tiles, the column index coming from a K-major LDS operand read with

@@ -83,19 +83,23 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   const int NB = Q / 16, nii = (NB + kDxWaves - 1) / kDxWaves;
   auto rb_of = [&](int ii) { return kDxWaves * ii + ((ii & 1) ? (kDxWaves - 1 - w) : w); };
   auto live = [&](int ii) { return ii < nii && rb_of(ii) < NB && rb_of(ii) * 16 < len; };
+  // Buffer resources over the chunk's valid rows: rows past its end read as
+  // zero and are not written.
+  const brsrc rx = make_rsrc(xb, (uint32_t)(len * xrow * 2)), rbm = make_rsrc(bb, (uint32_t)(len * brow * 2));
+  const brsrc rc = make_rsrc(cbt, (uint32_t)(len * Q * 2));
+  const brsrc rdx = make_rsrc(DX + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
   u32x4 px[P / 32];  // x_j, the lane's 8 adjacent columns per tile pair (pcol)
   u32x4 bq[N / 32], pc1, pcd;
   auto load_rb = [&](int rb) {
-    const int jr = rb * 16 + r, c0 = rb / 2;
-    const bool ok = jr < len, off = ok && c0 + 1 < (len + 31) / 32;
+    const uint32_t jr = rb * 16 + r, c0 = rb / 2;
+    const uint32_t xo = jr * (uint32_t)(xrow * 2) + q * 16, bo = jr * (uint32_t)(brow * 2) + q * 16;
+    const uint32_t co = jr * (uint32_t)(Q * 2) + q * 16;
 #pragma unroll
-    for (int s = 0; s < P / 32; ++s)
-      px[s] = ok ? *(const u32x4*)(xb + (int64_t)jr * xrow + 32 * s + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < P / 32; ++s) px[s] = buf_load16(rx, xo + 64 * s);
 #pragma unroll
-    for (int kk = 0; kk < N / 32; ++kk)
-      bq[kk] = ok ? *(const u32x4*)(bb + (int64_t)jr * brow + kk * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
-    pc1 = off ? *(const u32x4*)(cbt + (int64_t)jr * Q + (c0 + 1) * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
-    pcd = ok ? *(const u32x4*)(cbt + (int64_t)jr * Q + c0 * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < N / 32; ++kk) bq[kk] = buf_load16(rbm, bo + 64 * kk);
+    pc1 = buf_load16(rc, co + (c0 + 1) * 64);  // (unused when no later block exists)
+    pcd = buf_load16(rc, co + c0 * 64);
   };
   if (live(0)) load_rb(rb_of(0));
   // every prologue load in flight before the first LDS store waits on one:
@@ -191,11 +195,10 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
       for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= s0;
       const float* wrow = &wt[cb0][0];
       u32x4 cvn = pc1;
+      const uint32_t co = (uint32_t)jrow * (uint32_t)(Q * 2) + q * 16;
       for (int sx = cb0 + 1; sx < s_end; ++sx) {
         const u32x4 cv = cvn;
-        if (sx + 1 < s_end)  // one step of lookahead
-          cvn = rowok ? *(const u32x4*)(cbt + (int64_t)jrow * Q + (sx + 1) * 32 + q * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
+        if (sx + 1 < s_end) cvn = buf_load16(rc, co + (sx + 1) * 64);  // one step of lookahead
         const float4 f0 = *(const float4*)(wrow + sx * 32 + q * 8);
         const float4 f1 = *(const float4*)(wrow + sx * 32 + q * 8 + 4);
         u32x4 av;
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
     // per-row dots and the store
     const float dj = rowok ? sd[jrow] : 0.f;
     float xt = 0.f, dxx = 0.f;
-    uint16_t* dxrow = DX + (int64_t)(ci.start + jrow) * xrow + (int64_t)h * P;
+    const uint32_t dxo = (uint32_t)jrow * (uint32_t)(xrow * 2) + q * 16;
 #pragma unroll
     for (int s = 0; s < P / 32; ++s) {
       const u32x4 dq = lds_cols8_perm(dyt + jrow * LDY, s, q);  // rows past the end are zero
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
         o[2 * u] = pack_bf2(dj * a[0] + Dh * y0, dj * a[1] + Dh * y1);
         o[2 * u + 1] = pack_bf2(dj * a[2] + Dh * y2, dj * a[3] + Dh * y3);
       }
-      if (rowok) *(u32x4*)(dxrow + 32 * s + 8 * q) = o;
+      buf_store16(rdx, dxo + 64 * s, o);  // dropped for rows past the end
     }
     xs += __shfl_xor(xs, 16);
     xs += __shfl_xor(xs, 32);
@@ -353,18 +356,18 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
   for (int b = 0; b < 4; ++b) sum[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the next head's rows: this wave's dy fragments and this thread's x pieces
   u32x4 ay[P / 32], px[NPX];
+  // (buffer resources over the chunk's valid rows: rows past the end read as zero)
+  const uint32_t yo = (uint32_t)irow * (uint32_t)(xrow * 2) + q * 16;
   auto load_head = [&](int h) {
-    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
-    const uint16_t* xb = X + (int64_t)(ci.start + jt0) * xrow + (int64_t)h * P;
+    const brsrc rdy = make_rsrc(DY + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
+    const brsrc rxt = make_rsrc(X + (int64_t)(ci.start + jt0) * xrow + (int64_t)h * P,
+                                (uint32_t)(max(len - jt0, 0) * xrow * 2));
 #pragma unroll
-    for (int kb = 0; kb < P / 32; ++kb)
-      ay[kb] = (irow < len) ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < P / 32; ++kb) ay[kb] = buf_load16(rdy, yo + 64 * kb);
 #pragma unroll
     for (int c = 0; c < NPX; ++c) {
-      const int e = tid + c * 256, row = e / PER, c8 = e % PER;
-      px[c] = (jt0 + row < len) ? *(const u32x4*)(xb + (int64_t)row * xrow + c8 * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t e = tid + c * 256, row = e / PER, c8 = e % PER;
+      px[c] = buf_load16(rxt, row * (uint32_t)(xrow * 2) + c8 * 16);
     }
   };
   // Per head of a block of 8, sv holds acs of the tile's rows [0, 64), acs of
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
 // column groups permuted (common.hpp, pcol), so a lane's outputs are 8 adjacent
 // columns per tile pair and C is loaded and dC stored 16 bytes at a time.
 template <int P, int N>
-__global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
+__global__ __launch_bounds__(256, 3) void bwd_dc_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ DY, const uint16_t* __restrict__ dCBg,
     const float* __restrict__ acs, const uint16_t* __restrict__ Hs, uint16_t* __restrict__ dC,
@@ -524,7 +527,10 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   const int i0 = tile * 64 + w * 16;
   const bool active = i0 < len;
   const int irow = i0 + r;
-  const bool rowok = irow < len;
+  // buffer resources over the chunk's valid rows (rows past the end: zero, not written)
+  const brsrc rdcb = make_rsrc(dcb, (uint32_t)(len * Q * 2)), rcm = make_rsrc(cb, (uint32_t)(len * brow * 2));
+  const uint32_t ro = (uint32_t)irow * (uint32_t)(brow * 2) + q * 16;  // this lane's offset in a B/C row
+  const uint32_t yo = (uint32_t)irow * (uint32_t)(xrow * 2) + q * 16;  // and in an x/dy row
   // acc[nb][rr] = dC[irow][pcol(nb, 4 q + rr)]
   f32x4 acc[N / 16];
 #pragma unroll
@@ -536,8 +542,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     __syncthreads();
     if (!active) continue;
     for (int jb = jt * 64; jb < min(jt * 64 + 64, i0 + 16); jb += 32) {
-      const bf16x8 a = as_bf16x8(rowok ? *(const u32x4*)(dcb + (int64_t)irow * Q + jb + q * 8)
-                                       : u32x4{0u, 0u, 0u, 0u});
+      const bf16x8 a = as_bf16x8(buf_load16(rdcb, (uint32_t)irow * (uint32_t)(Q * 2) + jb * 2 + q * 16));
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
         acc[nb] = mfma_bf16(frag_kmajor(bt + (jb - jt * 64) * LDB + nb * 16, LDB, lane), a, acc[nb]);
@@ -546,8 +551,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
   // C_i values of this lane's outputs, 8 adjacent per tile pair
   u32x4 cq[N / 32];
 #pragma unroll
-  for (int s = 0; s < N / 32; ++s)
-    cq[s] = rowok ? *(const u32x4*)(cb + (int64_t)irow * brow + 32 * s + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+  for (int s = 0; s < N / 32; ++s) cq[s] = buf_load16(rcm, ro + 64 * s);
   // the next head's H pieces, dy fragments and acs_i
   u32x4 ph[NPH], py[P / 32];
   float pa = 0.f;
@@ -559,11 +563,10 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
       const int e = (tid + c * 256) * 8;
       ph[c] = e < P * N ? *(const u32x4*)(src + e) : u32x4{0u, 0u, 0u, 0u};
     }
-    const uint16_t* dyb = DY + (int64_t)ci.start * xrow + (int64_t)h * P;
+    const brsrc rdy = make_rsrc(DY + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
 #pragma unroll
-    for (int kb = 0; kb < P / 32; ++kb)
-      py[kb] = rowok ? *(const u32x4*)(dyb + (int64_t)irow * xrow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
-    pa = rowok ? acs[kh * Q + irow] : 0.f;
+    for (int kb = 0; kb < P / 32; ++kb) py[kb] = buf_load16(rdy, yo + 64 * kb);
+    pa = irow < len ? acs[kh * Q + irow] : 0.f;
   };
   __syncthreads();  // every wave is done with the B pieces in ub[0]
   load_head(g * hpg);
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     }
     __syncthreads();
     // this head's dy fragment scaled by 2^acs_i (one row per lane)
-    const float ei = rowok ? exp2_fast(pa) : 0.f;
+    const float ei = irow < len ? exp2_fast(pa) : 0.f;
     bf16x8 ays[P / 32];
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb) {
@@ -602,12 +605,11 @@ __global__ __launch_bounds__(256) void bwd_dc_bf16_kernel(
     }
     rsum += __shfl_xor(rsum, 16);
     rsum += __shfl_xor(rsum, 32);
-    if (q == 0 && rowok) rout[kh * Q + irow] = rsum;
+    if (q == 0 && irow < len) rout[kh * Q + irow] = rsum;
   }
-  if (!rowok) return;
-  uint16_t* dcrow = dC + (int64_t)(ci.start + irow) * brow + (int64_t)g * N;
+  const brsrc rdc = make_rsrc(dC + (int64_t)ci.start * brow + (int64_t)g * N, (uint32_t)(len * brow * 2));
 #pragma unroll
-  for (int s = 0; s < N / 32; ++s) *(u32x4*)(dcrow + 32 * s + 8 * q) = pack_bf8(acc[2 * s], acc[2 * s + 1]);
+  for (int s = 0; s < N / 32; ++s) buf_store16(rdc, ro + 64 * s, pack_bf8(acc[2 * s], acc[2 * s + 1]));
 }
 
 // ------------------------------------------------------------ bwd_db bf16 ----
@@ -643,6 +645,9 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   const bool active = j0 < len;
   const int jrow = j0 + r;
   const bool rowok = jrow < len;
+  // buffer resources over the chunk's valid rows (rows past the end: zero, not written)
+  const brsrc rdcbt = make_rsrc(dcbt, (uint32_t)(len * Q * 2));
+  const uint32_t xo = (uint32_t)jrow * (uint32_t)(xrow * 2) + q * 16;
   f32x4 acc[N / 16];  // acc[nb][rr] = dB[jrow][pcol(nb, 4 q + rr)]
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -654,8 +659,7 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
     if (!active) continue;
     const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
     for (int ib = ib0; ib < min(it * 64 + 64, len); ib += 32) {
-      const bf16x8 a = as_bf16x8(rowok ? *(const u32x4*)(dcbt + (int64_t)jrow * Q + ib + q * 8)
-                                       : u32x4{0u, 0u, 0u, 0u});
+      const bf16x8 a = as_bf16x8(buf_load16(rdcbt, (uint32_t)jrow * (uint32_t)(Q * 2) + ib * 2 + q * 16));
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
         acc[nb] = mfma_bf16(frag_kmajor(ct + (ib - it * 64) * LDB + nb * 16, LDB, lane), a, acc[nb]);
@@ -671,10 +675,9 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
       const int e = (tid + c * 256) * 8;
       ph[c] = e < P * N ? *(const u32x4*)(src + e) : u32x4{0u, 0u, 0u, 0u};
     }
-    const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
+    const brsrc rxh = make_rsrc(X + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
 #pragma unroll
-    for (int kb = 0; kb < P / 32; ++kb)
-      px[kb] = rowok ? *(const u32x4*)(xb + (int64_t)jrow * xrow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < P / 32; ++kb) px[kb] = buf_load16(rxh, xo + 64 * kb);
     pl = acs[kh * Q + len - 1];
     pj = rowok ? acs[kh * Q + jrow] : 0.f;
     pd = rowok ? delta[kh * Q + jrow] : 0.f;
@@ -708,10 +711,10 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
       for (int nb = 0; nb < N / 16; ++nb)
         acc[nb] = mfma_bf16(frag_kmajor(dtt + kb * 32 * LDB + nb * 16, LDB, lane), axs[kb], acc[nb]);
   }
-  if (!rowok) return;
-  uint16_t* dbrow = dB + (int64_t)(ci.start + jrow) * brow + (int64_t)g * N;
+  const brsrc rdb = make_rsrc(dB + (int64_t)ci.start * brow + (int64_t)g * N, (uint32_t)(len * brow * 2));
+  const uint32_t bo = (uint32_t)jrow * (uint32_t)(brow * 2) + q * 16;
 #pragma unroll
-  for (int s = 0; s < N / 32; ++s) *(u32x4*)(dbrow + 32 * s + 8 * q) = pack_bf8(acc[2 * s], acc[2 * s + 1]);
+  for (int s = 0; s < N / 32; ++s) buf_store16(rdb, bo + 64 * s, pack_bf8(acc[2 * s], acc[2 * s + 1]));
 }
 
 // ------------------------------------------------------------ fp32 paths ----

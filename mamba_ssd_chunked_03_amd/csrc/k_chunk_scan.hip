@@ -75,18 +75,20 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
   auto live = [&](int ii) { return ii < nii && rb_of(ii) < NB && rb_of(ii) * 16 < len; };
   // (the diagonal fragment has its own register: indexing the array with the
   // run-time block index would become a select over every element)
+  // Buffer resources over the chunk's valid rows: rows past its end read as
+  // zero and are not written.
+  const brsrc rcm = make_rsrc(cb, (uint32_t)(len * crow * 2)), rcb = make_rsrc(cbm, (uint32_t)(len * Q * 2));
+  const brsrc ry = make_rsrc(Y + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
   u32x4 cf[N / 32], cbf[QMAX / 32], cbd;
   auto load_rb = [&](int rb) {
-    const int irow = rb * 16 + r, nb = rb / 2;
-    const bool ok = irow < len;
+    const uint32_t irow = rb * 16 + r, nb = rb / 2;
+    const uint32_t co = irow * (uint32_t)(crow * 2) + q * 16, bo = irow * (uint32_t)(Q * 2) + q * 16;
 #pragma unroll
-    for (int kb = 0; kb < N / 32; ++kb)
-      cf[kb] = ok ? *(const u32x4*)(cb + (int64_t)irow * crow + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < N / 32; ++kb) cf[kb] = buf_load16(rcm, co + 64 * kb);
 #pragma unroll
     for (int sx = 0; sx < QMAX / 32; ++sx)
-      cbf[sx] = (ok && sx < nb) ? *(const u32x4*)(cbm + (int64_t)irow * Q + sx * 32 + q * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
-    cbd = ok ? *(const u32x4*)(cbm + (int64_t)irow * Q + nb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+      cbf[sx] = (sx < (int)nb) ? buf_load16(rcb, bo + 64 * sx) : u32x4{0u, 0u, 0u, 0u};
+    cbd = buf_load16(rcb, bo + 64 * nb);
   };
   if (live(0)) load_rb(rb_of(0));
   {
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     }
     if (live(ii + 1)) load_rb(rb_of(ii + 1));  // the fragments above are dead now
     // 5. skip term and 16-byte stores of the lane's 8 adjacent outputs
-    if (rowok) {
-      uint16_t* yrow = Y + (int64_t)(ci.start + irow) * xrow + (int64_t)h * P;
+    {
+      const uint32_t yo = (uint32_t)irow * (uint32_t)(xrow * 2) + q * 16;
 #pragma unroll
       for (int s = 0; s < P / 32; ++s) {
         const u32x4 xv = lds_cols8_perm(xs + irow * LDX, s, q);
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
         y1[1] += Dh * bf_hi(xv[2]);
         y1[2] += Dh * bf_lo(xv[3]);
         y1[3] += Dh * bf_hi(xv[3]);
-        *(u32x4*)(yrow + 32 * s + 8 * q) = pack_bf8(y0, y1);
+        buf_store16(ry, yo + 64 * s, pack_bf8(y0, y1));  // dropped for rows past the end
       }
     }
   }

@@ -92,6 +92,10 @@ def test_bwd_validation(L):
     (dict(headdim=48), UNSUP), (dict(dstate=256), UNSUP), (dict(io_dtype=5), UNSUP),
     (dict(headdim=16), UNSUP),                 # bf16 needs headdim >= 32
     (dict(headdim=16, dstate=16, io_dtype=0), OK),
+    # one chunk's token rows must span less than 2^31 bytes (32-bit offsets)
+    (dict(nheads=16384, ngroups=8, headdim=128), UNSUP),
+    (dict(nheads=8192, ngroups=8, headdim=128), OK),
+    (dict(nheads=16384, ngroups=16384, headdim=32, dstate=128), UNSUP),
 ])
 def test_shape_validation(L, kw, code):
     p = prob(**kw)
