@@ -65,8 +65,8 @@ def kernel_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, d_final=False):
     tri = nck * G * (Q * (Q + 1) // 2) * esz
     s0 = nseq * H * P * N * 4
     return {
-        "chunk_cumsum": dt + 2 * f32_tok + decay,
-        "chunk_state": x + bc + 2 * f32_tok + st32,
+        "chunk_cumsum": dt + 2 * f32_tok + decay,        # (stage entry point; inside chunk_state)
+        "chunk_state": dt + x + bc + 2 * f32_tok + decay + st32,  # with the cumsum formed inline
         "state_passing": st32 + decay + st16 + (s0 if init else 0) + s0,
         "bmm_chunk": 2 * bc + 2 * tri,                   # CB and its transpose (saved for bwd)
         "chunk_scan": 2 * x + bc + tri + 2 * f32_tok + st16,

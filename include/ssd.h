@@ -102,9 +102,10 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   the results of a complete ssd_bwd call on the same arguments, so that the kernel
  *   finds its inputs; it rewrites its own outputs with the same values. */
 #define SSD_FLAG_BWD_KERNEL(k) ((k) << 8)
-/* SSD_FLAG_FWD_KERNEL(k), k = 1..5: the same for ssd_fwd, whose workspace and
+/* SSD_FLAG_FWD_KERNEL(k), k = 1..4: the same for ssd_fwd, whose workspace and
  *   outputs must hold a complete call's results on the same arguments: 1 chunk
- *   cumsum, 2 chunk states, 3 state passing, 4 C.B^T, 5 chunk scan. */
+ *   cumsum and chunk states (one kernel on the bf16 path), 2 state passing,
+ *   3 C.B^T, 4 chunk scan. */
 #define SSD_FLAG_FWD_KERNEL(k) ((k) << 12)
 
 typedef struct {

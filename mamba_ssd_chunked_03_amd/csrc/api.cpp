@@ -36,7 +36,7 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
     return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_BWD_KERNEL(7)) && !(pr->flags & SSD_FLAG_FROM_SAVED))
     return SSD_ERR_UNSUPPORTED;
-  if (((pr->flags >> 12) & 7) > 5) return SSD_ERR_UNSUPPORTED;
+  if (((pr->flags >> 12) & 7) > 4) return SSD_ERR_UNSUPPORTED;
   if (packed && (pr->batch != 1 || pr->nseq < 0)) return SSD_ERR_SHAPE;
   if (pr->io_dtype != SSD_F32 && pr->io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
   if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
@@ -267,8 +267,9 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   const int hb = p.io == SSD_BF16;
   void* CB = ws + l.CB;
   void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
-  // C.B^T needs only B and C: it runs on the side stream beside the cumsum, the
-  // chunk states and the state passing; the chunk scan waits for it.
+  // C.B^T needs only B and C: it runs on the side stream beside the cumsum and
+  // chunk states (one kernel on the bf16 path) and the state passing; the chunk
+  // scan waits for it.
   std::unique_lock<std::mutex> lane_lock;
   SideLane* side = (!only && p.nck > 0) ? side_lane(lane_lock) : nullptr;
   if (side) {  // events: 0 fork, 1 C.B^T done
@@ -277,16 +278,16 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, side->stream, CBt));
     SSD_TRY(hipEventRecord(side->ev[1], side->stream));
   }
-  if (!only || only == 1) SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
-  if (!only || only == 2) SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
-  if (!only || only == 3)
+  if (!only || only == 1)
+    SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st));
+  if (!only || only == 2)
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
   if (side) {
     SSD_TRY(hipStreamWaitEvent(st, side->ev[1], 0));
-  } else if (!only || only == 4) {
+  } else if (!only || only == 3) {
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
   }
-  if (!only || only == 5) SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
+  if (!only || only == 4) SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
   return SSD_OK;
 }
 
@@ -324,8 +325,7 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   float* U = (float*)(ws + l.U);
   void* dE = ws + l.dE;
   if (!(p.flags & SSD_FLAG_FROM_SAVED)) {  // forward intermediates, recomputed
-    SSD_TRY(launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st));
-    SSD_TRY(launch_chunk_state(p, x, B, delta, acs, T, kStateFwd, st));
+    SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st));
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, nullptr, 0, st));
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
   }

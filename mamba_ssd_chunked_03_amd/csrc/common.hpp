@@ -57,6 +57,22 @@ __device__ __forceinline__ float sigmoid_f(float z) {
   return z >= 0.f ? r : e * r;
 }
 
+// delta of one token (zero past the chunk's end): softplus(dt + bias) or dt + bias.
+// Shared by the cumsum kernel and the chunk-state kernel that forms it inline,
+// so that both produce the same bits.
+__device__ __forceinline__ float token_delta(float dtv, float bias, int softplus, bool in) {
+  const float z = dtv + bias;
+  const float d = softplus ? softplus_f(z) : z;
+  return in ? d : 0.f;
+}
+
+// The cumsum's per-token increment delta * A in log2 units, never fused into a
+// following add, so that every kernel that scans it rounds it the same way.
+__device__ __forceinline__ float scan_input(float d, float a2) {
+#pragma clang fp contract(off)
+  return d * a2;
+}
+
 // ----------------------------------------------------------------- MFMA ----
 // D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
 // Lane l holds A[l%16][8*(l/16) + 0..7], B[8*(l/16) + 0..7][l%16] and

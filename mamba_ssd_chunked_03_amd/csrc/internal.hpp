@@ -22,8 +22,9 @@ struct Prob {
 };
 
 // mode of the chunk-state contraction
-enum { kStateFwd = 0,      // T_c = sum_j delta_j 2^(acs_last - acs_j) x_j B_j^T
-       kStateDstates = 1   // U_c = sum_i 2^(acs_i) dy_i C_i^T
+enum { kStateFwd = 0,        // T_c = sum_j delta_j 2^(acs_last - acs_j) x_j B_j^T
+       kStateDstates = 1,    // U_c = sum_i 2^(acs_i) dy_i C_i^T
+       kStateFwdCumsum = 2   // kStateFwd with delta and acs formed in the kernel (stage 1 inline)
 };
 
 hipError_t launch_build_table(const Prob& p, const int32_t* cu_seqlens, int4* tab, int32_t* seq_off,
@@ -32,6 +33,12 @@ hipError_t launch_chunk_cumsum(const Prob& p, const float* dt, const float* dt_b
                                float* delta, float* acs, float* decay, hipStream_t st);
 hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,
                               const float* acs, float* out, int mode, hipStream_t st);
+// Stages 1 and 2 together: delta, acs and the chunk decays are written as
+// launch_chunk_cumsum writes them (bit for bit), and the chunk states T.  One
+// kernel on the bf16 path; the two kernels one after the other on the fp32 path.
+hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* Bm, const float* dt,
+                                     const float* dt_bias, const float* A, float* delta, float* acs,
+                                     float* decay, float* T, hipStream_t st);
 // passed: fp32, or bf16 when passed_bf16 (the carry and final_states stay fp32)
 hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
                                 const float* init, void* passed, int passed_bf16,

@@ -19,6 +19,13 @@
 // state keeps ~16 bits of precision; the states feed the fp32 final states.
 // Four wavefronts, each a (P/2) x (N/2) tile of 16x16 blocks.
 //
+// kStateFwdCumsum also forms stage 1 for its (chunk, head) first: wave w scans
+// tokens 64w .. 64w + 63 (delta, then the inclusive sum of delta A in log2
+// units) and adds the totals of the waves before it in order, which is the
+// cumsum kernel's pass-by-pass carry, so delta, acs and the chunk decay come out
+// with the same bits.  They are written for the later stages, and the token
+// scales are formed from the values in registers (no second read).
+//
 // fp32 path: one thread per output element, plain FMA loop (correctness path
 // for fp32 inputs; no rounding of any operand).
 #include "internal.hpp"
@@ -32,13 +39,20 @@ __device__ __forceinline__ float token_scale(int mode, const float* dl, const fl
 
 // MODE (kStateFwd / kStateDstates) is a template argument so that profiles
 // tell the forward chunk states and the backward adjoint states apart.
+// Stage-1 inputs of kStateFwdCumsum (unused by the other modes).
+struct CumsumIn {
+  const float *dt, *dt_bias, *A;
+  int softplus;
+  float* decay;
+};
+
 template <int P, int N, int MODE>
 __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, int H, int G,
                                                                const uint16_t* __restrict__ X,
                                                                const uint16_t* __restrict__ Y,
-                                                               const float* __restrict__ delta,
-                                                               const float* __restrict__ acs,
-                                                               float* __restrict__ out) {
+                                                               float* __restrict__ delta,
+                                                               float* __restrict__ acs,
+                                                               float* __restrict__ out, CumsumIn cs) {
   constexpr int KS = 64;       // tokens per LDS slice
   constexpr int LDX = P + 16;  // row strides: odd multiples of 32 bytes for the transpose reads
   constexpr int LDY = N + 16;
@@ -86,7 +100,32 @@ __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, in
     }
   };
   load_slice(0);  // independent of the token scales: in flight while they are formed
-  {
+  if constexpr (MODE == kStateFwdCumsum) {
+    __shared__ float wtot[4], alast;
+    const int t = tid;  // this thread's token (256 threads, chunks of at most 256 tokens); wave w
+                        // holds the cumsum's pass w
+    const bool in = t < len;
+    const float dtv = in ? cs.dt[(int64_t)(ci.start + t) * H + h] : 0.f;
+    const float bias = cs.dt_bias ? cs.dt_bias[h] : 0.f;
+    const float a2 = cs.A[h] * kLog2e;
+    const float d = token_delta(dtv, bias, cs.softplus, in);
+    const float sw = wave_inclusive_sum(scan_input(d, a2));
+    if (lane == 63) wtot[w] = sw;
+    __syncthreads();
+    float carry = 0.f;
+    for (int v = 0; v < w; ++v) carry = wtot[v] + carry;
+    const float incl = sw + carry;
+    if (t < Q) {
+      delta[kh * Q + t] = d;
+      acs[kh * Q + t] = in ? incl : 0.f;
+    }
+    if (t == len - 1) {
+      cs.decay[kh] = incl;
+      alast = incl;
+    }
+    __syncthreads();
+    if (t < Q) sc[t] = in ? d * exp2_fast(alast - incl) : 0.f;
+  } else {
     const float* dl = delta + kh * Q;
     const float* ac = acs + kh * Q;
     const float a_last = ac[len - 1];
@@ -176,15 +215,30 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H,
 }
 
 template <int P, int N>
-static void launch_cs_bf16(const Prob& p, const void* X, const void* Y, const float* delta,
-                           const float* acs, float* out, int mode, hipStream_t st) {
+static void launch_cs_bf16(const Prob& p, const void* X, const void* Y, float* delta, float* acs,
+                           float* out, int mode, const CumsumIn& cs, hipStream_t st) {
+  const dim3 grid((unsigned)p.nck, p.H);
+  const uint16_t *x = (const uint16_t*)X, *y = (const uint16_t*)Y;
   if (mode == kStateFwd)
-    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwd>), dim3((unsigned)p.nck, p.H), dim3(256),
-                       0, st, p.map, p.H, p.G, (const uint16_t*)X, (const uint16_t*)Y, delta, acs, out);
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwd>), grid, dim3(256), 0, st, p.map, p.H,
+                       p.G, x, y, delta, acs, out, cs);
+  else if (mode == kStateDstates)
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateDstates>), grid, dim3(256), 0, st, p.map,
+                       p.H, p.G, x, y, delta, acs, out, cs);
   else
-    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateDstates>), dim3((unsigned)p.nck, p.H),
-                       dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)X, (const uint16_t*)Y, delta,
-                       acs, out);
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwdCumsum>), grid, dim3(256), 0, st, p.map,
+                       p.H, p.G, x, y, delta, acs, out, cs);
+}
+
+static hipError_t launch_cs(const Prob& p, const void* X, const void* Y, float* delta, float* acs,
+                            float* out, int mode, const CumsumIn& cs, hipStream_t st) {
+#define SSD_CS_CASE(PP, NN) \
+  if (p.P == PP && p.N == NN) { launch_cs_bf16<PP, NN>(p, X, Y, delta, acs, out, mode, cs, st); return hipGetLastError(); }
+  SSD_CS_CASE(32, 32) SSD_CS_CASE(32, 64) SSD_CS_CASE(32, 128)
+  SSD_CS_CASE(64, 32) SSD_CS_CASE(64, 64) SSD_CS_CASE(64, 128)
+  SSD_CS_CASE(128, 32) SSD_CS_CASE(128, 64) SSD_CS_CASE(128, 128)
+#undef SSD_CS_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,
@@ -196,13 +250,20 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
                        mode, (const float*)X, (const float*)Y, delta, acs, out);
     return hipGetLastError();
   }
-#define SSD_CS_CASE(PP, NN) \
-  if (p.P == PP && p.N == NN) { launch_cs_bf16<PP, NN>(p, X, Y, delta, acs, out, mode, st); return hipGetLastError(); }
-  SSD_CS_CASE(32, 32) SSD_CS_CASE(32, 64) SSD_CS_CASE(32, 128)
-  SSD_CS_CASE(64, 32) SSD_CS_CASE(64, 64) SSD_CS_CASE(64, 128)
-  SSD_CS_CASE(128, 32) SSD_CS_CASE(128, 64) SSD_CS_CASE(128, 128)
-#undef SSD_CS_CASE
-  return hipErrorInvalidValue;
+  // (the kStateFwd and kStateDstates modes only read delta and acs)
+  return launch_cs(p, X, Y, const_cast<float*>(delta), const_cast<float*>(acs), out, mode, CumsumIn{}, st);
+}
+
+hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* Bm, const float* dt,
+                                     const float* dt_bias, const float* A, float* delta, float* acs,
+                                     float* decay, float* T, hipStream_t st) {
+  if (p.nck == 0) return hipSuccess;
+  if (p.io == 0 || p.Q > 256) {
+    const hipError_t e = launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st);
+    if (e != hipSuccess) return e;
+    return launch_chunk_state(p, X, Bm, delta, acs, T, kStateFwd, st);
+  }
+  return launch_cs(p, X, Bm, delta, acs, T, kStateFwdCumsum, CumsumIn{dt, dt_bias, A, p.softplus, decay}, st);
 }
 
 }  // namespace ssd

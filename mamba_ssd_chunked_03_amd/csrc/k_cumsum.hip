@@ -54,10 +54,8 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(ChunkMap m, int H, in
     for (int t0 = 0; t0 < Q; t0 += 64) {
       const int t = t0 + lane;
       const bool in = t < ci.len;
-      float z = tile[t * (kCumsumHeads + 1) + hh] + bias;
-      float d = softplus ? softplus_f(z) : z;
-      d = in ? d : 0.f;
-      float incl = wave_inclusive_sum(d * a2) + carry;
+      const float d = token_delta(tile[t * (kCumsumHeads + 1) + hh], bias, softplus, in);
+      float incl = wave_inclusive_sum(scan_input(d, a2)) + carry;
       carry = wave_last(incl);
       delta[base + t] = d;
       acs[base + t] = in ? incl : 0.f;

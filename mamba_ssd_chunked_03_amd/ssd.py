@@ -28,7 +28,8 @@ BWD_KERNELS = ("dstates", "reverse_state_passing", "bwd_dx", "bwd_dcb", "bwd_dc"
                "bwd_finalize")
 
 
-FWD_KERNELS = ("chunk_cumsum", "chunk_state", "state_passing", "bmm_chunk", "chunk_scan")
+# "chunk_state" forms delta and the within-chunk cumsum too (one kernel on the bf16 path)
+FWD_KERNELS = ("chunk_state", "state_passing", "bmm_chunk", "chunk_scan")
 
 
 def FLAG_BWD_KERNEL(k):

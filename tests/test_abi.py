@@ -142,8 +142,8 @@ def test_flags(L):
     assert fwd_status(L, prob(flags=ssd.FLAG_BWD_KERNEL(8))) == UNSUP
     p = prob(flags=ssd.FLAG_FROM_SAVED | ssd.FLAG_BWD_KERNEL(7))
     assert fwd_status(L, p, ws_bytes=1) == WS  # accepted: only the workspace is wrong
-    assert fwd_status(L, prob(flags=ssd.FLAG_FWD_KERNEL(6))) == UNSUP
-    assert fwd_status(L, prob(flags=ssd.FLAG_FWD_KERNEL(5)), ws_bytes=1) == WS
+    assert fwd_status(L, prob(flags=ssd.FLAG_FWD_KERNEL(5))) == UNSUP
+    assert fwd_status(L, prob(flags=ssd.FLAG_FWD_KERNEL(4)), ws_bytes=1) == WS
     p = prob(flags=1)  # keeping the forward's intermediates needs the backward-sized workspace
     fwd_need = L.ssd_fwd_workspace_bytes(ctypes.byref(p), 256, 0)
     assert fwd_status(L, p, ws_bytes=fwd_need) == WS

@@ -10,6 +10,8 @@ token-by-token oracle.  Gates:
             and a run without the D skip term (which dominates y) normwise <= 1e-2
             on the scan-only output.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -208,3 +210,37 @@ def test_full_size_sampled(cfg, heads):
     assert bf16_excess(ys, y_ref) <= 2e-2
     assert normwise(fs, f_ref) <= 1e-3
     assert torch.isfinite(y.float()).all()
+
+
+def _up256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kw,lengths,Q", STAGE_KW)
+def test_fused_cumsum_matches_stage(kw, lengths, Q):
+    """ssd_fwd forms delta, acs and the chunk decays inside the chunk-state kernel
+    (bf16 path): they must equal the stage-1 kernel's outputs bit for bit (the
+    saved context of a forward is what a recomputing backward would build).
+    Offsets follow the workspace layout: [chunk table, sequence offsets when
+    packed], delta, acs, decays, each piece 256-byte aligned."""
+    inp, o, mid, st, nk = stage_case(kw, lengths, Q)
+    d = to_dev(inp)
+    p = st.prob
+    ws = torch.empty(ssd.lib().ssd_bwd_workspace_bytes(ctypes.byref(p), Q, st.packed),
+                     dtype=torch.uint8, device="cuda")
+    gpu_fwd(ssd, inp, Q, workspace=ws, save_for_backward=True)
+    delta, acs, decay = st.chunk_cumsum(d["dt"], d["A"], d["dt_bias"])
+    torch.cuda.synchronize()
+    nck, H = delta.shape[0], p.nheads
+    off = _up256(nck * 16) + _up256((p.nseq + 1) * 4) if st.packed else 0
+    n_tok = nck * H * Q
+    w_delta = ws[off:off + 4 * n_tok].view(torch.float32).view(nck, H, Q)
+    off += _up256(4 * n_tok)
+    w_acs = ws[off:off + 4 * n_tok].view(torch.float32).view(nck, H, Q)
+    off += _up256(4 * n_tok)
+    w_decay = ws[off:off + 4 * nck * H].view(torch.float32).view(nck, H)
+    live = [k for k in range(nck) if k < nk]  # chunk slots past the last chunk are never written
+    assert torch.equal(w_delta[live], delta[live])
+    assert torch.equal(w_acs[live], acs[live])
+    assert torch.equal(w_decay[live], decay[live])
