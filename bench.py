@@ -73,7 +73,7 @@ def kernel_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, d_final=False):
         "dstates": x + bc + f32_tok + st32,
         "reverse_state_passing": st32 + decay + st16 + (s0 if d_final else 0) + s0,
         "bwd_dx": 3 * x + bc + tri + 2 * f32_tok + decay + 2 * st16 + 2 * f32_tok,
-        "bwd_dcb": 2 * x + tri + 2 * f32_tok + 2 * tri + 2 * f32_tok,
+        "bwd_dcb": 2 * x + tri + 2 * f32_tok + tri + 2 * f32_tok,
         "bwd_dc": 2 * bc + x + tri + f32_tok + st16 + bc + f32_tok,
         "bwd_db": x + bc + tri + 2 * f32_tok + st16 + bc,
         "bwd_finalize": dt + 6 * f32_tok + dt,

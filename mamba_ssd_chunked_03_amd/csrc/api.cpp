@@ -103,7 +103,7 @@ FwdLayout fwd_layout(const Prob& p) {
 }
 struct BwdLayout {
   FwdLayout f;
-  size_t CBt, dCBg, dCBgT, Rp, Kp, U, dE, ddd, Ks, rR, last, dDp, dAp, dbp, end;
+  size_t CBt, dCBg, Rp, Kp, U, dE, ddd, Ks, rR, last, dDp, dAp, dbp, end;
 };
 BwdLayout bwd_layout(const Prob& p) {
   BwdLayout l;
@@ -114,7 +114,6 @@ BwdLayout bwd_layout(const Prob& p) {
   const size_t tiles = p.io == SSD_BF16 ? nck * H * (size_t)(p.Q / 64) * p.Q * 4 : 0;
   l.CBt = o;  o += up(cb);
   l.dCBg = o; o += up(cb);
-  l.dCBgT = o; o += up(cb);
   l.Rp = o;   o += up(tiles);
   l.Kp = o;   o += up(tiles);
   l.U = o;    o += up(nck * H * st * 4);
@@ -334,7 +333,7 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.D = D;
   a.delta = delta; a.acs = acs; a.decay = decay; a.Hp = Hp; a.dE = dE;
   a.CB = CB; a.CBt = CBt;
-  a.dCBg = ws + l.dCBg; a.dCBgT = ws + l.dCBgT;
+  a.dCBg = ws + l.dCBg;
   a.Rp = (float*)(ws + l.Rp); a.Kp = (float*)(ws + l.Kp);
   a.dx = dx; a.dB = dB; a.dC = dC;
   a.ddt = ddt; a.dA = dA; a.dD = dD; a.d_dt_bias = d_dt_bias;

@@ -59,7 +59,7 @@ struct BwdArgs {
   const float *delta, *acs, *decay;
   const void *Hp, *dE;  // per (chunk, head) P x N: bf16 on the bf16 path, fp32 otherwise
   const void *CB, *CBt;
-  void *dCBg, *dCBgT;  // head-summed dCB per (chunk, group), both orientations
+  void* dCBg;          // head-summed dCB per (chunk, group), (Q, Q) row-major
   float *Rp, *Kp;      // per (chunk, head, 64-token tile, token): R and K partials
   void *dx, *dB, *dC;
   float *ddt, *dA, *dD, *d_dt_bias;

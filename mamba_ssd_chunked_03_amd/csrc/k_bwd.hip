@@ -21,8 +21,8 @@
 // Kernels (bf16 on MFMA; fp32 plain loops):
 //   bwd_dx   (chunk, head)            dx, direct d(delta), s_j, dD and
 //                                     alpha<dE,H> + sum s per chunk
-//   bwd_dcb  (chunk, group, 64x64 causal tile)  head-summed dCB_g in both
-//                                     orientations; per-head tile partials of R, K
+//   bwd_dcb  (chunk, group, 64x64 causal tile)  head-summed dCB_g; per-head
+//                                     tile partials of R, K
 //   bwd_dc   (chunk, group, 64 rows)  dC = dCB_g B + sum_h (state term); r_i
 //   bwd_db   (chunk, group, 64 rows)  dB = dCB_g^T C + sum_h (state term)
 //   finalize (chunk, head)        suffix sum of dAcs (DPP scan), d(delta)->ddt,
@@ -295,8 +295,8 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
 // ------------------------------------------------------------ bwd_dcb bf16 ----
 // One workgroup per (chunk, group, 64x64 causal tile (ti, tj), tj <= ti).  B and
 // C are shared by the group's heads, so the intra-chunk parts of dC and dB only
-// need the head-summed dCB_g = sum_h dCB^h: it is formed here once per tile and
-// written in both orientations, so dC and dB each become one GEMM per group.
+// need the head-summed dCB_g = sum_h dCB^h: it is formed here once per tile, so
+// dC and dB each become one GEMM per group (dB reads it down the columns).
 // For every head the tile's contributions to R_i (row sums over j < i) and K_j
 // (column sums over i > j) of M_ij = dCB_ij CB_ij come from the same values,
 // so they cancel exactly where the decay gradient subtracts them.
@@ -312,7 +312,7 @@ template <int P>
 __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ DY,
     const uint16_t* __restrict__ CB, const float* __restrict__ delta,
-    const float* __restrict__ acs, uint16_t* __restrict__ dCBg, uint16_t* __restrict__ dCBgT,
+    const float* __restrict__ acs, uint16_t* __restrict__ dCBg,
     float* __restrict__ Rp, float* __restrict__ Kp) {
   constexpr int LX = P + 8;          // x tile row stride (bf16)
   constexpr int LT = 64 + 8;         // output staging row stride
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
       __syncthreads();
     }
   }
-  // head-summed tile -> bf16, through LDS to 16-byte row stores in both orientations
+  // head-summed tile -> bf16, through LDS to 16-byte row stores
   uint16_t* stg = xt[0];  // every wave is past its last read of the x tiles (barrier above)
 #pragma unroll
   for (int b = 0; b < 4; ++b)
@@ -482,11 +482,6 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
   for (int e = tid; e < 64 * 8; e += 256) {
     const int row = e >> 3, c8 = e & 7;
     *(u32x4*)(dCBg + (kg * Q + ti * 64 + row) * Q + jt0 + c8 * 8) = *(const u32x4*)(stg + row * LT + c8 * 8);
-    u32x4 t;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      t[d] = (uint32_t)stg[(c8 * 8 + 2 * d) * LT + row] | ((uint32_t)stg[(c8 * 8 + 2 * d + 1) * LT + row] << 16);
-    *(u32x4*)(dCBgT + (kg * Q + jt0 + row) * Q + ti * 64 + c8 * 8) = t;
   }
 }
 
@@ -614,7 +609,9 @@ __global__ __launch_bounds__(256, 3) void bwd_dc_bf16_kernel(
 
 // ------------------------------------------------------------ bwd_db bf16 ----
 // One workgroup per (chunk, group, 64 rows j).  dB_j = sum_{i>=j} dCB_g[i][j] C_i
-// (fragments from the transposed dCB_g rows, C through LDS in 64-row pieces)
+// (per 64-row piece of i: the piece's C rows and its 64 x 64 tile of dCB_g
+// staged in LDS, the tile read with the transpose read, which hands each lane
+// dCB_g down a column j)
 // + sum_h w_j delta_j dT^T x_j (one K=headdim GEMM per head).  Per head, dT = dE_c
 // (bf16) is staged in a double-buffered LDS tile and the next head's dT, x
 // fragments and decay scalars are loaded into registers while this head is
@@ -623,12 +620,14 @@ __global__ __launch_bounds__(256, 3) void bwd_dc_bf16_kernel(
 template <int P, int N>
 __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
-    const uint16_t* __restrict__ dCBgT, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dCBg, const float* __restrict__ delta,
     const float* __restrict__ acs, const uint16_t* __restrict__ dE, uint16_t* __restrict__ dB) {
   constexpr int LDB = N + 16;
   constexpr int ROWS = P > 64 ? P : 64;
   constexpr int NPH = (P * N / 8 + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t ub[2][ROWS * LDB];
+  constexpr int LDT = 64 + 8;  // dCB_g tile row stride (bf16)
+  constexpr int UB = ROWS * LDB > 64 * LDT ? ROWS * LDB : 64 * LDT;
+  __shared__ __attribute__((aligned(16))) uint16_t ub[2][UB];
   const int T = m.Q / 64;
   const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
   const int tile = lid % T, k = lid / T / G, g = (lid / T) % G;
@@ -640,26 +639,29 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   const int hpg = H / G;
   const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
   const uint16_t* cb = Cm + (int64_t)ci.start * brow + (int64_t)g * N;
-  const uint16_t* dcbt = dCBgT + ((int64_t)k * G + g) * Q * Q;
+  const uint16_t* dcbg = dCBg + ((int64_t)k * G + g) * Q * Q;
   const int j0 = tile * 64 + w * 16;
   const bool active = j0 < len;
   const int jrow = j0 + r;
   const bool rowok = jrow < len;
-  // buffer resources over the chunk's valid rows (rows past the end: zero, not written)
-  const brsrc rdcbt = make_rsrc(dcbt, (uint32_t)(len * Q * 2));
   const uint32_t xo = (uint32_t)jrow * (uint32_t)(xrow * 2) + q * 16;
+
   f32x4 acc[N / 16];  // acc[nb][rr] = dB[jrow][pcol(nb, 4 q + rr)]
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint16_t* ct = ub[0];
+  uint16_t *ct = ub[0], *dt_ = ub[1];
   for (int it = tile; it * 64 < len; ++it) {
     __syncthreads();
+    // C rows of this piece and dCB_g[it-piece rows i][this tile's columns j]
+    // (rows past the chunk's end zero; the diagonal tile is zero above i = j)
     stage_rows<64, N, 256, true>(ct, LDB, cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
+    stage_rows<64, 64, 256>(dt_, LDT, dcbg + (int64_t)it * 64 * Q + tile * 64, Q, len - it * 64, tid);
     __syncthreads();
     if (!active) continue;
     const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
     for (int ib = ib0; ib < min(it * 64 + 64, len); ib += 32) {
-      const bf16x8 a = as_bf16x8(buf_load16(rdcbt, (uint32_t)jrow * (uint32_t)(Q * 2) + ib * 2 + q * 16));
+      // a[j][i] = dCB_g[i][j]: tile rows are k = i, the lane's column is j0 + r
+      const bf16x8 a = frag_kmajor(dt_ + (ib - it * 64) * LDT + w * 16, LDT, lane);
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
         acc[nb] = mfma_bf16(frag_kmajor(ct + (ib - it * 64) * LDB + nb * 16, LDB, lane), a, acc[nb]);
@@ -980,7 +982,7 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStrea
   hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
                      dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
                      (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
-                     (uint16_t*)a.dCBg, (uint16_t*)a.dCBgT, a.Rp, a.Kp);
+                     (uint16_t*)a.dCBg, a.Rp, a.Kp);
   if (!which || which == 3)
   hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
@@ -989,7 +991,7 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStrea
   if (!which || which == 4)
   hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
-                     (const uint16_t*)a.dCBgT, a.delta, a.acs, (const uint16_t*)a.dE, (uint16_t*)a.dB);
+                     (const uint16_t*)a.dCBg, a.delta, a.acs, (const uint16_t*)a.dE, (uint16_t*)a.dB);
 }
 
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
