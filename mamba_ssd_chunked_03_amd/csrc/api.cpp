@@ -340,18 +340,18 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   a.ddd = (float*)(ws + l.ddd); a.Ks = (float*)(ws + l.Ks); a.rR = (float*)(ws + l.rR);
   a.last_term = (float*)(ws + l.last); a.dDp = (float*)(ws + l.dDp);
   a.dAp = (float*)(ws + l.dAp); a.dbp = (float*)(ws + l.dbp);
-  // The head-summed dCB (with the R, K partials) and then dC need only forward
-  // quantities: on the bf16 path they run on a side stream beside the adjoint
-  // states, the reverse scan and dx; dB waits for dCB, the finalize for dC.
+  // The head-summed dCB (with the R, K partials), then dC, need only forward
+  // quantities, and dB needs dCB and the reverse scan's dE: on the bf16 path
+  // those three run on a side stream (dB after an event from the reverse scan)
+  // beside the adjoint states, the reverse scan and dx; the finalize waits for
+  // the side stream.  Each stream then carries about half of the work.
   std::unique_lock<std::mutex> lane_lock;
   SideLane* side = (!only && p.io == SSD_BF16 && p.nck > 0) ? side_lane(lane_lock) : nullptr;
-  if (side) {  // events: 0 fork, 1 dCB done, 2 dC done
+  if (side) {  // events: 0 fork, 1 reverse scan done, 2 side stream done
     SSD_TRY(hipEventRecord(side->ev[0], st));
     SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
     SSD_TRY(launch_bwd_chunk(p, a, 2, side->stream));
-    SSD_TRY(hipEventRecord(side->ev[1], side->stream));
     SSD_TRY(launch_bwd_chunk(p, a, 3, side->stream));
-    SSD_TRY(hipEventRecord(side->ev[2], side->stream));
   }
   // adjoint of the state carried into each chunk, then the reverse scan
   if (!only || only == 1)
@@ -359,9 +359,11 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   if (!only || only == 2)
     SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
   if (side) {
+    SSD_TRY(hipEventRecord(side->ev[1], st));
+    SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[1], 0));
+    SSD_TRY(launch_bwd_chunk(p, a, 4, side->stream));
+    SSD_TRY(hipEventRecord(side->ev[2], side->stream));
     SSD_TRY(launch_bwd_chunk(p, a, 1, st));
-    SSD_TRY(hipStreamWaitEvent(st, side->ev[1], 0));
-    SSD_TRY(launch_bwd_chunk(p, a, 4, st));
     SSD_TRY(hipStreamWaitEvent(st, side->ev[2], 0));
   } else if (!only || (only >= 3 && only <= 6)) {
     SSD_TRY(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
