@@ -885,10 +885,13 @@ __global__ __launch_bounds__(256) void bwd_db_f32_kernel(
 }
 
 // ---------------------------------------------------------------- finalize ----
-// One wavefront per (chunk, head): dAcs_i = rR_i - Ks_i + (R, K tile partials)
-// (+ last_term at the last token), ddA_t = sum_{i>=t} dAcs_i by a reversed DPP prefix sum in 64-token
-// blocks from the chunk's end, d(delta)_t = ddd_t + A ddA_t, ddt = d(delta)
-// sigmoid(z) when softplus is on; per-chunk partial sums of delta*ddA and ddt.
+// One workgroup per (chunk, head), one token per thread: dAcs_i = rR_i - Ks_i +
+// (R, K tile partials) (+ last_term at the last token); ddA_t = sum_{i>=t} dAcs_i,
+// d(delta)_t = ddd_t + A ddA_t, ddt = d(delta) sigmoid(z) when softplus is on;
+// per-chunk partial sums of delta*ddA and ddt.  Wave w holds the 64-token block
+// w from the chunk's end with its lanes reversed, so a DPP prefix sum over a
+// wave is a suffix sum over its tokens; the blocks' totals are added in order
+// from the chunk's end.  Every token's loads are issued at once.
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     ChunkMap m, int H, int softplus, const float* __restrict__ dt,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
@@ -896,49 +899,61 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     const float* __restrict__ ddd, const float* __restrict__ last_term,
     const float* __restrict__ Rp, const float* __restrict__ Kp, int ntile, float* __restrict__ ddt,
     float* __restrict__ dAp, float* __restrict__ dbp) {
-  const int k = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + w;
-  if (h >= H) return;
+  __shared__ float wtot[4], wpa[4], wpb[4];
+  const int k = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const ChunkInfo ci = chunk_info(m, k);
   const int64_t kh = (int64_t)k * H + h;
   if (ci.len <= 0) {
-    if (lane == 0) {
+    if (tid == 0) {
       dAp[kh] = 0.f;
       dbp[kh] = 0.f;
     }
     return;
   }
   const int Q = m.Q, len = ci.len;
+  const int t = Q - 64 * w - 1 - lane;  // negative for waves past a short chunk size
+  const bool in = t >= 0 && t < len;
   const float Ah = A[h], bias = dt_bias ? dt_bias[h] : 0.f;
-  const float lt = last_term[kh];
-  float carry = 0.f, pa = 0.f, pb = 0.f;
-  for (int t0 = Q - 64; t0 >= 0; t0 -= 64) {
-    const int t = t0 + 63 - lane;  // lane order reversed: prefix over lanes = suffix over t
-    float v = 0.f;
-    if (t < len) {
-      v = rR[kh * Q + t] - Ks[kh * Q + t] + (t == len - 1 ? lt : 0.f);
-      // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
-      for (int tl = 0; tl <= t / 64 && tl < ntile; ++tl) v += Rp[(kh * ntile + tl) * Q + t];
-      for (int tl = t / 64; tl <= (len - 1) / 64 && tl < ntile; ++tl) v -= Kp[(kh * ntile + tl) * Q + t];
-    }
-    const float incl = wave_inclusive_sum(v) + carry;
-    carry = wave_last(incl);
-    if (t < len) {
-      const float dl = delta[kh * Q + t];
-      const float dd = ddd[kh * Q + t] + Ah * incl;
-      const int64_t tok = ci.start + t;
-      const float g = softplus ? dd * sigmoid_f(dt[tok * H + h] + bias) : dd;
-      ddt[tok * H + h] = g;
-      pa += dl * incl;
-      pb += g;
-    }
+  float v = 0.f, dl = 0.f, d0 = 0.f, z = 0.f;
+  if (in) {
+    v = rR[kh * Q + t] - Ks[kh * Q + t] + (t == len - 1 ? last_term[kh] : 0.f);
+    // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
+    const int tt = t / 64, tlast = (len - 1) / 64;
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+      if (tl <= tt && tl < ntile) v += Rp[(kh * ntile + tl) * Q + t];
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+      if (tl >= tt && tl <= tlast && tl < ntile) v -= Kp[(kh * ntile + tl) * Q + t];
+    dl = delta[kh * Q + t];
+    d0 = ddd[kh * Q + t];
+    z = dt[(ci.start + t) * (int64_t)H + h] + bias;
+  }
+  const float sw = wave_inclusive_sum(v);
+  if (lane == 63) wtot[w] = sw;
+  __syncthreads();
+  float carry = 0.f;
+  for (int u = 0; u < w; ++u) carry = wtot[u] + carry;
+  const float incl = sw + carry;
+  float pa = 0.f, pb = 0.f;
+  if (in) {
+    const float dd = d0 + Ah * incl;
+    const float g = softplus ? dd * sigmoid_f(z) : dd;
+    ddt[(ci.start + t) * (int64_t)H + h] = g;
+    pa = dl * incl;
+    pb = g;
   }
   pa = wave_sum(pa);
   pb = wave_sum(pb);
   if (lane == 0) {
-    dAp[kh] = pa;
-    dbp[kh] = pb;
+    wpa[w] = pa;
+    wpb[w] = pb;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    dAp[kh] = ((wpa[0] + wpa[1]) + wpa[2]) + wpa[3];
+    dbp[kh] = ((wpb[0] + wpb[1]) + wpb[2]) + wpb[3];
   }
 }
 
@@ -1027,7 +1042,7 @@ hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStrea
 
 hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st) {
   if (p.nck > 0)
-    hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, (p.H + 3) / 4), dim3(256), 0, st,
+    hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, p.H), dim3(256), 0, st,
                        p.map, p.H, p.softplus, a.dt, a.dt_bias, a.A, a.delta, a.rR, a.Ks, a.ddd,
                        a.last_term, a.Rp, a.Kp, p.io == 0 ? 0 : p.Q / 64, a.ddt, a.dAp, a.dbp);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((p.H + 3) / 4), dim3(256), 0, st, (int)p.nck, p.H,
