@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum {
   SSD_OK = 0,
@@ -209,6 +209,45 @@ ssd_status ssd_stage_chunk_scan(const ssd_problem* problem, const void* x, const
                                 const float* passed, const float* D,
                                 const int32_t* cu_seqlens, int32_t chunk_size, void* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gated RMSNorm of the Mamba-2 layer, the normalisation applied to the SSD
+ * output y with the gate z (aitrends.kr/articles/109906, "B200에 맞춘 Helion
+ * Mamba-2 커널 최적화": the layer's _layer_norm_bwd kernel; the page prints no
+ * formula, the Mamba-2 gated RMSNorm normalised after gating is used).  Per row of
+ * `dim` columns, in groups of `group` consecutive columns:
+ *     s = z * sigmoid(z) (1 when z is NULL), v = y * s,
+ *     r = 1 / sqrt(mean over the group of v^2 + eps),  out = v * r * weight.
+ * Layouts: y, z, out, dout, dy, dz (rows, dim) io dtype, dim fastest; weight and
+ * dweight (dim) fp32; rstd (rows, dim / group) fp32.  The SSD output (batch,
+ * seqlen, nheads, headdim) is such a matrix with rows = batch * seqlen and
+ * dim = nheads * headdim.
+ * Supported: io_dtype SSD_BF16; dim a multiple of 512, at most 8192; group in
+ * {256, 512, 1024, 2048} dividing dim, or group == dim; eps >= 0 and finite;
+ * 16-byte aligned pointers.  Anything else returns SSD_ERR_UNSUPPORTED (or
+ * SSD_ERR_SHAPE / SSD_ERR_NULL / SSD_ERR_ALIGN) before anything is queued.
+ * Every reduction has a fixed order: results are bitwise reproducible.
+ */
+typedef struct {
+  int32_t rows;      /* tokens */
+  int32_t dim;       /* columns per row */
+  int32_t group;     /* columns per normalisation group */
+  int32_t io_dtype;  /* ssd_dtype of y, z, out, dout, dy, dz (SSD_BF16) */
+  float eps;
+} ssd_norm_problem;
+
+/* Workspace of ssd_gated_rmsnorm_bwd in bytes: per-workgroup partial sums of
+ * dweight, min(rows, 1024) x dim fp32 (0 for an invalid problem). */
+size_t ssd_gated_rmsnorm_bwd_workspace_bytes(const ssd_norm_problem* problem);
+/* Forward: out, and rstd (may be NULL) = r per (row, group).  z may be NULL (no gate). */
+ssd_status ssd_gated_rmsnorm_fwd(const ssd_norm_problem* problem, const void* y, const void* z,
+                                 const float* weight, void* out, float* rstd, void* stream);
+/* Backward for the loss <dout, out>: dy, dz (NULL iff z is NULL) and dweight
+ * (summed over rows).  r is recomputed from y and z. */
+ssd_status ssd_gated_rmsnorm_bwd(const ssd_norm_problem* problem, const void* dout, const void* y,
+                                 const void* z, const float* weight, void* dy, void* dz,
+                                 float* dweight, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* Plain device-to-device copy kernel of `bytes` bytes (16-byte multiple), used to
  * calibrate hardware traffic counters against a kernel of known traffic. */

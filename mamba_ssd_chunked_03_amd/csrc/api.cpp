@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -461,6 +462,59 @@ ssd_status ssd_stage_chunk_scan(const ssd_problem* pr, const void* x, const void
   s = setup_map(p, cu_seqlens, (char*)workspace, st);
   if (s != SSD_OK) return s;
   SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, passed, 0, D, out, st));
+  return SSD_OK;
+}
+
+}  // extern "C"
+
+namespace {
+ssd_status norm_check(const ssd_norm_problem* pr) {
+  if (!pr) return SSD_ERR_NULL;
+  if (pr->rows < 0 || pr->dim <= 0 || pr->group <= 0) return SSD_ERR_SHAPE;
+  if (pr->io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+  if (pr->dim % 512 || pr->dim > 8192) return SSD_ERR_UNSUPPORTED;
+  const int g = pr->group;
+  if (g != pr->dim && !((g == 256 || g == 512 || g == 1024 || g == 2048) && pr->dim % g == 0))
+    return SSD_ERR_UNSUPPORTED;
+  if (!(pr->eps >= 0.f) || !std::isfinite(pr->eps)) return SSD_ERR_UNSUPPORTED;
+  if ((int64_t)pr->rows * pr->dim > INT32_MAX / 2) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t ssd_gated_rmsnorm_bwd_workspace_bytes(const ssd_norm_problem* pr) {
+  if (norm_check(pr) != SSD_OK) return 0;
+  return (size_t)norm_bwd_blocks(pr->rows) * pr->dim * 4;
+}
+
+ssd_status ssd_gated_rmsnorm_fwd(const ssd_norm_problem* pr, const void* y, const void* z,
+                                 const float* weight, void* out, float* rstd, void* stream) {
+  ssd_status s = norm_check(pr);
+  if (s != SSD_OK) return s;
+  if (pr->rows > 0 && (!y || !weight || !out)) return SSD_ERR_NULL;
+  if (!all_aligned({y, z, weight, out, rstd})) return SSD_ERR_ALIGN;
+  if (pr->rows == 0) return SSD_OK;
+  SSD_TRY(launch_gated_rmsnorm(pr->rows, pr->dim, pr->group, pr->eps, y, z, weight, out, rstd, nullptr,
+                               nullptr, nullptr, nullptr, nullptr, false, (hipStream_t)stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_gated_rmsnorm_bwd(const ssd_norm_problem* pr, const void* dout, const void* y,
+                                 const void* z, const float* weight, void* dy, void* dz,
+                                 float* dweight, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  ssd_status s = norm_check(pr);
+  if (s != SSD_OK) return s;
+  if (!weight || !dweight) return SSD_ERR_NULL;
+  if (pr->rows > 0 && (!dout || !y || !dy)) return SSD_ERR_NULL;
+  if ((z == nullptr) != (dz == nullptr)) return SSD_ERR_NULL;
+  if (!all_aligned({dout, y, z, weight, dy, dz, dweight, workspace})) return SSD_ERR_ALIGN;
+  const size_t need = ssd_gated_rmsnorm_bwd_workspace_bytes(pr);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_WORKSPACE;
+  SSD_TRY(launch_gated_rmsnorm(pr->rows, pr->dim, pr->group, pr->eps, y, z, weight, nullptr, nullptr,
+                               dout, dy, dz, (float*)workspace, dweight, true, (hipStream_t)stream));
   return SSD_OK;
 }
 

@@ -51,6 +51,12 @@ hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const 
                              const float* delta, const float* acs, const void* passed,
                              int passed_bf16, const float* D, void* out, hipStream_t st);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+// Gated RMSNorm (validated shapes): forward (out, r) or backward (dy, dz, dw via
+// the per-workgroup partials dwp of norm_bwd_blocks(rows) x D floats).
+int norm_bwd_blocks(int rows);
+hipError_t launch_gated_rmsnorm(int rows, int D, int group, float eps, const void* y, const void* z,
+                                const float* w, void* out, float* r, const void* dout, void* dy, void* dz,
+                                float* dwp, float* dw, bool bwd, hipStream_t st);
 
 // Everything the backward chunk kernels read and write.
 struct BwdArgs {

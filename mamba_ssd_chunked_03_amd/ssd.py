@@ -23,6 +23,11 @@ class Problem(ctypes.Structure):
                 ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "nseq",
                  "io_dtype", "dt_softplus", "flags")]
 
+class NormProblem(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("dim", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
 FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED = 1, 2
 BWD_KERNELS = ("dstates", "reverse_state_passing", "bwd_dx", "bwd_dcb", "bwd_dc", "bwd_db",
                "bwd_finalize")
@@ -57,6 +62,9 @@ _SIGS = {
     "ssd_stage_bmm_chunk": ([_P, _P, _P, _P, _I32, _P, _P, _SZ, _P], _I32),
     "ssd_stage_chunk_scan": ([_P] + [_P] * 8 + [_I32, _P, _P, _SZ, _P], _I32),
     "ssd_util_copy": ([_P, _P, _SZ, _P], _I32),
+    "ssd_gated_rmsnorm_bwd_workspace_bytes": ([_P], _SZ),
+    "ssd_gated_rmsnorm_fwd": ([_P] + [_P] * 5 + [_P], _I32),
+    "ssd_gated_rmsnorm_bwd": ([_P] + [_P] * 8 + [_SZ, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -299,3 +307,56 @@ class Stages:
 def util_copy(dst, src):
     dev = _dev(dst, src)
     _check(lib().ssd_util_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(dev)))
+
+
+def norm_problem(y, group, eps):
+    """y: (..., dim) bf16; rows = the product of the leading sizes."""
+    if y.dtype != torch.bfloat16:
+        raise ValueError("the gated RMSNorm takes bfloat16 y, z")
+    dim = y.shape[-1]
+    return NormProblem(y.numel() // dim if dim else 0, dim, int(group), BF16, float(eps))
+
+
+def gated_rmsnorm_fwd(y, z, weight, group, eps=1e-5, out=None, rstd=None, prepare=False):
+    """out = RMSNorm(y * silu(z)) * weight over groups of `group` columns of the
+    last dimension (z may be None: no gate).  rstd: optional (rows, dim // group)
+    float32 output.  Returns out (or (launch, out) when prepare is set)."""
+    dev = _dev(y, z, weight, out, rstd)
+    _f32(weight, "weight")
+    if z is not None and (z.shape != y.shape or z.dtype != y.dtype):
+        raise ValueError("z must match y")
+    p = norm_problem(y, group, eps)
+    out = torch.empty_like(y) if out is None else out
+    args = (ctypes.byref(p), _ptr(y), _ptr(z), _ptr(weight), _ptr(out), _ptr(rstd), _stream(dev))
+
+    def launch():
+        _check(lib().ssd_gated_rmsnorm_fwd(*args), keep=p)
+
+    if prepare:
+        return launch, out
+    launch()
+    return out
+
+
+def gated_rmsnorm_bwd(dout, y, z, weight, group, eps=1e-5, workspace=None, grads=None, prepare=False):
+    """Gradients (dy, dz, dweight) of <dout, gated_rmsnorm_fwd(y, z, weight)>;
+    dz is None without a gate.  Returns them (or (launch, grads) with prepare)."""
+    dev = _dev(dout, y, z, weight)
+    _f32(weight, "weight")
+    p = norm_problem(y, group, eps)
+    if grads is None:
+        grads = (torch.empty_like(y), None if z is None else torch.empty_like(z),
+                 torch.empty_like(weight))
+    dy, dz, dw = grads
+    need = lib().ssd_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None else _ws(need, dev)
+    args = (ctypes.byref(p), _ptr(dout), _ptr(y), _ptr(z), _ptr(weight), _ptr(dy), _ptr(dz), _ptr(dw),
+            _ptr(ws), ws.numel(), _stream(dev))
+
+    def launch():
+        _check(lib().ssd_gated_rmsnorm_bwd(*args), keep=(p, ws))
+
+    if prepare:
+        return launch, grads
+    launch()
+    return grads

@@ -39,7 +39,7 @@ def test_header_and_binding_agree(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.ssd_abi_version() == 2
+    assert L.ssd_abi_version() == 3
     for s in range(8):
         assert len(L.ssd_status_string(s)) > 0
     assert L.ssd_status_string(99) == b"unknown status"
@@ -183,3 +183,49 @@ def test_stage_validation(L):
     assert L.ssd_stage_bmm_chunk(pp, FAKE + 4, FAKE, None, 256, FAKE, None, 0, None) == ALIGN
     assert L.ssd_util_copy(FAKE, FAKE, 17, None) == ALIGN
     assert L.ssd_util_copy(None, FAKE, 16, None) == NULL
+
+
+def nprob(**kw):
+    d = dict(rows=100, dim=4096, group=512, io_dtype=1, eps=1e-5)
+    d.update(kw)
+    return ssd.NormProblem(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(group=4096), OK), (dict(group=256, dim=512), OK), (dict(dim=8192, group=2048), OK),
+    (dict(rows=-1), SHAPE), (dict(dim=0), SHAPE), (dict(group=0), SHAPE),
+    (dict(io_dtype=0), UNSUP), (dict(dim=4000), UNSUP), (dict(dim=8704), UNSUP),
+    (dict(group=128), UNSUP), (dict(group=768), UNSUP), (dict(dim=1536, group=1024), UNSUP),
+    (dict(eps=-1.0), UNSUP), (dict(eps=float("inf")), UNSUP), (dict(eps=float("nan")), UNSUP),
+])
+def test_norm_validation(L, kw, code):
+    p = nprob(**kw)
+    # a misaligned output is only reported once the problem has passed validation,
+    # and nothing is launched either way
+    st = L.ssd_gated_rmsnorm_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE + 8, None, None)
+    need = L.ssd_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(p))
+    if code == OK:
+        assert st == ALIGN
+        # and the backward's: make only its workspace wrong
+        assert need == min(p.rows, 1024) * p.dim * 4
+        assert L.ssd_gated_rmsnorm_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, need - 1, None) == WS
+    else:
+        assert st == code and need == 0
+
+
+def test_norm_pointers(L):
+    p = nprob()
+    assert L.ssd_gated_rmsnorm_fwd(ctypes.byref(p), None, None, FAKE, FAKE, None, None) == NULL
+    assert L.ssd_gated_rmsnorm_fwd(ctypes.byref(p), FAKE, None, FAKE, FAKE + 8, None, None) == ALIGN
+    need = L.ssd_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(p))
+    # dz must be given exactly when z is
+    assert L.ssd_gated_rmsnorm_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   FAKE, need, None) == NULL
+    assert L.ssd_gated_rmsnorm_bwd(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, need, None) == NULL
+    assert L.ssd_gated_rmsnorm_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   FAKE, need, None) == NULL
+    # no rows: nothing to do, no data pointers needed
+    p0 = nprob(rows=0)
+    assert L.ssd_gated_rmsnorm_fwd(ctypes.byref(p0), None, None, FAKE, None, None, None) == OK
