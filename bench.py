@@ -367,6 +367,38 @@ def main():
         kernels["_backward_aggregate"] = aggregate(list(ssd.BWD_KERNELS))
         kernels["_all"] = aggregate(names)
 
+    # the layer's gated RMSNorm on the SSD output (rows = batch x seqlen, dim =
+    # heads x headdim, 8 groups of dim / 8 columns), gate and upstream gradient seeded
+    norm = None
+    if not args.no_kernels:
+        rows, dim = Bsz * L, H * P
+        group = dim // G
+        gen = torch.Generator(device=dev).manual_seed(7)
+        yn = y.view(rows, dim)
+        zn = torch.randn(rows, dim, generator=gen, device=dev).to(torch.bfloat16)
+        wn = torch.rand(dim, generator=gen, device=dev) + 0.5
+        dn = torch.randn(rows, dim, generator=gen, device=dev).to(torch.bfloat16)
+        rstd = torch.empty(rows, dim // group, device=dev)
+        nfwd, _ = ssd.gated_rmsnorm_fwd(yn, zn, wn, group, 1e-5, rstd=rstd, prepare=True)
+        nbwd, _ = ssd.gated_rmsnorm_bwd(dn, yn, zn, wn, group, 1e-5, prepare=True)
+        mat = rows * dim * 2
+        nb = {"fwd": 3 * mat + dim * 4 + rows * (dim // group) * 4,   # y, z, w -> out, rstd
+              "bwd": 5 * mat + 2 * dim * 4}                            # dout, y, z, w -> dy, dz, dw
+        norm = {"workload": "gated RMSNorm of the SSD output: %d rows x %d columns, groups of %d, "
+                            "bf16" % (rows, dim, group)}
+        for name, fn in (("fwd", nfwd), ("bwd", nbwd)):
+            ms, ms_min, ms_max = trials(fn, max(1, args.steps // 2))
+            ms_cold = cold(fn)
+            gbs = nb[name] / (ms * 1e-3) / 1e9
+            norm[name] = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_max": round(ms_max, 4),
+                          "ms_cold": round(ms_cold, 4), "alg_bytes": nb[name], "GB/s": round(gbs, 1),
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                          "frac_hbm_cold": round(nb[name] / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            print("bench: gated_rmsnorm %s %.4f ms (cold %.4f)  %.0f GB/s" % (name, ms, ms_cold, gbs),
+                  file=sys.stderr, flush=True)
+        norm["page_context"] = ("the pages' _layer_norm_bwd: 0.09 ms on one B200, bf16, batch 2, "
+                                "seqlen 8192 (layer dimensions not printed); another machine's number")
+
     cpu = cpu_par = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -406,6 +438,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "cpu_baseline_parallel": cpu_par,
+        "gated_rmsnorm": norm,
     }
     print(json.dumps(out))
 

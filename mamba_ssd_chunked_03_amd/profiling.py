@@ -12,7 +12,8 @@ Two inputs, both written by rocprofv3 with ``-f csv``:
   whether the numbers still describe the code.
 
 Kernels are named as bench.py names them; one "launch" of bwd_finalize is its
-two kernels (the per-chunk pass and the per-head reduction).
+two kernels (the per-chunk pass and the per-head reduction), and one of
+gated_rmsnorm_bwd its two (the rows and the dweight reduction).
 
     python -m mamba_ssd_chunked_03_amd.profiling stats TRACE.csv OUT.md --command "..."
     python -m mamba_ssd_chunked_03_amd.profiling traffic --fetch F.csv --write W.csv \\
@@ -40,6 +41,7 @@ KERNEL_FILES = {
     "reverse_state_passing": "k_state_passing.hip", "bwd_dx": "k_bwd.hip", "bwd_dcb": "k_bwd.hip",
     "bwd_dc": "k_bwd.hip", "bwd_db": "k_bwd.hip", "bwd_finalize": "k_bwd.hip",
     "bmm_chunk_cb_only": "k_bmm.hip",  # C.B^T without its transpose (a forward that keeps nothing)
+    "gated_rmsnorm_fwd": "k_norm.hip", "gated_rmsnorm_bwd": "k_norm.hip",  # the layer's norm
 }
 
 
@@ -69,7 +71,9 @@ def kernel_key(name):
     for prefix, key in (("chunk_cumsum", "chunk_cumsum"), ("bmm_chunk", "bmm_chunk"),
                         ("chunk_scan", "chunk_scan"), ("bwd_dx_", "bwd_dx"), ("bwd_dcb_", "bwd_dcb"),
                         ("bwd_dc_", "bwd_dc"), ("bwd_db_", "bwd_db"), ("bwd_finalize", "bwd_finalize"),
-                        ("bwd_reduce", "bwd_finalize"), ("copy_kernel", "copy")):
+                        ("bwd_reduce", "bwd_finalize"), ("gated_rmsnorm_fwd", "gated_rmsnorm_fwd"),
+                        ("gated_rmsnorm_bwd", "gated_rmsnorm_bwd"), ("norm_dw_reduce", "gated_rmsnorm_bwd"),
+                        ("copy_kernel", "copy")):
         if base.startswith(prefix):
             return key
     return None

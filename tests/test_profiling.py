@@ -27,6 +27,9 @@ def test_kernel_keys():
     assert k("void ssd::bwd_reduce_kernel(int)") == "bwd_finalize"
     assert k("void ssd::bmm_chunk_bf16_kernel<128, true>(x)") == "bmm_chunk"
     assert k("void ssd::bmm_chunk_bf16_kernel<128, false>(x)") == "bmm_chunk_cb_only"
+    assert k("void ssd::gated_rmsnorm_bwd_kernel<true>(x)") == "gated_rmsnorm_bwd"
+    assert k("void ssd::norm_dw_reduce_kernel(int)") == "gated_rmsnorm_bwd"
+    assert k("void ssd::gated_rmsnorm_fwd_kernel<false>(x)") == "gated_rmsnorm_fwd"
     assert k("void at::native::elementwise_kernel<4>(x)") is None
 
 
