@@ -68,7 +68,8 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   } else {
     p.nck = (int64_t)p.B * ((p.L + Q - 1) / Q);
   }
-  if (p.nck > INT32_MAX / 4) return SSD_ERR_UNSUPPORTED;
+  // 1-D grids over (chunk, head) and (chunk, group, tile) slots stay below 2^31 workgroups
+  if (p.nck > INT32_MAX / 4 || p.nck * (int64_t)p.H > INT32_MAX / 16) return SSD_ERR_UNSUPPORTED;
   std::memset(&p.map, 0, sizeof(p.map));
   p.map.Q = Q;
   p.map.nck = (int32_t)p.nck;

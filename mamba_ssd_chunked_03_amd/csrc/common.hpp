@@ -347,6 +347,16 @@ __device__ __forceinline__ int xcd_order(int L, int W) {
   return x * per + min(x, rem) + s;
 }
 
+// (chunk slot, head) of a workgroup of a 1-D grid over nck x H slots: in the
+// XCD-aware order above, head fastest.  Each XCD then works through all heads
+// of one chunk together: a token's row of x (every head) is read whole, and a
+// group's B and C.B^T tiles stay in that XCD's L2 for the group's heads.
+__device__ __forceinline__ void chunk_head(int H, int& k, int& h) {
+  const int l = xcd_order(blockIdx.x, gridDim.x);
+  k = l / H;
+  h = l % H;
+}
+
 // ------------------------------------------------------------ chunk map ----
 // A chunk slot k covers tokens [start, start + len) of the flattened
 // (batch * seqlen) token axis, inside sequence `seq`.  Batched rows: row b is

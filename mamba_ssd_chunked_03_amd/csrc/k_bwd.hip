@@ -55,7 +55,8 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   __shared__ float red[3][kDxWaves];
   __shared__ __attribute__((aligned(16))) float wt[QMAX / 32][QMAX];  // column factors per anchor
 
-  const int k = blockIdx.x, h = blockIdx.y;
+  int k, h;
+  chunk_head(H, k, h);
   const ChunkInfo ci = chunk_info(m, k);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t kh = (int64_t)k * H + h;
@@ -989,7 +990,7 @@ template <int P, int N>
 static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
   const int T = p.Q / 64;
   if (!which || which == 1)
-  hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)p.nck, p.H), dim3(kDxWaves * 64), 0, st, p.map,
+  hipLaunchKernelGGL((bwd_dx_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.H)), dim3(kDxWaves * 64), 0, st, p.map,
                      p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B, (const uint16_t*)a.dout,
                      (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, (const uint16_t*)a.dE, (const uint16_t*)a.Hp, a.D,
                      (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);

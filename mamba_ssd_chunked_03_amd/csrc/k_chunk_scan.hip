@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
   __shared__ float sa[QMAX], sd[QMAX];
   __shared__ __attribute__((aligned(16))) float vt[QMAX / 32][QMAX];  // column factors per anchor
 
-  const int k = blockIdx.x, h = blockIdx.y;
+  int k, h;
+  chunk_head(H, k, h);
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
   const int Q = m.Q, len = ci.len;
@@ -244,7 +245,7 @@ template <int P, int N>
 static void launch_scan_bf16(const Prob& p, const void* x, const void* C, const void* CB,
                              const float* delta, const float* acs, const void* passed,
                              int passed_bf16, const float* D, void* out, hipStream_t st) {
-  const dim3 grid((unsigned)p.nck, p.H), block(kScanWaves * 64);
+  const dim3 grid((unsigned)(p.nck * p.H)), block(kScanWaves * 64);  // XCD-aware (chunk, head)
   if (passed_bf16)
     hipLaunchKernelGGL((chunk_scan_bf16_kernel<P, N, uint16_t>), grid, block, 0, st, p.map, p.H,
                        p.G, (const uint16_t*)x, (const uint16_t*)C, (const uint16_t*)CB, delta, acs,

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, in
   __shared__ __attribute__((aligned(16))) uint16_t ys[KS * LDY];
   __shared__ float sc[256];
 
-  const int k = blockIdx.x, h = blockIdx.y;
+  int k, h;
+  chunk_head(H, k, h);
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
   const int Q = m.Q, len = ci.len;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H,
 template <int P, int N>
 static void launch_cs_bf16(const Prob& p, const void* X, const void* Y, float* delta, float* acs,
                            float* out, int mode, const CumsumIn& cs, hipStream_t st) {
-  const dim3 grid((unsigned)p.nck, p.H);
+  const dim3 grid((unsigned)(p.nck * p.H));  // (chunk, head) in the XCD-aware order
   const uint16_t *x = (const uint16_t*)X, *y = (const uint16_t*)Y;
   if (mode == kStateFwd)
     hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwd>), grid, dim3(256), 0, st, p.map, p.H,
