@@ -90,3 +90,14 @@ def test_norm_full_size_sampled():
         o_dw += norm.bwd(f64(dout[r0:r0 + 2048]), f64(y[r0:r0 + 2048]), f64(z[r0:r0 + 2048]), f64(w),
                          group, eps)[2]
     assert normwise(f64(dw), o_dw) <= 1e-4
+
+
+def test_norm_no_rows():
+    """No rows: the forward queues nothing; the backward still writes dweight = 0."""
+    y = torch.empty(0, 1024, dtype=torch.bfloat16, device="cuda")
+    w = torch.rand(1024, device="cuda") + 0.5
+    out = ssd.gated_rmsnorm_fwd(y, y, w, 512)
+    dw = torch.full((1024,), 7.0, device="cuda")
+    dy, dz, dw = ssd.gated_rmsnorm_bwd(y, y, y, w, 512, grads=(torch.empty_like(y), torch.empty_like(y), dw))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 1024) and torch.count_nonzero(dw).item() == 0
