@@ -100,13 +100,17 @@ __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, in
       yr[c] = (j < len) ? *(const u32x4*)(yb + (int64_t)j * yrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // kStateFwdCumsum: this thread's token (256 threads, chunks of at most 256
+  // tokens; wave w holds the cumsum's pass w).  Its dt is loaded before the
+  // first slice, so that waiting for it does not also wait for the slice (the
+  // memory counter completes in order).
+  const int t = tid;
+  const bool in = t < len;
+  float dtv = 0.f;
+  if constexpr (MODE == kStateFwdCumsum) dtv = in ? cs.dt[(int64_t)(ci.start + t) * H + h] : 0.f;
   load_slice(0);  // independent of the token scales: in flight while they are formed
   if constexpr (MODE == kStateFwdCumsum) {
     __shared__ float wtot[4], alast;
-    const int t = tid;  // this thread's token (256 threads, chunks of at most 256 tokens); wave w
-                        // holds the cumsum's pass w
-    const bool in = t < len;
-    const float dtv = in ? cs.dt[(int64_t)(ci.start + t) * H + h] : 0.f;
     const float bias = cs.dt_bias ? cs.dt_bias[h] : 0.f;
     const float a2 = cs.A[h] * kLog2e;
     const float d = token_delta(dtv, bias, cs.softplus, in);
