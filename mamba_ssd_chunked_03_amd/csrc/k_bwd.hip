@@ -533,15 +533,29 @@ __global__ __launch_bounds__(256, 3) void bwd_dc_bf16_kernel(
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* bt = ub[0];
   for (int jt = 0; jt <= tile; ++jt) {
-    __syncthreads();
-    stage_rows<64, N, 256, true>(bt, LDB, bb + (int64_t)jt * 64 * brow, brow, len - jt * 64, tid);
+    // this piece's B rows and this lane's two dCB_g fragments, all in flight
+    // together (one memory latency per piece); fragments past the row block's
+    // causal end are not needed
+    RowTile<64, N, 256, true> btile;
+    btile.load(bb + (int64_t)jt * 64 * brow, brow, len - jt * 64, tid);
+    const int jend = min(jt * 64 + 64, i0 + 16);
+    u32x4 af[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int jb = jt * 64 + 32 * u;
+      af[u] = (active && jb < jend) ? buf_load16(rdcb, (uint32_t)irow * (uint32_t)(Q * 2) + jb * 2 + q * 16)
+                                    : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();  // every wave is done with the previous piece
+    btile.store(bt, LDB, tid);
     __syncthreads();
     if (!active) continue;
-    for (int jb = jt * 64; jb < min(jt * 64 + 64, i0 + 16); jb += 32) {
-      const bf16x8 a = as_bf16x8(buf_load16(rdcb, (uint32_t)irow * (uint32_t)(Q * 2) + jb * 2 + q * 16));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (jt * 64 + 32 * u >= jend) break;
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
-        acc[nb] = mfma_bf16(frag_kmajor(bt + (jb - jt * 64) * LDB + nb * 16, LDB, lane), a, acc[nb]);
+        acc[nb] = mfma_bf16(frag_kmajor(bt + 32 * u * LDB + nb * 16, LDB, lane), as_bf16x8(af[u]), acc[nb]);
     }
   }
   // C_i values of this lane's outputs, 8 adjacent per tile pair
@@ -652,11 +666,16 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t *ct = ub[0], *dt_ = ub[1];
   for (int it = tile; it * 64 < len; ++it) {
-    __syncthreads();
     // C rows of this piece and dCB_g[it-piece rows i][this tile's columns j]
-    // (rows past the chunk's end zero; the diagonal tile is zero above i = j)
-    stage_rows<64, N, 256, true>(ct, LDB, cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
-    stage_rows<64, 64, 256>(dt_, LDT, dcbg + (int64_t)it * 64 * Q + tile * 64, Q, len - it * 64, tid);
+    // (rows past the chunk's end zero; the diagonal tile is zero above i = j),
+    // both in flight together: one memory latency per piece
+    RowTile<64, N, 256, true> ctile;
+    RowTile<64, 64, 256> dtile;
+    ctile.load(cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
+    dtile.load(dcbg + (int64_t)it * 64 * Q + tile * 64, Q, len - it * 64, tid);
+    __syncthreads();  // every wave is done with the previous piece
+    ctile.store(ct, LDB, tid);
+    dtile.store(dt_, LDT, tid);
     __syncthreads();
     if (!active) continue;
     const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
