@@ -18,6 +18,17 @@ gated_rmsnorm_bwd its two (the rows and the dweight reduction).
     python -m mamba_ssd_chunked_03_amd.profiling stats TRACE.csv OUT.md --command "..."
     python -m mamba_ssd_chunked_03_amd.profiling traffic --fetch F.csv --write W.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes 268435456 --out profiles/traffic.json
+
+A third summary, ``mlp``, reads one counter run with the MLP_COUNTERS below
+(one pass: 4 SQ, 2 TCP, 2 TA and 1 GRBM counters) and reports, per kernel, how
+the vector memory path was used: L1-to-L2 read requests per launch, their mean
+latency, the mean number in flight per compute unit (Little's law: total
+latency cycles over elapsed cycles), and how often the texture address unit
+was busy or held up by the L1.  Per compute unit a kernel can read at most
+(requests in flight x 128 bytes / latency), which is what bounds the staged
+kernels below the HBM peak.
+
+    python -m mamba_ssd_chunked_03_amd.profiling mlp --pmc DIR --md OUT.md --command "..."
 """
 import argparse
 import collections
@@ -181,6 +192,85 @@ def counter_means(counter_csv, counter):
             for k, d in per.items()}
 
 
+MLP_COUNTERS = ("TCP_TCC_READ_REQ_sum", "TCP_TCC_READ_REQ_LATENCY_sum", "TA_TA_BUSY_sum",
+                "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_BUSY_CYCLES",
+                "GRBM_GUI_ACTIVE")
+LINE_BYTES = 128  # one L1-to-L2 read request
+
+
+def agent_counts(agent_csv):
+    """(compute units, XCDs) of the GPU agent in a rocprofv3 agent-info CSV."""
+    for row in _rows(agent_csv):
+        if "gfx" in row.get("Name", ""):
+            return int(row["Cu_Count"]), int(row.get("Num_Xcc") or 1)
+    raise ValueError("no GPU agent in %s" % agent_csv)
+
+
+def mlp(counter_csv, cus, xcds):
+    """{key: figures} from one counter run holding MLP_COUNTERS.
+
+    Per kernel name: the mean of each counter and of the dispatch duration over
+    its launches; a key with several kernels sums them.  Elapsed cycles per
+    compute unit = GRBM_GUI_ACTIVE / XCDs (the counter sums the XCDs' clocks)."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(dict)
+    for row in _rows(counter_csv):
+        name = _col(row, "Kernel_Name")
+        key = kernel_key(name)
+        if key is None or key == "copy":
+            continue
+        vals[(key, name)][_col(row, "Counter_Name")].append(float(_col(row, "Counter_Value")))
+        durs[(key, name)][_col(row, "Dispatch_Id")] = (int(_col(row, "End_Timestamp"))
+                                                       - int(_col(row, "Start_Timestamp")))
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    for (key, name), d in vals.items():
+        for c, v in d.items():
+            tot[key][c] += _mean(v)
+        tot[key]["_ns"] += _mean(list(durs[(key, name)].values()))
+        tot[key]["_launches"] = len(durs[(key, name)])
+    out = {}
+    for key, t in tot.items():
+        if any(c not in t for c in MLP_COUNTERS):
+            continue
+        cyc = t["GRBM_GUI_ACTIVE"] / xcds
+        req = t["TCP_TCC_READ_REQ_sum"]
+        out[key] = {
+            "launches": int(t["_launches"]), "us": t["_ns"] / 1e3, "clock_ghz": cyc / t["_ns"],
+            "read_requests": req, "requested_mb": req * LINE_BYTES / 1e6,
+            "latency_cycles": t["TCP_TCC_READ_REQ_LATENCY_sum"] / req if req else float("nan"),
+            "in_flight_per_cu": t["TCP_TCC_READ_REQ_LATENCY_sum"] / (cus * cyc),
+            "ta_busy": t["TA_TA_BUSY_sum"] / (cus * cyc),
+            "ta_stalled_by_l1": t["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (cus * cyc),
+            "wave_wait_frac": t["SQ_WAIT_ANY"] / t["SQ_WAVE_CYCLES"],
+            "source_sha": source_hash(key) if key in KERNEL_FILES else ""}
+    return out
+
+
+def mlp_md(res, title, commands, summary_cmd, cus, xcds):
+    lines = (["# " + title, ""] if title else []) + [
+        "Counter run (from the repository root, one MI355X, one rocprofv3 pass):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "Summarised with:", "", "    " + summary_cmd, "",
+              "%d compute units in %d XCDs. Requests are L1-to-L2 reads of %d-byte lines "
+              "(TCP_TCC_READ_REQ); latency is TCP_TCC_READ_REQ_LATENCY per request, in cycles; "
+              "in flight = total latency cycles / (compute units x elapsed cycles); TA busy and TA "
+              "held by L1 are fractions of elapsed cycles per compute unit (TA_TA_BUSY, "
+              "TA_ADDR_STALLED_BY_TC_CYCLES); waves waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES. "
+              "Durations are those of the counter run."
+              % (cus, xcds, LINE_BYTES), "",
+              "| Kernel | us | Read requests (M) | Requested (MB) | Latency (cycles) | In flight per CU "
+              "| Per-CU read rate (B/cycle) | TA busy | TA held by L1 | Waves waiting | Source hash |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key in KERNEL_FILES:
+        if key in res:
+            e = res[key]
+            lines.append("| %s | %.1f | %.2f | %.0f | %.0f | %.1f | %.1f | %.2f | %.2f | %.2f | %s |" % (
+                key, e["us"], e["read_requests"] / 1e6, e["requested_mb"], e["latency_cycles"],
+                e["in_flight_per_cu"], e["in_flight_per_cu"] * LINE_BYTES / e["latency_cycles"],
+                e["ta_busy"], e["ta_stalled_by_l1"], e["wave_wait_frac"], e["source_sha"]))
+    return "\n".join(lines) + "\n"
+
+
 def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
     cf = counter_means(copy_fetch_csv, "FETCH_SIZE")["copy"][0]
     cw = counter_means(copy_write_csv, "WRITE_SIZE")["copy"][0]
@@ -216,13 +306,28 @@ def main(argv=None):
     t.add_argument("--title", default="")
     t.add_argument("--command", action="append", default=[],
                    help="a profiling command to record in the markdown (repeatable)")
+    m = sub.add_parser("mlp")
+    m.add_argument("--pmc", required=True, help="counter run directory (counter and agent CSVs)")
+    m.add_argument("--md", required=True)
+    m.add_argument("--json", help="also write the figures here")
+    m.add_argument("--title", default="")
+    m.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     here = "python -m mamba_ssd_chunked_03_amd.profiling " + shlex.join(argv if argv else sys.argv[1:])
 
     def csv_in(p, kind):
         return p if os.path.isfile(p) else _one(os.path.join(p, "**", "*%s.csv" % kind))
 
-    if a.cmd == "stats":
+    if a.cmd == "mlp":
+        cus, xcds = agent_counts(csv_in(a.pmc, "agent_info"))
+        res = mlp(csv_in(a.pmc, "counter_collection"), cus, xcds)
+        with open(a.md, "w") as f:
+            f.write(mlp_md(res, a.title, a.command, here, cus, xcds))
+        if a.json:
+            with open(a.json, "w") as f:
+                json.dump(res, f, indent=1, sort_keys=True)
+                f.write("\n")
+    elif a.cmd == "stats":
         text, _ = stats_table(csv_in(a.trace, "kernel_trace"), a.command, here)
         with open(a.out, "w") as f:
             f.write(("# " + a.title + "\n\n" if a.title else "") + text)

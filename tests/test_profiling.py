@@ -65,3 +65,25 @@ def test_traffic_calibration(tmp_path):
     profiling.main(["traffic", "--fetch", f, "--write", w, "--copy-fetch", cf, "--copy-write", cw,
                     "--copy-bytes", "268435456", "--out", str(out)])
     assert json.load(open(out))["bwd_dx"]["bytes_per_launch"] == 2000 * 2048 + 512 * 1024
+
+
+def test_mlp_littles_law(tmp_path):
+    dx = "void ssd::bwd_dx_bf16_kernel<64, 128>(a)"
+    cols = PMC_COLS + ["Start_Timestamp", "End_Timestamp"]
+    # 2 CUs in 2 XCDs; 1000 ns at 2 cycles/ns = 2000 cycles per CU (GRBM sums both XCDs: 4000)
+    vals = {"TCP_TCC_READ_REQ_sum": 400.0, "TCP_TCC_READ_REQ_LATENCY_sum": 400.0 * 500,
+            "TA_TA_BUSY_sum": 2000.0, "TA_ADDR_STALLED_BY_TC_CYCLES_sum": 1000.0,
+            "SQ_WAVE_CYCLES": 100.0, "SQ_WAIT_ANY": 25.0, "SQ_BUSY_CYCLES": 1.0, "GRBM_GUI_ACTIVE": 4000.0}
+    rows = [[d, dx, c, v, 10_000 * d, 10_000 * d + 1000] for d in (1, 2) for c, v in vals.items()]
+    p = write(tmp_path / "m.csv", cols, rows)
+    res = profiling.mlp(p, cus=2, xcds=2)["bwd_dx"]
+    assert res["launches"] == 2 and abs(res["us"] - 1.0) < 1e-12
+    assert abs(res["clock_ghz"] - 2.0) < 1e-12
+    assert res["latency_cycles"] == 500.0
+    assert res["in_flight_per_cu"] == 400.0 * 500 / (2 * 2000)   # 50 requests per CU
+    assert res["ta_busy"] == 0.5 and res["ta_stalled_by_l1"] == 0.25 and res["wave_wait_frac"] == 0.25
+    assert res["requested_mb"] == 400 * 128 / 1e6
+    agent = write(tmp_path / "a.csv", ["Name", "Cu_Count", "Num_Xcc"], [["gfx950", 2, 2]])
+    assert profiling.agent_counts(agent) == (2, 2)
+    md = profiling.mlp_md({"bwd_dx": res}, "t", ["cmd"], "sum", 2, 2)
+    assert "| bwd_dx | 1.0 | 0.00 | 0 | 500 | 50.0 | 12.8 | 0.50 | 0.25 | 0.25 |" in md
