@@ -195,18 +195,23 @@ def counter_means(counter_csv, counter):
 MLP_COUNTERS = ("TCP_TCC_READ_REQ_sum", "TCP_TCC_READ_REQ_LATENCY_sum", "TA_TA_BUSY_sum",
                 "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_BUSY_CYCLES",
                 "GRBM_GUI_ACTIVE")
+# optional in the same pass: executed MFMA work, for the cross-check of the
+# algorithmic flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 flops)
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA")
+MOPS_FLOPS = 512
 LINE_BYTES = 128  # one L1-to-L2 read request
 
 
 def agent_counts(agent_csv):
-    """(compute units, XCDs) of the GPU agent in a rocprofv3 agent-info CSV."""
+    """(compute units, XCDs, SIMDs per CU) of the GPU agent in a rocprofv3 agent-info CSV."""
     for row in _rows(agent_csv):
         if "gfx" in row.get("Name", ""):
-            return int(row["Cu_Count"]), int(row.get("Num_Xcc") or 1)
+            return (int(row["Cu_Count"]), int(row.get("Num_Xcc") or 1),
+                    int(row.get("Simd_Per_Cu") or 4))
     raise ValueError("no GPU agent in %s" % agent_csv)
 
 
-def mlp(counter_csv, cus, xcds):
+def mlp(counter_csv, cus, xcds, simds_per_cu=4):
     """{key: figures} from one counter run holding MLP_COUNTERS.
 
     Per kernel name: the mean of each counter and of the dispatch duration over
@@ -242,11 +247,19 @@ def mlp(counter_csv, cus, xcds):
             "ta_busy": t["TA_TA_BUSY_sum"] / (cus * cyc),
             "ta_stalled_by_l1": t["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (cus * cyc),
             "wave_wait_frac": t["SQ_WAIT_ANY"] / t["SQ_WAVE_CYCLES"],
+            "mfma_gflop": (t["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * MOPS_FLOPS / 1e9
+                           if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in t else None),
+            "mfma_insts": t.get("SQ_INSTS_MFMA"),
+            "mfma_busy": (t["SQ_VALU_MFMA_BUSY_CYCLES"] / (cus * simds_per_cu * cyc)
+                          if "SQ_VALU_MFMA_BUSY_CYCLES" in t else None),
             "source_sha": source_hash(key) if key in KERNEL_FILES else ""}
     return out
 
 
 def mlp_md(res, title, commands, summary_cmd, cus, xcds):
+    def opt(v, f):
+        return "-" if v is None or not v else f % v
+
     lines = (["# " + title, ""] if title else []) + [
         "Counter run (from the repository root, one MI355X, one rocprofv3 pass):", ""]
     lines += ["    " + c for c in commands]
@@ -256,18 +269,22 @@ def mlp_md(res, title, commands, summary_cmd, cus, xcds):
               "in flight = total latency cycles / (compute units x elapsed cycles); TA busy and TA "
               "held by L1 are fractions of elapsed cycles per compute unit (TA_TA_BUSY, "
               "TA_ADDR_STALLED_BY_TC_CYCLES); waves waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES. "
-              "Durations are those of the counter run."
-              % (cus, xcds, LINE_BYTES), "",
+              "MFMA GFLOP executed = SQ_INSTS_VALU_MFMA_MOPS_BF16 x %d; MFMA busy = "
+              "SQ_VALU_MFMA_BUSY_CYCLES per SIMD over elapsed cycles. Durations are those of the "
+              "counter run."
+              % (cus, xcds, LINE_BYTES, MOPS_FLOPS), "",
               "| Kernel | us | Read requests (M) | Requested (MB) | Latency (cycles) | In flight per CU "
-              "| Per-CU read rate (B/cycle) | TA busy | TA held by L1 | Waves waiting | Source hash |",
-              "|---|---|---|---|---|---|---|---|---|---|---|"]
+              "| Per-CU read rate (B/cycle) | TA busy | TA held by L1 | Waves waiting "
+              "| MFMA GFLOP executed | MFMA busy | Source hash |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for key in KERNEL_FILES:
         if key in res:
             e = res[key]
-            lines.append("| %s | %.1f | %.2f | %.0f | %.0f | %.1f | %.1f | %.2f | %.2f | %.2f | %s |" % (
+            lines.append("| %s | %.1f | %.2f | %.0f | %.0f | %.1f | %.1f | %.2f | %.2f | %.2f | %s | %s | %s |" % (
                 key, e["us"], e["read_requests"] / 1e6, e["requested_mb"], e["latency_cycles"],
                 e["in_flight_per_cu"], e["in_flight_per_cu"] * LINE_BYTES / e["latency_cycles"],
-                e["ta_busy"], e["ta_stalled_by_l1"], e["wave_wait_frac"], e["source_sha"]))
+                e["ta_busy"], e["ta_stalled_by_l1"], e["wave_wait_frac"],
+                opt(e.get("mfma_gflop"), "%.1f"), opt(e.get("mfma_busy"), "%.3f"), e["source_sha"]))
     return "\n".join(lines) + "\n"
 
 
@@ -319,8 +336,8 @@ def main(argv=None):
         return p if os.path.isfile(p) else _one(os.path.join(p, "**", "*%s.csv" % kind))
 
     if a.cmd == "mlp":
-        cus, xcds = agent_counts(csv_in(a.pmc, "agent_info"))
-        res = mlp(csv_in(a.pmc, "counter_collection"), cus, xcds)
+        cus, xcds, spc = agent_counts(csv_in(a.pmc, "agent_info"))
+        res = mlp(csv_in(a.pmc, "counter_collection"), cus, xcds, spc)
         with open(a.md, "w") as f:
             f.write(mlp_md(res, a.title, a.command, here, cus, xcds))
         if a.json:

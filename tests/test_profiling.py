@@ -83,7 +83,13 @@ def test_mlp_littles_law(tmp_path):
     assert res["in_flight_per_cu"] == 400.0 * 500 / (2 * 2000)   # 50 requests per CU
     assert res["ta_busy"] == 0.5 and res["ta_stalled_by_l1"] == 0.25 and res["wave_wait_frac"] == 0.25
     assert res["requested_mb"] == 400 * 128 / 1e6
-    agent = write(tmp_path / "a.csv", ["Name", "Cu_Count", "Num_Xcc"], [["gfx950", 2, 2]])
-    assert profiling.agent_counts(agent) == (2, 2)
+    assert res["mfma_gflop"] is None and res["mfma_busy"] is None   # not in this pass
+    agent = write(tmp_path / "a.csv", ["Name", "Cu_Count", "Num_Xcc", "Simd_Per_Cu"], [["gfx950", 2, 2, 4]])
+    assert profiling.agent_counts(agent) == (2, 2, 4)
     md = profiling.mlp_md({"bwd_dx": res}, "t", ["cmd"], "sum", 2, 2)
-    assert "| bwd_dx | 1.0 | 0.00 | 0 | 500 | 50.0 | 12.8 | 0.50 | 0.25 | 0.25 |" in md
+    assert "| bwd_dx | 1.0 | 0.00 | 0 | 500 | 50.0 | 12.8 | 0.50 | 0.25 | 0.25 | - | - |" in md
+    # with the MFMA counters: 2 CUs x 4 SIMDs x 2000 cycles; 4000 busy cycles -> 0.25
+    vals.update({"SQ_INSTS_VALU_MFMA_MOPS_BF16": 2e6, "SQ_VALU_MFMA_BUSY_CYCLES": 4000.0, "SQ_INSTS_MFMA": 10.0})
+    rows = [[d, dx, c, v, 10_000 * d, 10_000 * d + 1000] for d in (1, 2) for c, v in vals.items()]
+    res = profiling.mlp(write(tmp_path / "m2.csv", cols, rows), cus=2, xcds=2, simds_per_cu=4)["bwd_dx"]
+    assert res["mfma_gflop"] == 2e6 * 512 / 1e9 and res["mfma_busy"] == 0.25 and res["mfma_insts"] == 10.0
