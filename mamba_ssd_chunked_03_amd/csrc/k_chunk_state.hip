@@ -17,7 +17,11 @@
 // issued before the current slice's MFMAs, so memory latency overlaps compute.
 // The scaled operand is split into bf16 hi + lo parts (two MFMAs) so the chunk
 // state keeps ~16 bits of precision; the states feed the fp32 final states.
-// Four wavefronts, each a (P/2) x (N/2) tile of 16x16 blocks.
+// Four wavefronts per head, each a (P/2) x (N/2) tile of 16x16 blocks.  Where a
+// group has an even number of heads and the tiles fit, one workgroup holds two
+// heads of a group (eight wavefronts): the second operand (B, or C) is the
+// group's, so each slice of it is loaded and staged once for both heads, which
+// halves the L2 read requests for it.
 //
 // kStateFwdCumsum also forms stage 1 for its (chunk, head) first: wave w scans
 // tokens 64w .. 64w + 63 (delta, then the inclusive sum of delta A in log2
@@ -46,8 +50,8 @@ struct CumsumIn {
   float* decay;
 };
 
-template <int P, int N, int MODE>
-__global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, int H, int G,
+template <int P, int N, int MODE, int HP>
+__global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap m, int H, int G,
                                                                const uint16_t* __restrict__ X,
                                                                const uint16_t* __restrict__ Y,
                                                                float* __restrict__ delta,
@@ -59,20 +63,27 @@ __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, in
   constexpr int WM = 2, WN = 2;
   constexpr int TM = P / 16 / WM, TN = N / 16 / WN;
   constexpr int XC = KS * (P / 8) / 256;  // 16-byte chunks per thread per slice
-  constexpr int YC = KS * (N / 8) / 256;
-  static_assert(TM >= 1 && TN >= 1 && XC >= 1 && YC >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t xh[KS * LDX];
-  __shared__ __attribute__((aligned(16))) uint16_t xl[KS * LDX];
+  constexpr int YC = KS * (N / 8) / (256 * HP);  // shared operand: pieces per thread of the workgroup
+  static_assert(TM >= 1 && TN >= 1 && XC >= 1 && YC >= 1 && KS * (N / 8) % (256 * HP) == 0,
+                "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t xh_[HP][KS * LDX];
+  __shared__ __attribute__((aligned(16))) uint16_t xl_[HP][KS * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t ys[KS * LDY];
-  __shared__ float sc[256];
+  __shared__ float sc_[HP][256];
 
   int k, h;
-  chunk_head(H, k, h);
+  chunk_head(H / HP, k, h);
+  const int half = HP == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / 256);
+  h = h * HP + half;
+  uint16_t* xh = xh_[half];
+  uint16_t* xl = xl_[half];
+  float* sc = sc_[half];
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
   const int Q = m.Q, len = ci.len;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // tid: thread of this head's four wavefronts; gid: thread of the workgroup
+  const int gid = threadIdx.x, tid = HP == 1 ? gid : gid % 256, w = tid >> 6, lane = tid & 63;
   const int64_t kh = (int64_t)k * H + h;
   const int64_t xrow = (int64_t)H * P, yrow = (int64_t)G * N;
   const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, in
     }
 #pragma unroll
     for (int c = 0; c < YC; ++c) {
-      const int e = tid + c * 256, j = s0 + e / (N / 8), c8 = e % (N / 8);
+      const int e = gid + c * 256 * HP, j = s0 + e / (N / 8), c8 = e % (N / 8);
       yr[c] = (j < len) ? *(const u32x4*)(yb + (int64_t)j * yrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -110,7 +121,9 @@ __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, in
   if constexpr (MODE == kStateFwdCumsum) dtv = in ? cs.dt[(int64_t)(ci.start + t) * H + h] : 0.f;
   load_slice(0);  // independent of the token scales: in flight while they are formed
   if constexpr (MODE == kStateFwdCumsum) {
-    __shared__ float wtot[4], alast;
+    __shared__ float wtot_[HP][4], alast_[HP];
+    float* wtot = wtot_[half];
+    float& alast = alast_[half];
     const float bias = cs.dt_bias ? cs.dt_bias[h] : 0.f;
     const float a2 = cs.A[h] * kLog2e;
     const float d = token_delta(dtv, bias, cs.softplus, in);
@@ -154,7 +167,7 @@ __global__ __launch_bounds__(256, 4) void chunk_state_bf16_kernel(ChunkMap m, in
     }
 #pragma unroll
     for (int c = 0; c < YC; ++c) {
-      const int e = tid + c * 256, jj = e / (N / 8), c8 = e % (N / 8);
+      const int e = gid + c * 256 * HP, jj = e / (N / 8), c8 = e % (N / 8);
       *(u32x4*)(ys + jj * LDY + c8 * 8) = yr[c];
     }
     __syncthreads();
@@ -219,20 +232,38 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H,
   out[kh * (int64_t)(P * N) + o] = acc;
 }
 
+template <int P, int N, int HP>
+static void launch_cs_hp(const Prob& p, const void* X, const void* Y, float* delta, float* acs,
+                         float* out, int mode, const CumsumIn& cs, hipStream_t st) {
+  const dim3 grid((unsigned)(p.nck * (p.H / HP)));  // (chunk, head group of HP) in the XCD-aware order
+  const dim3 block(256 * HP);
+  const uint16_t *x = (const uint16_t*)X, *y = (const uint16_t*)Y;
+  if (mode == kStateFwd)
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwd, HP>), grid, block, 0, st, p.map, p.H,
+                       p.G, x, y, delta, acs, out, cs);
+  else if (mode == kStateDstates)
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateDstates, HP>), grid, block, 0, st, p.map,
+                       p.H, p.G, x, y, delta, acs, out, cs);
+  else
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwdCumsum, HP>), grid, block, 0, st, p.map,
+                       p.H, p.G, x, y, delta, acs, out, cs);
+}
+
+// LDS bytes of a chunk-state workgroup holding hp heads (the arrays above)
+constexpr int cs_lds_bytes(int P, int N, int hp) {
+  return hp * (2 * 64 * (P + 16) * 2 + 256 * 4 + 5 * 4) + 64 * (N + 16) * 2;
+}
+
 template <int P, int N>
 static void launch_cs_bf16(const Prob& p, const void* X, const void* Y, float* delta, float* acs,
                            float* out, int mode, const CumsumIn& cs, hipStream_t st) {
-  const dim3 grid((unsigned)(p.nck * p.H));  // (chunk, head) in the XCD-aware order
-  const uint16_t *x = (const uint16_t*)X, *y = (const uint16_t*)Y;
-  if (mode == kStateFwd)
-    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwd>), grid, dim3(256), 0, st, p.map, p.H,
-                       p.G, x, y, delta, acs, out, cs);
-  else if (mode == kStateDstates)
-    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateDstates>), grid, dim3(256), 0, st, p.map,
-                       p.H, p.G, x, y, delta, acs, out, cs);
-  else
-    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, kStateFwdCumsum>), grid, dim3(256), 0, st, p.map,
-                       p.H, p.G, x, y, delta, acs, out, cs);
+  // two heads per workgroup when a group's head count is even, the shared operand
+  // splits evenly over 512 threads, and two such workgroups still fit a CU's LDS
+  constexpr bool two_ok = 64 * (N / 8) % 512 == 0 && cs_lds_bytes(P, N, 2) <= 80 * 1024;
+  if constexpr (two_ok) {
+    if ((p.H / p.G) % 2 == 0) return launch_cs_hp<P, N, 2>(p, X, Y, delta, acs, out, mode, cs, st);
+  }
+  launch_cs_hp<P, N, 1>(p, X, Y, delta, acs, out, mode, cs, st);
 }
 
 static hipError_t launch_cs(const Prob& p, const void* X, const void* Y, float* delta, float* acs,

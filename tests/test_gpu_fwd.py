@@ -34,6 +34,10 @@ CASES = [
                           io="bf16", init="zeros", seed=13), (128,)),
     ("bf16_short", dict(batch=3, seqlen=37, nheads=2, headdim=64, dstate=64, ngroups=1,
                         io="bf16", init="randn", seed=14), (256,)),
+    # an odd number of heads per group: kernels that pair a group's heads in one
+    # workgroup take their one-head form here
+    ("bf16_odd_heads", dict(batch=1, seqlen=420, nheads=3, headdim=64, dstate=128, ngroups=1,
+                            io="bf16", init="randn", seed=17), (256,)),
     ("f32_cfg0_shape", dict(batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, ngroups=1,
                             io="f32", dt_mode="direct", init="none", seed=0), (64,)),
     ("f32_ragged", dict(batch=2, seqlen=150, nheads=2, headdim=16, dstate=32, ngroups=1,
