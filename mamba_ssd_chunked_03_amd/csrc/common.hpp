@@ -264,6 +264,27 @@ constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0
 constexpr int kRowRor8 = 0x128, kRowHalfMirror = 0x141, kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
+// Stores of 128-byte row spans, whole.  In a 16-row MFMA tile, lane (q, r) owns
+// row r and the 16-byte pieces at bytes q*16 (piece 0) and 64 + q*16 (piece 1)
+// of a 128-byte span.  Stored directly, each instruction would cover half of
+// every row's span; instead the first store covers rows 0..7 whole (lanes r < 8
+// piece 0 of row r, lanes r >= 8 piece 1 of row r - 8) and the second rows
+// 8..15, after a row rotate by 8 (lane r <-> lane r ^ 8) has moved the pieces:
+// half as many partial-line writes reach the L2.
+__device__ __forceinline__ uint32_t span_off(int r, int q) { return (r < 8 ? 0u : 64u) + q * 16; }
+// the lane's own (piece 0, piece 1) -> (a, b): a goes to row r & 7, b to row 8 + (r & 7),
+// both at byte span_off(r, q) of the span
+__device__ __forceinline__ void span_swap(int r, const u32x4& o0, const u32x4& o1, u32x4& a, u32x4& b) {
+  const bool lo = r < 8;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t recv =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(lo ? o1[d] : o0[d]), kRowRor8, 0xf, 0xf, false);
+    a[d] = lo ? o0[d] : recv;
+    b[d] = lo ? recv : o1[d];
+  }
+}
+
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ float dpp_f(float old, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,

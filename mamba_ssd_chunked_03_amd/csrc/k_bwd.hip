@@ -238,10 +238,12 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
         acc[tp] = mfma_bf16(frag_kmajor(dyt + cb0 * 32 * LDY + tp * 16, LDY, lane), a, acc[tp]);
     }
     if (live(ii + 1)) load_rb(rb_of(ii + 1));  // the fragments above are dead now
-    // per-row dots and the store
+    // per-row dots and the store: the lane's 8 adjacent columns per tile pair, written as
+    // whole 128-byte row spans (span_swap) where a row has two pieces per lane
     const float dj = rowok ? sd[jrow] : 0.f;
     float xt = 0.f, dxx = 0.f;
     const uint32_t dxo = (uint32_t)jrow * (uint32_t)(xrow * 2) + q * 16;
+    u32x4 os[P / 32];
 #pragma unroll
     for (int s = 0; s < P / 32; ++s) {
       const u32x4 dq = lds_cols8_perm(dyt + jrow * LDY, s, q);  // rows past the end are zero
@@ -257,7 +259,19 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
         o[2 * u] = pack_bf2(dj * a[0] + Dh * y0, dj * a[1] + Dh * y1);
         o[2 * u + 1] = pack_bf2(dj * a[2] + Dh * y2, dj * a[3] + Dh * y3);
       }
-      buf_store16(rdx, dxo + 64 * s, o);  // dropped for rows past the end
+      os[s] = o;
+    }
+    if constexpr (P >= 64) {
+      const uint32_t ra = (uint32_t)(j0 + (r & 7)), so = span_off(r, q);
+#pragma unroll
+      for (int m2 = 0; m2 < P / 64; ++m2) {
+        u32x4 a, b;
+        span_swap(r, os[2 * m2], os[2 * m2 + 1], a, b);
+        buf_store16(rdx, ra * (uint32_t)(xrow * 2) + so + 128 * m2, a);
+        buf_store16(rdx, (ra + 8) * (uint32_t)(xrow * 2) + so + 128 * m2, b);
+      }
+    } else {
+      buf_store16(rdx, dxo, os[0]);
     }
     xs += __shfl_xor(xs, 16);
     xs += __shfl_xor(xs, 32);

@@ -191,9 +191,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
         acc[tp] = mfma_bf16(frag_kmajor(xs + nb * 32 * LDX + tp * 16, LDX, lane), a, acc[tp]);
     }
     if (live(ii + 1)) load_rb(rb_of(ii + 1));  // the fragments above are dead now
-    // 5. skip term and 16-byte stores of the lane's 8 adjacent outputs
+    // 5. skip term; the lane's 8 adjacent outputs per tile pair are stored as whole
+    //    128-byte row spans (span_swap) where a row has two pieces per lane
     {
       const uint32_t yo = (uint32_t)irow * (uint32_t)(xrow * 2) + q * 16;
+      u32x4 ys_[P / 32];
 #pragma unroll
       for (int s = 0; s < P / 32; ++s) {
         const u32x4 xv = lds_cols8_perm(xs + irow * LDX, s, q);
@@ -206,7 +208,19 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
         y1[1] += Dh * bf_hi(xv[2]);
         y1[2] += Dh * bf_lo(xv[3]);
         y1[3] += Dh * bf_hi(xv[3]);
-        buf_store16(ry, yo + 64 * s, pack_bf8(y0, y1));  // dropped for rows past the end
+        ys_[s] = pack_bf8(y0, y1);
+      }
+      if constexpr (P >= 64) {
+        const uint32_t ra = (uint32_t)(rb_of(ii) * 16 + (r & 7)), so = span_off(r, q);
+#pragma unroll
+        for (int m2 = 0; m2 < P / 64; ++m2) {
+          u32x4 a, b;
+          span_swap(r, ys_[2 * m2], ys_[2 * m2 + 1], a, b);
+          buf_store16(ry, ra * (uint32_t)(xrow * 2) + so + 128 * m2, a);
+          buf_store16(ry, (ra + 8) * (uint32_t)(xrow * 2) + so + 128 * m2, b);
+        }
+      } else {
+        buf_store16(ry, yo, ys_[0]);
       }
     }
   }

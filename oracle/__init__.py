@@ -25,7 +25,7 @@ Modules
                 double-buffered Hillis-Steele, Blelloch).
 ``recurrence``  the literal token-by-token fp64 recurrence, forward and its
                 adjoint (backward) with segment checkpoints.  This is the
-                oracle the GPU path is judged against.
+                oracle the GPU path is checked against.
 ``chunked``     the four-stage chunked form in fp64 (cumsum, chunk states,
                 state passing, chunk output) and its backward.  Used to pin
                 ``recurrence`` and to give per-stage intermediates.
