@@ -72,9 +72,11 @@ def kernel_key(name):
         return None
     base = base.group(1)
     targs = re.search(r"<([^>]*)>", name)
-    last = targs.group(1).split(",")[-1].strip() if targs else ""
+    targ = [t.strip() for t in targs.group(1).split(",")] if targs else []
+    last = targ[-1] if targ else ""
     if base.startswith("chunk_state"):
-        return "dstates" if last == "1" else "chunk_state"
+        # chunk_state_bf16_kernel<P, N, MODE, heads per workgroup>: MODE 1 is the backward's dstates
+        return "dstates" if len(targ) >= 3 and targ[2] == "1" else "chunk_state"
     if base == "state_passing_kernel":
         return "reverse_state_passing" if last == "1" else "state_passing"
     if base.startswith("bmm_chunk_bf16"):

@@ -20,6 +20,9 @@ def test_kernel_keys():
     k = profiling.kernel_key
     assert k("void ssd::chunk_state_bf16_kernel<64, 128, 0>(ssd::ChunkMap)") == "chunk_state"
     assert k("void ssd::chunk_state_bf16_kernel<64, 128, 1>(ssd::ChunkMap)") == "dstates"
+    assert k("void ssd::chunk_state_bf16_kernel<64, 128, 1, 2>(ssd::ChunkMap)") == "dstates"
+    assert k("void ssd::chunk_state_bf16_kernel<64, 128, 2, 1>(ssd::ChunkMap)") == "chunk_state"
+    assert k("void ssd::chunk_state_bf16_kernel<64, 128, 0, 2>(ssd::ChunkMap)") == "chunk_state"
     assert k("void ssd::state_passing_kernel<16, 4, unsigned short, 1>(x)") == "reverse_state_passing"
     assert k("void ssd::state_passing_kernel<16, 4, unsigned short, 0>(x)") == "state_passing"
     assert k("void ssd::bwd_dc_bf16_kernel<64, 128>(x)") == "bwd_dc"
