@@ -41,7 +41,9 @@
  *    priority), forked from and joined back to `stream` with events: the call as a
  *    whole stays ordered on `stream`, and it can be captured into a HIP graph.
  *    Calls issued on different streams at the same time share that second stream
- *    (they stay correct; their side kernels queue behind each other).
+ *    (they stay correct; their side kernels queue behind each other).  The second
+ *    stream belongs to the current device: when `stream` belongs to another
+ *    device, the call queues all of its kernels on `stream` alone.
  *  - Every error the host can detect (NULL, shape, alignment, workspace size,
  *    unsupported configuration) is returned BEFORE anything is queued.  A failed
  *    launch returns SSD_ERR_HIP.  Nothing is printed; no exception crosses the ABI.

@@ -159,17 +159,27 @@ ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool 
 // not depend on the ones queued before them run there; the caller's stream forks
 // to it and joins it again through the events, so each call stays ordered on the
 // caller's stream as a whole.  The lock is held while a call queues its work, so
-// calls from several host threads do not interleave their event records.
+// calls from several host threads do not interleave their event records.  A
+// caller's stream that belongs to another device than the current one gets no
+// second stream (every kernel of the call then runs on the caller's stream).
 struct SideLane {
   bool tried = false, ok = false;
   hipStream_t stream = nullptr;
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
 };
-SideLane* side_lane(std::unique_lock<std::mutex>& lock) {
+SideLane* side_lane(hipStream_t caller, std::unique_lock<std::mutex>& lock) {
   static std::mutex mu;
   static SideLane lanes[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (caller != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(caller, &sdev) != hipSuccess) {
+      (void)hipGetLastError();  // not the caller's error: the call goes on without a second stream
+      return nullptr;
+    }
+    if (sdev != dev) return nullptr;
+  }
   lock = std::unique_lock<std::mutex>(mu);
   SideLane& l = lanes[dev];
   if (!l.tried) {
@@ -272,7 +282,7 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   // chunk states (one kernel on the bf16 path) and the state passing; the chunk
   // scan waits for it.
   std::unique_lock<std::mutex> lane_lock;
-  SideLane* side = (!only && p.nck > 0) ? side_lane(lane_lock) : nullptr;
+  SideLane* side = (!only && p.nck > 0) ? side_lane(st, lane_lock) : nullptr;
   if (side) {  // events: 0 fork, 1 C.B^T done
     SSD_TRY(hipEventRecord(side->ev[0], st));
     SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
@@ -348,7 +358,7 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   // beside the adjoint states, the reverse scan and dx; the finalize waits for
   // the side stream.  Each stream then carries about half of the work.
   std::unique_lock<std::mutex> lane_lock;
-  SideLane* side = (!only && p.io == SSD_BF16 && p.nck > 0) ? side_lane(lane_lock) : nullptr;
+  SideLane* side = (!only && p.io == SSD_BF16 && p.nck > 0) ? side_lane(st, lane_lock) : nullptr;
   if (side) {  // events: 0 fork, 1 reverse scan done, 2 side stream done
     SSD_TRY(hipEventRecord(side->ev[0], st));
     SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
