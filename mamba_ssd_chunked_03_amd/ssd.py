@@ -67,6 +67,8 @@ _SIGS = {
     "ssd_gated_rmsnorm_bwd": ([_P] + [_P] * 8 + [_SZ, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
+# The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
+ABI_VERSION = 3
 
 _lib = None
 
@@ -83,6 +85,9 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = res
+        if L.ssd_abi_version() != ABI_VERSION:
+            raise RuntimeError("libssd.so has ABI version %d, this binding expects %d; rebuild it"
+                               % (L.ssd_abi_version(), ABI_VERSION))
         _lib = L
     return _lib
 

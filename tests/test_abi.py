@@ -39,7 +39,9 @@ def test_header_and_binding_agree(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.ssd_abi_version() == 3
+    assert L.ssd_abi_version() == ssd.ABI_VERSION
+    hdr = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    assert "#define SSD_ABI_VERSION %d" % ssd.ABI_VERSION in hdr
     for s in range(8):
         assert len(L.ssd_status_string(s)) > 0
     assert L.ssd_status_string(99) == b"unknown status"
