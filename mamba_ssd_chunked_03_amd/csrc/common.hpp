@@ -125,6 +125,10 @@ __device__ __forceinline__ brsrc make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(brsrc r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// the same load marked nontemporal (the cache-policy operand's NT bit)
+__device__ __forceinline__ u32x4 buf_load16_nt(brsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 __device__ __forceinline__ void buf_store16(brsrc r, uint32_t off, u32x4 v) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 0);
@@ -225,29 +229,39 @@ __device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const fl
 // all be in flight before the first LDS store waits for its data.  STREAM
 // marks the loads nontemporal: for a tile that this kernel reads exactly once,
 // it keeps the tile from displacing the operands that other workgroups re-read
-// from the cache.
+// from the cache.  The loads go through a buffer resource that ends at row
+// nvalid, so rows past it read as zero with no branch: a load under a branch,
+// with zero on the other path, lets the register allocator give the two paths
+// one register, and the zero's move must then wait for the load in flight,
+// which serialises the tile's loads.  (nvalid * srow * 2 bytes stay below
+// 2^31: one chunk's rows at most.)
 template <int ROWS, int W, int NT = 256, bool PERM = false, bool STREAM = false>
 struct RowTile {
   static constexpr int PER = W / 8;
   static constexpr int NC = (ROWS * PER + NT - 1) / NT;
+  // every thread's every piece lies inside the tile: no test at all
+  static constexpr bool EXACT = (ROWS * PER) % NT == 0;
   static_assert(!PERM || W % 32 == 0, "permuted rows are whole 32-column blocks");
   u32x4 t[NC];
   __device__ __forceinline__ void load(const uint16_t* src, int64_t srow, int nvalid, int tid) {
+    const brsrc rs = make_rsrc(src, nvalid > 0 ? (uint32_t)nvalid * (uint32_t)(srow * 2) : 0u);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = tid + c * NT, j = e / PER, c8 = e % PER;
-      const u32x4* p = (const u32x4*)(src + (int64_t)j * srow + c8 * 8);
+      // pieces past the tile (a partial last round) get an offset beyond any range
+      const uint32_t off =
+          (EXACT || e < ROWS * PER) ? (uint32_t)j * (uint32_t)(srow * 2) + c8 * 16 : 0x80000000u;
       if constexpr (STREAM)
-        t[c] = (e < ROWS * PER && j < nvalid) ? __builtin_nontemporal_load(p) : u32x4{0u, 0u, 0u, 0u};
+        t[c] = buf_load16_nt(rs, off);
       else
-        t[c] = (e < ROWS * PER && j < nvalid) ? *p : u32x4{0u, 0u, 0u, 0u};
+        t[c] = buf_load16(rs, off);
     }
   }
   __device__ __forceinline__ void store(uint16_t* dst, int ld, int tid) const {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = tid + c * NT, j = e / PER, c8 = e % PER;
-      if (e < ROWS * PER) lds_piece<PERM>(dst + j * ld, c8, t[c]);
+      if (EXACT || e < ROWS * PER) lds_piece<PERM>(dst + j * ld, c8, t[c]);
     }
   }
 };

@@ -98,17 +98,21 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Buffer resources over the chunk's valid rows: rows past its end read as
+  // zero, with no branch (a load under a branch can leave its register shared
+  // with the other path's zero, whose move then waits for the load).
+  const brsrc rx = make_rsrc(xb, (uint32_t)(len * xrow * 2)), ry = make_rsrc(yb, (uint32_t)(len * yrow * 2));
   u32x4 xr[XC], yr[YC];
   auto load_slice = [&](int s0) {
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
       const int e = tid + c * 256, j = s0 + e / (P / 8), c8 = e % (P / 8);
-      xr[c] = (j < len) ? *(const u32x4*)(xb + (int64_t)j * xrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+      xr[c] = buf_load16(rx, (uint32_t)j * (uint32_t)(xrow * 2) + c8 * 16);
     }
 #pragma unroll
     for (int c = 0; c < YC; ++c) {
       const int e = gid + c * 256 * HP, j = s0 + e / (N / 8), c8 = e % (N / 8);
-      yr[c] = (j < len) ? *(const u32x4*)(yb + (int64_t)j * yrow + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+      yr[c] = buf_load16(ry, (uint32_t)j * (uint32_t)(yrow * 2) + c8 * 16);
     }
   };
   // kStateFwdCumsum: this thread's token (256 threads, chunks of at most 256
