@@ -125,6 +125,9 @@ __device__ __forceinline__ brsrc make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(brsrc r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ float buf_load_f32(brsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 // the same load marked nontemporal (the cache-policy operand's NT bit)
 __device__ __forceinline__ u32x4 buf_load16_nt(brsrc r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));

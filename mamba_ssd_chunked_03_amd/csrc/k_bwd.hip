@@ -949,21 +949,36 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
   const int t = Q - 64 * w - 1 - lane;  // negative for waves past a short chunk size
   const bool in = t >= 0 && t < len;
   const float Ah = A[h], bias = dt_bias ? dt_bias[h] : 0.f;
-  float v = 0.f, dl = 0.f, d0 = 0.f, z = 0.f;
-  if (in) {
-    v = rR[kh * Q + t] - Ks[kh * Q + t] + (t == len - 1 ? last_term[kh] : 0.f);
-    // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
-    const int tt = t / 64, tlast = (len - 1) / 64;
+  // Every load is issued unconditionally through a range-checked buffer
+  // resource (tokens outside the chunk get an offset past every range and read
+  // zero), and the masked terms are dropped by selects: loads under branches
+  // were serialised, each waiting for the one before.
+  const uint32_t ot = in ? (uint32_t)t * 4u : 0x80000000u;
+  const uint32_t rowb = (uint32_t)len * 4u;
+  const float r0 = buf_load_f32(make_rsrc(rR + kh * Q, rowb), ot);
+  const float k0 = buf_load_f32(make_rsrc(Ks + kh * Q, rowb), ot);
+  const float dlv = buf_load_f32(make_rsrc(delta + kh * Q, rowb), ot);
+  const float d0v = buf_load_f32(make_rsrc(ddd + kh * Q, rowb), ot);
+  const float dtv = buf_load_f32(make_rsrc(dt + (int64_t)ci.start * H + h, rowb * (uint32_t)H),
+                                 in ? (uint32_t)t * (uint32_t)H * 4u : 0x80000000u);
+  const brsrc rrp = make_rsrc(Rp + kh * ntile * Q, (uint32_t)(ntile * Q * 4));
+  const brsrc rkp = make_rsrc(Kp + kh * ntile * Q, (uint32_t)(ntile * Q * 4));
+  float rp[4], kp[4];
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl)
-      if (tl <= tt && tl < ntile) v += Rp[(kh * ntile + tl) * Q + t];
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl)
-      if (tl >= tt && tl <= tlast && tl < ntile) v -= Kp[(kh * ntile + tl) * Q + t];
-    dl = delta[kh * Q + t];
-    d0 = ddd[kh * Q + t];
-    z = dt[(ci.start + t) * (int64_t)H + h] + bias;
+  for (int tl = 0; tl < 4; ++tl) {
+    rp[tl] = buf_load_f32(rrp, ot + (uint32_t)(tl * Q * 4));
+    kp[tl] = buf_load_f32(rkp, ot + (uint32_t)(tl * Q * 4));
   }
+  const float lt = last_term[kh];
+  float v = r0 - k0 + (t == len - 1 ? lt : 0.f);
+  // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
+  const int tt = t / 64, tlast = (len - 1) / 64;
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) v = (tl <= tt && tl < ntile) ? v + rp[tl] : v;
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) v = (tl >= tt && tl <= tlast && tl < ntile) ? v - kp[tl] : v;
+  v = in ? v : 0.f;
+  const float dl = in ? dlv : 0.f, d0 = in ? d0v : 0.f, z = in ? dtv + bias : 0.f;
   const float sw = wave_inclusive_sum(v);
   if (lane == 63) wtot[w] = sw;
   __syncthreads();

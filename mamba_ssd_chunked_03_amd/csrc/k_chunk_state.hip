@@ -36,6 +36,8 @@
 
 namespace ssd {
 
+constexpr int QMAX_STATE = 256;  // largest chunk size
+
 __device__ __forceinline__ float token_scale(int mode, const float* dl, const float* ac, int j,
                                              float a_last) {
   return mode == kStateFwd ? dl[j] * exp2_fast(a_last - ac[j]) : exp2_fast(ac[j]);
@@ -119,11 +121,30 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
   // tokens; wave w holds the cumsum's pass w).  Its dt is loaded before the
   // first slice, so that waiting for it does not also wait for the slice (the
   // memory counter completes in order).
+  // The other modes load this thread's acs (and delta, and the chunk's last acs)
+  // the same way.  Range-checked buffer loads: tokens past the chunk's end read
+  // as zero, with no branch.
+  static_assert(QMAX_STATE <= 256, "one token per thread of a head");
   const int t = tid;
   const bool in = t < len;
-  float dtv = 0.f;
-  if constexpr (MODE == kStateFwdCumsum) dtv = in ? cs.dt[(int64_t)(ci.start + t) * H + h] : 0.f;
+  float dtv = 0.f, acv = 0.f, dlv = 0.f, alv = 0.f;
+  if constexpr (MODE == kStateFwdCumsum) {
+    const brsrc rdt = make_rsrc(cs.dt + (int64_t)ci.start * H + h, (uint32_t)(len * H * 4));
+    dtv = buf_load_f32(rdt, (uint32_t)(t * H * 4));
+  } else {
+    const brsrc ra = make_rsrc(acs + kh * Q, (uint32_t)(len * 4));
+    acv = buf_load_f32(ra, (uint32_t)(t * 4));
+    if constexpr (MODE == kStateFwd) {
+      const brsrc rd = make_rsrc(delta + kh * Q, (uint32_t)(len * 4));
+      dlv = buf_load_f32(rd, (uint32_t)(t * 4));
+      alv = buf_load_f32(ra, (uint32_t)((len - 1) * 4));
+    }
+  }
+  // (kept ahead of the slice's loads: the scheduler would otherwise sink them
+  // below, and waiting for them would then wait for the slice too)
+  __builtin_amdgcn_sched_barrier(0);
   load_slice(0);  // independent of the token scales: in flight while they are formed
+  __builtin_amdgcn_sched_barrier(0);  // (and all issued before the first wait)
   if constexpr (MODE == kStateFwdCumsum) {
     __shared__ float wtot_[HP][4], alast_[HP];
     float* wtot = wtot_[half];
@@ -148,10 +169,9 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
     __syncthreads();
     if (t < Q) sc[t] = in ? d * exp2_fast(alast - incl) : 0.f;
   } else {
-    const float* dl = delta + kh * Q;
-    const float* ac = acs + kh * Q;
-    const float a_last = ac[len - 1];
-    for (int t = tid; t < Q; t += 256) sc[t] = (t < len) ? token_scale(MODE, dl, ac, t, a_last) : 0.f;
+    // (every thread writes its entry, so the loads above are not sunk into a branch)
+    const float v = MODE == kStateFwd ? dlv * exp2_fast(alv - acv) : exp2_fast(acv);
+    sc[t] = in ? v : 0.f;
   }
   __syncthreads();
   for (int s0 = 0; s0 < len; s0 += KS) {
