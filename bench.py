@@ -330,8 +330,16 @@ def main():
         nbytes = kernel_bytes(Bsz, L, H, P, N, G, Q, nck, Bsz, 2, init=init is not None,
                               d_final=False)
         nflops = kernel_flops(Bsz, L, H, P, N, G, Q, nck)
+        # where the chunk-state kernel forms C.B^T (and its transpose) itself, its
+        # bytes and flops are that kernel's and no C.B^T kernel is launched
+        fwd_mask = lib.ssd_fwd_kernel_mask(ctypes.byref(prob), Q, 0)
+        if not fwd_mask & 4:
+            nbytes["chunk_state"] += nbytes["bmm_chunk"] - Bsz * L * G * N * 2  # (B is read once)
+            nflops["chunk_state"] += nflops["bmm_chunk"]
         fns = {}
         for k, name in enumerate(ssd.FWD_KERNELS, 1):
+            if not fwd_mask & (1 << (k - 1)):
+                continue
             fns[name] = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_b, out=y, final=final,
                                 save_for_backward=True, only_kernel=k, prepare=True, **common)[0]
         for k, name in enumerate(ssd.BWD_KERNELS, 1):
@@ -365,7 +373,7 @@ def main():
                     "frac_hbm": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "frac_hbm_cold": round(b / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         names = [n for n in kernels]
-        kernels["_forward_aggregate"] = aggregate(list(ssd.FWD_KERNELS))
+        kernels["_forward_aggregate"] = aggregate([n for n in ssd.FWD_KERNELS if n in kernels])
         kernels["_backward_aggregate"] = aggregate(list(ssd.BWD_KERNELS))
         kernels["_all"] = aggregate(names)
 

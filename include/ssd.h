@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum {
   SSD_OK = 0,
@@ -107,7 +107,8 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 /* SSD_FLAG_FWD_KERNEL(k), k = 1..4: the same for ssd_fwd, whose workspace and
  *   outputs must hold a complete call's results on the same arguments: 1 chunk
  *   cumsum and chunk states (one kernel on the bf16 path), 2 state passing,
- *   3 C.B^T, 4 chunk scan. */
+ *   3 C.B^T, 4 chunk scan.  Where ssd_fwd_kernel_mask() leaves bit 2 clear, C.B^T
+ *   is formed by kernel 1 and k = 3 launches nothing. */
 #define SSD_FLAG_FWD_KERNEL(k) ((k) << 12)
 
 typedef struct {
@@ -126,6 +127,13 @@ typedef struct {
 /* ABI version (SSD_ABI_VERSION) and a static message for a status code. */
 int32_t ssd_abi_version(void);
 const char* ssd_status_string(int32_t status);
+
+/* Which of the four forward kernels (bit k-1 for SSD_FLAG_FWD_KERNEL(k)) a complete
+ * ssd_fwd call on this problem launches: 0xF, or 0xB where the chunk-state kernel
+ * also forms C.B^T (bf16, chunk_size 256, eight heads per group, so that each pair
+ * of a group's heads holds one 64-row block of the chunk's C.B^T).  A profiling and
+ * accounting aid; the results do not depend on it.  Returns 0 for an invalid problem. */
+int32_t ssd_fwd_kernel_mask(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 
 /* Number of chunk slots the per-chunk stage arrays below must hold:
  * batch * ceil(seqlen / chunk_size), or floor((seqlen + nseq*(chunk_size-1)) / chunk_size)

@@ -232,6 +232,12 @@ int64_t ssd_num_chunks(const ssd_problem* pr, int32_t Q, int32_t packed) {
   return p.nck;
 }
 
+int32_t ssd_fwd_kernel_mask(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
+  return cb_in_chunk_state(p) ? 0xB : 0xF;
+}
+
 size_t ssd_fwd_workspace_bytes(const ssd_problem* pr, int32_t Q, int32_t packed) {
   Prob p;
   if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
@@ -278,11 +284,14 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   const int hb = p.io == SSD_BF16;
   void* CB = ws + l.CB;
   void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
-  // C.B^T needs only B and C: it runs on the side stream beside the cumsum and
-  // chunk states (one kernel on the bf16 path) and the state passing; the chunk
-  // scan waits for it.
+  // Where the chunk-state kernel forms C.B^T itself (it stages every B slice of
+  // the chunk already), the call is three kernels on `stream`.  Otherwise C.B^T,
+  // which needs only B and C, runs on the side stream beside the cumsum and chunk
+  // states (one kernel on the bf16 path) and the state passing; the chunk scan
+  // waits for it.
+  const bool cb_fused = cb_in_chunk_state(p);
   std::unique_lock<std::mutex> lane_lock;
-  SideLane* side = (!only && p.nck > 0) ? side_lane(st, lane_lock) : nullptr;
+  SideLane* side = (!only && p.nck > 0 && !cb_fused) ? side_lane(st, lane_lock) : nullptr;
   if (side) {  // events: 0 fork, 1 C.B^T done
     SSD_TRY(hipEventRecord(side->ev[0], st));
     SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
@@ -290,12 +299,13 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
     SSD_TRY(hipEventRecord(side->ev[1], side->stream));
   }
   if (!only || only == 1)
-    SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st));
+    SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st,
+                                      cb_fused ? C : nullptr, CB, CBt));
   if (!only || only == 2)
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
   if (side) {
     SSD_TRY(hipStreamWaitEvent(st, side->ev[1], 0));
-  } else if (!only || only == 3) {
+  } else if ((!only || only == 3) && !cb_fused) {
     SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
   }
   if (!only || only == 4) SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
@@ -336,9 +346,11 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   float* U = (float*)(ws + l.U);
   void* dE = ws + l.dE;
   if (!(p.flags & SSD_FLAG_FROM_SAVED)) {  // forward intermediates, recomputed
-    SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st));
+    const bool cb_fused = cb_in_chunk_state(p);
+    SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st,
+                                      cb_fused ? C : nullptr, CB, CBt));
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, nullptr, 0, st));
-    SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
+    if (!cb_fused) SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
   }
   BwdArgs a;
   a.x = x; a.B = B; a.C = C; a.dout = dout;

@@ -36,9 +36,15 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
 // Stages 1 and 2 together: delta, acs and the chunk decays are written as
 // launch_chunk_cumsum writes them (bit for bit), and the chunk states T.  One
 // kernel on the bf16 path; the two kernels one after the other on the fp32 path.
+// With C set (only where cb_in_chunk_state(p)), the same kernel also forms
+// C.B^T into CB and, if CBt is set, its transpose, as launch_bmm_chunk does.
 hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* Bm, const float* dt,
                                      const float* dt_bias, const float* A, float* delta, float* acs,
-                                     float* decay, float* T, hipStream_t st);
+                                     float* decay, float* T, hipStream_t st, const void* C = nullptr,
+                                     void* CB = nullptr, void* CBt = nullptr);
+// Whether the chunk-state kernel forms C.B^T for this problem (so that no
+// separate C.B^T kernel is launched).
+bool cb_in_chunk_state(const Prob& p);
 // passed: fp32, or bf16 when passed_bf16 (the carry and final_states stay fp32)
 hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
                                 const float* init, void* passed, int passed_bf16,

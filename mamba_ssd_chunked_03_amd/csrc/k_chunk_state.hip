@@ -50,6 +50,10 @@ struct CumsumIn {
   const float *dt, *dt_bias, *A;
   int softplus;
   float* decay;
+  // C.B^T formed here too when C is set (two heads per workgroup, a group's
+  // head pairs one per 64-row block of the chunk): CB[i][j], and CBt[j][i] if set
+  const uint16_t* C;
+  uint16_t *CB, *CBt;
 };
 
 template <int P, int N, int MODE, int HP>
@@ -72,6 +76,12 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
   __shared__ __attribute__((aligned(16))) uint16_t xl_[HP][KS * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t ys[KS * LDY];
   __shared__ float sc_[HP][256];
+  // C.B^T tile staging (see below): both orientations, so that every store
+  // instruction writes whole 128-byte rows
+  constexpr bool kCanFuseCB = MODE == kStateFwdCumsum && HP == 2;
+  constexpr int LT = 64 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t tcb[kCanFuseCB ? 64 * LT : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t tcbt[kCanFuseCB ? 64 * LT : 1];
 
   int k, h;
   chunk_head(H / HP, k, h);
@@ -144,6 +154,23 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
   // below, and waiting for them would then wait for the slice too)
   __builtin_amdgcn_sched_barrier(0);
   load_slice(0);  // independent of the token scales: in flight while they are formed
+  // C.B^T (kStateFwdCumsum with two heads): this workgroup's head pair is pair ib
+  // of its group, and it forms row block ib (rows 64 ib .. 64 ib + 63) of the
+  // chunk's C.B^T from each staged B slice j <= ib: wave w8 owns rows
+  // 64 ib + 16 (w8 % 4) + 0..15 and columns 32 (w8 / 4) .. +31 of each 64 x 64
+  // tile, and holds its 16 C rows as MFMA fragments for the whole chunk.
+  const bool fuse_cb = kCanFuseCB && cs.C != nullptr;
+  const int lq = lane >> 4, w8 = gid >> 6, ri = w8 & 3, cj = w8 >> 2;
+  const int ib = ((h % (H / G)) / HP);
+  u32x4 cfr[N / 32];
+  if constexpr (kCanFuseCB) {
+    if (fuse_cb) {
+      const brsrc rcm = make_rsrc(cs.C + (int64_t)ci.start * yrow + (int64_t)g * N, (uint32_t)(len * yrow * 2));
+      const uint32_t co = (uint32_t)(ib * 64 + ri * 16 + r) * (uint32_t)(yrow * 2) + lq * 16;
+#pragma unroll
+      for (int kk = 0; kk < N / 32; ++kk) cfr[kk] = buf_load16(rcm, co + 64 * kk);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);  // (and all issued before the first wait)
   if constexpr (MODE == kStateFwdCumsum) {
     __shared__ float wtot_[HP][4], alast_[HP];
@@ -213,6 +240,37 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
           acc[i][jj] = mfma_bf16(bv[jj], ah[i], acc[i][jj]);
           acc[i][jj] = mfma_bf16(bv[jj], al[i], acc[i][jj]);
         }
+    }
+    if constexpr (kCanFuseCB) {
+      // tile (ib, s0 / 64) of C.B^T from this slice of B (rows of ys, dstate
+      // contiguous, so the fragments are plain 16-byte LDS reads).  Both
+      // orientations come from the MFMA: with B as the first operand, lane
+      // (lq, r) holds CB[i = r][j = 4 lq .. +3] of its 16 x 16 block, with C
+      // first CB[i = 4 lq .. +3][j = r], i.e. CBt[j][i .. i + 3].  The two
+      // 64 x 64 tiles go through LDS, then each thread stores one 16-byte piece
+      // of each: every store instruction writes 8 whole 128-byte rows.
+      if (fuse_cb && s0 / KS <= ib) {
+        const int il = ri * 16;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+          const int jl = cj * 32 + bj * 16;
+          f32x4 d1 = f32x4{0.f, 0.f, 0.f, 0.f}, d2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < N / 32; ++kk) {
+            const bf16x8 bfr = as_bf16x8(*(const u32x4*)(ys + (jl + r) * LDY + kk * 32 + lq * 8));
+            d1 = mfma_bf16(bfr, as_bf16x8(cfr[kk]), d1);
+            d2 = mfma_bf16(as_bf16x8(cfr[kk]), bfr, d2);
+          }
+          *(uint2*)(tcb + (il + r) * LT + jl + 4 * lq) = make_uint2(pack_bf2(d1[0], d1[1]), pack_bf2(d1[2], d1[3]));
+          *(uint2*)(tcbt + (jl + r) * LT + il + 4 * lq) = make_uint2(pack_bf2(d2[0], d2[1]), pack_bf2(d2[2], d2[3]));
+        }
+        __syncthreads();
+        const int64_t kg = (int64_t)k * G + g;
+        const int row = gid >> 3, c16 = gid & 7;  // 512 threads: 64 rows x 8 pieces
+        *(u32x4*)(cs.CB + (kg * Q + ib * 64 + row) * Q + s0 + c16 * 8) = *(const u32x4*)(tcb + row * LT + c16 * 8);
+        if (cs.CBt)
+          *(u32x4*)(cs.CBt + (kg * Q + s0 + row) * Q + ib * 64 + c16 * 8) = *(const u32x4*)(tcbt + row * LT + c16 * 8);
+      }
     }
     __syncthreads();
   }
@@ -287,6 +345,7 @@ static void launch_cs_bf16(const Prob& p, const void* X, const void* Y, float* d
   if constexpr (two_ok) {
     if ((p.H / p.G) % 2 == 0) return launch_cs_hp<P, N, 2>(p, X, Y, delta, acs, out, mode, cs, st);
   }
+  if (cs.C) return;  // C.B^T is formed only by the two-head kernel (cb_in_chunk_state)
   launch_cs_hp<P, N, 1>(p, X, Y, delta, acs, out, mode, cs, st);
 }
 
@@ -314,16 +373,27 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
   return launch_cs(p, X, Y, const_cast<float*>(delta), const_cast<float*>(acs), out, mode, CumsumIn{}, st);
 }
 
+bool cb_in_chunk_state(const Prob& p) {
+  // bf16, chunks of four 64-row blocks, and two heads per workgroup with four
+  // head pairs per group (launch_cs_bf16's two-head condition)
+  return p.io == 1 && p.Q == 256 && p.G > 0 && p.H / p.G == 8 && (64 * (p.N / 8)) % 512 == 0 &&
+         cs_lds_bytes(p.P, p.N, 2) <= 80 * 1024;
+}
+
 hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* Bm, const float* dt,
                                      const float* dt_bias, const float* A, float* delta, float* acs,
-                                     float* decay, float* T, hipStream_t st) {
+                                     float* decay, float* T, hipStream_t st, const void* C, void* CB,
+                                     void* CBt) {
   if (p.nck == 0) return hipSuccess;
+  if (C && !cb_in_chunk_state(p)) return hipErrorInvalidValue;
   if (p.io == 0 || p.Q > 256) {
     const hipError_t e = launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st);
     if (e != hipSuccess) return e;
     return launch_chunk_state(p, X, Bm, delta, acs, T, kStateFwd, st);
   }
-  return launch_cs(p, X, Bm, delta, acs, T, kStateFwdCumsum, CumsumIn{dt, dt_bias, A, p.softplus, decay}, st);
+  const CumsumIn cs{dt, dt_bias, A, p.softplus, decay, (const uint16_t*)C, C ? (uint16_t*)CB : nullptr,
+                    C ? (uint16_t*)CBt : nullptr};
+  return launch_cs(p, X, Bm, delta, acs, T, kStateFwdCumsum, cs, st);
 }
 
 }  // namespace ssd

@@ -49,6 +49,7 @@ def FLAG_FWD_KERNEL(k):
 
 _SIGS = {
     "ssd_abi_version": ([], _I32),
+    "ssd_fwd_kernel_mask": ([_P, _I32, _I32], _I32),
     "ssd_status_string": ([_I32], ctypes.c_char_p),
     "ssd_num_chunks": ([_P, _I32, _I32], _I64),
     "ssd_fwd_workspace_bytes": ([_P, _I32, _I32], _SZ),
@@ -68,7 +69,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lib = None
 
