@@ -231,3 +231,19 @@ def test_norm_pointers(L):
     # no rows: nothing to do, no data pointers needed
     p0 = nprob(rows=0)
     assert L.ssd_gated_rmsnorm_fwd(ctypes.byref(p0), None, None, FAKE, None, None, None) == OK
+
+
+def test_fwd_kernel_mask(L):
+    # the chunk-state kernel forms C.B^T where each head pair of a group owns one
+    # 64-row block of the chunk: bf16, chunk 256, eight heads per group
+    layer = dict(batch=2, seqlen=8192, nheads=64, headdim=64, dstate=128, ngroups=8, io_dtype=1)
+    mask = lambda Q=256, packed=0, **kw: L.ssd_fwd_kernel_mask(ctypes.byref(prob(**{**layer, **kw})), Q, packed)
+    assert mask() == 0xB
+    assert mask(nheads=32, ngroups=4, seqlen=131072, batch=1) == 0xB   # long-context shape
+    assert mask(batch=1, seqlen=65536, nseq=8, packed=1) == 0xB         # packed sequences
+    assert mask(dstate=64) == 0xB
+    assert mask(Q=128) == 0xF and mask(Q=64) == 0xF                    # fewer row blocks than pairs
+    assert mask(ngroups=16) == 0xF and mask(ngroups=4) == 0xF          # 4 or 16 heads per group
+    assert mask(io_dtype=0) == 0xF                                      # fp32 path
+    assert mask(headdim=128) == 0xF                                     # one head per workgroup
+    assert mask(nheads=-1) == 0                                         # invalid problem
