@@ -961,22 +961,26 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
   const float d0v = buf_load_f32(make_rsrc(ddd + kh * Q, rowb), ot);
   const float dtv = buf_load_f32(make_rsrc(dt + (int64_t)ci.start * H + h, rowb * (uint32_t)H),
                                  in ? (uint32_t)t * (uint32_t)H * 4u : 0x80000000u);
+  // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
+  // (the others get an offset past the range: no memory access)
+  const int tt = t / 64, tlast = (len - 1) / 64;
   const brsrc rrp = make_rsrc(Rp + kh * ntile * Q, (uint32_t)(ntile * Q * 4));
   const brsrc rkp = make_rsrc(Kp + kh * ntile * Q, (uint32_t)(ntile * Q * 4));
   float rp[4], kp[4];
+  bool ur[4], uk[4];
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) {
-    rp[tl] = buf_load_f32(rrp, ot + (uint32_t)(tl * Q * 4));
-    kp[tl] = buf_load_f32(rkp, ot + (uint32_t)(tl * Q * 4));
+    ur[tl] = tl <= tt && tl < ntile;
+    uk[tl] = tl >= tt && tl <= tlast && tl < ntile;
+    rp[tl] = buf_load_f32(rrp, ur[tl] ? ot + (uint32_t)(tl * Q * 4) : 0x80000000u);
+    kp[tl] = buf_load_f32(rkp, uk[tl] ? ot + (uint32_t)(tl * Q * 4) : 0x80000000u);
   }
   const float lt = last_term[kh];
   float v = r0 - k0 + (t == len - 1 ? lt : 0.f);
-  // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
-  const int tt = t / 64, tlast = (len - 1) / 64;
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl) v = (tl <= tt && tl < ntile) ? v + rp[tl] : v;
+  for (int tl = 0; tl < 4; ++tl) v = ur[tl] ? v + rp[tl] : v;
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl) v = (tl >= tt && tl <= tlast && tl < ntile) ? v - kp[tl] : v;
+  for (int tl = 0; tl < 4; ++tl) v = uk[tl] ? v - kp[tl] : v;
   v = in ? v : 0.f;
   const float dl = in ? dlv : 0.f, d0 = in ? d0v : 0.f, z = in ? dtv + bias : 0.f;
   const float sw = wave_inclusive_sum(v);
