@@ -61,6 +61,11 @@ CASES = [
     # workgroup take their one-head form here
     ("bf16_odd_heads", dict(batch=1, seqlen=420, nheads=3, headdim=64, dstate=128, ngroups=1,
                             io="bf16", init="randn", seed=56), (256,)),
+    # eight heads per group: at chunk 256 the chunk-state kernel forms C.B^T and its
+    # transpose (the backward's recompute and dx read them); at 128 the separate kernel does
+    ("bf16_cb_in_chunk_state", dict(batch=2, seqlen=700, nheads=16, headdim=64, dstate=128,
+                                    ngroups=2, io="bf16", init="randn", seed=57, d_final=True),
+     (128, 256)),
     ("f32_cfg0_shape", dict(batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, ngroups=1,
                             io="f32", dt_mode="direct", init="none", seed=0), (64,)),
     ("f32_ragged", dict(batch=2, seqlen=150, nheads=2, headdim=16, dstate=32, ngroups=1,

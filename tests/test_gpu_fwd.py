@@ -248,3 +248,80 @@ def test_fused_cumsum_matches_stage(kw, lengths, Q):
     assert torch.equal(w_delta[live], delta[live])
     assert torch.equal(w_acs[live], acs[live])
     assert torch.equal(w_decay[live], decay[live])
+
+
+def _up(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("lengths", [None, [300, 0, 513, 77]], ids=["batched", "packed"])
+def test_cb_in_chunk_state_matches_stage_kernel(lengths):
+    """Where the chunk-state kernel forms C.B^T (8 heads per group, chunk 256), the
+    C.B^T and its transpose that a saving forward leaves in the workspace equal,
+    bit for bit, what the separate C.B^T stage kernel computes, on every 64 x 64
+    lower tile that starts inside its chunk.  The workspace offsets follow the
+    saved-context layout: delta, acs (nck, H, Q), decay (nck, H), chunk states
+    (nck, H, P, N) fp32, passed states in bf16, C.B^T (nck, G, Q, Q) bf16, then
+    (backward part) its transpose, each rounded up to 256 bytes."""
+    H, P, N, G, Q = 16, 64, 128, 2, 256
+    kw = dict(nheads=H, headdim=P, dstate=N, ngroups=G, io="bf16", init="randn", seed=51)
+    if lengths is None:
+        inp = inputs.make_inputs(batch=2, seqlen=700, **kw)
+    else:
+        inp = inputs.make_inputs(batch=1, seqlen=sum(lengths), lengths=lengths, **kw)
+    d = to_dev(inp)
+    prob = ssd.problem(d["x"], d["B"], d["cu_seqlens"])
+    packed = int(lengths is not None)
+    assert ssd.lib().ssd_fwd_kernel_mask(ctypes.byref(prob), Q, packed) == 0xB
+    nck = ssd.num_chunks(prob, Q, packed)
+    ws = torch.zeros(ssd.lib().ssd_bwd_workspace_bytes(ctypes.byref(prob), Q, packed),
+                     dtype=torch.uint8, device="cuda")
+    ssd.fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], dt_bias=d["dt_bias"], init=d["init"],
+            cu_seqlens=d["cu_seqlens"], chunk_size=Q, dt_softplus=inp["dt_softplus"], workspace=ws,
+            save_for_backward=True)
+    st = ssd.Stages(d["x"], d["B"], d["cu_seqlens"], Q, inp["dt_softplus"])
+    ref = st.bmm_chunk(d["B"], d["C"])
+    torch.cuda.synchronize()
+    o = 0
+    if packed:
+        o += _up(nck * 16) + _up((len(lengths) + 1) * 4)
+    o += 2 * _up(nck * H * Q * 4) + _up(nck * H * 4) + _up(nck * H * P * N * 4) + _up(nck * H * P * N * 2)
+    ncb = nck * G * Q * Q
+    cb = ws[o:o + ncb * 2].view(torch.int16).view(nck, G, Q, Q).cpu()
+    o += _up(ncb * 2)
+    cbt = ws[o:o + ncb * 2].view(torch.int16).view(nck, G, Q, Q).cpu()
+    ref = ref.view(torch.int16).cpu()
+    # chunk lengths: batched rows cut from their first token, packed sequences likewise
+    lens = []
+    if packed:
+        for n in lengths:
+            lens += [min(Q, n - c * Q) for c in range((n + Q - 1) // Q)]
+    else:
+        lens = [min(Q, 700 - c * Q) for c in range((700 + Q - 1) // Q)] * 2
+    assert len(lens) <= nck
+    checked = 0
+    for k, n in enumerate(lens):
+        for ti in range(Q // 64):
+            if ti * 64 >= n:
+                continue
+            for tj in range(ti + 1):
+                rs, cs = slice(ti * 64, ti * 64 + 64), slice(tj * 64, tj * 64 + 64)
+                assert torch.equal(cb[k, :, rs, cs], ref[k, :, rs, cs]), (k, ti, tj)
+                assert torch.equal(cbt[k, :, cs, rs].transpose(-1, -2), ref[k, :, rs, cs]), (k, ti, tj)
+                checked += 1
+    assert checked > 0
+
+
+FUSED_CB = dict(nheads=16, headdim=64, dstate=128, ngroups=2, io="bf16", init="randn")
+
+
+@pytest.mark.parametrize("lengths", [None, [300, 0, 513, 77]], ids=["batched", "packed"])
+def test_fwd_cb_in_chunk_state(lengths):
+    """End to end against the oracle on a shape whose chunk-state kernel forms C.B^T."""
+    if lengths is None:
+        inp = inputs.make_inputs(batch=2, seqlen=700, seed=52, **FUSED_CB)
+    else:
+        inp = inputs.make_inputs(batch=1, seqlen=sum(lengths), lengths=lengths, seed=53, **FUSED_CB)
+    y, final = gpu_fwd(ssd, inp, 256)
+    torch.cuda.synchronize()
+    check_fwd(inp, y, final, "bf16", "cb_in_chunk_state")
