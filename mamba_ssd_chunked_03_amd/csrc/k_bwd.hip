@@ -115,14 +115,15 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   float dot = 0.f;
   {
     constexpr int NT = kDxWaves * 64, NC = (P * N / 8 + NT - 1) / NT;
-    const uint16_t* de = dE + kh * (int64_t)(P * N);
-    const uint16_t* hh = Hs + kh * (int64_t)(P * N);
+    const brsrc rde = make_rsrc(dE + kh * (int64_t)(P * N), (uint32_t)(P * N * 2));
+    const brsrc rhh = make_rsrc(Hs + kh * (int64_t)(P * N), (uint32_t)(P * N * 2));
     u32x4 ta[NC], tb[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = (tid + c * NT) * 8;
-      ta[c] = (e < P * N) ? *(const u32x4*)(de + e) : u32x4{0u, 0u, 0u, 0u};
-      tb[c] = (e < P * N) ? *(const u32x4*)(hh + e) : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t off = e < P * N ? (uint32_t)e * 2u : 0x80000000u;
+      ta[c] = buf_load16(rde, off);
+      tb[c] = buf_load16(rhh, off);
     }
     ytile.store(dyt, LDY, tid);
     if (tid < Q) {
@@ -581,16 +582,17 @@ __global__ __launch_bounds__(256, 3) void bwd_dc_bf16_kernel(
   float pa = 0.f;
   auto load_head = [&](int h) {
     const int64_t kh = (int64_t)k * H + h;
-    const uint16_t* src = Hs + kh * (int64_t)(P * N);
+    // range-checked loads, no branches (rows past the chunk's end read zero)
+    const brsrc rh = make_rsrc(Hs + kh * (int64_t)(P * N), (uint32_t)(P * N * 2));
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
       const int e = (tid + c * 256) * 8;
-      ph[c] = e < P * N ? *(const u32x4*)(src + e) : u32x4{0u, 0u, 0u, 0u};
+      ph[c] = buf_load16(rh, e < P * N ? (uint32_t)e * 2u : 0x80000000u);
     }
     const brsrc rdy = make_rsrc(DY + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb) py[kb] = buf_load16(rdy, yo + 64 * kb);
-    pa = irow < len ? acs[kh * Q + irow] : 0.f;
+    pa = buf_load_f32(make_rsrc(acs + kh * Q, (uint32_t)(len * 4)), (uint32_t)irow * 4u);
   };
   __syncthreads();  // every wave is done with the B pieces in ub[0]
   load_head(g * hpg);
@@ -705,18 +707,20 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   float pl = 0.f, pj = 0.f, pd = 0.f;
   auto load_head = [&](int h) {
     const int64_t kh = (int64_t)k * H + h;
-    const uint16_t* src = dE + kh * (int64_t)(P * N);
+    // range-checked loads, no branches (rows past the chunk's end read zero)
+    const brsrc rh = make_rsrc(dE + kh * (int64_t)(P * N), (uint32_t)(P * N * 2));
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
       const int e = (tid + c * 256) * 8;
-      ph[c] = e < P * N ? *(const u32x4*)(src + e) : u32x4{0u, 0u, 0u, 0u};
+      ph[c] = buf_load16(rh, e < P * N ? (uint32_t)e * 2u : 0x80000000u);
     }
     const brsrc rxh = make_rsrc(X + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
 #pragma unroll
     for (int kb = 0; kb < P / 32; ++kb) px[kb] = buf_load16(rxh, xo + 64 * kb);
-    pl = acs[kh * Q + len - 1];
-    pj = rowok ? acs[kh * Q + jrow] : 0.f;
-    pd = rowok ? delta[kh * Q + jrow] : 0.f;
+    const brsrc ra = make_rsrc(acs + kh * Q, (uint32_t)(len * 4));
+    pl = buf_load_f32(ra, (uint32_t)(len - 1) * 4u);
+    pj = buf_load_f32(ra, (uint32_t)jrow * 4u);
+    pd = buf_load_f32(make_rsrc(delta + kh * Q, (uint32_t)(len * 4)), (uint32_t)jrow * 4u);
   };
   __syncthreads();  // every wave is done with the C pieces in ub[0]
   load_head(g * hpg);
