@@ -394,12 +394,35 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
   // so that its per-element factor is rho_i gam_j (a diagonal tile takes one
   // exp per element).  Called at the start of each block of 8 heads: the
   // previous block's readers are done (the column reduction ends in a barrier).
+  // Every value of the block is loaded before the first is stored (range-checked
+  // buffer loads, no branches: a load-then-store loop would wait for each load
+  // in turn), and every slot of sv is written (slots of heads past the group's
+  // end get zeros and are never read).
   auto fill_sv = [&](int h0, int nh) {
-    for (int e = tid; e < nh * 192; e += 256) {
-      const int sl = e / 192, c = e % 192;
-      const int64_t khs = (int64_t)k * H + h0 + sl;
-      const int t = (c < 64) ? ti * 64 + c : jt0 + (c % 64);  // < Q: inside the workspace
-      sv[sl][c] = (c < 128) ? acs[khs * Q + t] : delta[khs * Q + t];
+    const int64_t kh0 = (int64_t)k * H + h0;
+    const brsrc ra = make_rsrc(acs + kh0 * Q, (uint32_t)(nh * Q * 4));
+    const brsrc rd = make_rsrc(delta + kh0 * Q, (uint32_t)(nh * Q * 4));
+    float va[4], vd[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // acs of the tile's rows [0, 64) and columns [64, 128): 8 x 128
+      const int e = tid + u * 256, sl = e >> 7, c = e & 127;
+      const int t = (c < 64) ? ti * 64 + c : jt0 + (c - 64);  // < Q: inside the workspace
+      va[u] = buf_load_f32(ra, (uint32_t)(sl * Q + t) * 4u);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // delta of its columns [128, 192): 8 x 64
+      const int e = tid + u * 256, sl = e >> 6, c = e & 63;
+      vd[u] = buf_load_f32(rd, (uint32_t)(sl * Q + jt0 + c) * 4u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + u * 256;
+      sv[e >> 7][e & 127] = va[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + u * 256;
+      sv[e >> 6][128 + (e & 63)] = vd[u];
     }
     if (!diag) {
       __syncthreads();
@@ -416,12 +439,13 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
     const int h = g * hpg + hh;
     const int64_t kh = (int64_t)k * H + h;
     uint16_t* xbuf = xt[hh & 1];
+    // (the block's decay values are loaded while this head's rows are in flight)
+    if ((hh & 7) == 0) fill_sv(h, min(8, hpg - hh));
 #pragma unroll
     for (int c = 0; c < NPX; ++c) {
       const int e = tid + c * 256, row = e / PER, c8 = e % PER;
       *(u32x4*)(xbuf + row * LX + c8 * 8) = px[c];
     }
-    if ((hh & 7) == 0) fill_sv(h, min(8, hpg - hh));
     __syncthreads();
     bf16x8 af[P / 32];
 #pragma unroll
