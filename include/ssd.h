@@ -38,7 +38,8 @@
  *    it and the call returns before it runs; keep buffers alive until then.
  *    ssd_fwd and ssd_bwd run kernels that do not depend on each other on a second
  *    stream of the library's own (one per device, created on first use, default
- *    priority), forked from and joined back to `stream` with events: the call as a
+ *    priority; ssd_fwd has none where its chunk-state kernel forms C.B^T, see
+ *    ssd_fwd_kernel_mask), forked from and joined back to `stream` with events: the call as a
  *    whole stays ordered on `stream`, and it can be captured into a HIP graph.
  *    Calls issued on different streams at the same time share that second stream
  *    (they stay correct; their side kernels queue behind each other).  The second
