@@ -30,13 +30,19 @@
 // with the same bits.  They are written for the later stages, and the token
 // scales are formed from the values in registers (no second read).
 //
+// With two heads per workgroup, kStateFwdCumsum can also form the chunk's
+// C.B^T (the input of the output stage) from the same staged B slices: where a
+// group's head pairs are as many as the chunk's 64-row blocks (8 heads per group,
+// chunk 256), pair ib forms row block ib, in both orientations (the backward
+// reads the transpose), and no separate C.B^T kernel runs.
+//
 // fp32 path: one thread per output element, plain FMA loop (correctness path
 // for fp32 inputs; no rounding of any operand).
 #include "internal.hpp"
 
 namespace ssd {
 
-constexpr int QMAX_STATE = 256;  // largest chunk size
+constexpr int QMAX_STATE = 256;  // largest chunk size: one token per thread of a head
 
 __device__ __forceinline__ float token_scale(int mode, const float* dl, const float* ac, int j,
                                              float a_last) {
@@ -134,7 +140,6 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
   // The other modes load this thread's acs (and delta, and the chunk's last acs)
   // the same way.  Range-checked buffer loads: tokens past the chunk's end read
   // as zero, with no branch.
-  static_assert(QMAX_STATE <= 256, "one token per thread of a head");
   const int t = tid;
   const bool in = t < len;
   float dtv = 0.f, acv = 0.f, dlv = 0.f, alv = 0.f;
@@ -369,6 +374,7 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
                        mode, (const float*)X, (const float*)Y, delta, acs, out);
     return hipGetLastError();
   }
+  if (p.Q > QMAX_STATE) return hipErrorInvalidValue;  // one token per thread
   // (the kStateFwd and kStateDstates modes only read delta and acs)
   return launch_cs(p, X, Y, const_cast<float*>(delta), const_cast<float*>(acs), out, mode, CumsumIn{}, st);
 }
