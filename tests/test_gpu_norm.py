@@ -101,3 +101,14 @@ def test_norm_no_rows():
     dy, dz, dw = ssd.gated_rmsnorm_bwd(y, y, y, w, 512, grads=(torch.empty_like(y), torch.empty_like(y), dw))
     torch.cuda.synchronize()
     assert out.shape == (0, 1024) and torch.count_nonzero(dw).item() == 0
+
+
+@pytest.mark.parametrize("pieces", [1, 255, 256, 1000003])
+def test_util_copy(pieces):
+    """The plain copy kernel (counter calibration): every byte copied, nothing past the end."""
+    src = torch.randint(-2**31, 2**31 - 1, (pieces * 4 + 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    ssd.util_copy(dst[:pieces * 4], src[:pieces * 4])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:pieces * 4], src[:pieces * 4])
+    assert torch.equal(dst[pieces * 4:], torch.zeros(4, dtype=torch.int32, device="cuda"))
