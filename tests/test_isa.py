@@ -1,0 +1,88 @@
+"""Host-side check of the compiled gfx950 code of the step's kernels: no load is
+followed at once by a wait for every outstanding load at a branch join.
+
+That pattern appears when a load sits under a branch whose other path writes a
+zero into the same register (the zero's move must wait for the load in
+flight), and it serialises a tile's loads: a prologue meant to cost one memory
+latency then costs one per load.  The kernels load such tiles through
+range-checked buffer resources instead; this test keeps it that way.  It only
+compiles (hipcc -S, no GPU).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mamba_ssd_chunked_03_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# (source, kernel symbol prefix) at the layer workload's shapes (headdim 64, dstate 128)
+KERNELS = [
+    ("k_chunk_scan.hip", "_ZN3ssd22chunk_scan_bf16_kernelILi64ELi128EtEE"),
+    ("k_chunk_state.hip", "_ZN3ssd23chunk_state_bf16_kernelILi64ELi128ELi2ELi2EEE"),  # forward, cumsum + C.B^T
+    ("k_chunk_state.hip", "_ZN3ssd23chunk_state_bf16_kernelILi64ELi128ELi1ELi2EEE"),  # adjoint states
+    ("k_bwd.hip", "_ZN3ssd18bwd_dx_bf16_kernelILi64ELi128EEE"),
+    ("k_bwd.hip", "_ZN3ssd19bwd_dcb_bf16_kernelILi64EEE"),
+    ("k_bwd.hip", "_ZN3ssd18bwd_dc_bf16_kernelILi64ELi128EEE"),
+    ("k_bwd.hip", "_ZN3ssd18bwd_db_bf16_kernelILi64ELi128EEE"),
+    ("k_bwd.hip", "_ZN3ssd19bwd_finalize_kernelE"),
+]
+
+_asm = {}
+
+
+def assembly(src, tmp):
+    if src not in _asm:
+        out = os.path.join(tmp, src + ".s")
+        cmd = [HIPCC, "-x", "hip", "-S", "--offload-device-only", os.path.join(CSRC, src), "-o", out,
+               "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        _asm[src] = open(out).read().split("\n")
+    return _asm[src]
+
+
+def kernel_lines(lines, prefix):
+    out, on = [], False
+    for l in lines:
+        if not on and l.startswith(prefix) and l.split(":")[0].startswith(prefix) and ":" in l:
+            on = True
+        if on:
+            out.append(l)
+            if l.startswith(".Lfunc_end"):
+                break
+    return out
+
+
+@pytest.fixture(scope="module")
+def tmpdir_mod(tmp_path_factory):
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    return str(tmp_path_factory.mktemp("isa"))
+
+
+@pytest.mark.parametrize("src,prefix", KERNELS, ids=[k[1][5:40] for k in KERNELS])
+def test_no_load_then_full_wait_at_branch_join(src, prefix, tmpdir_mod):
+    body = kernel_lines(assembly(src, tmpdir_mod), prefix)
+    assert len(body) > 100, "kernel %s not found in %s" % (prefix, src)
+    bad = []
+    for i, l in enumerate(body):
+        if re.search(r"\b(global|buffer)_load", l):
+            nxt = body[i + 1:i + 4]
+            if any("s_waitcnt vmcnt(0)" in n for n in nxt[:1]) and any(n.startswith(".LBB") for n in nxt):
+                bad.append(i)
+            # inside a loop, a load whose value is waited for (all loads) and stored to
+            # LDS before the next load is issued: one memory latency per value
+            if any("in Loop" in b for b in body[max(0, i - 40):i]):
+                for j in range(i + 1, min(i + 14, len(body))):
+                    if re.search(r"\b(global|buffer)_load", body[j]):
+                        break
+                    if "s_waitcnt" in body[j] and "vmcnt" in body[j]:
+                        if "vmcnt(0)" in body[j] and any("ds_write" in n for n in body[j + 1:j + 3]):
+                            bad.append(i)
+                        break
+    assert not bad, "%s: serialised loads at lines %s" % (prefix, bad[:5])
