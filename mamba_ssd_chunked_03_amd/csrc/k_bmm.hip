@@ -40,6 +40,10 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
   const uint16_t* bb0 = Sm + (int64_t)ci.start * row + (int64_t)g * N;
   uint16_t* out = CB + ((int64_t)k * G + g) * Q * Q;
   uint16_t* tl = tls[w];
+  // range-checked buffer loads over the chunk's valid rows (rows past its end read
+  // as zero, with no branch: a load under a branch can leave its register shared
+  // with the other path's zero, whose move then waits for the load)
+  const brsrc rcr = make_rsrc(cb0, (uint32_t)(ci.len * row * 2)), rbr = make_rsrc(bb0, (uint32_t)(ci.len * row * 2));
   for (int tile = w; tile < ntiles; tile += 4) {
     int lo = 0;
     while ((lo + 1) * (lo + 2) / 2 <= tile) ++lo;
@@ -56,11 +60,10 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
       bf16x8 af[4], bf[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int i = ti * 64 + a * 16 + r;
-        const int j = tj * 64 + a * 16 + r;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        af[a] = as_bf16x8(i < ci.len ? *(const u32x4*)(cb0 + (int64_t)i * row + kk + q * 8) : z);
-        bf[a] = as_bf16x8(j < ci.len ? *(const u32x4*)(bb0 + (int64_t)j * row + kk + q * 8) : z);
+        const uint32_t i = ti * 64 + a * 16 + r;
+        const uint32_t j = tj * 64 + a * 16 + r;
+        af[a] = as_bf16x8(buf_load16(rcr, i * (uint32_t)(row * 2) + (kk + q * 8) * 2));
+        bf[a] = as_bf16x8(buf_load16(rbr, j * (uint32_t)(row * 2) + (kk + q * 8) * 2));
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)

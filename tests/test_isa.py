@@ -29,6 +29,7 @@ KERNELS = [
     ("k_bwd.hip", "_ZN3ssd18bwd_dc_bf16_kernelILi64ELi128EEE"),
     ("k_bwd.hip", "_ZN3ssd18bwd_db_bf16_kernelILi64ELi128EEE"),
     ("k_bwd.hip", "_ZN3ssd19bwd_finalize_kernelE"),
+    ("k_bmm.hip", "_ZN3ssd21bmm_chunk_bf16_kernelILi128ELb1EEE"),  # shapes without C.B^T in chunk_state
 ]
 
 _asm = {}
