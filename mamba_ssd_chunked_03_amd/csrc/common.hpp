@@ -182,40 +182,18 @@ __device__ __forceinline__ u32x4 pack_bf8(f32x4 a, f32x4 b) {
 }
 
 // --------------------------------------------------------- LDS staging ----
-// Copy ROWS token rows of W bf16 (16-byte pieces) from global rows `src`
-// (stride `srow` elements) into LDS rows `dst` (stride `ld`), in the natural or
-// the permuted column order; rows >= nvalid are zero.  Every load is issued
-// before the first LDS store, so the whole tile costs one memory latency (a
-// loop with a run-time trip count would wait on each load in turn).
-template <int ROWS, int W, int NT = 256, bool PERM = false>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, int ld, const uint16_t* src, int64_t srow,
-                                           int nvalid, int tid) {
-  constexpr int PER = W / 8;
-  constexpr int NC = (ROWS * PER + NT - 1) / NT;
-  static_assert(!PERM || W % 32 == 0, "permuted rows are whole 32-column blocks");
-  u32x4 t[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int e = tid + c * NT, j = e / PER, c8 = e % PER;
-    t[c] = (e < ROWS * PER && j < nvalid) ? *(const u32x4*)(src + (int64_t)j * srow + c8 * 8)
-                                          : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int e = tid + c * NT, j = e / PER, c8 = e % PER;
-    if (e < ROWS * PER) lds_piece<PERM>(dst + j * ld, c8, t[c]);
-  }
-}
-
-// fp32 P x N state (row-major) -> bf16 LDS [p][n] with row stride ld; loads first.
+// fp32 P x N state (row-major) -> bf16 LDS [p][n] with row stride ld; loads first
+// (range-checked buffer loads, no branches).
 template <int P, int N, int NT = 256>
 __device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const float* src, int tid) {
   constexpr int NC = (P * N / 4 + NT - 1) / NT;
+  const brsrc rs = make_rsrc(src, (uint32_t)(P * N * 4));
   float4 t[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int e = (tid + c * NT) * 4;
-    t[c] = (e < P * N) ? *(const float4*)(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const u32x4 v = buf_load16(rs, e < P * N ? (uint32_t)e * 4u : 0x80000000u);
+    t[c] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -228,8 +206,9 @@ __device__ __forceinline__ void stage_state_bf16(uint16_t* dst, int ld, const fl
   }
 }
 
-// stage_rows split in two, so that several tiles' loads (and other loads) can
-// all be in flight before the first LDS store waits for its data.  STREAM
+// A tile of ROWS token rows of W bf16 copied into LDS in two steps (load, then
+// store), so that several tiles' loads (and other loads) can all be in flight
+// before the first LDS store waits for its data.  STREAM
 // marks the loads nontemporal: for a tile that this kernel reads exactly once,
 // it keeps the tile from displacing the operands that other workgroups re-read
 // from the cache.  The loads go through a buffer resource that ends at row
