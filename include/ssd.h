@@ -36,15 +36,19 @@
  *    input.  Outputs must not alias inputs or the workspace.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is queued on
  *    it and the call returns before it runs; keep buffers alive until then.
- *    ssd_fwd and ssd_bwd run kernels that do not depend on each other on a second
- *    stream of the library's own (one per device, created on first use, default
- *    priority; ssd_fwd has none where its chunk-state kernel forms C.B^T, see
- *    ssd_fwd_kernel_mask), forked from and joined back to `stream` with events: the call as a
- *    whole stays ordered on `stream`, and it can be captured into a HIP graph.
- *    Calls issued on different streams at the same time share that second stream
- *    (they stay correct; their side kernels queue behind each other).  The second
- *    stream belongs to the current device: when `stream` belongs to another
- *    device, the call queues all of its kernels on `stream` alone.
+ *  - State kept across calls: none, except this.  ssd_fwd and ssd_bwd run kernels
+ *    that do not depend on each other on a second stream of the library's own
+ *    (one per device, with three events, created by the first call that uses it,
+ *    default priority, kept until the process ends; ssd_fwd uses none where its
+ *    chunk-state kernel forms C.B^T, see ssd_fwd_kernel_mask), forked from and
+ *    joined back to `stream` with events: the call as a whole stays ordered on
+ *    `stream`, also when a launch fails after the fork, and it can be captured
+ *    into a HIP graph.  Calls issued on different streams at the same time share
+ *    that second stream (they stay correct; their side kernels queue behind each
+ *    other).  The second stream belongs to the current device: when `stream`
+ *    belongs to another device, the call queues all of its kernels on `stream`
+ *    alone, and so does every call with SSD_FLAG_ONE_STREAM, which then creates
+ *    no stream and no event.
  *  - Every error the host can detect (NULL, shape, alignment, workspace size,
  *    unsupported configuration) is returned BEFORE anything is queued.  A failed
  *    launch returns SSD_ERR_HIP.  Nothing is printed; no exception crosses the ABI.
@@ -72,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum {
   SSD_OK = 0,
@@ -97,6 +101,9 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   checks this. */
 #define SSD_FLAG_SAVE_FOR_BWD 1
 #define SSD_FLAG_FROM_SAVED 2
+/* SSD_FLAG_ONE_STREAM: every kernel of the call runs on `stream`; the library
+ *   creates and uses no stream or event of its own.  Results are identical. */
+#define SSD_FLAG_ONE_STREAM 4
 /* SSD_FLAG_BWD_KERNEL(k), k = 1..7: a profiling aid, valid only together with
  *   SSD_FLAG_FROM_SAVED.  ssd_bwd launches only its k-th kernel: 1 adjoint chunk
  *   states, 2 reverse state passing, 3 dx (with the direct delta gradient),
@@ -154,7 +161,16 @@ size_t ssd_stage_workspace_bytes(const ssd_problem* problem, int32_t chunk_size,
 
 /* Forward pass: out = y, final_states = S_last (optional, may be NULL).
  * dt_bias, D, init_states and cu_seqlens may be NULL (zero bias, no skip term,
- * zero initial state, unpacked batch). */
+ * zero initial state, unpacked batch).
+ * What it computes: the selective-SSM recurrence of the scan page
+ * (gigipick.blogspot.com "LLM Mamba ...", section 1), evaluated chunk by chunk:
+ * within-chunk cumsum, chunk states, the cross-chunk carry as an associative
+ * scan (section 2 and its Hillis-Steele pseudo-code; aitrends.kr/articles/109906,
+ * "Helion-based B200 kernel redesign", for _state_passing_fwd), and the per-chunk
+ * output with C.h_prev and the D skip term fused (scan page, section 3, "kernel
+ * fusion" and "memory hierarchy").  One call replaces the whole forward module
+ * (aitrends.kr/articles/109906, "putting autotune results into the training
+ * pipeline": a 1:1 drop-in module). */
 ssd_status ssd_fwd(const ssd_problem* problem,
                    const void* x, const float* dt, const float* dt_bias, const float* A,
                    const void* B, const void* C, const float* D,
@@ -162,7 +178,13 @@ ssd_status ssd_fwd(const ssd_problem* problem,
                    void* out, float* final_states,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward pass for the loss L = <dout, y> + <d_final_states, final>.
+/* Backward pass for the loss L = <dout, y> + <d_final_states, final>: the adjoint
+ * of ssd_fwd's recurrence (scan page, section 1), with the cross-chunk part as the
+ * reverse associative scan that replaces _state_passing_bwd's sequential loop
+ * (aitrends.kr/articles/109906, "Helion-based B200 kernel redesign"), and every
+ * reduction over tokens or heads in a fixed order (the fixed-order tree fold of the
+ * FlashInfer Cake RMSNorm page, "key optimisation techniques"), so results are
+ * bitwise reproducible.
  * Inputs are those of ssd_fwd plus dout and d_final_states (NULL = 0).
  * Outputs: dx, dB, dC (io dtype; dB and dC summed over each group's heads in
  * fp32 before rounding), ddt (w.r.t. the raw dt input), dA (required), and the
@@ -191,30 +213,43 @@ ssd_status ssd_bwd(const ssd_problem* problem,
  *     CB             (nck, ngroups, chunk_size, chunk_size) io dtype: C_i . B_j for
  *                    j <= i (entries above the diagonal are not written)
  */
-/* Stage 1 — per-chunk cumulative sum of delta*A (wavefront prefix sum). */
+/* Stage 1 — per-chunk cumulative sum of delta*A (wavefront prefix sum): the
+ * log-decays of the recurrence (scan page, section 1) summed within each chunk of
+ * the chunked form (scan page, "memory hierarchy": work in chunks whose carry
+ * seeds the next).  dt_bias may be NULL. */
 ssd_status ssd_stage_chunk_cumsum(const ssd_problem* problem, const float* dt,
                                   const float* dt_bias, const float* A,
                                   const int32_t* cu_seqlens, int32_t chunk_size,
                                   float* delta, float* acs, float* chunk_decay,
                                   void* workspace, size_t workspace_bytes, void* stream);
-/* Stage 2 — chunk states T_c = sum_j delta_j exp(acs_last - acs_j) x_j B_j^T (MFMA). */
+/* Stage 2 — chunk states T_c = sum_j delta_j exp(acs_last - acs_j) x_j B_j^T (MFMA):
+ * each chunk's end state from a zero start, the carry-out of the scan page's
+ * "memory hierarchy" section, i.e. the b part of the chunk's pair in section 2. */
 ssd_status ssd_stage_chunk_state(const ssd_problem* problem, const void* x, const void* B,
                                  const float* delta, const float* acs,
                                  const int32_t* cu_seqlens, int32_t chunk_size, float* states,
                                  void* workspace, size_t workspace_bytes, void* stream);
 /* Stage 3 — cross-chunk state passing E_c = exp(chunk_decay_c) H_c + T_c as an
- * associative scan; passed = H_c, final_states = E_last (may be NULL). */
+ * associative scan (scan page, section 2 and its Hillis-Steele pseudo-code;
+ * aitrends.kr/articles/109906, "Helion-based B200 kernel redesign": the sequential
+ * _state_passing_fwd loop turned into an associative scan); passed = H_c,
+ * final_states = E_last (may be NULL).  init_states may be NULL (zero). */
 ssd_status ssd_stage_state_passing(const ssd_problem* problem, const float* states,
                                    const float* chunk_decay, const float* init_states,
                                    const int32_t* cu_seqlens, int32_t chunk_size,
                                    float* passed, float* final_states,
                                    void* workspace, size_t workspace_bytes, void* stream);
-/* Stage 4 — CB = C B^T per chunk and group (MFMA), lower triangle. */
+/* Stage 4 — CB = C B^T per chunk and group (MFMA), lower triangle: the
+ * within-chunk interaction matrix of the chunked form of the recurrence (scan page,
+ * section 1, unrolled over one chunk), shared by the group's heads. */
 ssd_status ssd_stage_bmm_chunk(const ssd_problem* problem, const void* B, const void* C,
                                const int32_t* cu_seqlens, int32_t chunk_size, void* CB,
                                void* workspace, size_t workspace_bytes, void* stream);
 /* Stage 5 — y_i = sum_{j<=i} CB_ij exp(acs_i - acs_j) delta_j x_j
- *               + exp(acs_i) H_c C_i + D x_i   (MFMA, bf16/fp32 store). */
+ *               + exp(acs_i) H_c C_i + D x_i   (MFMA, bf16/fp32 store):
+ * the recurrence's output (scan page, section 1) inside a chunk, seeded by the
+ * carried-in state, with the skip term and the store fused into the same kernel
+ * (scan page, section 3, "kernel fusion").  D may be NULL. */
 ssd_status ssd_stage_chunk_scan(const ssd_problem* problem, const void* x, const void* C,
                                 const void* CB, const float* delta, const float* acs,
                                 const float* passed, const float* D,

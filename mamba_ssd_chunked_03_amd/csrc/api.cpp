@@ -1,8 +1,11 @@
 // C ABI of libssd: argument validation, workspace layout and launch order.
 //
-// Every check the host can make happens before the first launch, so an error
-// return never leaves partial work queued.  The library allocates nothing and
-// keeps no state between calls.
+// Every check the host can make happens before the first launch.  The library
+// allocates no memory.  Its only state across calls is one side stream and three
+// events per device, created at the first call that forks to them and kept until
+// the process ends (side_lane below).  A launch that fails after a call has forked
+// to the side stream still joins it back to the caller's stream before the call
+// returns SSD_ERR_HIP, so whatever was queued stays ordered on the caller's stream.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -32,8 +35,8 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
     return SSD_ERR_SHAPE;
   if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
-  if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_BWD_KERNEL(7) |
-                    SSD_FLAG_FWD_KERNEL(7)))
+  if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_ONE_STREAM |
+                    SSD_FLAG_BWD_KERNEL(7) | SSD_FLAG_FWD_KERNEL(7)))
     return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_BWD_KERNEL(7)) && !(pr->flags & SSD_FLAG_FROM_SAVED))
     return SSD_ERR_UNSUPPORTED;
@@ -200,6 +203,21 @@ SideLane* side_lane(hipStream_t caller, std::unique_lock<std::mutex>& lock) {
     if ((expr) != hipSuccess) return SSD_ERR_HIP; \
   } while (0)
 
+// After a fork to the side stream: on a failed launch, join the side stream back
+// to the caller's stream (event 2) before returning, so that the work already
+// queued there stays ordered on the caller's stream.
+ssd_status join_failed(SideLane* side, hipStream_t st) {
+  if (side) {
+    (void)hipEventRecord(side->ev[2], side->stream);
+    (void)hipStreamWaitEvent(st, side->ev[2], 0);
+  }
+  return SSD_ERR_HIP;
+}
+#define SSD_TRY_FORKED(expr)                                 \
+  do {                                                       \
+    if ((expr) != hipSuccess) return join_failed(side, st);  \
+  } while (0)
+
 bool all_aligned(std::initializer_list<const void*> ps) {
   for (const void* q : ps)
     if (q && !al16(q)) return false;
@@ -291,24 +309,25 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   // waits for it.
   const bool cb_fused = cb_in_chunk_state(p);
   std::unique_lock<std::mutex> lane_lock;
-  SideLane* side = (!only && p.nck > 0 && !cb_fused) ? side_lane(st, lane_lock) : nullptr;
+  const bool one_stream = (p.flags & SSD_FLAG_ONE_STREAM) != 0;
+  SideLane* side = (!only && p.nck > 0 && !cb_fused && !one_stream) ? side_lane(st, lane_lock) : nullptr;
   if (side) {  // events: 0 fork, 1 C.B^T done
-    SSD_TRY(hipEventRecord(side->ev[0], st));
-    SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
-    SSD_TRY(launch_bmm_chunk(p, B, C, CB, side->stream, CBt));
-    SSD_TRY(hipEventRecord(side->ev[1], side->stream));
+    SSD_TRY_FORKED(hipEventRecord(side->ev[0], st));
+    SSD_TRY_FORKED(hipStreamWaitEvent(side->stream, side->ev[0], 0));
+    SSD_TRY_FORKED(launch_bmm_chunk(p, B, C, CB, side->stream, CBt));
+    SSD_TRY_FORKED(hipEventRecord(side->ev[1], side->stream));
   }
   if (!only || only == 1)
-    SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st,
+    SSD_TRY_FORKED(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st,
                                       cb_fused ? C : nullptr, CB, CBt));
   if (!only || only == 2)
-    SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
+    SSD_TRY_FORKED(launch_state_passing(p, T, decay, init_states, Hp, hb, final_states, 0, st));
   if (side) {
-    SSD_TRY(hipStreamWaitEvent(st, side->ev[1], 0));
+    SSD_TRY_FORKED(hipStreamWaitEvent(st, side->ev[1], 0));
   } else if ((!only || only == 3) && !cb_fused) {
-    SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, CBt));
+    SSD_TRY_FORKED(launch_bmm_chunk(p, B, C, CB, st, CBt));
   }
-  if (!only || only == 4) SSD_TRY(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
+  if (!only || only == 4) SSD_TRY_FORKED(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
   return SSD_OK;
 }
 
@@ -370,29 +389,31 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   // beside the adjoint states, the reverse scan and dx; the finalize waits for
   // the side stream.  Each stream then carries about half of the work.
   std::unique_lock<std::mutex> lane_lock;
-  SideLane* side = (!only && p.io == SSD_BF16 && p.nck > 0) ? side_lane(st, lane_lock) : nullptr;
+  const bool one_stream = (p.flags & SSD_FLAG_ONE_STREAM) != 0;
+  SideLane* side =
+      (!only && p.io == SSD_BF16 && p.nck > 0 && !one_stream) ? side_lane(st, lane_lock) : nullptr;
   if (side) {  // events: 0 fork, 1 reverse scan done, 2 side stream done
-    SSD_TRY(hipEventRecord(side->ev[0], st));
-    SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[0], 0));
-    SSD_TRY(launch_bwd_chunk(p, a, 2, side->stream));
-    SSD_TRY(launch_bwd_chunk(p, a, 3, side->stream));
+    SSD_TRY_FORKED(hipEventRecord(side->ev[0], st));
+    SSD_TRY_FORKED(hipStreamWaitEvent(side->stream, side->ev[0], 0));
+    SSD_TRY_FORKED(launch_bwd_chunk(p, a, 2, side->stream));
+    SSD_TRY_FORKED(launch_bwd_chunk(p, a, 3, side->stream));
   }
   // adjoint of the state carried into each chunk, then the reverse scan
   if (!only || only == 1)
-    SSD_TRY(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
+    SSD_TRY_FORKED(launch_chunk_state(p, dout, C, delta, acs, U, kStateDstates, st));
   if (!only || only == 2)
-    SSD_TRY(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
+    SSD_TRY_FORKED(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
   if (side) {
-    SSD_TRY(hipEventRecord(side->ev[1], st));
-    SSD_TRY(hipStreamWaitEvent(side->stream, side->ev[1], 0));
-    SSD_TRY(launch_bwd_chunk(p, a, 4, side->stream));
-    SSD_TRY(hipEventRecord(side->ev[2], side->stream));
-    SSD_TRY(launch_bwd_chunk(p, a, 1, st));
-    SSD_TRY(hipStreamWaitEvent(st, side->ev[2], 0));
+    SSD_TRY_FORKED(hipEventRecord(side->ev[1], st));
+    SSD_TRY_FORKED(hipStreamWaitEvent(side->stream, side->ev[1], 0));
+    SSD_TRY_FORKED(launch_bwd_chunk(p, a, 4, side->stream));
+    SSD_TRY_FORKED(hipEventRecord(side->ev[2], side->stream));
+    SSD_TRY_FORKED(launch_bwd_chunk(p, a, 1, st));
+    SSD_TRY_FORKED(hipStreamWaitEvent(st, side->ev[2], 0));
   } else if (!only || (only >= 3 && only <= 6)) {
-    SSD_TRY(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
+    SSD_TRY_FORKED(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
   }
-  if (!only || only == 7) SSD_TRY(launch_bwd_finalize(p, a, st));
+  if (!only || only == 7) SSD_TRY_FORKED(launch_bwd_finalize(p, a, st));
   return SSD_OK;
 }
 

@@ -28,7 +28,7 @@ class NormProblem(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
 
 
-FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED = 1, 2
+FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED, FLAG_ONE_STREAM = 1, 2, 4
 BWD_KERNELS = ("dstates", "reverse_state_passing", "bwd_dx", "bwd_dcb", "bwd_dc", "bwd_db",
                "bwd_finalize")
 
@@ -69,7 +69,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 
@@ -125,20 +125,65 @@ def _dev(*ts):
     return dev
 
 
-def _f32(t, name):
-    if t is not None and t.dtype != torch.float32:
-        raise ValueError("%s must be float32" % name)
+def _expect(t, name, shape, dtype, required=True):
+    """Raise ValueError unless t (None allowed when not required) has exactly this
+    shape and dtype.  The library sees only pointers, so a tensor of the wrong size
+    or element type would make its kernels read or write past the tensor."""
+    if t is None:
+        if required:
+            raise ValueError("%s is required" % name)
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(int(v) for v in shape),
+                                                             tuple(t.shape)))
+
+
+def _dims(x, B, cu_seqlens):
+    """(batch, seqlen, nheads, headdim, ngroups, dstate, nstates, io dtype) of a problem,
+    from x and B, after checking their rank and dtype."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a 4-D tensor (batch, seqlen, nheads, headdim)")
+    if not isinstance(B, torch.Tensor) or B.dim() != 4:
+        raise ValueError("B must be a 4-D tensor (batch, seqlen, ngroups, dstate)")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    _expect(B, "B", (batch, seqlen, ngroups, dstate), x.dtype)
+    if cu_seqlens is not None:
+        if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D tensor of nseq + 1 offsets")
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        if batch != 1:
+            raise ValueError("packed sequences (cu_seqlens) must come in one batch row")
+        nst = cu_seqlens.numel() - 1
+    else:
+        nst = batch
+    return batch, seqlen, nheads, headdim, ngroups, dstate, nst, x.dtype
+
+
+def _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens):
+    """Shapes and dtypes of ssd_fwd's / ssd_bwd's inputs; returns _dims()."""
+    dims = _dims(x, B, cu_seqlens)
+    batch, seqlen, H, P, G, N, nst, io = dims
+    _expect(C, "C", (batch, seqlen, G, N), io)
+    _expect(dt, "dt", (batch, seqlen, H), torch.float32)
+    _expect(A, "A", (H,), torch.float32)
+    _expect(D, "D", (H,), torch.float32, required=False)
+    _expect(dt_bias, "dt_bias", (H,), torch.float32, required=False)
+    _expect(init, "init", (nst, H, P, N), torch.float32, required=False)
+    return dims
 
 
 def problem(x, B, cu_seqlens=None, dt_softplus=True, flags=0):
-    batch, seqlen, nheads, headdim = x.shape
-    ngroups, dstate = B.shape[2], B.shape[3]
-    io = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
-    if io is None:
-        raise ValueError("x must be float32 or bfloat16")
-    if B.dtype != x.dtype:
-        raise ValueError("B, C must have x's dtype")
-    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    batch, seqlen, nheads, headdim, ngroups, dstate, nst, dtype = _dims(x, B, cu_seqlens)
+    io = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
+    nseq = 0 if cu_seqlens is None else nst
     return Problem(batch, seqlen, nheads, headdim, dstate, ngroups, nseq, io, int(bool(dt_softplus)),
                    int(flags))
 
@@ -157,7 +202,7 @@ def num_chunks(prob, chunk_size, packed):
 
 def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
         dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False,
-        only_kernel=0, prepare=False):
+        only_kernel=0, prepare=False, one_stream=False):
     """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h.
 
     save_for_backward: keep the intermediates in ``workspace`` (which must hold
@@ -166,16 +211,20 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     only_kernel: k >= 1 launches only the k-th forward kernel (profiling; needs the
     workspace, out and final of a complete call on the same inputs).
     prepare: launch nothing; return (launch, out, final) where launch() issues the
-    call with the arguments marshalled here (timing loops)."""
+    call with the arguments marshalled here (timing loops).
+    one_stream: queue every kernel on the current stream (the library then uses no
+    stream of its own)."""
     if only_kernel and (workspace is None or out is None):
         raise ValueError("only_kernel needs the workspace and outputs of a complete call")
+    batch, seqlen, H, P, G, N, nst, io = _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens)
+    _expect(out, "out", x.shape, io, required=False)
+    _expect(final, "final", (nst, H, P, N), torch.float32, required=False)
+    _expect(workspace, "workspace", (workspace.numel(),) if workspace is not None else (0,),
+            torch.uint8, required=False)
     dev = _dev(x, dt, A, B, C, D, dt_bias, init, cu_seqlens, workspace, out, final)
-    for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (dt_bias, "dt_bias"), (init, "init")):
-        _f32(t, n)
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be int32")
     prob = problem(x, B, cu_seqlens, dt_softplus,
-                   (FLAG_SAVE_FOR_BWD if save_for_backward else 0) | FLAG_FWD_KERNEL(only_kernel))
+                   (FLAG_SAVE_FOR_BWD if save_for_backward else 0) | FLAG_FWD_KERNEL(only_kernel) |
+                   (FLAG_ONE_STREAM if one_stream else 0))
     L = lib()
     packed = int(cu_seqlens is not None)
     if save_for_backward:
@@ -205,7 +254,7 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
 
 def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
         chunk_size=256, dt_softplus=True, workspace=None, from_saved=False, grads=None,
-        only_kernel=0, prepare=False):
+        only_kernel=0, prepare=False, one_stream=False):
     """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors).
 
     from_saved: ``workspace`` holds the intermediates of a save_for_backward
@@ -214,12 +263,28 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_
     only_kernel: k >= 1 launches only the k-th backward kernel (profiling; needs
     from_saved and the workspace and grads of a complete call on the same inputs).
     prepare: launch nothing; return (launch, grads) (see fwd)."""
-    dev = _dev(x, dt, A, B, C, dout, D, dt_bias, init, d_final, cu_seqlens, workspace)
+    batch, seqlen, H, P, G, N, nst, io = _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens)
+    _expect(dout, "dout", x.shape, io)
+    _expect(d_final, "d_final", (nst, H, P, N), torch.float32, required=False)
+    _expect(workspace, "workspace", (workspace.numel(),) if workspace is not None else (0,),
+            torch.uint8, required=False)
+    if grads is not None:
+        want = {"dx": (x.shape, io), "ddt": (dt.shape, torch.float32), "dA": ((H,), torch.float32),
+                "dB": (B.shape, io), "dC": (C.shape, io), "dD": ((H,), torch.float32),
+                "d_dt_bias": ((H,), torch.float32), "d_init": ((nst, H, P, N), torch.float32)}
+        for k, (shape, dtype) in want.items():
+            _expect(grads.get(k), "grads['%s']" % k, shape, dtype,
+                    required=k not in ("dD", "d_dt_bias", "d_init"))
+        if (D is None) != (grads.get("dD") is None):
+            raise ValueError("grads['dD'] must be given exactly when D is")
+    dev = _dev(x, dt, A, B, C, dout, D, dt_bias, init, d_final, cu_seqlens, workspace,
+               *([] if grads is None else [v for v in grads.values() if v is not None]))
     if from_saved and workspace is None:
         raise ValueError("from_saved needs the forward's workspace")
     if only_kernel and (not from_saved or grads is None):
         raise ValueError("only_kernel needs from_saved and the grads of a complete call")
-    flags = (FLAG_FROM_SAVED if from_saved else 0) | FLAG_BWD_KERNEL(only_kernel)
+    flags = (FLAG_FROM_SAVED if from_saved else 0) | FLAG_BWD_KERNEL(only_kernel) | \
+        (FLAG_ONE_STREAM if one_stream else 0)
     prob = problem(x, B, cu_seqlens, dt_softplus, flags)
     L = lib()
     packed = int(cu_seqlens is not None)
@@ -255,12 +320,15 @@ class Stages:
     """Run one forward stage at a time on explicit buffers (tests, timing)."""
 
     def __init__(self, x, B, cu_seqlens=None, chunk_size=256, dt_softplus=True):
+        self.dims = _dims(x, B, cu_seqlens)
         self.dev = _dev(x, B, cu_seqlens)
         self.prob = problem(x, B, cu_seqlens, dt_softplus)
         self.Q = chunk_size
         self.cu = cu_seqlens
         self.packed = int(cu_seqlens is not None)
         self.nck = num_chunks(self.prob, chunk_size, self.packed)
+        if self.nck < 0:
+            raise SSDError(3)
         self.ws = _ws(lib().ssd_stage_workspace_bytes(ctypes.byref(self.prob), chunk_size, self.packed), self.dev)
         self.io_dtype = x.dtype
 
@@ -270,10 +338,30 @@ class Stages:
     def _call(self, name, *args):
         _check(getattr(lib(), name)(ctypes.byref(self.prob), *args))
 
+    def _need(self, *checks):
+        """Check (tensor, name, shape, dtype, required) tuples, then placement."""
+        for t, name, shape, dtype, req in checks:
+            _expect(t, name, shape, dtype, required=req)
+        ts = [c[0] for c in checks if c[0] is not None]
+        if _dev(*ts) not in (None, self.dev):
+            raise ValueError("all tensors must be on one device")
+
+    def _shapes(self):
+        batch, seqlen, H, P, G, N, nst, io = self.dims
+        f = torch.float32
+        return dict(x=((batch, seqlen, H, P), io), B=((batch, seqlen, G, N), io),
+                    dt=((batch, seqlen, H), f), head=((H,), f), tok=((self.nck, H, self.Q), f),
+                    decay=((self.nck, H), f), state=((self.nck, H, P, N), f),
+                    init=((nst, H, P, N), f), CB=((self.nck, G, self.Q, self.Q), io))
+
     def chunk_cumsum(self, dt, A, dt_bias=None, out=None):
         p = self.prob
+        s = self._shapes()
         delta, acs, decay = out or (self._f(self.nck, p.nheads, self.Q), self._f(self.nck, p.nheads, self.Q),
                                     self._f(self.nck, p.nheads))
+        self._need((dt, "dt", *s["dt"], True), (A, "A", *s["head"], True),
+                   (dt_bias, "dt_bias", *s["head"], False), (delta, "delta", *s["tok"], True),
+                   (acs, "acs", *s["tok"], True), (decay, "chunk_decay", *s["decay"], True))
         self._call("ssd_stage_chunk_cumsum", _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(self.cu), self.Q,
                    _ptr(delta), _ptr(acs), _ptr(decay), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return delta, acs, decay
@@ -281,6 +369,9 @@ class Stages:
     def chunk_state(self, x, B, delta, acs, out=None):
         p = self.prob
         T = out if out is not None else self._f(self.nck, p.nheads, p.headdim, p.dstate)
+        s = self._shapes()
+        self._need((x, "x", *s["x"], True), (B, "B", *s["B"], True), (delta, "delta", *s["tok"], True),
+                   (acs, "acs", *s["tok"], True), (T, "states", *s["state"], True))
         self._call("ssd_stage_chunk_state", _ptr(x), _ptr(B), _ptr(delta), _ptr(acs), _ptr(self.cu),
                    self.Q, _ptr(T), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return T
@@ -290,6 +381,10 @@ class Stages:
         nst = p.nseq if self.packed else p.batch
         Hp, final = out or (self._f(self.nck, p.nheads, p.headdim, p.dstate),
                             self._f(nst, p.nheads, p.headdim, p.dstate))
+        s = self._shapes()
+        self._need((T, "states", *s["state"], True), (decay, "chunk_decay", *s["decay"], True),
+                   (init, "init", *s["init"], False), (Hp, "passed", *s["state"], True),
+                   (final, "final", *s["init"], False))
         self._call("ssd_stage_state_passing", _ptr(T), _ptr(decay), _ptr(init), _ptr(self.cu), self.Q,
                    _ptr(Hp), _ptr(final), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return Hp, final
@@ -298,12 +393,19 @@ class Stages:
         p = self.prob
         CB = out if out is not None else torch.empty(self.nck, p.ngroups, self.Q, self.Q,
                                                      dtype=self.io_dtype, device=self.dev)
+        s = self._shapes()
+        self._need((B, "B", *s["B"], True), (C, "C", *s["B"], True), (CB, "CB", *s["CB"], True))
         self._call("ssd_stage_bmm_chunk", _ptr(B), _ptr(C), _ptr(self.cu), self.Q, _ptr(CB),
                    _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return CB
 
     def chunk_scan(self, x, C, CB, delta, acs, Hp, D=None, out=None):
         y = out if out is not None else torch.empty_like(x)
+        s = self._shapes()
+        self._need((x, "x", *s["x"], True), (C, "C", *s["B"], True), (CB, "CB", *s["CB"], True),
+                   (delta, "delta", *s["tok"], True), (acs, "acs", *s["tok"], True),
+                   (Hp, "passed", *s["state"], True), (D, "D", *s["head"], False),
+                   (y, "out", *s["x"], True))
         self._call("ssd_stage_chunk_scan", _ptr(x), _ptr(C), _ptr(CB), _ptr(delta), _ptr(acs), _ptr(Hp),
                    _ptr(D), _ptr(self.cu), self.Q, _ptr(y), _ptr(self.ws), self.ws.numel(),
                    _stream(self.dev))
@@ -317,6 +419,8 @@ def util_copy(dst, src):
 
 def norm_problem(y, group, eps):
     """y: (..., dim) bf16; rows = the product of the leading sizes."""
+    if not isinstance(y, torch.Tensor) or y.dim() < 1:
+        raise ValueError("y must be a tensor of rank >= 1")
     if y.dtype != torch.bfloat16:
         raise ValueError("the gated RMSNorm takes bfloat16 y, z")
     dim = y.shape[-1]
@@ -327,11 +431,15 @@ def gated_rmsnorm_fwd(y, z, weight, group, eps=1e-5, out=None, rstd=None, prepar
     """out = RMSNorm(y * silu(z)) * weight over groups of `group` columns of the
     last dimension (z may be None: no gate).  rstd: optional (rows, dim // group)
     float32 output.  Returns out (or (launch, out) when prepare is set)."""
-    dev = _dev(y, z, weight, out, rstd)
-    _f32(weight, "weight")
-    if z is not None and (z.shape != y.shape or z.dtype != y.dtype):
-        raise ValueError("z must match y")
     p = norm_problem(y, group, eps)
+    _expect(z, "z", y.shape, y.dtype, required=False)
+    _expect(weight, "weight", (p.dim,), torch.float32)
+    _expect(out, "out", y.shape, y.dtype, required=False)
+    if rstd is not None:
+        if p.group <= 0 or p.dim % p.group:
+            raise ValueError("group must divide the last dimension")
+        _expect(rstd, "rstd", (p.rows, p.dim // p.group), torch.float32)
+    dev = _dev(y, z, weight, out, rstd)
     out = torch.empty_like(y) if out is None else out
     args = (ctypes.byref(p), _ptr(y), _ptr(z), _ptr(weight), _ptr(out), _ptr(rstd), _stream(dev))
 
@@ -347,9 +455,19 @@ def gated_rmsnorm_fwd(y, z, weight, group, eps=1e-5, out=None, rstd=None, prepar
 def gated_rmsnorm_bwd(dout, y, z, weight, group, eps=1e-5, workspace=None, grads=None, prepare=False):
     """Gradients (dy, dz, dweight) of <dout, gated_rmsnorm_fwd(y, z, weight)>;
     dz is None without a gate.  Returns them (or (launch, grads) with prepare)."""
-    dev = _dev(dout, y, z, weight)
-    _f32(weight, "weight")
     p = norm_problem(y, group, eps)
+    _expect(dout, "dout", y.shape, y.dtype)
+    _expect(z, "z", y.shape, y.dtype, required=False)
+    _expect(weight, "weight", (p.dim,), torch.float32)
+    if grads is not None:
+        _expect(grads[0], "dy", y.shape, y.dtype)
+        _expect(grads[1], "dz", y.shape, y.dtype, required=z is not None)
+        if z is None and grads[1] is not None:
+            raise ValueError("dz must be None without a gate")
+        _expect(grads[2], "dweight", (p.dim,), torch.float32)
+    _expect(workspace, "workspace", (workspace.numel(),) if workspace is not None else (0,),
+            torch.uint8, required=False)
+    dev = _dev(dout, y, z, weight, workspace, *([] if grads is None else [g for g in grads if g is not None]))
     if grads is None:
         grads = (torch.empty_like(y), None if z is None else torch.empty_like(z),
                  torch.empty_like(weight))

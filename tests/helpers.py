@@ -65,3 +65,30 @@ def gpu_bwd(ssd, inp, chunk_size, **kw):
                    dt_bias=d["dt_bias"], init=d["init"], d_final=d["d_final"],
                    cu_seqlens=d["cu_seqlens"], chunk_size=chunk_size,
                    dt_softplus=inp["dt_softplus"], **kw)
+
+
+def batch_rows(inp, rows):
+    """The inputs of some batch rows alone (each row is an independent problem)."""
+    out = dict(inp)
+    for k in ("x", "B", "C", "dt", "dout", "init", "d_final"):
+        if out.get(k) is not None:
+            out[k] = out[k][rows].contiguous()
+    return out
+
+
+def packed_sequences(inp, seqs):
+    """The inputs of some packed sequences alone, re-packed into one row (each
+    sequence is an independent problem).  Returns (inputs, token index list)."""
+    cu = [int(v) for v in inp["cu_seqlens"]]
+    toks = [t for s in seqs for t in range(cu[s], cu[s + 1])]
+    idx = torch.tensor(toks, dtype=torch.long)
+    out = dict(inp)
+    for k in ("x", "B", "C", "dt", "dout"):
+        if out.get(k) is not None:
+            out[k] = out[k][:, idx].contiguous()
+    for k in ("init", "d_final"):
+        if out.get(k) is not None:
+            out[k] = out[k][list(seqs)].contiguous()
+    lens = [cu[s + 1] - cu[s] for s in seqs]
+    out["cu_seqlens"] = inputs.cu_from_lengths(lens)
+    return out, toks

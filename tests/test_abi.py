@@ -139,7 +139,8 @@ def test_workspace(L):
 
 
 def test_flags(L):
-    assert fwd_status(L, prob(flags=4)) == UNSUP
+    assert fwd_status(L, prob(flags=8)) == UNSUP  # an unknown bit
+    assert fwd_status(L, prob(flags=ssd.FLAG_ONE_STREAM), ws_bytes=1) == WS  # accepted
     assert fwd_status(L, prob(flags=ssd.FLAG_BWD_KERNEL(3))) == UNSUP  # needs FROM_SAVED
     assert fwd_status(L, prob(flags=ssd.FLAG_BWD_KERNEL(8))) == UNSUP
     p = prob(flags=ssd.FLAG_FROM_SAVED | ssd.FLAG_BWD_KERNEL(7))

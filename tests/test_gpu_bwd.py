@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import gpu_bwd, gpu_fwd, has_gpu, normwise, np64, oracle_args, to_dev
+from helpers import (batch_rows, gpu_bwd, gpu_fwd, has_gpu, normwise, np64, oracle_args,
+                     packed_sequences, to_dev)
 from mamba_ssd_chunked_03_amd import inputs
 from oracle import recurrence
 
@@ -253,3 +254,74 @@ def test_graph_capture_of_training_step():
             assert torch.equal(g[k], ref[k]), (i, k)
         ssd.fwd(*args, **common)  # eager work of the library between replays
         torch.cuda.synchronize()
+
+
+def _group_heads(g, hpg):
+    return list(range(g * hpg, (g + 1) * hpg))
+
+
+def test_bwd_full_size_full_groups_layer():
+    """The layer workload (batch 2, seqlen 8192, 64 heads in 8 groups): every head
+    of group 0 on batch row 0 and every head of group 7 on batch row 1 against the
+    oracle run on those heads and that row alone.  The oracle's dB and dC of a
+    group then hold the whole group sum, so dB and dC are gated too, with every
+    per-head gradient of those 16 (row, head) pairs."""
+    inp = inputs.config_inputs(2)
+    inp["d_final"] = None
+    g = gpu_bwd(ssd, inp, 256)
+    torch.cuda.synchronize()
+    hpg = inp["x"].shape[2] // inp["B"].shape[2]
+    for row, grp in ((0, 0), (1, 7)):
+        heads = _group_heads(grp, hpg)
+        ref = oracle_bwd(batch_rows(inp, [row]), heads=heads)
+        sub = {k: (None if v is None else v[row:row + 1]) for k, v in g.items()
+               if k in ("dx", "ddt", "dB", "dC")}
+        got = dict(sub)
+        got["dB"] = sub["dB"][:, :, grp:grp + 1]
+        got["dC"] = sub["dC"][:, :, grp:grp + 1]
+        ref = dict(ref)
+        ref["dB"] = ref["dB"][:, :, grp:grp + 1]
+        ref["dC"] = ref["dC"][:, :, grp:grp + 1]
+        check(got, ref, "bf16", "config 2 row %d group %d" % (row, grp), keys=["dx", "ddt", "dB", "dC"],
+              heads=heads)
+
+
+def test_bwd_full_size_full_groups_packed():
+    """The packed workload (65536 tokens, 5 sequences, per-sequence init states):
+    the fourth sequence (8628 tokens, starting mid-chunk of the packed row) with
+    every head of groups 0 and 7 against the oracle run on that sequence alone;
+    dB and dC of those groups are whole group sums.  d_final is drawn here, so the
+    reverse scan starts from a nonzero state."""
+    inp = inputs.config_inputs(4)
+    gen = torch.Generator().manual_seed(404)
+    inp["d_final"] = 0.1 * torch.randn(inp["init"].shape, generator=gen)
+    g = gpu_bwd(ssd, inp, 256)
+    torch.cuda.synchronize()
+    hpg = inp["x"].shape[2] // inp["B"].shape[2]
+    heads = _group_heads(0, hpg) + _group_heads(7, hpg)
+    seq = 3
+    sub_inp, toks = packed_sequences(inp, [seq])
+    ref = oracle_bwd(sub_inp, heads=heads)
+    got = {"dx": g["dx"][:, toks], "ddt": g["ddt"][:, toks], "dB": g["dB"][:, toks][:, :, [0, 7]],
+           "dC": g["dC"][:, toks][:, :, [0, 7]], "d_init": g["d_init"][seq:seq + 1]}
+    ref = dict(ref)
+    ref["dB"] = ref["dB"][:, :, [0, 7]]
+    ref["dC"] = ref["dC"][:, :, [0, 7]]
+    check(got, ref, "bf16", "config 4 sequence 3 groups 0, 7", keys=["dx", "ddt", "dB", "dC", "d_init"],
+          heads=heads)
+
+
+def test_one_stream_flag_gives_identical_results():
+    """SSD_FLAG_ONE_STREAM queues every kernel on the caller's stream (no side stream):
+    outputs and gradients are bit-identical to the default two-stream call."""
+    inp = inputs.make_inputs(2, 700, 16, 64, 128, 2, io="bf16", init="randn", bwd=True,
+                             d_final=True, seed=63)
+    for Q in (128, 256):
+        y0, f0 = gpu_fwd(ssd, inp, Q)
+        y1, f1 = gpu_fwd(ssd, inp, Q, one_stream=True)
+        g0 = gpu_bwd(ssd, inp, Q)
+        g1 = gpu_bwd(ssd, inp, Q, one_stream=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(f0, f1), Q
+        for k in KEYS:
+            assert torch.equal(g0[k], g1[k]), (Q, k)

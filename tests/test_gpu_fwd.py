@@ -325,3 +325,37 @@ def test_fwd_cb_in_chunk_state(lengths):
     y, final = gpu_fwd(ssd, inp, 256)
     torch.cuda.synchronize()
     check_fwd(inp, y, final, "bf16", "cb_in_chunk_state")
+
+
+# The skip term D x dominates y (|D x| up to ~11 against an SSM term of ~0.01-0.03),
+# so a scan error as large as the SSM term itself could hide under the y gate.
+# Without D the output is the scan alone, gated normwise at 1e-2.  Every full-size
+# workload here takes the path whose chunk-state kernel also forms C.B^T.
+@pytest.mark.parametrize("cfg,heads", [(1, list(range(8)) + [63]), (3, [5, 16, 17, 30]),
+                                       (4, list(range(56, 64)))])
+def test_full_size_scan_only(cfg, heads):
+    inp = inputs.config_inputs(cfg)
+    inp["D"] = None
+    d = to_dev(inp)
+    prob = ssd.problem(d["x"], d["B"], d["cu_seqlens"])
+    assert ssd.lib().ssd_fwd_kernel_mask(ctypes.byref(prob), 256, int(d["cu_seqlens"] is not None)) == 0xB
+    y, final = gpu_fwd(ssd, inp, inputs.CONFIGS[cfg]["chunk"])
+    torch.cuda.synchronize()
+    y_ref, f_ref = recurrence.fwd(**oracle_args(inp), heads=heads)
+    assert normwise(np64(y[:, :, heads]), y_ref) <= 1e-2, normwise(np64(y[:, :, heads]), y_ref)
+    assert normwise(np64(final[:, heads]), f_ref) <= 1e-3
+
+
+@pytest.mark.parametrize("lengths", [None, [300, 0, 513, 77]], ids=["batched", "packed"])
+def test_fwd_cb_in_chunk_state_scan_only(lengths):
+    """The scan-only output (no D) on a shape whose chunk-state kernel forms C.B^T."""
+    if lengths is None:
+        inp = inputs.make_inputs(batch=2, seqlen=700, seed=54, with_D=False, **FUSED_CB)
+    else:
+        inp = inputs.make_inputs(batch=1, seqlen=sum(lengths), lengths=lengths, seed=55,
+                                 with_D=False, **FUSED_CB)
+    y, final = gpu_fwd(ssd, inp, 256)
+    torch.cuda.synchronize()
+    y_ref, f_ref = recurrence.fwd(**oracle_args(inp))
+    assert normwise(np64(y), y_ref) <= 1e-2
+    assert normwise(np64(final), f_ref) <= 1e-3
