@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 typedef enum {
   SSD_OK = 0,
@@ -177,6 +177,32 @@ ssd_status ssd_fwd(const ssd_problem* problem,
                    const float* init_states, const int32_t* cu_seqlens, int32_t chunk_size,
                    void* out, float* final_states,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): ssd_fwd with its workspace
+ * in a fixed device array of SSD_NOALLOC_SCRATCH_BYTES bytes inside the library,
+ * one per device, held from the library's first use on that device until the
+ * process ends.  Arguments and results are those of ssd_fwd (the same kernels, all
+ * on `stream`), without workspace and workspace_bytes.
+ *  - problem->flags must be 0 or SSD_FLAG_ONE_STREAM (no saved context, no
+ *    single-kernel launches): SSD_ERR_UNSUPPORTED otherwise.
+ *  - A problem whose forward workspace (ssd_fwd_workspace_bytes) exceeds
+ *    SSD_NOALLOC_SCRATCH_BYTES returns SSD_ERR_WORKSPACE before anything is queued.
+ *  - `stream` must belong to the current device (SSD_ERR_UNSUPPORTED otherwise).
+ *  - Nothing is allocated: no hipMalloc, hipFree, stream or event creation.  The
+ *    first call on a device looks up that device's array address once.  The
+ *    SSD_DEBUG check of cu_seqlens is not run (it would copy to the host).
+ *  - Every call on a device uses that device's one array, which keeps the last
+ *    call's contents (no value a call reads comes from an earlier call).  Calls
+ *    that overlap in time on one device -- on different streams, or from several
+ *    host threads before their work has finished -- race on it and give undefined
+ *    results: order them on one stream. */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+ssd_status ssd_fwd_noalloc(const ssd_problem* problem,
+                           const void* x, const float* dt, const float* dt_bias, const float* A,
+                           const void* B, const void* C, const float* D,
+                           const float* init_states, const int32_t* cu_seqlens, int32_t chunk_size,
+                           void* out, float* final_states, void* stream);
 
 /* Backward pass for the loss L = <dout, y> + <d_final_states, final>: the adjoint
  * of ssd_fwd's recurrence (scan page, section 1), with the cross-chunk part as the

@@ -137,13 +137,16 @@ size_t stage_ws(const Prob& p) { return fwd_layout(p).delta; }
 
 // Point the chunk map at the table inside a workspace and queue its build.
 // build = false: the workspace already holds the table (single-kernel relaunch).
-ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool build = true) {
+// debug_check = false: no SSD_DEBUG check of cu_seqlens (it copies to the host and
+// synchronises the stream).
+ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool build = true,
+                     bool debug_check = true) {
   if (!p.packed) return SSD_OK;
   FwdLayout l = fwd_layout(p);
   p.map.tab = (const int4*)(ws + l.tab);
   p.map.seq_off = (const int32_t*)(ws + l.seq_off);
   if (!build) return SSD_OK;
-  if (std::getenv("SSD_DEBUG") && std::getenv("SSD_DEBUG")[0] == '1') {
+  if (debug_check && std::getenv("SSD_DEBUG") && std::getenv("SSD_DEBUG")[0] == '1') {
     std::vector<int32_t> h((size_t)p.nseq + 1);
     if (hipMemcpyAsync(h.data(), cu, h.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
@@ -226,6 +229,39 @@ bool all_aligned(std::initializer_list<const void*> ps) {
 
 }  // namespace
 
+// ---------------------------------------------------- fixed device scratch ----
+// The workspace of ssd_fwd_noalloc: a file-scope device array of a fixed size.
+// Each device the library runs on holds its own copy, at its own address, until
+// the process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device, with that
+// device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// The current device's address of `scratch`.  `stream` must belong to the current
+// device (a stream of another device would run its kernels on that device, whose
+// copy has another address): SSD_ERR_UNSUPPORTED otherwise.
+ssd_status noalloc_scratch(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SSD_ERR_HIP;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SSD_ERR_HIP;
+    if (sdev != dev) return SSD_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return SSD_ERR_HIP;
+    addr[dev] = a;
+  }
+  *out = addr[dev];
+  return SSD_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t ssd_abi_version(void) { return SSD_ABI_VERSION; }
@@ -274,10 +310,12 @@ size_t ssd_stage_workspace_bytes(const ssd_problem* pr, int32_t Q, int32_t packe
   return stage_ws(p);
 }
 
-ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const float* dt_bias,
-                   const float* A, const void* B, const void* C, const float* D,
-                   const float* init_states, const int32_t* cu_seqlens, int32_t Q, void* out,
-                   float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+// The forward of ssd_fwd on a given workspace; debug_check as in setup_map.
+static ssd_status fwd_run(const ssd_problem* pr, const void* x, const float* dt,
+                          const float* dt_bias, const float* A, const void* B, const void* C,
+                          const float* D, const float* init_states, const int32_t* cu_seqlens,
+                          int32_t Q, void* out, float* final_states, void* workspace,
+                          size_t workspace_bytes, void* stream, bool debug_check) {
   Prob p;
   ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
   if (s != SSD_OK) return s;
@@ -292,7 +330,7 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int only = (p.flags >> 12) & 7;  // 0: every kernel
-  s = setup_map(p, cu_seqlens, ws, st, only == 0);
+  s = setup_map(p, cu_seqlens, ws, st, only == 0, debug_check);
   if (s != SSD_OK) return s;
   float* delta = (float*)(ws + l.delta);
   float* acs = (float*)(ws + l.acs);
@@ -329,6 +367,36 @@ ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const 
   }
   if (!only || only == 4) SSD_TRY_FORKED(launch_chunk_scan(p, x, C, CB, delta, acs, Hp, hb, D, out, st));
   return SSD_OK;
+}
+
+ssd_status ssd_fwd(const ssd_problem* pr, const void* x, const float* dt, const float* dt_bias,
+                   const float* A, const void* B, const void* C, const float* D,
+                   const float* init_states, const int32_t* cu_seqlens, int32_t Q, void* out,
+                   float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_run(pr, x, dt, dt_bias, A, B, C, D, init_states, cu_seqlens, Q, out, final_states,
+                 workspace, workspace_bytes, stream, true);
+}
+
+ssd_status ssd_fwd_noalloc(const ssd_problem* pr, const void* x, const float* dt,
+                           const float* dt_bias, const float* A, const void* B, const void* C,
+                           const float* D, const float* init_states, const int32_t* cu_seqlens,
+                           int32_t Q, void* out, float* final_states, void* stream) {
+  Prob p;
+  ssd_status s = make_prob(pr, Q, cu_seqlens != nullptr, p);
+  if (s != SSD_OK) return s;
+  if (p.flags & ~SSD_FLAG_ONE_STREAM) return SSD_ERR_UNSUPPORTED;
+  // the host-detectable errors first, before any HIP call (as ssd_fwd checks them)
+  if ((int64_t)p.B * p.L > 0 && (!x || !dt || !A || !B || !C || !out)) return SSD_ERR_NULL;
+  if (!all_aligned({x, dt, dt_bias, A, B, C, D, init_states, cu_seqlens, out, final_states}))
+    return SSD_ERR_ALIGN;
+  if (fwd_layout(p).end > (size_t)SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  s = noalloc_scratch((hipStream_t)stream, &ws);
+  if (s != SSD_OK) return s;
+  ssd_problem one = *pr;
+  one.flags = SSD_FLAG_ONE_STREAM;
+  return fwd_run(&one, x, dt, dt_bias, A, B, C, D, init_states, cu_seqlens, Q, out, final_states,
+                 ws, (size_t)SSD_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const float* dt_bias,

@@ -57,6 +57,7 @@ _SIGS = {
     "ssd_stage_workspace_bytes": ([_P, _I32, _I32], _SZ),
     "ssd_fwd": ([_P] + [_P] * 9 + [_I32, _P, _P, _P, _SZ, _P], _I32),
     "ssd_bwd": ([_P] + [_P] * 9 + [_I32] + [_P] * 11 + [_SZ, _P], _I32),
+    "ssd_fwd_noalloc": ([_P] + [_P] * 9 + [_I32, _P, _P, _P], _I32),
     "ssd_stage_chunk_cumsum": ([_P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
     "ssd_stage_chunk_state": ([_P, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], _I32),
     "ssd_stage_state_passing": ([_P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
@@ -69,7 +70,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 
@@ -249,6 +250,30 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     if prepare:
         return launch, out, final
     launch()
+    return out, final
+
+
+# SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h: the largest forward workspace fwd_noalloc takes
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fwd_noalloc(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
+                dt_softplus=True, out=None, final=None):
+    """fwd() through ssd_fwd_noalloc: no workspace, the library's fixed device array
+    instead (problems whose forward workspace exceeds NOALLOC_SCRATCH_BYTES raise).
+    Pass out and final to allocate nothing here either."""
+    batch, seqlen, H, P, G, N, nst, io = _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens)
+    _expect(out, "out", x.shape, io, required=False)
+    _expect(final, "final", (nst, H, P, N), torch.float32, required=False)
+    dev = _dev(x, dt, A, B, C, D, dt_bias, init, cu_seqlens, out, final)
+    prob = problem(x, B, cu_seqlens, dt_softplus)
+    if out is None:
+        out = torch.empty_like(x)
+    if final is None:
+        final = torch.empty(nst, H, P, N, dtype=torch.float32, device=dev)
+    _check(lib().ssd_fwd_noalloc(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(init), _ptr(cu_seqlens), chunk_size, _ptr(out),
+                                 _ptr(final), _stream(dev)))
     return out, final
 
 

@@ -248,3 +248,22 @@ def test_fwd_kernel_mask(L):
     assert mask(io_dtype=0) == 0xF                                      # fp32 path
     assert mask(headdim=128) == 0xF                                     # one head per workgroup
     assert mask(nheads=-1) == 0                                         # invalid problem
+
+
+def test_noalloc_host_validation(L):
+    """ssd_fwd_noalloc rejects, before any HIP call, what the host can detect: flags
+    other than SSD_FLAG_ONE_STREAM, NULL or misaligned pointers, and a forward
+    workspace larger than its fixed device array."""
+    def st(p, Q=256, x=FAKE, out=FAKE):
+        return L.ssd_fwd_noalloc(ctypes.byref(p), x, FAKE, None, FAKE, FAKE, FAKE, None, None, None, Q,
+                                 out, None, None)
+    big = prob(batch=2, seqlen=8192, nheads=64)
+    assert L.ssd_fwd_workspace_bytes(ctypes.byref(big), 256, 0) > ssd.NOALLOC_SCRATCH_BYTES
+    assert st(big) == WS
+    assert st(prob(flags=ssd.FLAG_SAVE_FOR_BWD)) == UNSUP
+    assert st(prob(flags=ssd.FLAG_FWD_KERNEL(2))) == UNSUP
+    assert st(prob(), x=None) == NULL
+    assert st(prob(), out=FAKE + 8) == ALIGN
+    assert st(prob(), Q=100) == UNSUP
+    hdr = open(HEADER).read()
+    assert "#define SSD_NOALLOC_SCRATCH_BYTES (%du << 20)" % (ssd.NOALLOC_SCRATCH_BYTES >> 20) in hdr
