@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
     ap.add_argument("--fwd-only", action="store_true", help="time ssd_fwd alone as the step")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the long-context and packed workloads reported beside the headline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run the library's plain copy kernel (counter calibration)")
     return ap.parse_args()
@@ -190,58 +192,161 @@ def cpu_baseline_parallel(with_bwd):
                       % (done, nproc, "fwd+bwd" if with_bwd else "fwd", sec)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (the SSD scan of one GPU's share); "
-              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    import torch
-    from mamba_ssd_chunked_03_amd import inputs, ssd
+class Workload:
+    """One named workload on the GPU: seeded inputs resident in HBM, workspaces,
+    and the library calls marshalled once (the timed loops only issue them)."""
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_bytes:
-        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            ssd.util_copy(dst, src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}))
-        return
-    cfg = inputs.CONFIGS[2]
-    Q = cfg["chunk"]
-    inp = inputs.config_inputs(2)
-    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
-    x, dt, A, Bm, Cm, D, bias, init, dout = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
-                                             d["dt_bias"], d["init"], d["dout"])
-    Bsz, L, H, P = x.shape
-    G, N = Bm.shape[2], Bm.shape[3]
-    prob = ssd.problem(x, Bm)
-    import ctypes
-    lib = ssd.lib()
-    ws_f = torch.empty(lib.ssd_fwd_workspace_bytes(ctypes.byref(prob), Q, 0), dtype=torch.uint8, device=dev)
-    y = torch.empty_like(x)
-    final = torch.empty(Bsz, H, P, N, dtype=torch.float32, device=dev)
+    def __init__(self, cfg_id, dev, with_bwd=True):
+        import ctypes
+        import torch
+        from mamba_ssd_chunked_03_amd import inputs, ssd
+        self.cfg_id = cfg_id
+        cfg = inputs.CONFIGS[cfg_id]
+        self.Q = Q = cfg["chunk"]
+        inp = inputs.config_inputs(cfg_id)
+        self.sha256 = input_sha256(inp)
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        self.d = d
+        x, Bm = d["x"], d["B"]
+        self.cu = d["cu_seqlens"]
+        self.packed = int(self.cu is not None)
+        self.lengths = None if self.cu is None else [int(b - a) for a, b in zip(inp["cu_seqlens"][:-1],
+                                                                              inp["cu_seqlens"][1:])]
+        self.Bsz, self.L, self.H, self.P = x.shape
+        self.G, self.N = Bm.shape[2], Bm.shape[3]
+        self.nseq = len(self.lengths) if self.packed else self.Bsz
+        self.prob = prob = ssd.problem(x, Bm, self.cu)
+        lib = ssd.lib()
+        ws_f = torch.empty(lib.ssd_fwd_workspace_bytes(ctypes.byref(prob), Q, self.packed),
+                           dtype=torch.uint8, device=dev)
+        self.y = torch.empty_like(x)
+        self.final = torch.empty(self.nseq, self.H, self.P, self.N, dtype=torch.float32, device=dev)
+        self.common = dict(D=d["D"], dt_bias=d["dt_bias"], init=d["init"], cu_seqlens=self.cu, chunk_size=Q)
+        self.args = (x, d["dt"], d["A"], Bm, d["C"])
+        self.fwd, _, _ = ssd.fwd(*self.args, workspace=ws_f, out=self.y, final=self.final, prepare=True,
+                                 **self.common)
+        self.with_bwd = with_bwd and d["dout"] is not None
+        self.fwd_mask = lib.ssd_fwd_kernel_mask(ctypes.byref(prob), Q, self.packed)
+        self.ws_b = torch.empty(lib.ssd_bwd_workspace_bytes(ctypes.byref(prob), Q, self.packed),
+                                dtype=torch.uint8, device=dev)
+        # the training forward keeps its intermediates for the backward
+        self.fwd_save, _, _ = ssd.fwd(*self.args, workspace=self.ws_b, out=self.y, final=self.final,
+                                      save_for_backward=True, prepare=True, **self.common)
+        self.grads = None
+        if self.with_bwd:
+            self.bwd_saved, self.grads = ssd.bwd(*self.args, d["dout"], workspace=self.ws_b,
+                                                 from_saved=True, prepare=True, **self.common)
+            self.bwd_recompute, _ = ssd.bwd(*self.args, d["dout"], workspace=self.ws_b, grads=self.grads,
+                                            prepare=True, **self.common)
 
-    # every call's arguments are marshalled once; the timed loops only issue them
-    common = dict(D=D, dt_bias=bias, init=init, chunk_size=Q)
-    fwd, _, _ = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_f, out=y, final=final, prepare=True, **common)
+    @property
+    def tokens(self):
+        return self.Bsz * self.L
 
-    have_bwd = not args.fwd_only
-    ws_b = torch.empty(lib.ssd_bwd_workspace_bytes(ctypes.byref(prob), Q, 0), dtype=torch.uint8, device=dev)
-    # the training forward keeps its intermediates for the backward
-    fwd_save, _, _ = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_b, out=y, final=final,
-                             save_for_backward=True, prepare=True, **common)
-    bwd_saved, grads = ssd.bwd(x, dt, A, Bm, Cm, dout, workspace=ws_b, from_saved=True,
-                               prepare=True, **common)
-    bwd_recompute, _ = ssd.bwd(x, dt, A, Bm, Cm, dout, workspace=ws_b, grads=grads, prepare=True,
-                               **common)
+    def chunks(self):
+        """chunk slots that hold tokens (packed sequences: each cut from its own start)"""
+        if self.packed:
+            return sum((n + self.Q - 1) // self.Q for n in self.lengths)
+        return self.Bsz * ((self.L + self.Q - 1) // self.Q)
 
-    def timed(fn, steps, warmup):
+    def step(self):
+        if self.with_bwd:
+            self.fwd_save()
+            self.bwd_saved()
+        else:
+            self.fwd()
+
+    def kernel_launches(self):
+        """name -> a launch of that kernel alone, on the buffers of a complete call"""
+        from mamba_ssd_chunked_03_amd import ssd
+        self.fwd_save()
+        if self.with_bwd:
+            self.bwd_saved()
+        fns = {}
+        for k, name in enumerate(ssd.FWD_KERNELS, 1):
+            if not self.fwd_mask & (1 << (k - 1)):
+                continue
+            fns[name] = ssd.fwd(*self.args, workspace=self.ws_b, out=self.y, final=self.final,
+                                save_for_backward=True, only_kernel=k, prepare=True, **self.common)[0]
+        if self.with_bwd:
+            for k, name in enumerate(ssd.BWD_KERNELS, 1):
+                fns[name] = ssd.bwd(*self.args, self.d["dout"], workspace=self.ws_b, from_saved=True,
+                                    grads=self.grads, only_kernel=k, prepare=True, **self.common)[0]
+        return fns
+
+    def scan_ab(self, tm, per):
+        """The state-passing kernels timed alone as the associative scan (default) and
+        as the sequential-carry loop it replaces (SSD_FLAG_SEQUENTIAL_SCAN), on the
+        same buffers: warm and cold ms and the fraction of 8 TB/s of each."""
+        from mamba_ssd_chunked_03_amd import ssd
+        nbytes, _ = self.alg()
+        res = {}
+        for seq in (False, True):
+            self.fwd_save()
+            if self.with_bwd:
+                self.bwd_saved()
+            runs = {"state_passing": ssd.fwd(*self.args, workspace=self.ws_b, out=self.y, final=self.final,
+                                             save_for_backward=True, only_kernel=2, sequential_scan=seq,
+                                             prepare=True, **self.common)[0]}
+            if self.with_bwd:
+                runs["reverse_state_passing"] = ssd.bwd(*self.args, self.d["dout"], workspace=self.ws_b,
+                                                        from_saved=True, grads=self.grads, only_kernel=2,
+                                                        sequential_scan=seq, prepare=True, **self.common)[0]
+            for name, fn in runs.items():
+                ms = tm.trials(fn, per)[0]
+                ms_cold = tm.cold(fn)
+                e = res.setdefault(name, {"alg_bytes": nbytes[name]})
+                key = "sequential" if seq else "associative"
+                e[key] = {"ms": round(ms, 4), "ms_cold": round(ms_cold, 4),
+                          "frac_hbm": round(nbytes[name] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "frac_hbm_cold": round(nbytes[name] / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                print("bench: %s %-12s %.4f ms (cold %.4f)" % (name, key, ms, ms_cold), file=sys.stderr,
+                      flush=True)
+        self.fwd_save()  # the workspace holds the default path's intermediates again
+        if self.with_bwd:
+            self.bwd_saved()
+        return res
+
+    def alg(self):
+        """algorithmic bytes and flops per kernel of this workload's step"""
+        nck = self.chunks()
+        nbytes = kernel_bytes(self.Bsz, self.L, self.H, self.P, self.N, self.G, self.Q, nck, self.nseq, 2,
+                              init=self.d["init"] is not None, d_final=False)
+        nflops = kernel_flops(self.Bsz, self.L, self.H, self.P, self.N, self.G, self.Q, nck)
+        # where the chunk-state kernel forms C.B^T (and its transpose) itself, its
+        # bytes and flops are that kernel's and no C.B^T kernel is launched
+        if not self.fwd_mask & 4:
+            nbytes["chunk_state"] += nbytes["bmm_chunk"] - self.tokens * self.G * self.N * 2  # (B read once)
+            nflops["chunk_state"] += nflops["bmm_chunk"]
+        return nbytes, nflops
+
+
+def input_sha256(inp):
+    """SHA-256 of every input tensor's bytes as drawn on the host (the bits the
+    GPU and the oracle both consume)."""
+    import hashlib
+    out = {}
+    for k, v in sorted(inp.items()):
+        if hasattr(v, "numpy"):
+            t = v.detach().cpu().contiguous()
+            if t.dtype.is_floating_point and t.element_size() == 2:
+                t = t.view(dtype=__import__("torch").int16)
+            out[k] = hashlib.sha256(t.numpy().tobytes()).hexdigest()
+    return out
+
+
+class Timer:
+    """Timing helpers: HIP events on torch's current stream, which is the stream
+    every library call of the step is issued on (a call's side-stream kernels are
+    joined back to it before the call's last kernel)."""
+
+    def __init__(self, dev):
+        import torch
+        self.torch = torch
+        self.flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def timed(self, fn, steps, warmup):
+        torch = self.torch
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -256,8 +361,9 @@ def main():
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return e0.elapsed_time(e1) / steps, wall
 
-    def trials(fn, per, n=7, warmup=2):
+    def trials(self, fn, per, n=7, warmup=2):
         """median / min / max ms per call over n back-to-back windows of `per` calls"""
+        torch = self.torch
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -274,15 +380,14 @@ def main():
         res.sort()
         return res[n // 2], res[0], res[-1]
 
-    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-
-    def cold(fn, n=7):
+    def cold(self, fn, n=7):
         """median ms of single calls, each after a 512 MiB read (outside the event pair)
         that replaces the last-level cache's contents with clean lines"""
+        torch = self.torch
         st = torch.cuda.current_stream()
         res = []
         for _ in range(n):
-            flush.sum()
+            self.flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(st)
             fn()
@@ -292,90 +397,134 @@ def main():
         res.sort()
         return res[n // 2]
 
-    def step():
-        if have_bwd:
-            fwd_save()
-            bwd_saved()
-        else:
-            fwd()
+
+def kernel_table(w, tm, per, label=""):
+    """Every kernel of a workload's step on its own (the step's own launch re-issued
+    through the single-kernel flags), warm and cold, against its algorithmic bytes."""
+    from mamba_ssd_chunked_03_amd import ssd
+    nbytes, nflops = w.alg()
+    kernels = {}
+    for name, fn in w.kernel_launches().items():
+        ms, ms_min, ms_max = tm.trials(fn, per)
+        ms_cold = tm.cold(fn)
+        gbs = nbytes[name] / (ms * 1e-3) / 1e9
+        e = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_max": round(ms_max, 4),
+             "ms_cold": round(ms_cold, 4), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
+             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+             "frac_hbm_cold": round(nbytes[name] / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if name in nflops:
+            tf = nflops[name] / (ms * 1e-3) / 1e12
+            e["alg_tflops"] = round(tf, 1)
+            e["frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        kernels[name] = e
+        print("bench: %skernel %-22s %.4f ms (cold %.4f)  %.0f GB/s" % (label, name, ms, ms_cold, gbs),
+              file=sys.stderr, flush=True)
+
+    def aggregate(names):
+        b = sum(kernels[n]["alg_bytes"] for n in names)
+        t = sum(kernels[n]["ms"] for n in names)
+        tc = sum(kernels[n]["ms_cold"] for n in names)
+        return {"ms": round(t, 4), "alg_bytes": b, "GB/s": round(b / (t * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "frac_hbm_cold": round(b / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    names = list(kernels)
+    kernels["_forward_aggregate"] = aggregate([n for n in ssd.FWD_KERNELS if n in kernels])
+    if w.with_bwd:
+        kernels["_backward_aggregate"] = aggregate(list(ssd.BWD_KERNELS))
+    kernels["_all"] = aggregate(names)
+    return kernels
+
+
+def other_workload(cfg_id, dev, tm, steps, label):
+    """Forward (and, where the workload has one, training step) timings of another
+    named workload, with its kernel table; reported beside the headline."""
+    from mamba_ssd_chunked_03_amd import inputs
+    c = inputs.CONFIGS[cfg_id]
+    w = Workload(cfg_id, dev)
+    per = max(1, steps // 4)
+    fwd_med, fwd_min, fwd_max = tm.trials(w.fwd, per)
+    res = {"workload": "%s: batch %d, %d tokens%s, %d heads, headdim %d, dstate %d, %d groups, chunk %d, "
+                       "bf16" % (label, w.Bsz, w.L, "" if not w.packed else
+                                 " packed in %d sequences %s" % (w.nseq, w.lengths),
+                                 w.H, w.P, w.N, w.G, w.Q),
+           "input_sha256": w.sha256,
+           "fwd": {"ms": round(fwd_med, 4), "ms_min": round(fwd_min, 4), "ms_max": round(fwd_max, 4),
+                   "ms_cold": round(tm.cold(w.fwd), 4),
+                   "tokens/s": round(w.tokens / (fwd_med * 1e-3), 1)}}
+    print("bench: %s fwd %.3f ms" % (label, fwd_med), file=sys.stderr, flush=True)
+    if w.with_bwd:
+        st_med, st_min, st_max = tm.trials(w.step, per)
+        res["fwd_bwd"] = {"ms": round(st_med, 4), "ms_min": round(st_min, 4), "ms_max": round(st_max, 4),
+                          "ms_cold": round(tm.cold(w.step), 4),
+                          "tokens/s": round(w.tokens / (st_med * 1e-3), 1),
+                          "bwd_ms": round(tm.trials(w.bwd_saved, per)[0], 4)}
+        print("bench: %s fwd+bwd %.3f ms" % (label, st_med), file=sys.stderr, flush=True)
+    res["kernels"] = kernel_table(w, tm, per, label + " ")
+    res["state_passing_ab"] = w.scan_ab(tm, per)
+    del w
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the SSD scan of one GPU's share); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mamba_ssd_chunked_03_amd import ssd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            ssd.util_copy(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}))
+        return
+    have_bwd = not args.fwd_only
+    w = Workload(2, dev, with_bwd=have_bwd)
+    tm = Timer(dev)
+    Bsz, L, H, P, N, G = w.Bsz, w.L, w.H, w.P, w.N, w.G
+    x, y = w.d["x"], w.y
 
     def step_recompute():
-        fwd()
-        bwd_recompute()
+        w.fwd()
+        w.bwd_recompute()
 
     print("bench: warmup %d, steps %d, bwd %s" % (args.warmup, args.steps, have_bwd), file=sys.stderr, flush=True)
-    ms_step, wall_step = timed(step, args.steps, args.warmup)
-    ms_fwd, _ = timed(fwd, args.steps, 2)
+    ms_step, wall_step = tm.timed(w.step, args.steps, args.warmup)
+    ms_fwd, _ = tm.timed(w.fwd, args.steps, 2)
     ms_bwd = ms_step_rc = None
     if have_bwd:
-        ms_fwd_save, _ = timed(fwd_save, args.steps, 2)
-        ms_bwd, _ = timed(bwd_saved, args.steps, 2)
-        ms_step_rc, _ = timed(step_recompute, args.steps, 2)
-    tokens = Bsz * L
+        ms_fwd_save, _ = tm.timed(w.fwd_save, args.steps, 2)
+        ms_bwd, _ = tm.timed(w.bwd_saved, args.steps, 2)
+        ms_step_rc, _ = tm.timed(step_recompute, args.steps, 2)
+    tokens = w.tokens
     print("bench: step %.3f ms (wall %.3f), fwd %.3f ms" % (ms_step, wall_step, ms_fwd), file=sys.stderr, flush=True)
-    step_med, step_min, step_max = trials(step, max(1, args.steps // 2))
-    step_cold = cold(step)
+    step_med, step_min, step_max = tm.trials(w.step, max(1, args.steps // 2))
+    step_cold = tm.cold(w.step)
     print("bench: step over 7 trials: median %.3f ms (min %.3f, max %.3f); cold %.3f ms"
           % (step_med, step_min, step_max, step_cold), file=sys.stderr, flush=True)
 
     # every kernel of the step on its own: the same launch (arguments, grid,
     # buffers) as inside the step, re-issued through the single-kernel flags
     kernels = {}
-    roof = None
+    roof = scan_ab = None
     if not args.no_kernels:
-        fwd_save()
-        bwd_saved()
-        torch.cuda.synchronize()
-        nck = ssd.num_chunks(prob, Q, 0)
-        nbytes = kernel_bytes(Bsz, L, H, P, N, G, Q, nck, Bsz, 2, init=init is not None,
-                              d_final=False)
-        nflops = kernel_flops(Bsz, L, H, P, N, G, Q, nck)
-        # where the chunk-state kernel forms C.B^T (and its transpose) itself, its
-        # bytes and flops are that kernel's and no C.B^T kernel is launched
-        fwd_mask = lib.ssd_fwd_kernel_mask(ctypes.byref(prob), Q, 0)
-        if not fwd_mask & 4:
-            nbytes["chunk_state"] += nbytes["bmm_chunk"] - Bsz * L * G * N * 2  # (B is read once)
-            nflops["chunk_state"] += nflops["bmm_chunk"]
-        fns = {}
-        for k, name in enumerate(ssd.FWD_KERNELS, 1):
-            if not fwd_mask & (1 << (k - 1)):
-                continue
-            fns[name] = ssd.fwd(x, dt, A, Bm, Cm, workspace=ws_b, out=y, final=final,
-                                save_for_backward=True, only_kernel=k, prepare=True, **common)[0]
-        for k, name in enumerate(ssd.BWD_KERNELS, 1):
-            fns[name] = ssd.bwd(x, dt, A, Bm, Cm, dout, workspace=ws_b, from_saved=True, grads=grads,
-                                only_kernel=k, prepare=True, **common)[0]
-        for name, fn in fns.items():
-            ms, ms_min, ms_max = trials(fn, max(1, args.steps // 2))
-            ms_cold = cold(fn)
-            gbs = nbytes[name] / (ms * 1e-3) / 1e9
-            e = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_max": round(ms_max, 4),
-                 "ms_cold": round(ms_cold, 4), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
-                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                 "frac_hbm_cold": round(nbytes[name] / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-            if name in nflops:
-                tf = nflops[name] / (ms * 1e-3) / 1e12
-                e["alg_tflops"] = round(tf, 1)
-                e["frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
-            kernels[name] = e
-            print("bench: kernel %-22s %.4f ms (cold %.4f)  %.0f GB/s" % (name, ms, ms_cold, gbs),
-                  file=sys.stderr, flush=True)
-        dom = max(kernels, key=lambda k: kernels[k]["ms"])
+        kernels = kernel_table(w, tm, max(1, args.steps // 2))
+        names = [n for n in kernels if not n.startswith("_")]
+        dom = max(names, key=lambda k: kernels[k]["ms"])
         s = kernels[dom]
         roof = {"kernel": dom, "bound": "hbm", "achieved": s["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": s["frac_hbm"], "traffic": load_traffic(dom),
                 "alg_bytes_per_launch": s["alg_bytes"], "avg_launch_ms": s["ms"]}
-        def aggregate(names):
-            b = sum(kernels[n]["alg_bytes"] for n in names)
-            t = sum(kernels[n]["ms"] for n in names)
-            tc = sum(kernels[n]["ms_cold"] for n in names)
-            return {"ms": round(t, 4), "alg_bytes": b, "GB/s": round(b / (t * 1e-3) / 1e9, 1),
-                    "frac_hbm": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "frac_hbm_cold": round(b / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        names = [n for n in kernels]
-        kernels["_forward_aggregate"] = aggregate([n for n in ssd.FWD_KERNELS if n in kernels])
-        kernels["_backward_aggregate"] = aggregate(list(ssd.BWD_KERNELS))
-        kernels["_all"] = aggregate(names)
+        scan_ab = w.scan_ab(tm, max(1, args.steps // 2))
 
     # the layer's gated RMSNorm on the SSD output (rows = batch x seqlen, dim =
     # heads x headdim, 8 groups of dim / 8 columns), gate and upstream gradient seeded
@@ -397,8 +546,8 @@ def main():
         norm = {"workload": "gated RMSNorm of the SSD output: %d rows x %d columns, groups of %d, "
                             "bf16" % (rows, dim, group)}
         for name, fn in (("fwd", nfwd), ("bwd", nbwd)):
-            ms, ms_min, ms_max = trials(fn, max(1, args.steps // 2))
-            ms_cold = cold(fn)
+            ms, ms_min, ms_max = tm.trials(fn, max(1, args.steps // 2))
+            ms_cold = tm.cold(fn)
             gbs = nb[name] / (ms * 1e-3) / 1e9
             norm[name] = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_max": round(ms_max, 4),
                           "ms_cold": round(ms_cold, 4), "alg_bytes": nb[name], "GB/s": round(gbs, 1),
@@ -408,6 +557,17 @@ def main():
                   file=sys.stderr, flush=True)
         norm["page_context"] = ("the pages' _layer_norm_bwd: 0.09 ms on one B200, bf16, batch 2, "
                                 "seqlen 8192 (layer dimensions not printed); another machine's number")
+
+    # the other full-size workloads, reported beside the headline (not the headline)
+    others = None
+    if not args.no_others:
+        sha = w.sha256
+        del w
+        torch.cuda.empty_cache()
+        others = {"long_context": other_workload(3, dev, tm, args.steps, "long context"),
+                  "packed": other_workload(4, dev, tm, args.steps, "packed sequences")}
+    else:
+        sha = w.sha256
 
     cpu = cpu_par = None
     if not args.no_cpu_baseline:
@@ -434,6 +594,7 @@ def main():
         "config": {"workload": "SSD layer %s, batch 2, seqlen 8192, 64 heads, headdim 64, "
                                "dstate 128, 8 groups, chunk 256" % ("fwd+bwd" if have_bwd else "fwd"),
                    "global_batch": Bsz, "seq_len": L, "parallelism": "single GPU"},
+        "input_sha256": sha,
         "fwd": {"ms": round(ms_fwd, 4), "tokens/s": round(tokens / (ms_fwd * 1e-3), 1)},
         "fwd_bwd": None if not have_bwd else {
             "ms": round(ms_step, 4), "fwd_save_ms": round(ms_fwd_save, 4), "bwd_ms": round(ms_bwd, 4),
@@ -449,6 +610,8 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_parallel": cpu_par,
         "gated_rmsnorm": norm,
+        "state_passing_ab": scan_ab,
+        "other_workloads": others,
     }
     print(json.dumps(out))
 

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 6
+#define SSD_ABI_VERSION 7
 
 typedef enum {
   SSD_OK = 0,
@@ -104,6 +104,14 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 /* SSD_FLAG_ONE_STREAM: every kernel of the call runs on `stream`; the library
  *   creates and uses no stream or event of its own.  Results are identical. */
 #define SSD_FLAG_ONE_STREAM 4
+/* SSD_FLAG_SEQUENTIAL_SCAN: the cross-chunk state passing (forward, and the reverse
+ *   pass of ssd_bwd) walks each sequence's chunks in order with one carry per state
+ *   element, the sequential loop that the associative scan replaces
+ *   (aitrends.kr/articles/109906, "Helion-based B200 kernel redesign"), instead of
+ *   the log-depth scan.  A comparison point for measurement; results agree with
+ *   the default to rounding (the association order differs).  Valid on ssd_fwd,
+ *   ssd_bwd and ssd_stage_state_passing. */
+#define SSD_FLAG_SEQUENTIAL_SCAN 8
 /* SSD_FLAG_BWD_KERNEL(k), k = 1..7: a profiling aid, valid only together with
  *   SSD_FLAG_FROM_SAVED.  ssd_bwd launches only its k-th kernel: 1 adjoint chunk
  *   states, 2 reverse state passing, 3 dx (with the direct delta gradient),

@@ -20,6 +20,8 @@
 
 using namespace ssd;
 
+static_assert(kFlagSequentialScan == SSD_FLAG_SEQUENTIAL_SCAN, "flag bit seen by the kernels");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -36,7 +38,7 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
   if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_ONE_STREAM |
-                    SSD_FLAG_BWD_KERNEL(7) | SSD_FLAG_FWD_KERNEL(7)))
+                    SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_BWD_KERNEL(7) | SSD_FLAG_FWD_KERNEL(7)))
     return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_BWD_KERNEL(7)) && !(pr->flags & SSD_FLAG_FROM_SAVED))
     return SSD_ERR_UNSUPPORTED;

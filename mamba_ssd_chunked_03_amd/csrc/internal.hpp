@@ -21,6 +21,10 @@ struct Prob {
   ChunkMap map;      // device view of the chunk layout (table pointers set when packed)
 };
 
+// Prob::flags bit (SSD_FLAG_SEQUENTIAL_SCAN of ssd.h): state passing, forward and
+// reverse, runs the sequential-carry kernel instead of the associative scan.
+constexpr int kFlagSequentialScan = 8;
+
 // mode of the chunk-state contraction
 enum { kStateFwd = 0,        // T_c = sum_j delta_j 2^(acs_last - acs_j) x_j B_j^T
        kStateDstates = 1,    // U_c = sum_i 2^(acs_i) dy_i C_i^T

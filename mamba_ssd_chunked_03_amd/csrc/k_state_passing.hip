@@ -151,6 +151,58 @@ __global__ __launch_bounds__(W * 64) void state_passing_kernel(ChunkMap m, int H
     *(float4*)(final_states + ((int64_t)s * H + h) * hstride + pn) = carry;
 }
 
+// The sequential-carry form, kept as the comparison point for the scan above (the
+// loop that the associative scan replaces): each lane owns 4 consecutive state
+// elements of one (sequence, head) and walks that sequence's chunks in order,
+// E = 2^l_c * E + T_c, writing the state entering each chunk; the next chunk's
+// loads are issued before the current one's update, so one chunk of loads is in
+// flight beside the dependent chain.  Same traffic as the scan (one read of T and
+// the decays, one write of the states); what differs is the dependency depth: the
+// chain is as long as the sequence's chunk count, and only B * H * P * N / 4 lanes
+// walk it.
+template <typename OutT, int REV>
+__global__ __launch_bounds__(256) void state_passing_seq_kernel(ChunkMap m, int H, int PN,
+                                                                const float* __restrict__ T,
+                                                                const float* __restrict__ decay,
+                                                                const float* __restrict__ init,
+                                                                OutT* __restrict__ Hout,
+                                                                float* __restrict__ final_states) {
+  constexpr bool reverse = REV != 0;
+  const int pn = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int h = blockIdx.y, s = blockIdx.z;
+  if (pn >= PN) return;  // (PN is a multiple of 4: every lane's 4 elements are in range)
+  const int64_t hoff = (int64_t)h * PN + pn;
+  const int64_t cstride = (int64_t)H * PN;
+  int c0, c1;
+  seq_chunks(m, s, c0, c1);
+  const int n = c1 - c0;
+  float4 E = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (init) E = *(const float4*)(init + (int64_t)s * H * PN + hoff);
+  auto chunk = [&](int i) { return reverse ? c1 - 1 - i : c0 + i; };
+  float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ln = 0.f;
+  if (n > 0) {
+    tn = *(const float4*)(T + (int64_t)chunk(0) * cstride + hoff);
+    ln = decay[(int64_t)chunk(0) * H + h];
+  }
+  for (int i = 0; i < n; ++i) {
+    const int c = chunk(i);
+    const float4 tv = tn;
+    const float lv = ln;
+    if (i + 1 < n) {
+      tn = *(const float4*)(T + (int64_t)chunk(i + 1) * cstride + hoff);
+      ln = decay[(int64_t)chunk(i + 1) * H + h];
+    }
+    store4(Hout + (int64_t)c * cstride + hoff, E);
+    const float a = exp2_fast(lv);
+    E.x = a * E.x + tv.x;
+    E.y = a * E.y + tv.y;
+    E.z = a * E.z + tv.z;
+    E.w = a * E.w + tv.w;
+  }
+  if (final_states) *(float4*)(final_states + (int64_t)s * H * PN + hoff) = E;
+}
+
 template <int W, int S>
 static void launch_sp(const Prob& p, dim3 grid, const float* states, const float* decay,
                       const float* init, void* passed, int passed_bf16, float* final_states,
@@ -174,8 +226,24 @@ hipError_t launch_state_passing(const Prob& p, const float* states, const float*
                                 const float* init, void* passed, int passed_bf16,
                                 float* final_states, int reverse, hipStream_t st) {
   const int PN = p.P * p.N;  // a multiple of 256 for every supported (P, N)
-  dim3 grid(PN / 256, p.H, p.nseq);
   if (p.nseq == 0) return hipSuccess;
+  if (p.flags & kFlagSequentialScan) {
+    const dim3 g((PN / 4 + 255) / 256, p.H, p.nseq);
+    if (passed_bf16 && reverse)
+      hipLaunchKernelGGL((state_passing_seq_kernel<uint16_t, 1>), g, dim3(256), 0, st, p.map, p.H, PN,
+                         states, decay, init, (uint16_t*)passed, final_states);
+    else if (passed_bf16)
+      hipLaunchKernelGGL((state_passing_seq_kernel<uint16_t, 0>), g, dim3(256), 0, st, p.map, p.H, PN,
+                         states, decay, init, (uint16_t*)passed, final_states);
+    else if (reverse)
+      hipLaunchKernelGGL((state_passing_seq_kernel<float, 1>), g, dim3(256), 0, st, p.map, p.H, PN,
+                         states, decay, init, (float*)passed, final_states);
+    else
+      hipLaunchKernelGGL((state_passing_seq_kernel<float, 0>), g, dim3(256), 0, st, p.map, p.H, PN,
+                         states, decay, init, (float*)passed, final_states);
+    return hipGetLastError();
+  }
+  dim3 grid(PN / 256, p.H, p.nseq);
   // segment shape from the longest chunk run a sequence can have
   const int64_t ncs = p.packed ? p.nck : (p.nck / (p.B > 0 ? p.B : 1));
   if (ncs <= 8)

@@ -28,7 +28,7 @@ class NormProblem(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
 
 
-FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED, FLAG_ONE_STREAM = 1, 2, 4
+FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED, FLAG_ONE_STREAM, FLAG_SEQUENTIAL_SCAN = 1, 2, 4, 8
 BWD_KERNELS = ("dstates", "reverse_state_passing", "bwd_dx", "bwd_dcb", "bwd_dc", "bwd_db",
                "bwd_finalize")
 
@@ -70,7 +70,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lib = None
 
@@ -203,7 +203,7 @@ def num_chunks(prob, chunk_size, packed):
 
 def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
         dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False,
-        only_kernel=0, prepare=False, one_stream=False):
+        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False):
     """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h.
 
     save_for_backward: keep the intermediates in ``workspace`` (which must hold
@@ -214,7 +214,9 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     prepare: launch nothing; return (launch, out, final) where launch() issues the
     call with the arguments marshalled here (timing loops).
     one_stream: queue every kernel on the current stream (the library then uses no
-    stream of its own)."""
+    stream of its own).
+    sequential_scan: the state passing walks the chunks with a sequential carry
+    instead of the associative scan (a comparison point)."""
     if only_kernel and (workspace is None or out is None):
         raise ValueError("only_kernel needs the workspace and outputs of a complete call")
     batch, seqlen, H, P, G, N, nst, io = _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens)
@@ -225,7 +227,8 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     dev = _dev(x, dt, A, B, C, D, dt_bias, init, cu_seqlens, workspace, out, final)
     prob = problem(x, B, cu_seqlens, dt_softplus,
                    (FLAG_SAVE_FOR_BWD if save_for_backward else 0) | FLAG_FWD_KERNEL(only_kernel) |
-                   (FLAG_ONE_STREAM if one_stream else 0))
+                   (FLAG_ONE_STREAM if one_stream else 0) |
+                   (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0))
     L = lib()
     packed = int(cu_seqlens is not None)
     if save_for_backward:
@@ -279,7 +282,7 @@ def fwd_noalloc(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None
 
 def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
         chunk_size=256, dt_softplus=True, workspace=None, from_saved=False, grads=None,
-        only_kernel=0, prepare=False, one_stream=False):
+        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False):
     """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors).
 
     from_saved: ``workspace`` holds the intermediates of a save_for_backward
@@ -309,7 +312,7 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_
     if only_kernel and (not from_saved or grads is None):
         raise ValueError("only_kernel needs from_saved and the grads of a complete call")
     flags = (FLAG_FROM_SAVED if from_saved else 0) | FLAG_BWD_KERNEL(only_kernel) | \
-        (FLAG_ONE_STREAM if one_stream else 0)
+        (FLAG_ONE_STREAM if one_stream else 0) | (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0)
     prob = problem(x, B, cu_seqlens, dt_softplus, flags)
     L = lib()
     packed = int(cu_seqlens is not None)
@@ -401,7 +404,8 @@ class Stages:
                    self.Q, _ptr(T), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return T
 
-    def state_passing(self, T, decay, init=None, out=None):
+    def state_passing(self, T, decay, init=None, out=None, sequential=False):
+        """sequential: the sequential-carry kernel instead of the associative scan"""
         p = self.prob
         nst = p.nseq if self.packed else p.batch
         Hp, final = out or (self._f(self.nck, p.nheads, p.headdim, p.dstate),
@@ -410,8 +414,13 @@ class Stages:
         self._need((T, "states", *s["state"], True), (decay, "chunk_decay", *s["decay"], True),
                    (init, "init", *s["init"], False), (Hp, "passed", *s["state"], True),
                    (final, "final", *s["init"], False))
-        self._call("ssd_stage_state_passing", _ptr(T), _ptr(decay), _ptr(init), _ptr(self.cu), self.Q,
-                   _ptr(Hp), _ptr(final), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
+        prob = self.prob
+        if sequential:
+            prob = Problem(*[getattr(p, n) for n, _ in Problem._fields_])
+            prob.flags = p.flags | FLAG_SEQUENTIAL_SCAN
+        _check(lib().ssd_stage_state_passing(ctypes.byref(prob), _ptr(T), _ptr(decay), _ptr(init),
+                                             _ptr(self.cu), self.Q, _ptr(Hp), _ptr(final), _ptr(self.ws),
+                                             self.ws.numel(), _stream(self.dev)))
         return Hp, final
 
     def bmm_chunk(self, B, C, out=None):

@@ -325,3 +325,20 @@ def test_one_stream_flag_gives_identical_results():
         assert torch.equal(y0, y1) and torch.equal(f0, f1), Q
         for k in KEYS:
             assert torch.equal(g0[k], g1[k]), (Q, k)
+
+
+def test_bwd_sequential_scan():
+    """ssd_bwd with the sequential-carry reverse state passing, against the oracle
+    (batched ragged and packed with an empty sequence)."""
+    inp = inputs.make_inputs(2, 700, 16, 64, 128, 2, io="bf16", init="randn", bwd=True,
+                             d_final=True, seed=83)
+    g = gpu_bwd(ssd, inp, 256, sequential_scan=True)
+    torch.cuda.synchronize()
+    check(g, oracle_bwd(inp), "bf16", "sequential batched")
+    lengths = [1, 0, 300, 513, 77]
+    inp = inputs.make_inputs(1, sum(lengths), 4, 64, 128, 2, io="bf16", init="randn", bwd=True,
+                             d_final=True, lengths=lengths, seed=84)
+    g = gpu_bwd(ssd, inp, 128, sequential_scan=True)
+    torch.cuda.synchronize()
+    check(g, oracle_bwd(inp), "bf16", "sequential packed")
+    assert torch.equal(g["d_init"][1].cpu(), inp["d_final"][1])

@@ -359,3 +359,45 @@ def test_fwd_cb_in_chunk_state_scan_only(lengths):
     y_ref, f_ref = recurrence.fwd(**oracle_args(inp))
     assert normwise(np64(y), y_ref) <= 1e-2
     assert normwise(np64(final), f_ref) <= 1e-3
+
+
+# ------------------------------------- sequential-carry state passing (A/B) ----
+@pytest.mark.parametrize("kw,lengths,Q", STAGE_KW)
+def test_stage_state_passing_sequential(kw, lengths, Q):
+    """The sequential-carry kernel (SSD_FLAG_SEQUENTIAL_SCAN) on the oracle's chunk
+    states: same gates as the associative scan's stage test."""
+    inp, o, mid, st, nk = stage_case(kw, lengths, Q)
+    d = to_dev(inp)
+    f32 = lambda a: torch.tensor(a, dtype=torch.float32, device="cuda")
+    nck = st.nck
+    pad = lambda a: np.concatenate([a, np.zeros((nck - nk,) + a.shape[1:])]) if nck > nk else a
+    last = np.array([mid["acs"][k, :, ch["len"] - 1] for k, ch in enumerate(mid["chunks"])])
+    o_decay = f32(pad(last * LOG2E)) if nk else torch.zeros(nck, kw["nheads"], device="cuda")
+    Hp, final = st.state_passing(f32(pad(mid["T"])), o_decay, d["init"], sequential=True)
+    torch.cuda.synchronize()
+    _, f_ref = chunked.state_passing(mid["T"], mid["acs"], mid["chunks"],
+                                     len(lengths) if lengths else kw["batch"], o["init"])
+    assert normwise(np64(Hp)[:nk], mid["Hin"]) <= 1e-5
+    assert normwise(np64(final), f_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("case", ["ragged", "packed", "long_context"])
+def test_fwd_sequential_scan(case):
+    """ssd_fwd with the sequential-carry state passing, against the oracle."""
+    if case == "ragged":
+        inp = inputs.make_inputs(2, 700, 16, 64, 128, 2, io="bf16", init="randn", seed=81)
+        heads, Q = None, 256
+    elif case == "packed":
+        inp = inputs.make_inputs(1, 891, 4, 64, 128, 2, io="bf16", init="randn", seed=82,
+                                 lengths=[1, 0, 300, 513, 77])
+        heads, Q = None, 128
+    else:
+        inp = inputs.config_inputs(3)   # 512 chunks: the longest carry chain
+        heads, Q = [9, 31], 256
+    y, final = gpu_fwd(ssd, inp, Q, sequential_scan=True)
+    torch.cuda.synchronize()
+    y_ref, f_ref = recurrence.fwd(**oracle_args(inp), heads=heads)
+    if heads is not None:
+        y, final = y[:, :, heads], final[:, heads]
+    assert bf16_excess(np64(y), y_ref) <= 2e-2
+    assert normwise(np64(final), f_ref) <= 1e-3
