@@ -274,30 +274,36 @@ class Workload:
                                     grads=self.grads, only_kernel=k, prepare=True, **self.common)[0]
         return fns
 
+    def assoc_variant(self):
+        """The associative-scan segment shape sized to this workload's chains
+        (the library's rule when it has no tuned table)."""
+        chain = self.chunks() // self.nseq
+        return 1 if chain <= 8 else 2 if chain <= 32 else 3 if chain <= 64 else 4
+
     def scan_ab(self, tm, per):
-        """The state-passing kernels timed alone as the associative scan (default) and
-        as the sequential-carry loop it replaces (SSD_FLAG_SEQUENTIAL_SCAN), on the
-        same buffers: warm and cold ms and the fraction of 8 TB/s of each."""
+        """The state-passing kernels timed alone as the log-depth associative scan
+        (segments sized to the chains), as the plain sequential-carry loop it
+        replaces (SSD_FLAG_SEQUENTIAL_SCAN), and as the tuned table's choice (the
+        default), on the same buffers: warm and cold ms and fraction of 8 TB/s."""
         from mamba_ssd_chunked_03_amd import ssd
         nbytes, _ = self.alg()
         res = {}
-        for seq in (False, True):
+        for key, v in (("associative", self.assoc_variant()), ("sequential", 5), ("table", 0)):
             self.fwd_save()
             if self.with_bwd:
                 self.bwd_saved()
             runs = {"state_passing": ssd.fwd(*self.args, workspace=self.ws_b, out=self.y, final=self.final,
-                                             save_for_backward=True, only_kernel=2, sequential_scan=seq,
+                                             save_for_backward=True, only_kernel=2, scan_variant=v,
                                              prepare=True, **self.common)[0]}
             if self.with_bwd:
                 runs["reverse_state_passing"] = ssd.bwd(*self.args, self.d["dout"], workspace=self.ws_b,
                                                         from_saved=True, grads=self.grads, only_kernel=2,
-                                                        sequential_scan=seq, prepare=True, **self.common)[0]
+                                                        scan_variant=v, prepare=True, **self.common)[0]
             for name, fn in runs.items():
                 ms = tm.trials(fn, per)[0]
                 ms_cold = tm.cold(fn)
                 e = res.setdefault(name, {"alg_bytes": nbytes[name]})
-                key = "sequential" if seq else "associative"
-                e[key] = {"ms": round(ms, 4), "ms_cold": round(ms_cold, 4),
+                e[key] = {"variant": v, "ms": round(ms, 4), "ms_cold": round(ms_cold, 4),
                           "frac_hbm": round(nbytes[name] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "frac_hbm_cold": round(nbytes[name] / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                 print("bench: %s %-12s %.4f ms (cold %.4f)" % (name, key, ms, ms_cold), file=sys.stderr,

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 7
+#define SSD_ABI_VERSION 8
 
 typedef enum {
   SSD_OK = 0,
@@ -112,6 +112,16 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   the default to rounding (the association order differs).  Valid on ssd_fwd,
  *   ssd_bwd and ssd_stage_state_passing. */
 #define SSD_FLAG_SEQUENTIAL_SCAN 8
+/* SSD_FLAG_SCAN_VARIANT(v), v = 0..7: which kernel runs the cross-chunk state
+ *   passing (forward and reverse).  0 (the default) takes the library's tuned
+ *   per-shape table (measured on this GPU by mamba_ssd_chunked_03_amd/tuning/sweep.py,
+ *   compiled into the library): the analogue of the pages' configuration files
+ *   written by an offline sweep and loaded at training time (aitrends.kr/articles/
+ *   109906, "putting autotune results into the training pipeline").  1..4: the
+ *   log-depth associative scan with W waves x S chunks per wave of
+ *   4x2, 8x4, 16x4, 16x8; 5..7: the sequential carry with 1, 4, 8 chunks of loads
+ *   in flight (5 is SSD_FLAG_SEQUENTIAL_SCAN).  Results agree to rounding. */
+#define SSD_FLAG_SCAN_VARIANT(v) ((v) << 16)
 /* SSD_FLAG_BWD_KERNEL(k), k = 1..7: a profiling aid, valid only together with
  *   SSD_FLAG_FROM_SAVED.  ssd_bwd launches only its k-th kernel: 1 adjoint chunk
  *   states, 2 reverse state passing, 3 dx (with the direct delta gradient),
@@ -150,6 +160,12 @@ const char* ssd_status_string(int32_t status);
  * of a group's heads holds one 64-row block of the chunk's C.B^T).  A profiling and
  * accounting aid; the results do not depend on it.  Returns 0 for an invalid problem. */
 int32_t ssd_fwd_kernel_mask(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+
+/* Which state-passing kernel (SSD_FLAG_SCAN_VARIANT numbering, 1..7) ssd_fwd and
+ * ssd_bwd run for this problem: the variant forced by problem->flags, else the
+ * tuned table's entry nearest to the problem's chunks per sequence and lane count
+ * (sequences x nheads x headdim x dstate / 4).  0 for an invalid problem. */
+int32_t ssd_scan_variant(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 
 /* Number of chunk slots the per-chunk stage arrays below must hold:
  * batch * ceil(seqlen / chunk_size), or floor((seqlen + nseq*(chunk_size-1)) / chunk_size)

@@ -21,6 +21,8 @@
 using namespace ssd;
 
 static_assert(kFlagSequentialScan == SSD_FLAG_SEQUENTIAL_SCAN, "flag bit seen by the kernels");
+static_assert(kScanVariantShift == 16 && SSD_FLAG_SCAN_VARIANT(1) == 1 << kScanVariantShift,
+              "variant field seen by the kernels");
 
 namespace {
 
@@ -38,8 +40,11 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
   if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_ONE_STREAM |
-                    SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_BWD_KERNEL(7) | SSD_FLAG_FWD_KERNEL(7)))
+                    SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_BWD_KERNEL(7) | SSD_FLAG_FWD_KERNEL(7) |
+                    SSD_FLAG_SCAN_VARIANT(15)))
     return SSD_ERR_UNSUPPORTED;
+  if (((pr->flags >> 16) & 15) > 7) return SSD_ERR_UNSUPPORTED;
+  if ((pr->flags & SSD_FLAG_SEQUENTIAL_SCAN) && ((pr->flags >> 16) & 15) != 0) return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_BWD_KERNEL(7)) && !(pr->flags & SSD_FLAG_FROM_SAVED))
     return SSD_ERR_UNSUPPORTED;
   if (((pr->flags >> 12) & 7) > 4) return SSD_ERR_UNSUPPORTED;
@@ -286,6 +291,12 @@ int64_t ssd_num_chunks(const ssd_problem* pr, int32_t Q, int32_t packed) {
   Prob p;
   if (make_prob(pr, Q, packed, p) != SSD_OK) return -1;
   return p.nck;
+}
+
+int32_t ssd_scan_variant(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
+  return scan_variant_for(p);
 }
 
 int32_t ssd_fwd_kernel_mask(const ssd_problem* pr, int32_t Q, int32_t packed) {

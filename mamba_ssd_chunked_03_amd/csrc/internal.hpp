@@ -24,6 +24,14 @@ struct Prob {
 // Prob::flags bit (SSD_FLAG_SEQUENTIAL_SCAN of ssd.h): state passing, forward and
 // reverse, runs the sequential-carry kernel instead of the associative scan.
 constexpr int kFlagSequentialScan = 8;
+// Prob::flags bits 16..19 (SSD_FLAG_SCAN_VARIANT of ssd.h): the state-passing
+// kernel, 0 = the tuned table's choice (scan_variant_for below).
+constexpr int kScanVariantShift = 16;
+enum { kScanTable = 0, kScanAssoc4x2 = 1, kScanAssoc8x4 = 2, kScanAssoc16x4 = 3, kScanAssoc16x8 = 4,
+       kScanSeq1 = 5, kScanSeq4 = 6, kScanSeq8 = 7 };
+// The variant a problem's state passing runs: the flag's choice, else the tuned
+// table's entry nearest to the problem's chain length and lane count.
+int scan_variant_for(const Prob& p);
 
 // mode of the chunk-state contraction
 enum { kStateFwd = 0,        // T_c = sum_j delta_j 2^(acs_last - acs_j) x_j B_j^T

@@ -35,10 +35,9 @@
 //
 // fp32 path: one thread per (token, p), plain loops.
 #include "internal.hpp"
+#include "scan_rows.hpp"
 
 namespace ssd {
-
-constexpr int kScanWaves = 8;
 
 // HT: element type of the passed states (fp32, or bf16 from the fused forward)
 template <int P, int N, typename HT>
@@ -47,7 +46,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     const uint16_t* __restrict__ CB, const float* __restrict__ delta,
     const float* __restrict__ acs, const HT* __restrict__ Hs, const float* __restrict__ D,
     uint16_t* __restrict__ Y) {
-  constexpr int QMAX = 256, LDX = P + 8, HLD = N + 8;
+  using Rows = ScanRows<P, N>;
+  constexpr int QMAX = Rows::QMAX, LDX = Rows::LDX, HLD = Rows::HLD;
   __shared__ __attribute__((aligned(16))) uint16_t xs[QMAX * LDX];
   __shared__ __attribute__((aligned(16))) uint16_t hs[P * HLD];
   __shared__ float sa[QMAX], sd[QMAX];
@@ -59,39 +59,23 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
   if (ci.len <= 0) return;
   const int Q = m.Q, len = ci.len;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int q = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x;
   const int64_t kh = (int64_t)k * H + h;
   const int64_t xrow = (int64_t)H * P, crow = (int64_t)G * N;
   const uint16_t* xb = X + (int64_t)ci.start * xrow + (int64_t)h * P;
-  const uint16_t* cb = Cm + (int64_t)ci.start * crow + (int64_t)g * N;
-  const uint16_t* cbm = CB + ((int64_t)k * G + g) * Q * Q;
 
-  // Row blocks of this wave (snake order), and their C / CB fragments: the next
-  // row block's are loaded before the current one's stores, so the wait for
-  // them does not also wait for those stores (one in-order memory counter);
-  // the first row block's are in flight during the prologue.
-  const int NB = Q / 16, nii = (NB + kScanWaves - 1) / kScanWaves;
-  auto rb_of = [&](int ii) { return kScanWaves * ii + ((ii & 1) ? (kScanWaves - 1 - w) : w); };
-  auto live = [&](int ii) { return ii < nii && rb_of(ii) < NB && rb_of(ii) * 16 < len; };
-  // (the diagonal fragment has its own register: indexing the array with the
-  // run-time block index would become a select over every element)
-  // Buffer resources over the chunk's valid rows: rows past its end read as
-  // zero and are not written.
-  const brsrc rcm = make_rsrc(cb, (uint32_t)(len * crow * 2)), rcb = make_rsrc(cbm, (uint32_t)(len * Q * 2));
-  const brsrc ry = make_rsrc(Y + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
-  u32x4 cf[N / 32], cbf[QMAX / 32], cbd;
-  auto load_rb = [&](int rb) {
-    const uint32_t irow = rb * 16 + r, nb = rb / 2;
-    const uint32_t co = irow * (uint32_t)(crow * 2) + q * 16, bo = irow * (uint32_t)(Q * 2) + q * 16;
-#pragma unroll
-    for (int kb = 0; kb < N / 32; ++kb) cf[kb] = buf_load16(rcm, co + 64 * kb);
-#pragma unroll
-    for (int sx = 0; sx < QMAX / 32; ++sx)
-      cbf[sx] = (sx < (int)nb) ? buf_load16(rcb, bo + 64 * sx) : u32x4{0u, 0u, 0u, 0u};
-    cbd = buf_load16(rcb, bo + 64 * nb);
-  };
-  if (live(0)) load_rb(rb_of(0));
+  Rows rows;
+  rows.xs = xs;
+  rows.hs = hs;
+  rows.sa = sa;
+  rows.sd = sd;
+  rows.vt = &vt[0][0];
+  rows.init(Cm + (int64_t)ci.start * crow + (int64_t)g * N, crow, CB + ((int64_t)k * G + g) * Q * Q,
+            Y + (int64_t)ci.start * xrow + (int64_t)h * P, xrow, Q, len, tid, D ? D[h] : 0.f);
+  // the first row block's C and C.B^T fragments are in flight during the prologue;
+  // the next one's are loaded before the current one's stores, so the wait for them
+  // does not also wait for those stores (one in-order memory counter)
+  rows.prefetch_first();
   {
     // every prologue load in flight before the first LDS store waits on one
     static_assert(QMAX <= kScanWaves * 64, "one acs/delta value per thread");
@@ -113,117 +97,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
     }
   }
   __syncthreads();
-  // column factors for anchor e = 32b - 1: 2^(acs_e - acs_j) delta_j for j <= e
-  for (int idx = tid; idx < (Q / 32) * Q; idx += kScanWaves * 64) {
-    const int b = idx / Q, j = idx % Q;
-    vt[b][j] = (b > 0 && j < 32 * b) ? exp2_fast(sa[32 * b - 1] - sa[j]) * sd[j] : 0.f;
-  }
+  Rows::column_factors(&vt[0][0], sa, sd, Q, tid);
   __syncthreads();
-
-  const float Dh = D ? D[h] : 0.f;
-  for (int ii = 0; ii < nii; ++ii) {
-    if (!live(ii)) continue;  // chunk sizes with fewer row blocks than wavefronts, short chunks
-    const int rb = rb_of(ii);
-    const int i0 = rb * 16;
-    const int irow = i0 + r;  // the output row of this lane
-    const bool rowok = irow < len;
-    const int nb = i0 / 32;   // 32-token blocks strictly before the diagonal block
-    const float ae = nb > 0 ? sa[32 * nb - 1] : 0.f;
-    // The products are issued with the operands swapped, so each lane holds the
-    // transposed tile: acc[tp][rr] = y[i0 + r][pcol(tp, 4 q + rr)].  A row
-    // factor is then one value per lane, and acc[2s], acc[2s + 1] are the
-    // lane's 8 adjacent outputs 32 s + 8 q .. +7.
-    f32x4 acc[P / 16];
-#pragma unroll
-    for (int tp = 0; tp < P / 16; ++tp) acc[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // 1. state carried in, pre-scaled by 2^acs_e
-#pragma unroll
-    for (int kb = 0; kb < N / 32; ++kb)
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(as_bf16x8(*(const u32x4*)(hs + pcol(tp, r) * HLD + kb * 32 + q * 8)),
-                            as_bf16x8(cf[kb]), acc[tp]);
-    {
-      const float s0 = exp2_fast(ae);
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= s0;
-    }
-    // 2. blocks before the diagonal block, through the anchor's column factors
-    const float* vrow = &vt[nb][0];
-#pragma unroll
-    for (int sx = 0; sx < QMAX / 32; ++sx) {
-      if (sx < nb) {
-        const float4 f0 = *(const float4*)(vrow + sx * 32 + q * 8);
-        const float4 f1 = *(const float4*)(vrow + sx * 32 + q * 8 + 4);
-        u32x4 av;
-        av[0] = pack_bf2(bf_lo(cbf[sx][0]) * f0.x, bf_hi(cbf[sx][0]) * f0.y);
-        av[1] = pack_bf2(bf_lo(cbf[sx][1]) * f0.z, bf_hi(cbf[sx][1]) * f0.w);
-        av[2] = pack_bf2(bf_lo(cbf[sx][2]) * f1.x, bf_hi(cbf[sx][2]) * f1.y);
-        av[3] = pack_bf2(bf_lo(cbf[sx][3]) * f1.z, bf_hi(cbf[sx][3]) * f1.w);
-        const bf16x8 a = as_bf16x8(av);
-#pragma unroll
-        for (int tp = 0; tp < P / 16; ++tp)
-          acc[tp] = mfma_bf16(frag_kmajor(xs + sx * 32 * LDX + tp * 16, LDX, lane), a, acc[tp]);
-      }
-    }
-    // 3. this lane's row factor 2^(acs_i - acs_e), which also turns 1.'s factor into 2^acs_i
-    {
-      const float u = rowok ? exp2_fast(sa[irow] - ae) : 0.f;
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= u;
-    }
-    // 4. the diagonal block, one exp per element
-    {
-      const float ai = sa[min(irow, Q - 1)];
-      u32x4 av;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int j0 = nb * 32 + q * 8 + 2 * d;
-        float v0 = bf_lo(cbd[d]) * exp2_fast(ai - sa[j0]) * sd[j0];
-        float v1 = bf_hi(cbd[d]) * exp2_fast(ai - sa[j0 + 1]) * sd[j0 + 1];
-        v0 = (j0 <= irow) ? v0 : 0.f;
-        v1 = (j0 + 1 <= irow) ? v1 : 0.f;
-        av[d] = pack_bf2(v0, v1);
-      }
-      const bf16x8 a = as_bf16x8(av);
-#pragma unroll
-      for (int tp = 0; tp < P / 16; ++tp)
-        acc[tp] = mfma_bf16(frag_kmajor(xs + nb * 32 * LDX + tp * 16, LDX, lane), a, acc[tp]);
-    }
-    if (live(ii + 1)) load_rb(rb_of(ii + 1));  // the fragments above are dead now
-    // 5. skip term; the lane's 8 adjacent outputs per tile pair are stored as whole
-    //    128-byte row spans (span_swap) where a row has two pieces per lane
-    {
-      const uint32_t yo = (uint32_t)irow * (uint32_t)(xrow * 2) + q * 16;
-      u32x4 ys_[P / 32];
-#pragma unroll
-      for (int s = 0; s < P / 32; ++s) {
-        const u32x4 xv = lds_cols8_perm(xs + irow * LDX, s, q);
-        f32x4 y0 = acc[2 * s], y1 = acc[2 * s + 1];
-        y0[0] += Dh * bf_lo(xv[0]);
-        y0[1] += Dh * bf_hi(xv[0]);
-        y0[2] += Dh * bf_lo(xv[1]);
-        y0[3] += Dh * bf_hi(xv[1]);
-        y1[0] += Dh * bf_lo(xv[2]);
-        y1[1] += Dh * bf_hi(xv[2]);
-        y1[2] += Dh * bf_lo(xv[3]);
-        y1[3] += Dh * bf_hi(xv[3]);
-        ys_[s] = pack_bf8(y0, y1);
-      }
-      if constexpr (P >= 64) {
-        const uint32_t ra = (uint32_t)(rb_of(ii) * 16 + (r & 7)), so = span_off(r, q);
-#pragma unroll
-        for (int m2 = 0; m2 < P / 64; ++m2) {
-          u32x4 a, b;
-          span_swap(r, ys_[2 * m2], ys_[2 * m2 + 1], a, b);
-          buf_store16(ry, ra * (uint32_t)(xrow * 2) + so + 128 * m2, a);
-          buf_store16(ry, (ra + 8) * (uint32_t)(xrow * 2) + so + 128 * m2, b);
-        }
-      } else {
-        buf_store16(ry, yo, ys_[0]);
-      }
-    }
-  }
+  rows.run();
 }
 
 __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(

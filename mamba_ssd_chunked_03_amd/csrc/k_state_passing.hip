@@ -28,6 +28,8 @@
 //    re-walks its segment from its carry, writing the states;
 //  * sequences longer than W*S chunks are processed block by block with the
 //    block's end state carried in LDS.
+#include <cmath>
+
 #include "internal.hpp"
 
 namespace ssd {
@@ -151,16 +153,18 @@ __global__ __launch_bounds__(W * 64) void state_passing_kernel(ChunkMap m, int H
     *(float4*)(final_states + ((int64_t)s * H + h) * hstride + pn) = carry;
 }
 
-// The sequential-carry form, kept as the comparison point for the scan above (the
-// loop that the associative scan replaces): each lane owns 4 consecutive state
-// elements of one (sequence, head) and walks that sequence's chunks in order,
-// E = 2^l_c * E + T_c, writing the state entering each chunk; the next chunk's
-// loads are issued before the current one's update, so one chunk of loads is in
-// flight beside the dependent chain.  Same traffic as the scan (one read of T and
-// the decays, one write of the states); what differs is the dependency depth: the
-// chain is as long as the sequence's chunk count, and only B * H * P * N / 4 lanes
-// walk it.
-template <typename OutT, int REV>
+// The sequential-carry form: each lane owns 4 consecutive state elements of one
+// (sequence, head) and walks that sequence's chunks in order,
+// E = 2^l_c * E + T_c, writing the state entering each chunk as it goes.  Same
+// traffic as the scan above (one read of T and the decays, one write of the
+// states); what differs is the dependency depth, as long as the sequence's chunk
+// count, walked by B * H * P * N / 4 independent lanes.  The loads do not depend
+// on the carry, so D chunks of them are kept in flight (a ring of D registers,
+// refilled as each is consumed; past the sequence's end the refill re-reads its
+// last chunk, which is never used) and the chain waits on memory only once per D
+// chunks.  D = 1 is the plain loop that the associative scan replaces
+// (SSD_FLAG_SEQUENTIAL_SCAN, the comparison point); deeper rings stream.
+template <typename OutT, int REV, int D>
 __global__ __launch_bounds__(256) void state_passing_seq_kernel(ChunkMap m, int H, int PN,
                                                                 const float* __restrict__ T,
                                                                 const float* __restrict__ decay,
@@ -179,28 +183,55 @@ __global__ __launch_bounds__(256) void state_passing_seq_kernel(ChunkMap m, int 
   float4 E = make_float4(0.f, 0.f, 0.f, 0.f);
   if (init) E = *(const float4*)(init + (int64_t)s * H * PN + hoff);
   auto chunk = [&](int i) { return reverse ? c1 - 1 - i : c0 + i; };
-  float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
-  float ln = 0.f;
   if (n > 0) {
-    tn = *(const float4*)(T + (int64_t)chunk(0) * cstride + hoff);
-    ln = decay[(int64_t)chunk(0) * H + h];
-  }
-  for (int i = 0; i < n; ++i) {
-    const int c = chunk(i);
-    const float4 tv = tn;
-    const float lv = ln;
-    if (i + 1 < n) {
-      tn = *(const float4*)(T + (int64_t)chunk(i + 1) * cstride + hoff);
-      ln = decay[(int64_t)chunk(i + 1) * H + h];
+    float4 buf[D];
+    float lb[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int c = chunk(min(u, n - 1));
+      buf[u] = *(const float4*)(T + (int64_t)c * cstride + hoff);
+      lb[u] = decay[(int64_t)c * H + h];
     }
-    store4(Hout + (int64_t)c * cstride + hoff, E);
-    const float a = exp2_fast(lv);
-    E.x = a * E.x + tv.x;
-    E.y = a * E.y + tv.y;
-    E.z = a * E.z + tv.z;
-    E.w = a * E.w + tv.w;
+    for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int i = i0 + u;
+        if (i < n) {  // (the same for every lane of the workgroup)
+          const float4 tv = buf[u];
+          const float lv = lb[u];
+          const int cn = chunk(min(i + D, n - 1));
+          buf[u] = *(const float4*)(T + (int64_t)cn * cstride + hoff);
+          lb[u] = decay[(int64_t)cn * H + h];
+          store4(Hout + (int64_t)chunk(i) * cstride + hoff, E);
+          const float a = exp2_fast(lv);
+          E.x = a * E.x + tv.x;
+          E.y = a * E.y + tv.y;
+          E.z = a * E.z + tv.z;
+          E.w = a * E.w + tv.w;
+        }
+      }
+    }
   }
   if (final_states) *(float4*)(final_states + (int64_t)s * H * PN + hoff) = E;
+}
+
+template <int D>
+static void launch_seq(const Prob& p, const float* states, const float* decay, const float* init,
+                       void* passed, int passed_bf16, float* final_states, int reverse, hipStream_t st) {
+  const int PN = p.P * p.N;
+  const dim3 g((PN / 4 + 255) / 256, p.H, p.nseq);
+  if (passed_bf16 && reverse)
+    hipLaunchKernelGGL((state_passing_seq_kernel<uint16_t, 1, D>), g, dim3(256), 0, st, p.map, p.H, PN,
+                       states, decay, init, (uint16_t*)passed, final_states);
+  else if (passed_bf16)
+    hipLaunchKernelGGL((state_passing_seq_kernel<uint16_t, 0, D>), g, dim3(256), 0, st, p.map, p.H, PN,
+                       states, decay, init, (uint16_t*)passed, final_states);
+  else if (reverse)
+    hipLaunchKernelGGL((state_passing_seq_kernel<float, 1, D>), g, dim3(256), 0, st, p.map, p.H, PN,
+                       states, decay, init, (float*)passed, final_states);
+  else
+    hipLaunchKernelGGL((state_passing_seq_kernel<float, 0, D>), g, dim3(256), 0, st, p.map, p.H, PN,
+                       states, decay, init, (float*)passed, final_states);
 }
 
 template <int W, int S>
@@ -222,38 +253,83 @@ static void launch_sp(const Prob& p, dim3 grid, const float* states, const float
                        p.H, PN, states, decay, init, (float*)passed, final_states);
 }
 
+// The tuned per-shape table: (chunks per sequence, independent lanes) -> variant,
+// measured by tuning/sweep.py and turned into tuned_table.inc by build.py.  An
+// empty table leaves the rule below.
+struct ScanEntry {
+  int32_t chunks;  // chunks per sequence of the measured shape
+  int64_t lanes;   // sequences x heads x headdim x dstate / 4 of the measured shape
+  int32_t variant;
+};
+#if __has_include("tuned_table.inc")
+#include "tuned_table.inc"
+#else
+static const ScanEntry kTunedScan[] = {{0, 0, 0}};
+static const int kTunedScanCount = 0;
+#endif
+
+int scan_variant_for(const Prob& p) {
+  const int v = (p.flags >> kScanVariantShift) & 15;
+  if (v != kScanTable) return v;
+  if (p.flags & kFlagSequentialScan) return kScanSeq1;
+  // chunks per sequence: exact for batched rows, the packed slots' average otherwise
+  const int64_t chain = p.packed ? (p.nck + p.nseq - 1) / (p.nseq > 0 ? p.nseq : 1)
+                                 : p.nck / (p.B > 0 ? p.B : 1);
+  const int64_t lanes = (int64_t)p.nseq * p.H * p.P * p.N / 4;
+  if (kTunedScanCount > 0 && chain > 0 && lanes > 0) {
+    // the nearest measured shape, distance in log2 of both coordinates
+    const double lc = std::log2((double)chain), ll = std::log2((double)lanes);
+    double best = 1e300;
+    int bv = kScanTable;
+    for (int i = 0; i < kTunedScanCount; ++i) {
+      const double dc = lc - std::log2((double)kTunedScan[i].chunks);
+      const double dl = ll - std::log2((double)kTunedScan[i].lanes);
+      const double d = dc * dc + dl * dl;
+      if (d < best) {
+        best = d;
+        bv = kTunedScan[i].variant;
+      }
+    }
+    if (bv >= kScanAssoc4x2 && bv <= kScanSeq8) return bv;
+  }
+  // no table: segments sized to the chain
+  if (chain <= 8) return kScanAssoc4x2;
+  if (chain <= 32) return kScanAssoc8x4;
+  if (chain <= 64) return kScanAssoc16x4;
+  return kScanAssoc16x8;
+}
+
 hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
                                 const float* init, void* passed, int passed_bf16,
                                 float* final_states, int reverse, hipStream_t st) {
   const int PN = p.P * p.N;  // a multiple of 256 for every supported (P, N)
   if (p.nseq == 0) return hipSuccess;
-  if (p.flags & kFlagSequentialScan) {
-    const dim3 g((PN / 4 + 255) / 256, p.H, p.nseq);
-    if (passed_bf16 && reverse)
-      hipLaunchKernelGGL((state_passing_seq_kernel<uint16_t, 1>), g, dim3(256), 0, st, p.map, p.H, PN,
-                         states, decay, init, (uint16_t*)passed, final_states);
-    else if (passed_bf16)
-      hipLaunchKernelGGL((state_passing_seq_kernel<uint16_t, 0>), g, dim3(256), 0, st, p.map, p.H, PN,
-                         states, decay, init, (uint16_t*)passed, final_states);
-    else if (reverse)
-      hipLaunchKernelGGL((state_passing_seq_kernel<float, 1>), g, dim3(256), 0, st, p.map, p.H, PN,
-                         states, decay, init, (float*)passed, final_states);
-    else
-      hipLaunchKernelGGL((state_passing_seq_kernel<float, 0>), g, dim3(256), 0, st, p.map, p.H, PN,
-                         states, decay, init, (float*)passed, final_states);
-    return hipGetLastError();
+  const dim3 grid(PN / 256, p.H, p.nseq);
+  switch (scan_variant_for(p)) {
+    case kScanAssoc4x2:
+      launch_sp<4, 2>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
+      break;
+    case kScanAssoc8x4:
+      launch_sp<8, 4>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
+      break;
+    case kScanAssoc16x4:
+      launch_sp<16, 4>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
+      break;
+    case kScanAssoc16x8:
+      launch_sp<16, 8>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
+      break;
+    case kScanSeq1:
+      launch_seq<1>(p, states, decay, init, passed, passed_bf16, final_states, reverse, st);
+      break;
+    case kScanSeq4:
+      launch_seq<4>(p, states, decay, init, passed, passed_bf16, final_states, reverse, st);
+      break;
+    case kScanSeq8:
+      launch_seq<8>(p, states, decay, init, passed, passed_bf16, final_states, reverse, st);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
-  dim3 grid(PN / 256, p.H, p.nseq);
-  // segment shape from the longest chunk run a sequence can have
-  const int64_t ncs = p.packed ? p.nck : (p.nck / (p.B > 0 ? p.B : 1));
-  if (ncs <= 8)
-    launch_sp<4, 2>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
-  else if (ncs <= 32)
-    launch_sp<8, 4>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
-  else if (ncs <= 64)
-    launch_sp<16, 4>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
-  else
-    launch_sp<16, 8>(p, grid, states, decay, init, passed, passed_bf16, final_states, reverse, st);
   return hipGetLastError();
 }
 

@@ -42,6 +42,13 @@ def FLAG_BWD_KERNEL(k):
     return int(k) << 8
 
 
+def FLAG_SCAN_VARIANT(v):
+    """State-passing kernel: 0 the tuned table's choice, 1..4 associative scan
+    (4x2, 8x4, 16x4, 16x8 waves x chunks), 5..7 sequential carry with 1, 4, 8
+    chunks of loads in flight."""
+    return int(v) << 16
+
+
 def FLAG_FWD_KERNEL(k):
     """ssd_fwd launches only its k-th kernel (1-based, order of FWD_KERNELS)."""
     return int(k) << 12
@@ -50,6 +57,7 @@ def FLAG_FWD_KERNEL(k):
 _SIGS = {
     "ssd_abi_version": ([], _I32),
     "ssd_fwd_kernel_mask": ([_P, _I32, _I32], _I32),
+    "ssd_scan_variant": ([_P, _I32, _I32], _I32),
     "ssd_status_string": ([_I32], ctypes.c_char_p),
     "ssd_num_chunks": ([_P, _I32, _I32], _I64),
     "ssd_fwd_workspace_bytes": ([_P, _I32, _I32], _SZ),
@@ -70,7 +78,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _lib = None
 
@@ -203,7 +211,7 @@ def num_chunks(prob, chunk_size, packed):
 
 def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
         dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False,
-        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False):
+        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0):
     """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h.
 
     save_for_backward: keep the intermediates in ``workspace`` (which must hold
@@ -216,7 +224,8 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     one_stream: queue every kernel on the current stream (the library then uses no
     stream of its own).
     sequential_scan: the state passing walks the chunks with a sequential carry
-    instead of the associative scan (a comparison point)."""
+    instead of the associative scan (a comparison point).
+    scan_variant: force a state-passing kernel (FLAG_SCAN_VARIANT); 0 = tuned table."""
     if only_kernel and (workspace is None or out is None):
         raise ValueError("only_kernel needs the workspace and outputs of a complete call")
     batch, seqlen, H, P, G, N, nst, io = _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens)
@@ -228,7 +237,7 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     prob = problem(x, B, cu_seqlens, dt_softplus,
                    (FLAG_SAVE_FOR_BWD if save_for_backward else 0) | FLAG_FWD_KERNEL(only_kernel) |
                    (FLAG_ONE_STREAM if one_stream else 0) |
-                   (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0))
+                   (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0) | FLAG_SCAN_VARIANT(scan_variant))
     L = lib()
     packed = int(cu_seqlens is not None)
     if save_for_backward:
@@ -282,7 +291,7 @@ def fwd_noalloc(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None
 
 def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
         chunk_size=256, dt_softplus=True, workspace=None, from_saved=False, grads=None,
-        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False):
+        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0):
     """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors).
 
     from_saved: ``workspace`` holds the intermediates of a save_for_backward
@@ -312,7 +321,8 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_
     if only_kernel and (not from_saved or grads is None):
         raise ValueError("only_kernel needs from_saved and the grads of a complete call")
     flags = (FLAG_FROM_SAVED if from_saved else 0) | FLAG_BWD_KERNEL(only_kernel) | \
-        (FLAG_ONE_STREAM if one_stream else 0) | (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0)
+        (FLAG_ONE_STREAM if one_stream else 0) | (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0) | \
+        FLAG_SCAN_VARIANT(scan_variant)
     prob = problem(x, B, cu_seqlens, dt_softplus, flags)
     L = lib()
     packed = int(cu_seqlens is not None)
@@ -404,8 +414,9 @@ class Stages:
                    self.Q, _ptr(T), _ptr(self.ws), self.ws.numel(), _stream(self.dev))
         return T
 
-    def state_passing(self, T, decay, init=None, out=None, sequential=False):
-        """sequential: the sequential-carry kernel instead of the associative scan"""
+    def state_passing(self, T, decay, init=None, out=None, sequential=False, variant=0):
+        """sequential: the sequential-carry kernel instead of the associative scan;
+        variant: force a state-passing kernel (FLAG_SCAN_VARIANT), 0 = tuned table"""
         p = self.prob
         nst = p.nseq if self.packed else p.batch
         Hp, final = out or (self._f(self.nck, p.nheads, p.headdim, p.dstate),
@@ -415,9 +426,9 @@ class Stages:
                    (init, "init", *s["init"], False), (Hp, "passed", *s["state"], True),
                    (final, "final", *s["init"], False))
         prob = self.prob
-        if sequential:
+        if sequential or variant:
             prob = Problem(*[getattr(p, n) for n, _ in Problem._fields_])
-            prob.flags = p.flags | FLAG_SEQUENTIAL_SCAN
+            prob.flags = p.flags | (FLAG_SEQUENTIAL_SCAN if sequential else 0) | FLAG_SCAN_VARIANT(variant)
         _check(lib().ssd_stage_state_passing(ctypes.byref(prob), _ptr(T), _ptr(decay), _ptr(init),
                                              _ptr(self.cu), self.Q, _ptr(Hp), _ptr(final), _ptr(self.ws),
                                              self.ws.numel(), _stream(self.dev)))

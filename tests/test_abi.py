@@ -141,6 +141,10 @@ def test_workspace(L):
 def test_flags(L):
     assert fwd_status(L, prob(flags=16)) == UNSUP  # an unknown bit
     assert fwd_status(L, prob(flags=ssd.FLAG_SEQUENTIAL_SCAN), ws_bytes=1) == WS  # accepted
+    assert fwd_status(L, prob(flags=ssd.FLAG_SCAN_VARIANT(7)), ws_bytes=1) == WS  # accepted
+    assert fwd_status(L, prob(flags=ssd.FLAG_SCAN_VARIANT(8))) == UNSUP
+    assert fwd_status(L, prob(flags=ssd.FLAG_SCAN_VARIANT(15))) == UNSUP
+    assert fwd_status(L, prob(flags=ssd.FLAG_SEQUENTIAL_SCAN | ssd.FLAG_SCAN_VARIANT(2))) == UNSUP
     assert fwd_status(L, prob(flags=ssd.FLAG_ONE_STREAM), ws_bytes=1) == WS  # accepted
     assert fwd_status(L, prob(flags=ssd.FLAG_BWD_KERNEL(3))) == UNSUP  # needs FROM_SAVED
     assert fwd_status(L, prob(flags=ssd.FLAG_BWD_KERNEL(8))) == UNSUP

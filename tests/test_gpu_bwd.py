@@ -327,18 +327,20 @@ def test_one_stream_flag_gives_identical_results():
             assert torch.equal(g0[k], g1[k]), (Q, k)
 
 
-def test_bwd_sequential_scan():
-    """ssd_bwd with the sequential-carry reverse state passing, against the oracle
-    (batched ragged and packed with an empty sequence)."""
+@pytest.mark.parametrize("variant", [5, 7, 2])
+def test_bwd_scan_variants(variant):
+    """ssd_bwd with the plain sequential carry (5), the streamed one (7) and an
+    associative scan (2) in the reverse state passing, against the oracle (batched
+    ragged, and packed with an empty sequence)."""
     inp = inputs.make_inputs(2, 700, 16, 64, 128, 2, io="bf16", init="randn", bwd=True,
                              d_final=True, seed=83)
-    g = gpu_bwd(ssd, inp, 256, sequential_scan=True)
+    g = gpu_bwd(ssd, inp, 256, scan_variant=variant)
     torch.cuda.synchronize()
-    check(g, oracle_bwd(inp), "bf16", "sequential batched")
+    check(g, oracle_bwd(inp), "bf16", "variant %d batched" % variant)
     lengths = [1, 0, 300, 513, 77]
     inp = inputs.make_inputs(1, sum(lengths), 4, 64, 128, 2, io="bf16", init="randn", bwd=True,
                              d_final=True, lengths=lengths, seed=84)
-    g = gpu_bwd(ssd, inp, 128, sequential_scan=True)
+    g = gpu_bwd(ssd, inp, 128, scan_variant=variant)
     torch.cuda.synchronize()
-    check(g, oracle_bwd(inp), "bf16", "sequential packed")
+    check(g, oracle_bwd(inp), "bf16", "variant %d packed" % variant)
     assert torch.equal(g["d_init"][1].cpu(), inp["d_final"][1])

@@ -362,10 +362,12 @@ def test_fwd_cb_in_chunk_state_scan_only(lengths):
 
 
 # ------------------------------------- sequential-carry state passing (A/B) ----
+@pytest.mark.parametrize("variant", range(1, 8))
 @pytest.mark.parametrize("kw,lengths,Q", STAGE_KW)
-def test_stage_state_passing_sequential(kw, lengths, Q):
-    """The sequential-carry kernel (SSD_FLAG_SEQUENTIAL_SCAN) on the oracle's chunk
-    states: same gates as the associative scan's stage test."""
+def test_stage_state_passing_variants(kw, lengths, Q, variant):
+    """Every state-passing kernel (SSD_FLAG_SCAN_VARIANT 1..7: the associative scan
+    at four segment shapes, the sequential carry with 1, 4, 8 chunks in flight) on
+    the oracle's chunk states: the gates of the stage test."""
     inp, o, mid, st, nk = stage_case(kw, lengths, Q)
     d = to_dev(inp)
     f32 = lambda a: torch.tensor(a, dtype=torch.float32, device="cuda")
@@ -373,7 +375,7 @@ def test_stage_state_passing_sequential(kw, lengths, Q):
     pad = lambda a: np.concatenate([a, np.zeros((nck - nk,) + a.shape[1:])]) if nck > nk else a
     last = np.array([mid["acs"][k, :, ch["len"] - 1] for k, ch in enumerate(mid["chunks"])])
     o_decay = f32(pad(last * LOG2E)) if nk else torch.zeros(nck, kw["nheads"], device="cuda")
-    Hp, final = st.state_passing(f32(pad(mid["T"])), o_decay, d["init"], sequential=True)
+    Hp, final = st.state_passing(f32(pad(mid["T"])), o_decay, d["init"], variant=variant)
     torch.cuda.synchronize()
     _, f_ref = chunked.state_passing(mid["T"], mid["acs"], mid["chunks"],
                                      len(lengths) if lengths else kw["batch"], o["init"])
@@ -381,9 +383,11 @@ def test_stage_state_passing_sequential(kw, lengths, Q):
     assert normwise(np64(final), f_ref) <= 1e-5
 
 
+@pytest.mark.parametrize("variant", [5, 7, 4])
 @pytest.mark.parametrize("case", ["ragged", "packed", "long_context"])
-def test_fwd_sequential_scan(case):
-    """ssd_fwd with the sequential-carry state passing, against the oracle."""
+def test_fwd_scan_variants(case, variant):
+    """ssd_fwd with the plain sequential carry (5), the streamed one (7) and the
+    widest associative scan (4), against the oracle."""
     if case == "ragged":
         inp = inputs.make_inputs(2, 700, 16, 64, 128, 2, io="bf16", init="randn", seed=81)
         heads, Q = None, 256
@@ -394,7 +398,7 @@ def test_fwd_sequential_scan(case):
     else:
         inp = inputs.config_inputs(3)   # 512 chunks: the longest carry chain
         heads, Q = [9, 31], 256
-    y, final = gpu_fwd(ssd, inp, Q, sequential_scan=True)
+    y, final = gpu_fwd(ssd, inp, Q, scan_variant=variant)
     torch.cuda.synchronize()
     y_ref, f_ref = recurrence.fwd(**oracle_args(inp), heads=heads)
     if heads is not None:

@@ -30,6 +30,10 @@ KERNELS = [
     ("k_bwd.hip", "_ZN3ssd18bwd_db_bf16_kernelILi64ELi128EEE"),
     ("k_bwd.hip", "_ZN3ssd19bwd_finalize_kernelE"),
     ("k_bmm.hip", "_ZN3ssd21bmm_chunk_bf16_kernelILi128ELb1EEE"),  # shapes without C.B^T in chunk_state
+    # the state passing the tuned table picks at the layer and packed workloads
+    ("k_state_passing.hip", "_ZN3ssd24state_passing_seq_kernelItLi0ELi1EEE"),
+    ("k_state_passing.hip", "_ZN3ssd24state_passing_seq_kernelItLi1ELi1EEE"),
+    ("k_state_passing.hip", "_ZN3ssd24state_passing_seq_kernelItLi0ELi4EEE"),
 ]
 
 _asm = {}
