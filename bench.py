@@ -274,6 +274,32 @@ class Workload:
                                     grads=self.grads, only_kernel=k, prepare=True, **self.common)[0]
         return fns
 
+    def chained_ab(self, tm, per):
+        """The fused single-pass forward (SSD_FLAG_CHAINED_FWD: C.B^T kernel, then one
+        kernel with the chunk carry handed from workgroup to workgroup) against the
+        staged forward, both plain and keeping the intermediates for the backward;
+        warm and cold ms."""
+        from mamba_ssd_chunked_03_amd import ssd
+        import ctypes
+        import torch
+        res = {}
+        for save in (False, True):
+            ws = self.ws_b if save else torch.empty_like(self.ws_b[:max(1, ssd.lib().ssd_fwd_workspace_bytes(
+                ctypes.byref(self.prob), self.Q, self.packed))])
+            for key, ch in (("staged", False), ("chained", True)):
+                fn = ssd.fwd(*self.args, workspace=ws, out=self.y, final=self.final, save_for_backward=save,
+                             chained=ch, prepare=True, **self.common)[0]
+                med, lo, hi = tm.trials(fn, per)
+                e = res.setdefault("save" if save else "plain", {})
+                e[key] = {"ms": round(med, 4), "ms_min": round(lo, 4), "ms_max": round(hi, 4),
+                          "ms_cold": round(tm.cold(fn), 4)}
+                print("bench: forward %s %-8s %.4f ms" % ("save " if save else "plain", key, med),
+                      file=sys.stderr, flush=True)
+        self.fwd_save()  # the workspace holds the default path's intermediates again
+        if self.with_bwd:
+            self.bwd_saved()
+        return res
+
     def assoc_variant(self):
         """The associative-scan segment shape sized to this workload's chains
         (the library's rule when it has no tuned table)."""
@@ -467,6 +493,7 @@ def other_workload(cfg_id, dev, tm, steps, label):
         print("bench: %s fwd+bwd %.3f ms" % (label, st_med), file=sys.stderr, flush=True)
     res["kernels"] = kernel_table(w, tm, per, label + " ")
     res["state_passing_ab"] = w.scan_ab(tm, per)
+    res["fused_chained_forward"] = w.chained_ab(tm, per)
     del w
     return res
 
@@ -521,7 +548,7 @@ def main():
     # every kernel of the step on its own: the same launch (arguments, grid,
     # buffers) as inside the step, re-issued through the single-kernel flags
     kernels = {}
-    roof = scan_ab = None
+    roof = scan_ab = chain_ab = None
     if not args.no_kernels:
         kernels = kernel_table(w, tm, max(1, args.steps // 2))
         names = [n for n in kernels if not n.startswith("_")]
@@ -531,6 +558,7 @@ def main():
                 "unit": "GB/s", "frac": s["frac_hbm"], "traffic": load_traffic(dom),
                 "alg_bytes_per_launch": s["alg_bytes"], "avg_launch_ms": s["ms"]}
         scan_ab = w.scan_ab(tm, max(1, args.steps // 2))
+        chain_ab = w.chained_ab(tm, max(1, args.steps // 2))
 
     # the layer's gated RMSNorm on the SSD output (rows = batch x seqlen, dim =
     # heads x headdim, 8 groups of dim / 8 columns), gate and upstream gradient seeded
@@ -617,6 +645,7 @@ def main():
         "cpu_baseline_parallel": cpu_par,
         "gated_rmsnorm": norm,
         "state_passing_ab": scan_ab,
+        "fused_chained_forward": chain_ab,
         "other_workloads": others,
     }
     print(json.dumps(out))

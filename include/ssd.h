@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 8
+#define SSD_ABI_VERSION 9
 
 typedef enum {
   SSD_OK = 0,
@@ -122,6 +122,20 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   4x2, 8x4, 16x4, 16x8; 5..7: the sequential carry with 1, 4, 8 chunks of loads
  *   in flight (5 is SSD_FLAG_SEQUENTIAL_SCAN).  Results agree to rounding. */
 #define SSD_FLAG_SCAN_VARIANT(v) ((v) << 16)
+/* SSD_FLAG_CHAINED_FWD: ssd_fwd runs the fused single-pass forward: after the
+ *   C.B^T kernel, one kernel forms each chunk's state, takes the state entering the
+ *   chunk from the previous chunk's workgroup (a chained scan: work is handed out
+ *   in chunk order, each chunk's carry-out published through memory with a release
+ *   store of a flag and picked up with an acquire), and writes the output, so the
+ *   chunk states and passed states never make a round trip through memory (scan
+ *   page, section 3, "kernel fusion" and "memory hierarchy": the chunk carry kept
+ *   on chip).  Every wait is bounded: a wait that runs out sets an error word
+ *   (ssd_fwd_chained_error) and the kernel still finishes.  Supported for bf16 io
+ *   with headdim in {32, 64, 128} and dstate in {64, 128} (SSD_ERR_UNSUPPORTED
+ *   otherwise), with or without SSD_FLAG_SAVE_FOR_BWD (the saved context is the one
+ *   ssd_bwd expects), not with SSD_FLAG_FWD_KERNEL.  All kernels run on `stream`.
+ *   Results agree with the default forward to rounding. */
+#define SSD_FLAG_CHAINED_FWD 16
 /* SSD_FLAG_BWD_KERNEL(k), k = 1..7: a profiling aid, valid only together with
  *   SSD_FLAG_FROM_SAVED.  ssd_bwd launches only its k-th kernel: 1 adjoint chunk
  *   states, 2 reverse state passing, 3 dx (with the direct delta gradient),
@@ -166,6 +180,12 @@ int32_t ssd_fwd_kernel_mask(const ssd_problem* problem, int32_t chunk_size, int3
  * tuned table's entry nearest to the problem's chunks per sequence and lane count
  * (sequences x nheads x headdim x dstate / 4).  0 for an invalid problem. */
 int32_t ssd_scan_variant(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+
+/* Byte offset, inside the workspace of an SSD_FLAG_CHAINED_FWD ssd_fwd call, of the
+ * int32 word that the call's fused kernel sets when a wait for the previous chunk's
+ * carry ran out (0: every wait ended normally; the results are then valid).  -1 for
+ * an invalid problem. */
+int64_t ssd_fwd_chained_error_offset(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 
 /* Number of chunk slots the per-chunk stage arrays below must hold:
  * batch * ceil(seqlen / chunk_size), or floor((seqlen + nseq*(chunk_size-1)) / chunk_size)

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "internal.hpp"
+#include "layout.hpp"
 #include "ssd.h"
 
 using namespace ssd;
@@ -26,8 +27,6 @@ static_assert(kScanVariantShift == 16 && SSD_FLAG_SCAN_VARIANT(1) == 1 << kScanV
 
 namespace {
 
-constexpr size_t kAlign = 256;
-inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool okdim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
@@ -40,9 +39,10 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
   if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_ONE_STREAM |
-                    SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_BWD_KERNEL(7) | SSD_FLAG_FWD_KERNEL(7) |
-                    SSD_FLAG_SCAN_VARIANT(15)))
+                    SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_CHAINED_FWD | SSD_FLAG_BWD_KERNEL(7) |
+                    SSD_FLAG_FWD_KERNEL(7) | SSD_FLAG_SCAN_VARIANT(15)))
     return SSD_ERR_UNSUPPORTED;
+  if ((pr->flags & SSD_FLAG_CHAINED_FWD) && (pr->flags & SSD_FLAG_FWD_KERNEL(7))) return SSD_ERR_UNSUPPORTED;
   if (((pr->flags >> 16) & 15) > 7) return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_SEQUENTIAL_SCAN) && ((pr->flags >> 16) & 15) != 0) return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_BWD_KERNEL(7)) && !(pr->flags & SSD_FLAG_FROM_SAVED))
@@ -90,56 +90,22 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
 }
 
 inline size_t esize(const Prob& p) { return p.io == SSD_BF16 ? 2 : 4; }
-// Passed states H_c and their adjoints dE_c: every consumer on the bf16 path
-// feeds them to bf16 matrix cores, so they are stored in bf16 there.
-inline size_t state_esize(const Prob& p) { return p.io == SSD_BF16 ? 2 : 4; }
 
-// Forward workspace layout (byte offsets, each 256-aligned).
-struct FwdLayout {
-  size_t tab, seq_off, delta, acs, decay, T, Hp, CB, end;
-};
-FwdLayout fwd_layout(const Prob& p) {
-  FwdLayout l;
-  size_t o = 0;
-  const size_t nck = (size_t)p.nck, H = p.H, st = (size_t)p.P * p.N;
-  l.tab = o;     o += p.packed ? up(nck * 16) : 0;
-  l.seq_off = o; o += p.packed ? up(((size_t)p.nseq + 1) * 4) : 0;
-  l.delta = o;   o += up(nck * H * p.Q * 4);
-  l.acs = o;     o += up(nck * H * p.Q * 4);
-  l.decay = o;   o += up(nck * H * 4);
-  l.T = o;       o += up(nck * H * st * 4);
-  l.Hp = o;      o += up(nck * H * st * state_esize(p));
-  l.CB = o;      o += up(nck * (size_t)p.G * p.Q * p.Q * esize(p));
-  l.end = o;
-  return l;
+LayoutDims dims(const Prob& p) {
+  LayoutDims d;
+  d.nck = p.nck;
+  d.H = p.H;
+  d.P = p.P;
+  d.N = p.N;
+  d.G = p.G;
+  d.Q = p.Q;
+  d.nseq = p.nseq;
+  d.packed = p.packed != 0;
+  d.bf16 = p.io == SSD_BF16;
+  return d;
 }
-struct BwdLayout {
-  FwdLayout f;
-  size_t CBt, dCBg, Rp, Kp, U, dE, ddd, Ks, rR, last, dDp, dAp, dbp, end;
-};
-BwdLayout bwd_layout(const Prob& p) {
-  BwdLayout l;
-  l.f = fwd_layout(p);
-  size_t o = l.f.end;
-  const size_t nck = (size_t)p.nck, H = p.H, st = (size_t)p.P * p.N;
-  const size_t cb = p.io == SSD_BF16 ? nck * (size_t)p.G * p.Q * p.Q * 2 : 0;
-  const size_t tiles = p.io == SSD_BF16 ? nck * H * (size_t)(p.Q / 64) * p.Q * 4 : 0;
-  l.CBt = o;  o += up(cb);
-  l.dCBg = o; o += up(cb);
-  l.Rp = o;   o += up(tiles);
-  l.Kp = o;   o += up(tiles);
-  l.U = o;    o += up(nck * H * st * 4);
-  l.dE = o;   o += up(nck * H * st * state_esize(p));
-  l.ddd = o;  o += up(nck * H * p.Q * 4);
-  l.Ks = o;   o += up(nck * H * p.Q * 4);
-  l.rR = o;   o += up(nck * H * p.Q * 4);
-  l.last = o; o += up(nck * H * 4);
-  l.dDp = o;  o += up(nck * H * 4);
-  l.dAp = o;  o += up(nck * H * 4);
-  l.dbp = o;  o += up(nck * H * 4);
-  l.end = o;
-  return l;
-}
+FwdLayout fwd_layout(const Prob& p) { return ssd::fwd_layout(dims(p)); }
+BwdLayout bwd_layout(const Prob& p) { return ssd::bwd_layout(dims(p)); }
 size_t stage_ws(const Prob& p) { return fwd_layout(p).delta; }
 
 // Point the chunk map at the table inside a workspace and queue its build.
@@ -293,6 +259,12 @@ int64_t ssd_num_chunks(const ssd_problem* pr, int32_t Q, int32_t packed) {
   return p.nck;
 }
 
+int64_t ssd_fwd_chained_error_offset(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return -1;
+  return (int64_t)(fwd_layout(p).sync + 8 * 4);
+}
+
 int32_t ssd_scan_variant(const ssd_problem* pr, int32_t Q, int32_t packed) {
   Prob p;
   if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
@@ -343,8 +315,27 @@ static ssd_status fwd_run(const ssd_problem* pr, const void* x, const float* dt,
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int only = (p.flags >> 12) & 7;  // 0: every kernel
+  if ((p.flags & SSD_FLAG_CHAINED_FWD) && !chained_supported(p)) return SSD_ERR_UNSUPPORTED;
   s = setup_map(p, cu_seqlens, ws, st, only == 0, debug_check);
   if (s != SSD_OK) return s;
+  if (p.flags & SSD_FLAG_CHAINED_FWD) {
+    // C.B^T (and its transpose for a saved context), then the fused chained kernel;
+    // the carry buffer is the chunk-state slot, the flags the sync slot
+    void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
+    if (p.nck > 0) SSD_TRY(launch_bmm_chunk(p, B, C, ws + l.CB, st, CBt));
+    ChainIO io;
+    io.x = x; io.B = B; io.C = C; io.CB = ws + l.CB;
+    io.dt = dt; io.dt_bias = dt_bias; io.A = A; io.D = D; io.init = init_states;
+    io.y = out; io.final_states = final_states;
+    io.E = (float*)(ws + l.T);
+    io.sync = (int32_t*)(ws + l.sync);
+    io.delta = save ? (float*)(ws + l.delta) : nullptr;
+    io.acs = save ? (float*)(ws + l.acs) : nullptr;
+    io.decay = save ? (float*)(ws + l.decay) : nullptr;
+    io.Hp = save ? (void*)(ws + l.Hp) : nullptr;
+    SSD_TRY(launch_fwd_chained(p, io, st));
+    return SSD_OK;
+  }
   float* delta = (float*)(ws + l.delta);
   float* acs = (float*)(ws + l.acs);
   float* decay = (float*)(ws + l.decay);

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace ssd {
 
@@ -44,7 +45,7 @@ hipError_t launch_build_table(const Prob& p, const int32_t* cu_seqlens, int4* ta
 hipError_t launch_chunk_cumsum(const Prob& p, const float* dt, const float* dt_bias, const float* A,
                                float* delta, float* acs, float* decay, hipStream_t st);
 hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,
-                              const float* acs, float* out, int mode, hipStream_t st);
+                              const float* acs, ChunkStateT* out, int mode, hipStream_t st);
 // Stages 1 and 2 together: delta, acs and the chunk decays are written as
 // launch_chunk_cumsum writes them (bit for bit), and the chunk states T.  One
 // kernel on the bf16 path; the two kernels one after the other on the fp32 path.
@@ -52,13 +53,13 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
 // C.B^T into CB and, if CBt is set, its transpose, as launch_bmm_chunk does.
 hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* Bm, const float* dt,
                                      const float* dt_bias, const float* A, float* delta, float* acs,
-                                     float* decay, float* T, hipStream_t st, const void* C = nullptr,
+                                     float* decay, ChunkStateT* T, hipStream_t st, const void* C = nullptr,
                                      void* CB = nullptr, void* CBt = nullptr);
 // Whether the chunk-state kernel forms C.B^T for this problem (so that no
 // separate C.B^T kernel is launched).
 bool cb_in_chunk_state(const Prob& p);
 // passed: fp32, or bf16 when passed_bf16 (the carry and final_states stay fp32)
-hipError_t launch_state_passing(const Prob& p, const float* states, const float* decay,
+hipError_t launch_state_passing(const Prob& p, const ChunkStateT* states, const float* decay,
                                 const float* init, void* passed, int passed_bf16,
                                 float* final_states, int reverse, hipStream_t st);
 // CBt (bf16 only, may be null): also store the transpose of every lower tile.
@@ -93,6 +94,21 @@ struct BwdArgs {
   // per (chunk, head): alpha<dE,H> + sum s, and partials of dD, dA, d_dt_bias
   float *last_term, *dDp, *dAp, *dbp;
 };
+// The fused chained forward (k_fwd_chained.hip).  `sync` holds kChainSyncWords
+// words (ticket counters, wait error) followed by one flag per (chunk slot, head).
+struct ChainIO {
+  const void *x, *B, *C, *CB;
+  const float *dt, *dt_bias, *A, *D, *init;
+  void* y;
+  float* final_states;
+  ChunkStateT* E;  // (nck, H, P, N) carry buffer (the chunk-state region)
+  FlagT* sync;     // kChainSyncWords + nck * H words
+  float *delta, *acs, *decay;  // saved context, or null
+  void* Hp;                    // bf16 passed states, or null
+};
+bool chained_supported(const Prob& p);
+hipError_t launch_fwd_chained(const Prob& p, const ChainIO& io, hipStream_t st);
+
 // which: 0 every chunk kernel; 1 dx, 2 dCB (or the fp32 r+R kernel), 3 dC, 4 dB
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st);
 hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st);

@@ -42,6 +42,9 @@
 
 namespace ssd {
 
+static_assert(sizeof(ChunkStateT) == 4 && (ChunkStateT)0.5f == 0.5f,
+              "the chunk states and their adjoints are written here as fp32 (float4 stores)");
+
 constexpr int QMAX_STATE = 256;  // largest chunk size: one token per thread of a head
 
 __device__ __forceinline__ float token_scale(int mode, const float* dl, const float* ac, int j,

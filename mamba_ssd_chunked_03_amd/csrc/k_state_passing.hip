@@ -34,6 +34,9 @@
 
 namespace ssd {
 
+static_assert(sizeof(ChunkStateT) == 4 && (ChunkStateT)0.5f == 0.5f,
+              "the scan reads its inputs (chunk states, their adjoints) as fp32 float4");
+
 // REV (0 forward, 1 reverse) is a template argument so that profiles tell the
 // two directions apart.
 template <int W, int S, typename OutT, int REV>

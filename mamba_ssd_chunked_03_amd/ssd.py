@@ -28,7 +28,8 @@ class NormProblem(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
 
 
-FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED, FLAG_ONE_STREAM, FLAG_SEQUENTIAL_SCAN = 1, 2, 4, 8
+FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED, FLAG_ONE_STREAM, FLAG_SEQUENTIAL_SCAN, FLAG_CHAINED_FWD = \
+    1, 2, 4, 8, 16
 BWD_KERNELS = ("dstates", "reverse_state_passing", "bwd_dx", "bwd_dcb", "bwd_dc", "bwd_db",
                "bwd_finalize")
 
@@ -58,6 +59,7 @@ _SIGS = {
     "ssd_abi_version": ([], _I32),
     "ssd_fwd_kernel_mask": ([_P, _I32, _I32], _I32),
     "ssd_scan_variant": ([_P, _I32, _I32], _I32),
+    "ssd_fwd_chained_error_offset": ([_P, _I32, _I32], _I64),
     "ssd_status_string": ([_I32], ctypes.c_char_p),
     "ssd_num_chunks": ([_P, _I32, _I32], _I64),
     "ssd_fwd_workspace_bytes": ([_P, _I32, _I32], _SZ),
@@ -78,7 +80,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _lib = None
 
@@ -211,7 +213,8 @@ def num_chunks(prob, chunk_size, packed):
 
 def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
         dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False,
-        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0):
+        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0,
+        chained=False):
     """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h.
 
     save_for_backward: keep the intermediates in ``workspace`` (which must hold
@@ -225,7 +228,8 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     stream of its own).
     sequential_scan: the state passing walks the chunks with a sequential carry
     instead of the associative scan (a comparison point).
-    scan_variant: force a state-passing kernel (FLAG_SCAN_VARIANT); 0 = tuned table."""
+    scan_variant: force a state-passing kernel (FLAG_SCAN_VARIANT); 0 = tuned table.
+    chained: the fused single-pass forward (chained scan across chunks)."""
     if only_kernel and (workspace is None or out is None):
         raise ValueError("only_kernel needs the workspace and outputs of a complete call")
     batch, seqlen, H, P, G, N, nst, io = _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens)
@@ -237,7 +241,8 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     prob = problem(x, B, cu_seqlens, dt_softplus,
                    (FLAG_SAVE_FOR_BWD if save_for_backward else 0) | FLAG_FWD_KERNEL(only_kernel) |
                    (FLAG_ONE_STREAM if one_stream else 0) |
-                   (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0) | FLAG_SCAN_VARIANT(scan_variant))
+                   (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0) | FLAG_SCAN_VARIANT(scan_variant) |
+                   (FLAG_CHAINED_FWD if chained else 0))
     L = lib()
     packed = int(cu_seqlens is not None)
     if save_for_backward:

@@ -139,7 +139,11 @@ def test_workspace(L):
 
 
 def test_flags(L):
-    assert fwd_status(L, prob(flags=16)) == UNSUP  # an unknown bit
+    assert fwd_status(L, prob(flags=32)) == UNSUP  # an unknown bit
+    assert fwd_status(L, prob(flags=ssd.FLAG_CHAINED_FWD), ws_bytes=1) == WS  # accepted
+    assert fwd_status(L, prob(flags=ssd.FLAG_CHAINED_FWD | ssd.FLAG_FWD_KERNEL(1))) == UNSUP
+    assert fwd_status(L, prob(flags=ssd.FLAG_CHAINED_FWD, io_dtype=0)) == UNSUP      # fp32 io
+    assert fwd_status(L, prob(flags=ssd.FLAG_CHAINED_FWD, dstate=32)) == UNSUP       # dstate 32
     assert fwd_status(L, prob(flags=ssd.FLAG_SEQUENTIAL_SCAN), ws_bytes=1) == WS  # accepted
     assert fwd_status(L, prob(flags=ssd.FLAG_SCAN_VARIANT(7)), ws_bytes=1) == WS  # accepted
     assert fwd_status(L, prob(flags=ssd.FLAG_SCAN_VARIANT(8))) == UNSUP
@@ -173,13 +177,14 @@ def test_num_chunks(L):
 def test_workspace_bytes_layout(L):
     # forward workspace = delta, acs (nck,H,Q) + decay (nck,H) + chunk states
     # (nck,H,P,N) fp32 + passed states (nck,H,P,N) in the io dtype + CB (nck,G,Q,Q)
-    # io dtype, each rounded up to 256 bytes
+    # io dtype + the chained forward's 16 + nck*H int32 words, each rounded up to
+    # 256 bytes
     up = lambda n: (n + 255) // 256 * 256
     nck = 64
     for io, es in ((1, 2), (0, 4)):
         p = prob(batch=2, seqlen=8192, nheads=64, headdim=64, dstate=128, ngroups=8, io_dtype=io)
         exp = (2 * up(nck * 64 * 256 * 4) + up(nck * 64 * 4) + up(nck * 64 * 64 * 128 * 4)
-               + up(nck * 64 * 64 * 128 * es) + up(nck * 8 * 256 * 256 * es))
+               + up(nck * 64 * 64 * 128 * es) + up(nck * 8 * 256 * 256 * es) + up((16 + nck * 64) * 4))
         assert L.ssd_fwd_workspace_bytes(ctypes.byref(p), 256, 0) == exp, io
 
 

@@ -261,8 +261,9 @@ def test_cb_in_chunk_state_matches_stage_kernel(lengths):
     bit for bit, what the separate C.B^T stage kernel computes, on every 64 x 64
     lower tile that starts inside its chunk.  The workspace offsets follow the
     saved-context layout: delta, acs (nck, H, Q), decay (nck, H), chunk states
-    (nck, H, P, N) fp32, passed states in bf16, C.B^T (nck, G, Q, Q) bf16, then
-    (backward part) its transpose, each rounded up to 256 bytes."""
+    (nck, H, P, N) fp32, passed states in bf16, C.B^T (nck, G, Q, Q) bf16, the chained
+    forward's 16 + nck * H flag words, then (backward part) its transpose, each rounded
+    up to 256 bytes."""
     H, P, N, G, Q = 16, 64, 128, 2, 256
     kw = dict(nheads=H, headdim=P, dstate=N, ngroups=G, io="bf16", init="randn", seed=51)
     if lengths is None:
@@ -289,6 +290,7 @@ def test_cb_in_chunk_state_matches_stage_kernel(lengths):
     ncb = nck * G * Q * Q
     cb = ws[o:o + ncb * 2].view(torch.int16).view(nck, G, Q, Q).cpu()
     o += _up(ncb * 2)
+    o += _up((16 + nck * H) * 4)  # the chained forward's flags (end of the forward part)
     cbt = ws[o:o + ncb * 2].view(torch.int16).view(nck, G, Q, Q).cpu()
     ref = ref.view(torch.int16).cpu()
     # chunk lengths: batched rows cut from their first token, packed sequences likewise
