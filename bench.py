@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
     ap.add_argument("--fwd-only", action="store_true", help="time ssd_fwd alone as the step")
+    ap.add_argument("--no-ab", action="store_true",
+                    help="skip the state-passing and chained-forward comparisons")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the long-context and packed workloads reported beside the headline")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -467,7 +469,7 @@ def kernel_table(w, tm, per, label=""):
     return kernels
 
 
-def other_workload(cfg_id, dev, tm, steps, label):
+def other_workload(cfg_id, dev, tm, steps, label, ab=True):
     """Forward (and, where the workload has one, training step) timings of another
     named workload, with its kernel table; reported beside the headline."""
     from mamba_ssd_chunked_03_amd import inputs
@@ -492,8 +494,9 @@ def other_workload(cfg_id, dev, tm, steps, label):
                           "bwd_ms": round(tm.trials(w.bwd_saved, per)[0], 4)}
         print("bench: %s fwd+bwd %.3f ms" % (label, st_med), file=sys.stderr, flush=True)
     res["kernels"] = kernel_table(w, tm, per, label + " ")
-    res["state_passing_ab"] = w.scan_ab(tm, per)
-    res["fused_chained_forward"] = w.chained_ab(tm, per)
+    if ab:
+        res["state_passing_ab"] = w.scan_ab(tm, per)
+        res["fused_chained_forward"] = w.chained_ab(tm, per)
     del w
     return res
 
@@ -557,8 +560,9 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": s["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": s["frac_hbm"], "traffic": load_traffic(dom),
                 "alg_bytes_per_launch": s["alg_bytes"], "avg_launch_ms": s["ms"]}
-        scan_ab = w.scan_ab(tm, max(1, args.steps // 2))
-        chain_ab = w.chained_ab(tm, max(1, args.steps // 2))
+        if not args.no_ab:
+            scan_ab = w.scan_ab(tm, max(1, args.steps // 2))
+            chain_ab = w.chained_ab(tm, max(1, args.steps // 2))
 
     # the layer's gated RMSNorm on the SSD output (rows = batch x seqlen, dim =
     # heads x headdim, 8 groups of dim / 8 columns), gate and upstream gradient seeded
@@ -598,8 +602,8 @@ def main():
         sha = w.sha256
         del w
         torch.cuda.empty_cache()
-        others = {"long_context": other_workload(3, dev, tm, args.steps, "long context"),
-                  "packed": other_workload(4, dev, tm, args.steps, "packed sequences")}
+        others = {"long_context": other_workload(3, dev, tm, args.steps, "long context", not args.no_ab),
+                  "packed": other_workload(4, dev, tm, args.steps, "packed sequences", not args.no_ab)}
     else:
         sha = w.sha256
 

@@ -53,13 +53,16 @@ KERNEL_FILES = {
     "bwd_dc": "k_bwd.hip", "bwd_db": "k_bwd.hip", "bwd_finalize": "k_bwd.hip",
     "bmm_chunk_cb_only": "k_bmm.hip",  # C.B^T without its transpose (a forward that keeps nothing)
     "gated_rmsnorm_fwd": "k_norm.hip", "gated_rmsnorm_bwd": "k_norm.hip",  # the layer's norm
+    "fwd_chained": "k_fwd_chained.hip",  # the fused chained forward (its clear and empty-final kernels too)
 }
+# headers whose code is compiled into every kernel
+SHARED_HEADERS = ("common.hpp", "internal.hpp", "layout.hpp", "scan_rows.hpp")
 
 
 def source_hash(kernel):
     """Hash of the kernel's source file and the headers every kernel includes."""
     h = hashlib.sha256()
-    for name in (KERNEL_FILES[kernel], "common.hpp", "internal.hpp"):
+    for name in (KERNEL_FILES[kernel],) + SHARED_HEADERS:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -79,6 +82,11 @@ def kernel_key(name):
         return "dstates" if len(targ) >= 3 and targ[2] == "1" else "chunk_state"
     if base == "state_passing_kernel":
         return "reverse_state_passing" if last == "1" else "state_passing"
+    if base == "state_passing_seq_kernel":
+        # state_passing_seq_kernel<output type, REV, loads in flight>
+        return "reverse_state_passing" if len(targ) >= 2 and targ[1] == "1" else "state_passing"
+    if base in ("fwd_chained_kernel", "chain_clear_kernel", "chain_empty_final_kernel"):
+        return "fwd_chained"
     if base.startswith("bmm_chunk_bf16"):
         return "bmm_chunk_cb_only" if last == "false" else "bmm_chunk"
     for prefix, key in (("chunk_cumsum", "chunk_cumsum"), ("bmm_chunk", "bmm_chunk"),

@@ -25,6 +25,11 @@ def test_kernel_keys():
     assert k("void ssd::chunk_state_bf16_kernel<64, 128, 0, 2>(ssd::ChunkMap)") == "chunk_state"
     assert k("void ssd::state_passing_kernel<16, 4, unsigned short, 1>(x)") == "reverse_state_passing"
     assert k("void ssd::state_passing_kernel<16, 4, unsigned short, 0>(x)") == "state_passing"
+    assert k("void ssd::state_passing_seq_kernel<unsigned short, 0, 1>(x)") == "state_passing"
+    assert k("void ssd::state_passing_seq_kernel<unsigned short, 1, 4>(x)") == "reverse_state_passing"
+    assert k("void ssd::state_passing_seq_kernel<float, 0, 8>(x)") == "state_passing"
+    assert k("void ssd::fwd_chained_kernel<64, 128>(ssd::ChunkMap)") == "fwd_chained"
+    assert k("ssd::chain_clear_kernel(int*, long)") == "fwd_chained"
     assert k("void ssd::bwd_dc_bf16_kernel<64, 128>(x)") == "bwd_dc"
     assert k("void ssd::bwd_dcb_bf16_kernel<64>(x)") == "bwd_dcb"
     assert k("void ssd::bwd_reduce_kernel(int)") == "bwd_finalize"
