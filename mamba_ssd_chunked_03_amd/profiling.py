@@ -186,6 +186,35 @@ def stats_table(trace_csv, command, summary_cmd=""):
     return "\n".join(lines) + "\n", total
 
 
+def kernels_table(trace_csv, command, summary_cmd="", keys=None):
+    """One row per launched kernel (template instance) rather than per path kernel:
+    for traces of programs that launch several forms of one kernel (a comparison of
+    variants), whose launches must not be summed or averaged together."""
+    times = kernel_times(trace_csv)
+    lines = ["Profiled with (from the repository root, one MI355X):", "", "    " + command, ""]
+    if summary_cmd:
+        lines += ["Summarised with:", "", "    " + summary_cmd, ""]
+    lines += ["One row per launched kernel (its template arguments name the form).  A launch "
+              "counts as overlapped when its interval meets another kernel's; the two kinds are "
+              "averaged apart.", "",
+              "| Kernel | Launched kernel | Launches | Alone | Alone avg (us) | Overlapped "
+              "| Overlapped avg (us) | Min (us) | Max (us) |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    fmt = lambda x: "-" if x != x else "%.1f" % x
+    for key in KERNEL_FILES:
+        if key not in times or (keys and key not in keys):
+            continue
+        for short in sorted(times[key]):
+            v = times[key][short]
+            alone = _mean([t for t, ov in v if not ov]) / 1e3
+            lapped = _mean([t for t, ov in v if ov]) / 1e3
+            lines.append("| %s | `%s` | %d | %d | %s | %d | %s | %.1f | %.1f |" % (
+                key, short, len(v), sum(1 for _, ov in v if not ov), fmt(alone),
+                sum(1 for _, ov in v if ov), fmt(lapped), min(t for t, _ in v) / 1e3,
+                max(t for t, _ in v) / 1e3))
+    return "\n".join(lines) + "\n"
+
+
 def counter_means(counter_csv, counter):
     """{key: (mean value per launch, launches)} for one counter; a launch of a
     multi-kernel key sums its kernels' means."""
@@ -324,6 +353,9 @@ def main(argv=None):
     s.add_argument("out")
     s.add_argument("--title", default="")
     s.add_argument("--command", required=True)
+    s.add_argument("--per-kernel", action="store_true",
+                   help="one row per launched kernel form (comparisons of variants)")
+    s.add_argument("--keys", nargs="*", help="only these path kernels (with --per-kernel)")
     t = sub.add_parser("traffic")
     for n in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument("--" + n, required=True, help="counter CSV, or a directory searched for one")
@@ -355,7 +387,10 @@ def main(argv=None):
                 json.dump(res, f, indent=1, sort_keys=True)
                 f.write("\n")
     elif a.cmd == "stats":
-        text, _ = stats_table(csv_in(a.trace, "kernel_trace"), a.command, here)
+        if a.per_kernel:
+            text = kernels_table(csv_in(a.trace, "kernel_trace"), a.command, here, a.keys)
+        else:
+            text, _ = stats_table(csv_in(a.trace, "kernel_trace"), a.command, here)
         with open(a.out, "w") as f:
             f.write(("# " + a.title + "\n\n" if a.title else "") + text)
     else:

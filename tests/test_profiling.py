@@ -101,3 +101,16 @@ def test_mlp_littles_law(tmp_path):
     rows = [[d, dx, c, v, 10_000 * d, 10_000 * d + 1000] for d in (1, 2) for c, v in vals.items()]
     res = profiling.mlp(write(tmp_path / "m2.csv", cols, rows), cus=2, xcds=2, simds_per_cu=4)["bwd_dx"]
     assert res["mfma_gflop"] == 2e6 * 512 / 1e9 and res["mfma_busy"] == 0.25 and res["mfma_insts"] == 10.0
+
+
+def test_kernels_table_keeps_forms_apart(tmp_path):
+    rows = [["void ssd::state_passing_kernel<8, 4, unsigned short, 0>(a)", 0, 4000],
+            ["void ssd::state_passing_seq_kernel<unsigned short, 0, 1>(a)", 10000, 13000],
+            ["void ssd::state_passing_seq_kernel<unsigned short, 0, 1>(a)", 20000, 23200],
+            ["void ssd::bwd_dx_bf16_kernel<64, 128>(a)", 30000, 31000]]
+    p = write(tmp_path / "t.csv", TRACE_COLS, rows)
+    text = profiling.kernels_table(p, "cmd", keys=["state_passing"])
+    lines = [l for l in text.splitlines() if l.startswith("| state_passing |")]
+    assert len(lines) == 2 and not any("bwd_dx" in l for l in text.splitlines())
+    assert "| 1 | 1 | 4.0 |" in [l for l in lines if "state_passing_kernel<" in l][0]
+    assert "| 2 | 2 | 3.1 |" in [l for l in lines if "seq_kernel" in l][0]
