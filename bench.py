@@ -82,6 +82,9 @@ def kernel_bytes(B, L, H, P, N, G, Q, nck, nseq, esz, init=True, d_final=False):
         "bwd_dcb": 2 * x + tri + 2 * f32_tok + tri + 2 * f32_tok,
         "bwd_dc": 2 * bc + x + tri + f32_tok + st16 + bc + f32_tok,
         "bwd_db": x + bc + tri + 2 * f32_tok + st16 + bc,
+        # the one kernel for dB and dC: x, dy, B, C, C.B^T, acs, delta, H, dE read;
+        # dB, dC, r, R, K written
+        "bwd_dbc": 2 * x + 2 * bc + tri + 2 * f32_tok + 2 * st16 + 2 * bc + 3 * f32_tok,
         "bwd_finalize": dt + 6 * f32_tok + dt,
     }
 
@@ -102,6 +105,7 @@ def kernel_flops(B, L, H, P, N, G, Q, nck):
         "bwd_dcb": nck * H * P * tri,
         "bwd_dc": nck * G * N * tri + state,
         "bwd_db": nck * G * N * tri + state,
+        "bwd_dbc": nck * H * P * tri + 2 * (nck * G * N * tri + state),
     }
 
 
@@ -229,6 +233,7 @@ class Workload:
                                  **self.common)
         self.with_bwd = with_bwd and d["dout"] is not None
         self.fwd_mask = lib.ssd_fwd_kernel_mask(ctypes.byref(prob), Q, self.packed)
+        self.bwd_mask = lib.ssd_bwd_kernel_mask(ctypes.byref(prob), Q, self.packed)
         self.ws_b = torch.empty(lib.ssd_bwd_workspace_bytes(ctypes.byref(prob), Q, self.packed),
                                 dtype=torch.uint8, device=dev)
         # the training forward keeps its intermediates for the backward
@@ -272,9 +277,33 @@ class Workload:
                                 save_for_backward=True, only_kernel=k, prepare=True, **self.common)[0]
         if self.with_bwd:
             for k, name in enumerate(ssd.BWD_KERNELS, 1):
+                if not self.bwd_mask & (1 << (k - 1)):
+                    continue
+                if k == 4 and not self.bwd_mask & 16:
+                    name = ssd.BWD_FUSED_KERNEL
                 fns[name] = ssd.bwd(*self.args, self.d["dout"], workspace=self.ws_b, from_saved=True,
                                     grads=self.grads, only_kernel=k, prepare=True, **self.common)[0]
         return fns
+
+    def fused_bwd_ab(self, tm, per):
+        """The backward from a saved forward with dB and dC formed by three kernels
+        (the default) against one kernel over one pass of x and dy
+        (SSD_FLAG_BWD_FUSED), and the training step with each; warm and cold ms."""
+        from mamba_ssd_chunked_03_amd import ssd
+        if not self.with_bwd:
+            return None
+        fused, _ = ssd.bwd(*self.args, self.d["dout"], workspace=self.ws_b, from_saved=True, grads=self.grads,
+                           fused=True, prepare=True, **self.common)
+        res = {}
+        for key, fn in (("three_kernels", self.bwd_saved), ("one_kernel", fused)):
+            med, lo, hi = tm.trials(fn, per)
+            step = lambda fn=fn: (self.fwd_save(), fn())
+            smed = tm.trials(step, per)[0]
+            res[key] = {"bwd_ms": round(med, 4), "bwd_ms_min": round(lo, 4), "bwd_ms_max": round(hi, 4),
+                        "bwd_ms_cold": round(tm.cold(fn), 4), "step_ms": round(smed, 4)}
+            print("bench: backward %-10s %.4f ms (step %.4f ms)" % (key, med, smed), file=sys.stderr, flush=True)
+        self.bwd_saved()  # the gradients of the default path again
+        return res
 
     def chained_ab(self, tm, per):
         """The fused single-pass forward (SSD_FLAG_CHAINED_FWD: C.B^T kernel, then one
@@ -464,7 +493,8 @@ def kernel_table(w, tm, per, label=""):
     names = list(kernels)
     kernels["_forward_aggregate"] = aggregate([n for n in ssd.FWD_KERNELS if n in kernels])
     if w.with_bwd:
-        kernels["_backward_aggregate"] = aggregate(list(ssd.BWD_KERNELS))
+        kernels["_backward_aggregate"] = aggregate(
+            [n for n in list(ssd.BWD_KERNELS) + [ssd.BWD_FUSED_KERNEL] if n in kernels])
     kernels["_all"] = aggregate(names)
     return kernels
 
@@ -497,6 +527,7 @@ def other_workload(cfg_id, dev, tm, steps, label, ab=True):
     if ab:
         res["state_passing_ab"] = w.scan_ab(tm, per)
         res["fused_chained_forward"] = w.chained_ab(tm, per)
+        res["bwd_dbdc_ab"] = w.fused_bwd_ab(tm, per)
     del w
     return res
 
@@ -551,7 +582,7 @@ def main():
     # every kernel of the step on its own: the same launch (arguments, grid,
     # buffers) as inside the step, re-issued through the single-kernel flags
     kernels = {}
-    roof = scan_ab = chain_ab = None
+    roof = scan_ab = chain_ab = split_ab = None
     if not args.no_kernels:
         kernels = kernel_table(w, tm, max(1, args.steps // 2))
         names = [n for n in kernels if not n.startswith("_")]
@@ -563,6 +594,7 @@ def main():
         if not args.no_ab:
             scan_ab = w.scan_ab(tm, max(1, args.steps // 2))
             chain_ab = w.chained_ab(tm, max(1, args.steps // 2))
+            split_ab = w.fused_bwd_ab(tm, max(1, args.steps // 2))
 
     # the layer's gated RMSNorm on the SSD output (rows = batch x seqlen, dim =
     # heads x headdim, 8 groups of dim / 8 columns), gate and upstream gradient seeded
@@ -650,6 +682,7 @@ def main():
         "gated_rmsnorm": norm,
         "state_passing_ab": scan_ab,
         "fused_chained_forward": chain_ab,
+        "bwd_dbdc_ab": split_ab,
         "other_workloads": others,
     }
     print(json.dumps(out))

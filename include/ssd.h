@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 9
+#define SSD_ABI_VERSION 10
 
 typedef enum {
   SSD_OK = 0,
@@ -136,13 +136,26 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   ssd_bwd expects), not with SSD_FLAG_FWD_KERNEL.  All kernels run on `stream`.
  *   Results agree with the default forward to rounding. */
 #define SSD_FLAG_CHAINED_FWD 16
+/* SSD_FLAG_BWD_FUSED: ssd_bwd forms dB and dC, their head-summed dCB and the
+ *   decay-gradient sums with one kernel, from one pass over x and dy (the scan page,
+ *   section 3, "kernel fusion": fewer global-memory passes), instead of three
+ *   kernels (the head-summed dCB with per-tile partials of the decay-gradient sums,
+ *   then dC, then dB, which read x and dy twice each).  A comparison point for
+ *   measurement (it moves fewer bytes but runs one workgroup per compute unit, and
+ *   is slower on MI355X): dB and dC are bitwise the same; ddt, dA and d_dt_bias
+ *   agree to rounding (their decay-gradient sums are added in another order).  bf16
+ *   io only; no effect on the fp32 path, which always runs its own kernels. */
+#define SSD_FLAG_BWD_FUSED 32
 /* SSD_FLAG_BWD_KERNEL(k), k = 1..7: a profiling aid, valid only together with
  *   SSD_FLAG_FROM_SAVED.  ssd_bwd launches only its k-th kernel: 1 adjoint chunk
  *   states, 2 reverse state passing, 3 dx (with the direct delta gradient),
  *   4 head-summed dCB with the decay-gradient partials, 5 dC, 6 dB, 7 finalize
- *   (ddt and the per-head sums).  The workspace and the gradient buffers must hold
- *   the results of a complete ssd_bwd call on the same arguments, so that the kernel
- *   finds its inputs; it rewrites its own outputs with the same values. */
+ *   (ddt and the per-head sums); where ssd_bwd_kernel_mask() leaves bits 4 and 5
+ *   clear (SSD_FLAG_BWD_FUSED), 4 is the one kernel forming dB and dC, and 5, 6
+ *   launch nothing.  The
+ *   workspace and the gradient buffers must hold the results of a complete ssd_bwd
+ *   call on the same arguments, so that the kernel finds its inputs; it rewrites
+ *   its own outputs with the same values. */
 #define SSD_FLAG_BWD_KERNEL(k) ((k) << 8)
 /* SSD_FLAG_FWD_KERNEL(k), k = 1..4: the same for ssd_fwd, whose workspace and
  *   outputs must hold a complete call's results on the same arguments: 1 chunk
@@ -174,6 +187,12 @@ const char* ssd_status_string(int32_t status);
  * of a group's heads holds one 64-row block of the chunk's C.B^T).  A profiling and
  * accounting aid; the results do not depend on it.  Returns 0 for an invalid problem. */
 int32_t ssd_fwd_kernel_mask(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+
+/* Which of the seven backward kernels (bit k-1 for SSD_FLAG_BWD_KERNEL(k)) a complete
+ * ssd_bwd call on this problem launches: 0x7F, or 0x4F where one kernel forms dB and
+ * dC (bf16 with SSD_FLAG_BWD_FUSED).  A profiling and accounting aid.  Returns 0
+ * for an invalid problem. */
+int32_t ssd_bwd_kernel_mask(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 
 /* Which state-passing kernel (SSD_FLAG_SCAN_VARIANT numbering, 1..7) ssd_fwd and
  * ssd_bwd run for this problem: the variant forced by problem->flags, else the

@@ -39,7 +39,7 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   if (pr->nheads % pr->ngroups) return SSD_ERR_SHAPE;
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
   if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_ONE_STREAM |
-                    SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_CHAINED_FWD | SSD_FLAG_BWD_KERNEL(7) |
+                    SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_CHAINED_FWD | SSD_FLAG_BWD_FUSED | SSD_FLAG_BWD_KERNEL(7) |
                     SSD_FLAG_FWD_KERNEL(7) | SSD_FLAG_SCAN_VARIANT(15)))
     return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_CHAINED_FWD) && (pr->flags & SSD_FLAG_FWD_KERNEL(7))) return SSD_ERR_UNSUPPORTED;
@@ -106,6 +106,9 @@ LayoutDims dims(const Prob& p) {
 }
 FwdLayout fwd_layout(const Prob& p) { return ssd::fwd_layout(dims(p)); }
 BwdLayout bwd_layout(const Prob& p) { return ssd::bwd_layout(dims(p)); }
+
+// Whether ssd_bwd forms dB and dC with the one kernel (launch_bwd_dbc).
+bool bwd_fused(const Prob& p) { return (p.flags & SSD_FLAG_BWD_FUSED) && bwd_fused_supported(p); }
 size_t stage_ws(const Prob& p) { return fwd_layout(p).delta; }
 
 // Point the chunk map at the table inside a workspace and queue its build.
@@ -275,6 +278,12 @@ int32_t ssd_fwd_kernel_mask(const ssd_problem* pr, int32_t Q, int32_t packed) {
   Prob p;
   if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
   return cb_in_chunk_state(p) ? 0xB : 0xF;
+}
+
+int32_t ssd_bwd_kernel_mask(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
+  return bwd_fused(p) ? 0x4F : 0x7F;
 }
 
 size_t ssd_fwd_workspace_bytes(const ssd_problem* pr, int32_t Q, int32_t packed) {
@@ -455,16 +464,19 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   a.ddd = (float*)(ws + l.ddd); a.Ks = (float*)(ws + l.Ks); a.rR = (float*)(ws + l.rR);
   a.last_term = (float*)(ws + l.last); a.dDp = (float*)(ws + l.dDp);
   a.dAp = (float*)(ws + l.dAp); a.dbp = (float*)(ws + l.dbp);
-  // The head-summed dCB (with the R, K partials), then dC, need only forward
-  // quantities, and dB needs dCB and the reverse scan's dE: on the bf16 path
-  // those three run on a side stream (dB after an event from the reverse scan)
-  // beside the adjoint states, the reverse scan and dx; the finalize waits for
-  // the side stream.  Each stream then carries about half of the work.
+  // dB and dC on the bf16 path: three kernels, the head-summed dCB (with R, K
+  // tile partials), then dC, which need only forward quantities, and dB, which
+  // needs dCB and the reverse scan's dE; with SSD_FLAG_BWD_FUSED one kernel forms
+  // all of them with whole R, K from one pass over x and dy, after the reverse
+  // scan.  Those run on a side stream (the first two from the start, dB or the
+  // one kernel after an event from the reverse scan) beside the adjoint states,
+  // the reverse scan and dx; the finalize waits for the side stream.
+  const bool fused = bwd_fused(p);
   std::unique_lock<std::mutex> lane_lock;
   const bool one_stream = (p.flags & SSD_FLAG_ONE_STREAM) != 0;
   SideLane* side =
       (!only && p.io == SSD_BF16 && p.nck > 0 && !one_stream) ? side_lane(st, lane_lock) : nullptr;
-  if (side) {  // events: 0 fork, 1 reverse scan done, 2 side stream done
+  if (side && !fused) {  // events: 0 fork, 1 reverse scan done, 2 side stream done
     SSD_TRY_FORKED(hipEventRecord(side->ev[0], st));
     SSD_TRY_FORKED(hipStreamWaitEvent(side->stream, side->ev[0], 0));
     SSD_TRY_FORKED(launch_bwd_chunk(p, a, 2, side->stream));
@@ -478,14 +490,17 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   if (side) {
     SSD_TRY_FORKED(hipEventRecord(side->ev[1], st));
     SSD_TRY_FORKED(hipStreamWaitEvent(side->stream, side->ev[1], 0));
-    SSD_TRY_FORKED(launch_bwd_chunk(p, a, 4, side->stream));
+    SSD_TRY_FORKED(fused ? launch_bwd_dbc(p, a, side->stream) : launch_bwd_chunk(p, a, 4, side->stream));
     SSD_TRY_FORKED(hipEventRecord(side->ev[2], side->stream));
     SSD_TRY_FORKED(launch_bwd_chunk(p, a, 1, st));
     SSD_TRY_FORKED(hipStreamWaitEvent(st, side->ev[2], 0));
+  } else if (fused) {
+    if (!only || only == 3) SSD_TRY_FORKED(launch_bwd_chunk(p, a, 1, st));
+    if (!only || only == 4) SSD_TRY_FORKED(launch_bwd_dbc(p, a, st));
   } else if (!only || (only >= 3 && only <= 6)) {
     SSD_TRY_FORKED(launch_bwd_chunk(p, a, only ? only - 2 : 0, st));
   }
-  if (!only || only == 7) SSD_TRY_FORKED(launch_bwd_finalize(p, a, st));
+  if (!only || only == 7) SSD_TRY_FORKED(launch_bwd_finalize(p, a, st, fused));
   return SSD_OK;
 }
 

@@ -111,6 +111,11 @@ hipError_t launch_fwd_chained(const Prob& p, const ChainIO& io, hipStream_t st);
 
 // which: 0 every chunk kernel; 1 dx, 2 dCB (or the fp32 r+R kernel), 3 dC, 4 dB
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st);
-hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st);
+// dB and dC, their dCB, r and whole R, K in one kernel (k_bwd_dbc.hip): R into
+// a.Rp and K into a.Kp, one value per (chunk, head, token); r into a.rR.
+bool bwd_fused_supported(const Prob& p);
+hipError_t launch_bwd_dbc(const Prob& p, const BwdArgs& a, hipStream_t st);
+// fused: R and K are whole per token (launch_bwd_dbc) rather than tile partials
+hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st, bool fused = false);
 
 }  // namespace ssd

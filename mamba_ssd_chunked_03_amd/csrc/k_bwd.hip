@@ -948,7 +948,8 @@ __global__ __launch_bounds__(256) void bwd_db_f32_kernel(
 
 // ---------------------------------------------------------------- finalize ----
 // One workgroup per (chunk, head), one token per thread: dAcs_i = rR_i - Ks_i +
-// (R, K tile partials) (+ last_term at the last token); ddA_t = sum_{i>=t} dAcs_i,
+// (R, K tile partials, or whole R, K per token: Rf, Kf) (+ last_term at the last
+// token); ddA_t = sum_{i>=t} dAcs_i,
 // d(delta)_t = ddd_t + A ddA_t, ddt = d(delta) sigmoid(z) when softplus is on;
 // per-chunk partial sums of delta*ddA and ddt.  Wave w holds the 64-token block
 // w from the chunk's end with its lanes reversed, so a DPP prefix sum over a
@@ -959,7 +960,8 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ delta, const float* __restrict__ rR, const float* __restrict__ Ks,
     const float* __restrict__ ddd, const float* __restrict__ last_term,
-    const float* __restrict__ Rp, const float* __restrict__ Kp, int ntile, float* __restrict__ ddt,
+    const float* __restrict__ Rp, const float* __restrict__ Kp, int ntile,
+    const float* __restrict__ Rf, const float* __restrict__ Kf, float* __restrict__ ddt,
     float* __restrict__ dAp, float* __restrict__ dbp) {
   __shared__ float wtot[4], wpa[4], wpb[4];
   const int k = blockIdx.x, h = blockIdx.y;
@@ -1003,8 +1005,12 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     rp[tl] = buf_load_f32(rrp, ur[tl] ? ot + (uint32_t)(tl * Q * 4) : 0x80000000u);
     kp[tl] = buf_load_f32(rkp, uk[tl] ? ot + (uint32_t)(tl * Q * 4) : 0x80000000u);
   }
+  // whole R and K per token (one kernel forms them), when given
+  const uint32_t ofr = Rf ? ot : 0x80000000u;
+  const float rf = buf_load_f32(make_rsrc(Rf ? Rf + kh * Q : rR, rowb), ofr);
+  const float kf = buf_load_f32(make_rsrc(Kf ? Kf + kh * Q : Ks, rowb), ofr);
   const float lt = last_term[kh];
-  float v = r0 - k0 + (t == len - 1 ? lt : 0.f);
+  float v = r0 - k0 + (t == len - 1 ? lt : 0.f) + (rf - kf);
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) v = ur[tl] ? v + rp[tl] : v;
 #pragma unroll
@@ -1121,11 +1127,12 @@ hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStrea
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st, bool fused) {
   if (p.nck > 0)
     hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, p.H), dim3(256), 0, st,
                        p.map, p.H, p.softplus, a.dt, a.dt_bias, a.A, a.delta, a.rR, a.Ks, a.ddd,
-                       a.last_term, a.Rp, a.Kp, p.io == 0 ? 0 : p.Q / 64, a.ddt, a.dAp, a.dbp);
+                       a.last_term, a.Rp, a.Kp, (p.io == 0 || fused) ? 0 : p.Q / 64,
+                       fused ? a.Rp : nullptr, fused ? a.Kp : nullptr, a.ddt, a.dAp, a.dbp);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((p.H + 3) / 4), dim3(256), 0, st, (int)p.nck, p.H,
                      a.dAp, a.dbp, a.dDp, a.dA, a.d_dt_bias, a.dD);
   return hipGetLastError();

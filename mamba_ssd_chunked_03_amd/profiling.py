@@ -51,6 +51,7 @@ KERNEL_FILES = {
     "chunk_scan": "k_chunk_scan.hip", "dstates": "k_chunk_state.hip",
     "reverse_state_passing": "k_state_passing.hip", "bwd_dx": "k_bwd.hip", "bwd_dcb": "k_bwd.hip",
     "bwd_dc": "k_bwd.hip", "bwd_db": "k_bwd.hip", "bwd_finalize": "k_bwd.hip",
+    "bwd_dbc": "k_bwd_dbc.hip",  # dB and dC with their dCB and decay-gradient sums, one kernel
     "bmm_chunk_cb_only": "k_bmm.hip",  # C.B^T without its transpose (a forward that keeps nothing)
     "gated_rmsnorm_fwd": "k_norm.hip", "gated_rmsnorm_bwd": "k_norm.hip",  # the layer's norm
     "fwd_chained": "k_fwd_chained.hip",  # the fused chained forward (its clear and empty-final kernels too)
@@ -90,7 +91,7 @@ def kernel_key(name):
     if base.startswith("bmm_chunk_bf16"):
         return "bmm_chunk_cb_only" if last == "false" else "bmm_chunk"
     for prefix, key in (("chunk_cumsum", "chunk_cumsum"), ("bmm_chunk", "bmm_chunk"),
-                        ("chunk_scan", "chunk_scan"), ("bwd_dx_", "bwd_dx"), ("bwd_dcb_", "bwd_dcb"),
+                        ("chunk_scan", "chunk_scan"), ("bwd_dx_", "bwd_dx"), ("bwd_dcb_", "bwd_dcb"), ("bwd_dbc_", "bwd_dbc"),
                         ("bwd_dc_", "bwd_dc"), ("bwd_db_", "bwd_db"), ("bwd_finalize", "bwd_finalize"),
                         ("bwd_reduce", "bwd_finalize"), ("gated_rmsnorm_fwd", "gated_rmsnorm_fwd"),
                         ("gated_rmsnorm_bwd", "gated_rmsnorm_bwd"), ("norm_dw_reduce", "gated_rmsnorm_bwd"),

@@ -30,8 +30,11 @@ class NormProblem(ctypes.Structure):
 
 FLAG_SAVE_FOR_BWD, FLAG_FROM_SAVED, FLAG_ONE_STREAM, FLAG_SEQUENTIAL_SCAN, FLAG_CHAINED_FWD = \
     1, 2, 4, 8, 16
+FLAG_BWD_FUSED = 32
 BWD_KERNELS = ("dstates", "reverse_state_passing", "bwd_dx", "bwd_dcb", "bwd_dc", "bwd_db",
                "bwd_finalize")
+# kernel 4 where ssd_bwd_kernel_mask leaves bits 4 and 5 clear (one kernel for dB and dC)
+BWD_FUSED_KERNEL = "bwd_dbc"
 
 
 # "chunk_state" forms delta and the within-chunk cumsum too (one kernel on the bf16 path)
@@ -58,6 +61,7 @@ def FLAG_FWD_KERNEL(k):
 _SIGS = {
     "ssd_abi_version": ([], _I32),
     "ssd_fwd_kernel_mask": ([_P, _I32, _I32], _I32),
+    "ssd_bwd_kernel_mask": ([_P, _I32, _I32], _I32),
     "ssd_scan_variant": ([_P, _I32, _I32], _I32),
     "ssd_fwd_chained_error_offset": ([_P, _I32, _I32], _I64),
     "ssd_status_string": ([_I32], ctypes.c_char_p),
@@ -80,7 +84,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _lib = None
 
@@ -296,9 +300,12 @@ def fwd_noalloc(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None
 
 def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
         chunk_size=256, dt_softplus=True, workspace=None, from_saved=False, grads=None,
-        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0):
+        only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0,
+        fused=False):
     """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors).
 
+    fused: dB and dC from one kernel, one pass over x and dy (SSD_FLAG_BWD_FUSED),
+    instead of the three-kernel form.
     from_saved: ``workspace`` holds the intermediates of a save_for_backward
     fwd call on the same inputs; the recompute is skipped.
     grads: a dict returned by an earlier call, written again instead of new tensors.
@@ -327,7 +334,7 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_
         raise ValueError("only_kernel needs from_saved and the grads of a complete call")
     flags = (FLAG_FROM_SAVED if from_saved else 0) | FLAG_BWD_KERNEL(only_kernel) | \
         (FLAG_ONE_STREAM if one_stream else 0) | (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0) | \
-        FLAG_SCAN_VARIANT(scan_variant)
+        FLAG_SCAN_VARIANT(scan_variant) | (FLAG_BWD_FUSED if fused else 0)
     prob = problem(x, B, cu_seqlens, dt_softplus, flags)
     L = lib()
     packed = int(cu_seqlens is not None)

@@ -139,7 +139,8 @@ def test_workspace(L):
 
 
 def test_flags(L):
-    assert fwd_status(L, prob(flags=32)) == UNSUP  # an unknown bit
+    assert fwd_status(L, prob(flags=64)) == UNSUP  # an unknown bit
+    assert fwd_status(L, prob(flags=ssd.FLAG_BWD_FUSED), ws_bytes=1) == WS  # accepted
     assert fwd_status(L, prob(flags=ssd.FLAG_CHAINED_FWD), ws_bytes=1) == WS  # accepted
     assert fwd_status(L, prob(flags=ssd.FLAG_CHAINED_FWD | ssd.FLAG_FWD_KERNEL(1))) == UNSUP
     assert fwd_status(L, prob(flags=ssd.FLAG_CHAINED_FWD, io_dtype=0)) == UNSUP      # fp32 io
@@ -277,3 +278,17 @@ def test_noalloc_host_validation(L):
     assert st(prob(), Q=100) == UNSUP
     hdr = open(HEADER).read()
     assert "#define SSD_NOALLOC_SCRATCH_BYTES (%du << 20)" % (ssd.NOALLOC_SCRATCH_BYTES >> 20) in hdr
+
+
+def test_bwd_kernel_mask(L):
+    # with SSD_FLAG_BWD_FUSED one kernel forms dB and dC on the bf16 path
+    # (kernels 5 and 6 launch nothing)
+    layer = dict(batch=2, seqlen=8192, nheads=64, headdim=64, dstate=128, ngroups=8, io_dtype=1)
+    mask = lambda Q=256, packed=0, **kw: L.ssd_bwd_kernel_mask(ctypes.byref(prob(**{**layer, **kw})), Q, packed)
+    F = ssd.FLAG_BWD_FUSED
+    assert mask() == 0x7F                                               # the three-kernel default
+    assert mask(flags=F) == 0x4F
+    assert mask(flags=F, Q=64) == 0x4F and mask(flags=F, headdim=128, dstate=32) == 0x4F
+    assert mask(flags=F, batch=1, seqlen=65536, nseq=8, packed=1) == 0x4F
+    assert mask(flags=F, io_dtype=0, headdim=16, dstate=16) == 0x7F     # fp32 path
+    assert mask(nheads=-1) == 0                                         # invalid problem

@@ -181,10 +181,12 @@ def test_bwd_full_size_sampled_heads():
           heads=heads)
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io", ["bf16", "f32", "bf16_fused"])
 def test_single_kernel_relaunch_is_idempotent(io):
     # the profiling flags re-launch one forward or backward kernel on the buffers
     # of a complete call: every output and gradient must come out bit-identical
+    fused = io == "bf16_fused"
+    io = "bf16" if fused else io
     kw = dict(nheads=4, headdim=64, dstate=128, ngroups=2) if io == "bf16" else \
         dict(nheads=2, headdim=16, dstate=32, ngroups=1)
     inp = inputs.make_inputs(2, 300, io=io, init="randn", bwd=True, d_final=True, seed=61, **kw)
@@ -202,7 +204,7 @@ def test_single_kernel_relaunch_is_idempotent(io):
         assert torch.equal(y, y0) and torch.equal(fin, f0), ssd.FWD_KERNELS[k - 1]
     args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["dout"])
     kw2 = dict(D=d["D"], dt_bias=d["dt_bias"], init=d["init"], d_final=d["d_final"], chunk_size=128,
-               dt_softplus=inp["dt_softplus"], workspace=ws, from_saved=True)
+               dt_softplus=inp["dt_softplus"], workspace=ws, from_saved=True, fused=fused)
     g = ssd.bwd(*args, **kw2)
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in g.items() if v is not None}
@@ -344,3 +346,59 @@ def test_bwd_scan_variants(variant):
     torch.cuda.synchronize()
     check(g, oracle_bwd(inp), "bf16", "variant %d packed" % variant)
     assert torch.equal(g["d_init"][1].cpu(), inp["d_final"][1])
+
+
+FUSED_CASES = [
+    ("ragged_q64", dict(batch=2, seqlen=700, nheads=4, headdim=64, dstate=128, ngroups=2,
+                        init="randn", seed=91, d_final=True), 64),
+    ("ragged_q128", dict(batch=2, seqlen=700, nheads=16, headdim=64, dstate=128, ngroups=2,
+                         init="randn", seed=92, d_final=True), 128),
+    ("ragged_q256", dict(batch=2, seqlen=700, nheads=16, headdim=64, dstate=128, ngroups=2,
+                         init="randn", seed=93, d_final=True), 256),
+    ("p32n64", dict(batch=1, seqlen=333, nheads=2, headdim=32, dstate=64, ngroups=1,
+                    init="randn", seed=94), 256),
+    ("p128n32", dict(batch=1, seqlen=300, nheads=4, headdim=128, dstate=32, ngroups=4,
+                     init="zeros", seed=95, d_final=True), 128),
+    ("p128n128", dict(batch=1, seqlen=520, nheads=4, headdim=128, dstate=128, ngroups=2,
+                      init="randn", seed=96), 256),
+    ("odd_heads_short", dict(batch=3, seqlen=37, nheads=3, headdim=64, dstate=64, ngroups=1,
+                             init="randn", seed=97), 256),
+    ("packed_empty_and_one", dict(batch=1, seqlen=891, nheads=8, headdim=64, dstate=128, ngroups=2,
+                                  init="randn", seed=98, d_final=True, lengths=[1, 0, 300, 513, 77]),
+     256),
+]
+
+
+@pytest.mark.parametrize("name,kw,Q", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_dbdc_matches_split_and_oracle(name, kw, Q):
+    """The one-kernel dB/dC (SSD_FLAG_BWD_FUSED) against the three-kernel form
+    (the default): dB, dC, dx and d_init bit for bit (same values, same order of
+    every sum); ddt, dA and d_dt_bias to rounding (the decay-gradient sums R and K
+    are added in another order); both against the oracle."""
+    if kw.get("lengths"):
+        kw = dict(kw, seqlen=sum(kw["lengths"]))
+    inp = inputs.make_inputs(io="bf16", bwd=True, **kw)
+    g = gpu_bwd(ssd, inp, Q, fused=True)
+    gs = gpu_bwd(ssd, inp, Q)
+    torch.cuda.synchronize()
+    for k in ("dx", "dB", "dC", "d_init", "dD"):
+        if g[k] is not None:
+            assert torch.equal(g[k], gs[k]), (name, k)
+    for k in ("ddt", "dA", "d_dt_bias"):
+        assert normwise(np64(g[k]), np64(gs[k])) <= 1e-5, (name, k)
+    ref = oracle_bwd(inp)
+    check(g, ref, "bf16", name + " fused")
+    check(gs, ref, "bf16", name + " split")
+
+
+def test_bwd_kernel_mask():
+    import ctypes
+    inp = inputs.make_inputs(1, 300, 4, 64, 128, 2, io="bf16", init="zeros", bwd=True, seed=99)
+    d = to_dev(inp)
+    L = ssd.lib()
+    assert L.ssd_bwd_kernel_mask(ctypes.byref(ssd.problem(d["x"], d["B"])), 256, 0) == 0x7F
+    assert L.ssd_bwd_kernel_mask(ctypes.byref(ssd.problem(d["x"], d["B"], flags=ssd.FLAG_BWD_FUSED)),
+                                 256, 0) == 0x4F
+    inp = inputs.make_inputs(1, 300, 2, 16, 32, 1, io="f32", init="zeros", bwd=True, seed=99)
+    d = to_dev(inp)
+    assert L.ssd_bwd_kernel_mask(ctypes.byref(ssd.problem(d["x"], d["B"])), 64, 0) == 0x7F

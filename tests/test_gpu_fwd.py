@@ -333,9 +333,11 @@ def test_fwd_cb_in_chunk_state(lengths):
 # so a scan error as large as the SSM term itself could hide under the y gate.
 # Without D the output is the scan alone, gated normwise at 1e-2.  Every full-size
 # workload here takes the path whose chunk-state kernel also forms C.B^T.
-@pytest.mark.parametrize("cfg,heads", [(1, list(range(8)) + [63]), (3, [5, 16, 17, 30]),
+@pytest.mark.parametrize("cfg,heads", [(1, list(range(64))), (3, [5, 16, 17, 30]),
                                        (4, list(range(56, 64)))])
 def test_full_size_scan_only(cfg, heads):
+    """The layer workload on every head (both batch rows, all 64 heads); the long
+    context and packed workloads on a group's worth of sampled heads."""
     inp = inputs.config_inputs(cfg)
     inp["D"] = None
     d = to_dev(inp)
