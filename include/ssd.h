@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 10
+#define SSD_ABI_VERSION 11
 
 typedef enum {
   SSD_OK = 0,
@@ -122,6 +122,21 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   4x2, 8x4, 16x4, 16x8; 5..7: the sequential carry with 1, 4, 8 chunks of loads
  *   in flight (5 is SSD_FLAG_SEQUENTIAL_SCAN).  Results agree to rounding. */
 #define SSD_FLAG_SCAN_VARIANT(v) ((v) << 16)
+/* SSD_FLAG_CS_VARIANT(v), v = 0..3: the form of the chunk-state kernels (the
+ *   forward's chunk states with the inline cumsum, and the backward's adjoint
+ *   chunk states) on the bf16 path.  0 (the default) takes the tuned per-shape
+ *   table's entry for the problem's (headdim, dstate, heads per group, chunk size),
+ *   measured on this GPU by mamba_ssd_chunked_03_amd/tuning/sweep.py and compiled
+ *   into the library (aitrends.kr/articles/109906, "putting autotune results into
+ *   the training pipeline"), else the widest form the shape allows.  1: one head
+ *   per workgroup, C.B^T by its own kernel; 2: two heads of a group per workgroup
+ *   (sharing each staged slice of B or C), C.B^T by its own kernel; 3: two heads per
+ *   workgroup, C.B^T formed inside the chunk-state kernel.  2 needs an even number
+ *   of heads per group (and, with dstate 32 or headdim 128 at dstate 128, is
+ *   outside the kernel's shapes); 3 also needs chunk_size 256 and eight heads per
+ *   group; a variant the problem cannot run, or 2 or 3 on the fp32 path, returns
+ *   SSD_ERR_UNSUPPORTED.  Results are bitwise the same for every variant. */
+#define SSD_FLAG_CS_VARIANT(v) ((v) << 20)
 /* SSD_FLAG_CHAINED_FWD: ssd_fwd runs the fused single-pass forward: after the
  *   C.B^T kernel, one kernel forms each chunk's state, takes the state entering the
  *   chunk from the previous chunk's workgroup (a chained scan: work is handed out
@@ -187,6 +202,11 @@ const char* ssd_status_string(int32_t status);
  * of a group's heads holds one 64-row block of the chunk's C.B^T).  A profiling and
  * accounting aid; the results do not depend on it.  Returns 0 for an invalid problem. */
 int32_t ssd_fwd_kernel_mask(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
+
+/* Which chunk-state form (SSD_FLAG_CS_VARIANT numbering, 1..3) ssd_fwd and ssd_bwd
+ * run for this problem: the variant forced by problem->flags, else the tuned
+ * table's entry, else the widest valid form.  0 for an invalid problem. */
+int32_t ssd_cs_variant(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 
 /* Which of the seven backward kernels (bit k-1 for SSD_FLAG_BWD_KERNEL(k)) a complete
  * ssd_bwd call on this problem launches: 0x7F, or 0x4F where one kernel forms dB and

@@ -24,6 +24,7 @@ using namespace ssd;
 static_assert(kFlagSequentialScan == SSD_FLAG_SEQUENTIAL_SCAN, "flag bit seen by the kernels");
 static_assert(kScanVariantShift == 16 && SSD_FLAG_SCAN_VARIANT(1) == 1 << kScanVariantShift,
               "variant field seen by the kernels");
+static_assert(SSD_FLAG_CS_VARIANT(1) == 1 << kCsVariantShift, "chunk-state variant field seen by the kernels");
 
 namespace {
 
@@ -40,7 +41,7 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   if (pr->dt_softplus != 0 && pr->dt_softplus != 1) return SSD_ERR_SHAPE;
   if (pr->flags & ~(SSD_FLAG_SAVE_FOR_BWD | SSD_FLAG_FROM_SAVED | SSD_FLAG_ONE_STREAM |
                     SSD_FLAG_SEQUENTIAL_SCAN | SSD_FLAG_CHAINED_FWD | SSD_FLAG_BWD_FUSED | SSD_FLAG_BWD_KERNEL(7) |
-                    SSD_FLAG_FWD_KERNEL(7) | SSD_FLAG_SCAN_VARIANT(15)))
+                    SSD_FLAG_FWD_KERNEL(7) | SSD_FLAG_SCAN_VARIANT(15) | SSD_FLAG_CS_VARIANT(3)))
     return SSD_ERR_UNSUPPORTED;
   if ((pr->flags & SSD_FLAG_CHAINED_FWD) && (pr->flags & SSD_FLAG_FWD_KERNEL(7))) return SSD_ERR_UNSUPPORTED;
   if (((pr->flags >> 16) & 15) > 7) return SSD_ERR_UNSUPPORTED;
@@ -86,6 +87,8 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   p.map.packed = packed;
   p.map.seqlen = p.L;
   p.map.ncs = (p.L + Q - 1) / Q;
+  const int csv = (p.flags >> kCsVariantShift) & 3;
+  if (csv != kCsTable && !cs_variant_valid(p, csv)) return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
 
@@ -272,6 +275,12 @@ int32_t ssd_scan_variant(const ssd_problem* pr, int32_t Q, int32_t packed) {
   Prob p;
   if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
   return scan_variant_for(p);
+}
+
+int32_t ssd_cs_variant(const ssd_problem* pr, int32_t Q, int32_t packed) {
+  Prob p;
+  if (make_prob(pr, Q, packed, p) != SSD_OK) return 0;
+  return cs_variant_for(p);
 }
 
 int32_t ssd_fwd_kernel_mask(const ssd_problem* pr, int32_t Q, int32_t packed) {

@@ -33,6 +33,19 @@ enum { kScanTable = 0, kScanAssoc4x2 = 1, kScanAssoc8x4 = 2, kScanAssoc16x4 = 3,
 // The variant a problem's state passing runs: the flag's choice, else the tuned
 // table's entry nearest to the problem's chain length and lane count.
 int scan_variant_for(const Prob& p);
+// Prob::flags bits 20..21 (SSD_FLAG_CS_VARIANT of ssd.h): the shape of the
+// chunk-state kernels on the bf16 path, 0 = the tuned table's choice.
+constexpr int kCsVariantShift = 20;
+enum { kCsTable = 0, kCsOneHead = 1, kCsTwoHeads = 2, kCsTwoHeadsCB = 3 };
+// Whether variant v (1..3) can run this problem: two heads per workgroup need an
+// even head count per group and a shape whose shared operand and LDS fit; C.B^T
+// inside the kernel needs bf16, chunk 256 and eight heads per group (one 64-row
+// block of C.B^T per head pair).  The fp32 path has one form (1).
+bool cs_variant_valid(const Prob& p, int v);
+// The variant the chunk-state kernels run: the flag's choice, else the tuned
+// table's entry for the problem's (headdim, dstate, heads per group, chunk), else
+// the widest valid form.
+int cs_variant_for(const Prob& p);
 
 // mode of the chunk-state contraction
 enum { kStateFwd = 0,        // T_c = sum_j delta_j 2^(acs_last - acs_j) x_j B_j^T

@@ -344,14 +344,15 @@ constexpr int cs_lds_bytes(int P, int N, int hp) {
   return hp * (2 * 64 * (P + 16) * 2 + 256 * 4 + 5 * 4) + 64 * (N + 16) * 2;
 }
 
+// two heads per workgroup need the shared operand to split evenly over 512
+// threads and two such workgroups to fit a CU's LDS
+constexpr bool cs_two_ok(int P, int N) { return 64 * (N / 8) % 512 == 0 && cs_lds_bytes(P, N, 2) <= 80 * 1024; }
+
 template <int P, int N>
 static void launch_cs_bf16(const Prob& p, const void* X, const void* Y, float* delta, float* acs,
                            float* out, int mode, const CumsumIn& cs, hipStream_t st) {
-  // two heads per workgroup when a group's head count is even, the shared operand
-  // splits evenly over 512 threads, and two such workgroups still fit a CU's LDS
-  constexpr bool two_ok = 64 * (N / 8) % 512 == 0 && cs_lds_bytes(P, N, 2) <= 80 * 1024;
-  if constexpr (two_ok) {
-    if ((p.H / p.G) % 2 == 0) return launch_cs_hp<P, N, 2>(p, X, Y, delta, acs, out, mode, cs, st);
+  if constexpr (cs_two_ok(P, N)) {
+    if (cs_variant_for(p) >= kCsTwoHeads) return launch_cs_hp<P, N, 2>(p, X, Y, delta, acs, out, mode, cs, st);
   }
   if (cs.C) return;  // C.B^T is formed only by the two-head kernel (cb_in_chunk_state)
   launch_cs_hp<P, N, 1>(p, X, Y, delta, acs, out, mode, cs, st);
@@ -382,12 +383,44 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
   return launch_cs(p, X, Y, const_cast<float*>(delta), const_cast<float*>(acs), out, mode, CumsumIn{}, st);
 }
 
-bool cb_in_chunk_state(const Prob& p) {
-  // bf16, chunks of four 64-row blocks, and two heads per workgroup with four
-  // head pairs per group (launch_cs_bf16's two-head condition)
-  return p.io == 1 && p.Q == 256 && p.G > 0 && p.H / p.G == 8 && (64 * (p.N / 8)) % 512 == 0 &&
-         cs_lds_bytes(p.P, p.N, 2) <= 80 * 1024;
+bool cs_variant_valid(const Prob& p, int v) {
+  if (v == kCsOneHead) return true;
+  if (p.io != 1 || p.G <= 0 || (v != kCsTwoHeads && v != kCsTwoHeadsCB)) return false;
+  const int hpg = p.H / p.G;
+  if (hpg % 2 || !cs_two_ok(p.P, p.N)) return false;
+  // C.B^T inside: chunks of four 64-row blocks and four head pairs per group
+  return v == kCsTwoHeads || (p.Q == 256 && hpg == 8);
 }
+
+// The tuned table's chunk-state rows, measured by tuning/sweep.py and turned into
+// tuned_cs.inc by build.py (an empty table leaves the widest valid form).
+struct CsEntry {
+  int32_t P, N, hpg, Q;  // headdim, dstate, heads per group, chunk size of the measured shape
+  int32_t variant;       // the fastest forward there (kCsOneHead .. kCsTwoHeadsCB)
+};
+#if __has_include("tuned_cs.inc")
+#include "tuned_cs.inc"
+#else
+static const CsEntry kTunedCs[] = {{0, 0, 0, 0, 0}};
+static const int kTunedCsCount = 0;
+#endif
+
+int cs_variant_for(const Prob& p) {
+  const int f = (p.flags >> kCsVariantShift) & 3;
+  if (f != kCsTable) return f;  // (make_prob refuses a variant the problem cannot run)
+  if (p.io != 1 || p.G <= 0) return kCsOneHead;
+  const int hpg = p.H / p.G;
+  for (int i = 0; i < kTunedCsCount; ++i) {
+    const CsEntry& e = kTunedCs[i];
+    if (e.P == p.P && e.N == p.N && e.hpg == hpg && e.Q == p.Q && cs_variant_valid(p, e.variant))
+      return e.variant;
+  }
+  for (int v = kCsTwoHeadsCB; v > kCsOneHead; --v)
+    if (cs_variant_valid(p, v)) return v;
+  return kCsOneHead;
+}
+
+bool cb_in_chunk_state(const Prob& p) { return p.io == 1 && cs_variant_for(p) == kCsTwoHeadsCB; }
 
 hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* Bm, const float* dt,
                                      const float* dt_bias, const float* A, float* delta, float* acs,

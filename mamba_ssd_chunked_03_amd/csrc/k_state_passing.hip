@@ -257,15 +257,15 @@ static void launch_sp(const Prob& p, dim3 grid, const float* states, const float
 }
 
 // The tuned per-shape table: (chunks per sequence, independent lanes) -> variant,
-// measured by tuning/sweep.py and turned into tuned_table.inc by build.py.  An
+// measured by tuning/sweep.py and turned into tuned_scan.inc by build.py.  An
 // empty table leaves the rule below.
 struct ScanEntry {
   int32_t chunks;  // chunks per sequence of the measured shape
   int64_t lanes;   // sequences x heads x headdim x dstate / 4 of the measured shape
   int32_t variant;
 };
-#if __has_include("tuned_table.inc")
-#include "tuned_table.inc"
+#if __has_include("tuned_scan.inc")
+#include "tuned_scan.inc"
 #else
 static const ScanEntry kTunedScan[] = {{0, 0, 0}};
 static const int kTunedScanCount = 0;

@@ -53,6 +53,12 @@ def FLAG_SCAN_VARIANT(v):
     return int(v) << 16
 
 
+def FLAG_CS_VARIANT(v):
+    """Chunk-state kernels: 0 the tuned table's choice, 1 one head per workgroup,
+    2 two heads per workgroup, 3 two heads with C.B^T formed inside."""
+    return int(v) << 20
+
+
 def FLAG_FWD_KERNEL(k):
     """ssd_fwd launches only its k-th kernel (1-based, order of FWD_KERNELS)."""
     return int(k) << 12
@@ -63,6 +69,7 @@ _SIGS = {
     "ssd_fwd_kernel_mask": ([_P, _I32, _I32], _I32),
     "ssd_bwd_kernel_mask": ([_P, _I32, _I32], _I32),
     "ssd_scan_variant": ([_P, _I32, _I32], _I32),
+    "ssd_cs_variant": ([_P, _I32, _I32], _I32),
     "ssd_fwd_chained_error_offset": ([_P, _I32, _I32], _I64),
     "ssd_status_string": ([_I32], ctypes.c_char_p),
     "ssd_num_chunks": ([_P, _I32, _I32], _I64),
@@ -84,7 +91,7 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 # The argument lists above follow this version of include/ssd.h (SSD_ABI_VERSION).
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 _lib = None
 
@@ -218,7 +225,7 @@ def num_chunks(prob, chunk_size, packed):
 def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_size=256,
         dt_softplus=True, workspace=None, out=None, final=None, save_for_backward=False,
         only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0,
-        chained=False):
+        chained=False, cs_variant=0):
     """y, final_states = SSD(x, ...) on the GPU.  Shapes as in include/ssd.h.
 
     save_for_backward: keep the intermediates in ``workspace`` (which must hold
@@ -233,7 +240,8 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
     sequential_scan: the state passing walks the chunks with a sequential carry
     instead of the associative scan (a comparison point).
     scan_variant: force a state-passing kernel (FLAG_SCAN_VARIANT); 0 = tuned table.
-    chained: the fused single-pass forward (chained scan across chunks)."""
+    chained: the fused single-pass forward (chained scan across chunks).
+    cs_variant: force a chunk-state form (FLAG_CS_VARIANT); 0 = tuned table."""
     if only_kernel and (workspace is None or out is None):
         raise ValueError("only_kernel needs the workspace and outputs of a complete call")
     batch, seqlen, H, P, G, N, nst, io = _check_inputs(x, dt, A, B, C, D, dt_bias, init, cu_seqlens)
@@ -246,7 +254,7 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None, chunk_
                    (FLAG_SAVE_FOR_BWD if save_for_backward else 0) | FLAG_FWD_KERNEL(only_kernel) |
                    (FLAG_ONE_STREAM if one_stream else 0) |
                    (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0) | FLAG_SCAN_VARIANT(scan_variant) |
-                   (FLAG_CHAINED_FWD if chained else 0))
+                   (FLAG_CHAINED_FWD if chained else 0) | FLAG_CS_VARIANT(cs_variant))
     L = lib()
     packed = int(cu_seqlens is not None)
     if save_for_backward:
@@ -301,11 +309,13 @@ def fwd_noalloc(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu_seqlens=None
 def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_seqlens=None,
         chunk_size=256, dt_softplus=True, workspace=None, from_saved=False, grads=None,
         only_kernel=0, prepare=False, one_stream=False, sequential_scan=False, scan_variant=0,
-        fused=False):
+        fused=False, cs_variant=0):
     """Gradients of <dout, y> + <d_final, final> (dict of GPU tensors).
 
     fused: dB and dC from one kernel, one pass over x and dy (SSD_FLAG_BWD_FUSED),
     instead of the three-kernel form.
+    cs_variant: force a chunk-state form (FLAG_CS_VARIANT) for the recompute and
+    the adjoint chunk states; 0 = tuned table.
     from_saved: ``workspace`` holds the intermediates of a save_for_backward
     fwd call on the same inputs; the recompute is skipped.
     grads: a dict returned by an earlier call, written again instead of new tensors.
@@ -334,7 +344,7 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None, cu_
         raise ValueError("only_kernel needs from_saved and the grads of a complete call")
     flags = (FLAG_FROM_SAVED if from_saved else 0) | FLAG_BWD_KERNEL(only_kernel) | \
         (FLAG_ONE_STREAM if one_stream else 0) | (FLAG_SEQUENTIAL_SCAN if sequential_scan else 0) | \
-        FLAG_SCAN_VARIANT(scan_variant) | (FLAG_BWD_FUSED if fused else 0)
+        FLAG_SCAN_VARIANT(scan_variant) | (FLAG_BWD_FUSED if fused else 0) | FLAG_CS_VARIANT(cs_variant)
     prob = problem(x, B, cu_seqlens, dt_softplus, flags)
     L = lib()
     packed = int(cu_seqlens is not None)

@@ -402,3 +402,47 @@ def test_bwd_kernel_mask():
     inp = inputs.make_inputs(1, 300, 2, 16, 32, 1, io="f32", init="zeros", bwd=True, seed=99)
     d = to_dev(inp)
     assert L.ssd_bwd_kernel_mask(ctypes.byref(ssd.problem(d["x"], d["B"])), 64, 0) == 0x7F
+
+
+CS_CASES = [
+    ("eight_heads_per_group", dict(batch=2, seqlen=700, nheads=16, headdim=64, dstate=128, ngroups=2,
+                                   init="randn", seed=101, d_final=True), 256, (1, 2, 3)),
+    ("four_heads_per_group", dict(batch=2, seqlen=450, nheads=8, headdim=32, dstate=64, ngroups=2,
+                                  init="randn", seed=102), 128, (1, 2)),
+    ("packed_eight_heads", dict(batch=1, seqlen=891, nheads=8, headdim=64, dstate=128, ngroups=1,
+                                init="randn", seed=103, d_final=True, lengths=[1, 0, 300, 513, 77]),
+     256, (1, 2, 3)),
+]
+
+
+@pytest.mark.parametrize("name,kw,Q,variants", CS_CASES, ids=[c[0] for c in CS_CASES])
+def test_chunk_state_variants_agree(name, kw, Q, variants):
+    """Every chunk-state form (SSD_FLAG_CS_VARIANT: one or two heads per workgroup,
+    C.B^T inside or by its own kernel) gives bit-identical outputs, final states and
+    gradients, also through the saved context; the first is checked against the oracle."""
+    import ctypes
+    if kw.get("lengths"):
+        kw = dict(kw, seqlen=sum(kw["lengths"]))
+    inp = inputs.make_inputs(io="bf16", bwd=True, **kw)
+    d = to_dev(inp)
+    base = None
+    for v in variants:
+        prob = ssd.problem(d["x"], d["B"], d["cu_seqlens"], flags=ssd.FLAG_CS_VARIANT(v))
+        assert ssd.lib().ssd_cs_variant(ctypes.byref(prob), Q, int(d["cu_seqlens"] is not None)) == v
+        need = ssd.lib().ssd_bwd_workspace_bytes(ctypes.byref(prob), Q, int(d["cu_seqlens"] is not None))
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        y, fin = gpu_fwd(ssd, inp, Q, cs_variant=v, workspace=ws, save_for_backward=True)
+        g = gpu_bwd(ssd, inp, Q, cs_variant=v, workspace=ws, from_saved=True)
+        g2 = gpu_bwd(ssd, inp, Q, cs_variant=v)  # recomputed forward
+        torch.cuda.synchronize()
+        for k in KEYS:
+            if g[k] is not None:
+                assert torch.equal(g[k], g2[k]), (name, v, k)
+        if base is None:
+            base = (y, fin, g)
+            check(g, oracle_bwd(inp), "bf16", "%s variant %d" % (name, v))
+            continue
+        assert torch.equal(y, base[0]) and torch.equal(fin, base[1]), (name, v)
+        for k in KEYS:
+            if g[k] is not None:
+                assert torch.equal(g[k], base[2][k]), (name, v, k)

@@ -12,16 +12,18 @@ TABLE = build.TABLE_JSON
 
 def test_include_matches_table(tmp_path, monkeypatch):
     monkeypatch.setattr(build, "BUILD_DIR", str(tmp_path))
-    path = build.write_table_include()
-    text = open(path).read()
-    if not os.path.exists(TABLE):
-        assert "kTunedScanCount = 0;" in text
-        return
-    t = json.load(open(TABLE))
-    rows = t["state_passing"]
+    scan_path, cs_path = build.write_table_include()
+    text, cs_text = open(scan_path).read(), open(cs_path).read()
+    t = json.load(open(TABLE)) if os.path.exists(TABLE) else {}
+    rows = t.get("state_passing", [])
     assert "kTunedScanCount = %d;" % len(rows) in text
     for e in rows:
         assert "{%d, %d, %d}," % (e["chunks_per_seq"], e["lanes"], e["variant"]) in text
+    cs = t.get("chunk_state", [])
+    assert "kTunedCsCount = %d;" % len(cs) in cs_text
+    for e in cs:
+        assert "{%d, %d, %d, %d, %d}," % (e["headdim"], e["dstate"], e["heads_per_group"], e["chunk"],
+                                          e["variant"]) in cs_text
 
 
 def test_table_rows_are_the_measured_best():
@@ -77,3 +79,54 @@ def test_library_looks_up_the_nearest_measured_shape():
             assert L.ssd_scan_variant(ctypes.byref(p), 256, packed) == forced
         p.flags = ssd.FLAG_SEQUENTIAL_SCAN
         assert L.ssd_scan_variant(ctypes.byref(p), 256, packed) == 5
+
+
+def test_chunk_state_rows_are_the_measured_best():
+    if not os.path.exists(TABLE):
+        pytest.skip("no tuned table")
+    rows = json.load(open(TABLE)).get("chunk_state", [])
+    seen = set()
+    for e in rows:
+        us = {int(k): v for k, v in e["us"].items()}
+        assert set(us) <= {1, 2, 3} and 1 in us
+        assert e["variant"] == min(us, key=us.get)
+        key = (e["headdim"], e["dstate"], e["heads_per_group"], e["chunk"])
+        assert key not in seen
+        seen.add(key)
+
+
+def _valid_cs(P, N, hpg, Q):
+    """Which chunk-state forms a bf16 problem can run (the rule the library states)."""
+    lds2 = 2 * (2 * 64 * (P + 16) * 2 + 256 * 4 + 5 * 4) + 64 * (N + 16) * 2
+    two = hpg % 2 == 0 and (64 * (N // 8)) % 512 == 0 and lds2 <= 80 * 1024
+    return {1} | ({2} if two else set()) | ({3} if two and Q == 256 and hpg == 8 else set())
+
+
+def test_library_looks_up_the_chunk_state_table():
+    from mamba_ssd_chunked_03_amd import ssd
+    if not os.path.exists(ssd.LIB_PATH):
+        pytest.skip("libssd.so not built")
+    import ctypes
+    L = ssd.lib()
+    rows = json.load(open(TABLE)).get("chunk_state", []) if os.path.exists(TABLE) else []
+    table = {(e["headdim"], e["dstate"], e["heads_per_group"], e["chunk"]): e["variant"] for e in rows}
+    for P in (32, 64, 128):
+        for N in (32, 64, 128):
+            for hpg in (1, 2, 3, 4, 8, 16):
+                for Q in (64, 128, 256):
+                    p = ssd.Problem(2, 1000, 16 * hpg, P, N, 16, 0, ssd.BF16, 1, 0)
+                    valid = _valid_cs(P, N, hpg, Q)
+                    v = L.ssd_cs_variant(ctypes.byref(p), Q, 0)
+                    want = table.get((P, N, hpg, Q))
+                    assert v == (want if want in valid else max(valid)), (P, N, hpg, Q, v)
+                    for forced in (1, 2, 3):
+                        p.flags = ssd.FLAG_CS_VARIANT(forced)
+                        got = L.ssd_cs_variant(ctypes.byref(p), Q, 0)
+                        assert got == (forced if forced in valid else 0), (P, N, hpg, Q, forced)
+                    p.flags = 0
+                    # C.B^T inside the chunk-state kernel is variant 3 (forward kernel mask 0xB)
+                    assert (L.ssd_fwd_kernel_mask(ctypes.byref(p), Q, 0) == 0xB) == (v == 3)
+    p = ssd.Problem(1, 100, 8, 16, 16, 1, 0, ssd.F32, 1, 0)   # fp32: one form
+    assert L.ssd_cs_variant(ctypes.byref(p), 64, 0) == 1
+    p.flags = ssd.FLAG_CS_VARIANT(2)
+    assert L.ssd_cs_variant(ctypes.byref(p), 64, 0) == 0
