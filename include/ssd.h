@@ -38,7 +38,7 @@
  *    it and the call returns before it runs; keep buffers alive until then.
  *  - State kept across calls: none, except this.  ssd_fwd and ssd_bwd run kernels
  *    that do not depend on each other on a second stream of the library's own
- *    (one per device, with three events, created by the first call that uses it,
+ *    (one per device, with four events, created by the first call that uses it,
  *    default priority, kept until the process ends; ssd_fwd uses none where its
  *    chunk-state kernel forms C.B^T, see ssd_fwd_kernel_mask), forked from and
  *    joined back to `stream` with events: the call as a whole stays ordered on

@@ -1,7 +1,7 @@
 // C ABI of libssd: argument validation, workspace layout and launch order.
 //
 // Every check the host can make happens before the first launch.  The library
-// allocates no memory.  Its only state across calls is one side stream and three
+// allocates no memory.  Its only state across calls is one side stream and four
 // events per device, created at the first call that forks to them and kept until
 // the process ends (side_lane below).  A launch that fails after a call has forked
 // to the side stream still joins it back to the caller's stream before the call
@@ -139,7 +139,7 @@ ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool 
   return SSD_OK;
 }
 
-// A second stream per device, with three events, created on first use (default
+// A second stream per device, with four events, created on first use (default
 // priority) and kept for the life of the process: kernels of one call that do
 // not depend on the ones queued before them run there; the caller's stream forks
 // to it and joins it again through the events, so each call stays ordered on the
@@ -150,7 +150,7 @@ ssd_status setup_map(Prob& p, const int32_t* cu, char* ws, hipStream_t st, bool 
 struct SideLane {
   bool tried = false, ok = false;
   hipStream_t stream = nullptr;
-  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 SideLane* side_lane(hipStream_t caller, std::unique_lock<std::mutex>& lock) {
   static std::mutex mu;
@@ -170,7 +170,7 @@ SideLane* side_lane(hipStream_t caller, std::unique_lock<std::mutex>& lock) {
   if (!l.tried) {
     l.tried = true;
     l.ok = hipStreamCreateWithFlags(&l.stream, hipStreamNonBlocking) == hipSuccess;
-    for (int i = 0; l.ok && i < 3; ++i)
+    for (int i = 0; l.ok && i < 4; ++i)
       l.ok = hipEventCreateWithFlags(&l.ev[i], hipEventDisableTiming) == hipSuccess;
   }
   if (!l.ok) {
@@ -479,17 +479,21 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   // all of them with whole R, K from one pass over x and dy, after the reverse
   // scan.  Those run on a side stream (the first two from the start, dB or the
   // one kernel after an event from the reverse scan) beside the adjoint states,
-  // the reverse scan and dx; the finalize waits for the side stream.
+  // the reverse scan and dx; the finalize waits for dCB and dC (or the one
+  // kernel) and runs beside dB, and the call ends once dB is done too.
   const bool fused = bwd_fused(p);
   std::unique_lock<std::mutex> lane_lock;
   const bool one_stream = (p.flags & SSD_FLAG_ONE_STREAM) != 0;
   SideLane* side =
       (!only && p.io == SSD_BF16 && p.nck > 0 && !one_stream) ? side_lane(st, lane_lock) : nullptr;
-  if (side && !fused) {  // events: 0 fork, 1 reverse scan done, 2 side stream done
+  // events: 0 fork, 1 reverse scan done, 2 what the finalize reads from the side
+  // stream is done (dCB's partials and dC's r; or the one kernel), 3 dB done
+  if (side && !fused) {
     SSD_TRY_FORKED(hipEventRecord(side->ev[0], st));
     SSD_TRY_FORKED(hipStreamWaitEvent(side->stream, side->ev[0], 0));
     SSD_TRY_FORKED(launch_bwd_chunk(p, a, 2, side->stream));
     SSD_TRY_FORKED(launch_bwd_chunk(p, a, 3, side->stream));
+    SSD_TRY_FORKED(hipEventRecord(side->ev[2], side->stream));
   }
   // adjoint of the state carried into each chunk, then the reverse scan
   if (!only || only == 1)
@@ -497,12 +501,17 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   if (!only || only == 2)
     SSD_TRY_FORKED(launch_state_passing(p, U, decay, d_final_states, dE, hb, d_init_states, 1, st));
   if (side) {
+    // dB (or the one kernel) after the reverse scan; the finalize, which reads
+    // nothing dB writes, runs beside dB once dx and dC are done
     SSD_TRY_FORKED(hipEventRecord(side->ev[1], st));
     SSD_TRY_FORKED(hipStreamWaitEvent(side->stream, side->ev[1], 0));
     SSD_TRY_FORKED(fused ? launch_bwd_dbc(p, a, side->stream) : launch_bwd_chunk(p, a, 4, side->stream));
-    SSD_TRY_FORKED(hipEventRecord(side->ev[2], side->stream));
+    SSD_TRY_FORKED(hipEventRecord(side->ev[fused ? 2 : 3], side->stream));
     SSD_TRY_FORKED(launch_bwd_chunk(p, a, 1, st));
     SSD_TRY_FORKED(hipStreamWaitEvent(st, side->ev[2], 0));
+    SSD_TRY_FORKED(launch_bwd_finalize(p, a, st, fused));
+    if (!fused) SSD_TRY_FORKED(hipStreamWaitEvent(st, side->ev[3], 0));
+    return SSD_OK;
   } else if (fused) {
     if (!only || only == 3) SSD_TRY_FORKED(launch_bwd_chunk(p, a, 1, st));
     if (!only || only == 4) SSD_TRY_FORKED(launch_bwd_dbc(p, a, st));

@@ -947,15 +947,19 @@ __global__ __launch_bounds__(256) void bwd_db_f32_kernel(
 }
 
 // ---------------------------------------------------------------- finalize ----
-// One workgroup per (chunk, head), one token per thread: dAcs_i = rR_i - Ks_i +
-// (R, K tile partials, or whole R, K per token: Rf, Kf) (+ last_term at the last
-// token); ddA_t = sum_{i>=t} dAcs_i,
-// d(delta)_t = ddd_t + A ddA_t, ddt = d(delta) sigmoid(z) when softplus is on;
-// per-chunk partial sums of delta*ddA and ddt.  Wave w holds the 64-token block
-// w from the chunk's end with its lanes reversed, so a DPP prefix sum over a
-// wave is a suffix sum over its tokens; the blocks' totals are added in order
-// from the chunk's end.  Every token's loads are issued at once.
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(
+// One workgroup per (chunk, 8 heads), one wavefront per head: dAcs_i = rR_i - Ks_i
+// + (R, K tile partials, or whole R, K per token: Rf, Kf) (+ last_term at the last
+// token); ddA_t = sum_{i>=t} dAcs_i, d(delta)_t = ddd_t + A ddA_t,
+// ddt = d(delta) sigmoid(z) when softplus is on; per-chunk partial sums of
+// delta*ddA and ddt.  Lane l holds four consecutive tokens, lane 0 the chunk's
+// last four, so that the suffix sum is the lane's own tokens summed from its last
+// plus a DPP prefix sum of the lane totals.  The per-head arrays are read four
+// tokens (16 bytes) at a time.  dt is read and ddt written through LDS, eight
+// adjacent heads of a token at a time: a head's values lie H floats apart, and
+// read one head per workgroup, every wave instruction touched 64 cache lines.
+// Every load is issued before the first wait.
+constexpr int kFinHeads = 8;  // heads per workgroup, one per wavefront
+__global__ __launch_bounds__(kFinHeads * 64) void bwd_finalize_kernel(
     ChunkMap m, int H, int softplus, const float* __restrict__ dt,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ delta, const float* __restrict__ rR, const float* __restrict__ Ks,
@@ -963,84 +967,115 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     const float* __restrict__ Rp, const float* __restrict__ Kp, int ntile,
     const float* __restrict__ Rf, const float* __restrict__ Kf, float* __restrict__ ddt,
     float* __restrict__ dAp, float* __restrict__ dbp) {
-  __shared__ float wtot[4], wpa[4], wpb[4];
-  const int k = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  constexpr int NT = kFinHeads * 64, NE = kFinHeads * QMAX / NT;
+  __shared__ __attribute__((aligned(16))) float tk[kFinHeads][QMAX];  // dt in, then ddt out
+  const int k = blockIdx.x, h0 = blockIdx.y * kFinHeads;
+  const int nh = min(kFinHeads, H - h0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's head: h0 + w
   const ChunkInfo ci = chunk_info(m, k);
-  const int64_t kh = (int64_t)k * H + h;
   if (ci.len <= 0) {
-    if (tid == 0) {
-      dAp[kh] = 0.f;
-      dbp[kh] = 0.f;
+    if (tid < nh) {
+      dAp[(int64_t)k * H + h0 + tid] = 0.f;
+      dbp[(int64_t)k * H + h0 + tid] = 0.f;
     }
     return;
   }
   const int Q = m.Q, len = ci.len;
-  const int t = Q - 64 * w - 1 - lane;  // negative for waves past a short chunk size
-  const bool in = t >= 0 && t < len;
-  const float Ah = A[h], bias = dt_bias ? dt_bias[h] : 0.f;
-  // Every load is issued unconditionally through a range-checked buffer
-  // resource (tokens outside the chunk get an offset past every range and read
-  // zero), and the masked terms are dropped by selects: loads under branches
-  // were serialised, each waiting for the one before.
-  const uint32_t ot = in ? (uint32_t)t * 4u : 0x80000000u;
-  const uint32_t rowb = (uint32_t)len * 4u;
-  const float r0 = buf_load_f32(make_rsrc(rR + kh * Q, rowb), ot);
-  const float k0 = buf_load_f32(make_rsrc(Ks + kh * Q, rowb), ot);
-  const float dlv = buf_load_f32(make_rsrc(delta + kh * Q, rowb), ot);
-  const float d0v = buf_load_f32(make_rsrc(ddd + kh * Q, rowb), ot);
-  const float dtv = buf_load_f32(make_rsrc(dt + (int64_t)ci.start * H + h, rowb * (uint32_t)H),
-                                 in ? (uint32_t)t * (uint32_t)H * 4u : 0x80000000u);
-  // 64x64 tile partials: R over column tiles <= t's, K over row tiles >= t's
-  // (the others get an offset past the range: no memory access)
-  const int tt = t / 64, tlast = (len - 1) / 64;
-  const brsrc rrp = make_rsrc(Rp + kh * ntile * Q, (uint32_t)(ntile * Q * 4));
-  const brsrc rkp = make_rsrc(Kp + kh * ntile * Q, (uint32_t)(ntile * Q * 4));
-  float rp[4], kp[4];
-  bool ur[4], uk[4];
+  // dt of the workgroup's heads: element e is token e / 8, head e % 8 (range-checked
+  // over the chunk's tokens; heads past H get an offset past every range)
+  const brsrc rdt = make_rsrc(dt + (int64_t)ci.start * H + h0, (uint32_t)len * (uint32_t)H * 4u);
+  float dtv[NE];
+#pragma unroll
+  for (int c = 0; c < NE; ++c) {
+    const int e = tid + NT * c, t = e / kFinHeads, hh = e % kFinHeads;
+    dtv[c] = buf_load_f32(rdt, (t < len && hh < nh) ? ((uint32_t)t * (uint32_t)H + hh) * 4u : 0x80000000u);
+  }
+  // this lane's tokens tb .. tb + 3 (lanes past the chunk size hold none), of head
+  // h0 + w (waves past H load nothing)
+  const bool hin = w < nh;
+  const int tb = Q - 4 * (lane + 1);
+  const bool lane_in = tb >= 0;
+  const uint32_t o = (lane_in && hin) ? (uint32_t)tb * 4u : 0x80000000u, qb = (uint32_t)Q * 4u;
+  const int tt = lane_in ? tb / 64 : 0, tlast = (len - 1) / 64;
+  const int64_t kh = (int64_t)k * H + h0 + (hin ? w : 0);
+  auto ld4 = [&](const float* base, uint32_t bytes, uint32_t off) {
+    const u32x4 v = buf_load16(make_rsrc(base, bytes), off);
+    return f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+  };
+  const f32x4 vr = ld4(rR + kh * Q, qb, o), vk = ld4(Ks + kh * Q, qb, o);
+  const f32x4 vd = ld4(delta + kh * Q, qb, o), v0 = ld4(ddd + kh * Q, qb, o);
+  const f32x4 vrf = ld4(Rf ? Rf + kh * Q : rR, qb, Rf ? o : 0x80000000u);
+  const f32x4 vkf = ld4(Kf ? Kf + kh * Q : Ks, qb, Kf ? o : 0x80000000u);
+  // 64x64 tile partials: R over column tiles <= the lane's, K over row tiles >= it
+  f32x4 vrp[4], vkp[4];
+  const uint32_t tbytes = (uint32_t)(ntile * Q * 4);
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) {
-    ur[tl] = tl <= tt && tl < ntile;
-    uk[tl] = tl >= tt && tl <= tlast && tl < ntile;
-    rp[tl] = buf_load_f32(rrp, ur[tl] ? ot + (uint32_t)(tl * Q * 4) : 0x80000000u);
-    kp[tl] = buf_load_f32(rkp, uk[tl] ? ot + (uint32_t)(tl * Q * 4) : 0x80000000u);
+    const bool ur = tl <= tt && tl < ntile, uk = tl >= tt && tl <= tlast && tl < ntile;
+    vrp[tl] = ld4(Rp + kh * ntile * Q, tbytes, ur ? o + (uint32_t)(tl * Q * 4) : 0x80000000u);
+    vkp[tl] = ld4(Kp + kh * ntile * Q, tbytes, uk ? o + (uint32_t)(tl * Q * 4) : 0x80000000u);
   }
-  // whole R and K per token (one kernel forms them), when given
-  const uint32_t ofr = Rf ? ot : 0x80000000u;
-  const float rf = buf_load_f32(make_rsrc(Rf ? Rf + kh * Q : rR, rowb), ofr);
-  const float kf = buf_load_f32(make_rsrc(Kf ? Kf + kh * Q : Ks, rowb), ofr);
-  const float lt = last_term[kh];
-  float v = r0 - k0 + (t == len - 1 ? lt : 0.f) + (rf - kf);
+  const float lt = hin ? last_term[kh] : 0.f;
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl) v = ur[tl] ? v + rp[tl] : v;
-#pragma unroll
-  for (int tl = 0; tl < 4; ++tl) v = uk[tl] ? v - kp[tl] : v;
-  v = in ? v : 0.f;
-  const float dl = in ? dlv : 0.f, d0 = in ? d0v : 0.f, z = in ? dtv + bias : 0.f;
-  const float sw = wave_inclusive_sum(v);
-  if (lane == 63) wtot[w] = sw;
-  __syncthreads();
-  float carry = 0.f;
-  for (int u = 0; u < w; ++u) carry = wtot[u] + carry;
-  const float incl = sw + carry;
-  float pa = 0.f, pb = 0.f;
-  if (in) {
-    const float dd = d0 + Ah * incl;
-    const float g = softplus ? dd * sigmoid_f(z) : dd;
-    ddt[(ci.start + t) * (int64_t)H + h] = g;
-    pa = dl * incl;
-    pb = g;
-  }
-  pa = wave_sum(pa);
-  pb = wave_sum(pb);
-  if (lane == 0) {
-    wpa[w] = pa;
-    wpb[w] = pb;
+  for (int c = 0; c < NE; ++c) {
+    const int e = tid + NT * c;
+    tk[e % kFinHeads][e / kFinHeads] = dtv[c];
   }
   __syncthreads();
-  if (tid == 0) {
-    dAp[kh] = ((wpa[0] + wpa[1]) + wpa[2]) + wpa[3];
-    dbp[kh] = ((wpb[0] + wpb[1]) + wpb[2]) + wpb[3];
+  if (hin) {  // (uniform per wave)
+    const int h = h0 + w;
+    const float Ah = A[h], bias = dt_bias ? dt_bias[h] : 0.f;
+    const float4 zr = lane_in ? *(const float4*)&tk[w][tb] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float z_[4] = {zr.x, zr.y, zr.z, zr.w};
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tb + j;
+      float a = vr[j] - vk[j] + (t == len - 1 ? lt : 0.f) + (vrf[j] - vkf[j]);
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) a += vrp[tl][j];
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) a -= vkp[tl][j];
+      v[j] = (lane_in && t < len) ? a : 0.f;
+    }
+    // suffix sums: the lane's own tokens from its last, then the lanes before it
+    // (which hold the later tokens)
+    float s[4];
+    s[3] = v[3];
+    s[2] = v[2] + s[3];
+    s[1] = v[1] + s[2];
+    s[0] = v[0] + s[1];
+    const float incl = wave_inclusive_sum(s[0]);
+    float carry = __shfl_up(incl, 1);  // the lanes before this one (no subtraction: exact)
+    carry = lane == 0 ? 0.f : carry;
+    float pa = 0.f, pb = 0.f, g4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tb + j;
+      const bool in = lane_in && t < len;
+      const float suf = s[j] + carry;
+      const float dd = v0[j] + Ah * suf;
+      const float g = softplus ? dd * sigmoid_f(z_[j] + bias) : dd;
+      g4[j] = in ? g : 0.f;
+      pa += in ? vd[j] * suf : 0.f;
+      pb += in ? g : 0.f;
+    }
+    if (lane_in) *(float4*)&tk[w][tb] = make_float4(g4[0], g4[1], g4[2], g4[3]);  // (own dt read above)
+    pa = wave_sum(pa);
+    pb = wave_sum(pb);
+    if (lane == 0) {
+      dAp[kh] = pa;
+      dbp[kh] = pb;
+    }
+  }
+  __syncthreads();
+  // ddt, eight adjacent heads of a token at a time
+  float* dtt = ddt + (int64_t)ci.start * H + h0;
+#pragma unroll
+  for (int c = 0; c < NE; ++c) {
+    const int e = tid + NT * c, t = e / kFinHeads, hh = e % kFinHeads;
+    if (t < len && hh < nh) dtt[(int64_t)t * H + hh] = tk[hh][t];
   }
 }
 
@@ -1129,7 +1164,8 @@ hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStrea
 
 hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st, bool fused) {
   if (p.nck > 0)
-    hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, p.H), dim3(256), 0, st,
+    hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, (p.H + kFinHeads - 1) / kFinHeads),
+                       dim3(kFinHeads * 64), 0, st,
                        p.map, p.H, p.softplus, a.dt, a.dt_bias, a.A, a.delta, a.rR, a.Ks, a.ddd,
                        a.last_term, a.Rp, a.Kp, (p.io == 0 || fused) ? 0 : p.Q / 64,
                        fused ? a.Rp : nullptr, fused ? a.Kp : nullptr, a.ddt, a.dAp, a.dbp);
