@@ -446,3 +446,38 @@ def test_chunk_state_variants_agree(name, kw, Q, variants):
         for k in KEYS:
             if g[k] is not None:
                 assert torch.equal(g[k], base[2][k]), (name, v, k)
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_opt_in_forms_full_size(cfg):
+    """At the layer (config 2) and packed (config 4) workloads: the one-kernel dB/dC
+    (SSD_FLAG_BWD_FUSED) gives the three-kernel form's dB, dC, dx and d_init bit for
+    bit and its ddt, dA, d_dt_bias to rounding; every chunk-state form gives the same
+    forward outputs and gradients bit for bit.  (The default forms are checked
+    against the oracle by the full-size tests above.)"""
+    import ctypes
+    inp = inputs.config_inputs(cfg)
+    d = to_dev(inp)
+    packed = int(d["cu_seqlens"] is not None)
+    g = gpu_bwd(ssd, inp, 256)
+    gf = gpu_bwd(ssd, inp, 256, fused=True)
+    torch.cuda.synchronize()
+    for k in ("dx", "dB", "dC", "d_init", "dD"):
+        if g[k] is not None:
+            assert torch.equal(g[k], gf[k]), (cfg, k)
+    for k in ("ddt", "dA", "d_dt_bias"):
+        assert normwise(np64(gf[k]), np64(g[k])) <= 1e-5, (cfg, k)
+    del gf
+    y0, f0 = gpu_fwd(ssd, inp, 256)
+    for v in (1, 2, 3):
+        prob = ssd.problem(d["x"], d["B"], d["cu_seqlens"], flags=ssd.FLAG_CS_VARIANT(v))
+        if ssd.lib().ssd_cs_variant(ctypes.byref(prob), 256, packed) != v:
+            continue
+        y, f = gpu_fwd(ssd, inp, 256, cs_variant=v)
+        gv = gpu_bwd(ssd, inp, 256, cs_variant=v)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0) and torch.equal(f, f0), (cfg, v)
+        for k in KEYS:
+            if g[k] is not None:
+                assert torch.equal(gv[k], g[k]), (cfg, v, k)
+        del gv
