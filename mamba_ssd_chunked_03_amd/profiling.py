@@ -346,6 +346,50 @@ def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
     return out
 
 
+REQ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_WRREQ_sum",
+                "TCC_EA0_WRREQ_64B_sum")
+
+
+def request_sizes(csv_paths, copy_paths):
+    """Mean per launch of the L2-to-memory request counters, per kernel of the path
+    and for the copy kernel, from one or more counter CSVs (one rocprofv3 pass
+    each: the counters do not all fit one pass); a launch of a multi-kernel key
+    sums its kernels' means."""
+    def load(paths):
+        per = {}
+        for path in paths:
+            for c in REQ_COUNTERS:
+                for key, (mean, _) in counter_means(path, c).items():
+                    per.setdefault(key, {})[c] = mean
+        return per
+    return load(csv_paths), load(copy_paths).get("copy", {})
+
+
+def request_md(res, cp, copy_bytes, title, commands, summary_cmd):
+    lines = (["# " + title, ""] if title else []) + [
+        "Counter runs (from the repository root, one MI355X, one rocprofv3 pass each):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "Summarised with:", "", "    " + summary_cmd, ""]
+    rd, wr = cp.get("TCC_EA0_RDREQ_sum", 0.0), cp.get("TCC_EA0_WRREQ_sum", 0.0)
+    if rd and wr:
+        lines += ["The copy kernel moves %d bytes each way: %.0f read requests (%.1f bytes each) and %.0f "
+                  "write requests (%.1f bytes each)." % (copy_bytes, rd, copy_bytes / rd, wr, copy_bytes / wr), ""]
+    lines += ["Mean per launch.  The 32-byte read requests and the 128-byte ones the derived FETCH_SIZE "
+              "counts as bubbles (`TCC_BUBBLE`) are listed beside all read requests; the reads at 128 "
+              "bytes each are the kernel's HBM read bytes.", "",
+              "| Kernel | read requests | of them 32-byte | TCC_BUBBLE | reads at 128 B (MB) | write requests | "
+              "of them 64-byte | writes at 64 B (MB) |", "|---|---|---|---|---|---|---|---|"]
+    for key in KERNEL_FILES:
+        v = res.get(key)
+        if not v:
+            continue
+        r, r32, bub = v.get("TCC_EA0_RDREQ_sum", 0), v.get("TCC_EA0_RDREQ_32B_sum", 0), v.get("TCC_BUBBLE_sum", 0)
+        w, w64 = v.get("TCC_EA0_WRREQ_sum", 0), v.get("TCC_EA0_WRREQ_64B_sum", 0)
+        lines.append("| %s | %.0f | %.0f | %.0f | %.1f | %.0f | %.0f | %.1f |" % (
+            key, r, r32, bub, r * 128 / 1e6, w, w64, w * 64 / 1e6))
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -366,6 +410,13 @@ def main(argv=None):
     t.add_argument("--title", default="")
     t.add_argument("--command", action="append", default=[],
                    help="a profiling command to record in the markdown (repeatable)")
+    q = sub.add_parser("reqsize")
+    q.add_argument("--pmc", nargs="+", required=True, help="counter run directories of the path")
+    q.add_argument("--copy", nargs="+", required=True, help="counter run directories of the copy kernel")
+    q.add_argument("--copy-bytes", type=int, required=True)
+    q.add_argument("--md", required=True)
+    q.add_argument("--title", default="")
+    q.add_argument("--command", action="append", default=[])
     m = sub.add_parser("mlp")
     m.add_argument("--pmc", required=True, help="counter run directory (counter and agent CSVs)")
     m.add_argument("--md", required=True)
@@ -378,7 +429,12 @@ def main(argv=None):
     def csv_in(p, kind):
         return p if os.path.isfile(p) else _one(os.path.join(p, "**", "*%s.csv" % kind))
 
-    if a.cmd == "mlp":
+    if a.cmd == "reqsize":
+        res, cp = request_sizes([csv_in(p, "counter_collection") for p in a.pmc],
+                                [csv_in(p, "counter_collection") for p in a.copy])
+        with open(a.md, "w") as f:
+            f.write(request_md(res, cp, a.copy_bytes, a.title, a.command, here))
+    elif a.cmd == "mlp":
         cus, xcds, spc = agent_counts(csv_in(a.pmc, "agent_info"))
         res = mlp(csv_in(a.pmc, "counter_collection"), cus, xcds, spc)
         with open(a.md, "w") as f:

@@ -32,6 +32,7 @@ def test_kernel_keys():
     assert k("ssd::chain_clear_kernel(int*, long)") == "fwd_chained"
     assert k("void ssd::bwd_dc_bf16_kernel<64, 128>(x)") == "bwd_dc"
     assert k("void ssd::bwd_dcb_bf16_kernel<64>(x)") == "bwd_dcb"
+    assert k("void ssd::bwd_dbc_bf16_kernel<64, 128>(x)") == "bwd_dbc"
     assert k("void ssd::bwd_reduce_kernel(int)") == "bwd_finalize"
     assert k("void ssd::bmm_chunk_bf16_kernel<128, true>(x)") == "bmm_chunk"
     assert k("void ssd::bmm_chunk_bf16_kernel<128, false>(x)") == "bmm_chunk_cb_only"
@@ -114,3 +115,23 @@ def test_kernels_table_keeps_forms_apart(tmp_path):
     assert len(lines) == 2 and not any("bwd_dx" in l for l in text.splitlines())
     assert "| 1 | 1 | 4.0 |" in [l for l in lines if "state_passing_kernel<" in l][0]
     assert "| 2 | 2 | 3.1 |" in [l for l in lines if "seq_kernel" in l][0]
+
+
+def test_request_sizes(tmp_path):
+    # two passes for the path, two for the copy; the finalize's two kernels make one launch
+    fin, red = "void ssd::bwd_finalize_kernel(x)", "void ssd::bwd_reduce_kernel(int)"
+    dx = "void ssd::bwd_dx_bf16_kernel<64, 128>(x)"
+    a = write(tmp_path / "a.csv", PMC_COLS, [
+        [1, dx, "TCC_EA0_RDREQ_sum", 1000], [1, dx, "TCC_EA0_RDREQ_32B_sum", 0],
+        [1, dx, "TCC_BUBBLE_sum", 0], [1, dx, "TCC_EA0_WRREQ_sum", 400],
+        [2, dx, "TCC_EA0_RDREQ_sum", 1200], [2, dx, "TCC_EA0_WRREQ_sum", 400],
+        [3, fin, "TCC_EA0_RDREQ_sum", 300], [4, red, "TCC_EA0_RDREQ_sum", 10]])
+    b = write(tmp_path / "b.csv", PMC_COLS, [[1, dx, "TCC_EA0_WRREQ_64B_sum", 400]])
+    ca = write(tmp_path / "ca.csv", PMC_COLS, [[1, "void ssd::copy_kernel(x)", "TCC_EA0_RDREQ_sum", 2048],
+                                               [1, "void ssd::copy_kernel(x)", "TCC_EA0_WRREQ_sum", 4096]])
+    res, cp = profiling.request_sizes([a, b], [ca])
+    assert res["bwd_dx"]["TCC_EA0_RDREQ_sum"] == 1100 and res["bwd_dx"]["TCC_EA0_WRREQ_64B_sum"] == 400
+    assert res["bwd_finalize"]["TCC_EA0_RDREQ_sum"] == 310
+    md = profiling.request_md(res, cp, 262144, "t", ["cmd"], "summary")
+    assert "2048 read requests (128.0 bytes each) and 4096 write requests (64.0 bytes each)" in md
+    assert "| bwd_dx | 1100 | 0 | 0 | 0.1 | 400 | 400 | 0.0 |" in md
