@@ -122,8 +122,16 @@ struct ChainIO {
 bool chained_supported(const Prob& p);
 hipError_t launch_fwd_chained(const Prob& p, const ChainIO& io, hipStream_t st);
 
-// which: 0 every chunk kernel; 1 dx, 2 dCB (or the fp32 r+R kernel), 3 dC, 4 dB
+// which: 0 every chunk kernel; 1 dx, 2 dCB (fp32: dCB, then the r + R rows), 3 dC, 4 dB
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st);
+// The fp32 path (k_f32.hip): the same stages on the fp32 matrix cores; io must be fp32.
+hipError_t launch_chunk_state_f32(const Prob& p, const float* X, const float* Y, const float* delta,
+                                  const float* acs, float* out, int mode, hipStream_t st);
+hipError_t launch_bmm_chunk_f32(const Prob& p, const float* B, const float* C, float* CB, hipStream_t st);
+hipError_t launch_chunk_scan_f32(const Prob& p, const float* x, const float* C, const float* CB,
+                                 const float* delta, const float* acs, const float* passed,
+                                 const float* D, float* out, hipStream_t st);
+hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int which, hipStream_t st);
 // dB and dC, their dCB, r and whole R, K in one kernel (k_bwd_dbc.hip): R into
 // a.Rp and K into a.Kp, one value per (chunk, head, token); r into a.rR.
 bool bwd_fused_supported(const Prob& p);

@@ -93,33 +93,10 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
   }
 }
 
-__global__ __launch_bounds__(256) void bmm_chunk_f32_kernel(ChunkMap m, int G, int N,
-                                                            const float* __restrict__ Bm,
-                                                            const float* __restrict__ Cm,
-                                                            float* __restrict__ CB) {
-  const int k = blockIdx.x, g = blockIdx.y;
-  const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0) return;
-  const int Q = m.Q;
-  const int o = blockIdx.z * 256 + threadIdx.x;
-  const int i = o / Q, j = o % Q;
-  if (i >= ci.len || j > i) return;
-  const float* ci_ = Cm + ((int64_t)(ci.start + i) * G + g) * N;
-  const float* bj_ = Bm + ((int64_t)(ci.start + j) * G + g) * N;
-  float acc = 0.f;
-  for (int n = 0; n < N; ++n) acc += ci_[n] * bj_[n];
-  CB[(((int64_t)k * G + g) * Q + i) * Q + j] = acc;
-}
-
 hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st,
                             void* CBt) {
   if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) {
-    dim3 grid((unsigned)p.nck, p.G, (p.Q * p.Q + 255) / 256);
-    hipLaunchKernelGGL(bmm_chunk_f32_kernel, grid, dim3(256), 0, st, p.map, p.G, p.N,
-                       (const float*)B, (const float*)C, (float*)CB);
-    return hipGetLastError();
-  }
+  if (p.io == 0) return launch_bmm_chunk_f32(p, (const float*)B, (const float*)C, (float*)CB, st);
   dim3 grid((unsigned)p.nck, p.G);
 #define SSD_BMM_CASE(NN)                                                                   \
   if (p.N == NN) {                                                                         \

@@ -789,171 +789,6 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   for (int s = 0; s < N / 32; ++s) buf_store16(rdb, bo + 64 * s, pack_bf8(acc[2 * s], acc[2 * s + 1]));
 }
 
-// ------------------------------------------------------------ fp32 paths ----
-// One thread per row j: dx, direct d(delta), K+s; workgroup sums in fixed order.
-__global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
-    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
-    const float* __restrict__ Bm, const float* __restrict__ DY, const float* __restrict__ CB,
-    const float* __restrict__ delta, const float* __restrict__ acs,
-    const float* __restrict__ decay, const float* __restrict__ dE, const float* __restrict__ Hs,
-    const float* __restrict__ D, float* __restrict__ DX, float* __restrict__ ddd,
-    float* __restrict__ Ks, float* __restrict__ last_term, float* __restrict__ dDp) {
-  __shared__ float red[3][256];
-  const int k = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const ChunkInfo ci = chunk_info(m, k);
-  const int64_t kh = (int64_t)k * H + h;
-  if (ci.len <= 0) {
-    if (tid == 0) {
-      last_term[kh] = 0.f;
-      dDp[kh] = 0.f;
-    }
-    return;
-  }
-  const int Q = m.Q, len = ci.len, g = h / (H / G);
-  const float* ac = acs + kh * Q;
-  const float* dl = delta + kh * Q;
-  const float* dT = dE + kh * (int64_t)P * N;
-  const float* cbm = CB + ((int64_t)k * G + g) * Q * Q;
-  const float Dh = D ? D[h] : 0.f;
-  float s_part = 0.f, dxx_part = 0.f, dot = 0.f;
-  for (int e = tid; e < P * N; e += 256) dot += dT[e] * Hs[kh * (int64_t)P * N + e];
-  for (int j = tid; j < len; j += 256) {
-    const int64_t tj = ci.start + j;
-    const float wj = exp2_fast(ac[len - 1] - ac[j]);
-    float xs = 0.f, xt = 0.f, dxx = 0.f;
-    for (int p = 0; p < P; ++p) {
-      float st = 0.f;
-      for (int n = 0; n < N; ++n) st += Bm[(tj * G + g) * N + n] * dT[p * N + n];
-      st *= wj;
-      float in = 0.f;
-      for (int i = j; i < len; ++i)
-        in += cbm[(int64_t)i * Q + j] * exp2_fast(ac[i] - ac[j]) * DY[((ci.start + i) * (int64_t)H + h) * P + p];
-      const float xjp = X[(tj * H + h) * P + p], dyjp = DY[(tj * H + h) * P + p];
-      xs += xjp * st;
-      xt += xjp * (st + in);
-      dxx += xjp * dyjp;
-      DX[(tj * H + h) * P + p] = dl[j] * (st + in) + Dh * dyjp;
-    }
-    const float cbjj = cbm[(int64_t)j * Q + j];
-    ddd[kh * Q + j] = xt;
-    Ks[kh * Q + j] = dl[j] * (xt - dxx * cbjj);
-    s_part += dl[j] * xs;
-    dxx_part += dxx;
-  }
-  red[0][tid] = s_part;
-  red[1][tid] = dxx_part;
-  red[2][tid] = dot;
-  __syncthreads();
-  if (tid == 0) {
-    float S = 0.f, DD = 0.f, HD = 0.f;
-    for (int t = 0; t < 256; ++t) {
-      S += red[0][t];
-      DD += red[1][t];
-      HD += red[2][t];
-    }
-    last_term[kh] = S + exp2_fast(decay[kh]) * HD;
-    dDp[kh] = DD;
-  }
-}
-
-// One thread per (i, n) of a group: dC summed over the group's heads.
-__global__ __launch_bounds__(256) void bwd_dc_f32_kernel(
-    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
-    const float* __restrict__ Bm, const float* __restrict__ DY, const float* __restrict__ delta,
-    const float* __restrict__ acs, const float* __restrict__ Hs, float* __restrict__ dC) {
-  const int k = blockIdx.x, g = blockIdx.y;
-  const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0) return;
-  const int o = blockIdx.z * 256 + threadIdx.x;
-  const int i = o / N, n = o % N;
-  if (i >= ci.len) return;
-  const int Q = m.Q, hpg = H / G;
-  const int64_t ti = ci.start + i;
-  float acc = 0.f;
-  for (int hh = 0; hh < hpg; ++hh) {
-    const int h = g * hpg + hh;
-    const int64_t kh = (int64_t)k * H + h;
-    const float* ac = acs + kh * Q;
-    const float* dl = delta + kh * Q;
-    float st = 0.f;
-    for (int p = 0; p < P; ++p) st += DY[(ti * H + h) * P + p] * Hs[kh * (int64_t)P * N + (int64_t)p * N + n];
-    acc += exp2_fast(ac[i]) * st;
-    for (int j = 0; j <= i; ++j) {
-      const int64_t tj = ci.start + j;
-      float dxij = 0.f;
-      for (int p = 0; p < P; ++p) dxij += DY[(ti * H + h) * P + p] * X[(tj * H + h) * P + p];
-      acc += dxij * exp2_fast(ac[i] - ac[j]) * dl[j] * Bm[(tj * G + g) * N + n];
-    }
-  }
-  dC[(ti * G + g) * N + n] = acc;
-}
-
-// One thread per (i) of a head: r_i + R_i.
-__global__ __launch_bounds__(256) void bwd_rr_f32_kernel(
-    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
-    const float* __restrict__ Cm, const float* __restrict__ DY, const float* __restrict__ CB,
-    const float* __restrict__ delta, const float* __restrict__ acs, const float* __restrict__ Hs,
-    float* __restrict__ rR) {
-  const int k = blockIdx.x, h = blockIdx.y;
-  const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0) return;
-  const int i = blockIdx.z * 256 + threadIdx.x;
-  if (i >= ci.len) return;
-  const int Q = m.Q, g = h / (H / G);
-  const int64_t kh = (int64_t)k * H + h, ti = ci.start + i;
-  const float* ac = acs + kh * Q;
-  const float* dl = delta + kh * Q;
-  const float* cbm = CB + ((int64_t)k * G + g) * Q * Q;
-  float rv = 0.f;
-  for (int p = 0; p < P; ++p) {
-    float hc = 0.f;
-    for (int n = 0; n < N; ++n) hc += Hs[kh * (int64_t)P * N + (int64_t)p * N + n] * Cm[(ti * G + g) * N + n];
-    rv += DY[(ti * H + h) * P + p] * hc;
-  }
-  rv *= exp2_fast(ac[i]);
-  float Rv = 0.f;
-  for (int j = 0; j < i; ++j) {
-    const int64_t tj = ci.start + j;
-    float dxij = 0.f;
-    for (int p = 0; p < P; ++p) dxij += DY[(ti * H + h) * P + p] * X[(tj * H + h) * P + p];
-    Rv += dxij * cbm[(int64_t)i * Q + j] * exp2_fast(ac[i] - ac[j]) * dl[j];
-  }
-  rR[kh * Q + i] = rv + Rv;
-}
-
-// One thread per (j, n) of a group: dB summed over the group's heads.
-__global__ __launch_bounds__(256) void bwd_db_f32_kernel(
-    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
-    const float* __restrict__ Cm, const float* __restrict__ DY, const float* __restrict__ delta,
-    const float* __restrict__ acs, const float* __restrict__ dE, float* __restrict__ dB) {
-  const int k = blockIdx.x, g = blockIdx.y;
-  const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0) return;
-  const int o = blockIdx.z * 256 + threadIdx.x;
-  const int j = o / N, n = o % N;
-  const int len = ci.len;
-  if (j >= len) return;
-  const int Q = m.Q, hpg = H / G;
-  const int64_t tj = ci.start + j;
-  float acc = 0.f;
-  for (int hh = 0; hh < hpg; ++hh) {
-    const int h = g * hpg + hh;
-    const int64_t kh = (int64_t)k * H + h;
-    const float* ac = acs + kh * Q;
-    const float* dl = delta + kh * Q;
-    float st = 0.f;
-    for (int p = 0; p < P; ++p) st += X[(tj * H + h) * P + p] * dE[kh * (int64_t)P * N + (int64_t)p * N + n];
-    acc += exp2_fast(ac[len - 1] - ac[j]) * dl[j] * st;
-    for (int i = j; i < len; ++i) {
-      const int64_t ti = ci.start + i;
-      float dxij = 0.f;
-      for (int p = 0; p < P; ++p) dxij += DY[(ti * H + h) * P + p] * X[(tj * H + h) * P + p];
-      acc += dxij * exp2_fast(ac[i] - ac[j]) * dl[j] * Cm[(ti * G + g) * N + n];
-    }
-  }
-  dB[(tj * G + g) * N + n] = acc;
-}
-
 // ---------------------------------------------------------------- finalize ----
 // One workgroup per (chunk, 8 heads), one wavefront per head: dAcs_i = rR_i - Ks_i
 // + (R, K tile partials, or whole R, K per token: Rf, Kf) (+ last_term at the last
@@ -1141,26 +976,7 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStrea
 
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) {
-    if (!which || which == 1)
-    hipLaunchKernelGGL(bwd_dx_f32_kernel, dim3((unsigned)p.nck, p.H), dim3(256), 0, st, p.map, p.H,
-                       p.G, p.P, p.N, (const float*)a.x, (const float*)a.B, (const float*)a.dout,
-                       (const float*)a.CB, a.delta, a.acs, a.decay, (const float*)a.dE, (const float*)a.Hp, a.D, (float*)a.dx,
-                       a.ddd, a.Ks, a.last_term, a.dDp);
-    if (!which || which == 3)
-    hipLaunchKernelGGL(bwd_dc_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
-                       dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
-                       (const float*)a.B, (const float*)a.dout, a.delta, a.acs, (const float*)a.Hp, (float*)a.dC);
-    if (!which || which == 2)
-    hipLaunchKernelGGL(bwd_rr_f32_kernel, dim3((unsigned)p.nck, p.H, (p.Q + 255) / 256), dim3(256), 0,
-                       st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x, (const float*)a.C,
-                       (const float*)a.dout, (const float*)a.CB, a.delta, a.acs, (const float*)a.Hp, a.rR);
-    if (!which || which == 4)
-    hipLaunchKernelGGL(bwd_db_f32_kernel, dim3((unsigned)p.nck, p.G, (p.Q * p.N + 255) / 256),
-                       dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N, (const float*)a.x,
-                       (const float*)a.C, (const float*)a.dout, a.delta, a.acs, (const float*)a.dE, (float*)a.dB);
-    return hipGetLastError();
-  }
+  if (p.io == 0) return launch_bwd_f32(p, a, which, st);
 #define SSD_BWD_CASE(PP, NN) \
   if (p.P == PP && p.N == NN) { launch_bwd_bf16<PP, NN>(p, a, which, st); return hipGetLastError(); }
   SSD_BWD_CASE(32, 32) SSD_BWD_CASE(32, 64) SSD_BWD_CASE(32, 128)

@@ -33,7 +33,7 @@
 //   5. + D x_i and the bf16 store.
 // The x and H tiles are read once per workgroup and loaded nontemporally.
 //
-// fp32 path: one thread per (token, p), plain loops.
+// fp32 path: k_f32.hip.
 #include "internal.hpp"
 #include "scan_rows.hpp"
 
@@ -102,35 +102,6 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_bf16_kernel(
   rows.run();
 }
 
-__global__ __launch_bounds__(256) void chunk_scan_f32_kernel(
-    ChunkMap m, int H, int G, int P, int N, const float* __restrict__ X,
-    const float* __restrict__ Cm, const float* __restrict__ CB, const float* __restrict__ delta,
-    const float* __restrict__ acs, const float* __restrict__ Hs, const float* __restrict__ D,
-    float* __restrict__ Y) {
-  const int k = blockIdx.x, h = blockIdx.y;
-  const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0) return;
-  const int Q = m.Q;
-  const int o = blockIdx.z * 256 + threadIdx.x;
-  const int i = o / P, p = o % P;
-  if (i >= ci.len) return;
-  const int g = h / (H / G);
-  const int64_t kh = (int64_t)k * H + h;
-  const float* ac = acs + kh * Q;
-  const float* dl = delta + kh * Q;
-  const float* cbr = CB + (((int64_t)k * G + g) * Q + i) * Q;
-  const float ai = ac[i];
-  float acc = 0.f;
-  for (int j = 0; j <= i; ++j)
-    acc += cbr[j] * exp2_fast(ai - ac[j]) * dl[j] * X[((int64_t)(ci.start + j) * H + h) * P + p];
-  const float* crow = Cm + ((int64_t)(ci.start + i) * G + g) * N;
-  const float* hrow = Hs + kh * (int64_t)(P * N) + (int64_t)p * N;
-  float inter = 0.f;
-  for (int n = 0; n < N; ++n) inter += crow[n] * hrow[n];
-  const float xi = X[((int64_t)(ci.start + i) * H + h) * P + p];
-  Y[((int64_t)(ci.start + i) * H + h) * P + p] = acc + exp2_fast(ai) * inter + (D ? D[h] : 0.f) * xi;
-}
-
 template <int P, int N>
 static void launch_scan_bf16(const Prob& p, const void* x, const void* C, const void* CB,
                              const float* delta, const float* acs, const void* passed,
@@ -152,11 +123,8 @@ hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const 
   if (p.nck == 0) return hipSuccess;
   if (p.io == 0) {
     if (passed_bf16) return hipErrorInvalidValue;
-    dim3 grid((unsigned)p.nck, p.H, (p.Q * p.P + 255) / 256);
-    hipLaunchKernelGGL(chunk_scan_f32_kernel, grid, dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N,
-                       (const float*)x, (const float*)C, (const float*)CB, delta, acs, (const float*)passed, D,
-                       (float*)out);
-    return hipGetLastError();
+    return launch_chunk_scan_f32(p, (const float*)x, (const float*)C, (const float*)CB, delta, acs,
+                                 (const float*)passed, D, (float*)out, st);
   }
 #define SSD_SCAN_CASE(PP, NN) \
   if (p.P == PP && p.N == NN) { launch_scan_bf16<PP, NN>(p, x, C, CB, delta, acs, passed, passed_bf16, D, out, st); return hipGetLastError(); }

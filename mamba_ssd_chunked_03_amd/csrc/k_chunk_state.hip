@@ -36,8 +36,7 @@
 // chunk 256), pair ib forms row block ib, in both orientations (the backward
 // reads the transpose), and no separate C.B^T kernel runs.
 //
-// fp32 path: one thread per output element, plain FMA loop (correctness path
-// for fp32 inputs; no rounding of any operand).
+// fp32 path: k_f32.hip (fp32 matrix cores, no rounding of any operand).
 #include "internal.hpp"
 
 namespace ssd {
@@ -46,11 +45,6 @@ static_assert(sizeof(ChunkStateT) == 4 && (ChunkStateT)0.5f == 0.5f,
               "the chunk states and their adjoints are written here as fp32 (float4 stores)");
 
 constexpr int QMAX_STATE = 256;  // largest chunk size: one token per thread of a head
-
-__device__ __forceinline__ float token_scale(int mode, const float* dl, const float* ac, int j,
-                                             float a_last) {
-  return mode == kStateFwd ? dl[j] * exp2_fast(a_last - ac[j]) : exp2_fast(ac[j]);
-}
 
 // MODE (kStateFwd / kStateDstates) is a template argument so that profiles
 // tell the forward chunk states and the backward adjoint states apart.
@@ -294,34 +288,6 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
           make_float4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
 }
 
-// fp32: grid (chunk, head, output blocks of 256 elements)
-__global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H, int G, int P,
-                                                              int N, int mode,
-                                                              const float* __restrict__ X,
-                                                              const float* __restrict__ Y,
-                                                              const float* __restrict__ delta,
-                                                              const float* __restrict__ acs,
-                                                              float* __restrict__ out) {
-  const int k = blockIdx.x, h = blockIdx.y;
-  const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0) return;
-  const int o = blockIdx.z * 256 + threadIdx.x;
-  if (o >= P * N) return;
-  const int p = o / N, n = o % N;
-  const int g = h / (H / G);
-  const int Q = m.Q;
-  const int64_t kh = (int64_t)k * H + h;
-  const float* dl = delta + kh * Q;
-  const float* ac = acs + kh * Q;
-  const float a_last = ac[ci.len - 1];
-  float acc = 0.f;
-  for (int j = 0; j < ci.len; ++j) {
-    const int64_t t = ci.start + j;
-    acc += token_scale(mode, dl, ac, j, a_last) * X[(t * H + h) * P + p] * Y[(t * G + g) * N + n];
-  }
-  out[kh * (int64_t)(P * N) + o] = acc;
-}
-
 template <int P, int N, int HP>
 static void launch_cs_hp(const Prob& p, const void* X, const void* Y, float* delta, float* acs,
                          float* out, int mode, const CumsumIn& cs, hipStream_t st) {
@@ -372,12 +338,7 @@ static hipError_t launch_cs(const Prob& p, const void* X, const void* Y, float* 
 hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,
                               const float* acs, float* out, int mode, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) {
-    dim3 grid((unsigned)p.nck, p.H, (p.P * p.N + 255) / 256);
-    hipLaunchKernelGGL(chunk_state_f32_kernel, grid, dim3(256), 0, st, p.map, p.H, p.G, p.P, p.N,
-                       mode, (const float*)X, (const float*)Y, delta, acs, out);
-    return hipGetLastError();
-  }
+  if (p.io == 0) return launch_chunk_state_f32(p, (const float*)X, (const float*)Y, delta, acs, out, mode, st);
   if (p.Q > QMAX_STATE) return hipErrorInvalidValue;  // one token per thread
   // (the kStateFwd and kStateDstates modes only read delta and acs)
   return launch_cs(p, X, Y, const_cast<float*>(delta), const_cast<float*>(acs), out, mode, CumsumIn{}, st);

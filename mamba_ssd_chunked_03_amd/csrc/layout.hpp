@@ -7,7 +7,7 @@
 //   forward's carry)                                             ChunkStateT (fp32)
 //   passed states H and their adjoints dE                         io-sized (bf16 or fp32)
 //   delta, within-chunk cumsum, per-token backward pieces, tile partials   fp32
-//   C.B^T and its transpose, the head-summed dCB                  io-sized
+//   C.B^T and the head-summed dCB (both paths), C.B^T transposed (bf16)  io-sized
 #pragma once
 
 #include <cstddef>
@@ -67,7 +67,7 @@ inline BwdLayout bwd_layout(const LayoutDims& d) {
   const size_t cb = d.bf16 ? nck * (size_t)d.G * d.Q * d.Q * 2 : 0;
   const size_t tiles = d.bf16 ? nck * H * (size_t)(d.Q / 64) * d.Q * sizeof(TokenT) : 0;
   l.CBt = o;  o += lay_up(cb);
-  l.dCBg = o; o += lay_up(cb);
+  l.dCBg = o; o += lay_up(nck * (size_t)d.G * d.Q * d.Q * io_size(d));
   l.Rp = o;   o += lay_up(tiles);
   l.Kp = o;   o += lay_up(tiles);
   l.U = o;    o += lay_up(nck * H * st * sizeof(ChunkStateT));

@@ -71,7 +71,7 @@ int main() {
               std::vector<Reg> br = fr;
               br.insert(br.end(), {
                   {"C.B^T transposed", b.CBt, cb},
-                  {"head-summed dCB", b.dCBg, cb},
+                  {"head-summed dCB", b.dCBg, (size_t)nck * 8 * Q * Q * io},
                   {"R partials", b.Rp, tiles},
                   {"K partials", b.Kp, tiles},
                   // written by the adjoint-state kernel, read by the reverse scan: fp32 on both sides

@@ -71,6 +71,16 @@ CASES = [
                             io="f32", dt_mode="direct", init="none", seed=0), (64,)),
     ("f32_ragged", dict(batch=2, seqlen=150, nheads=2, headdim=16, dstate=32, ngroups=1,
                         io="f32", init="randn", seed=55, d_final=True), (64, 128)),
+    # the fp32 matrix-core kernels over several row blocks, output tiles and 64-row
+    # blocks of dCB, with a ragged last chunk and two or four heads per group
+    ("f32_p64n128", dict(batch=2, seqlen=600, nheads=4, headdim=64, dstate=128, ngroups=2,
+                         io="f32", init="randn", seed=59, d_final=True), (128, 256)),
+    ("f32_p128n64", dict(batch=1, seqlen=333, nheads=2, headdim=128, dstate=64, ngroups=1,
+                         io="f32", init="randn", seed=60), (256,)),
+    ("f32_p32n128", dict(batch=1, seqlen=290, nheads=8, headdim=32, dstate=128, ngroups=2,
+                         io="f32", init="zeros", seed=61, d_final=True), (64, 256)),
+    ("f32_p128n128", dict(batch=1, seqlen=200, nheads=2, headdim=128, dstate=128, ngroups=1,
+                          io="f32", init="randn", seed=62), (128,)),
 ]
 
 
@@ -84,11 +94,12 @@ def test_bwd_end_to_end(name, kw, qs):
         check(g, ref, kw["io"], "%s Q=%d" % (name, Q))
 
 
-@pytest.mark.parametrize("io,Q", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("io,Q", [("bf16", 128), ("f32", 64), ("f32_wide", 256)])
 def test_bwd_packed(io, Q):
-    lengths = [1, 0, 300, 513, 77] if io == "bf16" else [65, 0, 0, 64, 3]
-    kw = dict(nheads=4, headdim=64, dstate=128, ngroups=2) if io == "bf16" else \
-        dict(nheads=2, headdim=16, dstate=16, ngroups=1)
+    lengths = [65, 0, 0, 64, 3] if io == "f32" else [1, 0, 300, 513, 77]
+    kw = dict(nheads=2, headdim=16, dstate=16, ngroups=1) if io == "f32" else \
+        dict(nheads=4, headdim=64, dstate=128, ngroups=2)
+    io = "f32" if io.startswith("f32") else io
     inp = inputs.make_inputs(batch=1, seqlen=sum(lengths), lengths=lengths, io=io, init="randn",
                              bwd=True, d_final=True, seed=56, **kw)
     ref = oracle_bwd(inp)

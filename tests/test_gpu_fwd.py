@@ -44,12 +44,22 @@ CASES = [
                         io="f32", init="randn", seed=15), (64, 128)),
     ("f32_p128", dict(batch=1, seqlen=70, nheads=2, headdim=128, dstate=128, ngroups=2,
                       io="f32", init="randn", seed=16), (64,)),
+    # the fp32 matrix-core kernels over several row blocks and output tiles, with a
+    # ragged last chunk, at every headdim and dstate above 16, two and four heads per group
+    ("f32_p64n128", dict(batch=2, seqlen=600, nheads=4, headdim=64, dstate=128, ngroups=2,
+                         io="f32", init="randn", seed=18), (128, 256)),
+    ("f32_p128n64", dict(batch=1, seqlen=333, nheads=2, headdim=128, dstate=64, ngroups=1,
+                         io="f32", init="randn", seed=19), (256,)),
+    ("f32_p32n128", dict(batch=1, seqlen=290, nheads=8, headdim=32, dstate=128, ngroups=2,
+                         io="f32", init="zeros", seed=20), (64, 256)),
 ]
 PACKED = [
     ("packed_bf16", dict(nheads=4, headdim=64, dstate=128, ngroups=2, io="bf16", init="randn",
                          seed=21), [1, 0, 300, 513, 77], (128, 256)),
     ("packed_f32", dict(nheads=2, headdim=16, dstate=16, ngroups=1, io="f32", init="randn",
                         seed=22), [65, 0, 0, 64, 3], (64,)),
+    ("packed_f32_p64", dict(nheads=4, headdim=64, dstate=64, ngroups=2, io="f32", init="randn",
+                            seed=23), [1, 0, 300, 257, 77], (128, 256)),
 ]
 
 
