@@ -25,8 +25,9 @@
 //                                     16-row blocks, the waves in snake order
 //   bwd_dx        (chunk, head)       dx, direct d(delta), K_j + s_j, dD and
 //                                     alpha <dE, H> + sum s per chunk
-//   bwd_dcb       (chunk, group, 64 rows)   head-summed dCB_g, zero above the diagonal
-//   bwd_dc/db     (chunk, group, 64 rows)   dC, dB
+//   bwd_dcb       (chunk, group, causal 64x64 tile)   head-summed dCB_g, zero above
+//                                     the diagonal
+//   bwd_dc/db     (chunk, group, 16 rows)   dC, dB; the waves split dstate
 // Every sum over heads, lanes and waves has a fixed order: results are bitwise
 // reproducible.
 #include "internal.hpp"
@@ -415,72 +416,81 @@ __global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
 
 // -------------------------------------------------------------- bwd dCB_g ----
 // dCB_g[i][j] = sum_h (dy_i . x_j) 2^(acs_i - acs_j) delta_j for j <= i < len, zero
-// elsewhere in the tiles it writes: every 16 x 64 piece (rows i of wave w, column
-// group jg <= the row block's) of the (chunk, group)'s rows, so that dC and dB
-// read no unwritten value.  A = dy_i (16-byte loads along headdim), B = x_j
-// (16-byte loads along headdim); heads summed in order.
+// elsewhere in the tiles it writes.  One workgroup per (chunk, group, causal 64 x 64
+// tile (ti, tj <= ti)), wave w its rows 16w .. 16w + 15: every tile that dC and dB
+// read is written whole, so they read no unwritten value.  A = dy_i (16-byte loads
+// along headdim), B = x_j (16-byte loads along headdim); heads summed in order.
 __global__ __launch_bounds__(256) void bwd_dcb_f32_kernel(ChunkMap m, int H, int G, int P,
                                                           const float* __restrict__ X,
                                                           const float* __restrict__ DY,
                                                           const float* __restrict__ delta,
                                                           const float* __restrict__ acs,
                                                           float* __restrict__ dCBg) {
-  const int Q = m.Q, T = Q / 64;
-  const int lid = xcd_order(blockIdx.x, gridDim.x);
-  const int ti = lid % T, g = (lid / T) % G, k = lid / T / G;
+  const int Q = m.Q, T = Q / 64, NT = T * (T + 1) / 2;
+  const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
+  const int tile = lid % NT, g = (lid / NT) % G, k = lid / NT / G;
+  int ti = 0;
+  while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+  const int tj = tile - ti * (ti + 1) / 2;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
   const int len = ci.len, hpg = H / G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
-  const int i0 = ti * 64 + 16 * w, ir = i0 + r;
+  const int i0 = ti * 64 + 16 * w, ir = i0 + r, jb = tj * 64;
   const uint32_t xrow = (uint32_t)(H * P) * 4u;
-  float* ob = dCBg + ((int64_t)k * G + g) * Q * Q;
-  for (int jg = 0; jg <= ti; ++jg) {
-    f32x4 sum[4];
+  f32x4 sum[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int hh = 0; hh < hpg && i0 < len; ++hh) {
-      const int h = g * hpg + hh;
-      const int64_t kh = (int64_t)k * H + h, xb = (int64_t)ci.start * H * P + (int64_t)h * P;
-      const brsrc rdy = make_rsrc(DY + xb, (uint32_t)len * xrow), rx = make_rsrc(X + xb, (uint32_t)len * xrow);
-      f32x4 acc[4];
+  for (int u = 0; u < 4; ++u) sum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < hpg && i0 < len; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h, xb = (int64_t)ci.start * H * P + (int64_t)h * P;
+    const brsrc rdy = make_rsrc(DY + xb, (uint32_t)len * xrow), rx = make_rsrc(X + xb, (uint32_t)len * xrow);
+    f32x4 acc[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int p0 = 0; p0 < P; p0 += 16) {
-        const f32x4 dv = ld4(rdy, (uint32_t)ir * xrow + (uint32_t)(p0 + 4 * q) * 4u);
-        f32x4 xv[4];
+    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < P; p0 += 16) {
+      const f32x4 dv = ld4(rdy, (uint32_t)ir * xrow + (uint32_t)(p0 + 4 * q) * 4u);
+      f32x4 xv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) xv[u] = ld4(rx, (uint32_t)(jg * 64 + u * 16 + r) * xrow + (uint32_t)(p0 + 4 * q) * 4u);
+      for (int u = 0; u < 4; ++u) xv[u] = ld4(rx, (uint32_t)(jb + u * 16 + r) * xrow + (uint32_t)(p0 + 4 * q) * 4u);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) acc[u] = mfma_f32(dv[s], xv[u][s], acc[u]);
-      }
-      float ai[4], aj[4], dj[4];
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_f32(dv[s], xv[u][s], acc[u]);
+    }
+    float ai[4], aj[4], dj[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ai[e] = acs[kh * Q + i0 + 4 * q + e];
+    for (int e = 0; e < 4; ++e) ai[e] = acs[kh * Q + i0 + 4 * q + e];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        aj[u] = acs[kh * Q + jg * 64 + u * 16 + r];
-        dj[u] = delta[kh * Q + jg * 64 + u * 16 + r];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + 4 * q + e, j = jg * 64 + u * 16 + r;
-          const float v = acc[u][e] * exp2_fast(ai[e] - aj[u]) * dj[u];
-          sum[u][e] += (j <= i && i < len) ? v : 0.f;
-        }
+    for (int u = 0; u < 4; ++u) {
+      aj[u] = acs[kh * Q + jb + u * 16 + r];
+      dj[u] = delta[kh * Q + jb + u * 16 + r];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ob[(int64_t)(i0 + 4 * q + e) * Q + jg * 64 + u * 16 + r] = sum[u][e];
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 4 * q + e, j = jb + u * 16 + r;
+        const float v = acc[u][e] * exp2_fast(ai[e] - aj[u]) * dj[u];
+        sum[u][e] += (j <= i && i < len) ? v : 0.f;
+      }
   }
+  float* ob = dCBg + ((int64_t)k * G + g) * Q * Q;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ob[(int64_t)(i0 + 4 * q + e) * Q + jb + u * 16 + r] = sum[u][e];
 }
 
 // ------------------------------------------------------------ bwd dC, dB ----
+// One workgroup per (chunk, group, 16 rows); its waves split the dstate tiles
+// (wave w takes tiles w, w + WN, ...), so every wave shares the rows' A operand
+// (L1 hits) and the grid has a workgroup per 16 rows.
+template <int N>
+struct DstateSplit {
+  static constexpr int NT = N / 16, WN = NT < 4 ? NT : 4, NTW = NT / WN;
+};
+
 // dC_i = sum_{j<=i} dCB_g[i][j] B_j + sum_h 2^(acs_i) H_h^T dy_i
 //   (A = dCB_g row i, 16-byte loads along j, with B = B_j[n], 4-byte loads; then
 //   A = 2^(acs_i) dy_i, 16-byte loads along headdim, with B = H_h[p][n], 4-byte loads)
@@ -492,31 +502,32 @@ __global__ __launch_bounds__(256) void bwd_dc_f32_kernel(ChunkMap m, int H, int 
                                                          const float* __restrict__ acs,
                                                          const float* __restrict__ Hs,
                                                          float* __restrict__ dC) {
-  constexpr int NT = N / 16;
-  const int Q = m.Q, T = Q / 64;
-  const int lid = xcd_order(blockIdx.x, gridDim.x);
-  const int ti = lid % T, g = (lid / T) % G, k = lid / T / G;
+  using S = DstateSplit<N>;
+  const int Q = m.Q, NB = Q / 16;
+  const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, 16-row block), block fastest
+  const int rb = lid % NB, g = (lid / NB) % G, k = lid / NB / G;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
   const int len = ci.len, hpg = H / G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
-  const int i0 = ti * 64 + 16 * w, ir = i0 + r;
-  if (i0 >= len) return;
+  const int i0 = rb * 16, ir = i0 + r;
+  if (i0 >= len || w >= S::WN) return;
   const uint32_t xrow = (uint32_t)(H * P) * 4u, brow = (uint32_t)(G * N) * 4u, qrow = (uint32_t)Q * 4u;
   const int64_t bbase = (int64_t)ci.start * G * N + (int64_t)g * N;
-  const brsrc rb = make_rsrc(Bm + bbase, (uint32_t)len * brow), ro = make_rsrc(dC + bbase, (uint32_t)len * brow);
+  const brsrc rb_ = make_rsrc(Bm + bbase, (uint32_t)len * brow), ro = make_rsrc(dC + bbase, (uint32_t)len * brow);
   const brsrc rcb = make_rsrc(dCBg + ((int64_t)k * G + g) * Q * Q, (uint32_t)Q * qrow);
-  f32x4 acc[NT];
+  f32x4 acc[S::NTW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < S::NTW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 <= i0; j0 += 16) {
     const f32x4 cv = ld4(rcb, (uint32_t)ir * qrow + (uint32_t)(j0 + 4 * q) * 4u);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = mfma_f32(cv[s], buf_load_f32(rb, (uint32_t)(j0 + 4 * q + s) * brow + (uint32_t)(nt * 16 + r) * 4u),
-                           acc[nt]);
+      for (int u = 0; u < S::NTW; ++u)
+        acc[u] = mfma_f32(
+            cv[s], buf_load_f32(rb_, (uint32_t)(j0 + 4 * q + s) * brow + (uint32_t)((w + S::WN * u) * 16 + r) * 4u),
+            acc[u]);
   }
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
@@ -529,15 +540,16 @@ __global__ __launch_bounds__(256) void bwd_dc_f32_kernel(ChunkMap m, int H, int 
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[nt] = mfma_f32(dv[s], buf_load_f32(rh, (uint32_t)((p0 + 4 * q + s) * N + nt * 16 + r) * 4u), acc[nt]);
+        for (int u = 0; u < S::NTW; ++u)
+          acc[u] = mfma_f32(dv[s], buf_load_f32(rh, (uint32_t)((p0 + 4 * q + s) * N + (w + S::WN * u) * 16 + r) * 4u),
+                            acc[u]);
     }
   }
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int u = 0; u < S::NTW; ++u)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      st1(ro, (uint32_t)(i0 + 4 * q + e) * brow + (uint32_t)(nt * 16 + r) * 4u, acc[nt][e]);
+      st1(ro, (uint32_t)(i0 + 4 * q + e) * brow + (uint32_t)((w + S::WN * u) * 16 + r) * 4u, acc[u][e]);
 }
 
 // dB_j = sum_{i>=j} dCB_g[i][j] C_i + sum_h w_j delta_j dE_h^T x_j
@@ -552,23 +564,23 @@ __global__ __launch_bounds__(256) void bwd_db_f32_kernel(ChunkMap m, int H, int 
                                                          const float* __restrict__ acs,
                                                          const float* __restrict__ dE,
                                                          float* __restrict__ dB) {
-  constexpr int NT = N / 16;
-  const int Q = m.Q, T = Q / 64;
+  using S = DstateSplit<N>;
+  const int Q = m.Q, NB = Q / 16;
   const int lid = xcd_order(blockIdx.x, gridDim.x);
-  const int tj = lid % T, g = (lid / T) % G, k = lid / T / G;
+  const int rb = lid % NB, g = (lid / NB) % G, k = lid / NB / G;
   const ChunkInfo ci = chunk_info(m, k);
   if (ci.len <= 0) return;
   const int len = ci.len, hpg = H / G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
-  const int j0 = tj * 64 + 16 * w, jr = j0 + r;
-  if (j0 >= len) return;
+  const int j0 = rb * 16, jr = j0 + r;
+  if (j0 >= len || w >= S::WN) return;
   const uint32_t xrow = (uint32_t)(H * P) * 4u, crow = (uint32_t)(G * N) * 4u, qrow = (uint32_t)Q * 4u;
   const int64_t cbase = (int64_t)ci.start * G * N + (int64_t)g * N;
   const brsrc rc = make_rsrc(Cm + cbase, (uint32_t)len * crow), ro = make_rsrc(dB + cbase, (uint32_t)len * crow);
   const brsrc rcb = make_rsrc(dCBg + ((int64_t)k * G + g) * Q * Q, (uint32_t)Q * qrow);
-  f32x4 acc[NT];
+  f32x4 acc[S::NTW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < S::NTW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int i0 = j0; i0 < len; i0 += 16) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -576,8 +588,8 @@ __global__ __launch_bounds__(256) void bwd_db_f32_kernel(ChunkMap m, int H, int 
       const float v = buf_load_f32(rcb, (uint32_t)i * qrow + (uint32_t)jr * 4u);
       const float a = i < len ? v : 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = mfma_f32(a, buf_load_f32(rc, (uint32_t)i * crow + (uint32_t)(nt * 16 + r) * 4u), acc[nt]);
+      for (int u = 0; u < S::NTW; ++u)
+        acc[u] = mfma_f32(a, buf_load_f32(rc, (uint32_t)i * crow + (uint32_t)((w + S::WN * u) * 16 + r) * 4u), acc[u]);
     }
   }
   for (int hh = 0; hh < hpg; ++hh) {
@@ -591,15 +603,16 @@ __global__ __launch_bounds__(256) void bwd_db_f32_kernel(ChunkMap m, int H, int 
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[nt] = mfma_f32(xv[s], buf_load_f32(rde, (uint32_t)((p0 + 4 * q + s) * N + nt * 16 + r) * 4u), acc[nt]);
+        for (int u = 0; u < S::NTW; ++u)
+          acc[u] = mfma_f32(xv[s], buf_load_f32(rde, (uint32_t)((p0 + 4 * q + s) * N + (w + S::WN * u) * 16 + r) * 4u),
+                            acc[u]);
     }
   }
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int u = 0; u < S::NTW; ++u)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      st1(ro, (uint32_t)(j0 + 4 * q + e) * crow + (uint32_t)(nt * 16 + r) * 4u, acc[nt][e]);
+      st1(ro, (uint32_t)(j0 + 4 * q + e) * crow + (uint32_t)((w + S::WN * u) * 16 + r) * 4u, acc[u][e]);
 }
 
 // -------------------------------------------------------------- launchers ----
@@ -645,7 +658,9 @@ hipError_t launch_chunk_scan_f32(const Prob& p, const float* x, const float* C, 
 
 // which: 0 every kernel; 1 dx; 2 the head-summed dCB and the r + R rows; 3 dC; 4 dB
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
-  const dim3 heads((unsigned)(p.nck * p.H)), rows((unsigned)(p.nck * p.G * (p.Q / 64))), block(256);
+  const int T = p.Q / 64;
+  const dim3 heads((unsigned)(p.nck * p.H)), tiles((unsigned)(p.nck * p.G * (T * (T + 1) / 2)));
+  const dim3 rows((unsigned)(p.nck * p.G * (p.Q / 16))), block(256);
   const float *x = (const float*)a.x, *B = (const float*)a.B, *C = (const float*)a.C, *dy = (const float*)a.dout;
   const float *CB = (const float*)a.CB, *Hp = (const float*)a.Hp, *dE = (const float*)a.dE;
   float* dCBg = (float*)a.dCBg;
@@ -662,7 +677,7 @@ hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int which, hipStream_
     if (!ok) return hipErrorInvalidValue;
   }
   if (!which || which == 2) {
-    hipLaunchKernelGGL(bwd_dcb_f32_kernel, rows, block, 0, st, p.map, p.H, p.G, p.P, x, dy, a.delta, a.acs, dCBg);
+    hipLaunchKernelGGL(bwd_dcb_f32_kernel, tiles, block, 0, st, p.map, p.H, p.G, p.P, x, dy, a.delta, a.acs, dCBg);
     ok = false;
 #define SSD_RR32(PP)                                                                                    \
   if (p.P == PP) {                                                                                      \

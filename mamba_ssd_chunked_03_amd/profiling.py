@@ -55,6 +55,10 @@ KERNEL_FILES = {
     "bmm_chunk_cb_only": "k_bmm.hip",  # C.B^T without its transpose (a forward that keeps nothing)
     "gated_rmsnorm_fwd": "k_norm.hip", "gated_rmsnorm_bwd": "k_norm.hip",  # the layer's norm
     "fwd_chained": "k_fwd_chained.hip",  # the fused chained forward (its clear and empty-final kernels too)
+    # the fp32 path's kernels, under their own names
+    "chunk_state_f32": "k_f32.hip", "bmm_chunk_f32": "k_f32.hip", "scan_rows_f32": "k_f32.hip",
+    "bwd_dx_f32": "k_f32.hip", "bwd_dcb_f32": "k_f32.hip", "bwd_dc_f32": "k_f32.hip",
+    "bwd_db_f32": "k_f32.hip",
 }
 # headers whose code is compiled into every kernel
 SHARED_HEADERS = ("common.hpp", "internal.hpp", "layout.hpp", "scan_rows.hpp")
@@ -78,6 +82,8 @@ def kernel_key(name):
     targs = re.search(r"<([^>]*)>", name)
     targ = [t.strip() for t in targs.group(1).split(",")] if targs else []
     last = targ[-1] if targ else ""
+    if base.endswith("_f32_kernel"):  # the fp32 path: chunk_state_f32, scan_rows_f32, bwd_dx_f32, ...
+        return base[:-len("_kernel")]
     if base.startswith("chunk_state"):
         # chunk_state_bf16_kernel<P, N, MODE, heads per workgroup>: MODE 1 is the backward's dstates
         return "dstates" if len(targ) >= 3 and targ[2] == "1" else "chunk_state"

@@ -39,6 +39,11 @@ def test_kernel_keys():
     assert k("void ssd::gated_rmsnorm_bwd_kernel<true>(x)") == "gated_rmsnorm_bwd"
     assert k("void ssd::norm_dw_reduce_kernel(int)") == "gated_rmsnorm_bwd"
     assert k("void ssd::gated_rmsnorm_fwd_kernel<false>(x)") == "gated_rmsnorm_fwd"
+    assert k("void ssd::chunk_state_f32_kernel<64, 128>(ssd::ChunkMap)") == "chunk_state_f32"
+    assert k("void ssd::scan_rows_f32_kernel<64, true>(x)") == "scan_rows_f32"
+    assert k("void ssd::bwd_dcb_f32_kernel(ssd::ChunkMap)") == "bwd_dcb_f32"
+    assert k("void ssd::bwd_dc_f32_kernel<128>(x)") == "bwd_dc_f32"
+    assert all(key in profiling.KERNEL_FILES for key in ("chunk_state_f32", "scan_rows_f32", "bwd_dcb_f32"))
     assert k("void at::native::elementwise_kernel<4>(x)") is None
 
 
