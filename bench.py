@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "SSD layer tokens/s + ms/call (fwd, fwd+bwd) & % HBM peak, B=2 L=8192"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
+MFMA_F32_PEAK_TFLOPS = 157.3    # dense fp32 matrix
 FLUSH_BYTES = 512 << 20         # > the 256 MB last-level cache, read before each cold call
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -202,14 +203,16 @@ class Workload:
     """One named workload on the GPU: seeded inputs resident in HBM, workspaces,
     and the library calls marshalled once (the timed loops only issue them)."""
 
-    def __init__(self, cfg_id, dev, with_bwd=True):
+    def __init__(self, cfg_id, dev, with_bwd=True, inp=None, chunk=None):
         import ctypes
         import torch
         from mamba_ssd_chunked_03_amd import inputs, ssd
         self.cfg_id = cfg_id
-        cfg = inputs.CONFIGS[cfg_id]
-        self.Q = Q = cfg["chunk"]
-        inp = inputs.config_inputs(cfg_id)
+        if inp is None:  # a named workload, else the given inputs at the given chunk size
+            self.Q = Q = inputs.CONFIGS[cfg_id]["chunk"]
+            inp = inputs.config_inputs(cfg_id)
+        else:
+            self.Q = Q = chunk
         self.sha256 = input_sha256(inp)
         d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
         self.d = d
@@ -532,6 +535,34 @@ def other_workload(cfg_id, dev, tm, steps, label, ab=True):
     return res
 
 
+def fp32_layer(dev, tm, steps):
+    """The layer workload's shape with fp32 io, which runs the fp32 path (true fp32
+    products on the fp32 matrix cores): forward, and the training step (forward
+    keeping its intermediates, then backward), against the dense fp32 matrix peak.
+    Reported beside the headline, not as it."""
+    from mamba_ssd_chunked_03_amd import inputs
+    B, L, H, P, N, G, Q = 2, 8192, 64, 64, 128, 8, 256
+    w = Workload(None, dev, inp=inputs.make_inputs(B, L, H, P, N, G, io="f32", init="zeros", bwd=True, seed=5),
+                 chunk=Q)
+    per = max(1, steps // 4)
+    fl = kernel_flops(B, L, H, P, N, G, Q, w.chunks())
+    fwd_fl = fl["chunk_state"] + fl["bmm_chunk"] + fl["chunk_scan"]
+    bwd_fl = fl["dstates"] + fl["bwd_dx"] + fl["bwd_dcb"] + fl["bwd_dc"] + fl["bwd_db"]
+    res = {"workload": "fp32 io: batch %d, seqlen %d, %d heads, headdim %d, dstate %d, %d groups, chunk %d"
+                       % (B, L, H, P, N, G, Q), "input_sha256": w.sha256}
+    for name, fn, flops in (("fwd", w.fwd, fwd_fl), ("bwd", w.bwd_saved, bwd_fl), ("fwd_bwd", w.step, None)):
+        ms, ms_min, ms_max = tm.trials(fn, per)
+        r = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_max": round(ms_max, 4),
+             "tokens/s": round(B * L / (ms * 1e-3), 1)}
+        if flops:
+            tf = flops / (ms * 1e-3) / 1e12
+            r.update({"alg_tflops": round(tf, 1), "frac_mfma_f32": round(tf / MFMA_F32_PEAK_TFLOPS, 4)})
+        res[name] = r
+        print("bench: fp32 layer %s %.3f ms" % (name, ms), file=sys.stderr, flush=True)
+    del w
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -635,7 +666,8 @@ def main():
         del w
         torch.cuda.empty_cache()
         others = {"long_context": other_workload(3, dev, tm, args.steps, "long context", not args.no_ab),
-                  "packed": other_workload(4, dev, tm, args.steps, "packed sequences", not args.no_ab)}
+                  "packed": other_workload(4, dev, tm, args.steps, "packed sequences", not args.no_ab),
+                  "fp32_layer": fp32_layer(dev, tm, args.steps)}
     else:
         sha = w.sha256
 
