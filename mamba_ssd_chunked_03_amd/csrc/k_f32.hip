@@ -41,15 +41,56 @@ __device__ __forceinline__ void st1(brsrc rs, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
 }
 
+// V consecutive floats (V = 1, 2 or 4) in one load or store
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+template <int V>
+__device__ __forceinline__ void ldv(brsrc rs, uint32_t off, float (&o)[V]) {
+  if constexpr (V == 4) {
+    const f32x4 t = ld4(rs, off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = t[i];
+  } else if constexpr (V == 2) {
+    const u32x2v t = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    o[0] = __uint_as_float(t[0]);
+    o[1] = __uint_as_float(t[1]);
+  } else {
+    o[0] = buf_load_f32(rs, off);
+  }
+}
+template <int V>
+__device__ __forceinline__ void stv(brsrc rs, uint32_t off, const float (&o)[V]) {
+  if constexpr (V == 4) {
+    buf_store16(rs, off, u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])});
+  } else if constexpr (V == 2) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2v{__float_as_uint(o[0]), __float_as_uint(o[1])}, rs, off, 0, 0);
+  } else {
+    st1(rs, off, o[0]);
+  }
+}
+
+// Permuted output columns.  A row of W = 16 T values (T tiles of 16 columns) is
+// split into groups of V tiles (V = min(4, T)); tile c V + t of group c holds the
+// columns 16 V c + V r + t, r = 0..15.  Lane r of a row then owns V consecutive
+// columns, 16 V c + V r .. + V - 1, one per tile of the group: the operand that
+// runs along those columns is loaded, and the output stored, V values a lane.
+template <int T>
+struct ColGroups {
+  static constexpr int V = T < 4 ? T : 4, NG = T / V;
+  // first column of lane r in group c
+  static __device__ __forceinline__ int col0(int c, int r) { return 16 * V * c + V * r; }
+};
+
 }  // namespace
 
 // ------------------------------------------------------------ chunk states ----
 // out[p][n] = sum_j s_j X_j[p] Y_j[n] per (chunk, head):
 //   kStateFwd:     X = x, Y = B, s_j = delta_j 2^(acs_last - acs_j)  (T_c)
 //   kStateDstates: X = dy, Y = C, s_j = 2^(acs_j)                    (U_c)
-// Products D[n][p] (A = s_j Y_j[n], B = X_j[p]), so each lane ends with 4
-// consecutive n of one row p: 16-byte stores.  The waves split the output tiles
-// along p first (WP waves), then along n (WN).
+// Products D[n][p] (A = s_j Y_j[n], B = X_j[p]).  The waves split the output
+// tiles along p first (WP waves), then along n (WN), each taking a contiguous run
+// of tiles; inside a run the columns are permuted in groups (ColGroups), so each
+// token's Y and X values come 4 (or 2) to a load and a lane's outputs of one p
+// are consecutive n: vector stores.
 template <int P, int N>
 __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H, int G, int mode,
                                                               const float* __restrict__ X,
@@ -61,6 +102,8 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H,
   constexpr int WP = PT < 4 ? PT : 4;
   constexpr int WN = NT < 4 / WP ? NT : 4 / WP;
   constexpr int PTW = PT / WP, NTW = NT / WN;
+  using CP = ColGroups<PTW>;
+  using CN = ColGroups<NTW>;
   __shared__ float ss[256];
   int k, h;
   chunk_head(H, k, h);
@@ -79,6 +122,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H,
   __syncthreads();
   if (w >= WP * WN) return;
   const int wp = w % WP, wn = w / WP;
+  const int pb = wp * PTW * 16, nb = wn * NTW * 16;  // this wave's first p and n
   const uint32_t xrow = (uint32_t)(H * P) * 4u, yrow = (uint32_t)(G * N) * 4u;
   const brsrc rx = make_rsrc(X + (int64_t)ci.start * H * P + (int64_t)h * P, (uint32_t)len * xrow);
   const brsrc ry = make_rsrc(Y + (int64_t)ci.start * G * N + (int64_t)g * N, (uint32_t)len * yrow);
@@ -90,24 +134,33 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(ChunkMap m, int H,
   for (int j0 = 0; j0 < len; j0 += 4) {
     const int j = j0 + q;  // <= Q - 1: j0 < len <= Q, both multiples of 4
     const float s = ss[j];
-    float a[NTW], b[PTW];
+    float a[CN::NG][CN::V], b[CP::NG][CP::V];
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) a[u] = buf_load_f32(ry, (uint32_t)j * yrow + (uint32_t)(((wn + WN * u) * 16 + r) * 4)) * s;
+    for (int c = 0; c < CN::NG; ++c) ldv<CN::V>(ry, (uint32_t)j * yrow + (uint32_t)(nb + CN::col0(c, r)) * 4u, a[c]);
 #pragma unroll
-    for (int v = 0; v < PTW; ++v) b[v] = buf_load_f32(rx, (uint32_t)j * xrow + (uint32_t)(((wp + WP * v) * 16 + r) * 4));
+    for (int c = 0; c < CP::NG; ++c) ldv<CP::V>(rx, (uint32_t)j * xrow + (uint32_t)(pb + CP::col0(c, r)) * 4u, b[c]);
 #pragma unroll
     for (int u = 0; u < NTW; ++u)
 #pragma unroll
-      for (int v = 0; v < PTW; ++v) acc[u][v] = mfma_f32(a[u], b[v], acc[u][v]);
+      for (int v = 0; v < PTW; ++v)
+        acc[u][v] = mfma_f32(a[u / CN::V][u % CN::V] * s, b[v / CP::V][v % CP::V], acc[u][v]);
   }
+  // tile (u, v), element e: n = nb + 16 V c + V (4q + e) + t (u = c V + t), p = pb + col of lane r in v
   float* ob = out + kh * (int64_t)(P * N);
+  const brsrc ro = make_rsrc(ob, (uint32_t)(P * N) * 4u);
 #pragma unroll
-  for (int u = 0; u < NTW; ++u)
+  for (int v = 0; v < PTW; ++v) {
+    const int p = pb + CP::col0(v / CP::V, r) + v % CP::V;
 #pragma unroll
-    for (int v = 0; v < PTW; ++v) {
-      const int n0 = (wn + WN * u) * 16 + 4 * q, p = (wp + WP * v) * 16 + r;
-      *(f32x4*)(ob + p * N + n0) = acc[u][v];
-    }
+    for (int c = 0; c < CN::NG; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float o[CN::V];
+#pragma unroll
+        for (int t = 0; t < CN::V; ++t) o[t] = acc[c * CN::V + t][v][e];
+        stv<CN::V>(ro, (uint32_t)(p * N + nb + 16 * CN::V * c + CN::V * (4 * q + e)) * 4u, o);
+      }
+  }
 }
 
 // ------------------------------------------------------------------ C.B^T ----
@@ -164,7 +217,9 @@ __global__ __launch_bounds__(256) void bmm_chunk_f32_kernel(ChunkMap m, int G, i
 // the state term's r_i and R_i = sum_{j<i} (dy_i . x_j) CB_ij L_ij delta_j together.
 // Products D[i][p]: A = 2^(acs_i) C_i (16-byte loads along dstate) or the decayed
 // C.B^T row (16-byte loads along j), B = H_c[p] (16-byte loads along dstate) or
-// x_j[p] (4-byte loads along p).  Row blocks in snake order over the four waves.
+// x_j[p], whose headdim columns are permuted in groups (ColGroups): a lane loads
+// its x, dy and y values 16 bytes at a time.  Row blocks in snake order over the
+// four waves.
 template <int P, bool RR>
 __global__ __launch_bounds__(256) void scan_rows_f32_kernel(
     ChunkMap m, int H, int G, int N, const float* __restrict__ X, const float* __restrict__ Cm,
@@ -172,6 +227,8 @@ __global__ __launch_bounds__(256) void scan_rows_f32_kernel(
     const float* __restrict__ Hs, const float* __restrict__ D, float* __restrict__ Y,
     const float* __restrict__ DY, float* __restrict__ rR) {
   constexpr int PT = P / 16;
+  using CG = ColGroups<PT>;
+  constexpr int V = CG::V, NG = CG::NG;
   __shared__ float sa[256], sd[256];
   int k, h;
   chunk_head(H, k, h);
@@ -209,7 +266,8 @@ __global__ __launch_bounds__(256) void scan_rows_f32_kernel(
       const f32x4 cv = ld4(rc, (uint32_t)ir * crow + (uint32_t)(n0 + 4 * q) * 4u) * sc;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        const f32x4 hv = ld4(rh, (uint32_t)((pt * 16 + r) * N + n0 + 4 * q) * 4u);
+        const int p = CG::col0(pt / V, r) + pt % V;
+        const f32x4 hv = ld4(rh, (uint32_t)(p * N + n0 + 4 * q) * 4u);
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[pt] = mfma_f32(cv[s], hv[s], acc[pt]);
       }
@@ -228,19 +286,26 @@ __global__ __launch_bounds__(256) void scan_rows_f32_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-          acc[pt] = mfma_f32(mv[s], buf_load_f32(rx, (uint32_t)(j0 + 4 * q + s) * xrow + (uint32_t)(pt * 16 + r) * 4u),
-                             acc[pt]);
+        for (int c = 0; c < NG; ++c) {
+          float xv[V];
+          ldv<V>(rx, (uint32_t)(j0 + 4 * q + s) * xrow + (uint32_t)CG::col0(c, r) * 4u, xv);
+#pragma unroll
+          for (int t = 0; t < V; ++t) acc[c * V + t] = mfma_f32(mv[s], xv[t], acc[c * V + t]);
+        }
     }
-    // lane (r, q) holds rows i0 + 4q + e, column p = 16 pt + r
+    // lane (r, q) holds rows i0 + 4q + e, columns col0(c, r) + t of tile c V + t
     if constexpr (!RR) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t io = (uint32_t)(i0 + 4 * q + e) * xrow;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const uint32_t o = io + (uint32_t)(pt * 16 + r) * 4u;
-          st1(ry, o, acc[pt][e] + Dh * buf_load_f32(rx, o));
+        for (int c = 0; c < NG; ++c) {
+          const uint32_t o = io + (uint32_t)CG::col0(c, r) * 4u;
+          float xv[V], yv[V];
+          ldv<V>(rx, o, xv);
+#pragma unroll
+          for (int t = 0; t < V; ++t) yv[t] = acc[c * V + t][e] + Dh * xv[t];
+          stv<V>(ry, o, yv);
         }
       }
     } else {
@@ -250,11 +315,16 @@ __global__ __launch_bounds__(256) void scan_rows_f32_kernel(
         const uint32_t io = (uint32_t)i * xrow;
         float ya = 0.f, yx = 0.f;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const uint32_t o = io + (uint32_t)(pt * 16 + r) * 4u;
-          const float dyv = buf_load_f32(rdy, o);
-          ya += dyv * acc[pt][e];
-          yx += dyv * buf_load_f32(rx, o);
+        for (int c = 0; c < NG; ++c) {
+          const uint32_t o = io + (uint32_t)CG::col0(c, r) * 4u;
+          float dyv[V], xv[V];
+          ldv<V>(rdy, o, dyv);
+          ldv<V>(rx, o, xv);
+#pragma unroll
+          for (int t = 0; t < V; ++t) {
+            ya += dyv[t] * acc[c * V + t][e];
+            yx += dyv[t] * xv[t];
+          }
         }
         const float mii = i < len ? buf_load_f32(rcb, (uint32_t)i * qrow + (uint32_t)i * 4u) * sd[i] : 0.f;
         const float v = row_sum16(ya) - mii * row_sum16(yx);
@@ -268,7 +338,8 @@ __global__ __launch_bounds__(256) void scan_rows_f32_kernel(
 // Per (chunk, head) and 16-row block of tokens j, the bracket
 //   U_j[p] = w_j (dT B_j)[p] + sum_{i>=j} CB_ij 2^(acs_i - acs_j) dy_i[p],  w_j = 2^(acs_last - acs_j)
 // (A = w_j B_j, 16-byte loads along dstate, with B = dE_c[p], 16-byte loads; then
-// A = the decayed C.B^T column j, 4-byte loads along j, with B = dy_i[p]), and
+// A = the decayed C.B^T column j, 4-byte loads along j, with B = dy_i[p], headdim
+// columns permuted in groups as in the rows kernel above), and
 //   dx_j = delta_j U_j + D dy_j,  d(delta)_j direct = x_j . U_j,
 //   K_j + s_j = delta_j (x_j . U_j - (x_j . dy_j) CB_jj)   (s_j = delta_j x_j . w_j dT B_j),
 // dD's per-chunk part sum_j x_j . dy_j and alpha <dE, H> + sum_j s_j per chunk.
@@ -281,6 +352,8 @@ __global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
     float* __restrict__ ddd, float* __restrict__ Ks, float* __restrict__ last_term,
     float* __restrict__ dDp) {
   constexpr int PT = P / 16;
+  using CG = ColGroups<PT>;
+  constexpr int V = CG::V, NG = CG::NG;
   __shared__ float sa[256], sd[256];
   __shared__ float red[3][4];
   int k, h;
@@ -333,7 +406,8 @@ __global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
       const f32x4 bv = ld4(rb, (uint32_t)jr * brow + (uint32_t)(n0 + 4 * q) * 4u) * wj;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        const f32x4 ev = ld4(rde, (uint32_t)((pt * 16 + r) * N + n0 + 4 * q) * 4u);
+        const int p = CG::col0(pt / V, r) + pt % V;
+        const f32x4 ev = ld4(rde, (uint32_t)(p * N + n0 + 4 * q) * 4u);
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[pt] = mfma_f32(bv[s], ev[s], acc[pt]);
       }
@@ -345,7 +419,12 @@ __global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
       const uint32_t jo = (uint32_t)(j0 + 4 * q + e) * xrow;
       float v = 0.f;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) v += buf_load_f32(rx, jo + (uint32_t)(pt * 16 + r) * 4u) * acc[pt][e];
+      for (int c = 0; c < NG; ++c) {
+        float xv[V];
+        ldv<V>(rx, jo + (uint32_t)CG::col0(c, r) * 4u, xv);
+#pragma unroll
+        for (int t = 0; t < V; ++t) v += xv[t] * acc[c * V + t][e];
+      }
       xs[e] = v;
     }
     // later tokens of the chunk: i >= j
@@ -361,9 +440,12 @@ __global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-          acc[pt] = mfma_f32(mv[s], buf_load_f32(rdy, (uint32_t)(i0 + 4 * q + s) * xrow + (uint32_t)(pt * 16 + r) * 4u),
-                             acc[pt]);
+        for (int c = 0; c < NG; ++c) {
+          float yv[V];
+          ldv<V>(rdy, (uint32_t)(i0 + 4 * q + s) * xrow + (uint32_t)CG::col0(c, r) * 4u, yv);
+#pragma unroll
+          for (int t = 0; t < V; ++t) acc[c * V + t] = mfma_f32(mv[s], yv[t], acc[c * V + t]);
+        }
     }
     // dx, and the per-row dots
 #pragma unroll
@@ -373,12 +455,19 @@ __global__ __launch_bounds__(256) void bwd_dx_f32_kernel(
       const uint32_t jo = (uint32_t)j * xrow;
       float xt = 0.f, dxx = 0.f;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        const uint32_t o = jo + (uint32_t)(pt * 16 + r) * 4u;
-        const float xv = buf_load_f32(rx, o), yv = buf_load_f32(rdy, o);
-        xt += xv * acc[pt][e];
-        dxx += xv * yv;
-        st1(rdx, o, dj * acc[pt][e] + Dh * yv);
+      for (int c = 0; c < NG; ++c) {
+        const uint32_t o = jo + (uint32_t)CG::col0(c, r) * 4u;
+        float xv[V], yv[V], ov[V];
+        ldv<V>(rx, o, xv);
+        ldv<V>(rdy, o, yv);
+#pragma unroll
+        for (int t = 0; t < V; ++t) {
+          const float a = acc[c * V + t][e];
+          xt += xv[t] * a;
+          dxx += xv[t] * yv[t];
+          ov[t] = dj * a + Dh * yv[t];
+        }
+        stv<V>(rdx, o, ov);
       }
       xt = row_sum16(xt);
       dxx = row_sum16(dxx);
