@@ -492,3 +492,27 @@ def test_opt_in_forms_full_size(cfg):
             if g[k] is not None:
                 assert torch.equal(gv[k], g[k]), (cfg, v, k)
         del gv
+
+
+def test_fp32_layer_shape_full_group():
+    """The layer workload's shape with fp32 io (batch 2, seqlen 8192, 64 heads in 8
+    groups, the fp32 matrix-core path at full size): every head of group 3 on batch
+    row 1, forward (y, final states) and backward (including that group's dB and
+    dC), against the oracle on that row and those heads, at the fp32 gate."""
+    inp = inputs.make_inputs(2, 8192, 64, 64, 128, 8, io="f32", init="randn", bwd=True, seed=63)
+    y, final = gpu_fwd(ssd, inp, 256)
+    g = gpu_bwd(ssd, inp, 256)
+    torch.cuda.synchronize()
+    row, grp = 1, 3
+    heads = _group_heads(grp, 8)
+    one = batch_rows(inp, [row])
+    o = oracle_args(one)
+    y_ref, f_ref = recurrence.fwd(**o, heads=heads)
+    assert normwise(np64(y[row:row + 1, :, heads]), y_ref) <= 1e-4
+    assert normwise(np64(final[row:row + 1, heads]), f_ref) <= 1e-4
+    ref = dict(oracle_bwd(one, heads=heads))
+    got = {k: g[k][row:row + 1] for k in ("dx", "ddt", "dB", "dC", "d_init")}
+    got["dB"], got["dC"] = got["dB"][:, :, grp:grp + 1], got["dC"][:, :, grp:grp + 1]
+    ref["dB"], ref["dC"] = ref["dB"][:, :, grp:grp + 1], ref["dC"][:, :, grp:grp + 1]
+    check(got, ref, "f32", "fp32 layer shape row %d group %d" % (row, grp),
+          keys=["dx", "ddt", "dB", "dC", "d_init"], heads=heads)
