@@ -745,54 +745,39 @@ hipError_t launch_chunk_scan_f32(const Prob& p, const float* x, const float* C, 
   return hipErrorInvalidValue;
 }
 
-// which: 0 every kernel; 1 dx; 2 the head-summed dCB and the r + R rows; 3 dC; 4 dB
-hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
+template <int P, int N>
+static void launch_bwd_f32_pn(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
   const int T = p.Q / 64;
   const dim3 heads((unsigned)(p.nck * p.H)), tiles((unsigned)(p.nck * p.G * (T * (T + 1) / 2)));
   const dim3 rows((unsigned)(p.nck * p.G * (p.Q / 16))), block(256);
   const float *x = (const float*)a.x, *B = (const float*)a.B, *C = (const float*)a.C, *dy = (const float*)a.dout;
   const float *CB = (const float*)a.CB, *Hp = (const float*)a.Hp, *dE = (const float*)a.dE;
   float* dCBg = (float*)a.dCBg;
-  bool ok = false;
-  if (!which || which == 1) {
-#define SSD_DX32(PP)                                                                                      \
-  if (p.P == PP) {                                                                                        \
-    hipLaunchKernelGGL((bwd_dx_f32_kernel<PP>), heads, block, 0, st, p.map, p.H, p.G, p.N, x, B, dy, CB,  \
-                       a.delta, a.acs, a.decay, dE, Hp, a.D, (float*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp); \
-    ok = true;                                                                                            \
-  }
-    SSD_F32_P(SSD_DX32)
-#undef SSD_DX32
-    if (!ok) return hipErrorInvalidValue;
-  }
+  if (!which || which == 1)
+    hipLaunchKernelGGL((bwd_dx_f32_kernel<P>), heads, block, 0, st, p.map, p.H, p.G, N, x, B, dy, CB, a.delta,
+                       a.acs, a.decay, dE, Hp, a.D, (float*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
   if (!which || which == 2) {
-    hipLaunchKernelGGL(bwd_dcb_f32_kernel, tiles, block, 0, st, p.map, p.H, p.G, p.P, x, dy, a.delta, a.acs, dCBg);
-    ok = false;
-#define SSD_RR32(PP)                                                                                    \
-  if (p.P == PP) {                                                                                      \
-    hipLaunchKernelGGL((scan_rows_f32_kernel<PP, true>), heads, block, 0, st, p.map, p.H, p.G, p.N, x, C, \
-                       CB, a.delta, a.acs, Hp, nullptr, nullptr, dy, a.rR);                             \
-    ok = true;                                                                                          \
+    hipLaunchKernelGGL(bwd_dcb_f32_kernel, tiles, block, 0, st, p.map, p.H, p.G, P, x, dy, a.delta, a.acs, dCBg);
+    hipLaunchKernelGGL((scan_rows_f32_kernel<P, true>), heads, block, 0, st, p.map, p.H, p.G, N, x, C, CB, a.delta,
+                       a.acs, Hp, nullptr, nullptr, dy, a.rR);
   }
-    SSD_F32_P(SSD_RR32)
-#undef SSD_RR32
-    if (!ok) return hipErrorInvalidValue;
-  }
-  ok = false;
-#define SSD_DCDB32(NN)                                                                                   \
-  if (p.N == NN) {                                                                                       \
-    if (!which || which == 3)                                                                            \
-      hipLaunchKernelGGL((bwd_dc_f32_kernel<NN>), rows, block, 0, st, p.map, p.H, p.G, p.P, B, dy, dCBg, \
-                         a.acs, Hp, (float*)a.dC);                                                       \
-    if (!which || which == 4)                                                                            \
-      hipLaunchKernelGGL((bwd_db_f32_kernel<NN>), rows, block, 0, st, p.map, p.H, p.G, p.P, x, C, dCBg,  \
-                         a.delta, a.acs, dE, (float*)a.dB);                                              \
-    ok = true;                                                                                           \
-  }
-  SSD_F32_P(SSD_DCDB32)
-#undef SSD_DCDB32
-  if (!ok) return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (!which || which == 3)
+    hipLaunchKernelGGL((bwd_dc_f32_kernel<N>), rows, block, 0, st, p.map, p.H, p.G, P, B, dy, dCBg, a.acs, Hp,
+                       (float*)a.dC);
+  if (!which || which == 4)
+    hipLaunchKernelGGL((bwd_db_f32_kernel<N>), rows, block, 0, st, p.map, p.H, p.G, P, x, C, dCBg, a.delta, a.acs,
+                       dE, (float*)a.dB);
+}
+
+// which: 0 every kernel; 1 dx; 2 the head-summed dCB and the r + R rows; 3 dC; 4 dB
+hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
+#define SSD_BWD32(PP, NN) \
+  if (p.P == PP && p.N == NN) { launch_bwd_f32_pn<PP, NN>(p, a, which, st); return hipGetLastError(); }
+#define SSD_BWD32_N(PP) SSD_BWD32(PP, 16) SSD_BWD32(PP, 32) SSD_BWD32(PP, 64) SSD_BWD32(PP, 128)
+  SSD_F32_P(SSD_BWD32_N)
+#undef SSD_BWD32_N
+#undef SSD_BWD32
+  return hipErrorInvalidValue;
 }
 
 #undef SSD_F32_P
