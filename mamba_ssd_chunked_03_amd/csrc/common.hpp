@@ -358,18 +358,37 @@ __device__ __forceinline__ float wave_last(float v) {
 // the other: tiles that share operands (the row tiles of one chunk and group)
 // then find them in that XCD's L2 instead of fetching them again from HBM.
 constexpr int kNumXcd = 8;
-__device__ __forceinline__ int xcd_order(int L, int W) {
+__host__ __device__ __forceinline__ int xcd_order(int L, int W) {
   const int x = L % kNumXcd, s = L / kNumXcd;
   const int per = W / kNumXcd, rem = W % kNumXcd;
-  return x * per + min(x, rem) + s;
+  return x * per + (x < rem ? x : rem) + s;
+}
+
+// xcd_order, and inside each XCD's sequence of slots s = L / 8, every block of
+// 32 R slots laid out so that R consecutive logical ids take slots c, c + 32,
+// ..., c + 32 (R - 1).  An XCD has 32 compute units and hands its workgroups to
+// them in turn, so slots s and s + 32 tend to run on one unit at the same time:
+// R neighbouring ids (heads of one group) then meet in that unit's L1 cache,
+// where one's operand loads can hit the other's lines.  Only the speed depends
+// on this; every order covers each id once.
+constexpr int kCusPerXcd = 32;
+__host__ __device__ __forceinline__ int xcd_order_cu(int L, int W, int R) {
+  const int x = L % kNumXcd, s = L / kNumXcd;
+  const int per = W / kNumXcd, rem = W % kNumXcd;
+  const int blk = kCusPerXcd * R;
+  int sp = s;
+  if (s < (per / blk) * blk) sp = (s / blk) * blk + (s % kCusPerXcd) * R + (s % blk) / kCusPerXcd;
+  return x * per + (x < rem ? x : rem) + sp;
 }
 
 // (chunk slot, head) of a workgroup of a 1-D grid over nck x H slots: in the
-// XCD-aware order above, head fastest.  Each XCD then works through all heads
-// of one chunk together: a token's row of x (every head) is read whole, and a
-// group's B and C.B^T tiles stay in that XCD's L2 for the group's heads.
+// XCD-aware order above, head fastest, with pairs of neighbouring heads placed
+// to share a compute unit.  Each XCD then works through all heads of one chunk
+// together: a token's row of x (every head) is read whole, and a group's B and
+// C.B^T tiles stay in that XCD's L2 (and, for the pair on one unit, its L1) for
+// the group's heads.
 __device__ __forceinline__ void chunk_head(int H, int& k, int& h) {
-  const int l = xcd_order(blockIdx.x, gridDim.x);
+  const int l = xcd_order_cu(blockIdx.x, gridDim.x, 2);
   k = l / H;
   h = l % H;
 }
