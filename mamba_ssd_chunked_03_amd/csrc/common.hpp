@@ -368,9 +368,9 @@ __host__ __device__ __forceinline__ int xcd_order(int L, int W) {
 // 32 R slots laid out so that R consecutive logical ids take slots c, c + 32,
 // ..., c + 32 (R - 1).  An XCD has 32 compute units and hands its workgroups to
 // them in turn, so slots s and s + 32 tend to run on one unit at the same time:
-// R neighbouring ids (heads of one group) then meet in that unit's L1 cache,
-// where one's operand loads can hit the other's lines.  Only the speed depends
-// on this; every order covers each id once.
+// R neighbouring ids (heads of one group) then request the lines they share at
+// about the same moment.  Only the speed depends on this; every order covers
+// each id once.
 constexpr int kCusPerXcd = 32;
 __host__ __device__ __forceinline__ int xcd_order_cu(int L, int W, int R) {
   const int x = L % kNumXcd, s = L / kNumXcd;
@@ -385,8 +385,7 @@ __host__ __device__ __forceinline__ int xcd_order_cu(int L, int W, int R) {
 // XCD-aware order above, head fastest, with pairs of neighbouring heads placed
 // to share a compute unit.  Each XCD then works through all heads of one chunk
 // together: a token's row of x (every head) is read whole, and a group's B and
-// C.B^T tiles stay in that XCD's L2 (and, for the pair on one unit, its L1) for
-// the group's heads.
+// C.B^T tiles stay in that XCD's L2 for the group's heads.
 __device__ __forceinline__ void chunk_head(int H, int& k, int& h) {
   const int l = xcd_order_cu(blockIdx.x, gridDim.x, 2);
   k = l / H;
