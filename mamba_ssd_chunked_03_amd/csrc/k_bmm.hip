@@ -10,7 +10,7 @@
 // The backward also reads the transpose, CBt[j][i] = CB[i][j]: when asked, each
 // lower tile is stored a second time, transposed, from the same LDS copy.
 //
-// fp32 path: one thread per (i, j <= i), plain dot product.
+// fp32 path: k_f32.hip (fp32 matrix cores).
 #include "internal.hpp"
 
 namespace ssd {

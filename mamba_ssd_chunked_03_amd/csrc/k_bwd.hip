@@ -18,14 +18,14 @@
 // the dx accumulator.  R_i and K_j are built together from one set of M values
 // (they cancel exactly where the decay gradient subtracts them).
 //
-// Kernels (bf16 on MFMA; fp32 plain loops):
+// Kernels (bf16 MFMA; the fp32 path's counterparts are in k_f32.hip):
 //   bwd_dx   (chunk, head)            dx, direct d(delta), s_j, dD and
 //                                     alpha<dE,H> + sum s per chunk
 //   bwd_dcb  (chunk, group, 64x64 causal tile)  head-summed dCB_g; per-head
 //                                     tile partials of R, K
 //   bwd_dc   (chunk, group, 64 rows)  dC = dCB_g B + sum_h (state term); r_i
 //   bwd_db   (chunk, group, 64 rows)  dB = dCB_g^T C + sum_h (state term)
-//   finalize (chunk, head)        suffix sum of dAcs (DPP scan), d(delta)->ddt,
+//   finalize (chunk, 8 heads)     suffix sum of dAcs (DPP scan), d(delta)->ddt,
 //                                 per-chunk partials of dA and d_dt_bias
 //   reduce   (head)               fixed-order sums over chunks: dA, dD, d_dt_bias
 // Every reduction has a fixed order, so results are bitwise reproducible.
