@@ -54,7 +54,9 @@
  *    launch returns SSD_ERR_HIP.  Nothing is printed; no exception crosses the ABI.
  *  - Pointers must be 16-byte aligned.
  *  - Supported: io dtype f32 or bf16; headdim and dstate in {16, 32, 64, 128}
- *    (bf16 additionally needs headdim >= 32 and dstate >= 32);
+ *    (a bf16 problem with headdim or dstate 16 runs on the fp32 matrix-core
+ *    kernels: its bf16 tensors are widened to fp32 in registers, its
+ *    intermediates are fp32, and its outputs are rounded to bf16);
  *    chunk_size in {64, 128, 256}; nheads % ngroups == 0; chunk_size * nheads *
  *    headdim * 4 and chunk_size * ngroups * dstate * 4 at most 2^31 - 1 (one
  *    chunk's token rows are addressed with 32-bit byte offsets); any seqlen >= 0
@@ -134,7 +136,8 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   workgroup, C.B^T formed inside the chunk-state kernel.  2 needs an even number
  *   of heads per group (and, with dstate 32 or headdim 128 at dstate 128, is
  *   outside the kernel's shapes); 3 also needs chunk_size 256 and eight heads per
- *   group; a variant the problem cannot run, or 2 or 3 on the fp32 path, returns
+ *   group; a variant the problem cannot run, or 2 or 3 where the fp32 matrix-core
+ *   kernels run (fp32 io, or bf16 with headdim or dstate 16), returns
  *   SSD_ERR_UNSUPPORTED.  Results are bitwise the same for every variant. */
 #define SSD_FLAG_CS_VARIANT(v) ((v) << 20)
 /* SSD_FLAG_CHAINED_FWD: ssd_fwd runs the fused single-pass forward: after the
@@ -159,7 +162,8 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   measurement (it moves fewer bytes but runs one workgroup per compute unit, and
  *   is slower on MI355X): dB and dC are bitwise the same; ddt, dA and d_dt_bias
  *   agree to rounding (their decay-gradient sums are added in another order).  bf16
- *   io only; no effect on the fp32 path, which always runs its own kernels. */
+ *   io with headdim and dstate >= 32 only; no effect where the fp32 matrix-core
+ *   kernels run, which always form dB and dC their own way. */
 #define SSD_FLAG_BWD_FUSED 32
 /* SSD_FLAG_BWD_KERNEL(k), k = 1..7: a profiling aid, valid only together with
  *   SSD_FLAG_FROM_SAVED.  ssd_bwd launches only its k-th kernel: 1 adjoint chunk
@@ -235,8 +239,9 @@ int64_t ssd_num_chunks(const ssd_problem* problem, int32_t chunk_size, int32_t p
 /* Workspace sizes in bytes (0 for an invalid problem).  `packed` = 1 when
  * cu_seqlens will be passed.  The forward workspace holds the chunk table,
  * delta, the within-chunk cumsum, the chunk states (fp32), the passed states
- * (bf16 with bf16 io, where they only feed bf16 matrix products; fp32
- * otherwise) and C.B^T per chunk; the backward one adds the adjoint states. */
+ * (bf16 where the bf16 kernels run, which only feed them to bf16 matrix
+ * products; fp32 otherwise) and C.B^T per chunk; the backward one adds the
+ * adjoint states. */
 size_t ssd_fwd_workspace_bytes(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 size_t ssd_bwd_workspace_bytes(const ssd_problem* problem, int32_t chunk_size, int32_t packed);
 /* Workspace for the ssd_stage_* entries (the chunk table only). */

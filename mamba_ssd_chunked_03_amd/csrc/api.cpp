@@ -53,7 +53,6 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   if (pr->io_dtype != SSD_F32 && pr->io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
   if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
   if (!okdim(pr->headdim) || !okdim(pr->dstate)) return SSD_ERR_UNSUPPORTED;
-  if (pr->io_dtype == SSD_BF16 && (pr->headdim < 32 || pr->dstate < 32)) return SSD_ERR_UNSUPPORTED;
   const int64_t tokens = (int64_t)pr->batch * pr->seqlen;
   if (tokens > INT32_MAX / 2 || (int64_t)pr->nheads > 65535 || (int64_t)pr->ngroups > 65535)
     return SSD_ERR_UNSUPPORTED;
@@ -68,6 +67,8 @@ ssd_status make_prob(const ssd_problem* pr, int32_t Q, int packed, Prob& p) {
   p.N = pr->dstate;
   p.G = pr->ngroups;
   p.io = pr->io_dtype;
+  // bf16 io below the bf16 kernels' 32-wide operand tiles: the fp32 matrix-core kernels
+  p.wide = p.io == SSD_BF16 && (pr->headdim < 32 || pr->dstate < 32);
   p.softplus = pr->dt_softplus;
   p.Q = Q;
   p.packed = packed;
@@ -105,6 +106,7 @@ LayoutDims dims(const Prob& p) {
   d.nseq = p.nseq;
   d.packed = p.packed != 0;
   d.bf16 = p.io == SSD_BF16;
+  d.wide = p.wide != 0;
   return d;
 }
 FwdLayout fwd_layout(const Prob& p) { return ssd::fwd_layout(dims(p)); }
@@ -339,7 +341,7 @@ static ssd_status fwd_run(const ssd_problem* pr, const void* x, const float* dt,
   if (p.flags & SSD_FLAG_CHAINED_FWD) {
     // C.B^T (and its transpose for a saved context), then the fused chained kernel;
     // the carry buffer is the chunk-state slot, the flags the sync slot
-    void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
+    void* CBt = (save && bf16_kernels(p)) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
     if (p.nck > 0) SSD_TRY(launch_bmm_chunk(p, B, C, ws + l.CB, st, CBt));
     ChainIO io;
     io.x = x; io.B = B; io.C = C; io.CB = ws + l.CB;
@@ -359,9 +361,9 @@ static ssd_status fwd_run(const ssd_problem* pr, const void* x, const float* dt,
   float* decay = (float*)(ws + l.decay);
   float* T = (float*)(ws + l.T);
   void* Hp = ws + l.Hp;
-  const int hb = p.io == SSD_BF16;
+  const int hb = bf16_kernels(p);
   void* CB = ws + l.CB;
-  void* CBt = (save && p.io == SSD_BF16) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
+  void* CBt = (save && bf16_kernels(p)) ? (void*)(ws + bwd_layout(p).CBt) : nullptr;
   // Where the chunk-state kernel forms C.B^T itself (it stages every B slice of
   // the chunk already), the call is three kernels on `stream`.  Otherwise C.B^T,
   // which needs only B and C, runs on the side stream beside the cumsum and chunk
@@ -449,7 +451,7 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   float* decay = (float*)(ws + l.f.decay);
   float* T = (float*)(ws + l.f.T);
   void* Hp = ws + l.f.Hp;
-  const int hb = p.io == SSD_BF16;
+  const int hb = bf16_kernels(p);
   void* CB = ws + l.f.CB;
   void* CBt = ws + l.CBt;
   float* U = (float*)(ws + l.U);
@@ -459,7 +461,7 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
     SSD_TRY(launch_cumsum_chunk_state(p, x, B, dt, dt_bias, A, delta, acs, decay, T, st,
                                       cb_fused ? C : nullptr, CB, CBt));
     SSD_TRY(launch_state_passing(p, T, decay, init_states, Hp, hb, nullptr, 0, st));
-    if (!cb_fused) SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, p.io == SSD_BF16 ? CBt : nullptr));
+    if (!cb_fused) SSD_TRY(launch_bmm_chunk(p, B, C, CB, st, bf16_kernels(p) ? CBt : nullptr));
   }
   BwdArgs a;
   a.x = x; a.B = B; a.C = C; a.dout = dout;
@@ -485,7 +487,7 @@ ssd_status ssd_bwd(const ssd_problem* pr, const void* x, const float* dt, const 
   std::unique_lock<std::mutex> lane_lock;
   const bool one_stream = (p.flags & SSD_FLAG_ONE_STREAM) != 0;
   SideLane* side =
-      (!only && p.io == SSD_BF16 && p.nck > 0 && !one_stream) ? side_lane(st, lane_lock) : nullptr;
+      (!only && bf16_kernels(p) && p.nck > 0 && !one_stream) ? side_lane(st, lane_lock) : nullptr;
   // events: 0 fork, 1 reverse scan done, 2 what the finalize reads from the side
   // stream is done (dCB's partials and dC's r; or the one kernel), 3 dB done
   if (side && !fused) {

@@ -13,7 +13,9 @@ namespace ssd {
 struct Prob {
   int32_t B, L, H, P, N, G;
   int32_t nseq;      // number of state slots (batch rows, or packed sequences)
-  int32_t io;        // 0 fp32, 1 bf16
+  int32_t io;        // io tensors: 0 fp32, 1 bf16
+  int32_t wide;      // 1: bf16 io with headdim or dstate 16, run by the fp32 matrix-core
+                     // kernels (bf16 tensors widened to fp32 in registers)
   int32_t softplus;  // delta = softplus(dt + bias)
   int32_t Q;         // chunk size
   int32_t packed;
@@ -21,6 +23,10 @@ struct Prob {
   int64_t nck;       // chunk slots
   ChunkMap map;      // device view of the chunk layout (table pointers set when packed)
 };
+
+// Whether the bf16 MFMA kernels run (bf16 io, headdim and dstate >= 32); otherwise
+// the fp32 matrix-core kernels of k_f32.hip, with fp32 intermediates.
+inline bool bf16_kernels(const Prob& p) { return p.io == 1 && !p.wide; }
 
 // Prob::flags bit (SSD_FLAG_SEQUENTIAL_SCAN of ssd.h): state passing, forward and
 // reverse, runs the sequential-carry kernel instead of the associative scan.
@@ -40,7 +46,7 @@ enum { kCsTable = 0, kCsOneHead = 1, kCsTwoHeads = 2, kCsTwoHeadsCB = 3 };
 // Whether variant v (1..3) can run this problem: two heads per workgroup need an
 // even head count per group and a shape whose shared operand and LDS fit; C.B^T
 // inside the kernel needs bf16, chunk 256 and eight heads per group (one 64-row
-// block of C.B^T per head pair).  The fp32 path has one form (1).
+// block of C.B^T per head pair).  The fp32 matrix-core path has one form (1).
 bool cs_variant_valid(const Prob& p, int v);
 // The variant the chunk-state kernels run: the flag's choice, else the tuned
 // table's entry for the problem's (headdim, dstate, heads per group, chunk), else
@@ -124,13 +130,14 @@ hipError_t launch_fwd_chained(const Prob& p, const ChainIO& io, hipStream_t st);
 
 // which: 0 every chunk kernel; 1 dx, 2 dCB (fp32: dCB, then the r + R rows), 3 dC, 4 dB
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st);
-// The fp32 path (k_f32.hip): the same stages on the fp32 matrix cores; io must be fp32.
-hipError_t launch_chunk_state_f32(const Prob& p, const float* X, const float* Y, const float* delta,
+// The fp32 matrix-core path (k_f32.hip), where !bf16_kernels(p): the same stages;
+// the io tensors (x, B, C, C.B^T, y and the gradients) in p.io's type.
+hipError_t launch_chunk_state_f32(const Prob& p, const void* X, const void* Y, const float* delta,
                                   const float* acs, float* out, int mode, hipStream_t st);
-hipError_t launch_bmm_chunk_f32(const Prob& p, const float* B, const float* C, float* CB, hipStream_t st);
-hipError_t launch_chunk_scan_f32(const Prob& p, const float* x, const float* C, const float* CB,
+hipError_t launch_bmm_chunk_f32(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st);
+hipError_t launch_chunk_scan_f32(const Prob& p, const void* x, const void* C, const void* CB,
                                  const float* delta, const float* acs, const float* passed,
-                                 const float* D, float* out, hipStream_t st);
+                                 const float* D, void* out, hipStream_t st);
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int which, hipStream_t st);
 // dB and dC, their dCB, r and whole R, K in one kernel (k_bwd_dbc.hip): R into
 // a.Rp and K into a.Kp, one value per (chunk, head, token); r into a.rR.

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
 hipError_t launch_bmm_chunk(const Prob& p, const void* B, const void* C, void* CB, hipStream_t st,
                             void* CBt) {
   if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) return launch_bmm_chunk_f32(p, (const float*)B, (const float*)C, (float*)CB, st);
+  if (!bf16_kernels(p)) return launch_bmm_chunk_f32(p, B, C, CB, st);
   dim3 grid((unsigned)p.nck, p.G);
 #define SSD_BMM_CASE(NN)                                                                   \
   if (p.N == NN) {                                                                         \

@@ -976,7 +976,7 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStrea
 
 hipError_t launch_bwd_chunk(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) return launch_bwd_f32(p, a, which, st);
+  if (!bf16_kernels(p)) return launch_bwd_f32(p, a, which, st);
 #define SSD_BWD_CASE(PP, NN) \
   if (p.P == PP && p.N == NN) { launch_bwd_bf16<PP, NN>(p, a, which, st); return hipGetLastError(); }
   SSD_BWD_CASE(32, 32) SSD_BWD_CASE(32, 64) SSD_BWD_CASE(32, 128)
@@ -991,7 +991,7 @@ hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st, 
     hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, (p.H + kFinHeads - 1) / kFinHeads),
                        dim3(kFinHeads * 64), 0, st,
                        p.map, p.H, p.softplus, a.dt, a.dt_bias, a.A, a.delta, a.rR, a.Ks, a.ddd,
-                       a.last_term, a.Rp, a.Kp, (p.io == 0 || fused) ? 0 : p.Q / 64,
+                       a.last_term, a.Rp, a.Kp, (!bf16_kernels(p) || fused) ? 0 : p.Q / 64,
                        fused ? a.Rp : nullptr, fused ? a.Kp : nullptr, a.ddt, a.dAp, a.dbp);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((p.H + 3) / 4), dim3(256), 0, st, (int)p.nck, p.H,
                      a.dAp, a.dbp, a.dDp, a.dA, a.d_dt_bias, a.dD);

@@ -455,7 +455,7 @@ static void launch_dbc(const Prob& p, const BwdArgs& a, hipStream_t st) {
                      (uint16_t*)a.dC, a.rR, a.Rp, a.Kp);
 }
 
-bool bwd_fused_supported(const Prob& p) { return p.io == 1 && p.Q <= QMAXF && p.P >= 32 && p.N >= 32; }
+bool bwd_fused_supported(const Prob& p) { return bf16_kernels(p) && p.Q <= QMAXF && p.P >= 32 && p.N >= 32; }
 
 hipError_t launch_bwd_dbc(const Prob& p, const BwdArgs& a, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;

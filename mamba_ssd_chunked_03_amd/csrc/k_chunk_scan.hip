@@ -121,10 +121,9 @@ hipError_t launch_chunk_scan(const Prob& p, const void* x, const void* C, const 
                              const float* delta, const float* acs, const void* passed,
                              int passed_bf16, const float* D, void* out, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) {
+  if (!bf16_kernels(p)) {
     if (passed_bf16) return hipErrorInvalidValue;
-    return launch_chunk_scan_f32(p, (const float*)x, (const float*)C, (const float*)CB, delta, acs,
-                                 (const float*)passed, D, (float*)out, st);
+    return launch_chunk_scan_f32(p, x, C, CB, delta, acs, (const float*)passed, D, out, st);
   }
 #define SSD_SCAN_CASE(PP, NN) \
   if (p.P == PP && p.N == NN) { launch_scan_bf16<PP, NN>(p, x, C, CB, delta, acs, passed, passed_bf16, D, out, st); return hipGetLastError(); }

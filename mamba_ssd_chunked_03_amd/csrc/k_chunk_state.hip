@@ -338,7 +338,7 @@ static hipError_t launch_cs(const Prob& p, const void* X, const void* Y, float* 
 hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const float* delta,
                               const float* acs, float* out, int mode, hipStream_t st) {
   if (p.nck == 0) return hipSuccess;
-  if (p.io == 0) return launch_chunk_state_f32(p, (const float*)X, (const float*)Y, delta, acs, out, mode, st);
+  if (!bf16_kernels(p)) return launch_chunk_state_f32(p, X, Y, delta, acs, out, mode, st);
   if (p.Q > QMAX_STATE) return hipErrorInvalidValue;  // one token per thread
   // (the kStateFwd and kStateDstates modes only read delta and acs)
   return launch_cs(p, X, Y, const_cast<float*>(delta), const_cast<float*>(acs), out, mode, CumsumIn{}, st);
@@ -346,7 +346,7 @@ hipError_t launch_chunk_state(const Prob& p, const void* X, const void* Y, const
 
 bool cs_variant_valid(const Prob& p, int v) {
   if (v == kCsOneHead) return true;
-  if (p.io != 1 || p.G <= 0 || (v != kCsTwoHeads && v != kCsTwoHeadsCB)) return false;
+  if (!bf16_kernels(p) || p.G <= 0 || (v != kCsTwoHeads && v != kCsTwoHeadsCB)) return false;
   const int hpg = p.H / p.G;
   if (hpg % 2 || !cs_two_ok(p.P, p.N)) return false;
   // C.B^T inside: chunks of four 64-row blocks and four head pairs per group
@@ -369,7 +369,7 @@ static const int kTunedCsCount = 0;
 int cs_variant_for(const Prob& p) {
   const int f = (p.flags >> kCsVariantShift) & 3;
   if (f != kCsTable) return f;  // (make_prob refuses a variant the problem cannot run)
-  if (p.io != 1 || p.G <= 0) return kCsOneHead;
+  if (!bf16_kernels(p) || p.G <= 0) return kCsOneHead;
   const int hpg = p.H / p.G;
   for (int i = 0; i < kTunedCsCount; ++i) {
     const CsEntry& e = kTunedCs[i];
@@ -381,7 +381,7 @@ int cs_variant_for(const Prob& p) {
   return kCsOneHead;
 }
 
-bool cb_in_chunk_state(const Prob& p) { return p.io == 1 && cs_variant_for(p) == kCsTwoHeadsCB; }
+bool cb_in_chunk_state(const Prob& p) { return bf16_kernels(p) && cs_variant_for(p) == kCsTwoHeadsCB; }
 
 hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* Bm, const float* dt,
                                      const float* dt_bias, const float* A, float* delta, float* acs,
@@ -389,7 +389,7 @@ hipError_t launch_cumsum_chunk_state(const Prob& p, const void* X, const void* B
                                      void* CBt) {
   if (p.nck == 0) return hipSuccess;
   if (C && !cb_in_chunk_state(p)) return hipErrorInvalidValue;
-  if (p.io == 0 || p.Q > 256) {
+  if (!bf16_kernels(p) || p.Q > 256) {
     const hipError_t e = launch_chunk_cumsum(p, dt, dt_bias, A, delta, acs, decay, st);
     if (e != hipSuccess) return e;
     return launch_chunk_state(p, X, Bm, delta, acs, T, kStateFwd, st);

@@ -316,7 +316,7 @@ __global__ void chain_clear_kernel(int32_t* __restrict__ p, int64_t n) {
 }
 
 bool chained_supported(const Prob& p) {
-  return p.io == 1 && p.Q <= kScanQmax && (p.P == 32 || p.P == 64 || p.P == 128) &&
+  return bf16_kernels(p) && p.Q <= kScanQmax && (p.P == 32 || p.P == 64 || p.P == 128) &&
          (p.N == 64 || p.N == 128);
 }
 

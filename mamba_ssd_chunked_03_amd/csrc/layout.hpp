@@ -5,9 +5,11 @@
 // the region's size with it:
 //   chunk states T and their adjoints U (the scan's inputs; also the chained
 //   forward's carry)                                             ChunkStateT (fp32)
-//   passed states H and their adjoints dE                         io-sized (bf16 or fp32)
+//   passed states H and their adjoints dE         bf16 where the bf16 kernels run, else fp32
 //   delta, within-chunk cumsum, per-token backward pieces, tile partials   fp32
-//   C.B^T and the head-summed dCB (both paths), C.B^T transposed (bf16)  io-sized
+//   C.B^T                                                         io-sized (bf16 or fp32)
+//   the head-summed dCB                           bf16 where the bf16 kernels run, else fp32
+//   C.B^T transposed, R and K tile partials       only where the bf16 kernels run
 #pragma once
 
 #include <cstddef>
@@ -26,14 +28,17 @@ struct LayoutDims {
   int64_t nseq;           // sequences (packed) or batch rows
   bool packed;
   bool bf16;              // io dtype bf16 (else fp32)
+  bool wide;              // bf16 io run by the fp32 matrix-core kernels (headdim or dstate 16)
 };
 
 constexpr size_t kLayoutAlign = 256;
 inline size_t lay_up(size_t x) { return (x + kLayoutAlign - 1) / kLayoutAlign * kLayoutAlign; }
 inline size_t io_size(const LayoutDims& d) { return d.bf16 ? 2 : 4; }
-// passed states and their adjoints: every consumer on the bf16 path feeds them to bf16
-// matrix products, so they are stored in bf16 there
-inline size_t passed_size(const LayoutDims& d) { return d.bf16 ? 2 : 4; }
+// whether the bf16 MFMA kernels run (their intermediates are partly bf16)
+inline bool bf16_kernels(const LayoutDims& d) { return d.bf16 && !d.wide; }
+// passed states and their adjoints: every consumer on the bf16 kernels' path feeds
+// them to bf16 matrix products, so they are stored in bf16 there (fp32 otherwise)
+inline size_t passed_size(const LayoutDims& d) { return bf16_kernels(d) ? 2 : 4; }
 
 struct FwdLayout {
   size_t tab, seq_off, delta, acs, decay, T, Hp, CB, sync, end;
@@ -64,10 +69,11 @@ inline BwdLayout bwd_layout(const LayoutDims& d) {
   l.f = fwd_layout(d);
   size_t o = l.f.end;
   const size_t nck = (size_t)d.nck, H = (size_t)d.H, st = (size_t)(d.P * d.N);
-  const size_t cb = d.bf16 ? nck * (size_t)d.G * d.Q * d.Q * 2 : 0;
-  const size_t tiles = d.bf16 ? nck * H * (size_t)(d.Q / 64) * d.Q * sizeof(TokenT) : 0;
+  const bool bk = bf16_kernels(d);
+  const size_t cb = bk ? nck * (size_t)d.G * d.Q * d.Q * 2 : 0;
+  const size_t tiles = bk ? nck * H * (size_t)(d.Q / 64) * d.Q * sizeof(TokenT) : 0;
   l.CBt = o;  o += lay_up(cb);
-  l.dCBg = o; o += lay_up(nck * (size_t)d.G * d.Q * d.Q * io_size(d));
+  l.dCBg = o; o += lay_up(nck * (size_t)d.G * d.Q * d.Q * (bk ? 2 : 4));
   l.Rp = o;   o += lay_up(tiles);
   l.Kp = o;   o += lay_up(tiles);
   l.U = o;    o += lay_up(nck * H * st * sizeof(ChunkStateT));

@@ -46,9 +46,13 @@ int main() {
         for (int N : Ns)
           for (int Q : Qs)
             for (long long nck : {0LL, 1LL, 3LL, 64LL, 517LL}) {
-              LayoutDims d{nck, 64, P, N, 8, Q, packed ? 5 : 2, packed != 0, bf != 0};
+              // bf16 io below 32-wide headdim or dstate runs the fp32 matrix-core kernels
+              const bool wide = bf && (P < 32 || N < 32);
+              LayoutDims d{nck, 64, P, N, 8, Q, packed ? 5 : 2, packed != 0, bf != 0, wide};
               const size_t st = (size_t)nck * 64 * P * N, tok = (size_t)nck * 64 * Q, ch = (size_t)nck * 64;
-              const size_t io = bf ? 2 : 4;
+              const size_t io = bf ? 2 : 4;               // io tensors: C.B^T
+              const bool bk = bf && !wide;                 // the bf16 kernels run
+              const size_t pas = bk ? 2 : 4;               // passed states and their adjoints
               const FwdLayout f = fwd_layout(d);
               std::vector<Reg> fr = {
                   {"chunk table", f.tab, packed ? (size_t)nck * 16 : 0},
@@ -58,7 +62,7 @@ int main() {
                   {"decay", f.decay, ch * sizeof(float)},
                   // written by the chunk-state kernel, read by the scan: fp32 on both sides
                   {"chunk states T", f.T, st * sizeof(ChunkStateT)},
-                  {"passed states H", f.Hp, st * io},
+                  {"passed states H", f.Hp, st * pas},
                   {"C.B^T", f.CB, (size_t)nck * 8 * Q * Q * io},
                   {"chained flags", f.sync, nck ? (size_t)(kChainSyncWords + nck * 64) * 4 : 0},
               };
@@ -66,17 +70,17 @@ int main() {
               const BwdLayout b = bwd_layout(d);
               CHECK(b.f.end == f.end && b.f.T == f.T && b.f.Hp == f.Hp && b.f.CB == f.CB && b.f.delta == f.delta,
                     "the backward's saved-context offsets differ from the forward's");
-              const size_t cb = bf ? (size_t)nck * 8 * Q * Q * 2 : 0;
-              const size_t tiles = bf ? (size_t)nck * 64 * (Q / 64) * Q * 4 : 0;
+              const size_t cb = bk ? (size_t)nck * 8 * Q * Q * 2 : 0;
+              const size_t tiles = bk ? (size_t)nck * 64 * (Q / 64) * Q * 4 : 0;
               std::vector<Reg> br = fr;
               br.insert(br.end(), {
                   {"C.B^T transposed", b.CBt, cb},
-                  {"head-summed dCB", b.dCBg, (size_t)nck * 8 * Q * Q * io},
+                  {"head-summed dCB", b.dCBg, (size_t)nck * 8 * Q * Q * (bk ? 2 : 4)},
                   {"R partials", b.Rp, tiles},
                   {"K partials", b.Kp, tiles},
                   // written by the adjoint-state kernel, read by the reverse scan: fp32 on both sides
                   {"adjoint chunk states U", b.U, st * sizeof(ChunkStateT)},
-                  {"adjoint passed states dE", b.dE, st * io},
+                  {"adjoint passed states dE", b.dE, st * pas},
                   {"direct ddelta", b.ddd, tok * 4},
                   {"K + s", b.Ks, tok * 4},
                   {"r + R", b.rR, tok * 4},

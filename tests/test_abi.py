@@ -92,7 +92,8 @@ def test_bwd_validation(L):
     (dict(ngroups=3), SHAPE), (dict(nheads=0), SHAPE), (dict(batch=-1), SHAPE),
     (dict(seqlen=-5), SHAPE), (dict(dt_softplus=2), SHAPE),
     (dict(headdim=48), UNSUP), (dict(dstate=256), UNSUP), (dict(io_dtype=5), UNSUP),
-    (dict(headdim=16), UNSUP),                 # bf16 needs headdim >= 32
+    # bf16 with headdim or dstate 16 runs on the fp32 matrix-core kernels
+    (dict(headdim=16), OK), (dict(dstate=16), OK), (dict(headdim=16, dstate=16), OK),
     (dict(headdim=16, dstate=16, io_dtype=0), OK),
     # one chunk's token rows must span less than 2^31 bytes (32-bit offsets)
     (dict(nheads=16384, ngroups=8, headdim=128), UNSUP),

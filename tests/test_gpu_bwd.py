@@ -81,6 +81,13 @@ CASES = [
                          io="f32", init="zeros", seed=61, d_final=True), (64, 256)),
     ("f32_p128n128", dict(batch=1, seqlen=200, nheads=2, headdim=128, dstate=128, ngroups=1,
                           io="f32", init="randn", seed=62), (128,)),
+    # bf16 io with headdim or dstate 16: the fp32 matrix-core kernels on bf16 tensors
+    ("bf16_p16n64", dict(batch=2, seqlen=333, nheads=4, headdim=16, dstate=64, ngroups=2,
+                         io="bf16", init="randn", seed=64, d_final=True), (64, 256)),
+    ("bf16_p64n16", dict(batch=1, seqlen=400, nheads=8, headdim=64, dstate=16, ngroups=2,
+                         io="bf16", init="randn", seed=65), (128,)),
+    ("bf16_p16n16", dict(batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, ngroups=1,
+                         io="bf16", dt_mode="direct", init="none", seed=66), (64,)),
 ]
 
 

@@ -52,6 +52,13 @@ CASES = [
                          io="f32", init="randn", seed=19), (256,)),
     ("f32_p32n128", dict(batch=1, seqlen=290, nheads=8, headdim=32, dstate=128, ngroups=2,
                          io="f32", init="zeros", seed=20), (64, 256)),
+    # bf16 io with headdim or dstate 16: the fp32 matrix-core kernels on bf16 tensors
+    ("bf16_p16n64", dict(batch=2, seqlen=333, nheads=4, headdim=16, dstate=64, ngroups=2,
+                         io="bf16", init="randn", seed=24), (64, 256)),
+    ("bf16_p64n16", dict(batch=1, seqlen=400, nheads=8, headdim=64, dstate=16, ngroups=2,
+                         io="bf16", init="randn", seed=25), (128,)),
+    ("bf16_p16n16", dict(batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, ngroups=1,
+                         io="bf16", dt_mode="direct", init="none", seed=26), (64,)),
 ]
 PACKED = [
     ("packed_bf16", dict(nheads=4, headdim=64, dstate=128, ngroups=2, io="bf16", init="randn",
@@ -60,6 +67,8 @@ PACKED = [
                         seed=22), [65, 0, 0, 64, 3], (64,)),
     ("packed_f32_p64", dict(nheads=4, headdim=64, dstate=64, ngroups=2, io="f32", init="randn",
                             seed=23), [1, 0, 300, 257, 77], (128, 256)),
+    ("packed_bf16_p16", dict(nheads=4, headdim=16, dstate=128, ngroups=2, io="bf16", init="randn",
+                             seed=27), [1, 0, 300, 257, 77], (64, 256)),
 ]
 
 
@@ -159,6 +168,8 @@ STAGE_KW = [
      [1, 0, 300, 513, 77], 128),
     (dict(batch=1, seqlen=200, nheads=2, headdim=16, dstate=16, ngroups=1, io="f32",
           init="randn", seed=43), None, 64),
+    (dict(batch=1, seqlen=200, nheads=2, headdim=16, dstate=32, ngroups=1, io="bf16",
+          init="randn", seed=44), None, 64),
 ]
 
 
