@@ -104,7 +104,7 @@ struct BwdArgs {
   const void *Hp, *dE;  // per (chunk, head) P x N: bf16 on the bf16 path, fp32 otherwise
   const void *CB, *CBt;
   void* dCBg;          // head-summed dCB per (chunk, group), (Q, Q) row-major
-  float *Rp, *Kp;      // per (chunk, head, 64-token tile, token): R and K partials
+  float *Rp, *Kp;      // per (chunk, head, tile of 64 or 128 tokens, token): R and K partials
   void *dx, *dB, *dC;
   float *ddt, *dA, *dD, *d_dt_bias;
   // per token (nck, H, Q): direct d(delta); s (bf16 path) or K+s (fp32 path);

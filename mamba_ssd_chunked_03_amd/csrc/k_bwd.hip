@@ -21,7 +21,8 @@
 // Kernels (bf16 MFMA; the fp32 path's counterparts are in k_f32.hip):
 //   bwd_dx   (chunk, head)            dx, direct d(delta), s_j, dD and
 //                                     alpha<dE,H> + sum s per chunk
-//   bwd_dcb  (chunk, group, 64x64 causal tile)  head-summed dCB_g; per-head
+//   bwd_dcb  (chunk, group, 128x128 causal super-tile; 64x64 tiles where the
+//            chunk size is 64 or headdim 128)  head-summed dCB_g; per-head
 //                                     tile partials of R, K
 //   bwd_dc   (chunk, group, 64 rows)  dC = dCB_g B + sum_h (state term); r_i
 //   bwd_db   (chunk, group, 64 rows)  dB = dCB_g^T C + sum_h (state term)
@@ -525,6 +526,260 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
   }
 }
 
+// ----------------------------------------------------- bwd_dcb bf16, 128 ----
+// The head-summed dCB_g of bwd_dcb_bf16_kernel, on 128x128 super-tiles (si, sj),
+// sj <= si, for chunk sizes that are multiples of 128.  A (chunk, group) has
+// T2 (T2 + 1) / 2 of them (3 at chunk 256) against T (T + 1) / 2 64x64 tiles
+// (10): each head's dy and x rows of 128 tokens serve two 64x64 tiles each way,
+// so a chunk's rows are read 12 times per head instead of 20.  Every element is
+// formed exactly as in the 64x64 kernel (the 64x64 tiles' decay anchors, the
+// same operand order and the same head order of the sum), so dCB_g is the same
+// bit for bit; the tile partials of R and K cover 128 columns / rows.
+//
+// Eight waves; wave w owns rows 128 si + 16 w .. +15 and the super-tile's 8
+// column blocks of 16 (on a diagonal super-tile only blocks b <= w: the others
+// lie above the diagonal).  Per head, x's 128 rows are staged in LDS by all
+// waves (double-buffered), each wave's dy rows stay in registers, and the
+// head's decay factors go to LDS (double-buffered), all loaded one head ahead;
+// the previous head's column sums are reduced across the waves after the
+// barrier that starts the next head.  A wave whose rows all lie past the
+// chunk's end does no work (so no value read past the end, where a decay anchor
+// of a short chunk can lie, enters a product).
+constexpr int kT128Waves = 8;
+
+template <int P>
+__global__ __launch_bounds__(kT128Waves * 64, 4) void bwd_dcb_t128_bf16_kernel(
+    ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ DY,
+    const uint16_t* __restrict__ CB, const float* __restrict__ delta,
+    const float* __restrict__ acs, uint16_t* __restrict__ dCBg,
+    float* __restrict__ Rp, float* __restrict__ Kp) {
+  constexpr int NT = kT128Waves * 64;
+  constexpr int LX = P + 8;             // x tile row stride (bf16)
+  constexpr int LT = 128 + 8;           // output staging row stride
+  constexpr int PER = P / 8;            // 16-byte pieces per row
+  constexpr int NPX = 128 * PER / NT;   // x pieces per thread per head
+  constexpr int XS = 128 * LX;          // one x buffer
+  constexpr int XL = 2 * XS > 128 * LT ? 2 * XS : 128 * LT;
+  static_assert(NPX >= 1 && 128 * PER % NT == 0, "headdim");
+  __shared__ __attribute__((aligned(16))) uint16_t xt[XL];
+  __shared__ __attribute__((aligned(16))) float kred[2][kT128Waves][128];
+  __shared__ __attribute__((aligned(16))) float sv[2][384];  // one head's decay factors (below)
+  const int Q = m.Q, T2 = Q / 128, NS = T2 * (T2 + 1) / 2;
+  const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, super-tile), super-tile fastest
+  const int tile = lid % NS, k = lid / NS / G, g = (lid / NS) % G;
+  const ChunkInfo ci = chunk_info(m, k);
+  int si = 0;
+  while ((si + 1) * (si + 2) / 2 <= tile) ++si;
+  const int sj = tile - si * (si + 1) / 2;
+  if (ci.len <= 0 || si * 128 >= ci.len) return;
+  const int len = ci.len;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r = lane & 15;
+  const int hpg = H / G;
+  const int64_t xrow = (int64_t)H * P;
+  const int i0 = si * 128 + w * 16, jt0 = sj * 128;
+  const bool diag = si == sj;
+  const bool live = i0 < len;          // (uniform per wave)
+  const int nblk = diag ? w + 1 : 8;   // column blocks this wave works on
+  const int64_t kg = (int64_t)k * G + g;
+  const uint16_t* cbm = CB + kg * Q * Q;
+  // C.B^T at this lane's 32 outputs (rows i0 + 4 q + rr, columns jt0 + 16 b + r),
+  // two bf16 values per register, zero unless j < i < len
+  // (range-checked 2-byte loads, the mask folded into an offset past the range:
+  // no load sits under a branch, so all 32 are in flight together)
+  const brsrc rcb = make_rsrc(cbm, (uint32_t)(Q * Q * 2));
+  uint32_t cbp[8][2];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    uint32_t v[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
+      const bool ok = live && b < nblk && i < len && j < i;
+      v[rr] = __builtin_amdgcn_raw_buffer_load_b16(rcb, ok ? (uint32_t)(i * Q + j) * 2u : 0x80000000u, 0, 0);
+    }
+    cbp[b][0] = v[0] | (v[1] << 16);
+    cbp[b][1] = v[2] | (v[3] << 16);
+  }
+  // This thread's decay inputs per head (tokens are chunk positions < Q, inside
+  // the workspace; 0x80000000: none).  Off the diagonal, the super-tile's four
+  // 64x64 tiles are all off the diagonal, tile (ti, tj) anchored at its last
+  // column e = 64 tj + 63:
+  //   [0, 256)   rho[a][i] = 2^(acs_i - acs_e(a)) (0 past the chunk's end), a = tj - 2 sj
+  //   [256, 384) gam[j] = 2^(acs_e(j) - acs_j) delta_j
+  // On the diagonal, tile (2 si + 1, 2 si) is anchored at e = 128 si + 63 and the
+  // two diagonal tiles take one exp per element:
+  //   [0, 64) rho of rows 64..127, [64, 128) gam of columns 0..63,
+  //   [128, 256) acs of the 128 tokens, [256, 384) their delta.
+  // Thread t's entry t of that table: its token, its anchor (or -1) and its kind.
+  // Formed from an opaque copy of the thread index where used, so that the
+  // compiler does not keep them in registers across the head loop.
+  struct Role {
+    int tok, anc, kind;  // kind: 0 none, 1 rho, 2 gam, 3 acs, 4 delta
+  };
+  auto role = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    Role o{0, -1, 0};
+    if (!diag) {
+      if (t < 256) o = Role{si * 128 + (t & 127), sj * 128 + (t >> 7) * 64 + 63, 1};
+      else if (t < 384) o = Role{jt0 + t - 256, jt0 + ((t - 256) >> 6) * 64 + 63, 2};
+    } else {
+      const int e = si * 128 + 63;
+      if (t < 64) o = Role{si * 128 + 64 + t, e, 1};
+      else if (t < 128) o = Role{si * 128 + t - 64, e, 2};
+      else if (t < 256) o = Role{si * 128 + t - 128, -1, 3};
+      else if (t < 384) o = Role{si * 128 + t - 256, -1, 4};
+    }
+    return o;
+  };
+  f32x4 sum[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) sum[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the next head's rows and decay inputs
+  u32x4 ay[P / 32], px[NPX];
+  float pa = 0.f, pd = 0.f, pe = 0.f;
+  const uint32_t yo = (uint32_t)(i0 + r) * (uint32_t)(xrow * 2) + q * 16;
+  auto load_head = [&](int h) {
+    const brsrc rdy = make_rsrc(DY + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
+    const brsrc rxt = make_rsrc(X + (int64_t)(ci.start + jt0) * xrow + (int64_t)h * P,
+                                (uint32_t)(max(len - jt0, 0) * xrow * 2));
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb) ay[kb] = buf_load16(rdy, yo + 64 * kb);
+#pragma unroll
+    for (int c = 0; c < NPX; ++c) {
+      const uint32_t e = tid + c * NT, row = e / PER, c8 = e % PER;
+      px[c] = buf_load16(rxt, row * (uint32_t)(xrow * 2) + c8 * 16);
+    }
+    const int64_t kh = (int64_t)k * H + h;
+    const brsrc ra = make_rsrc(acs + kh * Q, (uint32_t)(Q * 4));
+    const brsrc rd = make_rsrc(delta + kh * Q, (uint32_t)(Q * 4));
+    const Role o = role();
+    constexpr uint32_t kNone = 0x80000000u;  // past every range: reads zero
+    const uint32_t ot = (uint32_t)o.tok * 4u;
+    pa = buf_load_f32(ra, (o.kind == 1 || o.kind == 2 || o.kind == 3) ? ot : kNone);
+    pd = buf_load_f32(rd, (o.kind == 2 || o.kind == 4) ? ot : kNone);
+    pe = buf_load_f32(ra, o.anc >= 0 ? (uint32_t)o.anc * 4u : kNone);
+  };
+  load_head(g * hpg);
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int64_t kh = (int64_t)k * H + h;
+    const int buf = hh & 1;
+    uint16_t* xbuf = xt + buf * XS;
+#pragma unroll
+    for (int c = 0; c < NPX; ++c) {
+      const int e = tid + c * NT, row = e / PER, c8 = e % PER;
+      *(u32x4*)(xbuf + row * LX + c8 * 8) = px[c];
+    }
+    {
+      const Role o = role();
+      float f = o.kind == 3 ? pa : pd;
+      if (o.kind == 1) f = (o.tok < len) ? exp2_fast(pa - pe) : 0.f;
+      if (o.kind == 2) f = exp2_fast(pe - pa) * pd;
+      if (o.kind) sv[buf][tid] = f;
+    }
+    __syncthreads();
+    if (hh > 0 && tid < 128) {  // the previous head's column sums, fixed order over the waves
+      const int j = jt0 + tid;
+      float v = 0.f;
+#pragma unroll
+      for (int u = 0; u < kT128Waves; ++u) v += kred[buf ^ 1][u][tid];
+      if (j < len) Kp[((kh - 1) * T2 + si) * Q + j] = v;
+    }
+    bf16x8 af[P / 32];
+#pragma unroll
+    for (int kb = 0; kb < P / 32; ++kb) af[kb] = as_bf16x8(ay[kb]);
+    if (hh + 1 < hpg) load_head(h + 1);  // in flight during this head's work
+    const float* svh = sv[buf];
+    // this lane's x fragment base (an opaque copy of the lane index: the block and
+    // k-step offsets become immediates instead of 16 hoisted addresses)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint16_t* xl = xbuf + (ln & 15) * LX + (ln >> 4) * 8;
+    float Rl[4] = {0.f, 0.f, 0.f, 0.f}, Kl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float kA = 0.f, kB = 0.f;  // column sums over the wave's rows (below)
+    if (live) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        if (b == 4) kA = col_reduce_scatter4(Kl[0], Kl[1], Kl[2], Kl[3]);
+        if (b >= nblk) continue;
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < P / 32; ++kb)
+          d = mfma_bf16(af[kb], as_bf16x8(*(const u32x4*)(xl + b * 16 * LX + kb * 32)), d);
+        // (unpacked here from opaque copies: hoisted out of the head loop, the 32
+        // values would not fit the registers)
+        uint32_t c01 = cbp[b][0], c23 = cbp[b][1];
+        asm volatile("" : "+v"(c01), "+v"(c23));
+        float cb[4];
+        cb[0] = __uint_as_float(c01 << 16);
+        cb[1] = __uint_as_float(c01 & 0xffff0000u);
+        cb[2] = __uint_as_float(c23 << 16);
+        cb[3] = __uint_as_float(c23 & 0xffff0000u);
+        // v = dCB^h_ij, M_ij = v CB_ij; R_i and K_j both add the exact products
+        if (!diag || (w >= 4 && b < 4)) {  // a 64x64 tile off the diagonal
+          const int ro = diag ? (w - 4) * 16 + q * 4 : (b >> 2) * 128 + w * 16 + q * 4;
+          const float4 rho = *(const float4*)(svh + ro);
+          const float rr4[4] = {rho.x, rho.y, rho.z, rho.w};
+          const float gam = svh[(diag ? 64 : 256) + b * 16 + r];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float v = d[rr] * rr4[rr] * gam;
+            sum[b][rr] += v;
+            Rl[rr] = fmaf(v, cb[rr], Rl[rr]);
+            Kl[b] = fmaf(v, cb[rr], Kl[b]);
+          }
+        } else {  // a diagonal 64x64 tile: one exp per element and the causal mask
+          const float aj = svh[128 + b * 16 + r], dj = svh[256 + b * 16 + r];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int i = i0 + (ln >> 4) * 4 + rr, j = jt0 + b * 16 + (ln & 15);  // (masks formed per head)
+            float v = d[rr] * exp2_fast(svh[128 + w * 16 + q * 4 + rr] - aj) * dj;
+            v = (j <= i && i < len) ? v : 0.f;
+            sum[b][rr] += v;
+            Rl[rr] = fmaf(v, cb[rr], Rl[rr]);  // cb is zero unless j < i < len
+            Kl[b] = fmaf(v, cb[rr], Kl[b]);
+          }
+        }
+      }
+      kB = col_reduce_scatter4(Kl[4], Kl[5], Kl[6], Kl[7]);
+      // row sums: lane r ends with row i0 + 4q + r/4; lanes r % 4 == 0 store
+      const float v = row_reduce_scatter4(Rl[0], Rl[1], Rl[2], Rl[3], r);
+      const int i = i0 + q * 4 + (r >> 2);
+      if ((r & 3) == 0 && i < len) Rp[(kh * T2 + sj) * Q + i] = v;
+    }
+    // column sums over the wave's rows: lane (r, q) holds columns 16 q + r and 64 + 16 q + r
+    kred[buf][w][q * 16 + r] = kA;
+    kred[buf][w][64 + q * 16 + r] = kB;
+  }
+  __syncthreads();
+  if (tid < 128) {  // the last head's column sums
+    const int64_t khl = (int64_t)k * H + g * hpg + hpg - 1;
+    const int j = jt0 + tid;
+    float v = 0.f;
+#pragma unroll
+    for (int u = 0; u < kT128Waves; ++u) v += kred[(hpg - 1) & 1][u][tid];
+    if (j < len) Kp[(khl * T2 + si) * Q + j] = v;
+  }
+  // head-summed tile -> bf16, through LDS to 16-byte row stores of the 64x64
+  // tiles that the 64x64 kernel writes (tj <= ti, rows of the tile before the
+  // chunk's end)
+  uint16_t* stg = xt;  // every wave is past its last read of the x tiles (barrier above)
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) stg[(w * 16 + q * 4 + rr) * LT + b * 16 + r] = f2bf(sum[b][rr]);
+  __syncthreads();
+  for (int e = tid; e < 128 * 16; e += NT) {
+    const int row = e >> 4, c8 = e & 15;
+    const bool upper = diag && row < 64 && c8 >= 8;
+    if (!upper && si * 128 + (row & ~63) < len)
+      *(u32x4*)(dCBg + (kg * Q + si * 128 + row) * Q + jt0 + c8 * 8) = *(const u32x4*)(stg + row * LT + c8 * 8);
+  }
+}
+
 // ------------------------------------------------------------ bwd_dc bf16 ----
 // One workgroup per (chunk, group, 64 rows i).  dC_i = sum_{j<=i} dCB_g[i][j] B_j
 // (dCB_g fragments straight from its rows, B through LDS one 64-row piece at a
@@ -807,7 +1062,7 @@ __global__ __launch_bounds__(kFinHeads * 64) void bwd_finalize_kernel(
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ delta, const float* __restrict__ rR, const float* __restrict__ Ks,
     const float* __restrict__ ddd, const float* __restrict__ last_term,
-    const float* __restrict__ Rp, const float* __restrict__ Kp, int ntile,
+    const float* __restrict__ Rp, const float* __restrict__ Kp, int ntile, int tsh,
     const float* __restrict__ Rf, const float* __restrict__ Kf, float* __restrict__ ddt,
     float* __restrict__ dAp, float* __restrict__ dbp) {
   constexpr int NT = kFinHeads * 64, NE = kFinHeads * QMAX / NT;
@@ -840,7 +1095,7 @@ __global__ __launch_bounds__(kFinHeads * 64) void bwd_finalize_kernel(
   const int tb = Q - 4 * (lane + 1);
   const bool lane_in = tb >= 0;
   const uint32_t o = (lane_in && hin) ? (uint32_t)tb * 4u : 0x80000000u, qb = (uint32_t)Q * 4u;
-  const int tt = lane_in ? tb / 64 : 0, tlast = (len - 1) / 64;
+  const int tt = lane_in ? tb >> tsh : 0, tlast = (len - 1) >> tsh;
   const int64_t kh = (int64_t)k * H + h0 + (hin ? w : 0);
   auto ld4 = [&](const float* base, uint32_t bytes, uint32_t off) {
     const u32x4 v = buf_load16(make_rsrc(base, bytes), off);
@@ -850,7 +1105,8 @@ __global__ __launch_bounds__(kFinHeads * 64) void bwd_finalize_kernel(
   const f32x4 vd = ld4(delta + kh * Q, qb, o), v0 = ld4(ddd + kh * Q, qb, o);
   const f32x4 vrf = ld4(Rf ? Rf + kh * Q : rR, qb, Rf ? o : 0x80000000u);
   const f32x4 vkf = ld4(Kf ? Kf + kh * Q : Ks, qb, Kf ? o : 0x80000000u);
-  // 64x64 tile partials: R over column tiles <= the lane's, K over row tiles >= it
+  // tile partials (tiles of 2^tsh tokens): R over column tiles <= the lane's, K over
+  // row tiles >= it
   f32x4 vrp[4], vkp[4];
   const uint32_t tbytes = (uint32_t)(ntile * Q * 4);
 #pragma unroll
@@ -950,6 +1206,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(int nck, int H, const f
 }
 
 // ---------------------------------------------------------------- launchers ----
+// The head-summed dCB on 128x128 super-tiles where the chunk size allows and the
+// kernel fits its registers and LDS (headdim <= 64); 64x64 tiles otherwise.
+static bool dcb_t128(const Prob& p) { return p.Q % 128 == 0 && p.P <= 64; }
+
 template <int P, int N>
 static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStream_t st) {
   const int T = p.Q / 64;
@@ -958,11 +1218,23 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStrea
                      p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.B, (const uint16_t*)a.dout,
                      (const uint16_t*)a.CBt, a.delta, a.acs, a.decay, (const uint16_t*)a.dE, (const uint16_t*)a.Hp, a.D,
                      (uint16_t*)a.dx, a.ddd, a.Ks, a.last_term, a.dDp);
-  if (!which || which == 2)
-  hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
-                     dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
-                     (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
-                     (uint16_t*)a.dCBg, a.Rp, a.Kp);
+  bool t128 = false;
+  if constexpr (P <= 64) {
+    if ((!which || which == 2) && dcb_t128(p)) {
+      const int T2 = p.Q / 128;
+      hipLaunchKernelGGL((bwd_dcb_t128_bf16_kernel<P>), dim3((unsigned)(p.nck * p.G * (T2 * (T2 + 1) / 2))),
+                         dim3(kT128Waves * 64), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
+                         (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
+                         (uint16_t*)a.dCBg, a.Rp, a.Kp);
+      t128 = true;
+    }
+  }
+  if ((!which || which == 2) && !t128) {
+    hipLaunchKernelGGL((bwd_dcb_bf16_kernel<P>), dim3((unsigned)(p.nck * p.G * (T * (T + 1) / 2))),
+                       dim3(256), 0, st, p.map, p.H, p.G, (const uint16_t*)a.x,
+                       (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
+                       (uint16_t*)a.dCBg, a.Rp, a.Kp);
+  }
   if (!which || which == 3)
   hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
@@ -991,7 +1263,9 @@ hipError_t launch_bwd_finalize(const Prob& p, const BwdArgs& a, hipStream_t st, 
     hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)p.nck, (p.H + kFinHeads - 1) / kFinHeads),
                        dim3(kFinHeads * 64), 0, st,
                        p.map, p.H, p.softplus, a.dt, a.dt_bias, a.A, a.delta, a.rR, a.Ks, a.ddd,
-                       a.last_term, a.Rp, a.Kp, (!bf16_kernels(p) || fused) ? 0 : p.Q / 64,
+                       a.last_term, a.Rp, a.Kp,
+                       (!bf16_kernels(p) || fused) ? 0 : (dcb_t128(p) ? p.Q / 128 : p.Q / 64),
+                       dcb_t128(p) ? 7 : 6,
                        fused ? a.Rp : nullptr, fused ? a.Kp : nullptr, a.ddt, a.dAp, a.dbp);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((p.H + 3) / 4), dim3(256), 0, st, (int)p.nck, p.H,
                      a.dAp, a.dbp, a.dDp, a.dA, a.d_dt_bias, a.dD);

@@ -391,8 +391,13 @@ FUSED_CASES = [
 def test_fused_dbdc_matches_split_and_oracle(name, kw, Q):
     """The one-kernel dB/dC (SSD_FLAG_BWD_FUSED) against the three-kernel form
     (the default): dB, dC, dx and d_init bit for bit (same values, same order of
-    every sum); ddt, dA and d_dt_bias to rounding (the decay-gradient sums R and K
-    are added in another order); both against the oracle."""
+    every sum); ddt, dA and d_dt_bias to rounding: the decay-gradient sums R and K
+    are added in another grouping (whole per token, against partials over 64- or
+    128-token tiles), and dA can cancel to a small fraction of its terms (0.046
+    from terms of order 1 in the p32n64 case, where the fp32 grouping alone moves
+    it by 1e-5 of its size), so the two forms are held to 1e-4 of each other,
+    still far below either one's distance to the oracle (~3e-3); both against
+    the oracle."""
     if kw.get("lengths"):
         kw = dict(kw, seqlen=sum(kw["lengths"]))
     inp = inputs.make_inputs(io="bf16", bwd=True, **kw)
@@ -403,7 +408,7 @@ def test_fused_dbdc_matches_split_and_oracle(name, kw, Q):
         if g[k] is not None:
             assert torch.equal(g[k], gs[k]), (name, k)
     for k in ("ddt", "dA", "d_dt_bias"):
-        assert normwise(np64(g[k]), np64(gs[k])) <= 1e-5, (name, k)
+        assert normwise(np64(g[k]), np64(gs[k])) <= 1e-4, (name, k)
     ref = oracle_bwd(inp)
     check(g, ref, "bf16", name + " fused")
     check(gs, ref, "bf16", name + " split")
@@ -483,8 +488,8 @@ def test_opt_in_forms_full_size(cfg):
     for k in ("dx", "dB", "dC", "d_init", "dD"):
         if g[k] is not None:
             assert torch.equal(g[k], gf[k]), (cfg, k)
-    for k in ("ddt", "dA", "d_dt_bias"):
-        assert normwise(np64(gf[k]), np64(g[k])) <= 1e-5, (cfg, k)
+    for k in ("ddt", "dA", "d_dt_bias"):  # (the bar of test_fused_dbdc_matches_split_and_oracle)
+        assert normwise(np64(gf[k]), np64(g[k])) <= 1e-4, (cfg, k)
     del gf
     y0, f0 = gpu_fwd(ssd, inp, 256)
     for v in (1, 2, 3):

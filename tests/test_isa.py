@@ -1,5 +1,6 @@
 """Host-side check of the compiled gfx950 code of the step's kernels: no load is
-followed at once by a wait for every outstanding load at a branch join.
+followed within a few instructions by a wait for every outstanding load and then
+a branch join.
 
 That pattern appears when a load sits under a branch whose other path writes a
 zero into the same register (the zero's move must wait for the load in
@@ -25,7 +26,8 @@ KERNELS = [
     ("k_chunk_state.hip", "_ZN3ssd23chunk_state_bf16_kernelILi64ELi128ELi2ELi2EEE"),  # forward, cumsum + C.B^T
     ("k_chunk_state.hip", "_ZN3ssd23chunk_state_bf16_kernelILi64ELi128ELi1ELi2EEE"),  # adjoint states
     ("k_bwd.hip", "_ZN3ssd18bwd_dx_bf16_kernelILi64ELi128EEE"),
-    ("k_bwd.hip", "_ZN3ssd19bwd_dcb_bf16_kernelILi64EEE"),
+    ("k_bwd.hip", "_ZN3ssd24bwd_dcb_t128_bf16_kernelILi64EEE"),  # chunk 256: 128x128 super-tiles
+    ("k_bwd.hip", "_ZN3ssd19bwd_dcb_bf16_kernelILi64EEE"),        # chunk 64: 64x64 tiles
     ("k_bwd.hip", "_ZN3ssd18bwd_dc_bf16_kernelILi64ELi128EEE"),
     ("k_bwd.hip", "_ZN3ssd18bwd_db_bf16_kernelILi64ELi128EEE"),
     ("k_bwd.hip", "_ZN3ssd19bwd_finalize_kernelE"),
@@ -77,8 +79,10 @@ def test_no_load_then_full_wait_at_branch_join(src, prefix, tmpdir_mod):
     bad = []
     for i, l in enumerate(body):
         if re.search(r"\b(global|buffer)_load", l):
-            nxt = body[i + 1:i + 4]
-            if any("s_waitcnt vmcnt(0)" in n for n in nxt[:1]) and any(n.startswith(".LBB") for n in nxt):
+            # a wait for every load within a few instructions, then a branch join
+            nxt = body[i + 1:i + 7]
+            w = [k for k, n in enumerate(nxt) if "s_waitcnt vmcnt(0)" in n]
+            if w and any(n.startswith(".LBB") for n in nxt[w[0]:]):
                 bad.append(i)
             # inside a loop, a load whose value is waited for (all loads) and stored to
             # LDS before the next load is issued: one memory latency per value
