@@ -24,8 +24,8 @@
 //   bwd_dcb  (chunk, group, 128x128 causal super-tile; 64x64 tiles where the
 //            chunk size is 64 or headdim 128)  head-summed dCB_g; per-head
 //                                     tile partials of R, K
-//   bwd_dc   (chunk, group, 64 rows)  dC = dCB_g B + sum_h (state term); r_i
-//   bwd_db   (chunk, group, 64 rows)  dB = dCB_g^T C + sum_h (state term)
+//   bwd_dc   (chunk, group, 128 rows; 64 at chunk 64)  dC = dCB_g B + sum_h (state term); r_i
+//   bwd_db   (chunk, group, 128 rows; 64 at chunk 64)  dB = dCB_g^T C + sum_h (state term)
 //   finalize (chunk, 8 heads)     suffix sum of dAcs (DPP scan), d(delta)->ddt,
 //                                 per-chunk partials of dA and d_dt_bias
 //   reduce   (head)               fixed-order sums over chunks: dA, dD, d_dt_bias
@@ -781,7 +781,10 @@ __global__ __launch_bounds__(kT128Waves * 64, 4) void bwd_dcb_t128_bf16_kernel(
 }
 
 // ------------------------------------------------------------ bwd_dc bf16 ----
-// One workgroup per (chunk, group, 64 rows i).  dC_i = sum_{j<=i} dCB_g[i][j] B_j
+// One workgroup of W waves per (chunk, group, 16 W rows i): W = 8 (128 rows) where
+// the chunk size is a multiple of 128, so that each head's H tile is staged once
+// for 128 rows (half the requests for it of 64-row workgroups), else W = 4.
+// dC_i = sum_{j<=i} dCB_g[i][j] B_j
 // (dCB_g fragments straight from its rows, B through LDS one 64-row piece at a
 // time and read with transpose reads) + sum_h 2^acs_i H^T dy_i (one K=headdim
 // GEMM per head); r_i = C_i . (that head's state term).  Per head, H (bf16) is
@@ -791,21 +794,22 @@ __global__ __launch_bounds__(kT128Waves * 64, 4) void bwd_dcb_t128_bf16_kernel(
 // one row i: its r_i reduces over four lanes.  B and H are staged with their
 // column groups permuted (common.hpp, pcol), so a lane's outputs are 8 adjacent
 // columns per tile pair and C is loaded and dC stored 16 bytes at a time.
-template <int P, int N>
-__global__ __launch_bounds__(256, 4) void bwd_dc_bf16_kernel(
+template <int P, int N, int W>
+__global__ __launch_bounds__(W * 64, 4) void bwd_dc_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ DY, const uint16_t* __restrict__ dCBg,
     const float* __restrict__ acs, const uint16_t* __restrict__ Hs, uint16_t* __restrict__ dC,
     float* __restrict__ rout) {
   constexpr int LDB = N + 16;  // odd multiple of 32 bytes for the transpose reads
   constexpr int ROWS = P > 64 ? P : 64;
-  constexpr int NPH = (P * N / 8 + 255) / 256;  // 16-byte pieces of H per thread
+  constexpr int NT = W * 64, RW = 16 * W;      // threads; rows per workgroup
+  constexpr int NPH = (P * N / 8 + NT - 1) / NT;  // 16-byte pieces of H per thread
   __shared__ __attribute__((aligned(16))) uint16_t ub[2][ROWS * LDB];
-  const int T = m.Q / 64;
+  const int T = m.Q / RW;
   const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
   const int tile = lid % T, k = lid / T / G, g = (lid / T) % G;
   const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0 || tile * 64 >= ci.len) return;
+  if (ci.len <= 0 || tile * RW >= ci.len) return;
   const int Q = m.Q, len = ci.len;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, r = lane & 15;
@@ -814,7 +818,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dc_bf16_kernel(
   const uint16_t* bb = Bm + (int64_t)ci.start * brow + (int64_t)g * N;
   const uint16_t* cb = Cm + (int64_t)ci.start * brow + (int64_t)g * N;
   const uint16_t* dcb = dCBg + ((int64_t)k * G + g) * Q * Q;
-  const int i0 = tile * 64 + w * 16;
+  const int i0 = tile * RW + w * 16;
   const bool active = i0 < len;
   const int irow = i0 + r;
   // buffer resources over the chunk's valid rows (rows past the end: zero, not written)
@@ -826,11 +830,11 @@ __global__ __launch_bounds__(256, 4) void bwd_dc_bf16_kernel(
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* bt = ub[0];
-  for (int jt = 0; jt <= tile; ++jt) {
+  for (int jt = 0; jt * 64 < tile * RW + RW && jt * 64 < len; ++jt) {
     // this piece's B rows and this lane's two dCB_g fragments, all in flight
     // together (one memory latency per piece); fragments past the row block's
     // causal end are not needed
-    RowTile<64, N, 256, true> btile;
+    RowTile<64, N, NT, true> btile;
     btile.load(bb + (int64_t)jt * 64 * brow, brow, len - jt * 64, tid);
     const int jend = min(jt * 64 + 64, i0 + 16);
     u32x4 af[2];
@@ -865,7 +869,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dc_bf16_kernel(
     const brsrc rh = make_rsrc(Hs + kh * (int64_t)(P * N), (uint32_t)(P * N * 2));
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
-      const int e = (tid + c * 256) * 8;
+      const int e = (tid + c * NT) * 8;
       ph[c] = buf_load16(rh, e < P * N ? (uint32_t)e * 2u : 0x80000000u);
     }
     const brsrc rdy = make_rsrc(DY + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
@@ -889,7 +893,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dc_bf16_kernel(
     for (int s = 0; s < N / 32; ++s) asm volatile("" : "+v"(cq[s]));
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
-      const int e = (tz + c * 256) * 8;
+      const int e = (tz + c * NT) * 8;
       if (e < P * N) lds_piece<true>(ht + (e / N) * LDB, (e % N) / 8, ph[c]);
     }
     __syncthreads();
@@ -926,8 +930,9 @@ __global__ __launch_bounds__(256, 4) void bwd_dc_bf16_kernel(
 }
 
 // ------------------------------------------------------------ bwd_db bf16 ----
-// One workgroup per (chunk, group, 64 rows j).  dB_j = sum_{i>=j} dCB_g[i][j] C_i
-// (per 64-row piece of i: the piece's C rows and its 64 x 64 tile of dCB_g
+// One workgroup of W waves per (chunk, group, 16 W rows j), W = 8 or 4 as for dC
+// (each head's dT tile staged once per 128 rows).  dB_j = sum_{i>=j} dCB_g[i][j] C_i
+// (per 64-row piece of i: the piece's C rows and its 64 x 16 W tile of dCB_g
 // staged in LDS, the tile read with the transpose read, which hands each lane
 // dCB_g down a column j)
 // + sum_h w_j delta_j dT^T x_j (one K=headdim GEMM per head).  Per head, dT = dE_c
@@ -935,22 +940,23 @@ __global__ __launch_bounds__(256, 4) void bwd_dc_bf16_kernel(
 // fragments and decay scalars are loaded into registers while this head is
 // worked on.  Operands swapped and C, dT staged in the permuted column order as
 // in bwd_dc: each lane owns one row j and stores dB 16 bytes at a time.
-template <int P, int N>
-__global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
+template <int P, int N, int W>
+__global__ __launch_bounds__(W * 64, 4) void bwd_db_bf16_kernel(
     ChunkMap m, int H, int G, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dCBg, const float* __restrict__ delta,
     const float* __restrict__ acs, const uint16_t* __restrict__ dE, uint16_t* __restrict__ dB) {
   constexpr int LDB = N + 16;
   constexpr int ROWS = P > 64 ? P : 64;
-  constexpr int NPH = (P * N / 8 + 255) / 256;
-  constexpr int LDT = 64 + 8;  // dCB_g tile row stride (bf16)
+  constexpr int NT = W * 64, RW = 16 * W;  // threads; rows per workgroup
+  constexpr int NPH = (P * N / 8 + NT - 1) / NT;
+  constexpr int LDT = RW + 8;  // dCB_g tile row stride (bf16)
   constexpr int UB = ROWS * LDB > 64 * LDT ? ROWS * LDB : 64 * LDT;
   __shared__ __attribute__((aligned(16))) uint16_t ub[2][UB];
-  const int T = m.Q / 64;
+  const int T = m.Q / RW;
   const int lid = xcd_order(blockIdx.x, gridDim.x);  // (chunk, group, tile), tile fastest
   const int tile = lid % T, k = lid / T / G, g = (lid / T) % G;
   const ChunkInfo ci = chunk_info(m, k);
-  if (ci.len <= 0 || tile * 64 >= ci.len) return;
+  if (ci.len <= 0 || tile * RW >= ci.len) return;
   const int Q = m.Q, len = ci.len;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, r = lane & 15;
@@ -958,7 +964,7 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
   const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
   const uint16_t* cb = Cm + (int64_t)ci.start * brow + (int64_t)g * N;
   const uint16_t* dcbg = dCBg + ((int64_t)k * G + g) * Q * Q;
-  const int j0 = tile * 64 + w * 16;
+  const int j0 = tile * RW + w * 16;
   const bool active = j0 < len;
   const int jrow = j0 + r;
   const bool rowok = jrow < len;
@@ -968,20 +974,20 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t *ct = ub[0], *dt_ = ub[1];
-  for (int it = tile; it * 64 < len; ++it) {
+  for (int it = tile * RW / 64; it * 64 < len; ++it) {
     // C rows of this piece and dCB_g[it-piece rows i][this tile's columns j]
     // (rows past the chunk's end zero; the diagonal tile is zero above i = j),
     // both in flight together: one memory latency per piece
-    RowTile<64, N, 256, true> ctile;
-    RowTile<64, 64, 256> dtile;
+    RowTile<64, N, NT, true> ctile;
+    RowTile<64, RW, NT> dtile;
     ctile.load(cb + (int64_t)it * 64 * brow, brow, len - it * 64, tid);
-    dtile.load(dcbg + (int64_t)it * 64 * Q + tile * 64, Q, len - it * 64, tid);
+    dtile.load(dcbg + (int64_t)it * 64 * Q + tile * RW, Q, len - it * 64, tid);
     __syncthreads();  // every wave is done with the previous piece
     ctile.store(ct, LDB, tid);
     dtile.store(dt_, LDT, tid);
     __syncthreads();
     if (!active) continue;
-    const int ib0 = (it == tile) ? (j0 / 32) * 32 : it * 64;
+    const int ib0 = max(it * 64, (j0 / 32) * 32);  // rows i >= this wave's first 32-block
     for (int ib = ib0; ib < min(it * 64 + 64, len); ib += 32) {
       // a[j][i] = dCB_g[i][j]: tile rows are k = i, the lane's column is j0 + r
       const bf16x8 a = frag_kmajor(dt_ + (ib - it * 64) * LDT + w * 16, LDT, lane);
@@ -998,7 +1004,7 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
     const brsrc rh = make_rsrc(dE + kh * (int64_t)(P * N), (uint32_t)(P * N * 2));
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
-      const int e = (tid + c * 256) * 8;
+      const int e = (tid + c * NT) * 8;
       ph[c] = buf_load16(rh, e < P * N ? (uint32_t)e * 2u : 0x80000000u);
     }
     const brsrc rxh = make_rsrc(X + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
@@ -1016,7 +1022,7 @@ __global__ __launch_bounds__(256, 4) void bwd_db_bf16_kernel(
     uint16_t* dtt = ub[hh & 1];
 #pragma unroll
     for (int c = 0; c < NPH; ++c) {
-      const int e = (tid + c * 256) * 8;
+      const int e = (tid + c * NT) * 8;
       if (e < P * N) lds_piece<true>(dtt + (e / N) * LDB, (e % N) / 8, ph[c]);
     }
     __syncthreads();
@@ -1235,13 +1241,24 @@ static void launch_bwd_bf16(const Prob& p, const BwdArgs& a, int which, hipStrea
                        (const uint16_t*)a.dout, (const uint16_t*)a.CB, a.delta, a.acs,
                        (uint16_t*)a.dCBg, a.Rp, a.Kp);
   }
-  if (!which || which == 3)
-  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
+  // dC and dB: 128 rows per workgroup (eight waves) where the chunk size allows
+  const bool r128 = p.Q % 128 == 0;
+  if ((!which || which == 3) && r128)
+  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N, 8>), dim3((unsigned)(p.nck * p.G * (p.Q / 128))), dim3(512), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
                      (const uint16_t*)a.dout, (const uint16_t*)a.dCBg, a.acs, (const uint16_t*)a.Hp,
                      (uint16_t*)a.dC, a.rR);
-  if (!which || which == 4)
-  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
+  if ((!which || which == 3) && !r128)
+  hipLaunchKernelGGL((bwd_dc_bf16_kernel<P, N, 4>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
+                     p.map, p.H, p.G, (const uint16_t*)a.B, (const uint16_t*)a.C,
+                     (const uint16_t*)a.dout, (const uint16_t*)a.dCBg, a.acs, (const uint16_t*)a.Hp,
+                     (uint16_t*)a.dC, a.rR);
+  if ((!which || which == 4) && r128)
+  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N, 8>), dim3((unsigned)(p.nck * p.G * (p.Q / 128))), dim3(512), 0, st,
+                     p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
+                     (const uint16_t*)a.dCBg, a.delta, a.acs, (const uint16_t*)a.dE, (uint16_t*)a.dB);
+  if ((!which || which == 4) && !r128)
+  hipLaunchKernelGGL((bwd_db_bf16_kernel<P, N, 4>), dim3((unsigned)(p.nck * p.G * T)), dim3(256), 0, st,
                      p.map, p.H, p.G, (const uint16_t*)a.x, (const uint16_t*)a.C,
                      (const uint16_t*)a.dCBg, a.delta, a.acs, (const uint16_t*)a.dE, (uint16_t*)a.dB);
 }

@@ -28,8 +28,10 @@ KERNELS = [
     ("k_bwd.hip", "_ZN3ssd18bwd_dx_bf16_kernelILi64ELi128EEE"),
     ("k_bwd.hip", "_ZN3ssd24bwd_dcb_t128_bf16_kernelILi64EEE"),  # chunk 256: 128x128 super-tiles
     ("k_bwd.hip", "_ZN3ssd19bwd_dcb_bf16_kernelILi64EEE"),        # chunk 64: 64x64 tiles
-    ("k_bwd.hip", "_ZN3ssd18bwd_dc_bf16_kernelILi64ELi128EEE"),
-    ("k_bwd.hip", "_ZN3ssd18bwd_db_bf16_kernelILi64ELi128EEE"),
+    ("k_bwd.hip", "_ZN3ssd18bwd_dc_bf16_kernelILi64ELi128ELi8EEE"),  # 128 rows per workgroup
+    ("k_bwd.hip", "_ZN3ssd18bwd_db_bf16_kernelILi64ELi128ELi8EEE"),
+    ("k_bwd.hip", "_ZN3ssd18bwd_dc_bf16_kernelILi64ELi128ELi4EEE"),  # 64 rows (chunk 64)
+    ("k_bwd.hip", "_ZN3ssd18bwd_db_bf16_kernelILi64ELi128ELi4EEE"),
     ("k_bwd.hip", "_ZN3ssd19bwd_finalize_kernelE"),
     ("k_bmm.hip", "_ZN3ssd21bmm_chunk_bf16_kernelILi128ELb1EEE"),  # shapes without C.B^T in chunk_state
     # the state passing the tuned table picks at the layer and packed workloads
