@@ -303,7 +303,7 @@ class Workload:
             step = lambda fn=fn: (self.fwd_save(), fn())
             smed = tm.trials(step, per)[0]
             res[key] = {"bwd_ms": round(med, 4), "bwd_ms_min": round(lo, 4), "bwd_ms_max": round(hi, 4),
-                        "bwd_ms_cold": round(tm.cold(fn), 4), "step_ms": round(smed, 4)}
+                        "bwd_ms_cold": round(tm.cold(fn, wait=True), 4), "step_ms": round(smed, 4)}
             print("bench: backward %-10s %.4f ms (step %.4f ms)" % (key, med, smed), file=sys.stderr, flush=True)
         self.bwd_saved()  # the gradients of the default path again
         return res
@@ -326,7 +326,7 @@ class Workload:
                 med, lo, hi = tm.trials(fn, per)
                 e = res.setdefault("save" if save else "plain", {})
                 e[key] = {"ms": round(med, 4), "ms_min": round(lo, 4), "ms_max": round(hi, 4),
-                          "ms_cold": round(tm.cold(fn), 4)}
+                          "ms_cold": round(tm.cold(fn, wait=True), 4)}
                 print("bench: forward %s %-8s %.4f ms" % ("save " if save else "plain", key, med),
                       file=sys.stderr, flush=True)
         self.fwd_save()  # the workspace holds the default path's intermediates again
@@ -446,14 +446,22 @@ class Timer:
         res.sort()
         return res[n // 2], res[0], res[-1]
 
-    def cold(self, fn, n=7):
+    def cold(self, fn, n=7, wait=False):
         """median ms of single calls, each after a 512 MiB read (outside the event pair)
-        that replaces the last-level cache's contents with clean lines"""
+        that replaces the last-level cache's contents with clean lines.  A single
+        kernel is issued right behind the read, long before the read ends.  wait: the
+        host waits for the read first, for calls of many kernels (a training step's
+        launches take the host about as long, ~0.1 ms, as the read takes the GPU, so
+        issued right behind it, later launches could arrive after the GPU had run dry
+        and that idle time would be timed; after the wait only the first launch's
+        issue is)."""
         torch = self.torch
         st = torch.cuda.current_stream()
         res = []
         for _ in range(n):
             self.flush.sum()
+            if wait:
+                torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(st)
             fn()
@@ -516,13 +524,13 @@ def other_workload(cfg_id, dev, tm, steps, label, ab=True):
                                  w.H, w.P, w.N, w.G, w.Q),
            "input_sha256": w.sha256,
            "fwd": {"ms": round(fwd_med, 4), "ms_min": round(fwd_min, 4), "ms_max": round(fwd_max, 4),
-                   "ms_cold": round(tm.cold(w.fwd), 4),
+                   "ms_cold": round(tm.cold(w.fwd, wait=True), 4),
                    "tokens/s": round(w.tokens / (fwd_med * 1e-3), 1)}}
     print("bench: %s fwd %.3f ms" % (label, fwd_med), file=sys.stderr, flush=True)
     if w.with_bwd:
         st_med, st_min, st_max = tm.trials(w.step, per)
         res["fwd_bwd"] = {"ms": round(st_med, 4), "ms_min": round(st_min, 4), "ms_max": round(st_max, 4),
-                          "ms_cold": round(tm.cold(w.step), 4),
+                          "ms_cold": round(tm.cold(w.step, wait=True), 4),
                           "tokens/s": round(w.tokens / (st_med * 1e-3), 1),
                           "bwd_ms": round(tm.trials(w.bwd_saved, per)[0], 4)}
         print("bench: %s fwd+bwd %.3f ms" % (label, st_med), file=sys.stderr, flush=True)
@@ -606,7 +614,7 @@ def main():
     tokens = w.tokens
     print("bench: step %.3f ms (wall %.3f), fwd %.3f ms" % (ms_step, wall_step, ms_fwd), file=sys.stderr, flush=True)
     step_med, step_min, step_max = tm.trials(w.step, max(1, args.steps // 2))
-    step_cold = tm.cold(w.step)
+    step_cold = tm.cold(w.step, wait=True)
     print("bench: step over 7 trials: median %.3f ms (min %.3f, max %.3f); cold %.3f ms"
           % (step_med, step_min, step_max, step_cold), file=sys.stderr, flush=True)
 
@@ -706,7 +714,8 @@ def main():
         "step_trials": {"median_ms": round(step_med, 4), "min_ms": round(step_min, 4),
                         "max_ms": round(step_max, 4), "cold_ms": round(step_cold, 4),
                         "note": "7 windows of steps/2 back-to-back steps; cold = single steps "
-                                "after a 512 MiB read that evicts the last-level cache"},
+                                "after a 512 MiB read that evicts the last-level cache (the host "
+                                "waits for the read, then issues the step)"},
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
