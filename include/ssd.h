@@ -325,7 +325,14 @@ ssd_status ssd_bwd(const ssd_problem* problem,
  *     states, passed (nck, nheads, headdim, dstate): chunk-local end state T_c, and
  *                    the state H_c entering each chunk
  *     CB             (nck, ngroups, chunk_size, chunk_size) io dtype: C_i . B_j for
- *                    j <= i (entries above the diagonal are not written)
+ *                    j <= i (entries above the diagonal are not written).  Where
+ *                    the bf16 matrix-core kernels run (bf16 io, headdim and dstate
+ *                    >= 32) each chunk's Q x Q matrix is stored in fragment order:
+ *                    element (i, j) at offset ((i/16)(Q/32) + j/32) 512
+ *                    + ((j%32)/8 16 + i%16) 8 + j%8, i.e. 16 x 32 blocks of 1 KB, each
+ *                    laid out as the 64 lanes of an MFMA operand load read it; the
+ *                    fp32 matrix-core kernels store it row-major.  ssd_stage_bmm_chunk
+ *                    writes and ssd_stage_chunk_scan reads the same order.
  */
 /* Stage 1 — per-chunk cumulative sum of delta*A (wavefront prefix sum): the
  * log-decays of the recurrence (scan page, section 1) summed within each chunk of

@@ -137,6 +137,26 @@ __device__ __forceinline__ void buf_store16(brsrc r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 0);
 }
 
+// ------------------------------------------------- C.B^T fragment order ----
+// A chunk's C.B^T (and its transpose) on the bf16 path is a Q x Q bf16 matrix
+// stored as 16 x 32 blocks of 1 KB, in the order an MFMA A-operand load reads
+// them: block (R, S) = rows 16R..16R+15, columns 32S..32S+31 at element offset
+// (R * Q/32 + S) * 512, and inside it the 16 bytes of lane l = 16 q + r holding
+// the 8 consecutive columns 32S + 8q .. +7 of row 16R + r.
+// A wave's fragment load is then 1 KB contiguous (8 whole 128-byte lines), where
+// row-major storage makes it 16 half-lines of 16 rows: with most of these reads
+// hitting the L2 (a group's heads share the matrix), the texture address unit
+// and the L1 then take about twice as long per load.  Row block R occupies the
+// same bytes as rows 16R..16R+15 of the row-major matrix, so a range check that
+// ends at a whole row block keeps the "rows past the end" rule.
+__host__ __device__ __forceinline__ uint32_t cbf_off(int i, int j, int Q) {  // element offset of (i, j)
+  return (uint32_t)(((i >> 4) * (Q >> 5) + (j >> 5)) * 512 + (((j & 31) >> 3) * 16 + (i & 15)) * 8 + (j & 7));
+}
+// byte offset of the 16-byte piece that lane (q, r) loads of block (R, S)
+__host__ __device__ __forceinline__ uint32_t cbf_piece(int R, int S, int lane, int Q) {
+  return (uint32_t)((R * (Q >> 5) + S) * 1024 + lane * 16);
+}
+
 // ---------------------------------------------- column order of MFMA rows ----
 // A row of W outputs (W a multiple of 32) computed as W/16 transposed 16x16
 // tiles, the column index coming from a K-major LDS operand read with

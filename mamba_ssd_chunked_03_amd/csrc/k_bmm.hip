@@ -8,7 +8,9 @@
 // (16 bytes per lane) without LDS staging.  Tiles above the diagonal are never
 // computed; inside diagonal tiles the upper part is written but unspecified.
 // The backward also reads the transpose, CBt[j][i] = CB[i][j]: when asked, each
-// lower tile is stored a second time, transposed, from the same LDS copy.
+// lower tile is stored a second time, transposed, from the same LDS copy.  Both
+// are stored in fragment order (common.hpp, cbf_off): each store instruction of
+// a wave writes one 1 KB block.
 //
 // fp32 path: k_f32.hip (fp32 matrix cores).
 #include "internal.hpp"
@@ -16,9 +18,10 @@
 namespace ssd {
 
 // out[a][b] = R_a . S_b on the lower tile triangle.
-// Each wavefront's 64x64 tile goes through LDS so every store is a 16-byte row
-// piece; with DUAL the transposed tile is stored too (outT[b][a]), which the
-// backward reads when the forward keeps its intermediates.
+// Each wavefront's 64x64 tile goes through LDS so that every store instruction
+// writes one 16 x 32 block in fragment order; with DUAL the transposed tile is
+// stored too (outT[b][a]), which the backward reads when the forward keeps its
+// intermediates.
 template <int N, bool DUAL>
 __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
                                                              const uint16_t* __restrict__ Sm,
@@ -77,16 +80,20 @@ __global__ __launch_bounds__(256) void bmm_chunk_bf16_kernel(ChunkMap m, int G,
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) tl[(a * 16 + q * 4 + rr) * LT + b * 16 + r] = f2bf(acc[a][b][rr]);
     __builtin_amdgcn_wave_barrier();
+    // block (rr, cc) of the tile: lane (q, r) holds row 16 rr + r, columns
+    // 32 cc + 8 q .. +7 (and of the transposed tile, row and column swapped)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int e = lane + 64 * c, rw = e >> 3, c8 = e & 7;
-      *(u32x4*)(out + (int64_t)(ti * 64 + rw) * Q + tj * 64 + c8 * 8) = *(const u32x4*)(tl + rw * LT + c8 * 8);
+      const int rr = c >> 1, cc = c & 1;
+      *(u32x4*)((char*)out + cbf_piece(ti * 4 + rr, tj * 2 + cc, lane, Q)) =
+          *(const u32x4*)(tl + (rr * 16 + r) * LT + cc * 32 + q * 8);
       if (DUAL) {
         u32x4 t;
 #pragma unroll
         for (int d = 0; d < 4; ++d)
-          t[d] = (uint32_t)tl[(c8 * 8 + 2 * d) * LT + rw] | ((uint32_t)tl[(c8 * 8 + 2 * d + 1) * LT + rw] << 16);
-        *(u32x4*)(CBt + ((int64_t)k * G + g) * Q * Q + (int64_t)(tj * 64 + rw) * Q + ti * 64 + c8 * 8) = t;
+          t[d] = (uint32_t)tl[(cc * 32 + q * 8 + 2 * d) * LT + rr * 16 + r] |
+                 ((uint32_t)tl[(cc * 32 + q * 8 + 2 * d + 1) * LT + rr * 16 + r] << 16);
+        *(u32x4*)((char*)(CBt + ((int64_t)k * G + g) * Q * Q) + cbf_piece(tj * 4 + rr, ti * 2 + cc, lane, Q)) = t;
       }
     }
     __builtin_amdgcn_wave_barrier();

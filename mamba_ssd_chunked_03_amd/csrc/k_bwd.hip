@@ -88,20 +88,20 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
   // Buffer resources over the chunk's valid rows: rows past its end read as
   // zero and are not written.
   const brsrc rx = make_rsrc(xb, (uint32_t)(len * xrow * 2)), rbm = make_rsrc(bb, (uint32_t)(len * brow * 2));
-  const brsrc rc = make_rsrc(cbt, (uint32_t)(len * Q * 2));
+  const brsrc rc = make_rsrc(cbt, (uint32_t)(((len + 15) & ~15) * Q * 2));  // fragment order: whole 16-row blocks
   const brsrc rdx = make_rsrc(DX + (int64_t)ci.start * xrow + (int64_t)h * P, (uint32_t)(len * xrow * 2));
   u32x4 px[P / 32];  // x_j, the lane's 8 adjacent columns per tile pair (pcol)
   u32x4 bq[N / 32], pc1, pcd;
   auto load_rb = [&](int rb) {
     const uint32_t jr = rb * 16 + r, c0 = rb / 2;
     const uint32_t xo = jr * (uint32_t)(xrow * 2) + q * 16, bo = jr * (uint32_t)(brow * 2) + q * 16;
-    const uint32_t co = jr * (uint32_t)(Q * 2) + q * 16;
+    const uint32_t co = cbf_piece(rb, 0, q * 16 + r, Q);  // CBt block (rb, sx) at co + 1024 sx
 #pragma unroll
     for (int s = 0; s < P / 32; ++s) px[s] = buf_load16(rx, xo + 64 * s);
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk) bq[kk] = buf_load16(rbm, bo + 64 * kk);
-    pc1 = buf_load16(rc, co + (c0 + 1) * 64);  // (unused when no later block exists)
-    pcd = buf_load16(rc, co + c0 * 64);
+    pc1 = buf_load16(rc, co + (c0 + 1) * 1024);  // (unused when no later block exists)
+    pcd = buf_load16(rc, co + c0 * 1024);
   };
   if (live(0)) load_rb(rb_of(0));
   // every prologue load in flight before the first LDS store waits on one:
@@ -198,10 +198,10 @@ __global__ __launch_bounds__(kDxWaves * 64, 4) void bwd_dx_bf16_kernel(
       for (int tp = 0; tp < P / 16; ++tp) acc[tp] *= s0;
       const float* wrow = &wt[cb0][0];
       u32x4 cvn = pc1;
-      const uint32_t co = (uint32_t)jrow * (uint32_t)(Q * 2) + q * 16;
+      const uint32_t co = cbf_piece(rb, 0, q * 16 + r, Q);
       for (int sx = cb0 + 1; sx < s_end; ++sx) {
         const u32x4 cv = cvn;
-        if (sx + 1 < s_end) cvn = buf_load16(rc, co + (sx + 1) * 64);  // one step of lookahead
+        if (sx + 1 < s_end) cvn = buf_load16(rc, co + (sx + 1) * 1024);  // one step of lookahead
         const float4 f0 = *(const float4*)(wrow + sx * 32 + q * 8);
         const float4 f1 = *(const float4*)(wrow + sx * 32 + q * 8 + 4);
         u32x4 av;
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256, 4) void bwd_dcb_bf16_kernel(
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
-      const float c = bf2f(cbm[(int64_t)i * Q + j]);
+      const float c = bf2f(cbm[cbf_off(i, j, Q)]);  // (fragment order)
       cbv[b][rr] = (i < len && j < i) ? c : 0.f;
     }
   f32x4 sum[4];
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kT128Waves * 64, 4) void bwd_dcb_t128_bf16_kernel(
     for (int rr = 0; rr < 4; ++rr) {
       const int i = i0 + q * 4 + rr, j = jt0 + b * 16 + r;
       const bool ok = live && b < nblk && i < len && j < i;
-      v[rr] = __builtin_amdgcn_raw_buffer_load_b16(rcb, ok ? (uint32_t)(i * Q + j) * 2u : 0x80000000u, 0, 0);
+      v[rr] = __builtin_amdgcn_raw_buffer_load_b16(rcb, ok ? cbf_off(i, j, Q) * 2u : 0x80000000u, 0, 0);
     }
     cbp[b][0] = v[0] | (v[1] << 16);
     cbp[b][1] = v[2] | (v[3] << 16);

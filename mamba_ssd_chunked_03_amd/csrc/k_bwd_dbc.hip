@@ -116,7 +116,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dbc_bf16_kernel(
           for (int u = 0; u < 2; ++u) {
             const int a = t0 + rowA + 2 * h2 + u, o = s * 64 + ccol(c);
             const int i = s <= rb ? a : o, j = s <= rb ? o : a;
-            const uint32_t cv = cbm[(int64_t)i * Q + j];
+            const uint32_t cv = cbm[cbf_off(i, j, Q)];  // (fragment order)
             v |= ((i < len && j < i) ? cv : 0u) << (16 * u);
           }
         }

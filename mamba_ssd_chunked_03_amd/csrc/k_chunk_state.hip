@@ -250,7 +250,8 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
       // (lq, r) holds CB[i = r][j = 4 lq .. +3] of its 16 x 16 block, with C
       // first CB[i = 4 lq .. +3][j = r], i.e. CBt[j][i .. i + 3].  The two
       // 64 x 64 tiles go through LDS, then each thread stores one 16-byte piece
-      // of each: every store instruction writes 8 whole 128-byte rows.
+      // of each in fragment order (common.hpp, cbf_off): wave f writes block
+      // (f / 2, f % 2) of each tile, 1 KB contiguous per store instruction.
       if (fuse_cb && s0 / KS <= ib) {
         const int il = ri * 16;
 #pragma unroll
@@ -268,10 +269,12 @@ __global__ __launch_bounds__(256 * HP, 4) void chunk_state_bf16_kernel(ChunkMap 
         }
         __syncthreads();
         const int64_t kg = (int64_t)k * G + g;
-        const int row = gid >> 3, c16 = gid & 7;  // 512 threads: 64 rows x 8 pieces
-        *(u32x4*)(cs.CB + (kg * Q + ib * 64 + row) * Q + s0 + c16 * 8) = *(const u32x4*)(tcb + row * LT + c16 * 8);
+        // 512 threads: 8 blocks of 16 rows x 32 columns, lane (q, r) = row r, columns 8q .. +7
+        const int f = gid >> 6, fl = gid & 63, rr = f >> 1, cc = f & 1, fq = fl >> 4, fr = fl & 15;
+        const int lo = (rr * 16 + fr) * LT + cc * 32 + fq * 8;
+        *(u32x4*)((char*)(cs.CB + kg * Q * Q) + cbf_piece(ib * 4 + rr, s0 / 32 + cc, fl, Q)) = *(const u32x4*)(tcb + lo);
         if (cs.CBt)
-          *(u32x4*)(cs.CBt + (kg * Q + s0 + row) * Q + ib * 64 + c16 * 8) = *(const u32x4*)(tcbt + row * LT + c16 * 8);
+          *(u32x4*)((char*)(cs.CBt + kg * Q * Q) + cbf_piece(s0 / 16 + rr, ib * 2 + cc, fl, Q)) = *(const u32x4*)(tcbt + lo);
       }
     }
     __syncthreads();

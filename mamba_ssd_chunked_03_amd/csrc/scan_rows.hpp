@@ -41,7 +41,8 @@ struct ScanRows {
   float Dh;
   u32x4 cf[N / 32], cbf[QMAX / 32], cbd;
 
-  // cb: the chunk's C rows of its group; cbm: its C.B^T (Q x Q); yb: its y rows
+  // cb: the chunk's C rows of its group; cbm: its C.B^T (Q x Q, fragment order:
+  // common.hpp, cbf_off); yb: its y rows
   __device__ __forceinline__ void init(const uint16_t* cb, int64_t crow, const uint16_t* cbm,
                                        uint16_t* yb, int64_t xrow_, int Q_, int len_, int tid,
                                        float Dh_) {
@@ -56,7 +57,7 @@ struct ScanRows {
     NB = Q / 16;
     nii = (NB + NW - 1) / NW;
     rcm = make_rsrc(cb, (uint32_t)(len * crow * 2));
-    rcb = make_rsrc(cbm, (uint32_t)(len * Q * 2));
+    rcb = make_rsrc(cbm, (uint32_t)(((len + 15) & ~15) * Q * 2));  // whole 16-row blocks
     ry = make_rsrc(yb, (uint32_t)(len * xrow * 2));
     crow_ = crow;
   }
@@ -72,13 +73,14 @@ struct ScanRows {
   // all C and C.B^T fragments of a row block, in flight together (one memory latency)
   __device__ __forceinline__ void load_rb(int rb) {
     const uint32_t irow = rb * 16 + r, nb = rb / 2;
-    const uint32_t co = irow * (uint32_t)(crow_ * 2) + q * 16, bo = irow * (uint32_t)(Q * 2) + q * 16;
+    const uint32_t co = irow * (uint32_t)(crow_ * 2) + q * 16;
+    const uint32_t bo = cbf_piece(rb, 0, q * 16 + r, Q);  // block (rb, sx) at bo + 1024 sx
 #pragma unroll
     for (int kb = 0; kb < N / 32; ++kb) cf[kb] = buf_load16(rcm, co + 64 * kb);
 #pragma unroll
     for (int sx = 0; sx < QMAX / 32; ++sx)
-      cbf[sx] = (sx < (int)nb) ? buf_load16(rcb, bo + 64 * sx) : u32x4{0u, 0u, 0u, 0u};
-    cbd = buf_load16(rcb, bo + 64 * nb);
+      cbf[sx] = (sx < (int)nb) ? buf_load16(rcb, bo + 1024 * sx) : u32x4{0u, 0u, 0u, 0u};
+    cbd = buf_load16(rcb, bo + 1024 * nb);
   }
   __device__ __forceinline__ void prefetch_first() {
     if (live(0)) load_rb(rb_of(0));

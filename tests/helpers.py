@@ -92,3 +92,30 @@ def packed_sequences(inp, seqs):
     lens = [cu[s + 1] - cu[s] for s in seqs]
     out["cu_seqlens"] = inputs.cu_from_lengths(lens)
     return out, toks
+
+
+def bf16_kernels(io, headdim, dstate):
+    """Whether a problem runs on the bf16 matrix-core kernels (the rest run on the
+    fp32 ones): they store C.B^T in fragment order (include/ssd.h)."""
+    return io == "bf16" and headdim >= 32 and dstate >= 32
+
+
+def cb_rows(cb, Q):
+    """C.B^T (..., Q, Q) in fragment order -> row-major (a tensor or an array)."""
+    lead = tuple(cb.shape[:-2])
+    f = cb.reshape(lead + (Q // 16, Q // 32, 4, 16, 8))  # (R, S, q, r, e) = [16R + r][32S + 8q + e]
+    n = len(lead)
+    perm = tuple(range(n)) + (n, n + 3, n + 1, n + 2, n + 4)  # -> (R, r, S, q, e)
+    f = f.permute(perm) if hasattr(f, "permute") else f.transpose(perm)
+    return f.reshape(lead + (Q, Q))
+
+
+def cb_frag(cb, Q):
+    """Row-major C.B^T (..., Q, Q) -> fragment order (the inverse of cb_rows)."""
+    lead = tuple(cb.shape[:-2])
+    f = cb.reshape(lead + (Q // 16, 16, Q // 32, 4, 8))  # (R, r, S, q, e)
+    n = len(lead)
+    perm = tuple(range(n)) + (n, n + 2, n + 3, n + 1, n + 4)  # -> (R, S, q, r, e)
+    f = f.permute(perm) if hasattr(f, "permute") else f.transpose(perm)
+    return f.reshape(lead + (Q, Q))
+

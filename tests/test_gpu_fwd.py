@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (LOG2E, bf16_excess, gpu_fwd, has_gpu, normwise, np64, oracle_args, to_dev)
+from helpers import (LOG2E, bf16_excess, bf16_kernels, cb_frag, cb_rows, gpu_fwd, has_gpu, normwise, np64,
+                     oracle_args, to_dev)
 from mamba_ssd_chunked_03_amd import inputs
 from oracle import chunked, recurrence
 
@@ -202,8 +203,10 @@ def test_stages(kw, lengths, Q):
                                      len(lengths) if lengths else kw["batch"], o["init"])
     assert normwise(np64(Hp)[:nk], mid["Hin"]) <= 1e-5
     assert normwise(np64(final), f_ref) <= 1e-5
-    # stage 4: C B^T (lower triangle)
+    # stage 4: C B^T (lower triangle; fragment order on the bf16 kernels, include/ssd.h)
+    frag = bf16_kernels(kw["io"], kw["headdim"], kw["dstate"])
     CB = np64(st.bmm_chunk(d["B"], d["C"]))[:nk]
+    CB = cb_rows(CB, Q) if frag else CB
     mask = np.tril(np.ones((Q, Q), dtype=bool))
     lim = 1e-5 if kw["io"] == "f32" else 4e-3
     for k, ch in enumerate(mid["chunks"]):
@@ -212,7 +215,8 @@ def test_stages(kw, lengths, Q):
         assert normwise(CB[k][:, :n, :n][:, m], mid["CB"][k][:, :n, :n][:, m]) <= lim
     # stage 5: output from the oracle's intermediates
     CBt = torch.tensor(pad(mid["CB"]), dtype=d["x"].dtype, device="cuda")
-    y = st.chunk_scan(d["x"], d["C"], CBt, o_delta, o_acs, f32(pad(mid["Hin"])), d["D"])
+    y = st.chunk_scan(d["x"], d["C"], cb_frag(CBt, Q).contiguous() if frag else CBt, o_delta, o_acs,
+                      f32(pad(mid["Hin"])), d["D"])
     torch.cuda.synchronize()
     y_ref = chunked.chunk_scan(o["x"], o["C"], np64(CBt.float()), mid["delta"], mid["acs"],
                                mid["Hin"], mid["chunks"], o["D"])
@@ -314,6 +318,8 @@ def test_cb_in_chunk_state_matches_stage_kernel(lengths):
     o += _up((16 + nck * H) * 4)  # the chained forward's flags (end of the forward part)
     cbt = ws[o:o + ncb * 2].view(torch.int16).view(nck, G, Q, Q).cpu()
     ref = ref.view(torch.int16).cpu()
+    # all three in fragment order (include/ssd.h); compared as rows
+    cb, cbt, ref = cb_rows(cb, Q), cb_rows(cbt, Q), cb_rows(ref, Q)
     # chunk lengths: batched rows cut from their first token, packed sequences likewise
     lens = []
     if packed:
