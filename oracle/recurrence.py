@@ -125,6 +125,10 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None,
     Keys: dx, ddt (w.r.t. the raw dt input), dA, dB, dC, dD (None when D is
     None), d_dt_bias, d_init.  With ``heads`` given, dB and dC hold only the
     contributions of those heads, and per-head outputs carry only those heads.
+    Also dA_abs, per head the sum of the absolute values of the terms that dA
+    sums: a diagnostic, not a gradient.  dA is a sum over tokens whose terms
+    can cancel to a small fraction of their size; the error of a computed sum
+    is naturally measured against the sum of its terms' magnitudes.
 
     Let G_t = dL/dS_t (total).  Walking tokens backwards:
         G_t   = dy_t C_t^T + a_{t+1} G_{t+1}    (G_last adds d_final)
@@ -151,6 +155,7 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None,
     dB = np.zeros_like(B)
     dC = np.zeros_like(C)
     dA = np.zeros(nh)
+    dA_abs = np.zeros(nh)
     dD = np.zeros(nh)
     d_init = np.zeros((len(seqs), nh, headdim, dstate))
     onehot = np.zeros((nh, ngroups))
@@ -198,6 +203,7 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None,
                 gs = np.einsum("hpn,hpn->h", G, before[k])
                 ddelta[b, t] = np.einsum("hp,hp->h", xt, GB) + Ah * a * gs
                 dA += d * a * gs
+                dA_abs += np.abs(d * a * gs)
                 dD += np.einsum("hp,hp->h", dyt, xt)
                 G = a[:, None, None] * G
         d_init[s] = G
@@ -205,5 +211,5 @@ def bwd(x, dt, A, B, C, dout, D=None, dt_bias=None, init=None, d_final=None,
     return {
         "dx": dx, "ddt": ddt, "dA": dA, "dB": dB, "dC": dC,
         "dD": None if D is None else dD,
-        "d_dt_bias": ddt.sum(axis=(0, 1)), "d_init": d_init,
+        "d_dt_bias": ddt.sum(axis=(0, 1)), "d_init": d_init, "dA_abs": dA_abs,
     }

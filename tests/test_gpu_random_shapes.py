@@ -8,7 +8,8 @@ and dstate far apart, chunks longer than the sequence, empty and one-token
 sequences); half of them are held to the bf16 matrix-core kernels.  Gates as
 elsewhere: fp32 io normwise <= 1e-4; bf16 io y within 2e-2 beyond half a bf16
 ulp (and normwise <= 1e-2 without the skip term), final states <= 1e-3,
-gradients <= 3e-2.
+gradients <= 3e-2; the per-head sums dA, d_dt_bias and dD may instead be held
+to that bar against the summed magnitudes of their terms (check_bwd).
 
 The same shapes also check what include/ssd.h promises of each opt-in form:
 one stream, every chunk-state form and the saved context give the default's
@@ -95,7 +96,21 @@ def check_fwd(kw, y, final, y_ref, f_ref, label):
         assert normwise(np64(final), f_ref) <= 1e-3, label
 
 
-def check_bwd(io, g, ref, label):
+def sum_scales(inp, ref):
+    """Per head, the summed magnitudes of the terms that dA, d_dt_bias and dD add up:
+    the oracle's dA_abs, sum |ddt| over tokens, sum |dy . x| over tokens."""
+    a = inputs.to_f64(inp)
+    sc = {"dA": ref["dA_abs"], "d_dt_bias": np.abs(ref["ddt"]).sum(axis=(0, 1))}
+    if ref["dD"] is not None:
+        sc["dD"] = np.abs(np.einsum("bthp,bthp->bth", a["dout"], a["x"])).sum(axis=(0, 1))
+    return sc
+
+
+def check_bwd(io, g, ref, label, scales=None):
+    """normwise <= tol for every gradient.  dA, d_dt_bias and dD are per-head sums
+    over tokens whose terms can cancel (with one head, dA came out at 1/84 to 1/562
+    of its terms' summed size in drawn cases): for them the error may instead be
+    measured against those summed magnitudes, the usual error measure of a sum."""
     tol = 1e-4 if io == "f32" else 3e-2
     errs = {}
     for k in KEYS:
@@ -103,6 +118,9 @@ def check_bwd(io, g, ref, label):
             assert g[k] is None or k == "dD", (label, k)
             continue
         errs[k] = normwise(np64(g[k]), ref[k])
+        if scales is not None and k in scales and float(np.max(scales[k])) > 0:
+            diff = float(np.max(np.abs(np64(g[k]) - ref[k])))
+            errs[k] = min(errs[k], diff / float(np.max(scales[k])))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, (label, errs)
 
@@ -122,7 +140,7 @@ def test_random_shape(seed, main):
     g = gpu_bwd(ssd, inp, Q)
     torch.cuda.synchronize()
     check_fwd(kw, y, final, y_ref, f_ref, label)
-    check_bwd(kw["io"], g, ref, label)
+    check_bwd(kw["io"], g, ref, label, sum_scales(inp, ref))
 
 
 def saved_workspace(inp, Q, flags=0):
@@ -176,14 +194,15 @@ def test_random_shape_opt_in_forms(seed, main):
     torch.cuda.synchronize()
     assert not same(g0, gf, ["dx", "dB", "dC", "d_init"]), (label, "fused dB/dC")
     y_ref, f_ref, ref = oracle_both(inp)
-    check_bwd(io, gf, ref, label + " fused dB/dC")
+    sc = sum_scales(inp, ref)
+    check_bwd(io, gf, ref, label + " fused dB/dC", sc)
     # a forced state-passing kernel (associative scan shapes 1-4, sequential carry 5-7)
     v = 1 + seed % 7
     ys, fs = gpu_fwd(ssd, inp, Q, scan_variant=v)
     gs = gpu_bwd(ssd, inp, Q, scan_variant=v)
     torch.cuda.synchronize()
     check_fwd(kw, ys, fs, y_ref, f_ref, "%s scan variant %d" % (label, v))
-    check_bwd(io, gs, ref, "%s scan variant %d" % (label, v))
+    check_bwd(io, gs, ref, "%s scan variant %d" % (label, v), sc)
     # the chained forward where the shape allows it; its saved context feeds the backward
     wc = saved_workspace(inp, Q)
     r = unsupported(lambda: gpu_fwd(ssd, inp, Q, chained=True, workspace=wc, save_for_backward=True))
@@ -196,4 +215,4 @@ def test_random_shape_opt_in_forms(seed, main):
         gc = gpu_bwd(ssd, inp, Q, workspace=wc, from_saved=True)
         torch.cuda.synchronize()
         check_fwd(kw, r[0], r[1], y_ref, f_ref, label + " chained")
-        check_bwd(io, gc, ref, label + " chained, saved context")
+        check_bwd(io, gc, ref, label + " chained, saved context", sc)

@@ -174,3 +174,29 @@ def test_packed_bwd_equals_separate():
         assert np.allclose(g["d_init"][s], gs["d_init"][0], rtol=1e-12, atol=1e-13)
         dA += gs["dA"]
     assert np.allclose(g["dA"], dA, rtol=1e-12, atol=1e-13)
+
+
+def test_dA_abs_is_the_sum_of_the_terms_magnitudes():
+    """dA_abs (a diagnostic: per head, the sum over tokens of |delta a <G, S_prev>|,
+    the terms whose signed sum is dA) equals dA where every term has the same
+    sign, exceeds |dA| where they have both signs, and is never below |dA|."""
+    rng = np.random.default_rng(31)
+    # one head, headdim = dstate = 1, positive inputs and upstream gradient:
+    # G_t, S_t, the decays and delta are all positive, so every term is positive
+    L = 9
+    p = dict(x=rng.uniform(0.5, 1.5, (1, L, 1, 1)), dt=rng.uniform(-1.0, 0.5, (1, L, 1)),
+             A=np.array([-0.7]), B=rng.uniform(0.5, 1.5, (1, L, 1, 1)),
+             C=rng.uniform(0.5, 1.5, (1, L, 1, 1)), D=None, dt_bias=None,
+             init=rng.uniform(0.5, 1.5, (1, 1, 1, 1)), dt_softplus=True)
+    dout = rng.uniform(0.5, 1.5, (1, L, 1, 1))
+    g = recurrence.bwd(**p, dout=dout)
+    assert g["dA"][0] > 0
+    assert math.isclose(g["dA_abs"][0], g["dA"][0], rel_tol=1e-12)
+    # the upstream gradient alternating in sign: terms of both signs
+    dalt = dout * np.array([1.0, -1.0] * L)[:L, None, None][None]
+    g2 = recurrence.bwd(**p, dout=dalt)
+    assert g2["dA_abs"][0] > abs(g2["dA"][0]) * (1 + 1e-6)
+    # any problem: the triangle inequality, per head
+    q, dq, dfq = tiny(32)
+    g3 = recurrence.bwd(**q, dout=dq, d_final=dfq)
+    assert np.all(g3["dA_abs"] >= np.abs(g3["dA"]) * (1 - 1e-12))
