@@ -574,7 +574,7 @@ def fp32_layer(dev, tm, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (the SSD scan of one GPU's share); "
+        print("bench.py: libssd times one GPU (the SSD scan over one GPU's share of the batch); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

@@ -8,8 +8,8 @@ is the seeded input generator (``mamba_ssd_chunked_03_amd.inputs``), which
 holds none of the method's arithmetic.
 
 Sources (the pages' own equations were lost in extraction; the formulas used
-are the Mamba-2 selective-SSM recurrence as stated for this build, and every
-function cites the passage it follows):
+are the Mamba-2 selective-SSM recurrence in its standard form, written out in
+each function, and every function cites the passage it follows):
 
 * gigipick.blogspot.com, "LLM Mamba ...": section 1 (the selective SSM as a
   linear recurrence, h_t needs h_{t-1}), section 2 (the scan element pair and
