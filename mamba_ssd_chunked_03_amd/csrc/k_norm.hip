@@ -50,6 +50,18 @@ __device__ __forceinline__ float group_total(float q, int group, float* ws, int 
   return t;
 }
 
+// The gate's sigmoid, 1 / (1 + exp(-z)), from the hardware base-2 exponential and
+// reciprocal (exp(-|z|) = 2^(-|z| log2 e) <= 1, so nothing overflows).  Their
+// error, about 1e-6 of the value here, is far below the bf16 rounding of every
+// output that uses it; the library-accurate exp and an IEEE division took ~25
+// VALU instructions per element and made these kernels wait on the VALU rather
+// than on memory.
+__device__ __forceinline__ float gate_sigmoid(float z) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(z) * 1.4426950408889634f);
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
+  return z >= 0.f ? r : e * r;
+}
+
 __device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -58,36 +70,52 @@ __device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
   }
 }
 
-// One row per workgroup of D/8 threads (16384 independent workgroups at the
-// layer shapes schedule better here than a persistent loop over rows, which was
-// measured 10 % slower).
+// kNormFwdRows rows per workgroup of D/8 threads: every row's loads are issued
+// before the first is used, and w (fp32, twice a bf16 row's bytes) is read once
+// for all of them instead of once per row.  Each row's arithmetic is the same
+// whatever the count.  (Independent workgroups schedule better here than a
+// persistent loop over rows, which was measured 10 % slower.)
+constexpr int kNormFwdRows = 2;
+
 template <bool GATE>
 __global__ __launch_bounds__(1024) void gated_rmsnorm_fwd_kernel(
-    int D, int group, float eps, const uint16_t* __restrict__ Y, const uint16_t* __restrict__ Z,
+    int rows, int D, int group, float eps, const uint16_t* __restrict__ Y, const uint16_t* __restrict__ Z,
     const float* __restrict__ W, uint16_t* __restrict__ OUT, float* __restrict__ R) {
+  constexpr int RR = kNormFwdRows;
   __shared__ float ws[kNormMaxWaves];
-  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
-  const int64_t base = (int64_t)row * D;
-  const u32x4 yv = __builtin_nontemporal_load((const u32x4*)(Y + base) + tid);
-  u32x4 zv = u32x4{0u, 0u, 0u, 0u};
-  if constexpr (GATE) zv = __builtin_nontemporal_load((const u32x4*)(Z + base) + tid);
-  const float4 w0 = ((const float4*)W)[2 * tid], w1 = ((const float4*)W)[2 * tid + 1];
-  float yf[8], zf[8], v[8];
-  unpack8(yv, yf);
-  unpack8(zv, zf);
-  float q = 0.f;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
+  const int row0 = blockIdx.x * RR, nr = min(RR, rows - row0);  // (uniform; a missing row loads the last)
+  u32x4 yv[RR], zv[RR];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    v[e] = GATE ? yf[e] * (zf[e] * sigmoid_f(zf[e])) : yf[e];
-    q += v[e] * v[e];
+  for (int i = 0; i < RR; ++i) {
+    const int64_t base = (int64_t)(row0 + min(i, nr - 1)) * D;
+    yv[i] = __builtin_nontemporal_load((const u32x4*)(Y + base) + tid);
+    zv[i] = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (GATE) zv[i] = __builtin_nontemporal_load((const u32x4*)(Z + base) + tid);
   }
-  const float r = 1.f / sqrtf(group_total(q, group, ws, w, lane, nw) / (float)group + eps);
+  const float4 w0 = ((const float4*)W)[2 * tid], w1 = ((const float4*)W)[2 * tid + 1];
   const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  u32x4 o;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) o[d] = pack_bf2(v[2 * d] * r * wv[2 * d], v[2 * d + 1] * r * wv[2 * d + 1]);
-  ((u32x4*)(OUT + base))[tid] = o;
-  if (R && (tid * 8) % group == 0) R[(int64_t)row * (D / group) + tid * 8 / group] = r;
+  for (int i = 0; i < RR; ++i) {
+    float yf[8], zf[8], v[8];
+    unpack8(yv[i], yf);
+    unpack8(zv[i], zf);
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = GATE ? yf[e] * (zf[e] * gate_sigmoid(zf[e])) : yf[e];
+      q += v[e] * v[e];
+    }
+    const float r = 1.f / sqrtf(group_total(q, group, ws, w, lane, nw) / (float)group + eps);
+    if (i < nr) {
+      const int row = row0 + i;
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] = pack_bf2(v[2 * d] * r * wv[2 * d], v[2 * d + 1] * r * wv[2 * d + 1]);
+      ((u32x4*)(OUT + (int64_t)row * D))[tid] = o;
+      if (R && (tid * 8) % group == 0) R[(int64_t)row * (D / group) + tid * 8 / group] = r;
+    }
+  }
 }
 
 // Workgroup b takes rows b, b + gridDim.x, ...; its per-column dw sums go to
@@ -122,7 +150,7 @@ __global__ __launch_bounds__(1024) void gated_rmsnorm_bwd_kernel(
     float v[8], sg[8], qv = 0.f, qc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sg[e] = GATE ? sigmoid_f(zf[e]) : 1.f;
+      sg[e] = GATE ? gate_sigmoid(zf[e]) : 1.f;
       v[e] = GATE ? yf[e] * (zf[e] * sg[e]) : yf[e];
       qv += v[e] * v[e];
       qc += (wv[e] * df[e]) * v[e];
@@ -198,12 +226,13 @@ hipError_t launch_gated_rmsnorm(int rows, int D, int group, float eps, const voi
   const uint16_t *Y = (const uint16_t*)y, *Z = (const uint16_t*)z;
   if (!bwd) {
     if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + kNormFwdRows - 1) / kNormFwdRows));
     if (z)
-      hipLaunchKernelGGL((gated_rmsnorm_fwd_kernel<true>), dim3((unsigned)rows), block, 0, st, D, group, eps, Y,
-                         Z, w, (uint16_t*)out, r);
+      hipLaunchKernelGGL((gated_rmsnorm_fwd_kernel<true>), grid, block, 0, st, rows, D, group, eps, Y, Z, w,
+                         (uint16_t*)out, r);
     else
-      hipLaunchKernelGGL((gated_rmsnorm_fwd_kernel<false>), dim3((unsigned)rows), block, 0, st, D, group, eps, Y,
-                         Z, w, (uint16_t*)out, r);
+      hipLaunchKernelGGL((gated_rmsnorm_fwd_kernel<false>), grid, block, 0, st, rows, D, group, eps, Y, Z, w,
+                         (uint16_t*)out, r);
     return hipGetLastError();
   }
   const int nb = norm_bwd_blocks(rows);

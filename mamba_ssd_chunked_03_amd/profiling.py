@@ -29,6 +29,14 @@ was busy or held up by the L1.  Per compute unit a kernel can read at most
 kernels below the HBM peak.
 
     python -m mamba_ssd_chunked_03_amd.profiling mlp --pmc DIR --md OUT.md --command "..."
+
+A fourth, ``issue``, reads two counter runs holding ISSUE_COUNTERS (8 SQ
+counters each) and reports the instruction mix per kernel: VALU, transcendental,
+scalar, LDS and MFMA instructions per launch, and the time the VALU instructions
+alone occupy the SIMDs (a wave64 instruction takes 4 cycles on a 16-lane SIMD, a
+transcendental one 16) as a fraction of the kernel's duration.
+
+    python -m mamba_ssd_chunked_03_amd.profiling issue --pmc DIR_A DIR_B --md OUT.md --command "..."
 """
 import argparse
 import collections
@@ -302,6 +310,80 @@ def mlp(counter_csv, cus, xcds, simds_per_cu=4):
     return out
 
 
+ISSUE_COUNTERS = (("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+                   "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"),
+                  ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_ANY",
+                   "SQ_INSTS_MFMA", "SQ_INST_CYCLES_VALU", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_MISC"))
+# the ones the summary uses (gfx950 returns no SQ_INST_CYCLES_VALU)
+ISSUE_USED = ("SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU_TRANS_F32",
+              "SQ_WAIT_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_MFMA")
+VALU_CYCLES, TRANS_CYCLES = 4, 16  # per wave64 instruction on a 16-lane SIMD (transcendentals: quarter rate)
+
+
+def issue_mix(counter_csvs, cus, simds_per_cu, ghz):
+    """{key: figures} from counter runs holding ISSUE_COUNTERS.  Per kernel name the
+    mean of each counter over its launches (a key with several kernels sums them);
+    the duration is the mean dispatch time of the first run."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(dict)
+    for n, path in enumerate(counter_csvs):
+        for row in _rows(path):
+            name = _col(row, "Kernel_Name")
+            key = kernel_key(name)
+            if key is None or key == "copy":
+                continue
+            vals[(key, name)][_col(row, "Counter_Name")].append(float(_col(row, "Counter_Value")))
+            if n == 0:
+                durs[(key, name)][_col(row, "Dispatch_Id")] = (int(_col(row, "End_Timestamp"))
+                                                               - int(_col(row, "Start_Timestamp")))
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    for (key, name), d in vals.items():
+        for c, v in d.items():
+            tot[key][c] += _mean(v)
+        if durs[(key, name)]:
+            tot[key]["_ns"] += _mean(list(durs[(key, name)].values()))
+    out = {}
+    for key, t in tot.items():
+        if any(c not in t for c in ISSUE_USED) or not t["_ns"]:
+            continue
+        valu, trans = t["SQ_INSTS_VALU"], t["SQ_INSTS_VALU_TRANS_F32"]
+        issue_us = (valu * VALU_CYCLES + trans * (TRANS_CYCLES - VALU_CYCLES)) / (cus * simds_per_cu) / ghz / 1e3
+        out[key] = {
+            "us": t["_ns"] / 1e3, "valu": valu, "trans": trans, "salu": t["SQ_INSTS_SALU"],
+            "lds": t["SQ_INSTS_LDS"], "mfma": t["SQ_INSTS_MFMA"], "valu_issue_us": issue_us,
+            "valu_issue_frac": issue_us / (t["_ns"] / 1e3),
+            "wave_wait_frac": t["SQ_WAIT_ANY"] / t["SQ_WAVE_CYCLES"],
+            "lds_conflict_per_inst": t["SQ_LDS_BANK_CONFLICT"] / t["SQ_INSTS_LDS"] if t["SQ_INSTS_LDS"] else 0.0,
+            "source_sha": source_hash(key) if key in KERNEL_FILES else ""}
+    return out
+
+
+def issue_md(res, title, commands, summary_cmd, cus, simds_per_cu, ghz):
+    lines = (["# " + title, ""] if title else []) + [
+        "Counter runs (from the repository root, one MI355X, one rocprofv3 pass each):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "Summarised with:", "", "    " + summary_cmd, "",
+              "Instructions are wave instructions per launch (SQ_INSTS_VALU, SQ_INSTS_VALU_TRANS_F32, "
+              "SQ_INSTS_SALU, SQ_INSTS_LDS, SQ_INSTS_MFMA). VALU issue = the SIMD time of the VALU "
+              "instructions alone, %d cycles each (a wave64 instruction on a 16-lane SIMD) and %d for a "
+              "transcendental one, over %d compute units x %d SIMDs at %.1f GHz, as a fraction of the "
+              "kernel's duration in the first run; MFMA instructions run on their own unit and are not "
+              "in it. Waves waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES. LDS conflict = SQ_LDS_BANK_CONFLICT "
+              "cycles per LDS instruction."
+              % (VALU_CYCLES, TRANS_CYCLES, cus, simds_per_cu, ghz), "",
+              "| Kernel | us | VALU (M) | of them transcendental (M) | SALU (M) | LDS (M) | MFMA (M) "
+              "| VALU issue (us) | VALU issue / duration | Waves waiting | LDS conflict | Source hash |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key in KERNEL_FILES:
+        if key in res:
+            e = res[key]
+            lines.append("| %s | %.1f | %.2f | %.2f | %.2f | %.2f | %.2f | %.1f | %.2f | %.2f | %.2f | %s |" % (
+                key, e["us"], e["valu"] / 1e6, e["trans"] / 1e6, e["salu"] / 1e6, e["lds"] / 1e6,
+                e["mfma"] / 1e6, e["valu_issue_us"], e["valu_issue_frac"], e["wave_wait_frac"],
+                e["lds_conflict_per_inst"], e["source_sha"]))
+    return "\n".join(lines) + "\n"
+
+
 def mlp_md(res, title, commands, summary_cmd, cus, xcds):
     def opt(v, f):
         return "-" if v is None or not v else f % v
@@ -429,6 +511,12 @@ def main(argv=None):
     m.add_argument("--json", help="also write the figures here")
     m.add_argument("--title", default="")
     m.add_argument("--command", action="append", default=[])
+    i = sub.add_parser("issue")
+    i.add_argument("--pmc", nargs=2, required=True, help="the two counter run directories (ISSUE_COUNTERS)")
+    i.add_argument("--md", required=True)
+    i.add_argument("--ghz", type=float, default=2.4, help="shader clock for the VALU issue time")
+    i.add_argument("--title", default="")
+    i.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     here = "python -m mamba_ssd_chunked_03_amd.profiling " + shlex.join(argv if argv else sys.argv[1:])
 
@@ -440,6 +528,11 @@ def main(argv=None):
                                 [csv_in(p, "counter_collection") for p in a.copy])
         with open(a.md, "w") as f:
             f.write(request_md(res, cp, a.copy_bytes, a.title, a.command, here))
+    elif a.cmd == "issue":
+        cus, _, spc = agent_counts(csv_in(a.pmc[0], "agent_info"))
+        res = issue_mix([csv_in(p, "counter_collection") for p in a.pmc], cus, spc, a.ghz)
+        with open(a.md, "w") as f:
+            f.write(issue_md(res, a.title, a.command, here, cus, spc, a.ghz))
     elif a.cmd == "mlp":
         cus, xcds, spc = agent_counts(csv_in(a.pmc, "agent_info"))
         res = mlp(csv_in(a.pmc, "counter_collection"), cus, xcds, spc)

@@ -509,9 +509,10 @@ def gated_rmsnorm_fwd(y, z, weight, group, eps=1e-5, out=None, rstd=None, prepar
     dev = _dev(y, z, weight, out, rstd)
     out = torch.empty_like(y) if out is None else out
     args = (ctypes.byref(p), _ptr(y), _ptr(z), _ptr(weight), _ptr(out), _ptr(rstd), _stream(dev))
+    L = lib()
 
     def launch():
-        _check(lib().ssd_gated_rmsnorm_fwd(*args), keep=p)
+        _check(L.ssd_gated_rmsnorm_fwd(*args), keep=p)
 
     if prepare:
         return launch, out
@@ -544,8 +545,10 @@ def gated_rmsnorm_bwd(dout, y, z, weight, group, eps=1e-5, workspace=None, grads
     args = (ctypes.byref(p), _ptr(dout), _ptr(y), _ptr(z), _ptr(weight), _ptr(dy), _ptr(dz), _ptr(dw),
             _ptr(ws), ws.numel(), _stream(dev))
 
+    L = lib()
+
     def launch():
-        _check(lib().ssd_gated_rmsnorm_bwd(*args), keep=(p, ws))
+        _check(L.ssd_gated_rmsnorm_bwd(*args), keep=(p, ws))
 
     if prepare:
         return launch, grads

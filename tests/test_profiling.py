@@ -109,6 +109,30 @@ def test_mlp_littles_law(tmp_path):
     assert res["mfma_gflop"] == 2e6 * 512 / 1e9 and res["mfma_busy"] == 0.25 and res["mfma_insts"] == 10.0
 
 
+def test_issue_mix(tmp_path):
+    """VALU issue time: 4 cycles per wave instruction, 16 per transcendental one, over
+    CUs x SIMDs at the given clock, as a fraction of the first run's duration."""
+    dx = "void ssd::bwd_dx_bf16_kernel<64, 128>(a)"
+    cols = PMC_COLS + ["Start_Timestamp", "End_Timestamp"]
+    run_a = {"SQ_WAVE_CYCLES": 100.0, "SQ_INSTS_VALU": 1000.0, "SQ_INSTS_VALU_TRANS_F32": 100.0,
+             "SQ_INSTS_SALU": 7.0, "SQ_INSTS_LDS": 60.0}
+    run_b = {"SQ_WAIT_ANY": 25.0, "SQ_LDS_BANK_CONFLICT": 30.0, "SQ_INSTS_MFMA": 5.0}
+    pa = write(tmp_path / "a.csv", cols, [[d, dx, c, v, 10_000 * d, 10_000 * d + 1000]
+                                          for d in (1, 2) for c, v in run_a.items()])
+    pb = write(tmp_path / "b.csv", cols, [[d, dx, c, v, 10_000 * d, 10_000 * d + 3000]
+                                          for d in (1, 2) for c, v in run_b.items()])
+    e = profiling.issue_mix([pa, pb], cus=2, simds_per_cu=4, ghz=2.0)["bwd_dx"]
+    # (1000 x 4 + 100 x 12) cycles over 8 SIMDs = 650 cycles = 325 ns of a 1000 ns launch
+    assert abs(e["us"] - 1.0) < 1e-12 and abs(e["valu_issue_us"] - 0.325) < 1e-12
+    assert abs(e["valu_issue_frac"] - 0.325) < 1e-12
+    assert e["wave_wait_frac"] == 0.25 and e["lds_conflict_per_inst"] == 0.5
+    assert (e["valu"], e["trans"], e["salu"], e["lds"], e["mfma"]) == (1000.0, 100.0, 7.0, 60.0, 5.0)
+    md = profiling.issue_md({"bwd_dx": e}, "t", ["cmd"], "sum", 2, 4, 2.0)
+    assert "| bwd_dx | 1.0 | 0.00 | 0.00 | 0.00 | 0.00 | 0.00 | 0.3 | 0.33 | 0.25 | 0.50 |" in md
+    # a kernel missing a counter the summary uses is left out
+    assert profiling.issue_mix([pa], cus=2, simds_per_cu=4, ghz=2.0) == {}
+
+
 def test_kernels_table_keeps_forms_apart(tmp_path):
     rows = [["void ssd::state_passing_kernel<8, 4, unsigned short, 0>(a)", 0, 4000],
             ["void ssd::state_passing_seq_kernel<unsigned short, 0, 1>(a)", 10000, 13000],
